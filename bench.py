@@ -1,0 +1,242 @@
+#!/usr/bin/env python3
+"""Throughput of one verification step on one MI355X.
+
+A step is one pass of the whole hot path over one batch already resident in
+HBM: ``sv_spec_verify`` (softmax statistics of every draft and target row,
+accept tests, first-rejection scan, residual or bonus sample, plus the
+estimator feature and score of every draft row from the same pass) followed
+by ``sv_av_fit_step`` (one damped IRLS step over the batch's labels).
+
+Default workload: B=256 requests, K=4 drafts, V=128256, bf16 logits
+(``bf16_b256_k4_v128256_peaked``).  Several independently drawn input sets
+rotate between steps so that no step reads rows the previous one left in the
+256 MB Infinity Cache.
+
+Prints one JSON line: positions/s over the timed steps, the roofline of the
+verification kernel (algorithmic HBM bytes per launch / its mean duration from
+HIP events on the launching stream, against the 8 TB/s HBM3E peak) and the
+CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "verified draft positions/sec at B=256,K=4,V=128256 bf16; achieved HBM GB/s"
+PEAK_HBM_GBS = 8000.0
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="bf16_b256_k4_v128256_peaked")
+    p.add_argument("--rotate", type=int, default=3, help="input sets cycled between steps")
+    p.add_argument("--graph", type=int, default=1, help="replay the steps from a captured HIP graph")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                   help="per-launch HBM bytes measured with rocprofv3 counters (optional)")
+    return p.parse_args()
+
+
+def to_device(batch, dev):
+    import numpy as np
+    import torch
+
+    def rows(a):
+        if batch.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+
+    t = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a)).to(device=dev, dtype=dt)
+    return dict(draft=rows(batch.draft), draft_row_start=t(batch.draft_row_start, torch.int64),
+                target=rows(batch.target), target_row_start=t(batch.target_row_start, torch.int64),
+                num_draft=t(batch.num_draft, torch.int32), draft_tokens=t(batch.draft_tokens, torch.int32),
+                temperature=t(batch.temperature, torch.float32), u_accept=t(batch.u_accept, torch.float32),
+                u_residual=t(batch.u_residual, torch.float32), u_bonus=t(batch.u_bonus, torch.float32))
+
+
+def cpu_baseline(batch, budget_s):
+    """The oracle, untuned, on the first requests of input set 0 until the
+    time budget is spent: verification, estimator feature/score of the
+    request's draft rows, and the refit sums of its labels."""
+    import numpy as np
+
+    from oracle import av as oav
+    from oracle import verify as ov
+
+    t0 = time.perf_counter()
+    n = pos = 0
+    feats, labs = [], []
+    while n < batch.B and (time.perf_counter() - t0 < budget_s or n < 4):
+        k = int(batch.num_draft[n])
+        ds, ts = int(batch.draft_row_start[n]), int(batch.target_row_start[n])
+        zd = ov.decode_rows(batch.draft[ds:ds + k], batch.dtype)
+        zt = ov.decode_rows(batch.target[ts:ts + k + 1], batch.dtype)
+        res = ov.verify_request(zd, zt, batch.draft_tokens[n, :k], float(batch.temperature[n]),
+                                batch.u_accept[n, :k], float(batch.u_residual[n]), float(batch.u_bonus[n]))
+        f = np.full(batch.max_k, np.nan, np.float32)
+        for i in range(k):
+            f[i] = oav.feature(zd[i], float(batch.temperature[n]))
+            oav.score(f[i], batch.av_params, i)
+        lab = np.full(batch.max_k, -1, np.int8)
+        lab[:k] = res.labels
+        feats.append(f)
+        labs.append(lab)
+        n += 1
+        pos += k
+    oav.fit_step(np.array(feats), np.array(labs), batch.av_params, np.zeros((batch.max_k, 6)), do_update=True)
+    dt = time.perf_counter() - t0
+    return {"value": pos / dt, "unit": "positions/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {n} requests ({pos} positions) of input set 0; fp64 numpy verify + "
+                      f"feature/score + refit, {dt:.1f} s single-threaded"}
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (requests shard across GPUs "
+              "with no exchange, so the one-GPU rate is the per-GPU rate).", file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import draft_token_verification_spec_amd as sv
+    from synth import gen
+
+    dev = torch.device("cuda:0")
+    print(f"bench: drawing {args.rotate} input sets of {args.workload}", file=sys.stderr, flush=True)
+    sets = []
+    for r in range(args.rotate):
+        b = gen.make_batch(args.workload, trial=r)
+        sets.append((b, to_device(b, dev)))
+    b0 = sets[0][0]
+    B, K, V = b0.B, b0.max_k, b0.V
+    positions = int(b0.num_draft.sum())
+    assert all(int(s[0].num_draft.sum()) == positions for s in sets)
+    bytes_per_launch = b0.algorithmic_bytes()
+
+    params = torch.tensor(b0.av_params, device=dev)
+    accum = torch.zeros(K, 6, dtype=torch.float64, device=dev)
+    ws = sv.Workspace()
+    outs = []
+    for _, d in sets:
+        o = {"accept_len": torch.empty(B, dtype=torch.int32, device=dev),
+             "out_tokens": torch.empty(B, K + 1, dtype=torch.int32, device=dev),
+             "labels": torch.empty(B, K, dtype=torch.int8, device=dev),
+             "p_draft": torch.empty(B, K, dtype=torch.float32, device=dev),
+             "p_target": torch.empty(B, K, dtype=torch.float32, device=dev),
+             "av_feature": torch.empty(B, K, dtype=torch.float32, device=dev),
+             "av_score": torch.empty(B, K, dtype=torch.float32, device=dev)}
+        outs.append(o)
+    ws.get(dev, sv.sv_workspace_size(B, V, K, sv.SV_BF16 if b0.dtype == "bf16" else sv.SV_F32))
+
+    def step(i, ev=None):
+        _, d = sets[i % len(sets)]
+        o = outs[i % len(sets)]
+        if ev is not None:
+            ev[0].record()
+        sv.sv_spec_verify(d["draft"], d["draft_row_start"], d["target"], d["target_row_start"], d["num_draft"],
+                          d["draft_tokens"], d["temperature"], d["u_accept"], d["u_residual"], d["u_bonus"],
+                          max_k=K, av_params=params, want_feature=True, workspace=ws, out=o)
+        if ev is not None:
+            ev[1].record()
+        sv.sv_av_fit_step(o["av_feature"], o["labels"], params, accum, do_update=True)
+
+    for w in range(args.warmup):
+        step(w)
+    torch.cuda.synchronize(dev)
+
+    steps = args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    graph = None
+    if args.graph:
+        # capture one rotation period per graph replay; the library issues no
+        # memset and allocates nothing, so the steps capture as plain kernels
+        period = len(sets)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(period):
+                step(i)
+        graph.replay()
+        torch.cuda.synchronize(dev)
+
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    start.record()
+    if graph is not None:
+        reps = max(1, steps // len(sets))
+        steps = reps * len(sets)
+        for _ in range(reps):
+            graph.replay()
+        end.record()
+        torch.cuda.synchronize(dev)
+        # per-kernel time from a separate pass of eagerly launched steps with events
+        for k in range(min(steps, 3 * len(sets) * 10)):
+            step(k, evs[k])
+        torch.cuda.synchronize(dev)
+        vms = [a.elapsed_time(z) for a, z in evs[:min(steps, 3 * len(sets) * 10)]]
+    else:
+        for k in range(steps):
+            step(k, evs[k])
+        end.record()
+        torch.cuda.synchronize(dev)
+        vms = [a.elapsed_time(z) for a, z in evs]
+    wall = time.perf_counter() - t0
+    ms_total = start.elapsed_time(end)
+    ms_per_step = ms_total / steps
+    verify_ms = float(np.mean(vms))
+    value = positions / (ms_per_step * 1e-3)
+    achieved = bytes_per_launch / (verify_ms * 1e-3) / 1e9
+
+    traffic = None
+    if os.path.exists(args.traffic):
+        try:
+            tr = json.load(open(args.traffic))
+            if tr.get("workload") == args.workload:
+                traffic = tr.get("bytes_per_launch")
+        except (OSError, ValueError):
+            traffic = None
+
+    al = outs[0]["accept_len"].float().mean().item()
+    res = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "positions/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "B": B, "K": K, "V": V, "logits": b0.dtype,
+                   "step": "sv_spec_verify (with estimator feature+score) + sv_av_fit_step",
+                   "input_sets_rotated": len(sets), "graph_replay": bool(graph is not None)},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
+                     "kernel": "spec_verify_kernel", "kernel_ms": verify_ms,
+                     "algorithmic_bytes_per_launch": bytes_per_launch},
+        "extra": {"mean_accept_len": al, "positions_per_step": positions, "wall_s": wall},
+    }
+    if not args.no_cpu_baseline:
+        print("bench: timing the CPU oracle", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(b0, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

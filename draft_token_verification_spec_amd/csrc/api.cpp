@@ -1,0 +1,159 @@
+// C entry points of libspecverify.so: host-side argument checks, workspace
+// layout and kernel launches on the caller's stream.  No call allocates,
+// frees or synchronises the host.
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "sv_internal.hpp"
+
+using namespace sv;
+
+namespace {
+
+// Work items of one call are numbered with 32-bit claim counters; the
+// scoring kernel's 1-D grid is limited to 2^32 - 1 threads.
+constexpr uint64_t kMaxItems = uint64_t(1) << 31;
+constexpr uint64_t kMaxGrid = (uint64_t(1) << 32) / kThreads - 1;
+
+bool dtype_ok(int dtype) { return dtype == SV_F32 || dtype == SV_BF16; }
+
+int check_sizes(int B, int V, int max_k, int dtype) {
+  if (B < 0 || V < 1 || max_k < 0 || !dtype_ok(dtype)) return SV_ERR_INVALID_ARG;
+  if (max_k > SV_MAX_K || V > SV_MAX_V || B > SV_MAX_B) return SV_ERR_UNSUPPORTED;
+  const uint64_t items = uint64_t(B) * (uint64_t(rows_per_request(max_k)) * num_segments(V, dtype) +
+                                        uint64_t(num_sample_segments(V, dtype)));
+  if (items > kMaxItems || items > kMaxGrid) return SV_ERR_UNSUPPORTED;
+  return SV_OK;
+}
+
+int to_status(hipError_t e) { return e == hipSuccess ? SV_OK : SV_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+size_t sv_workspace_size(int B, int V, int max_k, int dtype) {
+  if (check_sizes(B, V, max_k, dtype) != SV_OK) return 0;
+  return ws_layout(B, V, max_k, dtype).total;
+}
+
+int sv_spec_verify(void* stream, int B, int V, int max_k, int dtype, const void* draft_logits,
+                   const int64_t* draft_row_start, int64_t draft_row_stride, const void* target_logits,
+                   const int64_t* target_row_start, int64_t target_row_stride, const int32_t* num_draft,
+                   const int32_t* draft_tokens, const float* temperature, const float* u_accept,
+                   const float* u_residual, const float* u_bonus, int32_t* accept_len, int32_t* out_tokens,
+                   int8_t* labels, float* p_draft_at_token, float* p_target_at_token, const float* av_params,
+                   float* av_feature, float* av_score, void* workspace, size_t workspace_bytes) {
+  const int st = check_sizes(B, V, max_k, dtype);
+  if (st != SV_OK) return st;
+  if (B == 0) return SV_OK;
+  if (!target_logits || !target_row_start || !num_draft || !temperature || !u_residual || !u_bonus ||
+      !accept_len || !out_tokens)
+    return SV_ERR_INVALID_ARG;
+  if (max_k > 0 && (!draft_logits || !draft_row_start || !draft_tokens || !u_accept)) return SV_ERR_INVALID_ARG;
+  if (target_row_stride < V || (max_k > 0 && draft_row_stride < V)) return SV_ERR_INVALID_ARG;
+  if (av_score && (!av_feature || !av_params)) return SV_ERR_INVALID_ARG;
+  const WsLayout L = ws_layout(B, V, max_k, dtype);
+  if (!workspace || workspace_bytes < L.total) return SV_ERR_WORKSPACE;
+
+  char* ws = static_cast<char*>(workspace);
+  VerifyArgs a;
+  a.B = B;
+  a.V = V;
+  a.max_k = max_k;
+  a.nseg = L.nseg;
+  a.nseg2 = L.nseg2;
+  a.R = L.R;
+  a.draft = draft_logits;
+  a.draft_start = draft_row_start;
+  a.draft_stride = draft_row_stride;
+  a.target = target_logits;
+  a.target_start = target_row_start;
+  a.target_stride = target_row_stride;
+  a.num_draft = num_draft;
+  a.tokens = draft_tokens;
+  a.temperature = temperature;
+  a.u_accept = u_accept;
+  a.u_residual = u_residual;
+  a.u_bonus = u_bonus;
+  a.accept_len = accept_len;
+  a.out_tokens = out_tokens;
+  a.labels = labels;
+  a.p_draft = p_draft_at_token;
+  a.p_target = p_target_at_token;
+  a.av_params = av_params;
+  a.av_feature = av_feature;
+  a.av_score = av_score;
+  a.ctrl = reinterpret_cast<uint32_t*>(ws + L.ctrl);
+  a.tickets = reinterpret_cast<uint32_t*>(ws + L.tickets);
+  a.tickets2 = reinterpret_cast<uint32_t*>(ws + L.tickets2);
+  a.flags = reinterpret_cast<int*>(ws + L.flags);
+  a.partials = reinterpret_cast<Partial*>(ws + L.partials);
+  a.zval = reinterpret_cast<float*>(ws + L.zval);
+  a.records = reinterpret_cast<Record*>(ws + L.records);
+  a.segsum = reinterpret_cast<float*>(ws + L.segsum);
+  return to_status(launch_spec_verify(a, dtype, static_cast<hipStream_t>(stream)));
+}
+
+int sv_av_score(void* stream, int B, int V, int max_k, int dtype, const void* draft_logits,
+                const int64_t* draft_row_start, int64_t draft_row_stride, const int32_t* num_draft,
+                const float* temperature, const float* params, float prune_threshold, float* feature,
+                float* score, int32_t* num_kept, void* workspace, size_t workspace_bytes) {
+  const int st = check_sizes(B, V, max_k, dtype);
+  if (st != SV_OK) return st;
+  if (B == 0) return SV_OK;
+  if (!num_draft || !temperature) return SV_ERR_INVALID_ARG;
+  if (max_k == 0) {
+    if (!num_kept) return SV_OK;
+  } else if (!draft_logits || !draft_row_start || !params || !feature || !score || draft_row_stride < V) {
+    return SV_ERR_INVALID_ARG;
+  }
+  const WsLayout L = ws_layout(B, V, max_k, dtype);
+  if (!workspace || workspace_bytes < L.total) return SV_ERR_WORKSPACE;
+
+  char* ws = static_cast<char*>(workspace);
+  ScoreArgs a;
+  a.B = B;
+  a.V = V;
+  a.max_k = max_k;
+  a.nseg = L.nseg;
+  a.R = L.R;
+  a.draft = draft_logits;
+  a.draft_start = draft_row_start;
+  a.draft_stride = draft_row_stride;
+  a.num_draft = num_draft;
+  a.temperature = temperature;
+  a.params = params;
+  a.threshold = prune_threshold;
+  a.feature = feature;
+  a.score = score;
+  a.num_kept = num_kept;
+  a.tickets = reinterpret_cast<uint32_t*>(ws + L.tickets);
+  a.partials = reinterpret_cast<Partial*>(ws + L.partials);
+  return to_status(launch_av_score(a, dtype, static_cast<hipStream_t>(stream)));
+}
+
+int sv_av_fit_step(void* stream, int B, int max_k, const float* feature, const int8_t* labels, float* params,
+                   double* accum, float damping_c, float ridge, int do_update) {
+  if (B < 0 || max_k < 0) return SV_ERR_INVALID_ARG;
+  if (max_k > SV_MAX_K) return SV_ERR_UNSUPPORTED;
+  if (!(damping_c >= 0.f) || !(ridge >= 0.f)) return SV_ERR_INVALID_ARG;
+  if (max_k == 0) return SV_OK;
+  if (!params || !accum || (B > 0 && (!feature || !labels))) return SV_ERR_INVALID_ARG;
+  return to_status(launch_av_fit(B, max_k, feature, labels, params, accum, damping_c, ridge, do_update,
+                                 static_cast<hipStream_t>(stream)));
+}
+
+const char* sv_status_string(int status) {
+  switch (status) {
+    case SV_OK: return "ok";
+    case SV_ERR_INVALID_ARG: return "invalid argument";
+    case SV_ERR_UNSUPPORTED: return "unsupported size";
+    case SV_ERR_WORKSPACE: return "workspace missing or too small";
+    case SV_ERR_HIP: return "HIP runtime error at launch";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,201 @@
+// Online acceptance estimator for gfx950.
+//
+// Method: [AV] "Adaptive Verification ohne Confidence Head" (spke.com; Arabic
+// mirror "التحقق التكيفي بدون رأس ثقة"):
+//   "Solution" / "Scoring the distribution": score_i = sigmoid(omega * x +
+//   beta_i) with x = logit(q_max) of the draft distribution, one shared slope
+//   and one intercept per draft position;
+//   "Other features considered": survival = running product of the scores;
+//   "Fitting the coefficients": IRLS on the accept/reject labels up to the
+//   first rejection, H and g accumulated over a round and the Newton system
+//   solved on its last step, each step damped by n / (n + constant).
+#include "sv_device.hpp"
+
+namespace sv {
+
+// ---------------------------------------------------------------------------
+// scoring: workgroup (b, i, s) reduces segment s of draft row i with the
+// maxima kept out of the sum; the request's last workgroup turns the row
+// statistics into feature, score, survival and the kept count.
+// ---------------------------------------------------------------------------
+
+template <typename ET>
+__global__ __launch_bounds__(kThreads) void av_score_kernel(ScoreArgs a) {
+  __shared__ Partial lds_part[kWaves];
+  __shared__ float sc[SV_MAX_K];
+  __shared__ int lds_flag;
+
+  constexpr int SEG = kSegBytes / int(sizeof(ET));
+  const int tid = threadIdx.x;
+  const int item = blockIdx.x;
+  const int s = item % a.nseg;
+  const int rr = item / a.nseg;
+  const int max_k = a.max_k;
+  const int mk1 = max_k > 0 ? max_k : 1;  // requests with no drafts still own one workgroup
+  const int i = rr % mk1;
+  const int b = rr / mk1;
+  const int K = min(max(a.num_draft[b], 0), max_k);
+  const float T = a.temperature[b];
+  const float c = kLog2e / ((T > 0.f) ? T : 1.f);
+
+  if (K == 0) {  // nothing to score: one workgroup fills the request's outputs
+    if (i == 0 && s == 0) {
+      if (tid < max_k) {
+        a.feature[size_t(b) * max_k + tid] = NAN;
+        a.score[size_t(b) * max_k + tid] = NAN;
+      }
+      if (tid == 0 && a.num_kept) a.num_kept[b] = 0;
+    }
+    return;
+  }
+  if (i >= K) return;
+
+  const ET* row = static_cast<const ET*>(a.draft) + (a.draft_start[b] + i) * a.draft_stride;
+  const Partial p = segment_stats<ET, kSumExclusive>(row, s * SEG, a.V, is_aligned16(row), c, lds_part);
+  if (tid == 0) publish(&a.partials[(size_t(b) * a.R + i) * a.nseg + s], p);
+
+  if (!arrive_last(&a.tickets[b], uint32_t(a.nseg) * uint32_t(K), &lds_flag)) return;
+
+  if (tid < max_k) {
+    float x = NAN, score = NAN;
+    if (tid < K) {
+      const Partial D = combine_published(&a.partials[(size_t(b) * a.R + tid) * a.nseg], a.nseg, c, false);
+      const float so = D.s + (D.cnt - 1.f);
+      x = (so > 0.f) ? fminf(-fast_log2(so) * kLn2, 80.f) : 80.f;
+      const float t = a.params[0] * x + a.params[1 + tid];
+      score = 1.f / (1.f + fast_exp2(-t * kLog2e));
+    }
+    a.feature[size_t(b) * max_k + tid] = x;
+    a.score[size_t(b) * max_k + tid] = score;
+    sc[tid] = score;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    if (a.num_kept) {
+      int kept = K;
+      if (a.threshold > 0.f) {
+        float surv = 1.f;
+        kept = 0;
+        for (int j = 0; j < K; ++j) {
+          surv *= sc[j];
+          if (!(surv >= a.threshold)) break;
+          ++kept;
+        }
+      }
+      a.num_kept[b] = kept;
+    }
+    store_dev(&a.tickets[b], 0u);
+  }
+}
+
+hipError_t launch_av_score(const ScoreArgs& a, int dtype, hipStream_t stream) {
+  const unsigned grid = unsigned(a.B) * unsigned(a.max_k > 0 ? a.max_k : 1) * unsigned(a.nseg);
+  if (dtype == SV_BF16)
+    hipLaunchKernelGGL(av_score_kernel<uint16_t>, dim3(grid), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(av_score_kernel<float>, dim3(grid), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// refit step: one workgroup.  For each position, threads take requests
+// b = tid, tid + 256, ... and accumulate the six sums in fp64; a fixed-order
+// reduction (wave butterfly, then waves in order) makes the result
+// deterministic.  On the round's last step thread 0 solves the arrowhead
+// Newton system H * delta = -g by eliminating the intercepts (Schur
+// complement on the slope), damps, updates the parameters and clears the
+// accumulator.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ double sigmoid_d(double t) {
+  if (t >= 0.0) return 1.0 / (1.0 + exp(-t));
+  const double e = exp(t);
+  return e / (1.0 + e);
+}
+
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__global__ __launch_bounds__(kThreads) void av_fit_kernel(int B, int max_k, const float* feature,
+                                                          const int8_t* labels, float* params, double* accum,
+                                                          float damping_c, float ridge, int do_update) {
+  __shared__ double red[kWaves][6];
+  __shared__ double acc[SV_MAX_K][6];  // accumulator after this step
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const double omega = params[0];
+  for (int i = 0; i < max_k; ++i) {
+    const double beta = params[1 + i];
+    double v[6] = {0, 0, 0, 0, 0, 0};
+    for (int b = tid; b < B; b += kThreads) {
+      const int y = labels[size_t(b) * max_k + i];
+      if (y != 0 && y != 1) continue;
+      const double x = feature[size_t(b) * max_k + i];
+      const double pi = sigmoid_d(omega * x + beta);
+      const double w = pi * (1.0 - pi);
+      const double r = pi - double(y);
+      v[0] += 1.0;
+      v[1] += w;
+      v[2] += w * x;
+      v[3] += w * x * x;
+      v[4] += r;
+      v[5] += r * x;
+    }
+#pragma unroll
+    for (int k = 0; k < 6; ++k) v[k] = wave_sum_d(v[k]);
+    if (lane == 0)
+#pragma unroll
+      for (int k = 0; k < 6; ++k) red[wave][k] = v[k];
+    __syncthreads();
+    if (tid < 6) {
+      double t = red[0][tid];
+      for (int w = 1; w < kWaves; ++w) t += red[w][tid];
+      t += accum[size_t(i) * 6 + tid];
+      acc[i][tid] = t;
+      if (!do_update) accum[size_t(i) * 6 + tid] = t;
+    }
+    __syncthreads();
+  }
+  if (!do_update) return;
+  if (tid == 0) {
+    double N = 0.0, h = ridge, gw = 0.0;
+    for (int i = 0; i < max_k; ++i) {
+      N += acc[i][0];
+      h += acc[i][3];
+      gw += acc[i][5];
+    }
+    if (N > 0.0) {
+      // eliminate the intercepts of positions with labels
+      double schur = h, rhs = -gw;
+      for (int i = 0; i < max_k; ++i) {
+        const double n = acc[i][0];
+        if (n <= 0.0) continue;
+        const double D = acc[i][1] + ridge, Bi = acc[i][2], gb = acc[i][4];
+        schur -= Bi * Bi / D;
+        rhs += Bi * gb / D;
+      }
+      const double dw = (schur > 0.0) ? rhs / schur : 0.0;
+      params[0] = float(omega + dw * (N / (N + double(damping_c))));
+      for (int i = 0; i < max_k; ++i) {
+        const double n = acc[i][0];
+        if (n <= 0.0) continue;
+        const double D = acc[i][1] + ridge, Bi = acc[i][2], gb = acc[i][4];
+        const double db = (-gb - Bi * dw) / D;
+        params[1 + i] = float(double(params[1 + i]) + db * (n / (n + double(damping_c))));
+      }
+    }
+  }
+  __syncthreads();
+  for (int k = tid; k < 6 * max_k; k += kThreads) accum[k] = 0.0;
+}
+
+hipError_t launch_av_fit(int B, int max_k, const float* feature, const int8_t* labels, float* params,
+                         double* accum, float damping_c, float ridge, int do_update, hipStream_t stream) {
+  hipLaunchKernelGGL(av_fit_kernel, dim3(1), dim3(kThreads), 0, stream, B, max_k, feature, labels, params, accum,
+                     damping_c, ridge, do_update);
+  return hipGetLastError();
+}
+
+}  // namespace sv

@@ -1,0 +1,174 @@
+// Internal layout shared by the host dispatch (api.cpp) and the kernels.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/specverify.h"
+
+namespace sv {
+
+// Threads per workgroup (4 wave64s) and 16-byte vectors each thread loads per
+// row segment of a statistics item: one segment is kThreads * kVecsPerThread
+// 16-byte vectors = 64 KiB of a row, whatever the element type.
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr int kVecsPerThread = 16;
+constexpr int kSegBytes = kThreads * kVecsPerThread * 16;
+// The draw splits a row into 32 KiB sampling segments: kWaves groups of
+// kGroup blocks, a block being 64 lanes x one 16-byte vector.
+constexpr int kGroup = 8;
+constexpr int kSampleSegBytes = kWaves * kGroup * 64 * 16;
+
+__host__ __device__ constexpr int elems_per_vec(int dtype) { return dtype == SV_BF16 ? 8 : 4; }
+__host__ __device__ constexpr int seg_elems(int dtype) { return kSegBytes / (dtype == SV_BF16 ? 2 : 4); }
+__host__ __device__ inline int num_segments(int V, int dtype) {
+  return (V + seg_elems(dtype) - 1) / seg_elems(dtype);
+}
+__host__ __device__ inline int num_sample_segments(int V, int dtype) {
+  const int e = kSampleSegBytes / (dtype == SV_BF16 ? 2 : 4);
+  return (V + e - 1) / e;
+}
+
+// Rows of one request in the grid: draft rows 0..max_k-1, then target rows
+// 0..max_k (slot max_k + j).
+__host__ __device__ inline int rows_per_request(int max_k) { return 2 * max_k + 1; }
+
+// Statistics of one segment of one row.
+//   m    largest logit of the segment (-inf if none is finite)
+//   s    sum of exp((z - m) / T) over the segment; for rows summed
+//        "exclusively" the terms with z == m are left out of s and counted
+//        in cnt instead (exact 1.0 each), which keeps sum_{v != argmax}
+//        accurate when it is tiny
+//   cnt  number of z == m terms left out of s (0 for inclusive sums)
+//   idx  lowest index with z == m (greedy rows only)
+struct Partial {
+  float m;
+  float s;
+  float cnt;
+  int idx;
+};
+
+// Byte offsets inside the caller's workspace.
+//
+// The workspace starts with a fixed arena - a 256-byte control block, then
+// three per-request-slot arrays of SV_MAX_B words - which every call leaves
+// zeroed and no call writes partial data into, whatever its shape.  After the
+// arena comes the per-call region, laid out for the call's (B, V, max_k).
+constexpr size_t kCtrlBytes = 256;
+constexpr int kCtrlWork = 0;    // work-item claim counter
+constexpr int kCtrlExit = 32;   // workgroups that finished (separate cache line)
+constexpr int kCtrlError = 48;  // set if a bounded wait ever expired
+constexpr size_t kArenaBytes = kCtrlBytes + 3 * size_t(SV_MAX_B) * 4;
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// How a request's emitted token is drawn, decided by its statistics phase.
+enum DrawMode { kUnresolved = 0, kNoDraw = 1, kResidual = 2, kBonus = 3 };
+
+// Decision of one request, read by its sampling items.
+struct Record {
+  int a;      // accept length
+  int mode;   // DrawMode
+  float kt;   // log2 normaliser of the target row: log2 pt(v) = z*c - kt
+  float kd;   // same for the draft row (residual only)
+  float c;    // log2(e) / T
+  float u;    // uniform of the draw
+  int pad[2];
+};
+
+struct WsLayout {
+  size_t ctrl;      // uint32 [64]
+  size_t tickets;   // uint32 [SV_MAX_B]  statistics arrivals per request
+  size_t tickets2;  // uint32 [SV_MAX_B]  sampling arrivals per request
+  size_t flags;     // int [SV_MAX_B]     DrawMode once decided, 0 otherwise
+  size_t partials;  // Partial [B][R][nseg]
+  size_t zval;      // float [B][R]       logit at the draft token, per row
+  size_t records;   // Record [B]
+  size_t segsum;    // float [B][nseg2]   weight of each sampling segment
+  size_t total;
+  int nseg;   // statistics segments per row
+  int nseg2;  // sampling segments per row
+  int R;
+};
+
+inline WsLayout ws_layout(int B, int V, int max_k, int dtype) {
+  WsLayout L;
+  L.nseg = num_segments(V, dtype);
+  L.nseg2 = num_sample_segments(V, dtype);
+  L.R = rows_per_request(max_k);
+  L.ctrl = 0;
+  L.tickets = kCtrlBytes;
+  L.tickets2 = L.tickets + size_t(SV_MAX_B) * 4;
+  L.flags = L.tickets2 + size_t(SV_MAX_B) * 4;
+  L.partials = kArenaBytes;
+  L.zval = L.partials + align256(size_t(B) * L.R * L.nseg * sizeof(Partial));
+  L.records = L.zval + align256(size_t(B) * L.R * 4);
+  L.segsum = L.records + align256(size_t(B) * sizeof(Record));
+  L.total = L.segsum + align256(size_t(B) * L.nseg2 * 4);
+  return L;
+}
+
+struct VerifyArgs {
+  int B, V, max_k, nseg, nseg2, R;
+  const void* draft;
+  const int64_t* draft_start;
+  int64_t draft_stride;
+  const void* target;
+  const int64_t* target_start;
+  int64_t target_stride;
+  const int32_t* num_draft;
+  const int32_t* tokens;
+  const float* temperature;
+  const float* u_accept;
+  const float* u_residual;
+  const float* u_bonus;
+  int32_t* accept_len;
+  int32_t* out_tokens;
+  int8_t* labels;
+  float* p_draft;
+  float* p_target;
+  const float* av_params;
+  float* av_feature;
+  float* av_score;
+  // workspace
+  uint32_t* ctrl;
+  uint32_t* tickets;
+  uint32_t* tickets2;
+  int* flags;
+  Partial* partials;
+  float* zval;
+  Record* records;
+  float* segsum;
+  // work-item schedule (see the kernel)
+  int group;         // requests per group
+  int ngroups;
+  uint32_t total_items;
+  uint32_t spin_limit;
+};
+
+struct ScoreArgs {
+  int B, V, max_k, nseg, R;
+  const void* draft;
+  const int64_t* draft_start;
+  int64_t draft_stride;
+  const int32_t* num_draft;
+  const float* temperature;
+  const float* params;
+  float threshold;
+  float* feature;
+  float* score;
+  int32_t* num_kept;
+  uint32_t* tickets;
+  Partial* partials;
+};
+
+hipError_t launch_spec_verify(VerifyArgs a, int dtype, hipStream_t stream);
+hipError_t launch_av_score(const ScoreArgs& a, int dtype, hipStream_t stream);
+hipError_t launch_av_fit(int B, int max_k, const float* feature, const int8_t* labels,
+                         float* params, double* accum, float damping_c, float ridge,
+                         int do_update, hipStream_t stream);
+
+}  // namespace sv

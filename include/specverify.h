@@ -1,0 +1,200 @@
+/*
+ * specverify.h - C ABI of libspecverify.so: batched draft-token verification
+ * and the online acceptance estimator of speculative decoding, for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Pages this interface follows:
+ *   [CS] "Speculative Decoding: Draft, EAGLE, MTP" (cheat sheet, nextadmin.net):
+ *        sections "One speculative step", "Algorithm loop in code",
+ *        "Functions in the lessons" (spec_step, residual).
+ *   [AV] "Adaptive Verification ohne Confidence Head" (spke.com, German; Arabic
+ *        mirror "التحقق التكيفي بدون رأس ثقة"): sections "Solution",
+ *        "Scoring the distribution", "Fitting the coefficients".
+ *
+ * Letters: "draft" is the cheap model's distribution pd, "target" the
+ * verifier's pt.  Both are softmax(logits / T) of a logit row.
+ *
+ * Conventions shared by every entry point:
+ *   - Every array argument is device memory owned by the caller; the library
+ *     never allocates, frees or keeps a pointer after the call returns.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *     on it and the call returns without synchronising the host.  Outputs are
+ *     valid once the stream reaches that point.
+ *   - Host-side argument checks run before anything is enqueued; a negative
+ *     status means nothing was launched.  SV_ERR_HIP reports a launch error
+ *     from the HIP runtime.  Conditions that only the device data can show
+ *     (listed per call as "device preconditions") are not checked: checking
+ *     them would cost bandwidth; violating them gives unspecified outputs
+ *     (never an out-of-bounds access for token ids < 0 or >= V).
+ *   - Outputs are a deterministic function of the inputs: the same inputs at
+ *     the same addresses give bit-identical outputs.
+ *   - Row addressing: request b's draft row i (0 <= i < K_b) starts at element
+ *     (draft_row_start[b] + i) * draft_row_stride of draft_logits, and its
+ *     target row j (0 <= j <= K_b) at (target_row_start[b] + j) *
+ *     target_row_stride of target_logits.  This covers padded [B, max_k, V]
+ *     batches, packed ragged batches, and stride-0 broadcasts (all starts 0).
+ *     Rows whose start is 16-byte aligned are read with 16-byte vector loads.
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Largest draft length per request, vocabulary, and requests per call. */
+#define SV_MAX_K 16
+#define SV_MAX_V (1 << 21)
+#define SV_MAX_B (1 << 18)
+
+typedef enum {
+  SV_OK = 0,
+  SV_ERR_INVALID_ARG = -1, /* null required pointer, negative size, stride < V, ... */
+  SV_ERR_UNSUPPORTED = -2, /* size beyond SV_MAX_K / SV_MAX_V / SV_MAX_B / grid  */
+  SV_ERR_WORKSPACE = -3,   /* workspace null or smaller than the size query       */
+  SV_ERR_HIP = -4          /* the HIP runtime reported an error at launch          */
+} sv_status;
+
+/* Element type of the logit rows. */
+typedef enum {
+  SV_F32 = 0,  /* IEEE binary32                                      */
+  SV_BF16 = 1  /* bfloat16 (upper 16 bits of binary32), stored as u16 */
+} sv_dtype;
+
+/* Bytes of workspace needed by sv_spec_verify and by sv_av_score for a batch
+ * of B requests, vocabulary V, at most max_k drafts each, elements of type
+ * `dtype`.  Returns 0 for arguments those calls would reject.
+ *
+ * The workspace starts with a fixed arena of SV_MAX_B arrival counters (one
+ * per request slot), followed by per-row partial statistics.  Zero-fill the
+ * workspace once after allocation; every call leaves the counters at zero
+ * again, and no call writes anything else into the arena, so one workspace
+ * (of the largest size needed) serves any sequence of calls of any shapes on
+ * one stream without further clearing.  Calls that can run concurrently
+ * (different streams) need different workspaces.  If a call is aborted part
+ * way (device fault), zero-fill the workspace again. */
+size_t sv_workspace_size(int B, int V, int max_k, int dtype);
+
+/* Batched speculative verification, one step for B requests.
+ *
+ * [CS] "One speculative step" / "Algorithm loop in code", per request b with
+ * K_b = num_draft[b] drafts d_i = draft_tokens[b*max_k + i] and temperature
+ * T = temperature[b]:
+ *   1. pd_i = softmax(draft row i / T), pt_j = softmax(target row j / T)
+ *      (row maximum subtracted: numerically safe).
+ *   2. Walk i = 0..K_b-1: accept d_i iff u_accept[b*max_k+i] < min(1,
+ *      pt_i(d_i) / pd_i(d_i)), the ratio being +inf when pd_i(d_i) = 0.
+ *   3. a_b = the first rejected position (K_b if none): accept_len[b].
+ *   4. If a_b < K_b: emit the token drawn from the normalised residual
+ *      (pt_a - pd_a)+ (page [CS] function `residual`); if that residual has
+ *      no mass (only reachable through rounding) pt_a itself is used.
+ *      If a_b = K_b: emit the bonus token drawn from pt_{K_b}.
+ *      "Drawn with u" means the inverse CDF in ascending token order: the
+ *      first token v whose running sum of weights exceeds u times the total,
+ *      with u = u_residual[b] or u_bonus[b] respectively.
+ *   T = 0 (greedy): d_i is accepted iff it equals the lowest-index argmax of
+ *   target row i; the emitted correction or bonus is that argmax.  Greedy
+ *   requests do not read their draft rows unless av_feature is requested.
+ *
+ * Inputs (device):
+ *   draft_logits   elements of type dtype; rows as described above.  May be
+ *                  NULL when max_k == 0.
+ *   draft_row_start / target_row_start   int64 [B], in rows.
+ *   draft_row_stride / target_row_stride   elements between consecutive
+ *                  rows, >= V.
+ *   num_draft      int32 [B]   K_b.
+ *   draft_tokens   int32 [B*max_k]   (entries at i >= K_b are ignored).
+ *   temperature    float [B]   T_b >= 0.
+ *   u_accept       float [B*max_k] in [0, 1).
+ *   u_residual, u_bonus   float [B] in [0, 1).
+ * Outputs (device, written for every request):
+ *   accept_len     int32 [B]            a_b.
+ *   out_tokens     int32 [B*(max_k+1)]  d_0..d_{a-1}, then the residual or
+ *                  bonus token, then -1 up to max_k.
+ *   labels         int8 [B*max_k]  nullable: 1 before the first rejection,
+ *                  0 at it, -1 after it and past K_b ([AV] "Fitting the
+ *                  coefficients": only drafts up to the first rejection are
+ *                  labelled).
+ *   p_draft_at_token, p_target_at_token   float [B*max_k]  nullable:
+ *                  pd_i(d_i), pt_i(d_i); NaN past K_b.  For greedy requests
+ *                  p_target is 1 if d_i is the target argmax else 0, and
+ *                  p_draft is NaN.
+ *   av_feature     float [B*max_k]  nullable: the estimator feature
+ *                  logit(max_v pd_i(v)) (see sv_av_score), produced from the
+ *                  same pass over the draft rows; NaN past K_b.
+ *   av_score       float [B*max_k]  nullable, needs av_feature and av_params:
+ *                  sigmoid(omega * feature + beta_i).
+ *   av_params      float [max_k+1]  nullable: omega, beta_0..beta_{max_k-1}.
+ * Device preconditions: 0 <= K_b <= max_k; token ids in [0, V); every row
+ * read has at least one finite logit and no NaN or +inf (-inf is allowed and
+ * means probability 0); u in [0, 1).
+ * Returns SV_OK, or a negative sv_status without launching anything. */
+int sv_spec_verify(void* stream, int B, int V, int max_k, int dtype,
+                   const void* draft_logits, const int64_t* draft_row_start,
+                   int64_t draft_row_stride,
+                   const void* target_logits, const int64_t* target_row_start,
+                   int64_t target_row_stride,
+                   const int32_t* num_draft, const int32_t* draft_tokens,
+                   const float* temperature, const float* u_accept,
+                   const float* u_residual, const float* u_bonus,
+                   int32_t* accept_len, int32_t* out_tokens, int8_t* labels,
+                   float* p_draft_at_token, float* p_target_at_token,
+                   const float* av_params, float* av_feature, float* av_score,
+                   void* workspace, size_t workspace_bytes);
+
+/* Acceptance-estimator scoring of the draft rows, before verification.
+ *
+ * [AV] "Solution" / "Scoring the distribution": per draft row i of request b
+ *   feature[b*max_k+i] = logit(q_max), q_max the largest probability of
+ *       softmax(row / T) (T = 0 is scored at T = 1), computed as
+ *       -log(sum over v != argmax of exp((z_v - z_max) / T)), which equals
+ *       logit(q_max) exactly and counts tied maxima; clamped to <= 80;
+ *   score[b*max_k+i] = sigmoid(omega * feature + beta_i), params = [omega,
+ *       beta_0, ..., beta_{max_k-1}] (one shared slope, one intercept per
+ *       position: max_k + 1 parameters);
+ *   num_kept[b] (nullable) = the number of leading positions whose survival,
+ *       the running product of the scores ([AV] "Other features
+ *       considered"), is >= prune_threshold; K_b when prune_threshold <= 0.
+ *       It can be passed as num_draft of a following sv_spec_verify call.
+ * Entries past K_b are NaN.  Uses the same workspace as sv_spec_verify.
+ * Device preconditions: as for sv_spec_verify's draft rows. */
+int sv_av_score(void* stream, int B, int V, int max_k, int dtype,
+                const void* draft_logits, const int64_t* draft_row_start,
+                int64_t draft_row_stride, const int32_t* num_draft,
+                const float* temperature, const float* params,
+                float prune_threshold, float* feature, float* score,
+                int32_t* num_kept, void* workspace, size_t workspace_bytes);
+
+/* One step of the estimator's online refit ([AV] "Fitting the coefficients").
+ *
+ * Over the labelled drafts of the batch (labels 0 or 1; -1 is skipped), at
+ * the parameters `params` held fixed for the round, with
+ * pi = sigmoid(omega*x + beta_i), w = pi(1-pi), r = pi - y, it adds to
+ * accum[i*6 + k], k = 0..5, the sums  n_i, sum w, sum w*x, sum w*x^2,
+ * sum r, sum r*x  (fp64).  These are the entries of the gradient g and the
+ * Hessian H of the summed negative log-likelihood: H is an arrowhead
+ * (slope row/column plus a diagonal over the intercepts).
+ * If do_update != 0 (last step of the round) it then solves H * delta = -g
+ * over the slope and the intercepts of positions with labels (ridge added to
+ * H's diagonal), scales the slope's step by N/(N + damping_c) (N = all
+ * labels) and each intercept's by n_i/(n_i + damping_c), adds delta to
+ * params (fp32, in place) and zero-fills accum.
+ *   feature  float [B*max_k], labels int8 [B*max_k] (e.g. from sv_spec_verify).
+ *   params   float [max_k+1] in/out.   accum double [6*max_k] in/out,
+ *            zero-filled by the caller before a round's first step.
+ * A round with no labels leaves params unchanged. */
+int sv_av_fit_step(void* stream, int B, int max_k, const float* feature,
+                   const int8_t* labels, float* params, double* accum,
+                   float damping_c, float ridge, int do_update);
+
+/* Static description of a status code. */
+const char* sv_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECVERIFY_H */

@@ -233,7 +233,8 @@ def _gumbel_argmax(g, rows_f32: np.ndarray, T: float) -> np.ndarray:
 
 
 def _one_request(args):
-    wl, seed_seq, b, max_k = args
+    name, seed_seq, b, max_k = args
+    wl = WORKLOADS[name]
     g = np.random.Generator(np.random.PCG64(seed_seq))
     k = int(g.integers(1, max_k + 1)) if wl.ragged else max_k
     d32, t32 = wl.recipe(g, k, wl.V)
@@ -261,7 +262,7 @@ def make_batch(name: str, trial: int = 0, B: Optional[int] = None, workers: Opti
     B = wl.B if B is None else int(B)
     seed = 1000 * wl.index + trial
     children = np.random.SeedSequence(seed).spawn(B)
-    jobs = [(wl, children[b], b, wl.max_k) for b in range(B)]
+    jobs = [(name, children[b], b, wl.max_k) for b in range(B)]
     big = B * (2 * wl.max_k + 1) * wl.V > 50_000_000
     if workers is None:
         workers = min(8, len(os.sched_getaffinity(0))) if big else 1

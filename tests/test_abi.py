@@ -1,0 +1,152 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/specverify.h declares, sizes workspaces, and rejects bad arguments on
+the host before anything is launched.  No call here reaches the HIP runtime."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import draft_token_verification_spec_amd as sv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "specverify.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(sv.lib_path()), reason="libspecverify.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:size_t|int|const char\s*\*)\s*(sv_\w+)\s*\(", text, re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert set(names) == {"sv_workspace_size", "sv_spec_verify", "sv_av_score", "sv_av_fit_step",
+                          "sv_status_string"}
+    lib = ctypes.CDLL(sv.lib_path())
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) <= set(sv.__all__)
+
+
+def test_header_constants_match_binding():
+    text = open(HEADER).read()
+    assert int(re.search(r"#define SV_MAX_K (\d+)", text).group(1)) == sv.SV_MAX_K
+    assert re.search(r"#define SV_MAX_V \(1 << (\d+)\)", text).group(1) == str(sv.SV_MAX_V.bit_length() - 1)
+    assert re.search(r"#define SV_MAX_B \(1 << (\d+)\)", text).group(1) == str(sv.SV_MAX_B.bit_length() - 1)
+
+
+def test_status_strings():
+    assert sv.sv_status_string(0) == "ok"
+    assert "argument" in sv.sv_status_string(-1)
+    assert "unsupported" in sv.sv_status_string(-2)
+    assert "workspace" in sv.sv_status_string(-3)
+    assert "HIP" in sv.sv_status_string(-4)
+    assert sv.sv_status_string(12345) == "unknown status"
+
+
+def test_workspace_size():
+    small = sv.sv_workspace_size(4, 1024, 4, sv.SV_F32)
+    assert small > 0 and small % 256 == 0
+    big = sv.sv_workspace_size(256, 128256, 4, sv.SV_BF16)
+    assert big > small
+    assert sv.sv_workspace_size(-1, 1024, 4, 0) == 0
+    assert sv.sv_workspace_size(4, 0, 4, 0) == 0
+    assert sv.sv_workspace_size(4, 1024, sv.SV_MAX_K + 1, 0) == 0
+    assert sv.sv_workspace_size(4, sv.SV_MAX_V + 1, 4, 0) == 0
+    assert sv.sv_workspace_size(4, 1024, 4, 9) == 0
+    assert sv.sv_workspace_size(sv.SV_MAX_B + 1, 8, 1, 0) == 0
+    assert sv.sv_workspace_size(sv.SV_MAX_B, 8, 1, 0) > 0
+
+
+FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: every call below fails host checks first
+
+
+def verify_call(**kw):
+    args = dict(stream=None, B=4, V=1024, max_k=4, dtype=0, draft=FAKE, dstart=FAKE, dstride=1024, target=FAKE,
+                tstart=FAKE, tstride=1024, num_draft=FAKE, tokens=FAKE, temp=FAKE, u_acc=FAKE, u_res=FAKE,
+                u_bon=FAKE, accept_len=FAKE, out_tokens=FAKE, labels=None, p_d=None, p_t=None, params=None,
+                feat=None, score=None, ws=FAKE, ws_bytes=1 << 30)
+    args.update(kw)
+    lib = sv._load()
+    return lib.sv_spec_verify(*args.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), -1),
+    (dict(V=0), -1),
+    (dict(max_k=-1), -1),
+    (dict(max_k=17), -2),
+    (dict(V=sv.SV_MAX_V + 1, dstride=sv.SV_MAX_V + 1, tstride=sv.SV_MAX_V + 1), -2),
+    (dict(dtype=5), -1),
+    (dict(B=(1 << 18) + 1), -2),
+    (dict(target=None), -1),
+    (dict(tstart=None), -1),
+    (dict(num_draft=None), -1),
+    (dict(temp=None), -1),
+    (dict(u_res=None), -1),
+    (dict(u_bon=None), -1),
+    (dict(accept_len=None), -1),
+    (dict(out_tokens=None), -1),
+    (dict(draft=None), -1),
+    (dict(tokens=None), -1),
+    (dict(u_acc=None), -1),
+    (dict(tstride=1023), -1),
+    (dict(dstride=100), -1),
+    (dict(score=FAKE), -1),  # score needs feature and params
+    (dict(score=FAKE, feat=FAKE), -1),
+    (dict(ws=None), -3),
+    (dict(ws_bytes=100), -3),
+])
+def test_spec_verify_rejects_before_launch(kw, status):
+    assert verify_call(**kw) == status
+
+
+def test_spec_verify_empty_batch_is_a_noop():
+    assert verify_call(B=0, ws=None, ws_bytes=0, target=None) in (-1, 0)
+    assert verify_call(B=0) == 0
+
+
+def test_av_score_rejects_before_launch():
+    lib = sv._load()
+    base = [None, 4, 1024, 4, 0, FAKE, FAKE, 1024, FAKE, FAKE, FAKE, ctypes.c_float(0.3), FAKE, FAKE, FAKE, FAKE,
+            1 << 30]
+    def call(i, v):
+        a = list(base)
+        a[i] = v
+        return lib.sv_av_score(*a)
+    assert call(1, -1) == -1
+    assert call(3, 17) == -2
+    assert call(5, None) == -1   # draft logits
+    assert call(7, 10) == -1     # stride < V
+    assert call(10, None) == -1  # params
+    assert call(12, None) == -1  # feature
+    assert call(15, None) == -3  # workspace
+    assert call(16, 8) == -3
+    assert call(1, 0) == 0       # empty batch
+
+
+def test_av_fit_rejects_before_launch():
+    lib = sv._load()
+    f = ctypes.c_float
+    assert lib.sv_av_fit_step(None, -1, 4, FAKE, FAKE, FAKE, FAKE, f(10), f(1e-6), 0) == -1
+    assert lib.sv_av_fit_step(None, 4, 17, FAKE, FAKE, FAKE, FAKE, f(10), f(1e-6), 0) == -2
+    assert lib.sv_av_fit_step(None, 4, 4, None, FAKE, FAKE, FAKE, f(10), f(1e-6), 0) == -1
+    assert lib.sv_av_fit_step(None, 4, 4, FAKE, FAKE, None, FAKE, f(10), f(1e-6), 0) == -1
+    assert lib.sv_av_fit_step(None, 4, 4, FAKE, FAKE, FAKE, None, f(10), f(1e-6), 0) == -1
+    assert lib.sv_av_fit_step(None, 4, 4, FAKE, FAKE, FAKE, FAKE, f(-1), f(1e-6), 0) == -1
+    assert lib.sv_av_fit_step(None, 4, 4, FAKE, FAKE, FAKE, FAKE, f(10), f(float("nan")), 0) == -1
+    assert lib.sv_av_fit_step(None, 4, 0, None, None, None, None, f(10), f(1e-6), 0) == 0
+
+
+def test_binding_refuses_host_tensors():
+    """No CPU fallback: host tensors are rejected before any library call."""
+    x = torch.zeros(2, 16)
+    z = torch.zeros(1, dtype=torch.int64)
+    with pytest.raises(ValueError):
+        sv.sv_spec_verify(x, z, x, z, torch.zeros(1, dtype=torch.int32), torch.zeros(1, 1, dtype=torch.int32),
+                          torch.ones(1), torch.zeros(1, 1), torch.zeros(1), torch.zeros(1), max_k=1)
+    with pytest.raises(ValueError):
+        sv.sv_av_score(x, z, torch.zeros(1, dtype=torch.int32), torch.ones(1), torch.zeros(2), max_k=1)
