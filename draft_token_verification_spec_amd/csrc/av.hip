@@ -54,7 +54,7 @@ __global__ __launch_bounds__(kThreads) void av_score_kernel(ScoreArgs a) {
   const Partial p = segment_stats<ET, kSumExclusive>(row, s * SEG, a.V, is_aligned16(row), c, lds_part);
   if (tid == 0) publish(&a.partials[(size_t(b) * a.R + i) * a.nseg + s], p);
 
-  if (!arrive_last(&a.tickets[b], uint32_t(a.nseg) * uint32_t(K), &lds_flag)) return;
+  if (!arrive_last(&a.tickets[req_slot(b)], uint32_t(a.nseg) * uint32_t(K), &lds_flag)) return;
 
   if (tid < max_k) {
     float x = NAN, score = NAN;
@@ -84,7 +84,7 @@ __global__ __launch_bounds__(kThreads) void av_score_kernel(ScoreArgs a) {
       }
       a.num_kept[b] = kept;
     }
-    store_dev(&a.tickets[b], 0u);
+    store_dev(&a.tickets[req_slot(b)], 0u);
   }
 }
 

@@ -143,27 +143,44 @@ __device__ __forceinline__ float wave_inclusive_scan(float v, int lane) {
 
 enum SegMode { kSumInclusive = 0, kSumExclusive = 1, kArgmax = 2 };
 
-template <typename ET, int MODE>
-__device__ __forceinline__ Partial segment_stats(const ET* row, int seg_base, int V, bool aligned, float c,
-                                                 Partial* lds /* kWaves entries */) {
+// Issue the loads of one segment: thread t takes vectors t, t + kThreads, ...
+// of the segment.  Returns true when the fast path (kVecsPerThread plain
+// 16-byte loads, nothing else) was taken.
+template <typename ET>
+__device__ __forceinline__ bool load_segment(const ET* row, int seg_base, int V, bool aligned,
+                                             uint4 (&x)[kVecsPerThread]) {
   constexpr int N = Elem<ET>::N;
   const int tid = threadIdx.x;
-  uint4 x[kVecsPerThread];
   if (aligned && seg_base + kThreads * kVecsPerThread * N <= V) {
-    // whole segment inside the row: every load is issued back to back
 #pragma unroll
     for (int k = 0; k < kVecsPerThread; ++k) x[k] = load_vec16<ET>(row + seg_base + (k * kThreads + tid) * N);
-  } else {
-#pragma unroll
-    for (int k = 0; k < kVecsPerThread; ++k)
-      x[k] = load_raw<ET>(row, seg_base + (k * kThreads + tid) * N, V, aligned);
+    return true;
   }
+#pragma unroll
+  for (int k = 0; k < kVecsPerThread; ++k) x[k] = load_raw<ET>(row, seg_base + (k * kThreads + tid) * N, V, aligned);
+  return false;
+}
 
+// Reduce a loaded segment to its Partial (valid in thread 0).
+// Opaque to the optimiser: the raw vectors are decoded again after it instead
+// of keeping every decoded value alive between the two passes (for bf16 that
+// would double the registers held per thread).
+__device__ __forceinline__ void keep_raw(uint4& w) { asm volatile("" : "+v"(w.x), "+v"(w.y), "+v"(w.z), "+v"(w.w)); }
+
+template <typename ET, int MODE>
+__device__ __forceinline__ Partial stats_from_regs(uint4 (&x)[kVecsPerThread], int seg_base, float c,
+                                                   Partial* lds /* kWaves entries */) {
+  constexpr int N = Elem<ET>::N;
+  const int tid = threadIdx.x;
   float m = -INFINITY;
 #pragma unroll
   for (int k = 0; k < kVecsPerThread; ++k)
 #pragma unroll
     for (int j = 0; j < N; ++j) m = fmaxf(m, Elem<ET>::get(x[k], j));
+  if (N == 8) {
+#pragma unroll
+    for (int k = 0; k < kVecsPerThread; ++k) keep_raw(x[k]);
+  }
 
   float s = 0.f, cnt = 0.f;
   int idx = 0x7fffffff;
@@ -217,6 +234,15 @@ __device__ __forceinline__ Partial segment_stats(const ET* row, int seg_base, in
     }
   }
   return p;
+}
+
+// Load and reduce one segment (used where no prefetch is needed).
+template <typename ET, int MODE>
+__device__ __forceinline__ Partial segment_stats(const ET* row, int seg_base, int V, bool aligned, float c,
+                                                 Partial* lds) {
+  uint4 x[kVecsPerThread];
+  load_segment<ET>(row, seg_base, V, aligned, x);
+  return stats_from_regs<ET, MODE>(x, seg_base, c, lds);
 }
 
 // ---------------------------------------------------------------------------

@@ -57,11 +57,22 @@ struct Partial {
 // three per-request-slot arrays of SV_MAX_B words - which every call leaves
 // zeroed and no call writes partial data into, whatever its shape.  After the
 // arena comes the per-call region, laid out for the call's (B, V, max_k).
-constexpr size_t kCtrlBytes = 256;
-constexpr int kCtrlWork = 0;    // work-item claim counter
-constexpr int kCtrlExit = 32;   // workgroups that finished (separate cache line)
-constexpr int kCtrlError = 48;  // set if a bounded wait ever expired
+constexpr int kParts = 16;        // independent work schedules (claim counters)
+constexpr int kLineWords = 32;    // 128 bytes: one counter per cache line
+constexpr size_t kCtrlBytes = size_t(kParts + 2) * kLineWords * 4;
+constexpr int kCtrlWork = 0;                         // claim counter of partition p: kCtrlWork + p * kLineWords
+constexpr int kCtrlExit = kParts * kLineWords;       // workgroups that finished
+constexpr int kCtrlError = (kParts + 1) * kLineWords;  // set if a bounded wait ever expired
 constexpr size_t kArenaBytes = kCtrlBytes + 3 * size_t(SV_MAX_B) * 4;
+
+// Slot of request b in the per-request arrays of the arena: consecutive
+// requests land 128 bytes apart (for b < SV_MAX_B / 32), so the atomics of
+// different requests do not contend for one cache line.  A bijection on
+// [0, SV_MAX_B).
+__host__ __device__ constexpr int req_slot(int b) {
+  return ((b & (SV_MAX_B / kLineWords - 1)) * kLineWords) | (b / (SV_MAX_B / kLineWords));
+}
+static_assert(SV_MAX_B % kLineWords == 0, "arena slots");
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -80,7 +91,7 @@ struct Record {
 };
 
 struct WsLayout {
-  size_t ctrl;      // uint32 [64]
+  size_t ctrl;      // uint32 control block (claim/exit counters, error flag)
   size_t tickets;   // uint32 [SV_MAX_B]  statistics arrivals per request
   size_t tickets2;  // uint32 [SV_MAX_B]  sampling arrivals per request
   size_t flags;     // int [SV_MAX_B]     DrawMode once decided, 0 otherwise
@@ -143,9 +154,8 @@ struct VerifyArgs {
   Record* records;
   float* segsum;
   // work-item schedule (see the kernel)
-  int group;         // requests per group
-  int ngroups;
-  uint32_t total_items;
+  int parts;         // independent schedules; partition p owns requests b = p (mod parts)
+  int group;         // requests per group within a partition
   uint32_t spin_limit;
 };
 

@@ -19,13 +19,18 @@
 //     locates the segment where the running weight crosses u * total and
 //     searches it for the token.
 //
-// Items are claimed in this order: the statistics items of request group 0,
-// of group 1, the sampling items of group 0, statistics of group 2, sampling
-// of group 1, ...  A sampling item waits (bounded) until its request has been
-// decided.  Every item it waits for has a smaller claim number, and every
-// claimed item belongs to a running workgroup that is either processing it or
-// processing an earlier item, so the smallest unfinished item can always
-// proceed: no deadlock.  Because the workgroups persist, a long item never
+// Requests are split into 16 partitions (b mod 16), each an independent
+// schedule with its own claim counter on its own cache line: same-address
+// device atomics serialise (~12 ns each), so one counter for every item would
+// cap the item rate.  Within a partition, items are claimed in this order:
+// the statistics items of request group 0, of group 1, the sampling items of
+// group 0, statistics of group 2, sampling of group 1, ...  A sampling item
+// waits (bounded) until its request has been decided.  Every item it waits
+// for has a smaller claim number in the same partition, and every claimed
+// item belongs to a running workgroup that is either processing it or an
+// earlier item of the same partition (a workgroup claims one item ahead, and
+// only within its current partition), so the smallest unfinished item of a
+// partition can always proceed: no deadlock.  Because the workgroups persist, a long item never
 // stalls the hardware dispatch of others, and the draw of each request is
 // spread over many workgroups.  No host synchronisation; all counters are
 // reset by the kernel itself.
@@ -148,8 +153,8 @@ __device__ __forceinline__ void finish_request(const VerifyArgs& a, Shared<ET>& 
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_waitcnt(0);
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    store_dev(&a.flags[b], mode);
-    store_dev(&a.tickets[b], 0u);
+    store_dev(&a.flags[req_slot(b)], mode);
+    store_dev(&a.tickets[req_slot(b)], 0u);
   }
 }
 
@@ -192,7 +197,7 @@ __device__ __forceinline__ void stats_item(const VerifyArgs& a, Shared<ET>& sh, 
       if (d >= base && d < base + SEG && d < a.V) store_dev(&a.zval[size_t(b) * a.R + r], Elem<ET>::one(row + d));
     }
   }
-  if (arrive_last(&a.tickets[b], want, &sh.flag)) finish_request<ET>(a, sh, b, K, nd, greedy, want_feat, c);
+  if (arrive_last(&a.tickets[req_slot(b)], want, &sh.flag)) finish_request<ET>(a, sh, b, K, nd, greedy, want_feat, c);
 }
 
 // ---------------------------------------------------------------------------
@@ -204,10 +209,10 @@ __device__ __forceinline__ void sample_item(const VerifyArgs& a, Shared<ET>& sh,
   const int tid = threadIdx.x;
   // wait until request b has been decided
   if (tid == 0) {
-    int mode = load_dev(&a.flags[b]);
+    int mode = load_dev(&a.flags[req_slot(b)]);
     for (uint32_t n = 0; mode == kUnresolved && n < a.spin_limit; ++n) {
       __builtin_amdgcn_s_sleep(kSleep);
-      mode = load_dev(&a.flags[b]);
+      mode = load_dev(&a.flags[req_slot(b)]);
     }
     if (mode == kUnresolved) store_dev(&a.ctrl[kCtrlError], 1u);
     sh.flag = mode;
@@ -236,7 +241,7 @@ __device__ __forceinline__ void sample_item(const VerifyArgs& a, Shared<ET>& sh,
                         : segment_weight<ET, false>(rt, rt, fast, s, a.V, rec.c, rec.kt, rec.c, rec.kt, sh.g);
     if (tid == 0) store_dev(&a.segsum[size_t(b) * a.nseg2 + s], W);
   }
-  if (!arrive_last(&a.tickets2[b], uint32_t(a.nseg2), &sh.flag)) return;
+  if (!arrive_last(&a.tickets2[req_slot(b)], uint32_t(a.nseg2), &sh.flag)) return;
 
   // ---- the last sampling item of request b draws the token ----
   if (mode != kNoDraw) {
@@ -290,8 +295,8 @@ __device__ __forceinline__ void sample_item(const VerifyArgs& a, Shared<ET>& sh,
     if (tid == 0) a.out_tokens[size_t(b) * (a.max_k + 1) + rec.a] = tok;
   }
   if (tid == 0) {
-    store_dev(&a.flags[b], 0);
-    store_dev(&a.tickets2[b], 0u);
+    store_dev(&a.flags[req_slot(b)], 0);
+    store_dev(&a.tickets2[req_slot(b)], 0u);
   }
 }
 
@@ -299,57 +304,89 @@ __device__ __forceinline__ void sample_item(const VerifyArgs& a, Shared<ET>& sh,
 // persistent kernel
 // ---------------------------------------------------------------------------
 
+// Schedule of one partition: partition p owns requests b = p + j * parts
+// (j = 0 .. nreq-1), taken in groups of `group` requests.  Claim numbers run
+// over: statistics items of group 0, of group 1, sampling items of group 0,
+// statistics of group 2, sampling of group 1, ..., sampling of the last group.
+struct Schedule {
+  uint32_t A;      // statistics items per group
+  uint32_t C;      // sampling items per group
+  uint32_t ngroups;
+  uint32_t total;  // claim numbers of the partition
+  int nreq;
+};
+
+__device__ __forceinline__ Schedule schedule(const VerifyArgs& a, int p) {
+  Schedule S;
+  S.nreq = (a.B - p + a.parts - 1) / a.parts;
+  S.A = uint32_t(a.group) * uint32_t(a.R) * uint32_t(a.nseg);
+  S.C = uint32_t(a.group) * uint32_t(a.nseg2);
+  S.ngroups = (uint32_t(S.nreq) + a.group - 1) / a.group;
+  S.total = S.ngroups * (S.A + S.C);
+  return S;
+}
+
 template <typename ET>
-__global__ __launch_bounds__(kThreads) void spec_verify_kernel(VerifyArgs a) {
+__device__ __forceinline__ void run_item(const VerifyArgs& a, Shared<ET>& sh, const Schedule& S, int p, uint32_t id) {
+  bool stats;
+  uint32_t group, local;
+  if (id < S.A) {
+    stats = true;
+    group = 0;
+    local = id;
+  } else {
+    const uint32_t q = id - S.A, blk = q / (S.A + S.C), off = q % (S.A + S.C);
+    if (blk + 1 < S.ngroups) {
+      stats = off < S.A;
+      group = stats ? blk + 1 : blk;
+      local = stats ? off : off - S.A;
+    } else {
+      stats = false;
+      group = blk;
+      local = off;
+    }
+  }
+  const uint32_t per = stats ? uint32_t(a.R) * uint32_t(a.nseg) : uint32_t(a.nseg2);
+  const int j = int(group * uint32_t(a.group) + local / per);  // request index within the partition
+  if (j >= S.nreq) return;
+  const int b = p + j * a.parts;
+  const uint32_t rem = local % per;
+  if (stats)
+    stats_item<ET>(a, sh, b, int(rem / a.nseg), int(rem % a.nseg));
+  else
+    sample_item<ET>(a, sh, b, int(rem));
+}
+
+template <typename ET>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void spec_verify_kernel(VerifyArgs a) {
   __shared__ Shared<ET> sh;
   const int tid = threadIdx.x;
-  const uint32_t G = uint32_t(a.group);
-  const uint32_t A = G * uint32_t(a.R) * uint32_t(a.nseg);  // statistics items per group
-  const uint32_t C = G * uint32_t(a.nseg2);                 // sampling items per group
-
-  if (tid == 0) sh.next = claim(&a.ctrl[kCtrlWork]);
-  __syncthreads();
-  uint32_t id = sh.next;
-  __syncthreads();
-  while (id < a.total_items) {
-    if (tid == 0) sh.next = claim(&a.ctrl[kCtrlWork]);  // look one item ahead
-    // decode the claim number
-    bool stats;
-    uint32_t group, local;
-    if (id < A) {
-      stats = true;
-      group = 0;
-      local = id;
-    } else {
-      const uint32_t q = id - A, blk = q / (A + C), off = q % (A + C);
-      if (blk + 1 < uint32_t(a.ngroups)) {
-        stats = off < A;
-        group = stats ? blk + 1 : blk;
-        local = stats ? off : off - A;
-      } else {
-        stats = false;
-        group = blk;
-        local = off;
-      }
-    }
-    if (stats) {
-      const uint32_t per = uint32_t(a.R) * uint32_t(a.nseg);
-      const int b = int(group * G + local / per);
-      const uint32_t rem = local % per;
-      if (b < a.B) stats_item<ET>(a, sh, b, int(rem / a.nseg), int(rem % a.nseg));
-    } else {
-      const int b = int(group * G + local / a.nseg2);
-      if (b < a.B) sample_item<ET>(a, sh, b, int(local % a.nseg2));
-    }
+  // Start in partition blockIdx % parts; when it is exhausted, move through
+  // the others.  The next item is claimed one ahead within a partition only,
+  // so each partition keeps its own ordering argument.
+  int p = int(blockIdx.x % uint32_t(a.parts));
+  for (int visited = 0; visited < a.parts; ++visited, p = (p + 1) % a.parts) {
+    const Schedule S = schedule(a, p);
+    uint32_t* counter = &a.ctrl[kCtrlWork + p * kLineWords];
+    if (tid == 0) sh.next = claim(counter);
     __syncthreads();
-    id = sh.next;
+    uint32_t id = sh.next;
     __syncthreads();
+    while (id < S.total) {
+      uint32_t ahead = 0;
+      if (tid == 0) ahead = claim(counter);  // result is needed only at the end of the item
+      run_item<ET>(a, sh, S, p, id);
+      if (tid == 0) sh.next = ahead;
+      __syncthreads();
+      id = sh.next;
+      __syncthreads();
+    }
   }
   // the last workgroup out resets the claim counters for the next launch
   if (tid == 0) {
     const uint32_t done = __hip_atomic_fetch_add(&a.ctrl[kCtrlExit], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (done == gridDim.x - 1) {
-      store_dev(&a.ctrl[kCtrlWork], 0u);
+      for (int q = 0; q < a.parts; ++q) store_dev(&a.ctrl[kCtrlWork + q * kLineWords], 0u);
       store_dev(&a.ctrl[kCtrlExit], 0u);
     }
   }
@@ -378,16 +415,20 @@ static int resident_grid(int dtype) {
 
 hipError_t launch_spec_verify(VerifyArgs a, int dtype, hipStream_t stream) {
   const int cap = resident_grid(dtype);
-  // groups of requests: about two statistics items per resident workgroup,
-  // so a group's sampling items rarely find their request still undecided
+  a.parts = a.B < kParts ? a.B : kParts;
+  // groups of requests: about two statistics items per resident workgroup of
+  // the partition, so a group's sampling items rarely find their request
+  // still undecided
   const int per_request = a.R * a.nseg;
-  a.group = max(1, min(a.B, (2 * cap + per_request - 1) / per_request));
-  a.ngroups = (a.B + a.group - 1) / a.group;
-  const uint64_t total = uint64_t(a.ngroups) * uint64_t(a.group) * (uint64_t(a.R) * a.nseg + uint64_t(a.nseg2));
+  const int wg_per_part = (cap + a.parts - 1) / a.parts;
+  const int nreq_max = (a.B + a.parts - 1) / a.parts;
+  a.group = max(1, min(nreq_max, (2 * wg_per_part + per_request - 1) / per_request));
+  const uint64_t ngroups = (uint64_t(nreq_max) + a.group - 1) / a.group;
+  const uint64_t total = ngroups * uint64_t(a.group) * (uint64_t(a.R) * a.nseg + uint64_t(a.nseg2));
   if (total + uint64_t(cap) >= (uint64_t(1) << 32)) return hipErrorInvalidValue;
-  a.total_items = uint32_t(total);
   a.spin_limit = 1u << 20;  // ~1-2 s of polling: only reached if the schedule were broken
-  const unsigned grid = unsigned(total < uint64_t(cap) ? total : uint64_t(cap));
+  const uint64_t all = total * uint64_t(a.parts);
+  const unsigned grid = unsigned(all < uint64_t(cap) ? all : uint64_t(cap));
   if (dtype == SV_BF16)
     hipLaunchKernelGGL(spec_verify_kernel<uint16_t>, dim3(grid), dim3(kThreads), 0, stream, a);
   else
