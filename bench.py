@@ -45,6 +45,8 @@ def parse_args():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                    help="per-launch HBM bytes measured with rocprofv3 counters (optional)")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="after timing, copy a MIB-sized device buffer 3 times (reference for HBM counters)")
     return p.parse_args()
 
 
@@ -115,11 +117,11 @@ def main():
     from synth import gen
 
     dev = torch.device("cuda:0")
-    print(f"bench: drawing {args.rotate} input sets of {args.workload}", file=sys.stderr, flush=True)
-    sets = []
-    for r in range(args.rotate):
-        b = gen.make_batch(args.workload, trial=r)
-        sets.append((b, to_device(b, dev)))
+    log = lambda msg: print(f"bench: {msg}", file=sys.stderr, flush=True)
+    log(f"drawing {args.rotate} input sets of {args.workload}")
+    batches = [gen.make_batch(args.workload, trial=r) for r in range(args.rotate)]  # before any GPU use
+    log("moving inputs to the device")
+    sets = [(b, to_device(b, dev)) for b in batches]
     b0 = sets[0][0]
     B, K, V = b0.B, b0.max_k, b0.V
     positions = int(b0.num_draft.sum())
@@ -153,9 +155,11 @@ def main():
             ev[1].record()
         sv.sv_av_fit_step(o["av_feature"], o["labels"], params, accum, do_update=True)
 
+    log("warming up")
     for w in range(args.warmup):
         step(w)
     torch.cuda.synchronize(dev)
+    log("timing")
 
     steps = args.steps
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
@@ -232,8 +236,18 @@ def main():
                      "algorithmic_bytes_per_launch": bytes_per_launch},
         "extra": {"mean_accept_len": al, "positions_per_step": positions, "wall_s": wall},
     }
+    if args.copy_calibration > 0:
+        log("copy calibration")
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize(dev)
+        res["extra"]["copy_calibration_bytes"] = n
+        del src, dst
     if not args.no_cpu_baseline:
-        print("bench: timing the CPU oracle", file=sys.stderr, flush=True)
+        log("timing the CPU oracle")
         res["cpu_baseline"] = cpu_baseline(b0, args.cpu_seconds)
     print(json.dumps(res), flush=True)
 

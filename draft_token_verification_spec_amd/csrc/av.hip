@@ -14,14 +14,15 @@
 namespace sv {
 
 // ---------------------------------------------------------------------------
-// scoring: workgroup (b, i, s) reduces segment s of draft row i with the
-// maxima kept out of the sum; the request's last workgroup turns the row
-// statistics into feature, score, survival and the kept count.
+// scoring: workgroup (b, i, s) reduces segment s of draft row i; the
+// request's last workgroup turns the row statistics into feature, score,
+// survival and the kept count.
 // ---------------------------------------------------------------------------
 
 template <typename ET>
 __global__ __launch_bounds__(kThreads) void av_score_kernel(ScoreArgs a) {
   __shared__ Partial lds_part[kWaves];
+  __shared__ Partial rows[SV_MAX_K];
   __shared__ float sc[SV_MAX_K];
   __shared__ int lds_flag;
 
@@ -51,25 +52,40 @@ __global__ __launch_bounds__(kThreads) void av_score_kernel(ScoreArgs a) {
   if (i >= K) return;
 
   const ET* row = static_cast<const ET*>(a.draft) + (a.draft_start[b] + i) * a.draft_stride;
-  const Partial p = segment_stats<ET, kSumExclusive>(row, s * SEG, a.V, is_aligned16(row), c, lds_part);
+  const Partial p = segment_stats<ET, kSumInclusive>(row, s * SEG, a.V, is_aligned16(row), c, lds_part);
   if (tid == 0) publish(&a.partials[(size_t(b) * a.R + i) * a.nseg + s], p);
 
   if (!arrive_last(&a.tickets[req_slot(b)], uint32_t(a.nseg) * uint32_t(K), &lds_flag)) return;
 
+  // row statistics (thread j < K combines row j), then the feature as in the
+  // verification kernel: S - 1 directly when S >= 1.5, else the exact sum
+  if (tid < K) rows[tid] = combine_published(&a.partials[(size_t(b) * a.R + tid) * a.nseg], a.nseg, c, false);
+  __syncthreads();
   if (tid < max_k) {
     float x = NAN, score = NAN;
-    if (tid < K) {
-      const Partial D = combine_published(&a.partials[(size_t(b) * a.R + tid) * a.nseg], a.nseg, c, false);
-      const float so = D.s + (D.cnt - 1.f);
-      x = (so > 0.f) ? fminf(-fast_log2(so) * kLn2, 80.f) : 80.f;
-      const float t = a.params[0] * x + a.params[1 + tid];
-      score = 1.f / (1.f + fast_exp2(-t * kLog2e));
+    if (tid < K && rows[tid].s >= kRecomputeBelow) {
+      x = feature_from_other(rows[tid].s - 1.f);
+      score = sigmoid_score(a.params, tid, x);
     }
     a.feature[size_t(b) * max_k + tid] = x;
     a.score[size_t(b) * max_k + tid] = score;
     sc[tid] = score;
   }
   __syncthreads();
+  for (int j = 0; j < K; ++j) {
+    if (!(rows[j].s < kRecomputeBelow)) continue;
+    const ET* rj = static_cast<const ET*>(a.draft) + (a.draft_start[b] + j) * a.draft_stride;
+    const float so = exact_other_sum<ET>(rj, &a.partials[(size_t(b) * a.R + j) * a.nseg], a.nseg, a.V, rows[j].m, c,
+                                         lds_part);
+    if (tid == 0) {
+      const float x = feature_from_other(so);
+      const float score = sigmoid_score(a.params, j, x);
+      a.feature[size_t(b) * max_k + j] = x;
+      a.score[size_t(b) * max_k + j] = score;
+      sc[j] = score;
+    }
+    __syncthreads();
+  }
   if (tid == 0) {
     if (a.num_kept) {
       int kept = K;

@@ -314,6 +314,53 @@ __device__ __forceinline__ Partial combine_published(const Partial* parts, int n
 }
 
 // ---------------------------------------------------------------------------
+// estimator feature of a draft row
+// ---------------------------------------------------------------------------
+//
+// x = logit(q_max) = -log(sum_{v != argmax} exp((z_v - z_max) / T)).  The row
+// statistics are inclusive sums S (all terms, the maximum contributing 1), and
+// S - 1 is accurate whenever S >= 1.5 (q_max <= 2/3): its relative error is at
+// most 3x that of S.  For more confident rows the sum of the other tokens is
+// rebuilt exactly: segments whose maximum is below the row maximum keep their
+// inclusive partials, and the segment(s) holding the maximum are summed again
+// with the maximum's terms counted instead of added.
+
+constexpr float kFeatureClamp = 80.f;
+constexpr float kRecomputeBelow = 1.5f;
+
+__device__ __forceinline__ float feature_from_other(float so) {
+  return (so > 0.f) ? fminf(-fast_log2(so) * kLn2, kFeatureClamp) : kFeatureClamp;
+}
+
+// sigmoid(omega * x + beta_i), params = [omega, beta_0, ...]
+__device__ __forceinline__ float sigmoid_score(const float* params, int i, float x) {
+  const float t = params[0] * x + params[1 + i];
+  return 1.f / (1.f + fast_exp2(-t * kLog2e));
+}
+
+// Exact sum of the non-maximal terms of one row (row max m); all threads
+// participate, the result is valid in thread 0.  lds: kWaves Partials.
+template <typename ET>
+__device__ __forceinline__ float exact_other_sum(const ET* row, const Partial* parts, int nseg, int V, float m,
+                                                 float c, Partial* lds) {
+  constexpr int SEG = kSegBytes / int(sizeof(ET));
+  const bool aligned = is_aligned16(row);
+  float other = 0.f, cnt = 0.f;
+  for (int s = 0; s < nseg; ++s) {
+    const Partial q = fetch(&parts[s]);
+    if (q.m == m) {
+      const Partial e = segment_stats<ET, kSumExclusive>(row, s * SEG, V, aligned, c, lds);
+      other += e.s;  // thread 0 holds the reduced value
+      cnt += e.cnt;
+      __syncthreads();
+    } else if (q.m != -INFINITY) {
+      other += q.s * fast_exp2((q.m - m) * c);
+    }
+  }
+  return other + (cnt - 1.f);
+}
+
+// ---------------------------------------------------------------------------
 // inverse-CDF sampling over a full row, by one workgroup
 // ---------------------------------------------------------------------------
 //

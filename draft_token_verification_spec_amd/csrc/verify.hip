@@ -104,16 +104,11 @@ __device__ __forceinline__ void finish_request(const VerifyArgs& a, Shared<ET>& 
       if (a.p_target) a.p_target[o] = pt;
       if (want_feat) {
         float x = NAN, sc = NAN;
-        if (lane < K) {
-          const Partial D = sh.rows[lane];
-          const float so = D.s + (D.cnt - 1.f);
-          x = (so > 0.f) ? fminf(-fast_log2(so) * kLn2, 80.f) : 80.f;
-          if (a.av_params) {
-            const float t = a.av_params[0] * x + a.av_params[1 + lane];
-            sc = 1.f / (1.f + fast_exp2(-t * kLog2e));
-          }
+        if (lane < K && sh.rows[lane].s >= kRecomputeBelow) {
+          x = feature_from_other(sh.rows[lane].s - 1.f);
+          if (a.av_params) sc = sigmoid_score(a.av_params, lane, x);
         }
-        a.av_feature[o] = x;
+        a.av_feature[o] = x;  // rows with s < kRecomputeBelow are written below
         if (a.av_score) a.av_score[o] = sc;
       }
     }
@@ -124,6 +119,22 @@ __device__ __forceinline__ void finish_request(const VerifyArgs& a, Shared<ET>& 
     }
   }
   __syncthreads();
+
+  // confident draft rows: the feature needs the exact sum of the other tokens
+  if (want_feat) {
+    for (int i = 0; i < K; ++i) {
+      if (!(sh.rows[i].s < kRecomputeBelow)) continue;
+      const ET* row = static_cast<const ET*>(a.draft) + (a.draft_start[b] + i) * a.draft_stride;
+      const float so = exact_other_sum<ET>(row, &a.partials[(size_t(b) * a.R + i) * a.nseg], a.nseg, a.V,
+                                           sh.rows[i].m, c, sh.part);
+      if (tid == 0) {
+        const float x = feature_from_other(so);
+        a.av_feature[size_t(b) * max_k + i] = x;
+        if (a.av_score) a.av_score[size_t(b) * max_k + i] = sigmoid_score(a.av_params, i, x);
+      }
+      __syncthreads();
+    }
+  }
 
   if (tid == 0) {
     const int aa = sh.a;
@@ -181,8 +192,7 @@ __device__ __forceinline__ void stats_item(const VerifyArgs& a, Shared<ET>& sh, 
 
   Partial p;
   if (is_draft) {
-    p = want_feat ? segment_stats<ET, kSumExclusive>(row, base, a.V, aligned, c, sh.part)
-                  : segment_stats<ET, kSumInclusive>(row, base, a.V, aligned, c, sh.part);
+    p = segment_stats<ET, kSumInclusive>(row, base, a.V, aligned, c, sh.part);
   } else if (greedy) {
     p = segment_stats<ET, kArgmax>(row, base, a.V, aligned, c, sh.part);
   } else {

@@ -256,7 +256,7 @@ def make_batch(name: str, trial: int = 0, B: Optional[int] = None, workers: Opti
     """Draw workload ``name`` with seed ``1000*index + trial``.
 
     ``B`` truncates the batch to its first ``B`` requests (identical to those
-    of the full batch).  ``workers`` > 1 draws requests in a process pool.
+    of the full batch).  ``workers`` > 1 draws requests in a thread pool.
     """
     wl = WORKLOADS[name]
     B = wl.B if B is None else int(B)
@@ -267,10 +267,13 @@ def make_batch(name: str, trial: int = 0, B: Optional[int] = None, workers: Opti
     if workers is None:
         workers = min(8, len(os.sched_getaffinity(0))) if big else 1
     if workers > 1:
-        import multiprocessing as mp
+        # threads, not processes: numpy's random fills and ufuncs release the
+        # GIL, and a thread pool is safe in a process that already holds a GPU
+        # context or profiler threads (no fork) and needs no __main__ guard
+        from concurrent.futures import ThreadPoolExecutor
 
-        with mp.get_context("fork").Pool(workers) as pool:
-            res = pool.map(_one_request, jobs, chunksize=max(1, B // (4 * workers)))
+        with ThreadPoolExecutor(workers) as pool:
+            res = list(pool.map(_one_request, jobs))
     else:
         res = [_one_request(j) for j in jobs]
 
