@@ -67,6 +67,20 @@ def to_device(batch, dev):
                 u_residual=t(batch.u_residual, torch.float32), u_bonus=t(batch.u_bonus, torch.float32))
 
 
+def kernel_source_hash() -> str:
+    """sha256 over the library's kernel sources, to tell whether stored
+    counter measurements still describe the current kernels."""
+    import glob
+    import hashlib
+
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "draft_token_verification_spec_amd", "csrc")
+    for f in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.hpp"))):
+        h.update(os.path.basename(f).encode())
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
 def cpu_baseline(batch, budget_s):
     """The oracle, untuned, on the first requests of input set 0 until the
     time budget is spent: verification, estimator feature/score of the
@@ -204,11 +218,13 @@ def main():
     value = positions / (ms_per_step * 1e-3)
     achieved = bytes_per_launch / (verify_ms * 1e-3) / 1e9
 
+    # HBM bytes per launch from rocprofv3 counters, valid only for the kernel
+    # sources they were measured on
     traffic = None
     if os.path.exists(args.traffic):
         try:
             tr = json.load(open(args.traffic))
-            if tr.get("workload") == args.workload:
+            if tr.get("workload") == args.workload and tr.get("kernel_source_sha256") == kernel_source_hash():
                 traffic = tr.get("bytes_per_launch")
         except (OSError, ValueError):
             traffic = None
