@@ -41,6 +41,8 @@ def parse_args():
     p.add_argument("--workload", default="bf16_b256_k4_v128256_peaked")
     p.add_argument("--rotate", type=int, default=3, help="input sets cycled between steps")
     p.add_argument("--graph", type=int, default=1, help="replay the steps from a captured HIP graph")
+    p.add_argument("--kernel", choices=["resident", "streaming", "auto"], default="auto",
+                   help="verification kernel (sv_set_verify_kernel)")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
@@ -169,7 +171,11 @@ def main():
             ev[1].record()
         sv.sv_av_fit_step(o["av_feature"], o["labels"], params, accum, do_update=True)
 
-    log("warming up")
+    kernel = args.kernel
+    sv.sv_set_verify_kernel({"resident": sv.SV_KERNEL_RESIDENT, "streaming": sv.SV_KERNEL_STREAMING,
+                             "auto": sv.SV_KERNEL_AUTO}[kernel])
+    kernel_name = "resident_kernel" if kernel == "resident" else "spec_verify_kernel"
+    log(f"warming up ({kernel_name})")
     for w in range(args.warmup):
         step(w)
     torch.cuda.synchronize(dev)
@@ -224,7 +230,8 @@ def main():
     if os.path.exists(args.traffic):
         try:
             tr = json.load(open(args.traffic))
-            if tr.get("workload") == args.workload and tr.get("kernel_source_sha256") == kernel_source_hash():
+            if (tr.get("workload") == args.workload and tr.get("kernel", "spec_verify_kernel") == kernel_name
+                    and tr.get("kernel_source_sha256") == kernel_source_hash()):
                 traffic = tr.get("bytes_per_launch")
         except (OSError, ValueError):
             traffic = None
@@ -245,10 +252,11 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "B": B, "K": K, "V": V, "logits": b0.dtype,
                    "step": "sv_spec_verify (with estimator feature+score) + sv_av_fit_step",
-                   "input_sets_rotated": len(sets), "graph_replay": bool(graph is not None)},
+                   "input_sets_rotated": len(sets), "graph_replay": bool(graph is not None),
+                   "kernel": kernel},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
-                     "kernel": "spec_verify_kernel", "kernel_ms": verify_ms,
+                     "kernel": kernel_name, "kernel_ms": verify_ms,
                      "algorithmic_bytes_per_launch": bytes_per_launch},
         "extra": {"mean_accept_len": al, "positions_per_step": positions, "wall_s": wall},
     }

@@ -29,6 +29,10 @@ __all__ = [
     "sv_spec_verify",
     "sv_av_score",
     "sv_av_fit_step",
+    "sv_set_verify_kernel",
+    "SV_KERNEL_AUTO",
+    "SV_KERNEL_STREAMING",
+    "SV_KERNEL_RESIDENT",
     "Workspace",
 ]
 
@@ -36,6 +40,7 @@ SV_MAX_K = 16
 SV_MAX_V = 1 << 21
 SV_MAX_B = 1 << 18
 SV_F32, SV_BF16 = 0, 1
+SV_KERNEL_AUTO, SV_KERNEL_STREAMING, SV_KERNEL_RESIDENT = 0, 1, 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libspecverify.so")
@@ -58,6 +63,7 @@ _SIGNATURES = {
     "sv_av_score": (_i, [_p, _i, _i, _i, _i, _p, _p, _i64, _p, _p, _p, _f, _p, _p, _p, _p, _sz]),
     "sv_av_fit_step": (_i, [_p, _i, _i, _p, _p, _p, _p, _f, _f, _i]),
     "sv_status_string": (ctypes.c_char_p, [_i]),
+    "sv_set_verify_kernel": (_i, [_i]),
 }
 
 
@@ -91,6 +97,15 @@ def _check(status: int, what: str):
 
 def sv_workspace_size(B: int, V: int, max_k: int, dtype: int) -> int:
     return int(_load().sv_workspace_size(B, V, max_k, dtype))
+
+
+def sv_set_verify_kernel(kernel: int) -> int:
+    """Select the kernel sv_spec_verify launches (process-wide); returns the
+    previous setting."""
+    prev = int(_load().sv_set_verify_kernel(int(kernel)))
+    if prev < 0:
+        _check(prev, "sv_set_verify_kernel")
+    return prev
 
 
 # ---------------------------------------------------------------------------

@@ -29,6 +29,8 @@ int check_sizes(int B, int V, int max_k, int dtype) {
 
 int to_status(hipError_t e) { return e == hipSuccess ? SV_OK : SV_ERR_HIP; }
 
+int g_verify_kernel = SV_KERNEL_AUTO;  // accessed atomically
+
 }  // namespace
 
 extern "C" {
@@ -89,10 +91,19 @@ int sv_spec_verify(void* stream, int B, int V, int max_k, int dtype, const void*
   a.tickets = reinterpret_cast<uint32_t*>(ws + L.tickets);
   a.tickets2 = reinterpret_cast<uint32_t*>(ws + L.tickets2);
   a.flags = reinterpret_cast<int*>(ws + L.flags);
+  a.reqw = reinterpret_cast<uint32_t*>(ws + L.reqw);
   a.partials = reinterpret_cast<Partial*>(ws + L.partials);
   a.zval = reinterpret_cast<float*>(ws + L.zval);
   a.records = reinterpret_cast<Record*>(ws + L.records);
   a.segsum = reinterpret_cast<float*>(ws + L.segsum);
+  a.parts = a.group = a.stride = 0;
+  a.spin_limit = 0;
+  const int kind = __atomic_load_n(&g_verify_kernel, __ATOMIC_RELAXED);
+  hipError_t err = hipSuccess;
+  if (kind == SV_KERNEL_RESIDENT) {
+    if (!launch_resident(a, dtype, static_cast<hipStream_t>(stream), &err)) return SV_ERR_UNSUPPORTED;
+    return to_status(err);
+  }
   return to_status(launch_spec_verify(a, dtype, static_cast<hipStream_t>(stream)));
 }
 
@@ -143,6 +154,12 @@ int sv_av_fit_step(void* stream, int B, int max_k, const float* feature, const i
   if (!params || !accum || (B > 0 && (!feature || !labels))) return SV_ERR_INVALID_ARG;
   return to_status(launch_av_fit(B, max_k, feature, labels, params, accum, damping_c, ridge, do_update,
                                  static_cast<hipStream_t>(stream)));
+}
+
+int sv_set_verify_kernel(int kernel) {
+  if (kernel != SV_KERNEL_AUTO && kernel != SV_KERNEL_STREAMING && kernel != SV_KERNEL_RESIDENT)
+    return SV_ERR_INVALID_ARG;
+  return __atomic_exchange_n(&g_verify_kernel, kernel, __ATOMIC_RELAXED);
 }
 
 const char* sv_status_string(int status) {

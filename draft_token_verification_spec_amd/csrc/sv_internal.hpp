@@ -21,6 +21,13 @@ constexpr int kSegBytes = kThreads * kVecsPerThread * 16;
 // kGroup blocks, a block being 64 lanes x one 16-byte vector.
 constexpr int kGroup = 8;
 constexpr int kSampleSegBytes = kWaves * kGroup * 64 * 16;
+// A 32 KiB half segment: kHalfVecs 16-byte vectors per thread.  The
+// register-resident kernel pairs the half segment s of a draft row with the
+// same half of the target row, or takes a whole 64 KiB segment of a target row
+// that has no draft row beside it.
+constexpr int kHalfVecs = kVecsPerThread / 2;
+constexpr int kHalfBytes = kThreads * kHalfVecs * 16;
+static_assert(kHalfBytes == kSampleSegBytes, "half segments are the sampling segments");
 
 __host__ __device__ constexpr int elems_per_vec(int dtype) { return dtype == SV_BF16 ? 8 : 4; }
 __host__ __device__ constexpr int seg_elems(int dtype) { return kSegBytes / (dtype == SV_BF16 ? 2 : 4); }
@@ -53,17 +60,26 @@ struct Partial {
 
 // Byte offsets inside the caller's workspace.
 //
-// The workspace starts with a fixed arena - a 256-byte control block, then
-// three per-request-slot arrays of SV_MAX_B words - which every call leaves
-// zeroed and no call writes partial data into, whatever its shape.  After the
-// arena comes the per-call region, laid out for the call's (B, V, max_k).
+// The workspace starts with a fixed arena - a control block, three
+// per-request-slot arrays of SV_MAX_B words, then SV_MAX_B per-request blocks
+// of kReqWords words - which every call leaves zeroed and no call writes
+// partial data into, whatever its shape.  After the arena comes the per-call
+// region, laid out for the call's (B, V, max_k).
 constexpr int kParts = 16;        // independent work schedules (claim counters)
 constexpr int kLineWords = 32;    // 128 bytes: one counter per cache line
 constexpr size_t kCtrlBytes = size_t(kParts + 2) * kLineWords * 4;
 constexpr int kCtrlWork = 0;                         // claim counter of partition p: kCtrlWork + p * kLineWords
 constexpr int kCtrlExit = kParts * kLineWords;       // workgroups that finished
 constexpr int kCtrlError = (kParts + 1) * kLineWords;  // set if a bounded wait ever expired
-constexpr size_t kArenaBytes = kCtrlBytes + 3 * size_t(SV_MAX_B) * 4;
+constexpr int kArenaArrays = 3;  // tickets, tickets2, flags (streaming and scoring kernels)
+// Words of request b's block (register-resident kernel), one 128-byte line:
+constexpr int kReqWords = 32;
+constexpr int kWRow = 0;      // kWRow + i: arrivals of row i (i = 0..SV_MAX_K)
+constexpr int kWMask = 18;    // 64-bit: bit i = row i has its verdict, bit 32 + i = row i rejected
+constexpr int kWDepart = 20;  // items that left the request
+constexpr int kWDraw = 21;    // kWDraw + r: arrivals of the draw's segment weights, round r (0, 1)
+static_assert(kWRow + SV_MAX_K < kWMask && kWMask % 2 == 0 && kWDraw + 1 < kReqWords, "request block");
+constexpr size_t kArenaBytes = kCtrlBytes + kArenaArrays * size_t(SV_MAX_B) * 4 + size_t(SV_MAX_B) * kReqWords * 4;
 
 // Slot of request b in the per-request arrays of the arena: consecutive
 // requests land 128 bytes apart (for b < SV_MAX_B / 32), so the atomics of
@@ -81,27 +97,32 @@ enum DrawMode { kUnresolved = 0, kNoDraw = 1, kResidual = 2, kBonus = 3 };
 
 // Decision of one request, read by its sampling items.
 struct Record {
-  int a;      // accept length
-  int mode;   // DrawMode
-  float kt;   // log2 normaliser of the target row: log2 pt(v) = z*c - kt
-  float kd;   // same for the draft row (residual only)
-  float c;    // log2(e) / T
-  float u;    // uniform of the draw
-  int pad[2];
+  int a;         // accept length
+  int mode;      // DrawMode
+  float kt;      // log2 normaliser of the target row: log2 pt(v) = z*c - kt
+  float kd;      // same for the draft row (residual only)
+  float c;       // log2(e) / T
+  float u;       // uniform of the draw
+  float before;  // weight of the segments before the chosen one
+  float t;       // u * total weight: the draw is the first token whose running weight exceeds t
 };
+
+
+
 
 struct WsLayout {
   size_t ctrl;      // uint32 control block (claim/exit counters, error flag)
   size_t tickets;   // uint32 [SV_MAX_B]  statistics arrivals per request
   size_t tickets2;  // uint32 [SV_MAX_B]  sampling arrivals per request
-  size_t flags;     // int [SV_MAX_B]     DrawMode once decided, 0 otherwise
-  size_t partials;  // Partial [B][R][nseg]
+  size_t flags;     // int [SV_MAX_B]     decision once made, 0 otherwise
+  size_t reqw;      // uint32 [SV_MAX_B][kReqWords]  request blocks (register-resident kernel)
+  size_t partials;  // Partial [B][R][nseg2]
   size_t zval;      // float [B][R]       logit at the draft token, per row
   size_t records;   // Record [B]
-  size_t segsum;    // float [B][nseg2]   weight of each sampling segment
+  size_t segsum;    // float [2][B][nseg2]  weight of each sampling segment (per draw round)
   size_t total;
-  int nseg;   // statistics segments per row
-  int nseg2;  // sampling segments per row
+  int nseg;   // 64 KiB statistics segments per row
+  int nseg2;  // 32 KiB half segments per row (partials are strided by this)
   int R;
 };
 
@@ -114,11 +135,12 @@ inline WsLayout ws_layout(int B, int V, int max_k, int dtype) {
   L.tickets = kCtrlBytes;
   L.tickets2 = L.tickets + size_t(SV_MAX_B) * 4;
   L.flags = L.tickets2 + size_t(SV_MAX_B) * 4;
+  L.reqw = L.flags + size_t(SV_MAX_B) * 4;
   L.partials = kArenaBytes;
-  L.zval = L.partials + align256(size_t(B) * L.R * L.nseg * sizeof(Partial));
+  L.zval = L.partials + align256(size_t(B) * L.R * L.nseg2 * sizeof(Partial));
   L.records = L.zval + align256(size_t(B) * L.R * 4);
   L.segsum = L.records + align256(size_t(B) * sizeof(Record));
-  L.total = L.segsum + align256(size_t(B) * L.nseg2 * 4);
+  L.total = L.segsum + align256(2 * size_t(B) * L.nseg2 * 4);
   return L;
 }
 
@@ -149,13 +171,15 @@ struct VerifyArgs {
   uint32_t* tickets;
   uint32_t* tickets2;
   int* flags;
-  Partial* partials;
+  uint32_t* reqw;     // request blocks
+  Partial* partials;  // [B][R][nseg2]
   float* zval;
   Record* records;
-  float* segsum;
-  // work-item schedule (see the kernel)
+  float* segsum;      // [2][B][nseg2]
+  // work-item schedule (see the kernels)
   int parts;         // independent schedules; partition p owns requests b = p (mod parts)
-  int group;         // requests per group within a partition
+  int group;         // requests per group within a partition (streaming kernel)
+  int stride;        // item slots per request (register-resident kernel)
   uint32_t spin_limit;
 };
 
@@ -175,7 +199,12 @@ struct ScoreArgs {
   Partial* partials;
 };
 
+// Streaming kernel: any supported size.
 hipError_t launch_spec_verify(VerifyArgs a, int dtype, hipStream_t stream);
+// Register-resident kernel: returns false (nothing launched) when a request's
+// items do not fit the resident workgroups; otherwise launches and stores the
+// launch status in *err.
+bool launch_resident(VerifyArgs a, int dtype, hipStream_t stream, hipError_t* err);
 hipError_t launch_av_score(const ScoreArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_av_fit(int B, int max_k, const float* feature, const int8_t* labels,
                          float* params, double* accum, float damping_c, float ridge,

@@ -70,7 +70,7 @@ __device__ __forceinline__ void finish_request(const VerifyArgs& a, Shared<ET>& 
     const bool d2 = tid < max_k;
     const int i2 = d2 ? tid : tid - max_k;
     if (d2 ? (i2 < nd) : (i2 <= K))
-      sh.rows[tid] = combine_published(&a.partials[(size_t(b) * a.R + tid) * a.nseg], a.nseg, c, !d2 && greedy);
+      sh.rows[tid] = combine_published(&a.partials[(size_t(b) * a.R + tid) * a.nseg2], a.nseg, c, !d2 && greedy);
   }
   __syncthreads();
 
@@ -125,7 +125,7 @@ __device__ __forceinline__ void finish_request(const VerifyArgs& a, Shared<ET>& 
     for (int i = 0; i < K; ++i) {
       if (!(sh.rows[i].s < kRecomputeBelow)) continue;
       const ET* row = static_cast<const ET*>(a.draft) + (a.draft_start[b] + i) * a.draft_stride;
-      const float so = exact_other_sum<ET>(row, &a.partials[(size_t(b) * a.R + i) * a.nseg], a.nseg, a.V,
+      const float so = exact_other_sum<ET>(row, &a.partials[(size_t(b) * a.R + i) * a.nseg2], a.nseg, a.V,
                                            sh.rows[i].m, c, sh.part);
       if (tid == 0) {
         const float x = feature_from_other(so);
@@ -200,7 +200,7 @@ __device__ __forceinline__ void stats_item(const VerifyArgs& a, Shared<ET>& sh, 
   }
 
   if (tid == 0) {
-    publish(&a.partials[(size_t(b) * a.R + r) * a.nseg + s], p);
+    publish(&a.partials[(size_t(b) * a.R + r) * a.nseg2 + s], p);
     // logit at the draft token, from the segment that holds it
     if (!greedy && i < K) {
       const int d = a.tokens[size_t(b) * max_k + i];

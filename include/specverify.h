@@ -68,8 +68,9 @@ typedef enum {
  * of B requests, vocabulary V, at most max_k drafts each, elements of type
  * `dtype`.  Returns 0 for arguments those calls would reject.
  *
- * The workspace starts with a fixed arena of SV_MAX_B arrival counters (one
- * per request slot), followed by per-row partial statistics.  Zero-fill the
+ * The workspace starts with a fixed arena (work counters and four words per
+ * request slot, SV_MAX_B slots), followed by per-row partial statistics,
+ * decision records and draw weights.  Zero-fill the
  * workspace once after allocation; every call leaves the counters at zero
  * again, and no call writes anything else into the arena, so one workspace
  * (of the largest size needed) serves any sequence of calls of any shapes on
@@ -189,6 +190,28 @@ int sv_av_score(void* stream, int B, int V, int max_k, int dtype,
 int sv_av_fit_step(void* stream, int B, int max_k, const float* feature,
                    const int8_t* labels, float* params, double* accum,
                    float damping_c, float ridge, int do_update);
+
+/* Which kernel sv_spec_verify launches: a process-wide setting, default
+ * SV_KERNEL_AUTO.  Both kernels compute the same outputs.
+ *   SV_KERNEL_STREAMING  a statistics pass over every row, then a second pass
+ *                        over the rows the draw needs (one row pair, or the
+ *                        bonus row, per stochastic request).
+ *   SV_KERNEL_RESIDENT   every logit is read once: each row segment stays on
+ *                        chip (registers and LDS) until its row's verdict is
+ *                        known, and the token is drawn from that copy.  It
+ *                        trades the second pass for waits between the
+ *                        workgroups of a row.
+ *   SV_KERNEL_AUTO       the streaming kernel (measured faster on MI355X for
+ *                        rows of 64 KiB and more).
+ * Returns the previous setting, or SV_ERR_INVALID_ARG for an unknown value
+ * (the setting is then unchanged). */
+typedef enum {
+  SV_KERNEL_AUTO = 0,
+  SV_KERNEL_STREAMING = 1,
+  SV_KERNEL_RESIDENT = 2
+} sv_kernel;
+
+int sv_set_verify_kernel(int kernel);
 
 /* Static description of a status code. */
 const char* sv_status_string(int status);

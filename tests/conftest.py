@@ -31,3 +31,18 @@ def load_golden(name):
 @pytest.fixture
 def golden():
     return load_golden
+
+
+VERIFY_KERNELS = {"streaming": 1, "resident": 2}  # sv_kernel values of include/specverify.h
+
+
+@pytest.fixture(params=sorted(VERIFY_KERNELS))
+def verify_kernel(request):
+    """Run a test once per verification kernel (process-wide selector),
+    restoring the previous selection afterwards."""
+    import draft_token_verification_spec_amd as sv
+
+    prev = sv.sv_set_verify_kernel(VERIFY_KERNELS[request.param])
+    print(f"[kernel {request.param}]", flush=True)
+    yield request.param
+    sv.sv_set_verify_kernel(prev)

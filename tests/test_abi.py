@@ -24,7 +24,7 @@ def declared_functions():
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
     assert set(names) == {"sv_workspace_size", "sv_spec_verify", "sv_av_score", "sv_av_fit_step",
-                          "sv_status_string"}
+                          "sv_status_string", "sv_set_verify_kernel"}
     lib = ctypes.CDLL(sv.lib_path())
     for n in names:
         assert hasattr(lib, n), n
@@ -36,6 +36,17 @@ def test_header_constants_match_binding():
     assert int(re.search(r"#define SV_MAX_K (\d+)", text).group(1)) == sv.SV_MAX_K
     assert re.search(r"#define SV_MAX_V \(1 << (\d+)\)", text).group(1) == str(sv.SV_MAX_V.bit_length() - 1)
     assert re.search(r"#define SV_MAX_B \(1 << (\d+)\)", text).group(1) == str(sv.SV_MAX_B.bit_length() - 1)
+
+
+def test_kernel_selector():
+    text = open(HEADER).read()
+    for name in ("SV_KERNEL_AUTO", "SV_KERNEL_STREAMING", "SV_KERNEL_RESIDENT"):
+        assert int(re.search(name + r" = (\d+)", text).group(1)) == getattr(sv, name)
+    assert sv.sv_set_verify_kernel(sv.SV_KERNEL_STREAMING) == sv.SV_KERNEL_AUTO
+    assert sv.sv_set_verify_kernel(sv.SV_KERNEL_RESIDENT) == sv.SV_KERNEL_STREAMING
+    with pytest.raises(RuntimeError):
+        sv.sv_set_verify_kernel(7)
+    assert sv.sv_set_verify_kernel(sv.SV_KERNEL_AUTO) == sv.SV_KERNEL_RESIDENT
 
 
 def test_status_strings():

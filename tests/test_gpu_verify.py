@@ -16,7 +16,8 @@ from oracle import verify as ov
 from synth import gen
 
 pytestmark = [pytest.mark.gpu,
-              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a HIP device")]
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a HIP device"),
+              pytest.mark.usefixtures("verify_kernel")]
 
 
 def _log(msg):
@@ -288,3 +289,17 @@ def test_deterministic_and_workspace_reuse():
         assert np.array_equal(first[k], again[k], equal_nan=True), k
     for k in mid:
         assert np.array_equal(mid[k], fresh[k], equal_nan=True), k
+
+
+def test_long_rows_many_drafts():
+    """8 drafts of 2^20 fp32 logits: 128 half segments per row, so the
+    register-resident kernel runs with few partitions (its progress bound
+    is per row)."""
+    g = np.random.default_rng(12)
+    B, K, V = 2, 8, 1 << 20
+    zd = (2.0 * g.standard_normal((B, K, V))).astype(np.float32)
+    zt = np.concatenate([zd + 0.3 * g.standard_normal((B, K, V)), g.standard_normal((B, 1, V))], 1)
+    b = _custom_batch(zd, zt.astype(np.float32), _draw_tokens(zd, 1.0, 13), 1.0)
+    _log("case K=8 V=2^20 fp32")
+    gpu = gpu_verify(b, want_feature=True)
+    assert compare_verify(b, gpu, ov.verify_batch(b)) <= 1
