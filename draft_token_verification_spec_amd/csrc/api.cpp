@@ -96,15 +96,15 @@ int sv_spec_verify(void* stream, int B, int V, int max_k, int dtype, const void*
   a.zval = reinterpret_cast<float*>(ws + L.zval);
   a.records = reinterpret_cast<Record*>(ws + L.records);
   a.segsum = reinterpret_cast<float*>(ws + L.segsum);
+  a.rowrec = reinterpret_cast<RowRec*>(ws + L.rowrec);
+  a.tagged = reinterpret_cast<uint64_t*>(ws + L.tagged);
   a.parts = a.group = a.stride = 0;
   a.spin_limit = 0;
   const int kind = __atomic_load_n(&g_verify_kernel, __ATOMIC_RELAXED);
   hipError_t err = hipSuccess;
-  if (kind == SV_KERNEL_RESIDENT) {
-    if (!launch_resident(a, dtype, static_cast<hipStream_t>(stream), &err)) return SV_ERR_UNSUPPORTED;
-    return to_status(err);
-  }
-  return to_status(launch_spec_verify(a, dtype, static_cast<hipStream_t>(stream)));
+  if (kind != SV_KERNEL_RESIDENT) return to_status(launch_streaming(a, dtype, static_cast<hipStream_t>(stream)));
+  if (!launch_verify(a, dtype, true, static_cast<hipStream_t>(stream), &err)) return SV_ERR_UNSUPPORTED;
+  return to_status(err);
 }
 
 int sv_av_score(void* stream, int B, int V, int max_k, int dtype, const void* draft_logits,

@@ -59,6 +59,7 @@ constexpr int kMaxCum = 256;    // half segments per row: 2^21 fp32 elements / 3
 static_assert(int64_t(SV_MAX_V) * 4 / kHalfBytes <= kMaxCum, "segment weight prefix");
 constexpr uint32_t kNoClaim = 0xffffffffu;
 constexpr uint32_t kPlainMismatch = 0xfffffffeu;  // run the item with the other load kind
+constexpr uint32_t kPrefetched = 0xfffffffdu;     // the next item's Meta is in sh.meta
 
 // What every item of row i learns once the row is complete.
 struct RowView {
@@ -66,6 +67,23 @@ struct RowView {
   float kt, kd;   // log2 normalisers: log2 p(v) = z * c - k
   float pd, pt;   // probabilities of the draft token (stochastic rows i < K)
   int acc;        // accept test of position i (1 for the bonus row)
+};
+
+// A partition's claim schedule (see decode_claim).
+struct Sched {
+  int p;              // partition: requests b = p + j * parts
+  uint32_t nreq;      // requests of the partition
+  uint32_t A, C, L;   // statistics slots, sampling slots per request; sampling lag in requests
+  uint32_t total;     // claim numbers of the partition
+};
+
+// An item, decoded from its claim number, with its request's scalars.
+struct Meta {
+  uint32_t id;  // claim number; >= total: the partition is exhausted
+  int b, slot, stats;
+  int K;
+  float T;
+  int64_t ts, ds;  // target_row_start[b], draft_row_start[b]
 };
 
 // Outcome of the draw's scan over its segment weights.
@@ -90,6 +108,7 @@ struct RShared {
   uint64_t mask;
   int word;
   uint32_t next;
+  Meta meta;
 };
 
 __device__ __forceinline__ uint32_t claim(uint32_t* counter) {
@@ -157,6 +176,16 @@ __device__ __forceinline__ void load_halves(const ET* r0, int h0, const ET* r1, 
       hi[k] = load_raw<ET>(r1, h1 + (k * kThreads + tid) * N, V, a1);
     }
   }
+}
+
+// Loads one half from (r, hb).
+template <typename ET, bool PLAIN>
+__device__ __forceinline__ void load_half(const ET* r, int hb, int V, uint4 (&v)[kHalfVecs], int tid) {
+  constexpr int N = Elem<ET>::N;
+  const bool al = is_aligned16(r);
+#pragma unroll
+  for (int k = 0; k < kHalfVecs; ++k)
+    v[k] = PLAIN ? load_vec16<ET>(r + hb + (k * kThreads + tid) * N) : load_raw<ET>(r, hb + (k * kThreads + tid) * N, V, al);
 }
 
 // Opaque to the optimiser: values computed from the registers before a fence
@@ -470,6 +499,27 @@ __device__ __forceinline__ void wait_count(const VerifyArgs& a, const uint32_t* 
   __syncthreads();
 }
 
+// Zeroes request b's words (by its last departing item).
+__device__ __forceinline__ void clear_request(uint32_t* w, int K) {
+  for (int k = 0; k <= K; ++k) store_dev(&w[kWRow + k], 0u);
+  store_dev(&w[kWMask], 0u);
+  store_dev(&w[kWMask + 1], 0u);
+  store_dev(&w[kWDepart], 0u);
+  store_dev(&w[kWDraw], 0u);
+  store_dev(&w[kWDraw + 1], 0u);
+}
+
+// Departure of a streaming request's row evaluator or sampling item (thread
+// 0): the last of the n of them clears the verdict mask.
+__device__ __forceinline__ void depart(uint32_t* w, uint32_t n) {
+  const uint32_t out = __hip_atomic_fetch_add(&w[kWDepart], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (out == n - 1) {
+    store_dev(&w[kWMask], 0u);
+    store_dev(&w[kWMask + 1], 0u);
+    store_dev(&w[kWDepart], 0u);
+  }
+}
+
 // Adds one to *p once this workgroup's published stores are complete;
 // returns the previous value (thread 0).
 __device__ __forceinline__ uint32_t arrive_count(uint32_t* p) {
@@ -630,18 +680,167 @@ __device__ __forceinline__ Choice scan_segments(const float* segsum, int n, floa
   return ch;
 }
 
+// The row's outputs and its verdict bit (run once per row, by its leader);
+// publishes the request's outputs when this verdict fixed the accept length.
+__device__ __forceinline__ void row_verdict(const VerifyArgs& a, RShared& sh, int b, int i, bool pair, int K, int nd,
+                                            bool greedy, bool want_feat, const RowView& v, uint32_t* w, int tid) {
+  if (tid == 0) {
+    const size_t o = size_t(b) * a.max_k + i;
+    if (i < K) {
+      if (a.p_draft) a.p_draft[o] = v.pd;
+      if (a.p_target) a.p_target[o] = v.pt;
+      if (want_feat && pair && v.D.s >= kRecomputeBelow) {
+        const float x = feature_from_other(v.D.s - 1.f);
+        a.av_feature[o] = x;
+        if (a.av_score) a.av_score[o] = sigmoid_score(a.av_params, i, x);
+      }
+    }
+    const uint64_t bits = (uint64_t(1) << i) | ((i < K && !v.acc) ? (uint64_t(1) << (32 + i)) : 0);
+    const uint64_t old = __hip_atomic_fetch_or(reinterpret_cast<uint64_t*>(w + kWMask), bits, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+    const int an = decided_a(old | bits, K);
+    sh.word = (an >= 0 && decided_a(old, K) < 0) ? an : -1;
+  }
+  __syncthreads();
+  const int aa = uniform(sh.word);
+  __syncthreads();
+  if (aa >= 0) publish_decision(a, b, K, nd, aa, greedy, want_feat, tid);
+}
+
+// Confident draft row (inclusive sum below kRecomputeBelow): the first half
+// segment holding the row maximum, and the other halves' sums scaled to it
+// (thread 0; the same values in every thread).
+__device__ __forceinline__ void confident_split(const VerifyArgs& a, RShared& sh, int b, int i, float m, float c,
+                                                int& seg, float& rest) {
+  if (threadIdx.x == 0) {
+    const Partial* pp = &a.partials[(size_t(b) * a.R + i) * a.nseg2];
+    int sg = -1;
+    float r = 0.f;
+    for (int q = 0; q < a.nseg2; ++q) {
+      const Partial p = fetch(&pp[q]);
+      if (p.m == m && sg < 0)
+        sg = q;
+      else if (p.m != -INFINITY)
+        r += (p.s + p.cnt) * fast_exp2((p.m - m) * c);
+    }
+    sh.word = sg;
+    sh.fv = r;
+  }
+  __syncthreads();
+  seg = uniform(sh.word);
+  rest = uniform(sh.fv);
+  __syncthreads();
+}
+
+// Exact feature of draft row i from its half segment `seg` (starting at
+// element hb, data in v) and the other halves' sums.
+template <typename ET>
+__device__ __forceinline__ void exact_feature(const VerifyArgs& a, RShared& sh, int b, int i, uint4 (&v)[kHalfVecs],
+                                              int hb, float rest, float c, int tid) {
+  const int wave = tid >> 6, lane = tid & 63;
+  Partial e = wave_reduce<kSumExclusive>(thread_stats<ET, kSumExclusive>(v, hb, c, tid), c);
+  if (lane == 0) sh.part[0][wave] = e;
+  __syncthreads();
+  if (tid == 0) {
+    e = merge_waves<kSumExclusive>(sh.part[0], c);
+    const float xf = feature_from_other(e.s + (e.cnt - 1.f) + rest);
+    const size_t o = size_t(b) * a.max_k + i;
+    a.av_feature[o] = xf;
+    if (a.av_score) a.av_score[o] = sigmoid_score(a.av_params, i, xf);
+  }
+  __syncthreads();
+}
+
 // ---------------------------------------------------------------------------
-// one item
+// claims
 // ---------------------------------------------------------------------------
 
+// Claim number -> item of a partition with nreq requests of A statistics
+// slots and C sampling slots: statistics of requests 0..L-1, then statistics
+// of request j + L followed by the sampling of request j, then the sampling
+// of the last L requests.
+__device__ __forceinline__ void decode_claim(uint32_t id, uint32_t nreq, uint32_t A, uint32_t C, uint32_t L,
+                                             bool& stats, uint32_t& j, uint32_t& off) {
+  if (C == 0) {
+    stats = true;
+    j = id / A;
+    off = id % A;
+    return;
+  }
+  L = min(L, nreq);
+  if (id < L * A) {
+    stats = true;
+    j = id / A;
+    off = id % A;
+    return;
+  }
+  const uint32_t q = id - L * A, blk = q / (A + C), r = q % (A + C);
+  if (blk < nreq - L) {
+    stats = r < A;
+    j = stats ? L + blk : blk;
+    off = stats ? r : r - A;
+    return;
+  }
+  const uint32_t q2 = q - (nreq - L) * (A + C);
+  stats = false;
+  j = (nreq - L) + q2 / C;
+  off = q2 % C;
+}
+
+// Decodes claim number id of partition S and loads its request's scalars
+// (thread 0).
+__device__ __forceinline__ Meta load_meta(const VerifyArgs& a, const Sched& S, uint32_t id) {
+  Meta m;
+  m.id = id;
+  m.b = -1;
+  m.slot = m.stats = m.K = 0;
+  m.T = 0.f;
+  m.ts = m.ds = 0;
+  if (id >= S.total) return m;
+  bool st;
+  uint32_t j, off;
+  decode_claim(id, S.nreq, S.A, S.C, S.L, st, j, off);
+  m.b = S.p + int(j) * a.parts;
+  m.slot = int(off);
+  m.stats = st ? 1 : 0;
+  m.K = min(max(a.num_draft[m.b], 0), a.max_k);
+  m.T = a.temperature[m.b];
+  m.ts = a.target_start[m.b];
+  m.ds = a.max_k > 0 ? a.draft_start[m.b] : 0;
+  return m;
+}
+
+// sh.meta in every thread, as scalars.
+__device__ __forceinline__ Meta read_meta(const RShared& sh) {
+  Meta m = sh.meta;
+  m.id = uniform(m.id);
+  m.b = uniform(m.b);
+  m.slot = uniform(m.slot);
+  m.stats = uniform(m.stats);
+  m.K = uniform(m.K);
+  m.T = uniform(m.T);
+  m.ts = (int64_t(uniform(uint32_t(uint64_t(m.ts) >> 32))) << 32) | uniform(uint32_t(m.ts));
+  m.ds = (int64_t(uniform(uint32_t(uint64_t(m.ds) >> 32))) << 32) | uniform(uint32_t(m.ds));
+  return m;
+}
+
+// ---------------------------------------------------------------------------
+// one statistics item
+// ---------------------------------------------------------------------------
+
+// HOLD: the register-resident kernel (the item keeps its data until its
+// row's verdict, and draws from it); otherwise the item leaves once counted
+// in, the last item of the row evaluating it, and the draw re-reads row a in
+// separate sampling items.
 // Returns, in thread 0, the next claim number taken ahead, kNoClaim, or
 // kPlainMismatch (the item needs the other load kind; nothing was done).
-template <typename ET, bool PLAIN, bool GREEDY>
-__device__ __forceinline__ uint32_t run_item(const VerifyArgs& a, RShared& sh, int b, int slot, uint32_t* counter) {
+template <typename ET, bool PLAIN, bool GREEDY, bool HOLD>
+__device__ __forceinline__ uint32_t run_item(const VerifyArgs& a, RShared& sh, const Meta& me, const Sched& S,
+                                             uint32_t* counter) {
   const int tid = item_tid(), wave = tid >> 6, lane = tid & 63;
   const int max_k = a.max_k;
-  const int K = min(max(a.num_draft[b], 0), max_k);
-  const float T = a.temperature[b];
+  const int b = me.b, slot = me.slot, K = me.K;
+  const float T = me.T;
   constexpr bool greedy = GREEDY;
   const bool want_feat = a.av_feature != nullptr;
   const int nd = (!greedy || want_feat) ? K : 0;  // rows read as pairs
@@ -664,9 +863,11 @@ __device__ __forceinline__ uint32_t run_item(const VerifyArgs& a, RShared& sh, i
   const float c = kLog2e / (greedy ? 1.f : T);
   const int base = pair ? s * E2 : 2 * s * E2;
   const int hb = pair ? base : base + E2;  // element base of the hi half
-  const ET* rt = static_cast<const ET*>(a.target) + (a.target_start[b] + i) * a.target_stride;
-  const ET* rd = pair ? static_cast<const ET*>(a.draft) + (a.draft_start[b] + i) * a.draft_stride : rt;
+  const ET* rt = static_cast<const ET*>(a.target) + (me.ts + i) * a.target_stride;
+  const ET* rd = pair ? static_cast<const ET*>(a.draft) + (me.ds + i) * a.draft_stride : rt;
   if (plain_halves<ET>(rd, base, rt, hb, a.V) != PLAIN) return kPlainMismatch;
+  uint32_t ahead = kNoClaim;
+  if (!HOLD && tid == 0) ahead = claim(counter);  // a streaming item never waits
 
   uint4 lo[kHalfVecs], hi[kHalfVecs];
   load_halves<ET, PLAIN>(rd, base, rt, hb, a.V, lo, hi, tid);
@@ -707,6 +908,42 @@ __device__ __forceinline__ uint32_t run_item(const VerifyArgs& a, RShared& sh, i
       publish(&a.partials[(size_t(b) * a.R + max_k + i) * a.nseg2 + s], p1);
     }
   }
+  uint32_t* w = &a.reqw[size_t(b) * kReqWords];
+  const uint32_t n_row = pair ? uint32_t(a.nseg2) : uint32_t(a.nseg);
+  if (!HOLD) {
+    // ---- streaming: count in; the row's last item evaluates it ----
+    // Thread 0 loads the next item's scalars while its arrival is in flight.
+    Meta nx;
+    if (tid == 0) {
+      nx = load_meta(a, S, ahead);
+      sh.word = int(arrive_count(&w[kWRow + i]));
+    }
+    __syncthreads();
+    const bool last = uniform(uint32_t(sh.word)) + 1 == n_row;
+    __syncthreads();
+    if (last) {
+      const RowView v = row_view(a, sh, b, i, pair, K, greedy, c, tid);
+      if (want_feat && pair && v.D.s < kRecomputeBelow) {
+        int seg;
+        float rest;
+        confident_split(a, sh, b, i, v.D.m, c, seg, rest);
+        uint4 u[kHalfVecs];
+#pragma unroll
+        for (int k = 0; k < kHalfVecs; ++k)
+          u[k] = load_raw<ET>(rd, seg * E2 + (k * kThreads + tid) * Elem<ET>::N, a.V, is_aligned16(rd));
+        exact_feature<ET>(a, sh, b, i, u, seg * E2, rest, c, tid);
+      }
+      row_verdict(a, sh, b, i, pair, K, nd, greedy, want_feat, v, w, tid);
+      // every item of the row has counted in: the counter is free again
+      if (tid == 0) {
+        store_dev(&w[kWRow + i], 0u);
+        depart(w, uint32_t(K + 1) + (GREEDY ? 0u : uint32_t(a.nseg2)));
+      }
+    }
+    if (tid == 0) sh.meta = nx;
+    return kPrefetched;
+  }
+
   // park the first half in LDS: only `hi` stays in registers from here on
 #pragma unroll
   for (int k = 0; k < kHalfVecs; ++k) sh.park[k][tid] = lo[k];
@@ -716,8 +953,6 @@ __device__ __forceinline__ uint32_t run_item(const VerifyArgs& a, RShared& sh, i
   // Item 0 of each row leads it: it writes the row's outputs and its verdict
   // bit.  Items that may draw, or may hold a confident row's maximum, wait
   // for their row, then combine its partials themselves.
-  uint32_t* w = &a.reqw[size_t(b) * kReqWords];
-  const uint32_t n_row = pair ? uint32_t(a.nseg2) : uint32_t(a.nseg);
   const bool leader = s == 0;
   const bool may_draw = !GREEDY && (pair || i == K);
   const bool may_hold = want_feat && pair;
@@ -725,7 +960,6 @@ __device__ __forceinline__ uint32_t run_item(const VerifyArgs& a, RShared& sh, i
   __syncthreads();
   const uint32_t before_me = uniform(uint32_t(sh.word));
   __syncthreads();
-  uint32_t ahead = kNoClaim;
   bool draw = false;
   float kt = 0.f, kd = 0.f;
   if (leader || may_draw || may_hold) {
@@ -733,67 +967,19 @@ __device__ __forceinline__ uint32_t run_item(const VerifyArgs& a, RShared& sh, i
     const RowView v = row_view(a, sh, b, i, pair, K, greedy, c, tid);
     kt = v.kt;
     kd = v.kd;
-    const size_t o = size_t(b) * max_k + i;
-
     // confident draft row: the item holding the first maximum re-sums its half exactly
     if (may_hold && v.D.s < kRecomputeBelow) {
-      if (tid == 0) {
-        const Partial* pp = &a.partials[(size_t(b) * a.R + i) * a.nseg2];
-        int seg = -1;
-        float rest = 0.f;
-        for (int q = 0; q < a.nseg2; ++q) {
-          const Partial p = fetch(&pp[q]);
-          if (p.m == v.D.m && seg < 0)
-            seg = q;
-          else if (p.m != -INFINITY)
-            rest += (p.s + p.cnt) * fast_exp2((p.m - v.D.m) * c);
-        }
-        sh.word = seg;
-        sh.fv = rest;
-      }
-      __syncthreads();
-      const int seg = uniform(sh.word);
-      const float rest = sh.fv;
-      __syncthreads();
+      int seg;
+      float rest;
+      confident_split(a, sh, b, i, v.D.m, c, seg, rest);
       if (seg == s) {
         uint4 u[kHalfVecs];
 #pragma unroll
         for (int k = 0; k < kHalfVecs; ++k) u[k] = sh.park[k][tid];
-        Partial e = wave_reduce<kSumExclusive>(thread_stats<ET, kSumExclusive>(u, base, c, tid), c);
-        if (lane == 0) sh.part[0][wave] = e;
-        __syncthreads();
-        if (tid == 0) {
-          e = merge_waves<kSumExclusive>(sh.part[0], c);
-          const float xf = feature_from_other(e.s + (e.cnt - 1.f) + rest);
-          a.av_feature[o] = xf;
-          if (a.av_score) a.av_score[o] = sigmoid_score(a.av_params, i, xf);
-        }
-        __syncthreads();
+        exact_feature<ET>(a, sh, b, i, u, base, rest, c, tid);
       }
     }
-
-    if (leader) {
-      if (tid == 0) {
-        if (i < K) {
-          if (a.p_draft) a.p_draft[o] = v.pd;
-          if (a.p_target) a.p_target[o] = v.pt;
-          if (want_feat && pair && v.D.s >= kRecomputeBelow) {
-            const float x = feature_from_other(v.D.s - 1.f);
-            a.av_feature[o] = x;
-            if (a.av_score) a.av_score[o] = sigmoid_score(a.av_params, i, x);
-          }
-        }
-        const uint64_t bits = (uint64_t(1) << i) | ((i < K && !v.acc) ? (uint64_t(1) << (32 + i)) : 0);
-        const uint64_t old = __hip_atomic_fetch_or(reinterpret_cast<uint64_t*>(w + kWMask), bits, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT);
-        const int an = decided_a(old | bits, K);
-        sh.word = (an >= 0 && decided_a(old, K) < 0) ? an : -1;
-      }
-      __syncthreads();
-      const int aa = uniform(sh.word);
-      __syncthreads();
-      if (aa >= 0) publish_decision(a, b, K, nd, aa, greedy, want_feat, tid);
-    }
+    if (leader) row_verdict(a, sh, b, i, pair, K, nd, greedy, want_feat, v, w, tid);
 
     // is this row the one the token is drawn from?
     if (may_draw) {
@@ -847,45 +1033,143 @@ __device__ __forceinline__ uint32_t run_item(const VerifyArgs& a, RShared& sh, i
   // ---- leave the request; the last item out clears its words ----
   if (tid == 0) {
     const uint32_t out = arrive_count(&w[kWDepart]);
-    if (out == n_items - 1) {
-      for (int k = 0; k <= K; ++k) store_dev(&w[kWRow + k], 0u);
-      store_dev(&w[kWMask], 0u);
-      store_dev(&w[kWMask + 1], 0u);
-      store_dev(&w[kWDepart], 0u);
-      store_dev(&w[kWDraw], 0u);
-      store_dev(&w[kWDraw + 1], 0u);
-    }
+    if (out == n_items - 1) clear_request(w, K);
   }
   return ahead;
 }
 
+
+// ---------------------------------------------------------------------------
+// one sampling item (streaming kernel)
+// ---------------------------------------------------------------------------
+
+// Half segment s of the rows request b's token is drawn from: the draft and
+// target rows a (residual) or the target row K (bonus).  Publishes its draw
+// weight; the request's last sampling item scans the weights, re-reads the
+// half segment where the running weight crosses u * total and searches it.
+template <typename ET, bool PLAIN>
+__device__ __forceinline__ void sample_body(const VerifyArgs& a, RShared& sh, int b, int s, int K, int aa, float c,
+                                            uint32_t* w, int tid) {
+  constexpr int E2 = kHalfBytes / int(sizeof(ET));
+  const int max_k = a.max_k;
+  const bool pair = aa < K;
+  const ET* rt = static_cast<const ET*>(a.target) + (a.target_start[b] + aa) * a.target_stride;
+  const ET* rd = pair ? static_cast<const ET*>(a.draft) + (a.draft_start[b] + aa) * a.draft_stride : rt;
+  uint4 lo[kHalfVecs], hi[kHalfVecs];
+  if (pair)
+    load_halves<ET, PLAIN>(rd, s * E2, rt, s * E2, a.V, lo, hi, tid);
+  else
+    load_half<ET, PLAIN>(rt, s * E2, a.V, hi, tid);
+  const RowView v = row_view(a, sh, b, aa, pair, K, false, c, tid);
+  if (pair) {
+#pragma unroll
+    for (int k = 0; k < kHalfVecs; ++k) sh.park[k][tid] = lo[k];
+  }
+  const float W = pair ? range_weight<ET, kWResid>(hi, c, v.kt, v.kd, sh, tid)
+                       : range_weight<ET, kWTarget>(hi, c, v.kt, v.kd, sh, tid);
+  float* seg = &a.segsum[size_t(b) * a.nseg2];
+  if (tid == 0) {
+    store_dev(&seg[s], W);
+    sh.word = int(arrive_count(&w[kWDraw]));
+  }
+  __syncthreads();
+  const bool last = uniform(uint32_t(sh.word)) + 1 == uint32_t(a.nseg2);
+  __syncthreads();
+  if (!last) return;
+  if (tid == 0) store_dev(&w[kWDraw], 0u);  // every sampling item has counted in
+
+  const float u = pair ? a.u_residual[b] : a.u_bonus[b];
+  const Choice ch = scan_segments(seg, a.nseg2, u, sh, tid);
+  int tok = -1;
+  if (ch.k < 0) {
+    // the residual has no mass (reachable only through rounding): draw from pt itself
+    if (pair)
+      tok = cdf_sample<ET, false>(rt, c, v.kt, rt, c, v.kt, a.V, u, reinterpret_cast<float*>(&sh.park[0][0]), sh.wi);
+  } else {
+    if (ch.k != s) {  // re-read the crossing half segment
+      if (plain_halves<ET>(rd, ch.k * E2, rt, ch.k * E2, a.V)) {
+        if (pair) load_halves<ET, true>(rd, ch.k * E2, rt, ch.k * E2, a.V, lo, hi, tid);
+        else load_half<ET, true>(rt, ch.k * E2, a.V, hi, tid);
+      } else {
+        if (pair) load_halves<ET, false>(rd, ch.k * E2, rt, ch.k * E2, a.V, lo, hi, tid);
+        else load_half<ET, false>(rt, ch.k * E2, a.V, hi, tid);
+      }
+      __syncthreads();
+      if (pair) {
+#pragma unroll
+        for (int k = 0; k < kHalfVecs; ++k) sh.park[k][tid] = lo[k];
+      }
+    }
+    tok = pair ? range_search<ET, kWResid>(hi, ch.k * E2, c, v.kt, v.kd, ch.before, ch.t, ch.fb, sh, tid)
+               : range_search<ET, kWTarget>(hi, ch.k * E2, c, v.kt, v.kd, ch.before, ch.t, ch.fb, sh, tid);
+  }
+  if (tid == 0) a.out_tokens[size_t(b) * (max_k + 1) + aa] = tok;
+}
+
+// Returns, in thread 0, the next claim number taken ahead, or kNoClaim.
 template <typename ET>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void resident_kernel(VerifyArgs a) {
+__device__ __forceinline__ uint32_t sample_item(const VerifyArgs& a, RShared& sh, const Meta& me, const Sched& S,
+                                                uint32_t* counter) {
+  const int tid = item_tid();
+  const int b = me.b, s = me.slot, K = me.K;
+  const float T = me.T;
+  if (!(T > 0.f)) return kNoClaim;  // greedy requests draw nothing
+  constexpr int E2 = kHalfBytes / int(sizeof(ET));
+  uint32_t ahead = kNoClaim;
+  if (tid == 0) ahead = claim(counter);
+  uint32_t* w = &a.reqw[size_t(b) * kReqWords];
+  const uint64_t m = wait_mask(a, w, [&](uint64_t mm) { return decided_a(mm, K) >= 0; }, sh);
+  const int aa = decided_a(m, K);
+  Meta nx;
+  if (tid == 0) nx = load_meta(a, S, ahead);
+  if (aa >= 0) {  // (an expired wait leaves the token unwritten)
+    const bool pair = aa < K;
+    const ET* rt = static_cast<const ET*>(a.target) + (me.ts + aa) * a.target_stride;
+    const ET* rd = pair ? static_cast<const ET*>(a.draft) + (me.ds + aa) * a.draft_stride : rt;
+    if (plain_halves<ET>(rd, s * E2, rt, s * E2, a.V))
+      sample_body<ET, true>(a, sh, b, s, K, aa, kLog2e / T, w, tid);
+    else
+      sample_body<ET, false>(a, sh, b, s, K, aa, kLog2e / T, w, tid);
+  }
+  if (tid == 0) {
+    depart(w, uint32_t(K + 1) + uint32_t(a.nseg2));
+    sh.meta = nx;
+  }
+  return kPrefetched;
+}
+
+template <typename ET, bool HOLD>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void verify_kernel(VerifyArgs a) {
   __shared__ RShared sh;
   const int tid = threadIdx.x;
   int p = int(blockIdx.x % uint32_t(a.parts));
   for (int visited = 0; visited < a.parts; ++visited, p = (p + 1) % a.parts) {
-    const uint32_t nreq = uint32_t((a.B - p + a.parts - 1) / a.parts);
-    const uint32_t total = nreq * uint32_t(a.stride);
+    Sched S;
+    S.p = p;
+    S.nreq = uint32_t((a.B - p + a.parts - 1) / a.parts);
+    S.A = uint32_t(a.stride);
+    S.C = HOLD ? 0u : uint32_t(a.nseg2);
+    S.L = uint32_t(a.group);
+    S.total = S.nreq * (S.A + S.C);
     uint32_t* counter = &a.ctrl[kCtrlWork + p * kLineWords];
-    if (tid == 0) sh.next = claim(counter);
+    if (tid == 0) sh.meta = load_meta(a, S, claim(counter));
     __syncthreads();
-    uint32_t id = uniform(sh.next);
+    Meta m = read_meta(sh);
     __syncthreads();
-    while (id < total) {
-      const int b = p + int(id / uint32_t(a.stride)) * a.parts;
-      const int slot = int(id % uint32_t(a.stride));
-      uint32_t ahead;
-      if (a.temperature[b] > 0.f) {
-        ahead = run_item<ET, true, false>(a, sh, b, slot, counter);
-        if (ahead == kPlainMismatch) ahead = run_item<ET, false, false>(a, sh, b, slot, counter);
+    while (m.id < S.total) {
+      uint32_t r;
+      if (!m.stats) {
+        r = sample_item<ET>(a, sh, m, S, counter);
+      } else if (m.T > 0.f) {
+        r = run_item<ET, true, false, HOLD>(a, sh, m, S, counter);
+        if (r == kPlainMismatch) r = run_item<ET, false, false, HOLD>(a, sh, m, S, counter);
       } else {
-        ahead = run_item<ET, true, true>(a, sh, b, slot, counter);
-        if (ahead == kPlainMismatch) ahead = run_item<ET, false, true>(a, sh, b, slot, counter);
+        r = run_item<ET, true, true, HOLD>(a, sh, m, S, counter);
+        if (r == kPlainMismatch) r = run_item<ET, false, true, HOLD>(a, sh, m, S, counter);
       }
-      if (tid == 0) sh.next = (ahead == kNoClaim) ? claim(counter) : ahead;
+      if (tid == 0 && r != kPrefetched) sh.meta = load_meta(a, S, r == kNoClaim ? claim(counter) : r);
       __syncthreads();
-      id = uniform(sh.next);
+      m = read_meta(sh);
       __syncthreads();
     }
   }
@@ -898,58 +1182,73 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   }
 }
 
-int g_capacity[64][2];
+int g_capacity[64][2][2];
 
-int resident_capacity(int dtype) {
+// Resident workgroups of the kernel on the current device (occupancy x CUs).
+int capacity(int dtype, bool hold) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
   const int slot = dtype == SV_BF16 ? 1 : 0;
-  int cap = __atomic_load_n(&g_capacity[dev][slot], __ATOMIC_RELAXED);
+  int cap = __atomic_load_n(&g_capacity[dev][slot][hold], __ATOMIC_RELAXED);
   if (cap == 0) {
     int per_cu = 0, cus = 0;
-    const hipError_t e1 =
-        dtype == SV_BF16 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, resident_kernel<uint16_t>, kThreads, 0)
-                         : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, resident_kernel<float>, kThreads, 0);
+    hipError_t e1;
+    if (dtype == SV_BF16)
+      e1 = hold ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, verify_kernel<uint16_t, true>, kThreads, 0)
+                : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, verify_kernel<uint16_t, false>, kThreads, 0);
+    else
+      e1 = hold ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, verify_kernel<float, true>, kThreads, 0)
+                : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, verify_kernel<float, false>, kThreads, 0);
     const hipError_t e2 = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     cap = (e1 == hipSuccess && e2 == hipSuccess && per_cu > 0 && cus > 0) ? per_cu * cus : -1;
-    __atomic_store_n(&g_capacity[dev][slot], cap, __ATOMIC_RELAXED);
+    __atomic_store_n(&g_capacity[dev][slot][hold], cap, __ATOMIC_RELAXED);
   }
   return cap;
 }
 
 }  // namespace
 
-// Item slots a request may need: pair items for rows 0..max_k-1, single
+// Statistics slots a request may need: pair items for rows 0..max_k-1, single
 // items for the bonus row.  Requests with fewer pair rows need fewer slots
 // (nseg <= nseg2).
-int resident_stride(int max_k, int nseg, int nseg2) { return max_k * nseg2 + nseg; }
+int stats_stride(int max_k, int nseg, int nseg2) { return max_k * nseg2 + nseg; }
 
-// Launches the register-resident kernel if the request's items fit the
-// resident workgroups with room for progress; returns false otherwise (the
-// caller then uses the streaming kernel).
-bool launch_resident(VerifyArgs a, int dtype, hipStream_t stream, hipError_t* err) {
-  const int cap = resident_capacity(dtype);
+#ifndef SV_SAMPLE_LAG
+#define SV_SAMPLE_LAG 2.0
+#endif
+
+bool launch_verify(VerifyArgs a, int dtype, bool hold, hipStream_t stream, hipError_t* err) {
+  const int cap = capacity(dtype, hold);
   if (cap <= 0) return false;
-  a.stride = resident_stride(a.max_k, a.nseg, a.nseg2);
+  a.stride = stats_stride(a.max_k, a.nseg, a.nseg2);
   if (a.nseg2 > kMaxCum) return false;
-  // an item waits only for items of its own row and of earlier rows: with
-  // more resident workgroups than parts * (row items - 1), one is always free
-  const int row_items = a.nseg2;  // >= a.nseg
   int parts = a.B < kParts ? a.B : kParts;
-  if (row_items > 1) parts = min(parts, (cap - 1) / (row_items - 1));
-  if (parts < 1) return false;
+  if (hold) {
+    // an item waits only for items of its own row and of earlier rows: with
+    // more resident workgroups than parts * (row items - 1), one is always free
+    const int row_items = a.nseg2;  // >= a.nseg
+    if (row_items > 1) parts = min(parts, (cap - 1) / (row_items - 1));
+    if (parts < 1) return false;
+  }
   a.parts = parts;
-  a.group = 0;
   const uint64_t nreq = (uint64_t(a.B) + parts - 1) / parts;
-  const uint64_t per_part = nreq * uint64_t(a.stride);
+  const uint64_t per_part = nreq * uint64_t(a.stride + (hold ? 0 : a.nseg2));
   if (per_part + uint64_t(cap) >= (uint64_t(1) << 32)) return false;
+  // sampling of request j follows the statistics of request j + group: about
+  // SV_SAMPLE_LAG statistics items per resident workgroup of the partition
+  // in between, so that most decisions are made by the time they are claimed
+  const double wg_per_part = double(cap) / parts;
+  a.group = hold ? 0 : max(1, int(SV_SAMPLE_LAG * wg_per_part / a.stride + 0.999));
   a.spin_limit = 1u << 20;
   const uint64_t all = per_part * uint64_t(parts);
   const unsigned grid = unsigned(all < uint64_t(cap) ? all : uint64_t(cap));
-  if (dtype == SV_BF16)
-    hipLaunchKernelGGL(resident_kernel<uint16_t>, dim3(grid), dim3(kThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL(resident_kernel<float>, dim3(grid), dim3(kThreads), 0, stream, a);
+  if (dtype == SV_BF16) {
+    if (hold) hipLaunchKernelGGL((verify_kernel<uint16_t, true>), dim3(grid), dim3(kThreads), 0, stream, a);
+    else hipLaunchKernelGGL((verify_kernel<uint16_t, false>), dim3(grid), dim3(kThreads), 0, stream, a);
+  } else {
+    if (hold) hipLaunchKernelGGL((verify_kernel<float, true>), dim3(grid), dim3(kThreads), 0, stream, a);
+    else hipLaunchKernelGGL((verify_kernel<float, false>), dim3(grid), dim3(kThreads), 0, stream, a);
+  }
   *err = hipGetLastError();
   return true;
 }

@@ -107,8 +107,26 @@ struct Record {
   float t;       // u * total weight: the draw is the first token whose running weight exceeds t
 };
 
+// Handoff slot of the streaming kernels: 8 bytes written in one store, the
+// low word kSlotReady, the high word the value's bits.  The reader polls until
+// the low word is kSlotReady and clears the slot once consumed, so every slot
+// is zero between calls.  kSlotReady is a signalling-NaN bit pattern: no
+// float the kernels store and no index or count equals it, so a slot left
+// over from other data is never taken for a handed-off value.
+constexpr uint32_t kSlotReady = 0x7fb5a5a5u;
+__host__ __device__ constexpr uint64_t ready_slot(uint32_t bits) { return (uint64_t(bits) << 32) | kSlotReady; }
 
 
+
+
+// Statistics of one position for the decision and the draw (streaming
+// kernels), written by the position's last segment.
+struct RowRec {
+  float kt;    // log2 normaliser of the target row: log2 pt(v) = z*c - kt
+  float kd;    // same for the draft row (positions with a draft row read)
+  int argmax;  // lowest-index argmax of the target row (greedy requests)
+  int pad;
+};
 
 struct WsLayout {
   size_t ctrl;      // uint32 control block (claim/exit counters, error flag)
@@ -120,6 +138,9 @@ struct WsLayout {
   size_t zval;      // float [B][R]       logit at the draft token, per row
   size_t records;   // Record [B]
   size_t segsum;    // float [2][B][nseg2]  weight of each sampling segment (per draw round)
+  size_t rowrec;    // RowRec [B][max_k + 1]
+  size_t tagged;    // handoff slots (uint64): partials [B][R][nseg2][2], logits at the draft token [B][R],
+                    // segment weights [B][nseg2]
   size_t total;
   int nseg;   // 64 KiB statistics segments per row
   int nseg2;  // 32 KiB half segments per row (partials are strided by this)
@@ -140,7 +161,9 @@ inline WsLayout ws_layout(int B, int V, int max_k, int dtype) {
   L.zval = L.partials + align256(size_t(B) * L.R * L.nseg2 * sizeof(Partial));
   L.records = L.zval + align256(size_t(B) * L.R * 4);
   L.segsum = L.records + align256(size_t(B) * sizeof(Record));
-  L.total = L.segsum + align256(2 * size_t(B) * L.nseg2 * 4);
+  L.rowrec = L.segsum + align256(2 * size_t(B) * L.nseg2 * 4);
+  L.tagged = L.rowrec + align256(size_t(B) * (max_k + 1) * sizeof(RowRec));
+  L.total = L.tagged + align256((size_t(B) * L.R * L.nseg2 * 2 + size_t(B) * L.R + size_t(B) * L.nseg2) * 8);
   return L;
 }
 
@@ -176,6 +199,8 @@ struct VerifyArgs {
   float* zval;
   Record* records;
   float* segsum;      // [2][B][nseg2]
+  RowRec* rowrec;     // [B][max_k + 1]
+  uint64_t* tagged;   // handoff slots (see WsLayout::tagged)
   // work-item schedule (see the kernels)
   int parts;         // independent schedules; partition p owns requests b = p (mod parts)
   int group;         // requests per group within a partition (streaming kernel)
@@ -201,10 +226,12 @@ struct ScoreArgs {
 
 // Streaming kernel: any supported size.
 hipError_t launch_spec_verify(VerifyArgs a, int dtype, hipStream_t stream);
-// Register-resident kernel: returns false (nothing launched) when a request's
-// items do not fit the resident workgroups; otherwise launches and stores the
-// launch status in *err.
-bool launch_resident(VerifyArgs a, int dtype, hipStream_t stream, hipError_t* err);
+// Verification kernel, register-resident (hold) or streaming: returns false
+// (nothing launched) if the sizes do not fit it; otherwise launches and
+// stores the launch status in *err.
+bool launch_verify(VerifyArgs a, int dtype, bool hold, hipStream_t stream, hipError_t* err);
+// The two streaming kernels (statistics, then the draw).
+hipError_t launch_streaming(VerifyArgs a, int dtype, hipStream_t stream);
 hipError_t launch_av_score(const ScoreArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_av_fit(int B, int max_k, const float* feature, const int8_t* labels,
                          float* params, double* accum, float damping_c, float ridge,

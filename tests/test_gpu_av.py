@@ -44,20 +44,14 @@ def test_no_fit_identity_on_gpu():
 
 def test_fused_feature_equals_av_score(verify_kernel):
     """The feature and score sv_spec_verify produces from its own pass over the
-    draft rows agree with sv_av_score's: bit for bit for the streaming kernel
-    (same 64 KiB segments, same order of operations), to fp32 summation-order
-    rounding for the register-resident one (32 KiB halves), and both with the
-    oracle."""
+    draft rows agree with sv_av_score's (64 KiB segments there, 32 KiB halves
+    here: equal up to fp32 summation order) and with the oracle."""
     for name, B in [("bf16_b256_k4_v128256_peaked", 32), ("fp32_b1024_k1to3_v129280_greedy_mix", 32)]:
         b = gen.make_batch(name, B=B)
         v = gpu_verify(b, want_feature=True)
         s = gpu_score(b, threshold=0.0)
-        if verify_kernel == "streaming":
-            assert np.array_equal(v["av_feature"], s["feature"], equal_nan=True)
-            assert np.array_equal(v["av_score"], s["score"], equal_nan=True)
-        else:
-            assert np.all(rel_close(v["av_feature"], s["feature"], 1e-5, scale_floor=1.0))
-            assert np.all(rel_close(v["av_score"], s["score"], 1e-5))
+        assert np.all(rel_close(v["av_feature"], s["feature"], 1e-5, scale_floor=1.0))
+        assert np.all(rel_close(v["av_score"], s["score"], 1e-5))
         compare_scores(b, v["av_feature"], v["av_score"], oav.av_score_batch(b))
 
 
