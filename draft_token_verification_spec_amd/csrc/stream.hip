@@ -8,38 +8,62 @@
 // "Solution: online acceptance estimator" and "Scoring the distribution".
 //
 // statistics kernel: one workgroup per 32 KiB segment of every row read
-//   (draft rows 0..K_b-1, target rows 0..K_b), in position order.  Each
-//   reduces its segment to (max, sum of exp2((z - max) * c)) - or (max,
-//   lowest argmax) for greedy target rows - and publishes it.  The last
-//   segment of position i to arrive combines the position's partials,
-//   evaluates the accept test of position i, writes the position's outputs
-//   and sets the position's bits in the request's verdict mask (bit i:
-//   known; bit 32 + i: rejected).  The verdict that fixes the accept length
-//   (the first rejection once every earlier position was accepted, or all
-//   accepted once the bonus row is known) writes the request's outputs.
-//   Nothing waits: a few workgroups per row live slightly longer.
-// draw kernel: one workgroup per 32 KiB segment of the rows the token is
-//   drawn from (residual: draft and target row a; bonus: target row K_b),
-//   read again now that every decision is final.  Each publishes its
-//   segment's weight; the request's last one scans the weights, re-reads
-//   the segment where the running weight crosses u * total and searches it.
+//   (draft rows 0..K_b-1, target rows 0..K_b).  Each reduces its segment to
+//   (max, sum of exp2((z - max) * c)) - or (max, lowest argmax) for greedy
+//   target rows - stores it, and leaves; the segment holding a draft token
+//   also stores the logit at that token.  Nothing waits and nothing is
+//   counted: the kernel is a plain streaming reduction.
+// verdict + draw kernel: one workgroup per 32 KiB segment of the rows the
+//   emitted token is drawn from.  Every workgroup of a request first merges
+//   the request's segment statistics (a few KiB, from L2) into row
+//   statistics and evaluates the accept tests; all of them reach the same
+//   accept length a, as they compute the same function of the same data.
+//   The first one writes the request's outputs.  Then each reads its
+//   segment of the draw rows (residual: draft and target row a; bonus:
+//   target row K_b) and hands off the segment's weight; the request's last
+//   segment collects the weights, scans them, re-reads the segment where the
+//   running weight crosses u * total and searches it.
 //
-// Both kernels are plain grids: the hardware dispatcher keeps every
-// compute unit busy, and the statistics kernel's small register footprint
-// (8 x 16 bytes of data per thread) gives 8 waves per SIMD to hide memory
-// latency behind the exp2 arithmetic.
+// Workgroups are dispatched in index order, so the last segment of a
+// request only ever waits for workgroups that already hold a compute unit:
+// the wait ends.  A hand-off slot is 8 bytes written in one store (ready
+// marker, value) and is cleared by the workgroup that takes it, so no slot
+// holds the marker between calls and replays of a captured call need no
+// reset.
+//
+// Both kernels are plain grids: the hardware dispatcher keeps every compute
+// unit busy, and the statistics kernel's small register footprint (8 x 16
+// bytes of data per thread) gives 8 waves per SIMD to hide memory latency
+// behind the exp2 arithmetic.
 #include "sv_device.hpp"
 
 namespace sv {
 
 namespace {
 
-constexpr int kNV = 8;  // 16-byte vectors per thread: 32 KiB per workgroup
+constexpr int kNV = 8;     // 16-byte vectors per thread: 32 KiB per workgroup
+constexpr int kSleep = 2;  // s_sleep argument while polling a slot
+constexpr int kRowsPerPass = 3;  // rows each wave merges per pass over the segment statistics
 
-__device__ __forceinline__ void drain_stores() {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0);
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+// Hand a 32-bit value off in slot p.
+__device__ __forceinline__ void put_slot(uint64_t* p, uint32_t bits) {
+  __hip_atomic_store(p, ready_slot(bits), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wait for slot p (at most spin_limit polls), clear it, return its value.  An
+// expired wait (a broken dispatch order) sets the error word and gives NaN.
+__device__ __forceinline__ uint32_t take_slot(uint64_t* p, const VerifyArgs& a) {
+  uint64_t v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (uint32_t k = 0; uint32_t(v) != kSlotReady && k < a.spin_limit; ++k) {
+    __builtin_amdgcn_s_sleep(kSleep);
+    v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (uint32_t(v) != kSlotReady) {
+    store_dev(&a.ctrl[kCtrlError], 1u);
+    return 0x7fc00000u;
+  }
+  __hip_atomic_store(p, uint64_t(0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return uint32_t(v >> 32);
 }
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
@@ -65,6 +89,23 @@ __device__ __forceinline__ void load_seg(const ET* row, int hb, int V, uint4 (&v
   if (al && hb + kThreads * kNV * N <= V) {
 #pragma unroll
     for (int k = 0; k < kNV; ++k) v[k] = load_vec16<ET>(row + hb + (k * kThreads + tid) * N);
+  } else if (al && V % N == 0) {
+    // the tail of an aligned row: each vector is wholly inside or wholly past
+    // the end.  Every lane loads (the row's last vector standing in for one
+    // past the end), and only then are the vectors past the end set to -inf,
+    // so the loads are issued back to back instead of one branch at a time.
+    constexpr uint32_t ninf = N == 8 ? (Elem<ET>::kNegInf << 16 | Elem<ET>::kNegInf) : Elem<ET>::kNegInf;
+#pragma unroll
+    for (int k = 0; k < kNV; ++k) v[k] = load_vec16<ET>(row + min(hb + (k * kThreads + tid) * N, V - N));
+    const int t = fresh_tid(), lim = (V - hb) / N;  // vectors of the tail
+#pragma unroll
+    for (int k = 0; k < kNV; ++k) {
+      const bool in = k * kThreads + t < lim;
+      v[k].x = in ? v[k].x : ninf;
+      v[k].y = in ? v[k].y : ninf;
+      v[k].z = in ? v[k].z : ninf;
+      v[k].w = in ? v[k].w : ninf;
+    }
   } else {
 #pragma unroll
     for (int k = 0; k < kNV; ++k) v[k] = load_raw<ET>(row, hb + (k * kThreads + tid) * N, V, al);
@@ -143,213 +184,39 @@ __device__ __forceinline__ Partial block_reduce(Partial p, float c, Partial* lds
   return p;
 }
 
+// Slot of request b's segment s weight (uint64, see WsLayout::tagged).
+__device__ __forceinline__ uint64_t* weight_slot(const VerifyArgs& a, int b, int s) {
+  return a.tagged + size_t(b) * a.nseg2 + s;
+}
+
 // ---------------------------------------------------------------------------
-// request words and decisions
+// the statistics kernel
 // ---------------------------------------------------------------------------
 
-// Accept length fixed by the verdict mask, or -1 while it is open.
-__device__ __forceinline__ int decided_a(uint64_t mask, int K) {
-  const uint32_t known = uint32_t(mask), rej = uint32_t(mask >> 32);
-  const uint32_t acc = known & ~rej;
-  const int f = __builtin_ctz(~acc);  // first position not known to be accepted
-  if (f < K) return ((known >> f) & (rej >> f) & 1u) ? f : -1;
-  return ((known >> K) & 1u) ? K : -1;
-}
-
-struct StatsShared {
-  Partial red[kWaves];
-  Partial cp[2][64];
-  float zv[2];
-  int word;
-  float fv;
-};
-
-// Outputs fixed by the accept length a (once per request, by the position
-// verdict that fixed it).  The token at a of a stochastic request is written
-// by the draw kernel; a greedy request's is the argmax of target row a.
-__device__ __forceinline__ void publish_decision(const VerifyArgs& a, int b, int K, int aa, bool greedy,
-                                                 bool want_feat, int tid) {
-  const int max_k = a.max_k;
-  if (tid < 64) {
-    const int j = tid;
-    if (j < max_k) {
-      const size_t o = size_t(b) * max_k + j;
-      if (a.labels) a.labels[o] = (j < aa) ? 1 : ((j == aa && aa < K) ? 0 : -1);
-      if (j >= K) {
-        if (a.p_draft) a.p_draft[o] = NAN;
-        if (a.p_target) a.p_target[o] = NAN;
-        if (want_feat) {
-          a.av_feature[o] = NAN;
-          if (a.av_score) a.av_score[o] = NAN;
-        }
-      }
-    }
-    if (j <= max_k && j != aa) a.out_tokens[size_t(b) * (max_k + 1) + j] = (j < aa) ? a.tokens[size_t(b) * max_k + j] : -1;
-    if (j == 0) {
-      a.accept_len[b] = aa;
-      const RowRec* rr = &a.rowrec[size_t(b) * (max_k + 1) + aa];
-      Record* rec = &a.records[b];  // read by the draw kernel
-      rec->a = aa;
-      if (greedy) {
-        a.out_tokens[size_t(b) * (max_k + 1) + aa] = load_dev(&rr->argmax);
-        rec->mode = kNoDraw;
-      } else {
-        rec->mode = aa < K ? kResidual : kBonus;
-        rec->kt = load_dev(&rr->kt);
-        rec->kd = load_dev(&rr->kd);
-        rec->u = aa < K ? a.u_residual[b] : a.u_bonus[b];
-      }
-    }
-  }
-}
-
-// The last segment of position i: combine, test, outputs, verdict.
-template <typename ET>
-__device__ __forceinline__ void finish_position(const VerifyArgs& a, StatsShared& sh, int b, int i, int K, bool greedy,
-                                                bool want_feat, bool has_draft, float c, uint32_t* w, int tid) {
-  const int wave = tid >> 6, lane = tid & 63;
-  const int max_k = a.max_k, n = a.nseg2;
-  const Partial* pp = &a.partials[(size_t(b) * a.R + i) * a.nseg2];
-  const Partial* tp = &a.partials[(size_t(b) * a.R + max_k + i) * a.nseg2];
-  const bool test = i < K;
-  Partial D{-INFINITY, 0.f, 0.f, 0x7fffffff}, Tg = D;
-  for (int s0 = 0; s0 < n; s0 += 64) {
-    const int m = min(64, n - s0);
-    if (wave == 0 && has_draft && lane < m) sh.cp[0][lane] = fetch(&pp[s0 + lane]);
-    if (wave == 1 && lane < m) sh.cp[1][lane] = fetch(&tp[s0 + lane]);
-    if (wave == 2 && s0 == 0 && lane < 2 && test && !greedy)
-      sh.zv[lane] = load_dev(&a.zval[size_t(b) * a.R + (lane == 0 ? i : max_k + i)]);
-    __syncthreads();
-    if (tid == 0) {
-      for (int k = 0; k < m; ++k) {
-        if (has_draft) merge_ms(D.m, D.s, D.cnt, sh.cp[0][k].m, sh.cp[0][k].s, sh.cp[0][k].cnt, c);
-        if (greedy)
-          merge_argmax(Tg.m, Tg.idx, sh.cp[1][k].m, sh.cp[1][k].idx);
-        else
-          merge_ms(Tg.m, Tg.s, Tg.cnt, sh.cp[1][k].m, sh.cp[1][k].s, sh.cp[1][k].cnt, c);
-      }
-    }
-    __syncthreads();
-  }
-
-  // confident draft row: re-sum the first segment holding the maximum exactly
-  if (want_feat && has_draft) {
-    if (tid == 0) {
-      sh.word = -1;
-      sh.fv = 0.f;
-      if (D.s < kRecomputeBelow) {
-        int seg = -1;
-        float rest = 0.f;
-        for (int q = 0; q < n; ++q) {
-          const Partial p = fetch(&pp[q]);
-          if (p.m == D.m && seg < 0)
-            seg = q;
-          else if (p.m != -INFINITY)
-            rest += (p.s + p.cnt) * fast_exp2((p.m - D.m) * c);
-        }
-        sh.word = seg;
-        sh.fv = rest;
-      }
-    }
-    __syncthreads();
-    const int seg = uniform(sh.word);
-    const float rest = sh.fv;
-    __syncthreads();
-    if (seg >= 0) {
-      constexpr int E = kThreads * kNV * Elem<ET>::N;
-      const ET* rd = static_cast<const ET*>(a.draft) + (a.draft_start[b] + i) * a.draft_stride;
-      uint4 v[kNV];
-      load_seg<ET>(rd, seg * E, a.V, v, tid);
-      Partial e = block_reduce<kSumExclusive>(thread_stats<ET, kSumExclusive>(v, seg * E, c, tid), c, sh.red, tid);
-      if (tid == 0) {
-        const float x = feature_from_other(e.s + (e.cnt - 1.f) + rest);
-        const size_t o = size_t(b) * max_k + i;
-        a.av_feature[o] = x;
-        if (a.av_score) a.av_score[o] = sigmoid_score(a.av_params, i, x);
-      }
-      __syncthreads();
-    }
-  }
-
-  if (tid == 0) {
-    const size_t o = size_t(b) * max_k + i;
-    bool acc = true;
-    if (test) {
-      const int d = a.tokens[o];
-      float pd = NAN, pt;
-      if (greedy) {
-        acc = (d == Tg.idx);
-        pt = acc ? 1.f : 0.f;
-      } else {
-        const float l2d = (sh.zv[0] - D.m) * c - fast_log2(D.s + D.cnt);
-        const float l2t = (sh.zv[1] - Tg.m) * c - fast_log2(Tg.s + Tg.cnt);
-        pd = fast_exp2(l2d);
-        pt = fast_exp2(l2t);
-        acc = (l2d == -INFINITY) || (a.u_accept[o] < fast_exp2(l2t - l2d));
-      }
-      if (a.p_draft) a.p_draft[o] = pd;
-      if (a.p_target) a.p_target[o] = pt;
-      if (want_feat && has_draft && D.s >= kRecomputeBelow) {
-        const float x = feature_from_other(D.s - 1.f);
-        a.av_feature[o] = x;
-        if (a.av_score) a.av_score[o] = sigmoid_score(a.av_params, i, x);
-      }
-    }
-    RowRec* rr = &a.rowrec[size_t(b) * (max_k + 1) + i];
-    store_dev(&rr->kt, Tg.m * c + fast_log2(Tg.s + Tg.cnt));
-    store_dev(&rr->kd, has_draft ? D.m * c + fast_log2(D.s + D.cnt) : 0.f);
-    store_dev(&rr->argmax, Tg.idx);
-    store_dev(&w[kWRow + i], 0u);  // every segment of the position has arrived
-    drain_stores();
-    const uint64_t bits = (uint64_t(1) << i) | ((test && !acc) ? (uint64_t(1) << (32 + i)) : 0);
-    const uint64_t old = __hip_atomic_fetch_or(reinterpret_cast<uint64_t*>(w + kWMask), bits, __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT);
-    const int an = decided_a(old | bits, K);
-    sh.word = (an >= 0 && decided_a(old, K) < 0) ? an : -1;
-  }
-  __syncthreads();
-  const int aa = uniform(sh.word);
-  __syncthreads();
-  if (aa >= 0) publish_decision(a, b, K, aa, greedy, want_feat, tid);
-}
-
-// One segment: statistics, publication, arrival at its position; the last
-// segment of the position finishes it.  Instantiated per statistics mode so
-// that the mode choice is taken before the loads.
+// One segment of row slot rs: statistics, stored for the verdict.
+// Instantiated per statistics mode so that the mode choice is taken before
+// the loads.
 template <typename ET, int MODE>
-__device__ __forceinline__ void stats_segment(const VerifyArgs& a, StatsShared& sh, int b, int i, int s, bool draft,
-                                              int K, int nd, bool greedy, bool want_feat, float c, const ET* row,
-                                              int d, int tid) {
-  const int n = a.nseg2, R = a.R, max_k = a.max_k;
+__device__ __forceinline__ void stats_segment(const VerifyArgs& a, Partial* red, int b, int rs, int s, bool ztok,
+                                              float c, const ET* row, int d, int tid) {
   constexpr int E = kThreads * kNV * Elem<ET>::N;
   const int hb = s * E;
+  float z = 0.f;
+  if (ztok && tid == 0) z = Elem<ET>::one(row + d);  // in flight with the segment
   uint4 v[kNV];
   load_seg<ET>(row, hb, a.V, v, tid);
-  const Partial p = block_reduce<MODE>(thread_stats<ET, MODE>(v, hb, c, tid), c, sh.red, tid);
-
-  uint32_t* w = &a.reqw[size_t(b) * kReqWords];
+  const Partial p = block_reduce<MODE>(thread_stats<ET, MODE>(v, hb, c, tid), c, red, tid);
   if (tid == 0) {
-    publish(&a.partials[(size_t(b) * R + (draft ? i : max_k + i)) * n + s], p);
-    if (!greedy && i < K) {
-      if (d >= hb && d < hb + E && d < a.V)
-        store_dev(&a.zval[size_t(b) * R + (draft ? i : max_k + i)], Elem<ET>::one(row + d));
-    }
-    const uint32_t want = uint32_t(n) * (i < nd ? 2u : 1u);
-    drain_stores();
-    const uint32_t old = __hip_atomic_fetch_add(&w[kWRow + i], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    sh.word = (old + 1 == want) ? 1 : 0;
+    a.partials[(size_t(b) * a.R + rs) * a.nseg2 + s] = p;
+    if (ztok) a.zval[size_t(b) * a.R + rs] = z;
   }
-  __syncthreads();
-  if (uniform(sh.word) == 0) return;
-  __syncthreads();
-  finish_position<ET>(a, sh, b, i, K, greedy, want_feat, i < nd, c, w, tid);
 }
 
 // Workgroup = segment s of row slot r (position order: draft i, target i,
 // ..., target max_k) of request b.
 template <typename ET>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) void stats_kernel(VerifyArgs a) {
-  __shared__ StatsShared sh;
+  __shared__ Partial red[kWaves];
   const int tid = threadIdx.x;
   const int n = a.nseg2, R = a.R, max_k = a.max_k;
   const uint32_t item = blockIdx.x;
@@ -365,21 +232,31 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
   const int d = i < max_k ? a.tokens[size_t(b) * max_k + i] : -1;
   const int K = min(max(kraw, 0), max_k);
   const bool greedy = !(T > 0.f);
-  const bool want_feat = a.av_feature != nullptr;
-  const int nd = (!greedy || want_feat) ? K : 0;  // draft rows read
+  const int nd = (!greedy || a.av_feature != nullptr) ? K : 0;  // draft rows read
   if (draft ? (i >= nd) : (i > K)) return;
-  const float c = kLog2e / (greedy ? 1.f : T);
+  const float c = uniform(kLog2e / (greedy ? 1.f : T));
   const ET* row = draft ? static_cast<const ET*>(a.draft) + (start + i) * a.draft_stride
                         : static_cast<const ET*>(a.target) + (start + i) * a.target_stride;
+  constexpr int E = kThreads * kNV * Elem<ET>::N;
+  const bool ztok = !greedy && i < K && d >= s * E && d < (s + 1) * E && d < a.V;
+  const int rs = draft ? i : max_k + i;
   if (!draft && greedy)
-    stats_segment<ET, kArgmax>(a, sh, b, i, s, draft, K, nd, greedy, want_feat, c, row, d, tid);
+    stats_segment<ET, kArgmax>(a, red, b, rs, s, ztok, c, row, d, tid);
   else
-    stats_segment<ET, kSumInclusive>(a, sh, b, i, s, draft, K, nd, greedy, want_feat, c, row, d, tid);
+    stats_segment<ET, kSumInclusive>(a, red, b, rs, s, ztok, c, row, d, tid);
 }
 
 // ---------------------------------------------------------------------------
-// the draw
+// the verdict and the draw
 // ---------------------------------------------------------------------------
+
+// Statistics of a whole row.
+struct RowStat {
+  float m;  // maximum logit
+  float s;  // sum of exp2((z - m) * c) (sum rows)
+  int idx;  // lowest-index argmax (greedy target rows)
+  float z;  // logit at the draft token (rows of a test position)
+};
 
 struct DrawShared {
   float wt[kWaves];
@@ -388,7 +265,10 @@ struct DrawShared {
   float cum[256];
   float chunk[kMaxChunks];
   int li[4];
+  Partial red[kWaves];
+  RowStat row[2 * SV_MAX_K + 1];  // by row slot: draft i at i, target j at max_k + j
   int word;
+  float fv;
   float fz, ft, fb4;
   int fk, ffb;
 };
@@ -517,14 +397,17 @@ __device__ __forceinline__ int seg_search(uint4 (&t)[kNV], uint4 (&d)[kNV], int 
   return result;
 }
 
-// Segment weights published; the last segment scans them: Z, the crossing
-// segment k (-1 if Z is not positive), the weight before it, u * Z.
-__device__ __forceinline__ void scan_weights(const float* segsum, int n, float u, DrawShared& sh, int tid) {
+// The last segment collects the other segments' weights (its own is `own`)
+// and scans them: Z, the crossing segment k (-1 if Z is not positive), the
+// weight before it, u * Z.
+__device__ __forceinline__ void scan_weights(const VerifyArgs& a, int b, float own, int n, float u, DrawShared& sh,
+                                             int tid) {
   const int lane = tid & 63;
   if (tid < 64) {
     float carry = 0.f;
     for (int base = 0; base < n; base += 64) {
-      float x = (base + lane < n) ? load_dev(&segsum[base + lane]) : 0.f;
+      const int q = base + lane;
+      float x = (q < n - 1) ? __uint_as_float(take_slot(weight_slot(a, b, q), a)) : (q == n - 1 ? own : 0.f);
       x = wave_inclusive_scan(x, lane) + carry;
       if (base + lane < n) sh.cum[base + lane] = x;
       carry = __shfl(x, 63, 64);
@@ -561,25 +444,17 @@ __device__ __forceinline__ void scan_weights(const float* segsum, int n, float u
 
 template <typename ET, bool RESID>
 __device__ __forceinline__ void draw_segment(const VerifyArgs& a, DrawShared& sh, int b, int s, int aa, float c,
-                                             float kt, float kd, float u, const ET* rt, const ET* rd, uint32_t* w,
-                                             int tid) {
+                                             float kt, float kd, float u, const ET* rt, const ET* rd, int tid) {
   constexpr int E = kThreads * kNV * Elem<ET>::N;
   uint4 t[kNV], d[kNV];
   load_seg<ET>(rt, s * E, a.V, t, tid);
   if (RESID) load_seg<ET>(rd, s * E, a.V, d, tid);
   const float W = seg_weight<ET, RESID>(t, d, c, kt, kd, sh, tid);
-  float* segsum = &a.segsum[size_t(b) * a.nseg2];
-  if (tid == 0) {
-    store_dev(&segsum[s], W);
-    drain_stores();
-    const uint32_t old = __hip_atomic_fetch_add(&w[kWDraw], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    sh.word = (old + 1 == uint32_t(a.nseg2)) ? 1 : 0;
+  if (s < a.nseg2 - 1) {
+    if (tid == 0) put_slot(weight_slot(a, b, s), __float_as_uint(W));
+    return;
   }
-  __syncthreads();
-  if (uniform(sh.word) == 0) return;
-  if (tid == 0) store_dev(&w[kWDraw], 0u);  // every segment has arrived
-
-  scan_weights(segsum, a.nseg2, u, sh, tid);
+  scan_weights(a, b, W, a.nseg2, u, sh, tid);
   const int k = uniform(sh.fk);
   int tok = -1;
   if (k < 0) {
@@ -595,35 +470,206 @@ __device__ __forceinline__ void draw_segment(const VerifyArgs& a, DrawShared& sh
   if (tid == 0) a.out_tokens[size_t(b) * (a.max_k + 1) + aa] = tok;
 }
 
+// Row slot of the q-th row the verdict merges: draft rows 0..nd-1, then
+// target rows 0..K.
+__device__ __forceinline__ int row_slot(int q, int nd, int max_k) { return q < nd ? q : max_k + (q - nd); }
+
+// Merge the segment statistics of every row the request read into sh.row.
+// Wave w takes rows w, w + kWaves, ... (kRowsPerPass of them per pass, their
+// loads in flight together); lane l takes segments l, l + 64, ... in order,
+// and a butterfly combines the lanes.  Every workgroup of the request
+// evaluates the same function of the same data, so all reach the same
+// statistics.
+__device__ __forceinline__ void merge_rows(const VerifyArgs& a, DrawShared& sh, int b, int K, int nd, bool greedy,
+                                           float c, int tid) {
+  const int wave = tid >> 6, lane = tid & 63;
+  const int n = a.nseg2, max_k = a.max_k;
+  const int nrows = nd + K + 1;
+  const Partial* base = a.partials + size_t(b) * a.R * n;
+  const Partial none{-INFINITY, 0.f, 0.f, 0x7fffffff};
+  for (int q0 = wave; q0 < nrows; q0 += kWaves * kRowsPerPass) {
+    Partial acc[kRowsPerPass];
+    float z[kRowsPerPass];
+#pragma unroll
+    for (int r = 0; r < kRowsPerPass; ++r) {
+      const int q = q0 + r * kWaves;
+      const bool test = (q < nd ? q : q - nd) < K;  // a row of a tested position
+      acc[r] = none;
+      z[r] = (q < nrows && lane == 0 && test && !greedy) ? a.zval[size_t(b) * a.R + row_slot(q, nd, max_k)] : NAN;
+    }
+    for (int s0 = 0; s0 < n; s0 += 64) {
+      Partial p[kRowsPerPass];
+#pragma unroll
+      for (int r = 0; r < kRowsPerPass; ++r) {
+        const int q = q0 + r * kWaves;
+        p[r] = (q < nrows && s0 + lane < n) ? base[size_t(row_slot(q, nd, max_k)) * n + s0 + lane] : none;
+      }
+#pragma unroll
+      for (int r = 0; r < kRowsPerPass; ++r) {
+        if (greedy && q0 + r * kWaves >= nd)
+          merge_argmax(acc[r].m, acc[r].idx, p[r].m, p[r].idx);
+        else
+          merge_ms(acc[r].m, acc[r].s, acc[r].cnt, p[r].m, p[r].s, p[r].cnt, c);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < kRowsPerPass; ++r) {
+      const int q = q0 + r * kWaves;
+      const bool amax = greedy && q >= nd;
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) {
+        Partial x;
+        x.m = __shfl_xor(acc[r].m, o, 64);
+        x.s = __shfl_xor(acc[r].s, o, 64);
+        x.cnt = __shfl_xor(acc[r].cnt, o, 64);
+        x.idx = __shfl_xor(acc[r].idx, o, 64);
+        if (amax)
+          merge_argmax(acc[r].m, acc[r].idx, x.m, x.idx);
+        else
+          merge_ms(acc[r].m, acc[r].s, acc[r].cnt, x.m, x.s, x.cnt, c);
+      }
+      if (lane == 0 && q < nrows) sh.row[row_slot(q, nd, max_k)] = RowStat{acc[r].m, acc[r].s + acc[r].cnt, acc[r].idx, z[r]};
+    }
+  }
+  __syncthreads();
+}
+
+// Estimator feature of a confident draft row i (sum of the non-maximal
+// probabilities below kRecomputeBelow - 1): the first segment holding the
+// row maximum is summed again leaving out one maximal term exactly, and the
+// other segments' sums are added at the row maximum's scale.
+template <typename ET>
+__device__ __forceinline__ void confident_feature(const VerifyArgs& a, DrawShared& sh, int b, int i, float c,
+                                                  int tid) {
+  constexpr int E = kThreads * kNV * Elem<ET>::N;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int n = a.nseg2;
+  const float M = sh.row[i].m;
+  if (wave == 0) {
+    const Partial* pp = a.partials + (size_t(b) * a.R + i) * n;
+    int first = 0x7fffffff;
+    float rest = 0.f;
+    for (int s0 = 0; s0 < n; s0 += 64) {
+      const int q = s0 + lane;
+      const Partial p = q < n ? pp[q] : Partial{-INFINITY, 0.f, 0.f, 0x7fffffff};
+      const uint64_t hit = __ballot(q < n && p.m == M);
+      if (first == 0x7fffffff && hit) first = s0 + __ffsll(static_cast<long long>(hit)) - 1;
+      const float x = (p.m != -INFINITY && q != first) ? (p.s + p.cnt) * fast_exp2((p.m - M) * c) : 0.f;
+      rest += wave_sum(x);
+    }
+    if (lane == 0) {
+      sh.fk = first;
+      sh.fv = rest;
+    }
+  }
+  __syncthreads();
+  const int seg = uniform(sh.fk);
+  const float rest = sh.fv;
+  float x = kFeatureClamp;
+  if (seg != 0x7fffffff) {
+    const ET* rd = static_cast<const ET*>(a.draft) + (a.draft_start[b] + i) * a.draft_stride;
+    uint4 v[kNV];
+    load_seg<ET>(rd, seg * E, a.V, v, tid);
+    const Partial e = block_reduce<kSumExclusive>(thread_stats<ET, kSumExclusive>(v, seg * E, c, tid), c, sh.red, tid);
+    x = feature_from_other(e.s + (e.cnt - 1.f) + rest);
+  }
+  if (tid == 0) {
+    const size_t o = size_t(b) * a.max_k + i;
+    a.av_feature[o] = x;
+    if (a.av_score) a.av_score[o] = sigmoid_score(a.av_params, i, x);
+  }
+  __syncthreads();
+}
+
 // Workgroup = segment s of the draw rows of request b (requests in reverse
 // order: the last ones read by the statistics kernel are the likeliest to be
 // cached).
 template <typename ET>
-__global__ __launch_bounds__(kThreads) void draw_kernel(VerifyArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void draw_kernel(VerifyArgs a) {
   __shared__ DrawShared sh;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n = a.nseg2, max_k = a.max_k;
   const int s = int(blockIdx.x % uint32_t(n));
   const int b = a.B - 1 - int(blockIdx.x / uint32_t(n));
-  uint32_t* w = &a.reqw[size_t(b) * kReqWords];
-  if (s == 0 && tid == 0) {  // the statistics kernel is over: the verdict mask is free again
-    store_dev(&w[kWMask], 0u);
-    store_dev(&w[kWMask + 1], 0u);
-  }
-  // the decision record and the row starts in one round trip
-  const Record rec = a.records[b];
+  const int kraw = a.num_draft[b];
   const float T = a.temperature[b];
-  const int64_t ts = a.target_start[b];
-  const int64_t ds = max_k > 0 ? a.draft_start[b] : 0;
-  if (rec.mode != kResidual && rec.mode != kBonus) return;  // greedy requests draw nothing
-  const int aa = rec.a;
-  const float c = kLog2e / T;
-  const ET* rt = static_cast<const ET*>(a.target) + (ts + aa) * a.target_stride;
-  if (rec.mode == kResidual) {
-    const ET* rd = static_cast<const ET*>(a.draft) + (ds + aa) * a.draft_stride;
-    draw_segment<ET, true>(a, sh, b, s, aa, c, rec.kt, rec.kd, rec.u, rt, rd, w, tid);
+  const int K = min(max(kraw, 0), max_k);
+  const bool greedy = !(T > 0.f);
+  const bool want_feat = a.av_feature != nullptr;
+  const int nd = (!greedy || want_feat) ? K : 0;  // draft rows read
+  const float c = uniform(kLog2e / (greedy ? 1.f : T));
+  // lane i of wave 0 tests position i: its token and uniform, in flight with the merge
+  int dl = -1;
+  float ul = 0.f;
+  if (wave == 0 && lane < K) {
+    dl = a.tokens[size_t(b) * max_k + lane];
+    if (!greedy) ul = a.u_accept[size_t(b) * max_k + lane];
+  }
+  merge_rows(a, sh, b, K, nd, greedy, c, tid);
+
+  // the accept tests, and the accept length a: the first rejection, else K
+  float pd = NAN, pt = NAN;
+  if (wave == 0) {
+    bool rej = false;
+    if (lane < K) {
+      const RowStat tr = sh.row[max_k + lane];
+      if (greedy) {
+        rej = dl != tr.idx;
+        pt = rej ? 0.f : 1.f;
+      } else {
+        const RowStat dr = sh.row[lane];
+        const float l2d = (dr.z - dr.m) * c - fast_log2(dr.s);
+        const float l2t = (tr.z - tr.m) * c - fast_log2(tr.s);
+        pd = fast_exp2(l2d);
+        pt = fast_exp2(l2t);
+        rej = !((l2d == -INFINITY) || (ul < fast_exp2(l2t - l2d)));
+      }
+    }
+    const uint64_t rm = __ballot(rej);
+    if (lane == 0) sh.word = rm ? __ffsll(static_cast<long long>(rm)) - 1 : K;
+  }
+  __syncthreads();
+  const int aa = uniform(sh.word);
+
+  // the request's outputs, by its first workgroup (the token at a of a
+  // stochastic request comes from the draw)
+  if (s == 0 && wave == 0) {
+    const int j = lane;
+    if (j < max_k) {
+      const size_t o = size_t(b) * max_k + j;
+      if (a.labels) a.labels[o] = (j < aa) ? 1 : ((j == aa && aa < K) ? 0 : -1);
+      if (a.p_draft) a.p_draft[o] = j < K ? pd : NAN;
+      if (a.p_target) a.p_target[o] = j < K ? pt : NAN;
+      if (want_feat && !(j < nd && sh.row[j].s < kRecomputeBelow)) {  // confident rows: below
+        const float x = j < nd ? feature_from_other(sh.row[j].s - 1.f) : NAN;
+        a.av_feature[o] = x;
+        if (a.av_score) a.av_score[o] = j < nd ? sigmoid_score(a.av_params, j, x) : NAN;
+      }
+    }
+    if (j <= max_k && j != aa) a.out_tokens[size_t(b) * (max_k + 1) + j] = (j < aa) ? dl : -1;
+    if (j == 0) {
+      a.accept_len[b] = aa;
+      if (greedy) a.out_tokens[size_t(b) * (max_k + 1) + aa] = sh.row[max_k + aa].idx;
+    }
+  }
+  // features of confident draft rows: position i by the workgroup of segment i mod n
+  if (want_feat)
+    for (int i = s; i < nd; i += n)
+      if (sh.row[i].s < kRecomputeBelow) confident_feature<ET>(a, sh, b, i, c, tid);
+
+  if (greedy) return;
+  const bool resid = aa < K;
+  const RowStat tr = sh.row[max_k + aa];
+  const RowStat dr = sh.row[resid ? aa : 0];
+  const float kt = tr.m * c + fast_log2(tr.s);
+  const float kd = resid ? dr.m * c + fast_log2(dr.s) : 0.f;
+  const float u = resid ? a.u_residual[b] : a.u_bonus[b];
+  const ET* rt = static_cast<const ET*>(a.target) + (a.target_start[b] + aa) * a.target_stride;
+  if (resid) {
+    const ET* rd = static_cast<const ET*>(a.draft) + (a.draft_start[b] + aa) * a.draft_stride;
+    draw_segment<ET, true>(a, sh, b, s, aa, c, kt, kd, u, rt, rd, tid);
   } else {
-    draw_segment<ET, false>(a, sh, b, s, aa, c, rec.kt, rec.kd, rec.u, rt, rt, w, tid);
+    draw_segment<ET, false>(a, sh, b, s, aa, c, kt, kd, u, rt, rt, tid);
   }
 }
 
@@ -634,6 +680,7 @@ hipError_t launch_streaming(VerifyArgs a, int dtype, hipStream_t stream) {
   const uint64_t n2 = uint64_t(a.B) * uint64_t(a.nseg2);
   if (n1 == 0) return hipSuccess;
   if (n1 >= (uint64_t(1) << 31)) return hipErrorInvalidValue;
+  a.spin_limit = 1u << 18;  // a fraction of a second of polling: reached only if dispatch order were broken
   if (dtype == SV_BF16) {
     hipLaunchKernelGGL(stats_kernel<uint16_t>, dim3(unsigned(n1)), dim3(kThreads), 0, stream, a);
     hipLaunchKernelGGL(draw_kernel<uint16_t>, dim3(unsigned(n2)), dim3(kThreads), 0, stream, a);

@@ -107,17 +107,15 @@ struct Record {
   float t;       // u * total weight: the draw is the first token whose running weight exceeds t
 };
 
-// Handoff slot of the streaming kernels: 8 bytes written in one store, the
-// low word kSlotReady, the high word the value's bits.  The reader polls until
-// the low word is kSlotReady and clears the slot once consumed, so every slot
-// is zero between calls.  kSlotReady is a signalling-NaN bit pattern: no
-// float the kernels store and no index or count equals it, so a slot left
-// over from other data is never taken for a handed-off value.
+// Hand-off slot of the draw kernel: 8 bytes written in one store, the low
+// word kSlotReady, the high word the value's bits.  The reader polls until
+// the low word is kSlotReady and clears the slot once it has the value.  The
+// slots share the per-call region with other arrays when the call shapes
+// change; kSlotReady is a signalling-NaN bit pattern that none of them
+// holds (no float the kernels store and no index or count equals it), so
+// data left there is never taken for a handed-off value.
 constexpr uint32_t kSlotReady = 0x7fb5a5a5u;
 __host__ __device__ constexpr uint64_t ready_slot(uint32_t bits) { return (uint64_t(bits) << 32) | kSlotReady; }
-
-
-
 
 // Statistics of one position for the decision and the draw (streaming
 // kernels), written by the position's last segment.
@@ -139,8 +137,7 @@ struct WsLayout {
   size_t records;   // Record [B]
   size_t segsum;    // float [2][B][nseg2]  weight of each sampling segment (per draw round)
   size_t rowrec;    // RowRec [B][max_k + 1]
-  size_t tagged;    // handoff slots (uint64): partials [B][R][nseg2][2], logits at the draft token [B][R],
-                    // segment weights [B][nseg2]
+  size_t tagged;    // uint64 [B][nseg2]  hand-off slots of the draw's segment weights
   size_t total;
   int nseg;   // 64 KiB statistics segments per row
   int nseg2;  // 32 KiB half segments per row (partials are strided by this)
@@ -163,7 +160,7 @@ inline WsLayout ws_layout(int B, int V, int max_k, int dtype) {
   L.segsum = L.records + align256(size_t(B) * sizeof(Record));
   L.rowrec = L.segsum + align256(2 * size_t(B) * L.nseg2 * 4);
   L.tagged = L.rowrec + align256(size_t(B) * (max_k + 1) * sizeof(RowRec));
-  L.total = L.tagged + align256((size_t(B) * L.R * L.nseg2 * 2 + size_t(B) * L.R + size_t(B) * L.nseg2) * 8);
+  L.total = L.tagged + align256(size_t(B) * L.nseg2 * 8);
   return L;
 }
 
@@ -200,7 +197,7 @@ struct VerifyArgs {
   Record* records;
   float* segsum;      // [2][B][nseg2]
   RowRec* rowrec;     // [B][max_k + 1]
-  uint64_t* tagged;   // handoff slots (see WsLayout::tagged)
+  uint64_t* tagged;   // hand-off slots (see WsLayout::tagged)
   // work-item schedule (see the kernels)
   int parts;         // independent schedules; partition p owns requests b = p (mod parts)
   int group;         // requests per group within a partition (streaming kernel)
