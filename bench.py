@@ -13,9 +13,11 @@ rotate between steps so that no step reads rows the previous one left in the
 256 MB Infinity Cache.
 
 Prints one JSON line: positions/s over the timed steps, the roofline of the
-verification kernel (algorithmic HBM bytes per launch / its mean duration from
-HIP events on the launching stream, against the 8 TB/s HBM3E peak) and the
-CPU oracle timed on a bounded sample of the same workload.
+dominant kernel - the statistics kernel, which reads every logit once
+(algorithmic HBM bytes per launch / its mean duration from HIP events on the
+launching stream, against the 8 TB/s HBM3E peak) - with the whole
+verification call (statistics kernel + verdict and draw kernel) beside it,
+and the CPU oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -49,7 +51,49 @@ def parse_args():
                    help="per-launch HBM bytes measured with rocprofv3 counters (optional)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="after timing, copy a MIB-sized device buffer 3 times (reference for HBM counters)")
+    p.add_argument("--counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                   help="no GPU work: turn the counter_collection.csv files of a FETCH_SIZE and a WRITE_SIZE "
+                        "rocprofv3 pass (run with --copy-calibration) into per-launch HBM bytes, print them and "
+                        "store them in --traffic")
     return p.parse_args()
+
+
+def summarize_counters(args):
+    """Per-launch HBM bytes of the library's kernels from two rocprofv3
+    counter passes.  FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled
+    by what they read for the calibration copy of known size (the largest
+    copyBuffer dispatches: the copy reads and writes --copy-calibration MiB)."""
+    import csv
+    import re
+
+    per = {}
+    scale = {}
+    for counter, path in zip(("FETCH_SIZE", "WRITE_SIZE"), args.counters):
+        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+        copies = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
+        top = max(copies)
+        cal = [v for v in copies if v > 0.9 * top]
+        mib = args.copy_calibration or 512
+        scale[counter] = mib * 1024.0 / (sum(cal) / len(cal))
+        for r in rows:
+            m = re.search(r"sv::(?:\(anonymous namespace\)::)?(\w+)", r["Kernel_Name"])
+            if m and "copyBuffer" not in r["Kernel_Name"]:
+                per.setdefault(m.group(1), {}).setdefault(counter, []).append(float(r["Counter_Value"]))
+    out = {}
+    for k, d in sorted(per.items()):
+        f = sum(d["FETCH_SIZE"]) / len(d["FETCH_SIZE"]) * scale["FETCH_SIZE"] * 1024
+        w = sum(d["WRITE_SIZE"]) / len(d["WRITE_SIZE"]) * scale["WRITE_SIZE"] * 1024
+        out[k] = {"dispatches": len(d["FETCH_SIZE"]), "fetch_bytes_per_launch": f, "write_bytes_per_launch": w,
+                  "bytes_per_launch": f + w}
+        print(f"{k:16s} {len(d['FETCH_SIZE']):3d} dispatches  fetch {f / 1e6:9.2f} MB  write {w / 1e6:8.2f} MB")
+    print(f"scales: FETCH_SIZE x{scale['FETCH_SIZE']:.5f}, WRITE_SIZE x{scale['WRITE_SIZE']:.5f}")
+    rec = {"workload": args.workload, "kernel": "stats_kernel",
+           "bytes_per_launch": out["stats_kernel"]["bytes_per_launch"],
+           "fetch_scale": scale["FETCH_SIZE"], "write_scale": scale["WRITE_SIZE"], "kernels": out,
+           "kernel_source_sha256": kernel_source_hash()}
+    with open(args.traffic, "w") as fh:
+        json.dump(rec, fh, indent=1)
+        fh.write("\n")
 
 
 def to_device(batch, dev):
@@ -121,6 +165,9 @@ def cpu_baseline(batch, budget_s):
 
 def main():
     args = parse_args()
+    if args.counters:
+        summarize_counters(args)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (requests shard across GPUs "
               "with no exchange, so the one-GPU rate is the per-GPU rate).", file=sys.stderr, flush=True)
@@ -159,22 +206,20 @@ def main():
         outs.append(o)
     ws.get(dev, sv.sv_workspace_size(B, V, K, sv.SV_BF16 if b0.dtype == "bf16" else sv.SV_F32))
 
-    def step(i, ev=None):
+    def step(i):
         _, d = sets[i % len(sets)]
         o = outs[i % len(sets)]
-        if ev is not None:
-            ev[0].record()
         sv.sv_spec_verify(d["draft"], d["draft_row_start"], d["target"], d["target_row_start"], d["num_draft"],
                           d["draft_tokens"], d["temperature"], d["u_accept"], d["u_residual"], d["u_bonus"],
                           max_k=K, av_params=params, want_feature=True, workspace=ws, out=o)
-        if ev is not None:
-            ev[1].record()
         sv.sv_av_fit_step(o["av_feature"], o["labels"], params, accum, do_update=True)
 
     kernel = args.kernel
     sv.sv_set_verify_kernel({"resident": sv.SV_KERNEL_RESIDENT, "streaming": sv.SV_KERNEL_STREAMING,
                              "auto": sv.SV_KERNEL_AUTO}[kernel])
-    kernel_name = "resident_kernel" if kernel == "resident" else "spec_verify_kernel"
+    # phase 0 of a call is its dominant kernel: the statistics kernel (which
+    # reads every logit once), or the whole resident kernel
+    kernel_name = "resident_kernel" if kernel == "resident" else "stats_kernel"
     log(f"warming up ({kernel_name})")
     for w in range(args.warmup):
         step(w)
@@ -182,7 +227,6 @@ def main():
     log("timing")
 
     steps = args.steps
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     graph = None
     if args.graph:
         # capture one rotation period per graph replay; the library issues no
@@ -206,23 +250,30 @@ def main():
             graph.replay()
         end.record()
         torch.cuda.synchronize(dev)
-        # per-kernel time from a separate pass of eagerly launched steps with events
-        for k in range(min(steps, 3 * len(sets) * 10)):
-            step(k, evs[k])
-        torch.cuda.synchronize(dev)
-        vms = [a.elapsed_time(z) for a, z in evs[:min(steps, 3 * len(sets) * 10)]]
+        # kernel times from a separate pass of eagerly launched steps, with
+        # the library's HIP events on the launching stream
+        nk = min(steps, 30 * len(sets))
+        sv.sv_timing_enable(nk)
+        for k in range(nk):
+            step(k)
+        phases = sv.sv_timing_read(nk)
     else:
+        sv.sv_timing_enable(steps)
         for k in range(steps):
-            step(k, evs[k])
+            step(k)
         end.record()
         torch.cuda.synchronize(dev)
-        vms = [a.elapsed_time(z) for a, z in evs]
+        phases = sv.sv_timing_read(steps)
+    sv.sv_timing_enable(0)
     wall = time.perf_counter() - t0
     ms_total = start.elapsed_time(end)
     ms_per_step = ms_total / steps
-    verify_ms = float(np.mean(vms))
+    kernel_ms = float(np.mean(phases[:, 0]))
+    second_ms = float(np.mean(phases[:, 1]))
+    call_ms = kernel_ms + second_ms
     value = positions / (ms_per_step * 1e-3)
-    achieved = bytes_per_launch / (verify_ms * 1e-3) / 1e9
+    achieved = bytes_per_launch / (kernel_ms * 1e-3) / 1e9
+    call_gbs = bytes_per_launch / (call_ms * 1e-3) / 1e9
 
     # HBM bytes per launch from rocprofv3 counters, valid only for the kernel
     # sources they were measured on
@@ -230,7 +281,7 @@ def main():
     if os.path.exists(args.traffic):
         try:
             tr = json.load(open(args.traffic))
-            if (tr.get("workload") == args.workload and tr.get("kernel", "spec_verify_kernel") == kernel_name
+            if (tr.get("workload") == args.workload and tr.get("kernel") == kernel_name
                     and tr.get("kernel_source_sha256") == kernel_source_hash()):
                 traffic = tr.get("bytes_per_launch")
         except (OSError, ValueError):
@@ -256,9 +307,13 @@ def main():
                    "kernel": kernel},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
-                     "kernel": kernel_name, "kernel_ms": verify_ms,
+                     "kernel": kernel_name, "kernel_ms": kernel_ms,
                      "algorithmic_bytes_per_launch": bytes_per_launch},
-        "extra": {"mean_accept_len": al, "positions_per_step": positions, "wall_s": wall},
+        "extra": {"mean_accept_len": al, "positions_per_step": positions, "wall_s": wall,
+                  "sv_spec_verify_call": {"kernels": "stats_kernel + draw_kernel" if kernel != "resident"
+                                          else "resident_kernel",
+                                          "ms": call_ms, "draw_kernel_ms": second_ms,
+                                          "achieved_gbs": call_gbs, "frac": call_gbs / PEAK_HBM_GBS}},
     }
     if args.copy_calibration > 0:
         log("copy calibration")

@@ -30,6 +30,8 @@ __all__ = [
     "sv_av_score",
     "sv_av_fit_step",
     "sv_set_verify_kernel",
+    "sv_timing_enable",
+    "sv_timing_read",
     "SV_KERNEL_AUTO",
     "SV_KERNEL_STREAMING",
     "SV_KERNEL_RESIDENT",
@@ -64,6 +66,8 @@ _SIGNATURES = {
     "sv_av_fit_step": (_i, [_p, _i, _i, _p, _p, _p, _p, _f, _f, _i]),
     "sv_status_string": (ctypes.c_char_p, [_i]),
     "sv_set_verify_kernel": (_i, [_i]),
+    "sv_timing_enable": (_i, [_i]),
+    "sv_timing_read": (_i, [_p, _i]),
 }
 
 
@@ -97,6 +101,25 @@ def _check(status: int, what: str):
 
 def sv_workspace_size(B: int, V: int, max_k: int, dtype: int) -> int:
     return int(_load().sv_workspace_size(B, V, max_k, dtype))
+
+
+def sv_timing_enable(slots: int) -> None:
+    """Record HIP events around the kernels of the next sv_spec_verify calls
+    (a ring of `slots` calls); 0 turns timing off."""
+    _check(_load().sv_timing_enable(int(slots)), "sv_timing_enable")
+
+
+def sv_timing_read(max_calls: int):
+    """Milliseconds per recorded call, oldest first: an array of shape
+    (calls, 2) holding the statistics kernel's and the verdict + draw
+    kernel's time.  Waits for the events and empties the ring."""
+    import numpy as np
+
+    out = np.zeros((max(int(max_calls), 0), 2), dtype=np.float32)
+    n = int(_load().sv_timing_read(ctypes.c_void_p(out.ctypes.data), int(max_calls)))
+    if n < 0:
+        _check(n, "sv_timing_read")
+    return out[:n]
 
 
 def sv_set_verify_kernel(kernel: int) -> int:

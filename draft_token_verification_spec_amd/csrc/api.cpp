@@ -31,6 +31,22 @@ int to_status(hipError_t e) { return e == hipSuccess ? SV_OK : SV_ERR_HIP; }
 
 int g_verify_kernel = SV_KERNEL_AUTO;  // accessed atomically
 
+// Benchmark timing (sv_timing_enable): a ring of three events per call.
+struct Timing {
+  hipEvent_t* ev = nullptr;
+  int slots = 0;
+  long calls = 0;  // calls recorded since the last read
+};
+Timing g_timing;
+
+// The next call's three events, or null when timing is off.
+const hipEvent_t* next_events() {
+  if (g_timing.slots == 0) return nullptr;
+  const int k = int(g_timing.calls % g_timing.slots);
+  ++g_timing.calls;
+  return g_timing.ev + 3 * k;
+}
+
 }  // namespace
 
 extern "C" {
@@ -101,9 +117,13 @@ int sv_spec_verify(void* stream, int B, int V, int max_k, int dtype, const void*
   a.parts = a.group = a.stride = 0;
   a.spin_limit = 0;
   const int kind = __atomic_load_n(&g_verify_kernel, __ATOMIC_RELAXED);
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
   hipError_t err = hipSuccess;
-  if (kind != SV_KERNEL_RESIDENT) return to_status(launch_streaming(a, dtype, static_cast<hipStream_t>(stream)));
-  if (!launch_verify(a, dtype, true, static_cast<hipStream_t>(stream), &err)) return SV_ERR_UNSUPPORTED;
+  if (kind != SV_KERNEL_RESIDENT) return to_status(launch_streaming(a, dtype, hs, next_events()));
+  if (!launch_verify(a, dtype, true, hs, &err, next_events())) {
+    if (g_timing.slots) --g_timing.calls;  // nothing recorded
+    return SV_ERR_UNSUPPORTED;
+  }
   return to_status(err);
 }
 
@@ -160,6 +180,45 @@ int sv_set_verify_kernel(int kernel) {
   if (kernel != SV_KERNEL_AUTO && kernel != SV_KERNEL_STREAMING && kernel != SV_KERNEL_RESIDENT)
     return SV_ERR_INVALID_ARG;
   return __atomic_exchange_n(&g_verify_kernel, kernel, __ATOMIC_RELAXED);
+}
+
+int sv_timing_enable(int slots) {
+  if (slots < 0) return SV_ERR_INVALID_ARG;
+  hipError_t err = hipSuccess;
+  for (int i = 0; i < 3 * g_timing.slots; ++i) {
+    const hipError_t e = hipEventDestroy(g_timing.ev[i]);
+    if (err == hipSuccess) err = e;
+  }
+  delete[] g_timing.ev;
+  g_timing = Timing{};
+  if (slots == 0) return to_status(err);
+  g_timing.ev = new hipEvent_t[3 * size_t(slots)];
+  for (int i = 0; i < 3 * slots; ++i) {
+    const hipError_t e = hipEventCreate(&g_timing.ev[i]);
+    if (e != hipSuccess) {
+      for (int j = 0; j < i; ++j) (void)hipEventDestroy(g_timing.ev[j]);
+      delete[] g_timing.ev;
+      g_timing = Timing{};
+      return SV_ERR_HIP;
+    }
+  }
+  g_timing.slots = slots;
+  return to_status(err);
+}
+
+int sv_timing_read(float* ms, int max_calls) {
+  if (!ms || max_calls < 0) return SV_ERR_INVALID_ARG;
+  const long rec = g_timing.calls < g_timing.slots ? g_timing.calls : g_timing.slots;
+  const int n = int(rec < max_calls ? rec : max_calls);
+  const long first = g_timing.calls - n;  // the last n calls, oldest first
+  for (int c = 0; c < n; ++c) {
+    const hipEvent_t* ev = g_timing.ev + 3 * int((first + c) % g_timing.slots);
+    if (hipEventSynchronize(ev[2]) != hipSuccess || hipEventElapsedTime(&ms[2 * c], ev[0], ev[1]) != hipSuccess ||
+        hipEventElapsedTime(&ms[2 * c + 1], ev[1], ev[2]) != hipSuccess)
+      return SV_ERR_HIP;
+  }
+  g_timing.calls = 0;
+  return n;
 }
 
 const char* sv_status_string(int status) {

@@ -1217,7 +1217,7 @@ int stats_stride(int max_k, int nseg, int nseg2) { return max_k * nseg2 + nseg; 
 #define SV_SAMPLE_LAG 2.0
 #endif
 
-bool launch_verify(VerifyArgs a, int dtype, bool hold, hipStream_t stream, hipError_t* err) {
+bool launch_verify(VerifyArgs a, int dtype, bool hold, hipStream_t stream, hipError_t* err, const hipEvent_t* ev) {
   const int cap = capacity(dtype, hold);
   if (cap <= 0) return false;
   a.stride = stats_stride(a.max_k, a.nseg, a.nseg2);
@@ -1242,6 +1242,7 @@ bool launch_verify(VerifyArgs a, int dtype, bool hold, hipStream_t stream, hipEr
   a.spin_limit = 1u << 20;
   const uint64_t all = per_part * uint64_t(parts);
   const unsigned grid = unsigned(all < uint64_t(cap) ? all : uint64_t(cap));
+  if (ev) (void)hipEventRecord(ev[0], stream);
   if (dtype == SV_BF16) {
     if (hold) hipLaunchKernelGGL((verify_kernel<uint16_t, true>), dim3(grid), dim3(kThreads), 0, stream, a);
     else hipLaunchKernelGGL((verify_kernel<uint16_t, false>), dim3(grid), dim3(kThreads), 0, stream, a);
@@ -1250,6 +1251,10 @@ bool launch_verify(VerifyArgs a, int dtype, bool hold, hipStream_t stream, hipEr
     else hipLaunchKernelGGL((verify_kernel<float, false>), dim3(grid), dim3(kThreads), 0, stream, a);
   }
   *err = hipGetLastError();
+  if (ev) {
+    (void)hipEventRecord(ev[1], stream);
+    (void)hipEventRecord(ev[2], stream);
+  }
   return true;
 }
 

@@ -675,19 +675,28 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 
 }  // namespace
 
-hipError_t launch_streaming(VerifyArgs a, int dtype, hipStream_t stream) {
+hipError_t launch_streaming(VerifyArgs a, int dtype, hipStream_t stream, const hipEvent_t* ev) {
   const uint64_t n1 = uint64_t(a.B) * uint64_t(a.R) * uint64_t(a.nseg2);
   const uint64_t n2 = uint64_t(a.B) * uint64_t(a.nseg2);
-  if (n1 == 0) return hipSuccess;
+  if (n1 == 0) {
+    if (ev)
+      for (int k = 0; k < 3; ++k) (void)hipEventRecord(ev[k], stream);
+    return hipSuccess;
+  }
   if (n1 >= (uint64_t(1) << 31)) return hipErrorInvalidValue;
   a.spin_limit = 1u << 18;  // a fraction of a second of polling: reached only if dispatch order were broken
-  if (dtype == SV_BF16) {
+  const bool bf = dtype == SV_BF16;
+  if (ev) (void)hipEventRecord(ev[0], stream);
+  if (bf)
     hipLaunchKernelGGL(stats_kernel<uint16_t>, dim3(unsigned(n1)), dim3(kThreads), 0, stream, a);
-    hipLaunchKernelGGL(draw_kernel<uint16_t>, dim3(unsigned(n2)), dim3(kThreads), 0, stream, a);
-  } else {
+  else
     hipLaunchKernelGGL(stats_kernel<float>, dim3(unsigned(n1)), dim3(kThreads), 0, stream, a);
+  if (ev) (void)hipEventRecord(ev[1], stream);
+  if (bf)
+    hipLaunchKernelGGL(draw_kernel<uint16_t>, dim3(unsigned(n2)), dim3(kThreads), 0, stream, a);
+  else
     hipLaunchKernelGGL(draw_kernel<float>, dim3(unsigned(n2)), dim3(kThreads), 0, stream, a);
-  }
+  if (ev) (void)hipEventRecord(ev[2], stream);
   return hipGetLastError();
 }
 

@@ -221,14 +221,15 @@ struct ScoreArgs {
   Partial* partials;
 };
 
-// Streaming kernel: any supported size.
-hipError_t launch_spec_verify(VerifyArgs a, int dtype, hipStream_t stream);
 // Verification kernel, register-resident (hold) or streaming: returns false
 // (nothing launched) if the sizes do not fit it; otherwise launches and
-// stores the launch status in *err.
-bool launch_verify(VerifyArgs a, int dtype, bool hold, hipStream_t stream, hipError_t* err);
-// The two streaming kernels (statistics, then the draw).
-hipError_t launch_streaming(VerifyArgs a, int dtype, hipStream_t stream);
+// stores the launch status in *err.  `ev` (nullable): three events to record
+// before the kernel, after it, and after it again (an empty second phase).
+bool launch_verify(VerifyArgs a, int dtype, bool hold, hipStream_t stream, hipError_t* err,
+                   const hipEvent_t* ev = nullptr);
+// The two streaming kernels (statistics, then the verdict and the draw).
+// `ev` (nullable): three events to record before, between and after them.
+hipError_t launch_streaming(VerifyArgs a, int dtype, hipStream_t stream, const hipEvent_t* ev = nullptr);
 hipError_t launch_av_score(const ScoreArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_av_fit(int B, int max_k, const float* feature, const int8_t* labels,
                          float* params, double* accum, float damping_c, float ridge,

@@ -213,6 +213,23 @@ typedef enum {
 
 int sv_set_verify_kernel(int kernel);
 
+/* Kernel timing for benchmarks (a measurement aid, not part of the method).
+ * sv_timing_enable(slots) with slots > 0 makes every later sv_spec_verify
+ * record three HIP events on its stream: before its first kernel, between
+ * the statistics kernel and the verdict + draw kernel, and after its last
+ * kernel, into a ring of `slots` records (the resident kernel records its
+ * one kernel as phase 0 and an empty phase 1).  slots = 0 turns timing off
+ * and destroys the events.  The events are created here (no device memory is
+ * allocated); calls from several host threads at once are not supported
+ * while timing is on.
+ * sv_timing_read(ms, max_calls) waits for the recorded events and writes,
+ * for the last min(recorded, slots, max_calls) calls in call order, the
+ * milliseconds of phase 0 at ms[2c] and of phase 1 at ms[2c + 1]; it then
+ * empties the ring.  Returns the number of calls written, or a negative
+ * sv_status (SV_ERR_HIP if an event query failed). */
+int sv_timing_enable(int slots);
+int sv_timing_read(float* ms, int max_calls);
+
 /* Static description of a status code. */
 const char* sv_status_string(int status);
 

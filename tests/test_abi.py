@@ -24,7 +24,7 @@ def declared_functions():
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
     assert set(names) == {"sv_workspace_size", "sv_spec_verify", "sv_av_score", "sv_av_fit_step",
-                          "sv_status_string", "sv_set_verify_kernel"}
+                          "sv_status_string", "sv_set_verify_kernel", "sv_timing_enable", "sv_timing_read"}
     lib = ctypes.CDLL(sv.lib_path())
     for n in names:
         assert hasattr(lib, n), n
@@ -47,6 +47,14 @@ def test_kernel_selector():
     with pytest.raises(RuntimeError):
         sv.sv_set_verify_kernel(7)
     assert sv.sv_set_verify_kernel(sv.SV_KERNEL_AUTO) == sv.SV_KERNEL_RESIDENT
+
+
+def test_timing_without_events():
+    # no events exist: turning timing off and reading touch no device
+    sv.sv_timing_enable(0)
+    assert sv.sv_timing_read(4).shape == (0, 2)
+    with pytest.raises(RuntimeError):
+        sv.sv_timing_enable(-1)
 
 
 def test_status_strings():
