@@ -184,9 +184,13 @@ __device__ __forceinline__ Partial block_reduce(Partial p, float c, Partial* lds
   return p;
 }
 
-// Slot of request b's segment s weight (uint64, see WsLayout::tagged).
-__device__ __forceinline__ uint64_t* weight_slot(const VerifyArgs& a, int b, int s) {
-  return a.tagged + size_t(b) * a.nseg2 + s;
+// Slot of request b's slice q of the draw rows (slice q: vector q % kNV of
+// segment q / kNV), see WsLayout::tagged.
+static_assert(kNV == kDrawSlices, "one weight slot per vector of a draw segment");
+constexpr int kMaxDrawSegs = 256;  // 32 KiB segments of the longest row: 2^21 fp32 elements
+static_assert(int64_t(SV_MAX_V) * 4 / kHalfBytes <= kMaxDrawSegs, "draw segments per row");
+__device__ __forceinline__ uint64_t* weight_slot(const VerifyArgs& a, int b, int q) {
+  return a.tagged + (size_t(b) * a.nseg2) * kNV + q;
 }
 
 // ---------------------------------------------------------------------------
@@ -262,7 +266,7 @@ struct DrawShared {
   float wt[kWaves];
   float sw[kWaves][kNV];
   int wi[2 * kWaves];
-  float cum[256];
+  float cum[kDrawSlices * kMaxDrawSegs];  // running slice weights
   float chunk[kMaxChunks];
   int li[4];
   Partial red[kWaves];
@@ -281,135 +285,45 @@ __device__ __forceinline__ float elem_w(const uint4& zt, const uint4& zd, int j,
   return pt;
 }
 
-// Total weight of the segment (same value in every thread).
+// Weights of the segment's kNV slices (slice k: vector k of every thread, a
+// contiguous kThreads * N elements), handed off to the request's search in
+// slots[0 .. kNV-1].  Each slice's sum takes the same order in every call.
 template <typename ET, bool RESID>
-__device__ __forceinline__ float seg_weight(const uint4 (&t)[kNV], const uint4 (&d)[kNV], float c, float kt, float kd,
-                                            DrawShared& sh, int tid) {
-  constexpr int N = Elem<ET>::N;
-  float ls = 0.f;
-#pragma unroll
-  for (int k = 0; k < kNV; ++k)
-#pragma unroll
-    for (int j = 0; j < N; ++j) ls += elem_w<ET, RESID>(t[k], d[k], j, c, kt, kd);
-  ls = wave_sum(ls);
-  if ((tid & 63) == 0) sh.wt[tid >> 6] = ls;
-  __syncthreads();
-  float W = sh.wt[0];
-  for (int x = 1; x < kWaves; ++x) W += sh.wt[x];
-  __syncthreads();
-  return W;
-}
-
-// First element of the segment (starting at hb) whose running weight from
-// `before` exceeds t; if none (rounding, or `fallback`), the segment's last
-// positive-weight element.  The same value in every thread.
-template <typename ET, bool RESID>
-__device__ __forceinline__ int seg_search(uint4 (&t)[kNV], uint4 (&d)[kNV], int hb, float c, float kt, float kd,
-                                          float before, float thr, bool fallback, DrawShared& sh, int tid) {
+__device__ __forceinline__ void slice_weights(const uint4 (&t)[kNV], const uint4 (&d)[kNV], float c, float kt,
+                                              float kd, uint64_t* slots, DrawShared& sh, int tid) {
   constexpr int N = Elem<ET>::N;
   const int wave = tid >> 6, lane = tid & 63;
-  float r[kNV];
 #pragma unroll
   for (int k = 0; k < kNV; ++k) {
-    r[k] = 0.f;
+    float r = 0.f;
 #pragma unroll
-    for (int j = 0; j < N; ++j) r[k] += elem_w<ET, RESID>(t[k], d[k], j, c, kt, kd);
-  }
-#pragma unroll
-  for (int k = 0; k < kNV; ++k) {
-    const float x = wave_sum(r[k]);
-    if (lane == 0) sh.sw[wave][k] = x;
+    for (int j = 0; j < N; ++j) r += elem_w<ET, RESID>(t[k], d[k], j, c, kt, kd);
+    r = wave_sum(r);
+    if (lane == 0) sh.sw[wave][k] = r;
   }
   __syncthreads();
-  int J = -1;
-  float run = before, runJ = before;
-  if (!fallback) {
-#pragma unroll
-    for (int k = 0; k < kNV; ++k) {
-      float Tk = sh.sw[0][k];
-      for (int x = 1; x < kWaves; ++x) Tk += sh.sw[x][k];
-      if (J < 0) {
-        if (run + Tk > thr) {
-          J = k;
-          runJ = run;
-        } else {
-          run += Tk;
-        }
-      }
-    }
+  if (tid < kNV) {
+    float W = sh.sw[0][tid];
+    for (int x = 1; x < kWaves; ++x) W += sh.sw[x][tid];
+    put_slot(slots + tid, __float_as_uint(W));
   }
-  int result = -1;
-  if (J >= 0) {
-    float vJ = 0.f;
-    uint4 zt = {0u, 0u, 0u, 0u}, zd = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int k = 0; k < kNV; ++k)
-      if (k == J) {
-        vJ = r[k];
-        zt = t[k];
-        zd = d[k];
-      }
-    keep_raw(zt);
-    keep_raw(zd);
-    const float incl = wave_inclusive_scan(vJ, lane);
-    if (lane == 63) sh.wt[wave] = incl;
-    float excl = __shfl_up(incl, 1, 64);
-    if (lane == 0) excl = 0.f;
-    __syncthreads();
-    float wb = runJ;
-    for (int x = 0; x < wave; ++x) wb += sh.wt[x];
-    const float b0 = wb + excl;
-    int mine = -1;
-    float pre = 0.f;
-#pragma unroll
-    for (int j = 0; j < N; ++j) {
-      const float wj = elem_w<ET, RESID>(zt, zd, j, c, kt, kd);
-      pre += wj;
-      if (mine < 0 && wj > 0.f && b0 + pre > thr) mine = hb + (J * kThreads + tid) * N + j;
-    }
-    const unsigned long long hit = __ballot(mine >= 0);
-    const int found = hit ? __shfl(mine, __ffsll(static_cast<long long>(hit)) - 1, 64) : -1;
-    if (lane == 0) sh.wi[wave] = found;
-    __syncthreads();
-    for (int x = 0; x < kWaves && result < 0; ++x)
-      if (sh.wi[x] >= 0) result = sh.wi[x];
-  }
-  result = uniform(result);
-  if (result < 0) {
-    fence_regs(t);
-    fence_regs(d);
-    int last = -1;
-#pragma unroll
-    for (int k = 0; k < kNV; ++k)
-#pragma unroll
-      for (int j = 0; j < N; ++j)
-        if (elem_w<ET, RESID>(t[k], d[k], j, c, kt, kd) > 0.f) last = hb + (k * kThreads + tid) * N + j;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) last = max(last, __shfl_xor(last, o, 64));
-    __syncthreads();
-    if (lane == 0) sh.wi[kWaves + wave] = last;
-    __syncthreads();
-    result = sh.wi[kWaves];
-    for (int x = 1; x < kWaves; ++x) result = max(result, sh.wi[kWaves + x]);
-    result = uniform(result);
-  }
-  __syncthreads();
-  return result;
 }
 
-// The last segment collects the other segments' weights (its own is `own`)
-// and scans them: Z, the crossing segment k (-1 if Z is not positive), the
-// weight before it, u * Z.
-__device__ __forceinline__ void scan_weights(const VerifyArgs& a, int b, float own, int n, float u, DrawShared& sh,
-                                             int tid) {
+// Collect the m slice weights of request b, in token order, and scan them:
+// the crossing slice k (the first whose running weight exceeds u * Z; -1 if
+// Z is not positive; if rounding leaves u * Z at or above the last running
+// weight, the last slice with positive weight, flagged), the weight before
+// it, u * Z.
+__device__ __forceinline__ void scan_slices(const VerifyArgs& a, int b, int m, float u, DrawShared& sh, int tid) {
   const int lane = tid & 63;
   if (tid < 64) {
+    const uint64_t* slots = weight_slot(a, b, 0);
     float carry = 0.f;
-    for (int base = 0; base < n; base += 64) {
+    for (int base = 0; base < m; base += 64) {
       const int q = base + lane;
-      float x = (q < n - 1) ? __uint_as_float(take_slot(weight_slot(a, b, q), a)) : (q == n - 1 ? own : 0.f);
+      float x = (q < m) ? __uint_as_float(take_slot(const_cast<uint64_t*>(slots) + q, a)) : 0.f;
       x = wave_inclusive_scan(x, lane) + carry;
-      if (base + lane < n) sh.cum[base + lane] = x;
+      if (q < m) sh.cum[q] = x;
       carry = __shfl(x, 63, 64);
     }
     if (lane == 0) {
@@ -418,7 +332,7 @@ __device__ __forceinline__ void scan_weights(const VerifyArgs& a, int b, float o
       float thr = 0.f;
       if (Z > 0.f) {
         thr = u * Z;
-        int lo = 0, hi = n;  // first k with cum[k] > thr
+        int lo = 0, hi = m;  // first k with cum[k] > thr
         while (lo < hi) {
           const int mid = (lo + hi) >> 1;
           if (sh.cum[mid] > thr)
@@ -427,8 +341,8 @@ __device__ __forceinline__ void scan_weights(const VerifyArgs& a, int b, float o
             lo = mid + 1;
         }
         k = lo;
-        if (k == n) {  // rounding: the last segment with positive weight
-          k = n - 1;
+        if (k == m) {
+          k = m - 1;
           while (k > 0 && !(sh.cum[k] > sh.cum[k - 1])) --k;
           fb = 1;
         }
@@ -442,71 +356,121 @@ __device__ __forceinline__ void scan_weights(const VerifyArgs& a, int b, float o
   __syncthreads();
 }
 
+// Within one slice (thread t holds elements first + t*N .. + N-1): the first
+// element whose running weight from `before` exceeds thr; if none (rounding,
+// or `fallback`), the slice's last positive-weight element.  The same value
+// in every thread.
 template <typename ET, bool RESID>
-__device__ __forceinline__ void draw_segment(const VerifyArgs& a, DrawShared& sh, int b, int s, int aa, float c,
-                                             float kt, float kd, float u, const ET* rt, const ET* rd, int tid) {
+__device__ __forceinline__ int slice_search(const ET* rt, const ET* rd, int first, int V, float c, float kt, float kd,
+                                            float before, float thr, bool fallback, DrawShared& sh, int tid) {
+  constexpr int N = Elem<ET>::N;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int e0 = first + tid * N;
+  const uint4 zt = load_raw<ET>(rt, e0, V, is_aligned16(rt));
+  const uint4 zd = RESID ? load_raw<ET>(rd, e0, V, is_aligned16(rd)) : zt;
+  float w[N], vt = 0.f;
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    w[j] = elem_w<ET, RESID>(zt, zd, j, c, kt, kd);
+    vt += w[j];
+  }
+  const float incl = wave_inclusive_scan(vt, lane);
+  if (lane == 63) sh.wt[wave] = incl;
+  float excl = __shfl_up(incl, 1, 64);
+  if (lane == 0) excl = 0.f;
+  __syncthreads();
+  float run = before + excl;
+  for (int x = 0; x < wave; ++x) run += sh.wt[x];
+  int mine = -1, last = -1;
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    run += w[j];
+    if (w[j] > 0.f) {
+      last = e0 + j;
+      if (mine < 0 && !fallback && run > thr) mine = e0 + j;
+    }
+  }
+  const unsigned long long hit = __ballot(mine >= 0);
+  const int found = hit ? __shfl(mine, __ffsll(static_cast<long long>(hit)) - 1, 64) : -1;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) last = max(last, __shfl_xor(last, o, 64));
+  if (lane == 0) {
+    sh.wi[wave] = found;
+    sh.wi[kWaves + wave] = last;
+  }
+  __syncthreads();
+  int result = -1, lastall = -1;
+  for (int x = 0; x < kWaves; ++x) {
+    if (result < 0) result = sh.wi[x];
+    lastall = max(lastall, sh.wi[kWaves + x]);
+  }
+  __syncthreads();
+  return uniform(result >= 0 ? result : lastall);
+}
+
+// Weights of segment s of the draw rows, handed off to the request's search.
+template <typename ET, bool RESID>
+__device__ __forceinline__ void weight_segment(const VerifyArgs& a, DrawShared& sh, int b, int s, float c, float kt,
+                                               float kd, const ET* rt, const ET* rd, int tid) {
   constexpr int E = kThreads * kNV * Elem<ET>::N;
   uint4 t[kNV], d[kNV];
   load_seg<ET>(rt, s * E, a.V, t, tid);
   if (RESID) load_seg<ET>(rd, s * E, a.V, d, tid);
-  const float W = seg_weight<ET, RESID>(t, d, c, kt, kd, sh, tid);
-  if (s < a.nseg2 - 1) {
-    if (tid == 0) put_slot(weight_slot(a, b, s), __float_as_uint(W));
-    return;
-  }
-  scan_weights(a, b, W, a.nseg2, u, sh, tid);
+  slice_weights<ET, RESID>(t, d, c, kt, kd, weight_slot(a, b, s * kNV), sh, tid);
+}
+
+// The draw of request b once its slices' weights are in: scan them, read the
+// crossing slice again and search it.
+template <typename ET, bool RESID>
+__device__ __forceinline__ void search_request(const VerifyArgs& a, DrawShared& sh, int b, int aa, float c, float kt,
+                                               float kd, float u, const ET* rt, const ET* rd, int tid) {
+  constexpr int EV = kThreads * Elem<ET>::N;  // elements per slice
+  scan_slices(a, b, a.nseg2 * kNV, u, sh, tid);
   const int k = uniform(sh.fk);
   int tok = -1;
   if (k < 0) {
     // the residual has no mass (reachable only through rounding): draw from pt itself
     if (RESID) tok = cdf_sample<ET, false>(rt, c, kt, rt, c, kt, a.V, u, sh.chunk, sh.li);
   } else {
-    if (k != s) {
-      load_seg<ET>(rt, k * E, a.V, t, tid);
-      if (RESID) load_seg<ET>(rd, k * E, a.V, d, tid);
-    }
-    tok = seg_search<ET, RESID>(t, d, k * E, c, kt, kd, uniform(sh.fb4), uniform(sh.ft), uniform(sh.ffb) != 0, sh, tid);
+    tok = slice_search<ET, RESID>(rt, rd, k * EV, a.V, c, kt, kd, uniform(sh.fb4), uniform(sh.ft), uniform(sh.ffb) != 0,
+                                  sh, tid);
   }
   if (tid == 0) a.out_tokens[size_t(b) * (a.max_k + 1) + aa] = tok;
 }
 
-// Row slot of the q-th row the verdict merges: draft rows 0..nd-1, then
-// target rows 0..K.
-__device__ __forceinline__ int row_slot(int q, int nd, int max_k) { return q < nd ? q : max_k + (q - nd); }
-
-// Merge the segment statistics of every row the request read into sh.row.
-// Wave w takes rows w, w + kWaves, ... (kRowsPerPass of them per pass, their
-// loads in flight together); lane l takes segments l, l + 64, ... in order,
-// and a butterfly combines the lanes.  Every workgroup of the request
-// evaluates the same function of the same data, so all reach the same
-// statistics.
-__device__ __forceinline__ void merge_rows(const VerifyArgs& a, DrawShared& sh, int b, int K, int nd, bool greedy,
-                                           float c, int tid) {
+// Merge the segment statistics of the request's rows into sh.row, by row
+// slot (draft i at i, target j at max_k + j; slots of rows the statistics
+// kernel skipped hold stale values that nothing reads).  The loads do not
+// wait for the request's scalars.  Wave w takes slots w, w + kWaves, ...
+// (kRowsPerPass of them per pass, their loads in flight together); lane l
+// takes segments l, l + 64, ... in order, and a butterfly combines the lanes.
+// Every workgroup of the request evaluates the same function of the same
+// data, so all reach the same statistics.
+__device__ __forceinline__ void merge_rows(const VerifyArgs& a, DrawShared& sh, int b, bool greedy, float c,
+                                           int tid) {
   const int wave = tid >> 6, lane = tid & 63;
-  const int n = a.nseg2, max_k = a.max_k;
-  const int nrows = nd + K + 1;
-  const Partial* base = a.partials + size_t(b) * a.R * n;
+  const int n = a.nseg2, max_k = a.max_k, R = a.R;
+  const Partial* base = a.partials + size_t(b) * R * n;
   const Partial none{-INFINITY, 0.f, 0.f, 0x7fffffff};
-  for (int q0 = wave; q0 < nrows; q0 += kWaves * kRowsPerPass) {
+  for (int q0 = wave; q0 < R; q0 += kWaves * kRowsPerPass) {
     Partial acc[kRowsPerPass];
     float z[kRowsPerPass];
 #pragma unroll
     for (int r = 0; r < kRowsPerPass; ++r) {
       const int q = q0 + r * kWaves;
-      const bool test = (q < nd ? q : q - nd) < K;  // a row of a tested position
       acc[r] = none;
-      z[r] = (q < nrows && lane == 0 && test && !greedy) ? a.zval[size_t(b) * a.R + row_slot(q, nd, max_k)] : NAN;
+      z[r] = (q < R && lane == 0) ? a.zval[size_t(b) * R + q] : NAN;
     }
     for (int s0 = 0; s0 < n; s0 += 64) {
       Partial p[kRowsPerPass];
 #pragma unroll
       for (int r = 0; r < kRowsPerPass; ++r) {
         const int q = q0 + r * kWaves;
-        p[r] = (q < nrows && s0 + lane < n) ? base[size_t(row_slot(q, nd, max_k)) * n + s0 + lane] : none;
+        p[r] = (q < R && s0 + lane < n) ? base[size_t(q) * n + s0 + lane] : none;
       }
 #pragma unroll
       for (int r = 0; r < kRowsPerPass; ++r) {
-        if (greedy && q0 + r * kWaves >= nd)
+        if (greedy && q0 + r * kWaves >= max_k)
           merge_argmax(acc[r].m, acc[r].idx, p[r].m, p[r].idx);
         else
           merge_ms(acc[r].m, acc[r].s, acc[r].cnt, p[r].m, p[r].s, p[r].cnt, c);
@@ -515,7 +479,7 @@ __device__ __forceinline__ void merge_rows(const VerifyArgs& a, DrawShared& sh, 
 #pragma unroll
     for (int r = 0; r < kRowsPerPass; ++r) {
       const int q = q0 + r * kWaves;
-      const bool amax = greedy && q >= nd;
+      const bool amax = greedy && q >= max_k;
 #pragma unroll
       for (int o = 32; o >= 1; o >>= 1) {
         Partial x;
@@ -528,7 +492,7 @@ __device__ __forceinline__ void merge_rows(const VerifyArgs& a, DrawShared& sh, 
         else
           merge_ms(acc[r].m, acc[r].s, acc[r].cnt, x.m, x.s, x.cnt, c);
       }
-      if (lane == 0 && q < nrows) sh.row[row_slot(q, nd, max_k)] = RowStat{acc[r].m, acc[r].s + acc[r].cnt, acc[r].idx, z[r]};
+      if (lane == 0 && q < R) sh.row[q] = RowStat{acc[r].m, acc[r].s + acc[r].cnt, acc[r].idx, z[r]};
     }
   }
   __syncthreads();
@@ -581,16 +545,19 @@ __device__ __forceinline__ void confident_feature(const VerifyArgs& a, DrawShare
   __syncthreads();
 }
 
-// Workgroup = segment s of the draw rows of request b (requests in reverse
-// order: the last ones read by the statistics kernel are the likeliest to be
-// cached).
+// Workgroups 0 .. B*n-1: segment s of the draw rows of request b (weights);
+// then one search workgroup per request.  Requests in reverse order (the last
+// ones read by the statistics kernel are the likeliest to be cached); every
+// workgroup derives its request's verdict first.
 template <typename ET>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void draw_kernel(VerifyArgs a) {
   __shared__ DrawShared sh;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n = a.nseg2, max_k = a.max_k;
-  const int s = int(blockIdx.x % uint32_t(n));
-  const int b = a.B - 1 - int(blockIdx.x / uint32_t(n));
+  const uint32_t nw = uint32_t(a.B) * uint32_t(n);
+  const bool search = blockIdx.x >= nw;
+  const int s = search ? -1 : int(blockIdx.x % uint32_t(n));
+  const int b = a.B - 1 - int(search ? blockIdx.x - nw : blockIdx.x / uint32_t(n));
   const int kraw = a.num_draft[b];
   const float T = a.temperature[b];
   const int K = min(max(kraw, 0), max_k);
@@ -603,9 +570,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   float ul = 0.f;
   if (wave == 0 && lane < K) {
     dl = a.tokens[size_t(b) * max_k + lane];
-    if (!greedy) ul = a.u_accept[size_t(b) * max_k + lane];
+    ul = a.u_accept[size_t(b) * max_k + lane];
   }
-  merge_rows(a, sh, b, K, nd, greedy, c, tid);
+  merge_rows(a, sh, b, greedy, c, tid);
 
   // the accept tests, and the accept length a: the first rejection, else K
   float pd = NAN, pt = NAN;
@@ -630,9 +597,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   }
   __syncthreads();
   const int aa = uniform(sh.word);
+  const bool resid = aa < K;
+  const float u = greedy ? 0.f : (resid ? a.u_residual[b] : a.u_bonus[b]);
+  const ET* rt = static_cast<const ET*>(a.target) + (a.target_start[b] + aa) * a.target_stride;
+  const ET* rd = resid ? static_cast<const ET*>(a.draft) + (a.draft_start[b] + aa) * a.draft_stride : rt;
+  const RowStat tr = sh.row[max_k + aa];
+  const RowStat dr = sh.row[resid ? aa : max_k + aa];
+  const float kt = tr.m * c + fast_log2(tr.s);
+  const float kd = dr.m * c + fast_log2(dr.s);
+
+  if (search) {
+    if (greedy) return;
+    if (resid)
+      search_request<ET, true>(a, sh, b, aa, c, kt, kd, u, rt, rd, tid);
+    else
+      search_request<ET, false>(a, sh, b, aa, c, kt, kd, u, rt, rd, tid);
+    return;
+  }
 
   // the request's outputs, by its first workgroup (the token at a of a
-  // stochastic request comes from the draw)
+  // stochastic request comes from the search)
   if (s == 0 && wave == 0) {
     const int j = lane;
     if (j < max_k) {
@@ -649,35 +633,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     if (j <= max_k && j != aa) a.out_tokens[size_t(b) * (max_k + 1) + j] = (j < aa) ? dl : -1;
     if (j == 0) {
       a.accept_len[b] = aa;
-      if (greedy) a.out_tokens[size_t(b) * (max_k + 1) + aa] = sh.row[max_k + aa].idx;
+      if (greedy) a.out_tokens[size_t(b) * (max_k + 1) + aa] = tr.idx;
     }
+  }
+  if (!greedy) {
+    if (resid)
+      weight_segment<ET, true>(a, sh, b, s, c, kt, kd, rt, rd, tid);
+    else
+      weight_segment<ET, false>(a, sh, b, s, c, kt, kd, rt, rd, tid);
   }
   // features of confident draft rows: position i by the workgroup of segment i mod n
   if (want_feat)
     for (int i = s; i < nd; i += n)
       if (sh.row[i].s < kRecomputeBelow) confident_feature<ET>(a, sh, b, i, c, tid);
-
-  if (greedy) return;
-  const bool resid = aa < K;
-  const RowStat tr = sh.row[max_k + aa];
-  const RowStat dr = sh.row[resid ? aa : 0];
-  const float kt = tr.m * c + fast_log2(tr.s);
-  const float kd = resid ? dr.m * c + fast_log2(dr.s) : 0.f;
-  const float u = resid ? a.u_residual[b] : a.u_bonus[b];
-  const ET* rt = static_cast<const ET*>(a.target) + (a.target_start[b] + aa) * a.target_stride;
-  if (resid) {
-    const ET* rd = static_cast<const ET*>(a.draft) + (a.draft_start[b] + aa) * a.draft_stride;
-    draw_segment<ET, true>(a, sh, b, s, aa, c, kt, kd, u, rt, rd, tid);
-  } else {
-    draw_segment<ET, false>(a, sh, b, s, aa, c, kt, kd, u, rt, rt, tid);
-  }
 }
 
 }  // namespace
 
 hipError_t launch_streaming(VerifyArgs a, int dtype, hipStream_t stream, const hipEvent_t* ev) {
   const uint64_t n1 = uint64_t(a.B) * uint64_t(a.R) * uint64_t(a.nseg2);
-  const uint64_t n2 = uint64_t(a.B) * uint64_t(a.nseg2);
+  const uint64_t n2 = uint64_t(a.B) * uint64_t(a.nseg2 + 1);  // weight workgroups, then one search per request
   if (n1 == 0) {
     if (ev)
       for (int k = 0; k < 3; ++k) (void)hipEventRecord(ev[k], stream);

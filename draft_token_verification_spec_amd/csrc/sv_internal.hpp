@@ -28,6 +28,9 @@ constexpr int kSampleSegBytes = kWaves * kGroup * 64 * 16;
 constexpr int kHalfVecs = kVecsPerThread / 2;
 constexpr int kHalfBytes = kThreads * kHalfVecs * 16;
 static_assert(kHalfBytes == kSampleSegBytes, "half segments are the sampling segments");
+// The draw's weights are handed off per slice: one 16-byte vector of every
+// thread of a 32 KiB draw segment, kDrawSlices slices per segment.
+constexpr int kDrawSlices = kHalfVecs;
 
 __host__ __device__ constexpr int elems_per_vec(int dtype) { return dtype == SV_BF16 ? 8 : 4; }
 __host__ __device__ constexpr int seg_elems(int dtype) { return kSegBytes / (dtype == SV_BF16 ? 2 : 4); }
@@ -137,7 +140,7 @@ struct WsLayout {
   size_t records;   // Record [B]
   size_t segsum;    // float [2][B][nseg2]  weight of each sampling segment (per draw round)
   size_t rowrec;    // RowRec [B][max_k + 1]
-  size_t tagged;    // uint64 [B][nseg2]  hand-off slots of the draw's segment weights
+  size_t tagged;    // uint64 [B][nseg2][kDrawSlices]  hand-off slots of the draw's slice weights
   size_t total;
   int nseg;   // 64 KiB statistics segments per row
   int nseg2;  // 32 KiB half segments per row (partials are strided by this)
@@ -160,7 +163,7 @@ inline WsLayout ws_layout(int B, int V, int max_k, int dtype) {
   L.segsum = L.records + align256(size_t(B) * sizeof(Record));
   L.rowrec = L.segsum + align256(2 * size_t(B) * L.nseg2 * 4);
   L.tagged = L.rowrec + align256(size_t(B) * (max_k + 1) * sizeof(RowRec));
-  L.total = L.tagged + align256(size_t(B) * L.nseg2 * 8);
+  L.total = L.tagged + align256(size_t(B) * L.nseg2 * kDrawSlices * 8);
   return L;
 }
 
