@@ -558,8 +558,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   const bool search = blockIdx.x >= nw;
   const int s = search ? -1 : int(blockIdx.x % uint32_t(n));
   const int b = a.B - 1 - int(search ? blockIdx.x - nw : blockIdx.x / uint32_t(n));
+  // every scalar of the request in one round trip, with the merge's loads
   const int kraw = a.num_draft[b];
   const float T = a.temperature[b];
+  const int64_t ts = a.target_start[b];
+  const int64_t ds = max_k > 0 ? a.draft_start[b] : 0;
+  const float ures = a.u_residual[b], ubon = a.u_bonus[b];
   const int K = min(max(kraw, 0), max_k);
   const bool greedy = !(T > 0.f);
   const bool want_feat = a.av_feature != nullptr;
@@ -598,9 +602,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   __syncthreads();
   const int aa = uniform(sh.word);
   const bool resid = aa < K;
-  const float u = greedy ? 0.f : (resid ? a.u_residual[b] : a.u_bonus[b]);
-  const ET* rt = static_cast<const ET*>(a.target) + (a.target_start[b] + aa) * a.target_stride;
-  const ET* rd = resid ? static_cast<const ET*>(a.draft) + (a.draft_start[b] + aa) * a.draft_stride : rt;
+  const float u = resid ? ures : ubon;
+  const ET* rt = static_cast<const ET*>(a.target) + (ts + aa) * a.target_stride;
+  const ET* rd = resid ? static_cast<const ET*>(a.draft) + (ds + aa) * a.draft_stride : rt;
   const RowStat tr = sh.row[max_k + aa];
   const RowStat dr = sh.row[resid ? aa : max_k + aa];
   const float kt = tr.m * c + fast_log2(tr.s);
