@@ -21,8 +21,10 @@ bool dtype_ok(int dtype) { return dtype == SV_F32 || dtype == SV_BF16; }
 int check_sizes(int B, int V, int max_k, int dtype) {
   if (B < 0 || V < 1 || max_k < 0 || !dtype_ok(dtype)) return SV_ERR_INVALID_ARG;
   if (max_k > SV_MAX_K || V > SV_MAX_V || B > SV_MAX_B) return SV_ERR_UNSUPPORTED;
-  const uint64_t items = uint64_t(B) * (uint64_t(rows_per_request(max_k)) * num_segments(V, dtype) +
-                                        uint64_t(num_sample_segments(V, dtype)));
+  // a bound on the largest grid: the streaming kernels' statistics, weight and
+  // search workgroups (32 KiB segments)
+  const uint64_t n2 = uint64_t(num_sample_segments(V, dtype));
+  const uint64_t items = uint64_t(B) * (uint64_t(rows_per_request(max_k)) * n2 + n2 + 1);
   if (items > kMaxItems || items > kMaxGrid) return SV_ERR_UNSUPPORTED;
   return SV_OK;
 }
