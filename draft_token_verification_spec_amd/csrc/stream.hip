@@ -81,14 +81,16 @@ __device__ __forceinline__ int fresh_tid() {
 
 // Vector k of thread t holds elements hb + (k * kThreads + t) * N .. + N-1 of
 // its row (token order: vector, thread, element); past the end: -inf.
-template <typename ET>
-__device__ __forceinline__ void load_seg(const ET* row, int hb, int V, uint4 (&v)[kNV], int) {
+// load_vecs loads vectors K0 .. K0 + NV - 1 of the segment at hb.
+template <typename ET, int NV, int K0>
+__device__ __forceinline__ void load_vecs(const ET* row, int hb0, int V, uint4 (&v)[NV]) {
   constexpr int N = Elem<ET>::N;
   const int tid = fresh_tid();
   const bool al = is_aligned16(row);
-  if (al && hb + kThreads * kNV * N <= V) {
+  const int hb = hb0 + K0 * kThreads * N;
+  if (al && hb + kThreads * NV * N <= V) {
 #pragma unroll
-    for (int k = 0; k < kNV; ++k) v[k] = load_vec16<ET>(row + hb + (k * kThreads + tid) * N);
+    for (int k = 0; k < NV; ++k) v[k] = load_vec16<ET>(row + hb + (k * kThreads + tid) * N);
   } else if (al && V % N == 0) {
     // the tail of an aligned row: each vector is wholly inside or wholly past
     // the end.  Every lane loads (the row's last vector standing in for one
@@ -96,10 +98,10 @@ __device__ __forceinline__ void load_seg(const ET* row, int hb, int V, uint4 (&v
     // so the loads are issued back to back instead of one branch at a time.
     constexpr uint32_t ninf = N == 8 ? (Elem<ET>::kNegInf << 16 | Elem<ET>::kNegInf) : Elem<ET>::kNegInf;
 #pragma unroll
-    for (int k = 0; k < kNV; ++k) v[k] = load_vec16<ET>(row + min(hb + (k * kThreads + tid) * N, V - N));
+    for (int k = 0; k < NV; ++k) v[k] = load_vec16<ET>(row + min(hb + (k * kThreads + tid) * N, V - N));
     const int t = fresh_tid(), lim = (V - hb) / N;  // vectors of the tail
 #pragma unroll
-    for (int k = 0; k < kNV; ++k) {
+    for (int k = 0; k < NV; ++k) {
       const bool in = k * kThreads + t < lim;
       v[k].x = in ? v[k].x : ninf;
       v[k].y = in ? v[k].y : ninf;
@@ -108,8 +110,13 @@ __device__ __forceinline__ void load_seg(const ET* row, int hb, int V, uint4 (&v
     }
   } else {
 #pragma unroll
-    for (int k = 0; k < kNV; ++k) v[k] = load_raw<ET>(row, hb + (k * kThreads + tid) * N, V, al);
+    for (int k = 0; k < NV; ++k) v[k] = load_raw<ET>(row, hb + (k * kThreads + tid) * N, V, al);
   }
+}
+
+template <typename ET>
+__device__ __forceinline__ void load_seg(const ET* row, int hb, int V, uint4 (&v)[kNV], int) {
+  load_vecs<ET, kNV, 0>(row, hb, V, v);
 }
 
 __device__ __forceinline__ void fence_regs(uint4 (&v)[kNV]) {
@@ -266,9 +273,7 @@ struct DrawShared {
   float wt[kWaves];
   float sw[kWaves][kNV];
   int wi[2 * kWaves];
-  float cum[kDrawSlices * kMaxDrawSegs];  // running slice weights
-  float chunk[kMaxChunks];
-  int li[4];
+  float cum[kDrawSlices * kMaxDrawSegs];  // running slice weights (slices of a draw segment, or of a row)
   Partial red[kWaves];
   RowStat row[2 * SV_MAX_K + 1];  // by row slot: draft i at i, target j at max_k + j
   int word;
@@ -285,21 +290,41 @@ __device__ __forceinline__ float elem_w(const uint4& zt, const uint4& zd, int j,
   return pt;
 }
 
-// Weights of the segment's kNV slices (slice k: vector k of every thread, a
-// contiguous kThreads * N elements), handed off to the request's search in
-// slots[0 .. kNV-1].  Each slice's sum takes the same order in every call.
-template <typename ET, bool RESID>
-__device__ __forceinline__ void slice_weights(const uint4 (&t)[kNV], const uint4 (&d)[kNV], float c, float kt,
-                                              float kd, uint64_t* slots, DrawShared& sh, int tid) {
+// Weights of the kNV / 2 slices K0 .. of a segment (slice k: vector k of
+// every thread, a contiguous kThreads * N elements), per wave into sh.sw.
+template <typename ET, bool RESID, int K0>
+__device__ __forceinline__ void half_weights(const uint4 (&t)[kNV / 2], const uint4 (&d)[kNV / 2], float c, float kt,
+                                             float kd, DrawShared& sh, int tid) {
   constexpr int N = Elem<ET>::N;
   const int wave = tid >> 6, lane = tid & 63;
 #pragma unroll
-  for (int k = 0; k < kNV; ++k) {
+  for (int k = 0; k < kNV / 2; ++k) {
     float r = 0.f;
 #pragma unroll
     for (int j = 0; j < N; ++j) r += elem_w<ET, RESID>(t[k], d[k], j, c, kt, kd);
     r = wave_sum(r);
-    if (lane == 0) sh.sw[wave][k] = r;
+    if (lane == 0) sh.sw[wave][K0 + k] = r;
+  }
+}
+
+// Weights of the segment's kNV slices, handed off to the request's search in
+// slots[0 .. kNV-1]; the segment is read in two halves, so that a workgroup
+// holds 16 KiB of it at a time.  Each slice's sum takes the same order in
+// every call.
+template <typename ET, bool RESID>
+__device__ __forceinline__ void slice_weights(const ET* rt, const ET* rd, int hb, int V, float c, float kt, float kd,
+                                              uint64_t* slots, DrawShared& sh, int tid) {
+  {
+    uint4 t[kNV / 2], d[kNV / 2];
+    load_vecs<ET, kNV / 2, 0>(rt, hb, V, t);
+    if (RESID) load_vecs<ET, kNV / 2, 0>(rd, hb, V, d);
+    half_weights<ET, RESID, 0>(t, d, c, kt, kd, sh, tid);
+  }
+  {
+    uint4 t[kNV / 2], d[kNV / 2];
+    load_vecs<ET, kNV / 2, kNV / 2>(rt, hb, V, t);
+    if (RESID) load_vecs<ET, kNV / 2, kNV / 2>(rd, hb, V, d);
+    half_weights<ET, RESID, kNV / 2>(t, d, c, kt, kd, sh, tid);
   }
   __syncthreads();
   if (tid < kNV) {
@@ -309,19 +334,19 @@ __device__ __forceinline__ void slice_weights(const uint4 (&t)[kNV], const uint4
   }
 }
 
-// Collect the m slice weights of request b, in token order, and scan them:
-// the crossing slice k (the first whose running weight exceeds u * Z; -1 if
-// Z is not positive; if rounding leaves u * Z at or above the last running
-// weight, the last slice with positive weight, flagged), the weight before
+// Scan the m weights in sh.cum (in place, in token order) and find the
+// crossing entry k: the first whose running weight exceeds u * Z (-1 if Z is
+// not positive; if rounding leaves u * Z at or above the last running
+// weight, the last entry with positive weight, flagged), the weight before
 // it, u * Z.
-__device__ __forceinline__ void scan_slices(const VerifyArgs& a, int b, int m, float u, DrawShared& sh, int tid) {
+__device__ __forceinline__ void scan_cum(int m, float u, DrawShared& sh, int tid) {
   const int lane = tid & 63;
+  __syncthreads();
   if (tid < 64) {
-    const uint64_t* slots = weight_slot(a, b, 0);
     float carry = 0.f;
     for (int base = 0; base < m; base += 64) {
       const int q = base + lane;
-      float x = (q < m) ? __uint_as_float(take_slot(const_cast<uint64_t*>(slots) + q, a)) : 0.f;
+      float x = (q < m) ? sh.cum[q] : 0.f;
       x = wave_inclusive_scan(x, lane) + carry;
       if (q < m) sh.cum[q] = x;
       carry = __shfl(x, 63, 64);
@@ -354,6 +379,15 @@ __device__ __forceinline__ void scan_slices(const VerifyArgs& a, int b, int m, f
     }
   }
   __syncthreads();
+}
+
+// Collect the m slice weights of request b from their slots and scan them.
+__device__ __forceinline__ void scan_slices(const VerifyArgs& a, int b, int m, float u, DrawShared& sh, int tid) {
+  if (tid < 64) {
+    uint64_t* slots = weight_slot(a, b, 0);
+    for (int q = tid; q < m; q += 64) sh.cum[q] = __uint_as_float(take_slot(slots + q, a));
+  }
+  scan_cum(m, u, sh, tid);
 }
 
 // Within one slice (thread t holds elements first + t*N .. + N-1): the first
@@ -408,15 +442,41 @@ __device__ __forceinline__ int slice_search(const ET* rt, const ET* rd, int firs
   return uniform(result >= 0 ? result : lastall);
 }
 
+// The draw from pt itself (the residual has no mass, reachable only
+// through rounding): the row's slices are weighed by the waves in turn (wave
+// w takes slices w, w + kWaves, ...), then scanned and searched like the
+// residual's.  Slow and rarely taken; it holds one vector per lane.
+template <typename ET>
+__device__ __forceinline__ int draw_from_target(const ET* rt, int V, float c, float kt, float u, DrawShared& sh,
+                                                int tid) {
+  constexpr int N = Elem<ET>::N;
+  constexpr int EV = kThreads * N;  // elements per slice
+  const int wave = tid >> 6, lane = tid & 63;
+  const int m = (V + EV - 1) / EV;  // at most kDrawSlices * kMaxDrawSegs
+  const bool al = is_aligned16(rt);
+  for (int q = wave; q < m; q += kWaves) {
+    float w = 0.f;
+    for (int x = 0; x < kThreads / 64; ++x) {
+      const uint4 z = load_raw<ET>(rt, q * EV + (x * 64 + lane) * N, V, al);
+#pragma unroll
+      for (int j = 0; j < N; ++j) w += elem_w<ET, false>(z, z, j, c, kt, kt);
+    }
+    w = wave_sum(w);
+    if (lane == 0) sh.cum[q] = w;
+  }
+  scan_cum(m, u, sh, tid);
+  const int k = uniform(sh.fk);
+  if (k < 0) return -1;
+  return slice_search<ET, false>(rt, rt, k * EV, V, c, kt, kt, uniform(sh.fb4), uniform(sh.ft), uniform(sh.ffb) != 0,
+                                 sh, tid);
+}
+
 // Weights of segment s of the draw rows, handed off to the request's search.
 template <typename ET, bool RESID>
 __device__ __forceinline__ void weight_segment(const VerifyArgs& a, DrawShared& sh, int b, int s, float c, float kt,
                                                float kd, const ET* rt, const ET* rd, int tid) {
   constexpr int E = kThreads * kNV * Elem<ET>::N;
-  uint4 t[kNV], d[kNV];
-  load_seg<ET>(rt, s * E, a.V, t, tid);
-  if (RESID) load_seg<ET>(rd, s * E, a.V, d, tid);
-  slice_weights<ET, RESID>(t, d, c, kt, kd, weight_slot(a, b, s * kNV), sh, tid);
+  slice_weights<ET, RESID>(rt, rd, s * E, a.V, c, kt, kd, weight_slot(a, b, s * kNV), sh, tid);
 }
 
 // The draw of request b once its slices' weights are in: scan them, read the
@@ -430,7 +490,7 @@ __device__ __forceinline__ void search_request(const VerifyArgs& a, DrawShared& 
   int tok = -1;
   if (k < 0) {
     // the residual has no mass (reachable only through rounding): draw from pt itself
-    if (RESID) tok = cdf_sample<ET, false>(rt, c, kt, rt, c, kt, a.V, u, sh.chunk, sh.li);
+    if (RESID) tok = draw_from_target<ET>(rt, a.V, c, kt, u, sh, tid);
   } else {
     tok = slice_search<ET, RESID>(rt, rd, k * EV, a.V, c, kt, kd, uniform(sh.fb4), uniform(sh.ft), uniform(sh.ffb) != 0,
                                   sh, tid);
@@ -550,7 +610,7 @@ __device__ __forceinline__ void confident_feature(const VerifyArgs& a, DrawShare
 // ones read by the statistics kernel are the likeliest to be cached); every
 // workgroup derives its request's verdict first.
 template <typename ET>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void draw_kernel(VerifyArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) void draw_kernel(VerifyArgs a) {
   __shared__ DrawShared sh;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n = a.nseg2, max_k = a.max_k;
