@@ -106,23 +106,18 @@ int sv_spec_verify(void* stream, int B, int V, int max_k, int dtype, const void*
   a.av_feature = av_feature;
   a.av_score = av_score;
   a.ctrl = reinterpret_cast<uint32_t*>(ws + L.ctrl);
-  a.tickets = reinterpret_cast<uint32_t*>(ws + L.tickets);
-  a.tickets2 = reinterpret_cast<uint32_t*>(ws + L.tickets2);
-  a.flags = reinterpret_cast<int*>(ws + L.flags);
   a.reqw = reinterpret_cast<uint32_t*>(ws + L.reqw);
   a.partials = reinterpret_cast<Partial*>(ws + L.partials);
   a.zval = reinterpret_cast<float*>(ws + L.zval);
-  a.records = reinterpret_cast<Record*>(ws + L.records);
   a.segsum = reinterpret_cast<float*>(ws + L.segsum);
-  a.rowrec = reinterpret_cast<RowRec*>(ws + L.rowrec);
   a.tagged = reinterpret_cast<uint64_t*>(ws + L.tagged);
-  a.parts = a.group = a.stride = 0;
+  a.parts = a.stride = 0;
   a.spin_limit = 0;
   const int kind = __atomic_load_n(&g_verify_kernel, __ATOMIC_RELAXED);
   const hipStream_t hs = static_cast<hipStream_t>(stream);
   hipError_t err = hipSuccess;
   if (kind != SV_KERNEL_RESIDENT) return to_status(launch_streaming(a, dtype, hs, next_events()));
-  if (!launch_verify(a, dtype, true, hs, &err, next_events())) {
+  if (!launch_verify(a, dtype, hs, &err, next_events())) {
     if (g_timing.slots) --g_timing.calls;  // nothing recorded
     return SV_ERR_UNSUPPORTED;
   }

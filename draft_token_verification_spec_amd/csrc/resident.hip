@@ -1149,7 +1149,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     S.nreq = uint32_t((a.B - p + a.parts - 1) / a.parts);
     S.A = uint32_t(a.stride);
     S.C = HOLD ? 0u : uint32_t(a.nseg2);
-    S.L = uint32_t(a.group);
+    S.L = 0;
     S.total = S.nreq * (S.A + S.C);
     uint32_t* counter = &a.ctrl[kCtrlWork + p * kLineWords];
     if (tid == 0) sh.meta = load_meta(a, S, claim(counter));
@@ -1182,26 +1182,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   }
 }
 
-int g_capacity[64][2][2];
+int g_capacity[64][2];
 
 // Resident workgroups of the kernel on the current device (occupancy x CUs).
-int capacity(int dtype, bool hold) {
+int capacity(int dtype) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
   const int slot = dtype == SV_BF16 ? 1 : 0;
-  int cap = __atomic_load_n(&g_capacity[dev][slot][hold], __ATOMIC_RELAXED);
+  int cap = __atomic_load_n(&g_capacity[dev][slot], __ATOMIC_RELAXED);
   if (cap == 0) {
     int per_cu = 0, cus = 0;
-    hipError_t e1;
-    if (dtype == SV_BF16)
-      e1 = hold ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, verify_kernel<uint16_t, true>, kThreads, 0)
-                : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, verify_kernel<uint16_t, false>, kThreads, 0);
-    else
-      e1 = hold ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, verify_kernel<float, true>, kThreads, 0)
-                : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, verify_kernel<float, false>, kThreads, 0);
+    const hipError_t e1 =
+        dtype == SV_BF16 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, verify_kernel<uint16_t, true>, kThreads, 0)
+                         : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, verify_kernel<float, true>, kThreads, 0);
     const hipError_t e2 = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     cap = (e1 == hipSuccess && e2 == hipSuccess && per_cu > 0 && cus > 0) ? per_cu * cus : -1;
-    __atomic_store_n(&g_capacity[dev][slot][hold], cap, __ATOMIC_RELAXED);
+    __atomic_store_n(&g_capacity[dev][slot], cap, __ATOMIC_RELAXED);
   }
   return cap;
 }
@@ -1213,43 +1209,29 @@ int capacity(int dtype, bool hold) {
 // (nseg <= nseg2).
 int stats_stride(int max_k, int nseg, int nseg2) { return max_k * nseg2 + nseg; }
 
-#ifndef SV_SAMPLE_LAG
-#define SV_SAMPLE_LAG 2.0
-#endif
-
-bool launch_verify(VerifyArgs a, int dtype, bool hold, hipStream_t stream, hipError_t* err, const hipEvent_t* ev) {
-  const int cap = capacity(dtype, hold);
+bool launch_verify(VerifyArgs a, int dtype, hipStream_t stream, hipError_t* err, const hipEvent_t* ev) {
+  const int cap = capacity(dtype);
   if (cap <= 0) return false;
   a.stride = stats_stride(a.max_k, a.nseg, a.nseg2);
   if (a.nseg2 > kMaxCum) return false;
   int parts = a.B < kParts ? a.B : kParts;
-  if (hold) {
-    // an item waits only for items of its own row and of earlier rows: with
-    // more resident workgroups than parts * (row items - 1), one is always free
-    const int row_items = a.nseg2;  // >= a.nseg
-    if (row_items > 1) parts = min(parts, (cap - 1) / (row_items - 1));
-    if (parts < 1) return false;
-  }
+  // an item waits only for items of its own row and of earlier rows: with
+  // more resident workgroups than parts * (row items - 1), one is always free
+  const int row_items = a.nseg2;  // >= a.nseg
+  if (row_items > 1) parts = min(parts, (cap - 1) / (row_items - 1));
+  if (parts < 1) return false;
   a.parts = parts;
   const uint64_t nreq = (uint64_t(a.B) + parts - 1) / parts;
-  const uint64_t per_part = nreq * uint64_t(a.stride + (hold ? 0 : a.nseg2));
+  const uint64_t per_part = nreq * uint64_t(a.stride);
   if (per_part + uint64_t(cap) >= (uint64_t(1) << 32)) return false;
-  // sampling of request j follows the statistics of request j + group: about
-  // SV_SAMPLE_LAG statistics items per resident workgroup of the partition
-  // in between, so that most decisions are made by the time they are claimed
-  const double wg_per_part = double(cap) / parts;
-  a.group = hold ? 0 : max(1, int(SV_SAMPLE_LAG * wg_per_part / a.stride + 0.999));
   a.spin_limit = 1u << 20;
   const uint64_t all = per_part * uint64_t(parts);
   const unsigned grid = unsigned(all < uint64_t(cap) ? all : uint64_t(cap));
   if (ev) (void)hipEventRecord(ev[0], stream);
-  if (dtype == SV_BF16) {
-    if (hold) hipLaunchKernelGGL((verify_kernel<uint16_t, true>), dim3(grid), dim3(kThreads), 0, stream, a);
-    else hipLaunchKernelGGL((verify_kernel<uint16_t, false>), dim3(grid), dim3(kThreads), 0, stream, a);
-  } else {
-    if (hold) hipLaunchKernelGGL((verify_kernel<float, true>), dim3(grid), dim3(kThreads), 0, stream, a);
-    else hipLaunchKernelGGL((verify_kernel<float, false>), dim3(grid), dim3(kThreads), 0, stream, a);
-  }
+  if (dtype == SV_BF16)
+    hipLaunchKernelGGL((verify_kernel<uint16_t, true>), dim3(grid), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((verify_kernel<float, true>), dim3(grid), dim3(kThreads), 0, stream, a);
   *err = hipGetLastError();
   if (ev) {
     (void)hipEventRecord(ev[1], stream);

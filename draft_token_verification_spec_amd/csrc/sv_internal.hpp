@@ -63,18 +63,19 @@ struct Partial {
 
 // Byte offsets inside the caller's workspace.
 //
-// The workspace starts with a fixed arena - a control block, three
-// per-request-slot arrays of SV_MAX_B words, then SV_MAX_B per-request blocks
-// of kReqWords words - which every call leaves zeroed and no call writes
-// partial data into, whatever its shape.  After the arena comes the per-call
-// region, laid out for the call's (B, V, max_k).
+// The workspace starts with a fixed arena - a control block, a
+// per-request-slot array of SV_MAX_B words (scoring kernel), then SV_MAX_B
+// per-request blocks of kReqWords words (register-resident kernel) - which
+// every call leaves zeroed and no call writes partial data into, whatever its
+// shape.  After the arena comes the per-call region, laid out for the call's
+// (B, V, max_k).
 constexpr int kParts = 16;        // independent work schedules (claim counters)
 constexpr int kLineWords = 32;    // 128 bytes: one counter per cache line
 constexpr size_t kCtrlBytes = size_t(kParts + 2) * kLineWords * 4;
 constexpr int kCtrlWork = 0;                         // claim counter of partition p: kCtrlWork + p * kLineWords
 constexpr int kCtrlExit = kParts * kLineWords;       // workgroups that finished
 constexpr int kCtrlError = (kParts + 1) * kLineWords;  // set if a bounded wait ever expired
-constexpr int kArenaArrays = 3;  // tickets, tickets2, flags (streaming and scoring kernels)
+constexpr int kArenaArrays = 1;  // tickets (scoring kernel)
 // Words of request b's block (register-resident kernel), one 128-byte line:
 constexpr int kReqWords = 32;
 constexpr int kWRow = 0;      // kWRow + i: arrivals of row i (i = 0..SV_MAX_K)
@@ -95,21 +96,6 @@ static_assert(SV_MAX_B % kLineWords == 0, "arena slots");
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// How a request's emitted token is drawn, decided by its statistics phase.
-enum DrawMode { kUnresolved = 0, kNoDraw = 1, kResidual = 2, kBonus = 3 };
-
-// Decision of one request, read by its sampling items.
-struct Record {
-  int a;         // accept length
-  int mode;      // DrawMode
-  float kt;      // log2 normaliser of the target row: log2 pt(v) = z*c - kt
-  float kd;      // same for the draft row (residual only)
-  float c;       // log2(e) / T
-  float u;       // uniform of the draw
-  float before;  // weight of the segments before the chosen one
-  float t;       // u * total weight: the draw is the first token whose running weight exceeds t
-};
-
 // Hand-off slot of the draw kernel: 8 bytes written in one store, the low
 // word kSlotReady, the high word the value's bits.  The reader polls until
 // the low word is kSlotReady and clears the slot once it has the value.  The
@@ -120,26 +106,13 @@ struct Record {
 constexpr uint32_t kSlotReady = 0x7fb5a5a5u;
 __host__ __device__ constexpr uint64_t ready_slot(uint32_t bits) { return (uint64_t(bits) << 32) | kSlotReady; }
 
-// Statistics of one position for the decision and the draw (streaming
-// kernels), written by the position's last segment.
-struct RowRec {
-  float kt;    // log2 normaliser of the target row: log2 pt(v) = z*c - kt
-  float kd;    // same for the draft row (positions with a draft row read)
-  int argmax;  // lowest-index argmax of the target row (greedy requests)
-  int pad;
-};
-
 struct WsLayout {
   size_t ctrl;      // uint32 control block (claim/exit counters, error flag)
-  size_t tickets;   // uint32 [SV_MAX_B]  statistics arrivals per request
-  size_t tickets2;  // uint32 [SV_MAX_B]  sampling arrivals per request
-  size_t flags;     // int [SV_MAX_B]     decision once made, 0 otherwise
+  size_t tickets;   // uint32 [SV_MAX_B]  arrivals per request (scoring kernel)
   size_t reqw;      // uint32 [SV_MAX_B][kReqWords]  request blocks (register-resident kernel)
   size_t partials;  // Partial [B][R][nseg2]
   size_t zval;      // float [B][R]       logit at the draft token, per row
-  size_t records;   // Record [B]
-  size_t segsum;    // float [2][B][nseg2]  weight of each sampling segment (per draw round)
-  size_t rowrec;    // RowRec [B][max_k + 1]
+  size_t segsum;    // float [2][B][nseg2]  weight of each sampling segment per draw round (register-resident kernel)
   size_t tagged;    // uint64 [B][nseg2][kDrawSlices]  hand-off slots of the draw's slice weights
   size_t total;
   int nseg;   // 64 KiB statistics segments per row
@@ -154,15 +127,11 @@ inline WsLayout ws_layout(int B, int V, int max_k, int dtype) {
   L.R = rows_per_request(max_k);
   L.ctrl = 0;
   L.tickets = kCtrlBytes;
-  L.tickets2 = L.tickets + size_t(SV_MAX_B) * 4;
-  L.flags = L.tickets2 + size_t(SV_MAX_B) * 4;
-  L.reqw = L.flags + size_t(SV_MAX_B) * 4;
+  L.reqw = L.tickets + size_t(SV_MAX_B) * 4;
   L.partials = kArenaBytes;
   L.zval = L.partials + align256(size_t(B) * L.R * L.nseg2 * sizeof(Partial));
-  L.records = L.zval + align256(size_t(B) * L.R * 4);
-  L.segsum = L.records + align256(size_t(B) * sizeof(Record));
-  L.rowrec = L.segsum + align256(2 * size_t(B) * L.nseg2 * 4);
-  L.tagged = L.rowrec + align256(size_t(B) * (max_k + 1) * sizeof(RowRec));
+  L.segsum = L.zval + align256(size_t(B) * L.R * 4);
+  L.tagged = L.segsum + align256(2 * size_t(B) * L.nseg2 * 4);
   L.total = L.tagged + align256(size_t(B) * L.nseg2 * kDrawSlices * 8);
   return L;
 }
@@ -191,19 +160,13 @@ struct VerifyArgs {
   float* av_score;
   // workspace
   uint32_t* ctrl;
-  uint32_t* tickets;
-  uint32_t* tickets2;
-  int* flags;
   uint32_t* reqw;     // request blocks
   Partial* partials;  // [B][R][nseg2]
   float* zval;
-  Record* records;
   float* segsum;      // [2][B][nseg2]
-  RowRec* rowrec;     // [B][max_k + 1]
   uint64_t* tagged;   // hand-off slots (see WsLayout::tagged)
   // work-item schedule (see the kernels)
   int parts;         // independent schedules; partition p owns requests b = p (mod parts)
-  int group;         // requests per group within a partition (streaming kernel)
   int stride;        // item slots per request (register-resident kernel)
   uint32_t spin_limit;
 };
@@ -224,12 +187,11 @@ struct ScoreArgs {
   Partial* partials;
 };
 
-// Verification kernel, register-resident (hold) or streaming: returns false
-// (nothing launched) if the sizes do not fit it; otherwise launches and
-// stores the launch status in *err.  `ev` (nullable): three events to record
-// before the kernel, after it, and after it again (an empty second phase).
-bool launch_verify(VerifyArgs a, int dtype, bool hold, hipStream_t stream, hipError_t* err,
-                   const hipEvent_t* ev = nullptr);
+// The register-resident verification kernel: returns false (nothing
+// launched) if the sizes do not fit it; otherwise launches and stores the
+// launch status in *err.  `ev` (nullable): three events to record before the
+// kernel, after it, and after it again (an empty second phase).
+bool launch_verify(VerifyArgs a, int dtype, hipStream_t stream, hipError_t* err, const hipEvent_t* ev = nullptr);
 // The two streaming kernels (statistics, then the verdict and the draw).
 // `ev` (nullable): three events to record before, between and after them.
 hipError_t launch_streaming(VerifyArgs a, int dtype, hipStream_t stream, const hipEvent_t* ev = nullptr);

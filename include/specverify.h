@@ -68,13 +68,14 @@ typedef enum {
  * of B requests, vocabulary V, at most max_k drafts each, elements of type
  * `dtype`.  Returns 0 for arguments those calls would reject.
  *
- * The workspace starts with a fixed arena (work counters and four words per
- * request slot, SV_MAX_B slots), followed by per-row partial statistics,
- * decision records and draw weights.  Zero-fill the
- * workspace once after allocation; every call leaves the counters at zero
- * again, and no call writes anything else into the arena, so one workspace
- * (of the largest size needed) serves any sequence of calls of any shapes on
- * one stream without further clearing.  Calls that can run concurrently
+ * The workspace starts with a fixed arena (work counters, one word and one
+ * 128-byte block per request slot, SV_MAX_B slots), followed by per-row
+ * partial statistics, logits at the draft tokens and draw weights.
+ * Zero-fill the workspace once after allocation; every call leaves the
+ * counters at zero again, and no call writes anything else into the arena,
+ * so one workspace (of the largest size needed) serves any sequence of calls
+ * of any shapes on one stream without further clearing, and a call captured
+ * in a HIP graph replays without any reset.  Calls that can run concurrently
  * (different streams) need different workspaces.  If a call is aborted part
  * way (device fault), zero-fill the workspace again. */
 size_t sv_workspace_size(int B, int V, int max_k, int dtype);
