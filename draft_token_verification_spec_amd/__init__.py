@@ -29,6 +29,7 @@ __all__ = [
     "sv_spec_verify",
     "sv_av_score",
     "sv_av_fit_step",
+    "sv_av_budget",
     "sv_set_verify_kernel",
     "sv_timing_enable",
     "sv_timing_read",
@@ -41,6 +42,7 @@ __all__ = [
 SV_MAX_K = 16
 SV_MAX_V = 1 << 21
 SV_MAX_B = 1 << 18
+SV_BUDGET_MAX_ITEMS = 8192
 SV_F32, SV_BF16 = 0, 1
 SV_KERNEL_AUTO, SV_KERNEL_STREAMING, SV_KERNEL_RESIDENT = 0, 1, 2
 
@@ -65,6 +67,7 @@ _SIGNATURES = {
     "sv_av_score": (_i, [_p, _i, _i, _i, _i, _p, _p, _i64, _p, _p, _p, _f, _p, _p, _p, _p, _sz]),
     "sv_av_fit_step": (_i, [_p, _i, _i, _p, _p, _p, _p, _f, _f, _i]),
     "sv_status_string": (ctypes.c_char_p, [_i]),
+    "sv_av_budget": (_i, [_p, _i, _i, _p, _p, _p, _p, _p, _p]),
     "sv_set_verify_kernel": (_i, [_i]),
     "sv_timing_enable": (_i, [_i]),
     "sv_timing_read": (_i, [_p, _i]),
@@ -101,6 +104,33 @@ def _check(status: int, what: str):
 
 def sv_workspace_size(B: int, V: int, max_k: int, dtype: int) -> int:
     return int(_load().sv_workspace_size(B, V, max_k, dtype))
+
+
+def sv_av_budget(score: torch.Tensor, num_draft: torch.Tensor, draft_cost_ms: torch.Tensor,
+                 verify_cost_ms: torch.Tensor, *, out: Optional[dict] = None) -> dict:
+    """The global draft budget of a batch; see ``sv_av_budget``.  ``score``
+    float32 [B, max_k]; ``num_draft`` int32 [B]; both cost tables float32
+    with at least B*max_k + 1 entries.  Returns ``num_kept`` int32 [B] and
+    ``budget`` int32 [1], on the device (no host synchronisation)."""
+    if score.dim() != 2:
+        raise ValueError("score must be [B, max_k]")
+    B, max_k = score.shape
+    dev = score.device
+    _dev(score, "score", torch.float32)
+    _dev(num_draft, "num_draft", torch.int32, B)
+    for name, t in (("draft_cost_ms", draft_cost_ms), ("verify_cost_ms", verify_cost_ms)):
+        _dev(t, name, torch.float32)
+        if t.numel() < B * max_k + 1:
+            raise ValueError(f"{name} needs at least B*max_k + 1 = {B * max_k + 1} entries")
+    o = {} if out is None else out
+    _need(o, "num_kept", (B,), torch.int32, dev)
+    _need(o, "budget", (1,), torch.int32, dev)
+    _dev(o["num_kept"], "num_kept", torch.int32, B)
+    _dev(o["budget"], "budget", torch.int32, 1)
+    st = _load().sv_av_budget(_stream(dev), B, max_k, _ptr(score), _ptr(num_draft), _ptr(draft_cost_ms),
+                              _ptr(verify_cost_ms), _ptr(o["num_kept"]), _ptr(o["budget"]))
+    _check(st, "sv_av_budget")
+    return o
 
 
 def sv_timing_enable(slots: int) -> None:

@@ -173,6 +173,17 @@ int sv_av_fit_step(void* stream, int B, int max_k, const float* feature, const i
                                  static_cast<hipStream_t>(stream)));
 }
 
+int sv_av_budget(void* stream, int B, int max_k, const float* score, const int32_t* num_draft,
+                 const float* draft_cost_ms, const float* verify_cost_ms, int32_t* num_kept, int32_t* budget) {
+  if (B < 0 || max_k < 0) return SV_ERR_INVALID_ARG;
+  if (max_k > SV_MAX_K || int64_t(B) * max_k > SV_BUDGET_MAX_ITEMS) return SV_ERR_UNSUPPORTED;
+  if (B == 0) return SV_OK;
+  if (!num_draft || !draft_cost_ms || !verify_cost_ms || !num_kept || !budget || (max_k > 0 && !score))
+    return SV_ERR_INVALID_ARG;
+  return to_status(launch_av_budget(B, max_k, score, num_draft, draft_cost_ms, verify_cost_ms, num_kept, budget,
+                                    static_cast<hipStream_t>(stream)));
+}
+
 int sv_set_verify_kernel(int kernel) {
   if (kernel != SV_KERNEL_AUTO && kernel != SV_KERNEL_STREAMING && kernel != SV_KERNEL_RESIDENT)
     return SV_ERR_INVALID_ARG;

@@ -196,6 +196,8 @@ bool launch_verify(VerifyArgs a, int dtype, hipStream_t stream, hipError_t* err,
 // `ev` (nullable): three events to record before, between and after them.
 hipError_t launch_streaming(VerifyArgs a, int dtype, hipStream_t stream, const hipEvent_t* ev = nullptr);
 hipError_t launch_av_score(const ScoreArgs& a, int dtype, hipStream_t stream);
+hipError_t launch_av_budget(int B, int max_k, const float* score, const int32_t* num_draft, const float* draft_cost,
+                            const float* verify_cost, int32_t* num_kept, int32_t* budget, hipStream_t stream);
 hipError_t launch_av_fit(int B, int max_k, const float* feature, const int8_t* labels,
                          float* params, double* accum, float damping_c, float ridge,
                          int do_update, hipStream_t stream);

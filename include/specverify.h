@@ -192,6 +192,35 @@ int sv_av_fit_step(void* stream, int B, int max_k, const float* feature,
                    const int8_t* labels, float* params, double* accum,
                    float damping_c, float ridge, int do_update);
 
+/* The estimator's global draft budget: how many draft tokens of the batch to
+ * verify, and which.
+ *
+ * [AV] "Other features considered" (the budget decision): the survival of
+ * request b's draft i is the running product score_0 * ... * score_i (binary32,
+ * left to right) over the positions i < K_b = num_draft[b]; the batch's
+ * survivals are ranked, highest first (equal ones by flat index
+ * b*max_k + i); keeping the j highest is estimated to emit
+ * E(j) = B + (sum of those j survivals) tokens, and the budget is the j in
+ * 0..N (N = sum K_b) maximising E(j) / (draft_cost_ms[j] + verify_cost_ms[j]),
+ * the smallest such j on ties (sums and ratios in binary64).  The kept drafts
+ * of a request are always a prefix of its positions.
+ *   score          float [B*max_k]   per-position scores in [0, 1] (e.g. the
+ *                  `score` output of sv_av_score).
+ *   num_draft      int32 [B]         K_b.
+ *   draft_cost_ms, verify_cost_ms   float [B*max_k + 1]: the measured cost of
+ *                  a step that verifies j draft tokens, by j (only 0..N read).
+ * Outputs (device): num_kept int32 [B] (kept prefix length, <= K_b, summing to
+ * the budget), budget int32 [1].
+ * One workgroup decides the whole batch: B*max_k <= SV_BUDGET_MAX_ITEMS, else
+ * SV_ERR_UNSUPPORTED.  B = 0 launches nothing and writes nothing.
+ * Device preconditions: 0 <= K_b <= max_k; scores in [0, 1]; every cost sum
+ * read is > 0.
+ * Returns SV_OK, or a negative sv_status without launching anything. */
+#define SV_BUDGET_MAX_ITEMS 8192
+int sv_av_budget(void* stream, int B, int max_k, const float* score, const int32_t* num_draft,
+                 const float* draft_cost_ms, const float* verify_cost_ms, int32_t* num_kept,
+                 int32_t* budget);
+
 /* Which kernel sv_spec_verify launches: a process-wide setting, default
  * SV_KERNEL_AUTO.  Both kernels compute the same outputs.
  *   SV_KERNEL_STREAMING  a statistics pass over every row, then a second pass

@@ -24,7 +24,8 @@ def declared_functions():
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
     assert set(names) == {"sv_workspace_size", "sv_spec_verify", "sv_av_score", "sv_av_fit_step",
-                          "sv_status_string", "sv_set_verify_kernel", "sv_timing_enable", "sv_timing_read"}
+                          "sv_status_string", "sv_set_verify_kernel", "sv_timing_enable", "sv_timing_read",
+                          "sv_av_budget"}
     lib = ctypes.CDLL(sv.lib_path())
     for n in names:
         assert hasattr(lib, n), n
@@ -36,6 +37,7 @@ def test_header_constants_match_binding():
     assert int(re.search(r"#define SV_MAX_K (\d+)", text).group(1)) == sv.SV_MAX_K
     assert re.search(r"#define SV_MAX_V \(1 << (\d+)\)", text).group(1) == str(sv.SV_MAX_V.bit_length() - 1)
     assert re.search(r"#define SV_MAX_B \(1 << (\d+)\)", text).group(1) == str(sv.SV_MAX_B.bit_length() - 1)
+    assert int(re.search(r"#define SV_BUDGET_MAX_ITEMS (\d+)", text).group(1)) == sv.SV_BUDGET_MAX_ITEMS
 
 
 def test_kernel_selector():
@@ -169,3 +171,21 @@ def test_binding_refuses_host_tensors():
                           torch.ones(1), torch.zeros(1, 1), torch.zeros(1), torch.zeros(1), max_k=1)
     with pytest.raises(ValueError):
         sv.sv_av_score(x, z, torch.zeros(1, dtype=torch.int32), torch.ones(1), torch.zeros(2), max_k=1)
+
+
+@pytest.mark.parametrize("B,max_k,nulls,status", [
+    (-1, 4, (), -1), (4, -1, (), -1), (4, 17, (), -2), (2049, 4, (), -2), (513, 16, (), -2),
+    (4, 4, ("num_draft",), -1), (4, 4, ("draft_cost",), -1), (4, 4, ("verify_cost",), -1),
+    (4, 4, ("num_kept",), -1), (4, 4, ("budget",), -1), (4, 4, ("score",), -1),
+    (0, 4, ("score", "num_draft", "draft_cost", "verify_cost", "num_kept", "budget"), 0),
+])
+def test_budget_rejects_before_launch(B, max_k, nulls, status):
+    # every case is refused (or is empty) before anything reaches a device
+    lib = ctypes.CDLL(sv.lib_path())
+    fake = ctypes.c_void_p(16)
+    args = {k: (None if k in nulls else fake)
+            for k in ("score", "num_draft", "draft_cost", "verify_cost", "num_kept", "budget")}
+    lib.sv_av_budget.restype = ctypes.c_int
+    lib.sv_av_budget.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int] + [ctypes.c_void_p] * 6
+    assert lib.sv_av_budget(None, B, max_k, args["score"], args["num_draft"], args["draft_cost"],
+                            args["verify_cost"], args["num_kept"], args["budget"]) == status

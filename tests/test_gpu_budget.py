@@ -1,0 +1,145 @@
+"""GPU parity of the estimator's global draft budget (sv_av_budget) against
+the oracle ([AV] "Other features considered"): the budget and every kept
+prefix exactly, unless the oracle's best two ratios lie within MARGIN of each
+other (then a differing budget is a counted near-tie, and the result must
+still be a best choice within that margin)."""
+import numpy as np
+import pytest
+import torch
+
+import draft_token_verification_spec_amd as sv
+from gpu_harness import to_device
+from oracle import av as oav
+from oracle import budget as ob
+from synth import gen
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a HIP device")]
+
+MARGIN = 1e-12  # relative gap between the best two ratios below which the budget may differ
+
+
+def cost_tables(n, seed, step_draft=0.02, step_verify=0.01, base=8.0):
+    """Synthetic measured step costs by verified draft tokens j: rising, with
+    a little noise (no cost table is printed on the page)."""
+    g = np.random.default_rng(seed)
+    j = np.arange(n + 1, dtype=np.float64)
+    draft = step_draft * j * (1 + 0.05 * g.random(n + 1))
+    verify = base + step_verify * j + 0.1 * np.sqrt(j) + 0.01 * g.random(n + 1)
+    return draft.astype(np.float32), verify.astype(np.float32)
+
+
+def run_budget(scores, num_draft, draft, verify):
+    dev = torch.device("cuda")
+    t = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a)).to(device=dev, dtype=dt)
+    out = sv.sv_av_budget(t(scores, torch.float32), t(num_draft, torch.int32), t(draft, torch.float32),
+                          t(verify, torch.float32))
+    torch.cuda.synchronize()
+    return int(out["budget"].item()), out["num_kept"].cpu().numpy()
+
+
+def check(scores, num_draft, draft, verify):
+    budget, kept = run_budget(scores, num_draft, draft, verify)
+    ob_budget, ob_kept, ratios = ob.global_budget(scores, num_draft, draft, verify)
+    top = np.sort(ratios)[::-1]
+    near_tie = len(top) > 1 and (top[0] - top[1]) <= MARGIN * top[0]
+    if near_tie and budget != ob_budget:
+        assert ratios[budget] >= top[0] * (1 - MARGIN)
+        return 1
+    assert budget == ob_budget
+    np.testing.assert_array_equal(kept, ob_kept)
+    return 0
+
+
+def test_worked_example():
+    scores = np.array([[0.9, 0.5], [0.8, 0.9]], dtype=np.float32)
+    draft = np.array([0, 1, 2, 3, 4], dtype=np.float32)
+    verify = np.array([10, 10.5, 11, 11.5, 12], dtype=np.float32)
+    print("case budget worked example", flush=True)
+    budget, kept = run_budget(scores, np.array([2, 2], np.int32), draft, verify)
+    assert budget == 3 and kept.tolist() == [1, 2]
+
+
+@pytest.mark.parametrize("B,max_k,seed", [(1, 1, 0), (3, 2, 1), (64, 5, 2), (256, 4, 3), (1000, 8, 4),
+                                          (2048, 4, 5), (512, 16, 6), (8192, 1, 7), (77, 16, 8)])
+def test_random_batches(B, max_k, seed):
+    g = np.random.default_rng(seed)
+    x = g.normal(1.0, 1.5, (B, max_k))
+    scores = (1 / (1 + np.exp(-(1.2 * x + 0.4 - 0.1 * np.arange(max_k))))).astype(np.float32)
+    num_draft = g.integers(0, max_k + 1, B).astype(np.int32)
+    n = B * max_k
+    draft, verify = cost_tables(n, seed, step_draft=4.0 / max(n, 1), step_verify=2.0 / max(n, 1))
+    print(f"case budget random B={B} max_k={max_k} seed={seed}", flush=True)
+    assert check(scores, num_draft, draft, verify) == 0
+
+
+@pytest.mark.parametrize("variant", ["all_ones", "repeated_values", "zeros", "no_drafts", "max_k_zero",
+                                     "all_or_nothing_all", "all_or_nothing_none"])
+def test_degenerate_batches(variant):
+    g = np.random.default_rng(11)
+    B, max_k = 300, 6
+    num_draft = g.integers(0, max_k + 1, B).astype(np.int32)
+    if variant == "all_ones":  # every survival 1: ranking by flat index alone
+        scores = np.ones((B, max_k), np.float32)
+    elif variant == "repeated_values":  # many exactly equal survivals across requests
+        scores = g.choice(np.array([0.5, 0.75, 1.0], np.float32), (B, max_k))
+    elif variant == "zeros":
+        scores = np.zeros((B, max_k), np.float32)
+    elif variant == "no_drafts":
+        scores = g.random((B, max_k)).astype(np.float32)
+        num_draft = np.zeros(B, np.int32)
+    elif variant == "max_k_zero":
+        scores = np.zeros((B, 0), np.float32)
+        num_draft = np.zeros(B, np.int32)
+        max_k = 0
+    else:  # one draft each, equal scores, linear cost: everything or nothing
+        max_k = 1
+        num_draft = np.ones(B, np.int32)
+        s = 0.9 if variant.endswith("all") else 0.02  # (B + j s) / (1000 + 0.1 j) rises iff 1000 s > 0.1 B
+        scores = np.full((B, 1), s, np.float32)
+        j = np.arange(B + 1, dtype=np.float32)
+        draft, verify = (0.1 * j).astype(np.float32), np.full(B + 1, 1000.0, np.float32)
+    if not variant.startswith("all_or_nothing"):
+        n = B * max_k
+        draft, verify = cost_tables(n, 3, step_draft=3.0 / max(n, 1), step_verify=1.0 / max(n, 1))
+        if variant in ("all_ones", "repeated_values"):  # a cost step in the middle makes the cut land among ties
+            verify[n // 3:] += 0.5
+    print(f"case budget degenerate {variant}", flush=True)
+    assert check(scores, num_draft, draft, verify) == 0
+    if variant.startswith("all_or_nothing"):
+        budget, _ = run_budget(scores, num_draft, draft, verify)
+        assert budget == (B if variant.endswith("all") else 0)
+
+
+def test_score_then_budget_then_verify_on_device():
+    """The estimator's scores feed the budget, whose kept prefixes are the
+    drafts verified, with no host round trip in between."""
+    b = gen.make_batch("bf16_b64_k5_v32000", trial=4)
+    d = to_device(b)
+    print("case budget pipeline bf16_b64_k5_v32000", flush=True)
+    sc = sv.sv_av_score(d["draft"], d["draft_row_start"], d["num_draft"], d["temperature"], d["av_params"],
+                        b.max_k, 0.0)
+    n = b.B * b.max_k
+    draft, verify = cost_tables(n, 5, step_draft=6.0 / n, step_verify=2.0 / n)
+    dev = torch.device("cuda")
+    bud = sv.sv_av_budget(sc["score"], d["num_draft"], torch.from_numpy(draft).to(dev),
+                          torch.from_numpy(verify).to(dev))
+    out = sv.sv_spec_verify(d["draft"], d["draft_row_start"], d["target"], d["target_row_start"], bud["num_kept"],
+                            d["draft_tokens"], d["temperature"], d["u_accept"], d["u_residual"], d["u_bonus"],
+                            max_k=b.max_k)
+    torch.cuda.synchronize()
+    # the oracle, step by step, on the device's scores (scoring parity is its own test)
+    scores = sc["score"].cpu().numpy()
+    budget, kept, _ = ob.global_budget(scores, b.num_draft, draft, verify)
+    assert int(bud["budget"].item()) == budget
+    np.testing.assert_array_equal(bud["num_kept"].cpu().numpy(), kept)
+    acc = out["accept_len"].cpu().numpy()
+    assert np.all(acc <= kept) and np.all(acc >= 0)
+    assert kept.sum() == budget
+    # scores agree with the oracle's survival inputs
+    for r in range(0, b.B, 16):
+        k = int(b.num_draft[r])
+        zd = gen.bf16_bits_to_f32(b.draft[int(b.draft_row_start[r]):int(b.draft_row_start[r]) + k])
+        for i in range(k):
+            x = oav.feature(zd[i], float(b.temperature[r]))
+            assert scores[r, i] == pytest.approx(oav.score(x, b.av_params, i), rel=2e-3)
