@@ -114,16 +114,15 @@ def to_device(batch, dev):
 
 
 def kernel_source_hash() -> str:
-    """sha256 over the library's kernel sources, to tell whether stored
-    counter measurements still describe the current kernels."""
-    import glob
+    """sha256 over the sources the verification kernels are built from, to
+    tell whether stored counter measurements still describe them."""
     import hashlib
 
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "draft_token_verification_spec_amd", "csrc")
-    for f in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.hpp"))):
-        h.update(os.path.basename(f).encode())
-        h.update(open(f, "rb").read())
+    for name in ("stream.hip", "sv_device.hpp", "sv_internal.hpp"):
+        h.update(name.encode())
+        h.update(open(os.path.join(csrc, name), "rb").read())
     return h.hexdigest()
 
 
@@ -327,6 +326,27 @@ def main():
                                           "ms": call_ms, "draw_kernel_ms": second_ms,
                                           "achieved_gbs": call_gbs, "frac": call_gbs / PEAK_HBM_GBS}},
     }
+    # the estimator's global draft budget over the same batch's scores (one
+    # workgroup, latency-bound): the decision of how many drafts to verify
+    log("timing the global draft budget")
+    n = B * K
+    jj = torch.arange(n + 1, dtype=torch.float32, device=dev)
+    draft_cost = 0.02 * jj
+    verify_cost = 8.0 + 0.01 * jj
+    score = outs[0]["av_score"].nan_to_num(0.0)
+    nd = sets[0][1]["num_draft"]
+    bo = sv.sv_av_budget(score, nd, draft_cost, verify_cost)
+    torch.cuda.synchronize(dev)
+    reps = 200
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        sv.sv_av_budget(score, nd, draft_cost, verify_cost, out=bo)
+    e1.record()
+    torch.cuda.synchronize(dev)
+    res["extra"]["av_budget"] = {"us_per_call": e0.elapsed_time(e1) * 1000 / reps, "positions": n,
+                                 "bound": "latency (one workgroup)", "budget": int(bo["budget"].item()),
+                                 "note": "back-to-back calls between two events; synthetic linear cost tables"}
     if args.copy_calibration > 0:
         log("copy calibration")
         n = args.copy_calibration << 20
