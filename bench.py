@@ -331,8 +331,8 @@ def main():
     log("timing the global draft budget")
     n = B * K
     jj = torch.arange(n + 1, dtype=torch.float32, device=dev)
-    draft_cost = 0.02 * jj
-    verify_cost = 8.0 + 0.01 * jj
+    draft_cost = 0.0005 * jj
+    verify_cost = 8.0 + 0.0005 * jj
     score = outs[0]["av_score"].nan_to_num(0.0)
     nd = sets[0][1]["num_draft"]
     bo = sv.sv_av_budget(score, nd, draft_cost, verify_cost)

@@ -42,7 +42,7 @@ __all__ = [
 SV_MAX_K = 16
 SV_MAX_V = 1 << 21
 SV_MAX_B = 1 << 18
-SV_BUDGET_MAX_ITEMS = 8192
+SV_BUDGET_MAX_ITEMS = 4096
 SV_F32, SV_BF16 = 0, 1
 SV_KERNEL_AUTO, SV_KERNEL_STREAMING, SV_KERNEL_RESIDENT = 0, 1, 2
 

@@ -23,8 +23,11 @@ constexpr int kBT = 1024;      // threads of the workgroup
 constexpr int kBW = kBT / 64;  // waves
 static_assert((SV_BUDGET_MAX_ITEMS & (SV_BUDGET_MAX_ITEMS - 1)) == 0, "the sort size is a power of two");
 
+constexpr int kPer = SV_BUDGET_MAX_ITEMS / kBT;  // sorted elements per thread at most
+
 struct BudgetShared {
-  float vals[SV_BUDGET_MAX_ITEMS];  // survivals (-1 where no draft), then ranked
+  float surv[SV_BUDGET_MAX_ITEMS];  // survivals in flat order (b * max_k + i)
+  float vals[SV_BUDGET_MAX_ITEMS];  // exchange buffer of the sort, then the ranked survivals
   double dpart[kBW];
   int ipart[kBW];
   double best_r[kBW];
@@ -60,6 +63,31 @@ __device__ __forceinline__ int row_drafts(const int32_t* num_draft, int b, int m
   return min(max(num_draft[b], 0), max_k);
 }
 
+// Request b's survivals (running products of its scores in binary32, left to
+// right) at positions 0..max_k-1; -1, below every survival, past K_b.  The
+// scores are loaded together, without waiting for K_b.
+__device__ __forceinline__ void row_survivals(const float* score, int b, int K, int max_k,
+                                              float (&out)[SV_MAX_K]) {
+  float sc[SV_MAX_K];
+#pragma unroll
+  for (int i = 0; i < SV_MAX_K; ++i) sc[i] = i < max_k ? score[size_t(b) * max_k + i] : 0.f;
+  float run = 1.f;
+#pragma unroll
+  for (int i = 0; i < SV_MAX_K; ++i) {
+    if (i < K) run *= sc[i];
+    out[i] = i < K ? run : -1.f;
+  }
+}
+
+// One compare-exchange step of the bitonic network (pair distance `stride`
+// within blocks of `size`, descending overall) on element e = k * kBT + tid,
+// whose value is x and whose partner (e ^ stride) holds y.
+__device__ __forceinline__ float bitonic_keep(float x, float y, int e, int stride, int size) {
+  const bool lower = (e & stride) == 0;
+  const bool desc = ((e & ~stride) & size) == 0;  // direction of the pair's block
+  return (lower == desc) ? fmaxf(x, y) : fminf(x, y);
+}
+
 __global__ __launch_bounds__(kBT) void av_budget_kernel(int B, int max_k, const float* score,
                                                         const int32_t* num_draft, const float* draft_cost,
                                                         const float* verify_cost, int32_t* num_kept,
@@ -67,39 +95,69 @@ __global__ __launch_bounds__(kBT) void av_budget_kernel(int B, int max_k, const 
   __shared__ BudgetShared sh;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int items = B * max_k;
-  int P = 1;  // sort size: a power of two >= items
+  int P = kBT;  // sort size: a power of two >= items, at least one element per thread
   while (P < items) P <<= 1;
+  const int per = P / kBT;  // elements per thread: element k * kBT + tid in v[k]
 
-  // survivals (running products of the scores in binary32, left to right)
-  // in flat order; -1, below every survival, marks positions past K_b
+  // survivals in flat order into the exchange buffer (requests in contiguous
+  // runs per thread; the same runs pick the kept prefixes at the end)
+  const int rb = (B + kBT - 1) / kBT;
+  const int b0 = min(B, tid * rb), b1 = min(B, b0 + rb);
   int mine = 0;
-  for (int b = tid; b < B; b += kBT) {
+  for (int b = b0; b < b1; ++b) {
     const int K = row_drafts(num_draft, b, max_k);
-    float run = 1.f;
-    for (int i = 0; i < max_k; ++i) {
-      if (i < K) run *= score[size_t(b) * max_k + i];
-      sh.vals[b * max_k + i] = i < K ? run : -1.f;
-    }
+    float sv[SV_MAX_K];
+    row_survivals(score, b, K, max_k, sv);
+#pragma unroll
+    for (int i = 0; i < SV_MAX_K; ++i)
+      if (i < max_k) sh.surv[b * max_k + i] = sh.vals[b * max_k + i] = sv[i];
     mine += K;
   }
   for (int e = items + tid; e < P; e += kBT) sh.vals[e] = -1.f;
   int N = 0;
   (void)block_exclusive<int>(mine, sh.ipart, N, tid);  // also orders the stores above
 
-  // rank: bitonic sort, descending
+  // rank: bitonic sort, descending.  Pairs at distance < 64 are exchanged
+  // between the lanes of a wave, pairs at distance >= kBT inside a thread,
+  // and only the distances in between go through LDS.
+  float v[kPer];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) v[k] = k < per ? sh.vals[k * kBT + tid] : 0.f;
   for (int size = 2; size <= P; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int t = tid; t < P / 2; t += kBT) {
-        const int lo = 2 * t - (t & (stride - 1)), hi = lo + stride;
-        const float x = sh.vals[lo], y = sh.vals[hi];
-        if ((x < y) == ((lo & size) == 0)) {
-          sh.vals[lo] = y;
-          sh.vals[hi] = x;
+      if (stride >= kBT) {
+        const int ks = stride / kBT;
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+          if (k < per && (k & ks) == 0) {
+            const int e = k * kBT + tid;
+            const float x = v[k], y = v[k | ks];
+            const bool desc = (e & size) == 0;
+            v[k] = desc ? fmaxf(x, y) : fminf(x, y);
+            v[k | ks] = desc ? fminf(x, y) : fmaxf(x, y);
+          }
         }
+      } else if (stride < 64) {
+#pragma unroll
+        for (int k = 0; k < kPer; ++k)
+          if (k < per) v[k] = bitonic_keep(v[k], __shfl_xor(v[k], stride, 64), k * kBT + tid, stride, size);
+      } else {
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < kPer; ++k)
+          if (k < per) sh.vals[k * kBT + tid] = v[k];
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < kPer; ++k)
+          if (k < per) v[k] = bitonic_keep(v[k], sh.vals[(k * kBT + tid) ^ stride], k * kBT + tid, stride, size);
       }
-      __syncthreads();
     }
   }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < kPer; ++k)
+    if (k < per) sh.vals[k * kBT + tid] = v[k];
+  __syncthreads();
 
   // estimated tokens per cost for j = 0..N kept drafts (binary64 sums over
   // the ranked survivals, in rank order within each thread's run)
@@ -115,12 +173,23 @@ __global__ __launch_bounds__(kBT) void av_budget_kernel(int B, int max_k, const 
     best = double(B) / (double(draft_cost[0]) + double(verify_cost[0]));
     bj = 0;
   }
-  for (int j = j0; j < j1; ++j) {
-    run += double(sh.vals[j]);
-    const double r = (double(B) + run) / (double(draft_cost[j + 1]) + double(verify_cost[j + 1]));
-    if (r > best) {
-      best = r;
-      bj = j + 1;
+  for (int j0b = j0; j0b < j1; j0b += kPer) {
+    float dc[kPer], vc[kPer];  // the run's cost entries, loaded together
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      dc[q] = j0b + q < j1 ? draft_cost[j0b + q + 1] : 1.f;
+      vc[q] = j0b + q < j1 ? verify_cost[j0b + q + 1] : 1.f;
+    }
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      if (j0b + q < j1) {
+        run += double(sh.vals[j0b + q]);
+        const double r = (double(B) + run) / (double(dc[q]) + double(vc[q]));
+        if (r > best) {
+          best = r;
+          bj = j0b + q + 1;
+        }
+      }
     }
   }
   // the largest ratio; the smallest j among equal ones
@@ -154,30 +223,20 @@ __global__ __launch_bounds__(kBT) void av_budget_kernel(int B, int max_k, const 
 
   // kept drafts: survivals above the cut, then those equal to it in flat order
   const float cut = budget > 0 ? sh.vals[budget - 1] : 2.f;
-  const int rb = (B + kBT - 1) / kBT;  // requests per thread, contiguous
-  const int b0 = min(B, tid * rb), b1 = min(B, b0 + rb);
   int gt = 0, eq = 0;
-  for (int b = b0; b < b1; ++b) {
-    const int K = row_drafts(num_draft, b, max_k);
-    float s = 1.f;
-    for (int i = 0; i < K; ++i) {
-      s *= score[size_t(b) * max_k + i];
-      gt += s > cut;
-      eq += s == cut;
-    }
+  for (int e = b0 * max_k; e < b1 * max_k; ++e) {  // past K_b the survival is -1: neither
+    gt += sh.surv[e] > cut;
+    eq += sh.surv[e] == cut;
   }
   int gt_all = 0, eq_all = 0;
   (void)block_exclusive<int>(gt, sh.ipart, gt_all, tid);
   int eq_before = block_exclusive<int>(eq, sh.ipart, eq_all, tid);
   const int ties = budget - gt_all;  // equal survivals to keep, in flat order
   for (int b = b0; b < b1; ++b) {
-    const int K = row_drafts(num_draft, b, max_k);
-    float s = 1.f;
     int g = 0, e = 0;
-    for (int i = 0; i < K; ++i) {
-      s *= score[size_t(b) * max_k + i];
-      g += s > cut;
-      e += s == cut;
+    for (int i = 0; i < max_k; ++i) {
+      g += sh.surv[b * max_k + i] > cut;
+      e += sh.surv[b * max_k + i] == cut;
     }
     num_kept[b] = g + min(e, max(0, ties - eq_before));
     eq_before += e;

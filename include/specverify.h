@@ -216,7 +216,7 @@ int sv_av_fit_step(void* stream, int B, int max_k, const float* feature,
  * Device preconditions: 0 <= K_b <= max_k; scores in [0, 1]; every cost sum
  * read is > 0.
  * Returns SV_OK, or a negative sv_status without launching anything. */
-#define SV_BUDGET_MAX_ITEMS 8192
+#define SV_BUDGET_MAX_ITEMS 4096
 int sv_av_budget(void* stream, int B, int max_k, const float* score, const int32_t* num_draft,
                  const float* draft_cost_ms, const float* verify_cost_ms, int32_t* num_kept,
                  int32_t* budget);

@@ -174,7 +174,7 @@ def test_binding_refuses_host_tensors():
 
 
 @pytest.mark.parametrize("B,max_k,nulls,status", [
-    (-1, 4, (), -1), (4, -1, (), -1), (4, 17, (), -2), (2049, 4, (), -2), (513, 16, (), -2),
+    (-1, 4, (), -1), (4, -1, (), -1), (4, 17, (), -2), (1025, 4, (), -2), (257, 16, (), -2), (4097, 1, (), -2),
     (4, 4, ("num_draft",), -1), (4, 4, ("draft_cost",), -1), (4, 4, ("verify_cost",), -1),
     (4, 4, ("num_kept",), -1), (4, 4, ("budget",), -1), (4, 4, ("score",), -1),
     (0, 4, ("score", "num_draft", "draft_cost", "verify_cost", "num_kept", "budget"), 0),
