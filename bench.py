@@ -347,6 +347,26 @@ def main():
     res["extra"]["av_budget"] = {"us_per_call": e0.elapsed_time(e1) * 1000 / reps, "positions": n,
                                  "bound": "latency (one workgroup)", "budget": int(bo["budget"].item()),
                                  "note": "back-to-back calls between two events; synthetic linear cost tables"}
+    # calibration metrics of the estimator: one step's labelled items added to
+    # the stream accumulator, then AUC / log-loss / ECE (one workgroup each)
+    log("timing the calibration metrics")
+    acc = torch.zeros(sv.SV_CALIB_WORDS, dtype=torch.float64, device=dev)
+    sv.sv_av_calib_accumulate(score, outs[0]["labels"], acc)
+    torch.cuda.synchronize(dev)
+    e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    e0.record()
+    for _ in range(reps):
+        sv.sv_av_calib_accumulate(score, outs[0]["labels"], acc)
+    e1.record()
+    for _ in range(reps):
+        m = sv.sv_av_calib_metrics(acc)
+    e2.record()
+    torch.cuda.synchronize(dev)
+    mh = m.cpu().tolist()
+    res["extra"]["av_calibration"] = {"accumulate_us_per_call": e0.elapsed_time(e1) * 1000 / reps,
+                                      "metrics_us_per_call": e1.elapsed_time(e2) * 1000 / reps,
+                                      "positions": n, "bound": "latency (one workgroup)",
+                                      "auc": mh[0], "log_loss": mh[1], "ece": mh[2]}
     if args.copy_calibration > 0:
         log("copy calibration")
         n = args.copy_calibration << 20

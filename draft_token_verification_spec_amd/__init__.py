@@ -30,6 +30,8 @@ __all__ = [
     "sv_av_score",
     "sv_av_fit_step",
     "sv_av_budget",
+    "sv_av_calib_accumulate",
+    "sv_av_calib_metrics",
     "sv_set_verify_kernel",
     "sv_timing_enable",
     "sv_timing_read",
@@ -43,6 +45,8 @@ SV_MAX_K = 16
 SV_MAX_V = 1 << 21
 SV_MAX_B = 1 << 18
 SV_BUDGET_MAX_ITEMS = 4096
+SV_CALIB_AUC_BINS = 4096
+SV_CALIB_WORDS = 33 + 2 * SV_CALIB_AUC_BINS
 SV_F32, SV_BF16 = 0, 1
 SV_KERNEL_AUTO, SV_KERNEL_STREAMING, SV_KERNEL_RESIDENT = 0, 1, 2
 
@@ -68,6 +72,8 @@ _SIGNATURES = {
     "sv_av_fit_step": (_i, [_p, _i, _i, _p, _p, _p, _p, _f, _f, _i]),
     "sv_status_string": (ctypes.c_char_p, [_i]),
     "sv_av_budget": (_i, [_p, _i, _i, _p, _p, _p, _p, _p, _p]),
+    "sv_av_calib_accumulate": (_i, [_p, _i, _i, _p, _p, _p]),
+    "sv_av_calib_metrics": (_i, [_p, _p, _p, _i]),
     "sv_set_verify_kernel": (_i, [_i]),
     "sv_timing_enable": (_i, [_i]),
     "sv_timing_read": (_i, [_p, _i]),
@@ -131,6 +137,35 @@ def sv_av_budget(score: torch.Tensor, num_draft: torch.Tensor, draft_cost_ms: to
                               _ptr(verify_cost_ms), _ptr(o["num_kept"]), _ptr(o["budget"]))
     _check(st, "sv_av_budget")
     return o
+
+
+def sv_av_calib_accumulate(score: torch.Tensor, labels: torch.Tensor, accum: torch.Tensor) -> None:
+    """Add the labelled (score, label) items of one step to the calibration
+    accumulator (float64 [SV_CALIB_WORDS], zero-filled before a stream's
+    first step); see ``sv_av_calib_accumulate``."""
+    if score.dim() != 2:
+        raise ValueError("score must be [B, max_k]")
+    B, max_k = score.shape
+    dev = score.device
+    _dev(score, "score", torch.float32)
+    _dev(labels, "labels", torch.int8, B * max_k)
+    _dev(accum, "accum", torch.float64, SV_CALIB_WORDS)
+    _check(_load().sv_av_calib_accumulate(_stream(dev), B, max_k, _ptr(score), _ptr(labels), _ptr(accum)),
+           "sv_av_calib_accumulate")
+
+
+def sv_av_calib_metrics(accum: torch.Tensor, reset: bool = False, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """AUC, log-loss and ECE of the accumulated stream as a float64 [3]
+    device tensor (no host synchronisation); ``reset`` zero-fills the
+    accumulator afterwards."""
+    dev = accum.device
+    _dev(accum, "accum", torch.float64, SV_CALIB_WORDS)
+    if out is None:
+        out = torch.empty(3, dtype=torch.float64, device=dev)
+    _dev(out, "out", torch.float64, 3)
+    _check(_load().sv_av_calib_metrics(_stream(dev), _ptr(accum), _ptr(out), int(bool(reset))),
+           "sv_av_calib_metrics")
+    return out
 
 
 def sv_timing_enable(slots: int) -> None:

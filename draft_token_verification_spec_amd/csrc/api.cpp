@@ -184,6 +184,21 @@ int sv_av_budget(void* stream, int B, int max_k, const float* score, const int32
                                     static_cast<hipStream_t>(stream)));
 }
 
+int sv_av_calib_accumulate(void* stream, int B, int max_k, const float* score, const int8_t* labels,
+                           double* accum) {
+  if (B < 0 || max_k < 0) return SV_ERR_INVALID_ARG;
+  if (max_k > SV_MAX_K || B > SV_MAX_B) return SV_ERR_UNSUPPORTED;
+  if (!accum) return SV_ERR_INVALID_ARG;
+  if (B == 0 || max_k == 0) return SV_OK;
+  if (!score || !labels) return SV_ERR_INVALID_ARG;
+  return to_status(launch_calib_accumulate(B * max_k, score, labels, accum, static_cast<hipStream_t>(stream)));
+}
+
+int sv_av_calib_metrics(void* stream, double* accum, double* metrics, int reset) {
+  if (!accum || !metrics) return SV_ERR_INVALID_ARG;
+  return to_status(launch_calib_metrics(accum, metrics, reset ? 1 : 0, static_cast<hipStream_t>(stream)));
+}
+
 int sv_set_verify_kernel(int kernel) {
   if (kernel != SV_KERNEL_AUTO && kernel != SV_KERNEL_STREAMING && kernel != SV_KERNEL_RESIDENT)
     return SV_ERR_INVALID_ARG;

@@ -198,6 +198,9 @@ hipError_t launch_streaming(VerifyArgs a, int dtype, hipStream_t stream, const h
 hipError_t launch_av_score(const ScoreArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_av_budget(int B, int max_k, const float* score, const int32_t* num_draft, const float* draft_cost,
                             const float* verify_cost, int32_t* num_kept, int32_t* budget, hipStream_t stream);
+hipError_t launch_calib_accumulate(int items, const float* score, const int8_t* labels, double* accum,
+                                   hipStream_t stream);
+hipError_t launch_calib_metrics(double* accum, double* metrics, int reset, hipStream_t stream);
 hipError_t launch_av_fit(int B, int max_k, const float* feature, const int8_t* labels,
                          float* params, double* accum, float damping_c, float ridge,
                          int do_update, hipStream_t stream);

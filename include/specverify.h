@@ -221,6 +221,39 @@ int sv_av_budget(void* stream, int B, int max_k, const float* score, const int32
                  const float* draft_cost_ms, const float* verify_cost_ms, int32_t* num_kept,
                  int32_t* budget);
 
+/* Calibration metrics of the estimator over its labelled stream.
+ *
+ * [AV] "Other features considered": AUC = probability that an accepted draft
+ * scores above a rejected one (ties count half); log-loss = mean negative
+ * log-probability of the observed outcome; ECE = sum over probability bins of
+ * (share of the drafts in the bin) * |mean score - observed frequency|.
+ * The labels are the refit's ([AV] "Fitting the coefficients"): 1 accepted,
+ * 0 the first rejection, anything else (e.g. -1 from sv_spec_verify) no
+ * label, skipped.
+ *
+ * accum: caller-owned binary64 [SV_CALIB_WORDS], zero-filled before a
+ * stream's first call: labelled count, accepted count, sum of the log-loss
+ * terms (scores clamped to [1e-7, 1 - 1e-7]), per ECE bin (10 equal-width
+ * bins; score p in bin min(floor(10 p), 9)) the count, score sum and label
+ * sum, then per class (accepted, rejected) a histogram of the score over
+ * SV_CALIB_AUC_BINS equal-width bins.  The AUC is that of the binned scores:
+ * scores in one bin count as tied.
+ *
+ * sv_av_calib_accumulate adds B*max_k (score, label) items (row-major, e.g.
+ * the score and labels outputs of one verification step).  One workgroup
+ * with a fixed summation order: the same calls give bit-identical results.
+ * sv_av_calib_metrics writes metrics float64 [3] = AUC, log-loss, ECE (NaN
+ * when undefined: no labels, or no accepted or no rejected draft for the
+ * AUC) and, if reset != 0, zero-fills accum afterwards (a kernel store: safe
+ * inside a captured graph).
+ * Device preconditions: scores in [0, 1].  Both return SV_OK, or a negative
+ * sv_status without launching anything. */
+#define SV_CALIB_AUC_BINS 4096
+#define SV_CALIB_WORDS (33 + 2 * SV_CALIB_AUC_BINS)
+int sv_av_calib_accumulate(void* stream, int B, int max_k, const float* score, const int8_t* labels,
+                           double* accum);
+int sv_av_calib_metrics(void* stream, double* accum, double* metrics, int reset);
+
 /* Which kernel sv_spec_verify launches: a process-wide setting, default
  * SV_KERNEL_AUTO.  Both kernels compute the same outputs.
  *   SV_KERNEL_STREAMING  a statistics pass over every row, then a second pass

@@ -25,7 +25,7 @@ def test_every_declared_symbol_is_exported():
     names = declared_functions()
     assert set(names) == {"sv_workspace_size", "sv_spec_verify", "sv_av_score", "sv_av_fit_step",
                           "sv_status_string", "sv_set_verify_kernel", "sv_timing_enable", "sv_timing_read",
-                          "sv_av_budget"}
+                          "sv_av_budget", "sv_av_calib_accumulate", "sv_av_calib_metrics"}
     lib = ctypes.CDLL(sv.lib_path())
     for n in names:
         assert hasattr(lib, n), n
@@ -38,6 +38,8 @@ def test_header_constants_match_binding():
     assert re.search(r"#define SV_MAX_V \(1 << (\d+)\)", text).group(1) == str(sv.SV_MAX_V.bit_length() - 1)
     assert re.search(r"#define SV_MAX_B \(1 << (\d+)\)", text).group(1) == str(sv.SV_MAX_B.bit_length() - 1)
     assert int(re.search(r"#define SV_BUDGET_MAX_ITEMS (\d+)", text).group(1)) == sv.SV_BUDGET_MAX_ITEMS
+    assert int(re.search(r"#define SV_CALIB_AUC_BINS (\d+)", text).group(1)) == sv.SV_CALIB_AUC_BINS
+    assert re.search(r"#define SV_CALIB_WORDS \(33 \+ 2 \* SV_CALIB_AUC_BINS\)", text)
 
 
 def test_kernel_selector():
@@ -189,3 +191,21 @@ def test_budget_rejects_before_launch(B, max_k, nulls, status):
     lib.sv_av_budget.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int] + [ctypes.c_void_p] * 6
     assert lib.sv_av_budget(None, B, max_k, args["score"], args["num_draft"], args["draft_cost"],
                             args["verify_cost"], args["num_kept"], args["budget"]) == status
+
+
+def test_calib_rejects_before_launch():
+    lib = ctypes.CDLL(sv.lib_path())
+    fake = ctypes.c_void_p(16)
+    lib.sv_av_calib_accumulate.restype = ctypes.c_int
+    lib.sv_av_calib_accumulate.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int] + [ctypes.c_void_p] * 3
+    lib.sv_av_calib_metrics.restype = ctypes.c_int
+    lib.sv_av_calib_metrics.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int]
+    acc = lib.sv_av_calib_accumulate
+    assert acc(None, -1, 4, fake, fake, fake) == -1
+    assert acc(None, 4, 17, fake, fake, fake) == -2
+    assert acc(None, 4, 4, fake, fake, None) == -1
+    assert acc(None, 4, 4, None, fake, fake) == -1
+    assert acc(None, 4, 4, fake, None, fake) == -1
+    assert acc(None, 0, 4, None, None, fake) == 0  # nothing to add
+    assert lib.sv_av_calib_metrics(None, None, fake, 0) == -1
+    assert lib.sv_av_calib_metrics(None, fake, None, 1) == -1
