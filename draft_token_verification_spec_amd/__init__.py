@@ -32,6 +32,7 @@ __all__ = [
     "sv_av_budget",
     "sv_av_calib_accumulate",
     "sv_av_calib_metrics",
+    "sv_tts_grad",
     "sv_set_verify_kernel",
     "sv_timing_enable",
     "sv_timing_read",
@@ -74,6 +75,7 @@ _SIGNATURES = {
     "sv_av_budget": (_i, [_p, _i, _i, _p, _p, _p, _p, _p, _p]),
     "sv_av_calib_accumulate": (_i, [_p, _i, _i, _p, _p, _p]),
     "sv_av_calib_metrics": (_i, [_p, _p, _p, _i]),
+    "sv_tts_grad": (_i, [_p, _i, _i, _i, _i, _p, _p, _i64, _p, _p, _i64, _p, _p, _i64, _p, _p, _p, _f, _p, _p]),
     "sv_set_verify_kernel": (_i, [_i]),
     "sv_timing_enable": (_i, [_i]),
     "sv_timing_read": (_i, [_p, _i]),
@@ -166,6 +168,42 @@ def sv_av_calib_metrics(accum: torch.Tensor, reset: bool = False, out: Optional[
     _check(_load().sv_av_calib_metrics(_stream(dev), _ptr(accum), _ptr(out), int(bool(reset))),
            "sv_av_calib_metrics")
     return out
+
+
+def sv_tts_grad(draft_logits: torch.Tensor, draft_row_start: torch.Tensor, target_logits: torch.Tensor,
+                target_row_start: torch.Tensor, num_draft: torch.Tensor, temperature: torch.Tensor,
+                weights: torch.Tensor, max_k: int, lam: float = 0.0, *, prev_logits: Optional[torch.Tensor] = None,
+                prev_row_start: Optional[torch.Tensor] = None, out: Optional[dict] = None) -> dict:
+    """Distillation gradient and loss over the canvas; see ``sv_tts_grad``.
+    Returns ``grad`` [B*max_k, V] (the logits' dtype) and ``loss`` float32
+    [B, max_k]."""
+    dtype = _logits(target_logits, "target_logits")
+    V = target_logits.shape[1]
+    B = num_draft.numel()
+    dev = target_logits.device
+    if _logits(draft_logits, "draft_logits") != dtype or draft_logits.shape[1] != V:
+        raise ValueError("draft_logits and target_logits must share dtype and V")
+    _dev(draft_row_start, "draft_row_start", torch.int64, B)
+    _dev(target_row_start, "target_row_start", torch.int64, B)
+    _dev(num_draft, "num_draft", torch.int32)
+    _dev(temperature, "temperature", torch.float32, B)
+    _dev(weights, "weights", torch.float32, max_k)
+    if prev_logits is not None:
+        if _logits(prev_logits, "prev_logits") != dtype or prev_logits.shape[1] != V:
+            raise ValueError("prev_logits must share dtype and V with the draft rows")
+        _dev(prev_row_start, "prev_row_start", torch.int64, B)
+    o = {} if out is None else out
+    _need(o, "grad", (B * max_k, V), target_logits.dtype, dev)
+    _need(o, "loss", (B, max_k), torch.float32, dev)
+    _dev(o["grad"], "grad", target_logits.dtype, B * max_k * V)
+    _dev(o["loss"], "loss", torch.float32, B * max_k)
+    st = _load().sv_tts_grad(
+        _stream(dev), B, V, max_k, dtype, _ptr(draft_logits), _ptr(draft_row_start), draft_logits.stride(0),
+        _ptr(target_logits), _ptr(target_row_start), target_logits.stride(0),
+        _ptr(prev_logits), _ptr(prev_row_start), prev_logits.stride(0) if prev_logits is not None else V,
+        _ptr(num_draft), _ptr(temperature), _ptr(weights), float(lam), _ptr(o["grad"]), _ptr(o["loss"]))
+    _check(st, "sv_tts_grad")
+    return o
 
 
 def sv_timing_enable(slots: int) -> None:

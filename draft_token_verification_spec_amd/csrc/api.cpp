@@ -199,6 +199,25 @@ int sv_av_calib_metrics(void* stream, double* accum, double* metrics, int reset)
   return to_status(launch_calib_metrics(accum, metrics, reset ? 1 : 0, static_cast<hipStream_t>(stream)));
 }
 
+int sv_tts_grad(void* stream, int B, int V, int max_k, int dtype, const void* draft_logits,
+                const int64_t* draft_row_start, int64_t draft_row_stride, const void* target_logits,
+                const int64_t* target_row_start, int64_t target_row_stride, const void* prev_logits,
+                const int64_t* prev_row_start, int64_t prev_row_stride, const int32_t* num_draft,
+                const float* temperature, const float* weights, float lambda, void* grad, float* loss) {
+  if (B < 0 || V < 1 || max_k < 0 || !dtype_ok(dtype) || !(lambda >= 0.f)) return SV_ERR_INVALID_ARG;
+  if (max_k > SV_MAX_K || V > SV_MAX_V || B > SV_MAX_B) return SV_ERR_UNSUPPORTED;
+  if (B == 0 || max_k == 0) return SV_OK;
+  if (!draft_logits || !draft_row_start || !target_logits || !target_row_start || !num_draft || !temperature ||
+      !weights || !grad || !loss)
+    return SV_ERR_INVALID_ARG;
+  if (draft_row_stride < V || target_row_stride < V) return SV_ERR_INVALID_ARG;
+  if (prev_logits && (!prev_row_start || prev_row_stride < V)) return SV_ERR_INVALID_ARG;
+  return to_status(launch_tts_grad(B, V, max_k, dtype, draft_logits, draft_row_start, draft_row_stride,
+                                   target_logits, target_row_start, target_row_stride, prev_logits, prev_row_start,
+                                   prev_row_stride, num_draft, temperature, weights, lambda, grad, loss,
+                                   static_cast<hipStream_t>(stream)));
+}
+
 int sv_set_verify_kernel(int kernel) {
   if (kernel != SV_KERNEL_AUTO && kernel != SV_KERNEL_STREAMING && kernel != SV_KERNEL_RESIDENT)
     return SV_ERR_INVALID_ARG;

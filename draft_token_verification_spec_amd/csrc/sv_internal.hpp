@@ -201,6 +201,11 @@ hipError_t launch_av_budget(int B, int max_k, const float* score, const int32_t*
 hipError_t launch_calib_accumulate(int items, const float* score, const int8_t* labels, double* accum,
                                    hipStream_t stream);
 hipError_t launch_calib_metrics(double* accum, double* metrics, int reset, hipStream_t stream);
+hipError_t launch_tts_grad(int B, int V, int max_k, int dtype, const void* draft, const int64_t* draft_start,
+                           int64_t draft_stride, const void* target, const int64_t* target_start,
+                           int64_t target_stride, const void* prev, const int64_t* prev_start, int64_t prev_stride,
+                           const int32_t* num_draft, const float* temperature, const float* weights, float lambda,
+                           void* grad, float* loss, hipStream_t stream);
 hipError_t launch_av_fit(int B, int max_k, const float* feature, const int8_t* labels,
                          float* params, double* accum, float damping_c, float ridge,
                          int do_update, hipStream_t stream);

@@ -1,0 +1,248 @@
+// The test-time-speculation distillation gradient over the canvas.
+//
+// Page "ملخص تقني: التخمين في وقت الاختبار (TTS)", section "Algorithm",
+// step 3: one gradient step of the draft model on
+//   L_t(q) = KL~(p || q) + lambda * KL~(q_t || q)
+// with position weights w_k over the canvas.  For canvas position k of
+// request b (k < K_b) the kernel writes the gradient with respect to the
+// draft logits z, w_k * ((q - p) + lambda * (q - q_t)) / T, and the loss
+// w_k * (KL(p || q) + lambda * KL(q_t || q)), every distribution being
+// softmax(logits / T) (T = 0 counting as 1).
+//
+// One workgroup per canvas position: a statistics pass (online max and sum
+// of exp2 per row, each thread over its share, then the workgroup) and a
+// gradient pass over the same rows, 16 elements per row and thread in flight
+// per step.  HBM-bound: the rows are read twice, the gradient row written
+// once.
+#include "sv_device.hpp"
+
+namespace sv {
+
+namespace {
+
+constexpr int kTT = 256;  // threads
+// 16-byte vectors per row and thread per step: 16 elements of either type
+template <typename ET>
+constexpr int kTV = 16 / Elem<ET>::N;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Vectors base/N + k * kTT + t (k < kTV) of a row for thread t: elements
+// base + (k * kTT + t) * N .. + N - 1; past V: -inf.
+template <typename ET>
+__device__ __forceinline__ void load_step(const ET* row, int base, int V, uint4 (&v)[kTV<ET>], int tid) {
+  constexpr int N = Elem<ET>::N;
+  const bool al = is_aligned16(row);
+  if (al && base + kTT * kTV<ET> * N <= V) {
+#pragma unroll
+    for (int k = 0; k < kTV<ET>; ++k) v[k] = load_vec16<ET>(row + base + (k * kTT + tid) * N);
+  } else {
+#pragma unroll
+    for (int k = 0; k < kTV<ET>; ++k) v[k] = load_raw<ET>(row, base + (k * kTT + tid) * N, V, al);
+  }
+}
+
+// Online (max, sum of exp2((z - max) * c)) of one thread's elements.
+template <typename ET>
+__device__ __forceinline__ void online(const uint4 (&v)[kTV<ET>], float c, float& m, float& s) {
+  constexpr int N = Elem<ET>::N;
+  float mx = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < kTV<ET>; ++k)
+#pragma unroll
+    for (int j = 0; j < N; ++j) mx = fmaxf(mx, Elem<ET>::get(v[k], j));
+  if (mx == -INFINITY) return;
+  const float mn = fmaxf(m, mx);
+  float acc = (m == -INFINITY) ? 0.f : s * fast_exp2((m - mn) * c);
+#pragma unroll
+  for (int k = 0; k < kTV<ET>; ++k)
+#pragma unroll
+    for (int j = 0; j < N; ++j) acc += fast_exp2(fmaf(Elem<ET>::get(v[k], j), c, -mn * c));
+  m = mn;
+  s = acc;
+}
+
+// log2 normaliser of a row over the workgroup: log2 softmax(z / T)(v) = z c - k.
+__device__ __forceinline__ float block_norm(float m, float s, float c, float* red_m, float* red_s, int tid) {
+  float cnt = 0.f;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float m2 = __shfl_xor(m, o, 64), s2 = __shfl_xor(s, o, 64), c2 = 0.f;
+    merge_ms(m, s, cnt, m2, s2, c2, c);
+  }
+  if ((tid & 63) == 0) {
+    red_m[tid >> 6] = m;
+    red_s[tid >> 6] = s;
+  }
+  __syncthreads();
+  float M = red_m[0], S = red_s[0], C = 0.f;
+  for (int w = 1; w < kTT / 64; ++w) merge_ms(M, S, C, red_m[w], red_s[w], 0.f, c);
+  __syncthreads();
+  return M * c + fast_log2(S);
+}
+
+__device__ __forceinline__ float block_total(float x, float* red, int tid) {
+  x = wave_sum(x);
+  if ((tid & 63) == 0) red[tid >> 6] = x;
+  __syncthreads();
+  float t = 0.f;
+  for (int w = 0; w < kTT / 64; ++w) t += red[w];
+  __syncthreads();
+  return t;
+}
+
+// Round to bfloat16 (nearest, ties to even), as bits.
+__device__ __forceinline__ uint32_t to_bf16(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;  // NaN stays NaN
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+template <typename ET>
+__device__ __forceinline__ void store_grad(ET* out, int first, int V, const float (&g)[Elem<ET>::N], bool vec);
+
+template <>
+__device__ __forceinline__ void store_grad<uint16_t>(uint16_t* out, int first, int V, const float (&g)[8], bool vec) {
+  if (vec && first + 8 <= V) {
+    uint4 w;
+    w.x = to_bf16(g[0]) | (to_bf16(g[1]) << 16);
+    w.y = to_bf16(g[2]) | (to_bf16(g[3]) << 16);
+    w.z = to_bf16(g[4]) | (to_bf16(g[5]) << 16);
+    w.w = to_bf16(g[6]) | (to_bf16(g[7]) << 16);
+    *reinterpret_cast<uint4*>(out + first) = w;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (first + j < V) out[first + j] = uint16_t(to_bf16(g[j]));
+  }
+}
+
+template <>
+__device__ __forceinline__ void store_grad<float>(float* out, int first, int V, const float (&g)[4], bool vec) {
+  if (vec && first + 4 <= V) {
+    *reinterpret_cast<float4*>(out + first) = make_float4(g[0], g[1], g[2], g[3]);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (first + j < V) out[first + j] = g[j];
+  }
+}
+
+struct TtsArgs {
+  int B, V, max_k;
+  const void* draft;
+  const int64_t* draft_start;
+  int64_t draft_stride;
+  const void* target;
+  const int64_t* target_start;
+  int64_t target_stride;
+  const void* prev;  // null: the draft rows
+  const int64_t* prev_start;
+  int64_t prev_stride;
+  const int32_t* num_draft;
+  const float* temperature;
+  const float* weights;
+  float lambda;
+  void* grad;
+  float* loss;
+};
+
+template <typename ET, bool PREV>
+__device__ __forceinline__ void tts_position(const TtsArgs& a, const ET* rd, const ET* rt, const ET* rp, float c,
+                                             float invT, float w, ET* g, size_t o, int tid) {
+  constexpr int N = Elem<ET>::N;
+  constexpr int TV = kTV<ET>;
+  constexpr int STEP = kTT * TV * N;
+  __shared__ float red_m[kTT / 64], red_s[kTT / 64];
+  const int V = a.V;
+  // statistics
+  float md = -INFINITY, sd = 0.f, mt = -INFINITY, st = 0.f, mp = -INFINITY, sp = 0.f;
+  for (int base = 0; base < V; base += STEP) {
+    uint4 vd[TV], vt[TV], vp[TV];
+    load_step<ET>(rd, base, V, vd, tid);
+    load_step<ET>(rt, base, V, vt, tid);
+    if (PREV) load_step<ET>(rp, base, V, vp, tid);
+    online<ET>(vd, c, md, sd);
+    online<ET>(vt, c, mt, st);
+    if (PREV) online<ET>(vp, c, mp, sp);
+  }
+  const float kd = block_norm(md, sd, c, red_m, red_s, tid);
+  const float kt = block_norm(mt, st, c, red_m, red_s, tid);
+  const float kp = PREV ? block_norm(mp, sp, c, red_m, red_s, tid) : kd;
+  // gradient and loss (log2 units until the end)
+  const float lam = a.lambda;
+  const bool vec = is_aligned16(g);
+  float loss = 0.f;
+  for (int base = 0; base < V; base += STEP) {
+    uint4 vd[TV], vt[TV], vp[TV];
+    load_step<ET>(rd, base, V, vd, tid);
+    load_step<ET>(rt, base, V, vt, tid);
+    if (PREV) load_step<ET>(rp, base, V, vp, tid);
+#pragma unroll
+    for (int k = 0; k < TV; ++k) {
+      float gv[N];
+#pragma unroll
+      for (int j = 0; j < N; ++j) {
+        const float lq = fmaf(Elem<ET>::get(vd[k], j), c, -kd);
+        const float lp = fmaf(Elem<ET>::get(vt[k], j), c, -kt);
+        const float q = fast_exp2(lq), p = fast_exp2(lp);
+        float qt = q, lqt = lq;
+        if (PREV) {
+          lqt = fmaf(Elem<ET>::get(vp[k], j), c, -kp);
+          qt = fast_exp2(lqt);
+        }
+        gv[j] = w * ((q - p) + lam * (q - qt)) * invT;
+        loss += (p > 0.f ? p * (lp - lq) : 0.f) + (PREV && qt > 0.f ? lam * qt * (lqt - lq) : 0.f);
+      }
+      store_grad<ET>(g, base + (k * kTT + tid) * N, V, gv, vec);
+    }
+  }
+  loss = block_total(loss, red_m, tid);
+  if (tid == 0) a.loss[o] = w * kLn2 * loss;
+}
+
+template <typename ET, bool PREV>
+__global__ __launch_bounds__(kTT) __attribute__((amdgpu_waves_per_eu(4))) void tts_grad_kernel(TtsArgs a) {
+  const int tid = threadIdx.x;
+  const int b = int(blockIdx.x / uint32_t(a.max_k)), k = int(blockIdx.x % uint32_t(a.max_k));
+  const size_t o = size_t(b) * a.max_k + k;
+  const int K = min(max(a.num_draft[b], 0), a.max_k);
+  if (k >= K) {
+    if (tid == 0) a.loss[o] = NAN;
+    return;
+  }
+  const float T0 = a.temperature[b];
+  const float T = T0 > 0.f ? T0 : 1.f;
+  const float c = kLog2e / T;
+  const float w = a.weights[k];
+  const ET* rd = static_cast<const ET*>(a.draft) + (a.draft_start[b] + k) * a.draft_stride;
+  const ET* rt = static_cast<const ET*>(a.target) + (a.target_start[b] + k) * a.target_stride;
+  ET* g = static_cast<ET*>(a.grad) + o * size_t(a.V);
+  const ET* rp = PREV ? static_cast<const ET*>(a.prev) + (a.prev_start[b] + k) * a.prev_stride : rd;
+  tts_position<ET, PREV>(a, rd, rt, rp, c, 1.f / T, w, g, o, tid);
+}
+
+}  // namespace
+
+hipError_t launch_tts_grad(int B, int V, int max_k, int dtype, const void* draft, const int64_t* draft_start,
+                           int64_t draft_stride, const void* target, const int64_t* target_start,
+                           int64_t target_stride, const void* prev, const int64_t* prev_start, int64_t prev_stride,
+                           const int32_t* num_draft, const float* temperature, const float* weights, float lambda,
+                           void* grad, float* loss, hipStream_t stream) {
+  const TtsArgs a{B, V, max_k, draft, draft_start, draft_stride, target, target_start, target_stride, prev,
+                  prev_start, prev_stride, num_draft, temperature, weights, lambda, grad, loss};
+  const unsigned grid = unsigned(uint64_t(B) * uint64_t(max_k));
+  if (dtype == SV_BF16) {
+    if (prev)
+      hipLaunchKernelGGL((tts_grad_kernel<uint16_t, true>), dim3(grid), dim3(kTT), 0, stream, a);
+    else
+      hipLaunchKernelGGL((tts_grad_kernel<uint16_t, false>), dim3(grid), dim3(kTT), 0, stream, a);
+  } else {
+    if (prev)
+      hipLaunchKernelGGL((tts_grad_kernel<float, true>), dim3(grid), dim3(kTT), 0, stream, a);
+    else
+      hipLaunchKernelGGL((tts_grad_kernel<float, false>), dim3(grid), dim3(kTT), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace sv

@@ -254,6 +254,34 @@ int sv_av_calib_accumulate(void* stream, int B, int max_k, const float* score, c
                            double* accum);
 int sv_av_calib_metrics(void* stream, double* accum, double* metrics, int reset);
 
+/* The test-time-speculation distillation gradient over the canvas.
+ *
+ * Page "ملخص تقني: التخمين في وقت الاختبار (TTS)", section "Algorithm", step 3:
+ * one gradient step of the draft model on L_t(q) = KL~(p || q) + lambda *
+ * KL~(q_t || q) with position weights w_k.  For each canvas position k < K_b
+ * of request b (the draft row k, the target row k as teacher, and the row
+ * of the drafter that produced the canvas, q_t):
+ *   grad[(b*max_k + k)*V + v] = w_k * ((q(v) - p(v)) + lambda * (q(v) - q_t(v))) / T
+ *     (the gradient of the loss with respect to the draft logits z_v),
+ *   loss[b*max_k + k] = w_k * (KL(p || q) + lambda * KL(q_t || q))  (nats),
+ * with p, q, q_t = softmax(logits / T) at the request's temperature (T = 0
+ * counts as 1).  Rows k >= K_b: loss NaN, grad row not written.
+ *   draft_logits, target_logits: rows as for sv_spec_verify (dtype).
+ *   prev_logits / prev_row_start / prev_row_stride: the rows of q_t; NULL
+ *                  means the draft rows themselves (then the lambda terms
+ *                  vanish: the gradient step is taken at q = q_t).
+ *   num_draft int32 [B], temperature float [B], weights float [max_k] (w_k).
+ * Outputs (device): grad, elements of type dtype (bf16 rounded to nearest
+ * even), [B*max_k, V] row-major; loss float [B*max_k].
+ * Device preconditions as for sv_spec_verify.  Returns SV_OK, or a negative
+ * sv_status without launching anything. */
+int sv_tts_grad(void* stream, int B, int V, int max_k, int dtype,
+                const void* draft_logits, const int64_t* draft_row_start, int64_t draft_row_stride,
+                const void* target_logits, const int64_t* target_row_start, int64_t target_row_stride,
+                const void* prev_logits, const int64_t* prev_row_start, int64_t prev_row_stride,
+                const int32_t* num_draft, const float* temperature, const float* weights, float lambda,
+                void* grad, float* loss);
+
 /* Which kernel sv_spec_verify launches: a process-wide setting, default
  * SV_KERNEL_AUTO.  Both kernels compute the same outputs.
  *   SV_KERNEL_STREAMING  a statistics pass over every row, then a second pass

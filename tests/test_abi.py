@@ -25,7 +25,7 @@ def test_every_declared_symbol_is_exported():
     names = declared_functions()
     assert set(names) == {"sv_workspace_size", "sv_spec_verify", "sv_av_score", "sv_av_fit_step",
                           "sv_status_string", "sv_set_verify_kernel", "sv_timing_enable", "sv_timing_read",
-                          "sv_av_budget", "sv_av_calib_accumulate", "sv_av_calib_metrics"}
+                          "sv_av_budget", "sv_av_calib_accumulate", "sv_av_calib_metrics", "sv_tts_grad"}
     lib = ctypes.CDLL(sv.lib_path())
     for n in names:
         assert hasattr(lib, n), n
@@ -209,3 +209,26 @@ def test_calib_rejects_before_launch():
     assert acc(None, 0, 4, None, None, fake) == 0  # nothing to add
     assert lib.sv_av_calib_metrics(None, None, fake, 0) == -1
     assert lib.sv_av_calib_metrics(None, fake, None, 1) == -1
+
+
+def test_tts_grad_rejects_before_launch():
+    lib = ctypes.CDLL(sv.lib_path())
+    f = ctypes.c_void_p(16)
+    fn = lib.sv_tts_grad
+    fn.restype = ctypes.c_int
+    fn.argtypes = ([ctypes.c_void_p] + [ctypes.c_int] * 4 + [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64] * 3 +
+                   [ctypes.c_void_p] * 3 + [ctypes.c_float] + [ctypes.c_void_p] * 2)
+
+    def call(B=4, V=64, K=4, dt=1, lam=0.0, stride=64, pstride=64, prev=None, pstart=None, **nulls):
+        a = dict(draft=f, dstart=f, target=f, tstart=f, nd=f, temp=f, w=f, grad=f, loss=f)
+        a.update(nulls)
+        return fn(None, B, V, K, dt, a["draft"], a["dstart"], stride, a["target"], a["tstart"], stride,
+                  prev, pstart, pstride, a["nd"], a["temp"], a["w"], lam, a["grad"], a["loss"])
+
+    assert call(B=-1) == -1 and call(V=0) == -1 and call(dt=7) == -1 and call(lam=-1.0) == -1
+    assert call(K=17) == -2 and call(V=(1 << 21) + 1, stride=(1 << 21) + 1) == -2
+    for k in ("draft", "dstart", "target", "tstart", "nd", "temp", "w", "grad", "loss"):
+        assert call(**{k: None}) == -1, k
+    assert call(stride=63) == -1
+    assert call(prev=f, pstart=None) == -1 and call(prev=f, pstart=f, pstride=10) == -1
+    assert call(B=0) == 0 and call(K=0) == 0
