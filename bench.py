@@ -367,6 +367,30 @@ def main():
                                       "metrics_us_per_call": e1.elapsed_time(e2) * 1000 / reps,
                                       "positions": n, "bound": "latency (one workgroup)",
                                       "auc": mh[0], "log_loss": mh[1], "ece": mh[2]}
+    # the TTS distillation gradient over the same batch's canvas (draft rows
+    # against the target rows at the same positions), gradient rows in bf16
+    log("timing the distillation gradient")
+    d0 = sets[0][1]
+    wts = torch.ones(K, dtype=torch.float32, device=dev)
+    row_bytes = V * (2 if b0.dtype == "bf16" else 4)
+    alg = 3 * positions * row_bytes  # draft and target canvas rows read once, gradient rows written once
+    step(0)  # a verification of input set 0 on the workspace: its row statistics serve the second mode
+    tg = sv.sv_tts_grad(d0["draft"], d0["draft_row_start"], d0["target"], d0["target_row_start"], nd,
+                        d0["temperature"], wts, K, 0.0)
+    torch.cuda.synchronize(dev)
+    treps = 20
+    res["extra"]["tts_grad"] = {"algorithmic_bytes": alg, "bound": "hbm"}
+    for mode, vws in (("two_pass", None), ("verify_statistics", ws)):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(treps):
+            sv.sv_tts_grad(d0["draft"], d0["draft_row_start"], d0["target"], d0["target_row_start"], nd,
+                           d0["temperature"], wts, K, 0.0, verify_workspace=vws, out=tg)
+        e1.record()
+        torch.cuda.synchronize(dev)
+        tts_ms = e0.elapsed_time(e1) / treps
+        res["extra"]["tts_grad"][mode] = {"ms_per_call": tts_ms, "achieved_gbs": alg / (tts_ms * 1e-3) / 1e9,
+                                          "frac": alg / (tts_ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
     if args.copy_calibration > 0:
         log("copy calibration")
         n = args.copy_calibration << 20

@@ -75,7 +75,8 @@ _SIGNATURES = {
     "sv_av_budget": (_i, [_p, _i, _i, _p, _p, _p, _p, _p, _p]),
     "sv_av_calib_accumulate": (_i, [_p, _i, _i, _p, _p, _p]),
     "sv_av_calib_metrics": (_i, [_p, _p, _p, _i]),
-    "sv_tts_grad": (_i, [_p, _i, _i, _i, _i, _p, _p, _i64, _p, _p, _i64, _p, _p, _i64, _p, _p, _p, _f, _p, _p]),
+    "sv_tts_grad": (_i, [_p, _i, _i, _i, _i, _p, _p, _i64, _p, _p, _i64, _p, _p, _i64, _p, _p, _p, _f, _p, _p,
+                         _p, _sz]),
     "sv_set_verify_kernel": (_i, [_i]),
     "sv_timing_enable": (_i, [_i]),
     "sv_timing_read": (_i, [_p, _i]),
@@ -173,10 +174,12 @@ def sv_av_calib_metrics(accum: torch.Tensor, reset: bool = False, out: Optional[
 def sv_tts_grad(draft_logits: torch.Tensor, draft_row_start: torch.Tensor, target_logits: torch.Tensor,
                 target_row_start: torch.Tensor, num_draft: torch.Tensor, temperature: torch.Tensor,
                 weights: torch.Tensor, max_k: int, lam: float = 0.0, *, prev_logits: Optional[torch.Tensor] = None,
-                prev_row_start: Optional[torch.Tensor] = None, out: Optional[dict] = None) -> dict:
+                prev_row_start: Optional[torch.Tensor] = None, verify_workspace: Optional[Workspace] = None,
+                out: Optional[dict] = None) -> dict:
     """Distillation gradient and loss over the canvas; see ``sv_tts_grad``.
-    Returns ``grad`` [B*max_k, V] (the logits' dtype) and ``loss`` float32
-    [B, max_k]."""
+    ``verify_workspace``: the Workspace of the sv_spec_verify call just made
+    on the same rows, whose row statistics are then reused.  Returns ``grad``
+    [B*max_k, V] (the logits' dtype) and ``loss`` float32 [B, max_k]."""
     dtype = _logits(target_logits, "target_logits")
     V = target_logits.shape[1]
     B = num_draft.numel()
@@ -197,11 +200,15 @@ def sv_tts_grad(draft_logits: torch.Tensor, draft_row_start: torch.Tensor, targe
     _need(o, "loss", (B, max_k), torch.float32, dev)
     _dev(o["grad"], "grad", target_logits.dtype, B * max_k * V)
     _dev(o["loss"], "loss", torch.float32, B * max_k)
+    ws = None
+    if verify_workspace is not None:
+        ws = verify_workspace.get(dev, sv_workspace_size(B, V, max_k, dtype))
     st = _load().sv_tts_grad(
         _stream(dev), B, V, max_k, dtype, _ptr(draft_logits), _ptr(draft_row_start), draft_logits.stride(0),
         _ptr(target_logits), _ptr(target_row_start), target_logits.stride(0),
         _ptr(prev_logits), _ptr(prev_row_start), prev_logits.stride(0) if prev_logits is not None else V,
-        _ptr(num_draft), _ptr(temperature), _ptr(weights), float(lam), _ptr(o["grad"]), _ptr(o["loss"]))
+        _ptr(num_draft), _ptr(temperature), _ptr(weights), float(lam), _ptr(o["grad"]), _ptr(o["loss"]),
+        _ptr(ws), ws.numel() if ws is not None else 0)
     _check(st, "sv_tts_grad")
     return o
 

@@ -144,29 +144,57 @@ struct TtsArgs {
   float lambda;
   void* grad;
   float* loss;
+  // row statistics of a preceding sv_spec_verify call on the same rows
+  // (its workspace's segment partials), or null
+  const Partial* stats;
+  int R, nseg2;
 };
 
-template <typename ET, bool PREV>
+// log2 normaliser of a row from its segment partials (in segment order).
+__device__ __forceinline__ float stats_norm(const Partial* p, int n, float c, float* red_m, float* red_s, int tid) {
+  float m = -INFINITY, s = 0.f, cnt = 0.f;
+  for (int q = tid; q < n; q += kTT) {
+    const Partial x = p[q];
+    merge_ms(m, s, cnt, x.m, x.s + x.cnt, 0.f, c);
+  }
+  return block_norm(m, s, c, red_m, red_s, tid);
+}
+
+template <typename ET, bool PREV, bool REUSE>
 __device__ __forceinline__ void tts_position(const TtsArgs& a, const ET* rd, const ET* rt, const ET* rp, float c,
-                                             float invT, float w, ET* g, size_t o, int tid) {
+                                             float invT, float w, ET* g, size_t o, int b, int kpos, int tid) {
   constexpr int N = Elem<ET>::N;
   constexpr int TV = kTV<ET>;
   constexpr int STEP = kTT * TV * N;
   __shared__ float red_m[kTT / 64], red_s[kTT / 64];
   const int V = a.V;
-  // statistics
+  // statistics: a pass over the rows, or (REUSE) the verification's
+  // partials of the draft and target rows and a pass over q_t's rows only
   float md = -INFINITY, sd = 0.f, mt = -INFINITY, st = 0.f, mp = -INFINITY, sp = 0.f;
-  for (int base = 0; base < V; base += STEP) {
-    uint4 vd[TV], vt[TV], vp[TV];
-    load_step<ET>(rd, base, V, vd, tid);
-    load_step<ET>(rt, base, V, vt, tid);
-    if (PREV) load_step<ET>(rp, base, V, vp, tid);
-    online<ET>(vd, c, md, sd);
-    online<ET>(vt, c, mt, st);
-    if (PREV) online<ET>(vp, c, mp, sp);
+  if (!REUSE || PREV) {
+    for (int base = 0; base < V; base += STEP) {
+      uint4 vd[TV], vt[TV], vp[TV];
+      if (!REUSE) {
+        load_step<ET>(rd, base, V, vd, tid);
+        load_step<ET>(rt, base, V, vt, tid);
+      }
+      if (PREV) load_step<ET>(rp, base, V, vp, tid);
+      if (!REUSE) {
+        online<ET>(vd, c, md, sd);
+        online<ET>(vt, c, mt, st);
+      }
+      if (PREV) online<ET>(vp, c, mp, sp);
+    }
   }
-  const float kd = block_norm(md, sd, c, red_m, red_s, tid);
-  const float kt = block_norm(mt, st, c, red_m, red_s, tid);
+  float kd, kt;
+  if (REUSE) {
+    const Partial* base = a.stats + size_t(b) * a.R * a.nseg2;
+    kd = stats_norm(base + size_t(kpos) * a.nseg2, a.nseg2, c, red_m, red_s, tid);
+    kt = stats_norm(base + size_t(a.max_k + kpos) * a.nseg2, a.nseg2, c, red_m, red_s, tid);
+  } else {
+    kd = block_norm(md, sd, c, red_m, red_s, tid);
+    kt = block_norm(mt, st, c, red_m, red_s, tid);
+  }
   const float kp = PREV ? block_norm(mp, sp, c, red_m, red_s, tid) : kd;
   // gradient and loss (log2 units until the end)
   const float lam = a.lambda;
@@ -200,7 +228,7 @@ __device__ __forceinline__ void tts_position(const TtsArgs& a, const ET* rd, con
   if (tid == 0) a.loss[o] = w * kLn2 * loss;
 }
 
-template <typename ET, bool PREV>
+template <typename ET, bool PREV, bool REUSE>
 __global__ __launch_bounds__(kTT) __attribute__((amdgpu_waves_per_eu(4))) void tts_grad_kernel(TtsArgs a) {
   const int tid = threadIdx.x;
   const int b = int(blockIdx.x / uint32_t(a.max_k)), k = int(blockIdx.x % uint32_t(a.max_k));
@@ -218,7 +246,15 @@ __global__ __launch_bounds__(kTT) __attribute__((amdgpu_waves_per_eu(4))) void t
   const ET* rt = static_cast<const ET*>(a.target) + (a.target_start[b] + k) * a.target_stride;
   ET* g = static_cast<ET*>(a.grad) + o * size_t(a.V);
   const ET* rp = PREV ? static_cast<const ET*>(a.prev) + (a.prev_start[b] + k) * a.prev_stride : rd;
-  tts_position<ET, PREV>(a, rd, rt, rp, c, 1.f / T, w, g, o, tid);
+  tts_position<ET, PREV, REUSE>(a, rd, rt, rp, c, 1.f / T, w, g, o, b, k, tid);
+}
+
+template <typename ET, bool PREV>
+void launch_tts_kind(const TtsArgs& a, unsigned grid, hipStream_t stream) {
+  if (a.stats)
+    hipLaunchKernelGGL((tts_grad_kernel<ET, PREV, true>), dim3(grid), dim3(kTT), 0, stream, a);
+  else
+    hipLaunchKernelGGL((tts_grad_kernel<ET, PREV, false>), dim3(grid), dim3(kTT), 0, stream, a);
 }
 
 }  // namespace
@@ -227,20 +263,21 @@ hipError_t launch_tts_grad(int B, int V, int max_k, int dtype, const void* draft
                            int64_t draft_stride, const void* target, const int64_t* target_start,
                            int64_t target_stride, const void* prev, const int64_t* prev_start, int64_t prev_stride,
                            const int32_t* num_draft, const float* temperature, const float* weights, float lambda,
-                           void* grad, float* loss, hipStream_t stream) {
-  const TtsArgs a{B, V, max_k, draft, draft_start, draft_stride, target, target_start, target_stride, prev,
-                  prev_start, prev_stride, num_draft, temperature, weights, lambda, grad, loss};
+                           void* grad, float* loss, const Partial* stats, int R, int nseg2, hipStream_t stream) {
+  const TtsArgs a{B,           V,       max_k, draft,  draft_start, draft_stride, target,
+                  target_start, target_stride, prev, prev_start, prev_stride, num_draft, temperature,
+                  weights,     lambda,  grad,  loss,   stats,       R,            nseg2};
   const unsigned grid = unsigned(uint64_t(B) * uint64_t(max_k));
   if (dtype == SV_BF16) {
     if (prev)
-      hipLaunchKernelGGL((tts_grad_kernel<uint16_t, true>), dim3(grid), dim3(kTT), 0, stream, a);
+      launch_tts_kind<uint16_t, true>(a, grid, stream);
     else
-      hipLaunchKernelGGL((tts_grad_kernel<uint16_t, false>), dim3(grid), dim3(kTT), 0, stream, a);
+      launch_tts_kind<uint16_t, false>(a, grid, stream);
   } else {
     if (prev)
-      hipLaunchKernelGGL((tts_grad_kernel<float, true>), dim3(grid), dim3(kTT), 0, stream, a);
+      launch_tts_kind<float, true>(a, grid, stream);
     else
-      hipLaunchKernelGGL((tts_grad_kernel<float, false>), dim3(grid), dim3(kTT), 0, stream, a);
+      launch_tts_kind<float, false>(a, grid, stream);
   }
   return hipGetLastError();
 }

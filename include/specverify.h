@@ -271,16 +271,25 @@ int sv_av_calib_metrics(void* stream, double* accum, double* metrics, int reset)
  *                  means the draft rows themselves (then the lambda terms
  *                  vanish: the gradient step is taken at q = q_t).
  *   num_draft int32 [B], temperature float [B], weights float [max_k] (w_k).
+ *   verify_workspace, workspace_bytes: NULL, or the workspace of the
+ *                  sv_spec_verify call just made on the same rows, B, V,
+ *                  max_k, dtype, temperatures and row starts (no call on that
+ *                  workspace in between): the softmax statistics of the draft
+ *                  and target rows are then taken from it instead of a pass
+ *                  over the rows.  That call must have read every canvas
+ *                  draft row: each request stochastic (T > 0), or the call
+ *                  made with av_feature.
  * Outputs (device): grad, elements of type dtype (bf16 rounded to nearest
  * even), [B*max_k, V] row-major; loss float [B*max_k].
  * Device preconditions as for sv_spec_verify.  Returns SV_OK, or a negative
- * sv_status without launching anything. */
+ * sv_status without launching anything (SV_ERR_WORKSPACE if workspace_bytes
+ * is below sv_workspace_size for these sizes). */
 int sv_tts_grad(void* stream, int B, int V, int max_k, int dtype,
                 const void* draft_logits, const int64_t* draft_row_start, int64_t draft_row_stride,
                 const void* target_logits, const int64_t* target_row_start, int64_t target_row_stride,
                 const void* prev_logits, const int64_t* prev_row_start, int64_t prev_row_stride,
                 const int32_t* num_draft, const float* temperature, const float* weights, float lambda,
-                void* grad, float* loss);
+                void* grad, float* loss, const void* verify_workspace, size_t workspace_bytes);
 
 /* Which kernel sv_spec_verify launches: a process-wide setting, default
  * SV_KERNEL_AUTO.  Both kernels compute the same outputs.

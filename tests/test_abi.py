@@ -217,13 +217,14 @@ def test_tts_grad_rejects_before_launch():
     fn = lib.sv_tts_grad
     fn.restype = ctypes.c_int
     fn.argtypes = ([ctypes.c_void_p] + [ctypes.c_int] * 4 + [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64] * 3 +
-                   [ctypes.c_void_p] * 3 + [ctypes.c_float] + [ctypes.c_void_p] * 2)
+                   [ctypes.c_void_p] * 3 + [ctypes.c_float] + [ctypes.c_void_p] * 3 + [ctypes.c_size_t])
 
-    def call(B=4, V=64, K=4, dt=1, lam=0.0, stride=64, pstride=64, prev=None, pstart=None, **nulls):
+    def call(B=4, V=64, K=4, dt=1, lam=0.0, stride=64, pstride=64, prev=None, pstart=None, ws=None, wsb=0,
+             **nulls):
         a = dict(draft=f, dstart=f, target=f, tstart=f, nd=f, temp=f, w=f, grad=f, loss=f)
         a.update(nulls)
         return fn(None, B, V, K, dt, a["draft"], a["dstart"], stride, a["target"], a["tstart"], stride,
-                  prev, pstart, pstride, a["nd"], a["temp"], a["w"], lam, a["grad"], a["loss"])
+                  prev, pstart, pstride, a["nd"], a["temp"], a["w"], lam, a["grad"], a["loss"], ws, wsb)
 
     assert call(B=-1) == -1 and call(V=0) == -1 and call(dt=7) == -1 and call(lam=-1.0) == -1
     assert call(K=17) == -2 and call(V=(1 << 21) + 1, stride=(1 << 21) + 1) == -2
@@ -232,3 +233,4 @@ def test_tts_grad_rejects_before_launch():
     assert call(stride=63) == -1
     assert call(prev=f, pstart=None) == -1 and call(prev=f, pstart=f, pstride=10) == -1
     assert call(B=0) == 0 and call(K=0) == 0
+    assert call(ws=f, wsb=sv.sv_workspace_size(4, 64, 4, 1) - 1) == -3  # too small a verification workspace

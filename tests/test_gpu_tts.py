@@ -119,3 +119,36 @@ def test_identical_rows_and_benchmark_shape():
     torch.cuda.synchronize()
     assert float(same["grad"].float().abs().max()) == 0.0
     assert np.nanmax(np.abs(same["loss"].cpu().numpy())) == 0.0
+
+
+@pytest.mark.parametrize("prev", [False, True])
+def test_statistics_reused_from_the_verification(prev):
+    """The gradient taken with the row statistics of the sv_spec_verify call
+    just made on the same rows equals the oracle's like the two-pass one."""
+    b = gen.make_batch("bf16_b64_k5_v32000", trial=3)
+    from gpu_harness import to_device
+    d = to_device(b)
+    print(f"case tts reuse prev={prev}", flush=True)
+    ws = sv.Workspace()
+    sv.sv_spec_verify(d["draft"], d["draft_row_start"], d["target"], d["target_row_start"], d["num_draft"],
+                      d["draft_tokens"], d["temperature"], d["u_accept"], d["u_residual"], d["u_bonus"],
+                      max_k=b.max_k, want_feature=True, workspace=ws)
+    w = torch.linspace(1.0, 0.5, b.max_k, device=DEV)
+    prev_rows = (d["draft"].float() + 0.25).to(d["draft"].dtype) if prev else None
+    kw = dict(prev_logits=prev_rows, prev_row_start=d["draft_row_start"] if prev else None)
+    out = sv.sv_tts_grad(d["draft"], d["draft_row_start"], d["target"], d["target_row_start"], d["num_draft"],
+                         d["temperature"], w, b.max_k, 0.4, verify_workspace=ws, **kw)
+    torch.cuda.synchronize()
+    loss = out["loss"].cpu().numpy()
+    wh = w.cpu().numpy()
+    pr = prev_rows.float().cpu().numpy() if prev else None
+    for r in range(0, b.B, 7):
+        for k in range(int(b.num_draft[r])):
+            zd = gen.bf16_bits_to_f32(b.draft[int(b.draft_row_start[r]) + k])
+            zt = gen.bf16_bits_to_f32(b.target[int(b.target_row_start[r]) + k])
+            zp = pr[int(b.draft_row_start[r]) + k] if prev else None
+            gref, lref = ot.position(zd, zt, zp, float(b.temperature[r]), float(wh[k]), 0.4)
+            g = out["grad"][r * b.max_k + k].float().cpu().numpy()
+            scale = row_scale(zd, zt, float(b.temperature[r]), float(wh[k]))
+            assert np.all(np.abs(g - gref) <= REL["bf16"] * np.abs(gref) + ABS["bf16"] * scale)
+            assert loss[r, k] == pytest.approx(lref, rel=1e-4, abs=1e-6)
