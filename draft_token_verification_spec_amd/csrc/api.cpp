@@ -204,7 +204,7 @@ int sv_tts_grad(void* stream, int B, int V, int max_k, int dtype, const void* dr
                 const int64_t* target_row_start, int64_t target_row_stride, const void* prev_logits,
                 const int64_t* prev_row_start, int64_t prev_row_stride, const int32_t* num_draft,
                 const float* temperature, const float* weights, float lambda, void* grad, float* loss,
-                const void* verify_workspace, size_t workspace_bytes) {
+                void* verify_workspace, size_t workspace_bytes) {
   if (B < 0 || V < 1 || max_k < 0 || !dtype_ok(dtype) || !(lambda >= 0.f)) return SV_ERR_INVALID_ARG;
   if (max_k > SV_MAX_K || V > SV_MAX_V || B > SV_MAX_B) return SV_ERR_UNSUPPORTED;
   if (B == 0 || max_k == 0) return SV_OK;
@@ -214,19 +214,23 @@ int sv_tts_grad(void* stream, int B, int V, int max_k, int dtype, const void* dr
   if (draft_row_stride < V || target_row_stride < V) return SV_ERR_INVALID_ARG;
   if (prev_logits && (!prev_row_start || prev_row_stride < V)) return SV_ERR_INVALID_ARG;
   const Partial* stats = nullptr;
+  float* loss_parts = nullptr;
+  uint32_t* tickets = nullptr;
   int R = 0, nseg2 = 0;
   if (verify_workspace) {
     if (check_sizes(B, V, max_k, dtype) != SV_OK) return SV_ERR_UNSUPPORTED;
     const WsLayout L = ws_layout(B, V, max_k, dtype);
     if (workspace_bytes < L.total) return SV_ERR_WORKSPACE;
     stats = reinterpret_cast<const Partial*>(static_cast<const char*>(verify_workspace) + L.partials);
+    loss_parts = reinterpret_cast<float*>(static_cast<char*>(verify_workspace) + L.tts_loss);
+    tickets = reinterpret_cast<uint32_t*>(static_cast<char*>(verify_workspace) + L.tickets);
     R = L.R;
     nseg2 = L.nseg2;
   }
   return to_status(launch_tts_grad(B, V, max_k, dtype, draft_logits, draft_row_start, draft_row_stride,
                                    target_logits, target_row_start, target_row_stride, prev_logits, prev_row_start,
-                                   prev_row_stride, num_draft, temperature, weights, lambda, grad, loss, stats, R,
-                                   nseg2, static_cast<hipStream_t>(stream)));
+                                   prev_row_stride, num_draft, temperature, weights, lambda, grad, loss, stats,
+                                   loss_parts, tickets, R, nseg2, static_cast<hipStream_t>(stream)));
 }
 
 int sv_set_verify_kernel(int kernel) {

@@ -80,7 +80,9 @@ __device__ __forceinline__ int fresh_tid() {
 }
 
 // Vector k of thread t holds elements hb + (k * kThreads + t) * N .. + N-1 of
-// its row (token order: vector, thread, element); past the end: -inf.
+// its row (token order: vector, thread, element); past the end: -inf.  The
+// rows are streamed (non-temporal loads): each is read once per call, apart
+// from the few segments the verdict and the draw read again.
 // load_vecs loads vectors K0 .. K0 + NV - 1 of the segment at hb.
 template <typename ET, int NV, int K0>
 __device__ __forceinline__ void load_vecs(const ET* row, int hb0, int V, uint4 (&v)[NV]) {
@@ -90,7 +92,7 @@ __device__ __forceinline__ void load_vecs(const ET* row, int hb0, int V, uint4 (
   const int hb = hb0 + K0 * kThreads * N;
   if (al && hb + kThreads * NV * N <= V) {
 #pragma unroll
-    for (int k = 0; k < NV; ++k) v[k] = load_vec16<ET>(row + hb + (k * kThreads + tid) * N);
+    for (int k = 0; k < NV; ++k) v[k] = load_stream16(row + hb + (k * kThreads + tid) * N);
   } else if (al && V % N == 0) {
     // the tail of an aligned row: each vector is wholly inside or wholly past
     // the end.  Every lane loads (the row's last vector standing in for one
@@ -98,7 +100,7 @@ __device__ __forceinline__ void load_vecs(const ET* row, int hb0, int V, uint4 (
     // so the loads are issued back to back instead of one branch at a time.
     constexpr uint32_t ninf = N == 8 ? (Elem<ET>::kNegInf << 16 | Elem<ET>::kNegInf) : Elem<ET>::kNegInf;
 #pragma unroll
-    for (int k = 0; k < NV; ++k) v[k] = load_vec16<ET>(row + min(hb + (k * kThreads + tid) * N, V - N));
+    for (int k = 0; k < NV; ++k) v[k] = load_stream16(row + min(hb + (k * kThreads + tid) * N, V - N));
     const int t = fresh_tid(), lim = (V - hb) / N;  // vectors of the tail
 #pragma unroll
     for (int k = 0; k < NV; ++k) {

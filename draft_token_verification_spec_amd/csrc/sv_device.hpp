@@ -82,6 +82,15 @@ __device__ __forceinline__ uint4 load_vec16(const ET* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
 
+// The same, streaming: marked non-temporal, for data read once (the
+// logit rows of a verification or a distillation step), so that it does not
+// displace what the caches hold for other work.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_stream16(const void* p) {
+  const u32x4 x = __builtin_nontemporal_load(static_cast<const u32x4*>(p));
+  return make_uint4(x.x, x.y, x.z, x.w);
+}
+
 __device__ __forceinline__ bool is_aligned16(const void* p) {
   return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
 }

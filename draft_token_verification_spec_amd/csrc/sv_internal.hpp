@@ -75,7 +75,7 @@ constexpr size_t kCtrlBytes = size_t(kParts + 2) * kLineWords * 4;
 constexpr int kCtrlWork = 0;                         // claim counter of partition p: kCtrlWork + p * kLineWords
 constexpr int kCtrlExit = kParts * kLineWords;       // workgroups that finished
 constexpr int kCtrlError = (kParts + 1) * kLineWords;  // set if a bounded wait ever expired
-constexpr int kArenaArrays = 1;  // tickets (scoring kernel)
+constexpr int kArenaArrays = 1;  // tickets (scoring and distillation kernels)
 // Words of request b's block (register-resident kernel), one 128-byte line:
 constexpr int kReqWords = 32;
 constexpr int kWRow = 0;      // kWRow + i: arrivals of row i (i = 0..SV_MAX_K)
@@ -108,12 +108,13 @@ __host__ __device__ constexpr uint64_t ready_slot(uint32_t bits) { return (uint6
 
 struct WsLayout {
   size_t ctrl;      // uint32 control block (claim/exit counters, error flag)
-  size_t tickets;   // uint32 [SV_MAX_B]  arrivals per request (scoring kernel)
+  size_t tickets;   // uint32 [SV_MAX_B]  arrivals per request (scoring and distillation kernels)
   size_t reqw;      // uint32 [SV_MAX_B][kReqWords]  request blocks (register-resident kernel)
   size_t partials;  // Partial [B][R][nseg2]
   size_t zval;      // float [B][R]       logit at the draft token, per row
   size_t segsum;    // float [2][B][nseg2]  weight of each sampling segment per draw round (register-resident kernel)
   size_t tagged;    // uint64 [B][nseg2][kDrawSlices]  hand-off slots of the draw's slice weights
+  size_t tts_loss;  // float [B][max_k][nseg2]  distillation loss per canvas row segment
   size_t total;
   int nseg;   // 64 KiB statistics segments per row
   int nseg2;  // 32 KiB half segments per row (partials are strided by this)
@@ -132,7 +133,8 @@ inline WsLayout ws_layout(int B, int V, int max_k, int dtype) {
   L.zval = L.partials + align256(size_t(B) * L.R * L.nseg2 * sizeof(Partial));
   L.segsum = L.zval + align256(size_t(B) * L.R * 4);
   L.tagged = L.segsum + align256(2 * size_t(B) * L.nseg2 * 4);
-  L.total = L.tagged + align256(size_t(B) * L.nseg2 * kDrawSlices * 8);
+  L.tts_loss = L.tagged + align256(size_t(B) * L.nseg2 * kDrawSlices * 8);
+  L.total = L.tts_loss + align256(size_t(B) * max_k * L.nseg2 * 4);
   return L;
 }
 
@@ -205,7 +207,8 @@ hipError_t launch_tts_grad(int B, int V, int max_k, int dtype, const void* draft
                            int64_t draft_stride, const void* target, const int64_t* target_start,
                            int64_t target_stride, const void* prev, const int64_t* prev_start, int64_t prev_stride,
                            const int32_t* num_draft, const float* temperature, const float* weights, float lambda,
-                           void* grad, float* loss, const Partial* stats, int R, int nseg2, hipStream_t stream);
+                           void* grad, float* loss, const Partial* stats, float* loss_parts, uint32_t* tickets, int R, int nseg2,
+                           hipStream_t stream);
 hipError_t launch_av_fit(int B, int max_k, const float* feature, const int8_t* labels,
                          float* params, double* accum, float damping_c, float ridge,
                          int do_update, hipStream_t stream);

@@ -90,6 +90,13 @@ __device__ __forceinline__ float block_total(float x, float* red, int tid) {
   return t;
 }
 
+// Streaming 16-byte store: a gradient row is written once and not read
+// back here, so it is not kept in the caches.
+__device__ __forceinline__ void store_stream16(void* p, uint32_t x, uint32_t y, uint32_t z, uint32_t w) {
+  const u32x4 v = {x, y, z, w};
+  __builtin_nontemporal_store(v, static_cast<u32x4*>(p));
+}
+
 // Round to bfloat16 (nearest, ties to even), as bits.
 __device__ __forceinline__ uint32_t to_bf16(float f) {
   const uint32_t u = __float_as_uint(f);
@@ -103,12 +110,8 @@ __device__ __forceinline__ void store_grad(ET* out, int first, int V, const floa
 template <>
 __device__ __forceinline__ void store_grad<uint16_t>(uint16_t* out, int first, int V, const float (&g)[8], bool vec) {
   if (vec && first + 8 <= V) {
-    uint4 w;
-    w.x = to_bf16(g[0]) | (to_bf16(g[1]) << 16);
-    w.y = to_bf16(g[2]) | (to_bf16(g[3]) << 16);
-    w.z = to_bf16(g[4]) | (to_bf16(g[5]) << 16);
-    w.w = to_bf16(g[6]) | (to_bf16(g[7]) << 16);
-    *reinterpret_cast<uint4*>(out + first) = w;
+    store_stream16(out + first, to_bf16(g[0]) | (to_bf16(g[1]) << 16), to_bf16(g[2]) | (to_bf16(g[3]) << 16),
+                   to_bf16(g[4]) | (to_bf16(g[5]) << 16), to_bf16(g[6]) | (to_bf16(g[7]) << 16));
   } else {
 #pragma unroll
     for (int j = 0; j < 8; ++j)
@@ -119,7 +122,8 @@ __device__ __forceinline__ void store_grad<uint16_t>(uint16_t* out, int first, i
 template <>
 __device__ __forceinline__ void store_grad<float>(float* out, int first, int V, const float (&g)[4], bool vec) {
   if (vec && first + 4 <= V) {
-    *reinterpret_cast<float4*>(out + first) = make_float4(g[0], g[1], g[2], g[3]);
+    store_stream16(out + first, __float_as_uint(g[0]), __float_as_uint(g[1]), __float_as_uint(g[2]),
+                   __float_as_uint(g[3]));
   } else {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
@@ -147,6 +151,8 @@ struct TtsArgs {
   // row statistics of a preceding sv_spec_verify call on the same rows
   // (its workspace's segment partials), or null
   const Partial* stats;
+  float* loss_parts;  // [B][max_k][nseg2] (segmented kernel)
+  uint32_t* tickets;  // arrival counters per request slot (segmented kernel)
   int R, nseg2;
 };
 
@@ -249,12 +255,118 @@ __global__ __launch_bounds__(kTT) __attribute__((amdgpu_waves_per_eu(4))) void t
   tts_position<ET, PREV, REUSE>(a, rd, rt, rp, c, 1.f / T, w, g, o, b, k, tid);
 }
 
+// The gradient by row segments, with the draft and target rows' statistics
+// taken from the verification: workgroup (position, segment s) reads 32 KiB
+// of each row (in two 16 KiB halves) and writes its slice of the gradient
+// row.  Its loss goes to loss_parts; the last workgroup of a request to
+// arrive sums each position's segment losses in segment order, so the loss
+// does not depend on the arrival order.
+// log2 normaliser of a row from its segment partials, merged by one wave
+// (merge_ms is symmetric, so every lane and every wave gets the same value).
+__device__ __forceinline__ float wave_stats_norm(const Partial* p, int n, float c, int lane) {
+  float m = -INFINITY, s = 0.f, cnt = 0.f;
+  for (int q = lane; q < n; q += 64) {
+    const Partial x = p[q];
+    merge_ms(m, s, cnt, x.m, x.s + x.cnt, 0.f, c);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float m2 = __shfl_xor(m, o, 64), s2 = __shfl_xor(s, o, 64);
+    merge_ms(m, s, cnt, m2, s2, 0.f, c);
+  }
+  return m * c + fast_log2(s);
+}
+
+template <typename ET>
+__global__ __launch_bounds__(kTT) void tts_seg_kernel(TtsArgs a) {
+  constexpr int N = Elem<ET>::N;
+  constexpr int HALF = 4;                // vectors per row and thread per half
+  constexpr int HE = kTT * HALF * N;     // elements per half (16 KiB)
+  constexpr int E = 2 * HE;              // elements per segment (32 KiB)
+  __shared__ float red[kTT / 64];
+  __shared__ int last;
+  const int tid = threadIdx.x;
+  const int n = a.nseg2;
+  const uint32_t pos = blockIdx.x / uint32_t(n);
+  const int s = int(blockIdx.x % uint32_t(n));
+  const int b = int(pos / uint32_t(a.max_k)), k = int(pos % uint32_t(a.max_k));
+  const size_t o = size_t(b) * a.max_k + k;
+  const int K = min(max(a.num_draft[b], 0), a.max_k);
+  if (k >= K) {
+    if (s == 0 && tid == 0) a.loss[o] = NAN;
+    return;
+  }
+  const ET* rd = static_cast<const ET*>(a.draft) + (a.draft_start[b] + k) * a.draft_stride;
+  const ET* rt = static_cast<const ET*>(a.target) + (a.target_start[b] + k) * a.target_stride;
+  const bool ald = is_aligned16(rd), alt = is_aligned16(rt);
+  uint4 vd[HALF], vt[HALF];
+  auto load_half = [&](int hb) {
+    if (ald && alt && hb + HE <= a.V) {
+#pragma unroll
+      for (int q = 0; q < HALF; ++q) {
+        vd[q] = load_stream16(rd + hb + (q * kTT + tid) * N);
+        vt[q] = load_stream16(rt + hb + (q * kTT + tid) * N);
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < HALF; ++q) {
+        vd[q] = load_raw<ET>(rd, hb + (q * kTT + tid) * N, a.V, ald);
+        vt[q] = load_raw<ET>(rt, hb + (q * kTT + tid) * N, a.V, alt);
+      }
+    }
+  };
+  // the first half's rows are in flight while the normalisers are merged
+  load_half(s * E);
+  const float T0 = a.temperature[b];
+  const float T = T0 > 0.f ? T0 : 1.f;
+  const float c = kLog2e / T, invT = 1.f / T;
+  const float w = a.weights[k];
+  const Partial* base = a.stats + size_t(b) * a.R * n;
+  const float kd = wave_stats_norm(base + size_t(k) * n, n, c, tid & 63);
+  const float kt = wave_stats_norm(base + size_t(a.max_k + k) * n, n, c, tid & 63);
+  ET* g = static_cast<ET*>(a.grad) + o * size_t(a.V);
+  const bool vec = is_aligned16(g);
+  float loss = 0.f;
+#pragma unroll 1
+  for (int h = 0; h < 2; ++h) {
+    const int hb = s * E + h * HE;
+    if (h) load_half(hb);
+#pragma unroll
+    for (int q = 0; q < HALF; ++q) {
+      float gv[N];
+#pragma unroll
+      for (int j = 0; j < N; ++j) {
+        const float lq = fmaf(Elem<ET>::get(vd[q], j), c, -kd);
+        const float lp = fmaf(Elem<ET>::get(vt[q], j), c, -kt);
+        const float qv = fast_exp2(lq), pv = fast_exp2(lp);
+        gv[j] = w * (qv - pv) * invT;
+        loss += pv > 0.f ? pv * (lp - lq) : 0.f;
+      }
+      store_grad<ET>(g, hb + (q * kTT + tid) * N, a.V, gv, vec);
+    }
+  }
+  loss = block_total(loss, red, tid);
+  if (tid == 0) store_dev(&a.loss_parts[o * n + s], w * kLn2 * loss);
+  uint32_t* ticket = &a.tickets[req_slot(b)];
+  if (!arrive_last(ticket, uint32_t(n) * uint32_t(K), &last)) return;
+  if (tid < K) {
+    const float* lp = a.loss_parts + (size_t(b) * a.max_k + tid) * n;
+    float total = 0.f;
+    for (int q = 0; q < n; ++q) total += load_dev(&lp[q]);
+    a.loss[size_t(b) * a.max_k + tid] = total;
+  }
+  if (tid == 0) store_dev(ticket, 0u);
+}
+
 template <typename ET, bool PREV>
 void launch_tts_kind(const TtsArgs& a, unsigned grid, hipStream_t stream) {
-  if (a.stats)
+  if (a.stats && !PREV) {
+    hipLaunchKernelGGL(tts_seg_kernel<ET>, dim3(grid * unsigned(a.nseg2)), dim3(kTT), 0, stream, a);
+  } else if (a.stats) {
     hipLaunchKernelGGL((tts_grad_kernel<ET, PREV, true>), dim3(grid), dim3(kTT), 0, stream, a);
-  else
+  } else {
     hipLaunchKernelGGL((tts_grad_kernel<ET, PREV, false>), dim3(grid), dim3(kTT), 0, stream, a);
+  }
 }
 
 }  // namespace
@@ -263,10 +375,12 @@ hipError_t launch_tts_grad(int B, int V, int max_k, int dtype, const void* draft
                            int64_t draft_stride, const void* target, const int64_t* target_start,
                            int64_t target_stride, const void* prev, const int64_t* prev_start, int64_t prev_stride,
                            const int32_t* num_draft, const float* temperature, const float* weights, float lambda,
-                           void* grad, float* loss, const Partial* stats, int R, int nseg2, hipStream_t stream) {
-  const TtsArgs a{B,           V,       max_k, draft,  draft_start, draft_stride, target,
-                  target_start, target_stride, prev, prev_start, prev_stride, num_draft, temperature,
-                  weights,     lambda,  grad,  loss,   stats,       R,            nseg2};
+                           void* grad, float* loss, const Partial* stats, float* loss_parts, uint32_t* tickets,
+                           int R, int nseg2, hipStream_t stream) {
+  const TtsArgs a{B,       V,       max_k,     draft,        draft_start, draft_stride, target,
+                  target_start, target_stride, prev,   prev_start,  prev_stride,  num_draft, temperature,
+                  weights, lambda,  grad,      loss,         stats,       loss_parts,   tickets,  R,
+                  nseg2};
   const unsigned grid = unsigned(uint64_t(B) * uint64_t(max_k));
   if (dtype == SV_BF16) {
     if (prev)

@@ -276,9 +276,12 @@ int sv_av_calib_metrics(void* stream, double* accum, double* metrics, int reset)
  *                  max_k, dtype, temperatures and row starts (no call on that
  *                  workspace in between): the softmax statistics of the draft
  *                  and target rows are then taken from it instead of a pass
- *                  over the rows.  That call must have read every canvas
- *                  draft row: each request stochastic (T > 0), or the call
- *                  made with av_feature.
+ *                  over the rows; without prev_logits the gradient is then
+ *                  computed by row segments, whose losses this call writes
+ *                  into the workspace's own region and sums in segment order.
+ *                  That call must have read every canvas draft row: each
+ *                  request stochastic (T > 0), or the call made with
+ *                  av_feature.
  * Outputs (device): grad, elements of type dtype (bf16 rounded to nearest
  * even), [B*max_k, V] row-major; loss float [B*max_k].
  * Device preconditions as for sv_spec_verify.  Returns SV_OK, or a negative
@@ -289,7 +292,7 @@ int sv_tts_grad(void* stream, int B, int V, int max_k, int dtype,
                 const void* target_logits, const int64_t* target_row_start, int64_t target_row_stride,
                 const void* prev_logits, const int64_t* prev_row_start, int64_t prev_row_stride,
                 const int32_t* num_draft, const float* temperature, const float* weights, float lambda,
-                void* grad, float* loss, const void* verify_workspace, size_t workspace_bytes);
+                void* grad, float* loss, void* verify_workspace, size_t workspace_bytes);
 
 /* Which kernel sv_spec_verify launches: a process-wide setting, default
  * SV_KERNEL_AUTO.  Both kernels compute the same outputs.

@@ -152,3 +152,35 @@ def test_statistics_reused_from_the_verification(prev):
             scale = row_scale(zd, zt, float(b.temperature[r]), float(wh[k]))
             assert np.all(np.abs(g - gref) <= REL["bf16"] * np.abs(gref) + ABS["bf16"] * scale)
             assert loss[r, k] == pytest.approx(lref, rel=1e-4, abs=1e-6)
+
+
+def test_reused_statistics_calls_repeat_bit_identically():
+    """The segmented gradient hands each position's loss to the request's
+    last workgroup through an arrival counter in the workspace arena; every
+    call leaves the counters at zero, so the next call gives the same
+    gradient and loss bit for bit (other work in between on the stream)."""
+    b = gen.make_batch("bf16_b64_k5_v32000", trial=4)
+    from gpu_harness import to_device
+    d = to_device(b)
+    print("case tts reuse repeated", flush=True)
+    ws = sv.Workspace()
+    sv.sv_spec_verify(d["draft"], d["draft_row_start"], d["target"], d["target_row_start"], d["num_draft"],
+                      d["draft_tokens"], d["temperature"], d["u_accept"], d["u_residual"], d["u_bonus"],
+                      max_k=b.max_k, want_feature=True, workspace=ws)
+    w = torch.linspace(1.0, 0.25, b.max_k, device=DEV)
+    call = lambda: sv.sv_tts_grad(d["draft"], d["draft_row_start"], d["target"], d["target_row_start"],
+                                  d["num_draft"], d["temperature"], w, b.max_k, 0.0, verify_workspace=ws)
+    first = call()
+    torch.cuda.synchronize()
+    g0, l0 = first["grad"].clone(), first["loss"].cpu().numpy()
+    params = torch.tensor(b.av_params, device=DEV)
+    sv.sv_av_score(d["draft"], d["draft_row_start"], d["num_draft"], d["temperature"], params, b.max_k,
+                   workspace=sv.Workspace())
+    second = call()
+    torch.cuda.synchronize()
+    assert torch.equal(second["grad"], g0)
+    l1 = second["loss"].cpu().numpy()
+    np.testing.assert_array_equal(np.isnan(l1), np.isnan(l0))
+    np.testing.assert_array_equal(l1[~np.isnan(l1)], l0[~np.isnan(l0)])
+    K = b.num_draft
+    assert all(np.isnan(l1[r, k]) == (k >= K[r]) for r in range(b.B) for k in range(b.max_k))
