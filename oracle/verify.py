@@ -130,6 +130,19 @@ def verify_request(zd: np.ndarray, zt: np.ndarray, d, T: float, u_accept, u_resi
 
     log_pd = [log_softmax(zd[i], T) for i in range(K)]
     log_pt = [log_softmax(zt[j], T) for j in range(K + 1)]
+    return verify_logprobs(log_pd, log_pt, d, u_accept, u_residual, u_bonus)
+
+
+def verify_logprobs(log_pd, log_pt, d, u_accept, u_residual: float, u_bonus: float) -> VerifyResult:
+    """Steps 3-5 of [CS] "One speculative step" on given distributions:
+    ``log_pd`` K rows and ``log_pt`` K+1 rows of log-probabilities (-inf for
+    probability 0), draft tokens ``d``."""
+    K = len(log_pd)
+    d = [int(x) for x in d]
+    labels = np.full(K, -1, dtype=np.int8)
+    margins = np.full(K, np.inf)
+    p_draft = np.full(K, np.nan)
+    p_target = np.full(K, np.nan)
     a = K
     for i in range(K):
         p_draft[i] = np.exp(log_pd[i][d[i]])

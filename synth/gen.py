@@ -40,6 +40,23 @@ levels, not these distributions):
     with its top token lifted to (runner-up + U(2, 10)); the target's top
     token equals the draft's with probability 0.8.
 
+Filtered-sampling workloads (per-request ``top_k`` / ``top_p`` sampling
+parameters; the acceptance-estimator page samples at temperature 1 with
+top-p 0.95).  Their draws are those of the workload with the same seed index;
+draft tokens are still drawn from the unfiltered draft distribution, so a
+draft can fall outside its row's filtered set:
+
+``bf16_b256_k4_v128256_peaked_topp95``
+    the peaked B=256, K=4, V=128256 bf16 batch, every request at top-p 0.95.
+``bf16_b64_k5_v32000_filter_mix``
+    the B=64, K=5, V=32000 bf16 batch with request b unfiltered (b % 4 = 0),
+    top-p 0.9 (1), top-k 50 (2), or top-k 200 with top-p 0.8 (3).
+``fp32_b32_k4_v1024_filter_mix``
+    the tiny recipe (fp32, V=1024) for 32 requests, ragged K_b in 1..4,
+    temperatures cycling 1, 0.7, 0 (greedy), 1.3, and the filter settings of
+    the previous workload cycling with period 5 (top-k 1, top-k 7, top-p 0.5,
+    top-p 0.97 with top-k 600, none).
+
 Logits are generated in fp32 and, for bf16 workloads, rounded to bf16 with
 round-to-nearest-even; arrays hold the raw bf16 bit patterns as uint16.
 """
@@ -103,6 +120,14 @@ class Batch:
     av_params: np.ndarray  # float32 [max_k + 1] = omega, beta_0..beta_{max_k-1}
     prune_threshold: float = 0.0
     meta: dict = field(default_factory=dict)
+    top_k: Optional[np.ndarray] = None  # int32 [B] sampling top-k per request (0: off)
+    top_p: Optional[np.ndarray] = None  # float32 [B] sampling top-p per request (1: off)
+
+    def __post_init__(self):
+        if self.top_k is None:
+            self.top_k = np.zeros(self.B, dtype=np.int32)
+        if self.top_p is None:
+            self.top_p = np.ones(self.B, dtype=np.float32)
 
     @property
     def positions(self) -> int:
@@ -197,6 +222,8 @@ class Workload:
     omega: float = 1.0
     beta: Callable = lambda i: 0.0
     prune_threshold: float = 0.0
+    top_k: Callable = lambda b: 0  # b -> top-k of request b (0: off)
+    top_p: Callable = lambda b: 1.0  # b -> top-p of request b (1: off)
 
 
 WORKLOADS = {
@@ -211,6 +238,14 @@ WORKLOADS = {
                  lambda b: 0.7, prune_threshold=0.3),
         Workload("fp32_b1024_k1to3_v129280_greedy_mix", 5, 1024, 129280, 3, "f32", _recipe_margin,
                  lambda b: 0.0 if b % 2 == 0 else 1.0, ragged=True),
+        Workload("bf16_b256_k4_v128256_peaked_topp95", 3, 256, 128256, 4, "bf16", _recipe_peaked,
+                 lambda b: 1.0, top_p=lambda b: 0.95),
+        Workload("bf16_b64_k5_v32000_filter_mix", 2, 64, 32000, 5, "bf16", _recipe_llama2, lambda b: 1.0,
+                 omega=1.2, beta=lambda i: 0.5 - 0.3 * i, top_k=lambda b: (0, 0, 50, 200)[b % 4],
+                 top_p=lambda b: (1.0, 0.9, 1.0, 0.8)[b % 4]),
+        Workload("fp32_b32_k4_v1024_filter_mix", 1, 32, 1024, 4, "f32", _recipe_tiny,
+                 lambda b: (1.0, 0.7, 0.0, 1.3)[b % 4], ragged=True, top_k=lambda b: (1, 7, 0, 600, 0)[b % 5],
+                 top_p=lambda b: (1.0, 1.0, 0.5, 0.97, 1.0)[b % 5]),
     ]
 }
 
@@ -301,8 +336,10 @@ def make_batch(name: str, trial: int = 0, B: Optional[int] = None, workers: Opti
         toks[b, :k] = tk
         temp[b], u_acc[b], u_res[b], u_bon[b] = T, ua, ur, ub
     params = np.array([wl.omega] + [wl.beta(i) for i in range(max_k)], dtype=np.float32)
+    tk = np.array([wl.top_k(b) for b in range(B)], dtype=np.int32)
+    tp = np.array([wl.top_p(b) for b in range(B)], dtype=np.float32)
     return Batch(name, B, V, max_k, wl.dtype, draft, d_start, target, t_start, ks, toks, temp,
-                 u_acc, u_res, u_bon, params, wl.prune_threshold, meta={"seed": seed})
+                 u_acc, u_res, u_bon, params, wl.prune_threshold, meta={"seed": seed}, top_k=tk, top_p=tp)
 
 
 # --------------------------------------------------------------------------
@@ -374,4 +411,4 @@ def subset(batch: Batch, idx) -> Batch:
                    target_row_start=batch.target_row_start[idx], num_draft=batch.num_draft[idx],
                    draft_tokens=batch.draft_tokens[idx], temperature=batch.temperature[idx],
                    u_accept=batch.u_accept[idx], u_residual=batch.u_residual[idx],
-                   u_bonus=batch.u_bonus[idx])
+                   u_bonus=batch.u_bonus[idx], top_k=batch.top_k[idx], top_p=batch.top_p[idx])
