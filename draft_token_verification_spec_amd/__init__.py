@@ -27,6 +27,8 @@ __all__ = [
     "sv_workspace_size",
     "sv_status_string",
     "sv_spec_verify",
+    "sv_filtered_workspace_size",
+    "sv_spec_verify_filtered",
     "sv_av_score",
     "sv_av_fit_step",
     "sv_av_budget",
@@ -63,6 +65,12 @@ _f = ctypes.c_float
 
 _SIGNATURES = {
     "sv_workspace_size": (_sz, [_i, _i, _i, _i]),
+    "sv_filtered_workspace_size": (_sz, [_i, _i, _i, _i]),
+    "sv_spec_verify_filtered": (_i, [_p, _i, _i, _i, _i,
+                                     _p, _p, _i64, _p, _p, _i64,
+                                     _p, _p, _p, _p, _p, _p, _p, _p,
+                                     _p, _p, _p, _p, _p, _p,
+                                     _p, _sz]),
     "sv_spec_verify": (_i, [_p, _i, _i, _i, _i,
                             _p, _p, _i64, _p, _p, _i64,
                             _p, _p, _p, _p, _p, _p,
@@ -378,6 +386,70 @@ def sv_spec_verify(draft_logits: torch.Tensor, draft_row_start: torch.Tensor,
         _ptr(o.get("p_draft")), _ptr(o.get("p_target")), _ptr(av_params), _ptr(o.get("av_feature")),
         _ptr(o.get("av_score")), _ptr(ws), ws.numel())
     _check(st, "sv_spec_verify")
+    return o
+
+
+def sv_filtered_workspace_size(B: int, V: int, max_k: int, dtype: int) -> int:
+    return int(_load().sv_filtered_workspace_size(B, V, max_k, dtype))
+
+
+def sv_spec_verify_filtered(draft_logits: torch.Tensor, draft_row_start: torch.Tensor,
+                            target_logits: torch.Tensor, target_row_start: torch.Tensor,
+                            num_draft: torch.Tensor, draft_tokens: torch.Tensor, temperature: torch.Tensor,
+                            top_k: torch.Tensor, top_p: torch.Tensor, u_accept: torch.Tensor,
+                            u_residual: torch.Tensor, u_bonus: torch.Tensor, max_k: int, *,
+                            want_probs: bool = True, want_labels: bool = True, want_kept: bool = True,
+                            workspace: Optional[Workspace] = None, out: Optional[dict] = None) -> dict:
+    """Verify one step on top-k / top-p filtered rows; see
+    ``sv_spec_verify_filtered``.  Arguments as for ``sv_spec_verify`` plus
+    ``top_k`` int32 [B] and ``top_p`` float32 [B]; returns accept_len,
+    out_tokens and, when requested, labels, p_draft, p_target and ``kept``
+    int32 [B, 2*max_k + 1]."""
+    dtype = _logits(target_logits, "target_logits")
+    V = target_logits.shape[1]
+    B = num_draft.numel()
+    dev = target_logits.device
+    if max_k > 0:
+        if _logits(draft_logits, "draft_logits") != dtype or draft_logits.shape[1] != V:
+            raise ValueError("draft_logits and target_logits must share dtype and V")
+    _dev(draft_row_start, "draft_row_start", torch.int64, B)
+    _dev(target_row_start, "target_row_start", torch.int64, B)
+    _dev(num_draft, "num_draft", torch.int32)
+    _dev(draft_tokens, "draft_tokens", torch.int32, B * max_k)
+    _dev(temperature, "temperature", torch.float32, B)
+    _dev(top_k, "top_k", torch.int32, B)
+    _dev(top_p, "top_p", torch.float32, B)
+    _dev(u_accept, "u_accept", torch.float32, B * max_k)
+    _dev(u_residual, "u_residual", torch.float32, B)
+    _dev(u_bonus, "u_bonus", torch.float32, B)
+    o = {} if out is None else out
+    _need(o, "accept_len", (B), torch.int32, dev)
+    _need(o, "out_tokens", (B, max_k + 1), torch.int32, dev)
+    if want_labels:
+        _need(o, "labels", (B, max_k), torch.int8, dev)
+    if want_probs:
+        _need(o, "p_draft", (B, max_k), torch.float32, dev)
+        _need(o, "p_target", (B, max_k), torch.float32, dev)
+    if want_kept:
+        _need(o, "kept", (B, 2 * max_k + 1), torch.int32, dev)
+    for key, dt, n in (("accept_len", torch.int32, B), ("out_tokens", torch.int32, B * (max_k + 1)),
+                       ("labels", torch.int8, B * max_k), ("p_draft", torch.float32, B * max_k),
+                       ("p_target", torch.float32, B * max_k), ("kept", torch.int32, B * (2 * max_k + 1))):
+        if key in o:
+            _dev(o[key], key, dt, n)
+    nbytes = sv_filtered_workspace_size(B, V, max_k, dtype)
+    if nbytes == 0 and B > 0:
+        _check(-2, "sv_spec_verify_filtered")
+    ws = (workspace or _default_ws).get(dev, nbytes)
+    st = _load().sv_spec_verify_filtered(
+        _stream(dev), B, V, max_k, dtype,
+        _ptr(draft_logits) if max_k > 0 else None, _ptr(draft_row_start),
+        draft_logits.stride(0) if max_k > 0 else V,
+        _ptr(target_logits), _ptr(target_row_start), target_logits.stride(0),
+        _ptr(num_draft), _ptr(draft_tokens), _ptr(temperature), _ptr(top_k), _ptr(top_p), _ptr(u_accept),
+        _ptr(u_residual), _ptr(u_bonus), _ptr(o["accept_len"]), _ptr(o["out_tokens"]), _ptr(o.get("labels")),
+        _ptr(o.get("p_draft")), _ptr(o.get("p_target")), _ptr(o.get("kept")), _ptr(ws), ws.numel())
+    _check(st, "sv_spec_verify_filtered")
     return o
 
 

@@ -49,6 +49,52 @@ const hipEvent_t* next_events() {
   return g_timing.ev + 3 * k;
 }
 
+// Kernel arguments of a verification call (the estimator outputs unset).
+VerifyArgs verify_args(const WsLayout& L, void* workspace, int B, int V, int max_k, const void* draft_logits,
+                       const int64_t* draft_row_start, int64_t draft_row_stride, const void* target_logits,
+                       const int64_t* target_row_start, int64_t target_row_stride, const int32_t* num_draft,
+                       const int32_t* draft_tokens, const float* temperature, const float* u_accept,
+                       const float* u_residual, const float* u_bonus, int32_t* accept_len, int32_t* out_tokens,
+                       int8_t* labels, float* p_draft_at_token, float* p_target_at_token) {
+  char* ws = static_cast<char*>(workspace);
+  VerifyArgs a;
+  a.B = B;
+  a.V = V;
+  a.max_k = max_k;
+  a.nseg = L.nseg;
+  a.nseg2 = L.nseg2;
+  a.R = L.R;
+  a.draft = draft_logits;
+  a.draft_start = draft_row_start;
+  a.draft_stride = draft_row_stride;
+  a.target = target_logits;
+  a.target_start = target_row_start;
+  a.target_stride = target_row_stride;
+  a.num_draft = num_draft;
+  a.tokens = draft_tokens;
+  a.temperature = temperature;
+  a.u_accept = u_accept;
+  a.u_residual = u_residual;
+  a.u_bonus = u_bonus;
+  a.accept_len = accept_len;
+  a.out_tokens = out_tokens;
+  a.labels = labels;
+  a.p_draft = p_draft_at_token;
+  a.p_target = p_target_at_token;
+  a.av_params = nullptr;
+  a.av_feature = nullptr;
+  a.av_score = nullptr;
+  a.ctrl = reinterpret_cast<uint32_t*>(ws + L.ctrl);
+  a.reqw = reinterpret_cast<uint32_t*>(ws + L.reqw);
+  a.partials = reinterpret_cast<Partial*>(ws + L.partials);
+  a.zval = reinterpret_cast<float*>(ws + L.zval);
+  a.segsum = reinterpret_cast<float*>(ws + L.segsum);
+  a.tagged = reinterpret_cast<uint64_t*>(ws + L.tagged);
+  a.parts = a.stride = 0;
+  a.spin_limit = 0;
+  return a;
+}
+
 }  // namespace
 
 extern "C" {
@@ -76,43 +122,13 @@ int sv_spec_verify(void* stream, int B, int V, int max_k, int dtype, const void*
   if (av_score && (!av_feature || !av_params)) return SV_ERR_INVALID_ARG;
   const WsLayout L = ws_layout(B, V, max_k, dtype);
   if (!workspace || workspace_bytes < L.total) return SV_ERR_WORKSPACE;
-
-  char* ws = static_cast<char*>(workspace);
-  VerifyArgs a;
-  a.B = B;
-  a.V = V;
-  a.max_k = max_k;
-  a.nseg = L.nseg;
-  a.nseg2 = L.nseg2;
-  a.R = L.R;
-  a.draft = draft_logits;
-  a.draft_start = draft_row_start;
-  a.draft_stride = draft_row_stride;
-  a.target = target_logits;
-  a.target_start = target_row_start;
-  a.target_stride = target_row_stride;
-  a.num_draft = num_draft;
-  a.tokens = draft_tokens;
-  a.temperature = temperature;
-  a.u_accept = u_accept;
-  a.u_residual = u_residual;
-  a.u_bonus = u_bonus;
-  a.accept_len = accept_len;
-  a.out_tokens = out_tokens;
-  a.labels = labels;
-  a.p_draft = p_draft_at_token;
-  a.p_target = p_target_at_token;
+  VerifyArgs a = verify_args(L, workspace, B, V, max_k, draft_logits, draft_row_start, draft_row_stride,
+                             target_logits, target_row_start, target_row_stride, num_draft, draft_tokens,
+                             temperature, u_accept, u_residual, u_bonus, accept_len, out_tokens, labels,
+                             p_draft_at_token, p_target_at_token);
   a.av_params = av_params;
   a.av_feature = av_feature;
   a.av_score = av_score;
-  a.ctrl = reinterpret_cast<uint32_t*>(ws + L.ctrl);
-  a.reqw = reinterpret_cast<uint32_t*>(ws + L.reqw);
-  a.partials = reinterpret_cast<Partial*>(ws + L.partials);
-  a.zval = reinterpret_cast<float*>(ws + L.zval);
-  a.segsum = reinterpret_cast<float*>(ws + L.segsum);
-  a.tagged = reinterpret_cast<uint64_t*>(ws + L.tagged);
-  a.parts = a.stride = 0;
-  a.spin_limit = 0;
   const int kind = __atomic_load_n(&g_verify_kernel, __ATOMIC_RELAXED);
   const hipStream_t hs = static_cast<hipStream_t>(stream);
   hipError_t err = hipSuccess;
@@ -122,6 +138,40 @@ int sv_spec_verify(void* stream, int B, int V, int max_k, int dtype, const void*
     return SV_ERR_UNSUPPORTED;
   }
   return to_status(err);
+}
+
+size_t sv_filtered_workspace_size(int B, int V, int max_k, int dtype) {
+  if (check_sizes(B, V, max_k, dtype) != SV_OK) return 0;
+  return filter_layout(B, V, max_k, dtype).total;
+}
+
+int sv_spec_verify_filtered(void* stream, int B, int V, int max_k, int dtype, const void* draft_logits,
+                            const int64_t* draft_row_start, int64_t draft_row_stride, const void* target_logits,
+                            const int64_t* target_row_start, int64_t target_row_stride, const int32_t* num_draft,
+                            const int32_t* draft_tokens, const float* temperature, const int32_t* top_k,
+                            const float* top_p, const float* u_accept, const float* u_residual,
+                            const float* u_bonus, int32_t* accept_len, int32_t* out_tokens, int8_t* labels,
+                            float* p_draft_at_token, float* p_target_at_token, int32_t* kept, void* workspace,
+                            size_t workspace_bytes) {
+  const int st = check_sizes(B, V, max_k, dtype);
+  if (st != SV_OK) return st;
+  if (B == 0) return SV_OK;
+  if (!target_logits || !target_row_start || !num_draft || !temperature || !top_k || !top_p || !u_residual ||
+      !u_bonus || !accept_len || !out_tokens)
+    return SV_ERR_INVALID_ARG;
+  if (max_k > 0 && (!draft_logits || !draft_row_start || !draft_tokens || !u_accept)) return SV_ERR_INVALID_ARG;
+  if (target_row_stride < V || (max_k > 0 && draft_row_stride < V)) return SV_ERR_INVALID_ARG;
+  const WsLayout L = ws_layout(B, V, max_k, dtype);
+  const FilterLayout F = filter_layout(B, V, max_k, dtype);
+  if (!workspace || workspace_bytes < F.total) return SV_ERR_WORKSPACE;
+  VerifyArgs a = verify_args(L, workspace, B, V, max_k, draft_logits, draft_row_start, draft_row_stride,
+                             target_logits, target_row_start, target_row_stride, num_draft, draft_tokens,
+                             temperature, u_accept, u_residual, u_bonus, accept_len, out_tokens, labels,
+                             p_draft_at_token, p_target_at_token);
+  char* ws = static_cast<char*>(workspace);
+  const FilterIO io{top_k, top_p, kept, reinterpret_cast<uint64_t*>(ws + F.hmass),
+                    reinterpret_cast<uint32_t*>(ws + F.hcount), ws + F.search};
+  return to_status(launch_filtered(a, io, dtype, static_cast<hipStream_t>(stream)));
 }
 
 int sv_av_score(void* stream, int B, int V, int max_k, int dtype, const void* draft_logits,

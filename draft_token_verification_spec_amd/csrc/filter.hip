@@ -1,0 +1,727 @@
+// Verification on top-k / top-p filtered distributions.
+//
+// [AV] "Adaptive Verification ohne Confidence Head", sections "Other
+// features considered" and "Benchmarks": drafts are sampled and verified at
+// temperature 1 with top-p 0.95, so the distributions speculative sampling
+// ([CS] "One speculative step") compares are the filtered ones.  Readings:
+// top-p keeps a token when the tokens with a strictly larger logit hold less
+// than top_p of the row's probability; top-k keeps it when fewer than k
+// tokens have a strictly larger logit; with both, a token must pass both.
+// Each row of a stochastic request is filtered and renormalised; greedy
+// requests are not filtered (the argmax is always kept).
+//
+// A row's kept set is {v : key(z_v) >= t} for a threshold key t (key = the
+// order-preserving integer image of the logit), found by an exact radix
+// select with deterministic histograms:
+//   level 0  bins of 1/8 unit of log2 probability below the row maximum
+//            (255 bins, the last one collecting everything further down);
+//   level L  8-bit digits of the key within the interval the previous level
+//            left, until one key remains (bf16 keys: 2 levels, fp32: 4).
+// Each level is a streaming pass (one workgroup per 32 KiB row segment:
+// integer counts and masses in 2^-40 fixed point of exp2((z - max) * c), added
+// with LDS integer atomics, so the sums do not depend on the order) and a
+// selection (one workgroup per row: segment histograms merged in order,
+// exclusive scans, the boundary bin).  The verdict and the residual / bonus
+// draw then run one workgroup per request on the filtered rows.
+#include "sv_device.hpp"
+
+namespace sv {
+
+namespace {
+
+constexpr int kFT = 256;  // threads of the histogram and selection kernels
+constexpr int kFV = 8;    // 16-byte vectors per thread and segment (32 KiB)
+constexpr int kBins = 256;
+constexpr int kBinsPerLog2 = 8;
+constexpr float kFix = 1099511627776.f;  // 2^40
+constexpr int kVT = 512;                 // threads of the verdict / draw kernel
+constexpr int kVW = kVT / 64;
+constexpr int kChunk = kVT * 8;          // elements of the draw per chunk (8 per thread)
+constexpr int kGroup = 4;                // chunks in flight per thread
+constexpr int kMaxChunks = (SV_MAX_V + kChunk - 1) / kChunk;
+static_assert(kFT * kFV * 16 == kHalfBytes, "a histogram segment is a 32 KiB sampling segment");
+
+// Order-preserving key of a logit: bf16 rows use the 16 bits of the value,
+// fp32 rows all 32; -0 is keyed as +0.
+template <typename ET>
+struct Key;
+
+template <>
+struct Key<uint16_t> {
+  static constexpr uint32_t kMin = 0x007fu;  // -inf
+  static constexpr uint32_t kMax = 0xff80u;  // +inf
+  __device__ __forceinline__ static uint32_t of(float z) {
+    uint32_t u = __float_as_uint(z) >> 16;
+    if (u == 0x8000u) u = 0u;
+    return (u & 0x8000u) ? (~u & 0xffffu) : (u | 0x8000u);
+  }
+  __device__ __forceinline__ static float value(uint32_t k) {
+    const uint32_t u = (k & 0x8000u) ? (k & 0x7fffu) : (~k & 0xffffu);
+    return __uint_as_float(u << 16);
+  }
+};
+
+template <>
+struct Key<float> {
+  static constexpr uint32_t kMin = 0x007fffffu;
+  static constexpr uint32_t kMax = 0xff800000u;
+  __device__ __forceinline__ static uint32_t of(float z) {
+    uint32_t u = __float_as_uint(z);
+    if (u == 0x80000000u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  }
+  __device__ __forceinline__ static float value(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+  }
+};
+
+// Level-0 bin: floor of 8 x (log2 of the probability ratio to the row
+// maximum), clamped to [0, 255].  Non-increasing in z.
+__device__ __forceinline__ int bin0(float z, float c, float mc) {
+  const float e = fmaf(z, c, -mc);
+  return e >= 0.f ? 0 : (e > -32.f ? int(-e * float(kBinsPerLog2)) : kBins - 1);
+}
+
+__device__ __forceinline__ uint64_t fixed_mass(float z, float c, float mc) {
+  return uint64_t(__builtin_rintf(fast_exp2(fmaf(z, c, -mc)) * kFix));
+}
+
+// State of one threshold search of one row (slot 0: top-k, slot 1: top-p).
+struct FSearch {
+  uint32_t lo, hi;   // key interval holding the threshold
+  uint32_t cabove;   // tokens with a key above the interval
+  uint32_t state;    // 0 unused, 1 searching, 2 done
+  uint64_t mabove;   // fixed-point mass above the interval
+  uint64_t mfinal;   // done: mass of the kept tokens
+  double target;     // top-k: k; top-p: top_p x total mass
+  uint32_t key;      // done: the threshold key
+  uint32_t kept;     // done: kept tokens
+};
+static_assert(sizeof(FSearch) == kFilterSearchBytes, "search state layout");
+static_assert(kBins == kFilterBins, "histogram bins");
+
+struct FiltArgs {
+  int B, V, max_k, R, nseg2;
+  const void* draft;
+  const int64_t* draft_start;
+  int64_t draft_stride;
+  const void* target;
+  const int64_t* target_start;
+  int64_t target_stride;
+  const int32_t* num_draft;
+  const int32_t* tokens;
+  const float* temperature;
+  const int32_t* top_k;
+  const float* top_p;
+  const float* u_accept;
+  const float* u_residual;
+  const float* u_bonus;
+  int32_t* accept_len;
+  int32_t* out_tokens;
+  int8_t* labels;
+  float* p_draft;
+  float* p_target;
+  int32_t* kept;
+  const Partial* partials;  // [B][R][nseg2] of the statistics kernel
+  const float* zval;        // [B][R] logits at the draft tokens
+  uint64_t* hmass;          // [B][R][nseg2][2][kBins]
+  uint32_t* hcount;         // [B][R][nseg2][2][kBins]
+  FSearch* search;          // [B][R][2]
+};
+
+struct ReqFilter {
+  int K;
+  float T;
+  bool on_k, on_p;
+  int top_k;
+  float top_p;
+};
+
+__device__ __forceinline__ ReqFilter req_filter(const FiltArgs& a, int b) {
+  ReqFilter f;
+  f.K = min(max(a.num_draft[b], 0), a.max_k);
+  f.T = a.temperature[b];
+  f.top_k = a.top_k[b];
+  f.top_p = a.top_p[b];
+  const bool stoch = f.T > 0.f;
+  f.on_k = stoch && f.top_k > 0 && f.top_k < a.V;
+  f.on_p = stoch && f.top_p < 1.f;
+  return f;
+}
+
+// Is row slot rs (draft i at i, target j at max_k + j) of the request read
+// and filtered?
+__device__ __forceinline__ bool row_filtered(const FiltArgs& a, const ReqFilter& f, int rs) {
+  if (!(f.on_k || f.on_p)) return false;
+  return rs < a.max_k ? rs < f.K : rs - a.max_k <= f.K;
+}
+
+template <typename ET>
+__device__ __forceinline__ const ET* row_ptr(const FiltArgs& a, int b, int rs) {
+  if (rs < a.max_k) return static_cast<const ET*>(a.draft) + (a.draft_start[b] + rs) * a.draft_stride;
+  return static_cast<const ET*>(a.target) + (a.target_start[b] + (rs - a.max_k)) * a.target_stride;
+}
+
+// Maximum logit of a row from its segment statistics (exact: a maximum).
+__device__ __forceinline__ float wave_row_max(const Partial* p, int n, int lane) {
+  float m = -INFINITY;
+  for (int q = lane; q < n; q += 64) m = fmaxf(m, p[q].m);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  return m;
+}
+
+struct HistShared {
+  uint64_t mass[2][kBins];
+  uint32_t count[2][kBins];
+};
+
+// One level of the histograms: workgroup = segment s of row slot rs of
+// request b.  Level 0 bins every element; later levels bin the elements
+// whose key lies in a searching slot's interval by their digit there.
+template <typename ET, bool L0>
+__global__ __launch_bounds__(kFT) void filt_hist_kernel(FiltArgs a) {
+  __shared__ HistShared sh;
+  constexpr int N = Elem<ET>::N;
+  const int tid = threadIdx.x;
+  const int n = a.nseg2, R = a.R;
+  const uint32_t item = blockIdx.x;
+  const int s = int(item % uint32_t(n));
+  const int rs = int((item / uint32_t(n)) % uint32_t(R));
+  const int b = int(item / (uint32_t(n) * uint32_t(R)));
+  const ReqFilter f = req_filter(a, b);
+  if (!row_filtered(a, f, rs)) return;
+  const size_t row = size_t(b) * R + rs;
+  uint32_t lo[2] = {0u, 0u}, hi[2] = {0u, 0u};
+  int shift[2] = {0, 0};
+  bool on[2] = {true, false};
+  if (!L0) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const FSearch& st = a.search[row * 2 + q];
+      on[q] = st.state == 1u;
+      lo[q] = st.lo;
+      hi[q] = st.hi;
+      const uint32_t w = hi[q] - lo[q];
+      shift[q] = w == 0u ? 0 : max(0, 32 - __clz(w) - 8);
+    }
+    if (!on[0] && !on[1]) return;
+  }
+  const ET* rp = row_ptr<ET>(a, b, rs);
+  const bool al = is_aligned16(rp);
+  const int hb = s * kFT * kFV * N;
+  uint4 v[kFV];
+  if (al && hb + kFT * kFV * N <= a.V) {
+#pragma unroll
+    for (int k = 0; k < kFV; ++k) v[k] = load_stream16(rp + hb + (k * kFT + tid) * N);
+  } else {
+#pragma unroll
+    for (int k = 0; k < kFV; ++k) v[k] = load_raw<ET>(rp, hb + (k * kFT + tid) * N, a.V, al);
+  }
+  const float c = kLog2e / f.T;
+  const float mc = wave_row_max(a.partials + row * n, n, tid & 63) * c;
+  for (int j = tid; j < 2 * kBins; j += kFT) {
+    (&sh.mass[0][0])[j] = 0u;
+    (&sh.count[0][0])[j] = 0u;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < kFV; ++k) {
+    const int e0 = hb + (k * kFT + tid) * N;
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      if (e0 + j >= a.V) continue;
+      const float z = Elem<ET>::get(v[k], j);
+      if (L0) {
+        const int bn = bin0(z, c, mc);
+        atomicAdd(reinterpret_cast<unsigned long long*>(&sh.mass[0][bn]),
+                  static_cast<unsigned long long>(fixed_mass(z, c, mc)));
+        atomicAdd(&sh.count[0][bn], 1u);
+      } else {
+        const uint32_t key = Key<ET>::of(z);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          if (on[q] && key >= lo[q] && key <= hi[q]) {
+            const int dg = int((key - lo[q]) >> shift[q]);
+            atomicAdd(reinterpret_cast<unsigned long long*>(&sh.mass[q][dg]),
+                      static_cast<unsigned long long>(fixed_mass(z, c, mc)));
+            atomicAdd(&sh.count[q][dg], 1u);
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+  const size_t base = (row * n + s) * 2;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    if (!on[q]) continue;
+    a.hmass[(base + q) * kBins + tid] = sh.mass[q][tid];
+    a.hcount[(base + q) * kBins + tid] = sh.count[q][tid];
+  }
+}
+
+// Exclusive prefix over the workgroup in thread order (integers: exact).
+template <typename T>
+__device__ __forceinline__ T block_excl_scan(T x, T* part, int tid, T* total) {
+  const int lane = tid & 63, w = tid >> 6;
+  T incl = x;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const T y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) part[w] = incl;
+  __syncthreads();
+  T before = 0, all = 0;
+  for (int q = 0; q < kFT / 64; ++q) {
+    before += q < w ? part[q] : T(0);
+    all += part[q];
+  }
+  __syncthreads();
+  *total = all;
+  return before + incl - x;
+}
+
+__device__ __forceinline__ int block_max_int(int x, int* part, int tid) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = max(x, __shfl_xor(x, o, 64));
+  if ((tid & 63) == 0) part[tid >> 6] = x;
+  __syncthreads();
+  int m = part[0];
+  for (int q = 1; q < kFT / 64; ++q) m = max(m, part[q]);
+  __syncthreads();
+  return m;
+}
+
+// Keys mapping to level-0 bin j (a contiguous interval: bin0 is monotone in z).
+template <typename ET>
+__device__ void bin_keys(int j, float c, float mc, uint32_t* klo, uint32_t* khi) {
+  // klo: the smallest key with bin <= j (true at kMax); khi: the largest
+  // key with bin >= j (true at kMin)
+  uint64_t lo = Key<ET>::kMin, hi = Key<ET>::kMax;
+  while (lo < hi) {
+    const uint64_t mid = (lo + hi) >> 1;
+    if (bin0(Key<ET>::value(uint32_t(mid)), c, mc) <= j) hi = mid;
+    else lo = mid + 1;
+  }
+  *klo = uint32_t(lo);
+  lo = Key<ET>::kMin;
+  hi = Key<ET>::kMax;
+  while (lo < hi) {
+    const uint64_t mid = (lo + hi + 1) >> 1;
+    if (bin0(Key<ET>::value(uint32_t(mid)), c, mc) >= j) lo = mid;
+    else hi = mid - 1;
+  }
+  *khi = uint32_t(lo);
+}
+
+struct SelShared {
+  uint64_t p64[kFT / 64];
+  uint32_t p32[kFT / 64];
+  int pi[kFT / 64];
+  uint32_t bl[2], bh[2];
+};
+
+// Selection after level 0 (L0) or a key level: one workgroup per row slot;
+// thread j owns bin / digit j.
+template <typename ET, bool L0>
+__global__ __launch_bounds__(kFT) void filt_select_kernel(FiltArgs a) {
+  __shared__ SelShared sh;
+  const int tid = threadIdx.x;
+  const int n = a.nseg2, R = a.R;
+  const int rs = int(blockIdx.x % uint32_t(R));
+  const int b = int(blockIdx.x / uint32_t(R));
+  const ReqFilter f = req_filter(a, b);
+  if (!row_filtered(a, f, rs)) return;
+  const size_t row = size_t(b) * R + rs;
+  FSearch* st = a.search + row * 2;
+  if (L0) {
+    uint64_t m = 0;
+    uint32_t cnt = 0;
+    for (int s = 0; s < n; ++s) {
+      const size_t h = ((row * n + s) * 2) * kBins + tid;
+      m += a.hmass[h];
+      cnt += a.hcount[h];
+    }
+    uint64_t mtot;
+    uint32_t ctot;
+    const uint64_t fm = block_excl_scan<uint64_t>(m, sh.p64, tid, &mtot);
+    const uint32_t fc = block_excl_scan<uint32_t>(cnt, sh.p32, tid, &ctot);
+    const double tk = double(f.top_k);
+    const double tp = double(f.top_p) * double(mtot);
+    // boundary bin of each search: the last non-empty bin whose mass (count)
+    // above is below the target; the top non-empty bin when none is
+    const int jk = block_max_int(f.on_k && cnt > 0u && double(fc) < tk ? tid : -1, sh.pi, tid);
+    const int jp = block_max_int(f.on_p && cnt > 0u && double(fm) < tp ? tid : -1, sh.pi, tid);
+    const int top = -block_max_int(cnt > 0u ? -tid : -kBins, sh.pi, tid);
+    const int jq[2] = {jk >= 0 ? jk : top, jp >= 0 ? jp : top};
+    const float c = kLog2e / f.T;
+    const float mc = wave_row_max(a.partials + row * n, n, tid & 63) * c;
+    // the key interval of each boundary bin, one wave per search
+    if ((tid & 63) == 0 && (tid >> 6) < 2) {
+      const int q = tid >> 6;
+      uint32_t lo = 0, hi = 0;
+      if (q == 0 ? f.on_k : f.on_p) bin_keys<ET>(jq[q], c, mc, &lo, &hi);
+      sh.bl[q] = lo;
+      sh.bh[q] = hi;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const bool on = q == 0 ? f.on_k : f.on_p;
+      if (tid != jq[q]) continue;
+      FSearch w{};
+      if (on) {
+        w.lo = sh.bl[q];
+        w.hi = sh.bh[q];
+        w.cabove = fc;
+        w.mabove = fm;
+        w.target = q == 0 ? tk : tp;
+        w.state = 1u;
+        if (w.lo == w.hi) {
+          w.state = 2u;
+          w.key = w.lo;
+          w.kept = fc + cnt;
+          w.mfinal = fm + m;
+        }
+      }
+      st[q] = w;
+    }
+    return;
+  }
+#pragma unroll 1
+  for (int q = 0; q < 2; ++q) {
+    const FSearch cur = st[q];
+    if (cur.state != 1u) continue;
+    // thread j owns digit d = kBins - 1 - j, so that an exclusive scan in
+    // thread order sums the digits of larger keys
+    const int d = kBins - 1 - tid;
+    uint64_t md = 0;
+    uint32_t cd = 0;
+    for (int s = 0; s < n; ++s) {
+      const size_t h = ((row * n + s) * 2 + q) * kBins + d;
+      md += a.hmass[h];
+      cd += a.hcount[h];
+    }
+    uint64_t mtot;
+    uint32_t ctot;
+    const uint64_t fm = cur.mabove + block_excl_scan<uint64_t>(md, sh.p64, tid, &mtot);
+    const uint32_t fc = cur.cabove + block_excl_scan<uint32_t>(cd, sh.p32, tid, &ctot);
+    const bool ok = cd > 0u && (q == 0 ? double(fc) < cur.target : double(fm) < cur.target);
+    // the smallest qualifying digit (the largest non-empty one if none is)
+    const int dq = -block_max_int(ok ? -d : -kBins, sh.pi, tid);
+    const int dtop = block_max_int(cd > 0u ? d : -1, sh.pi, tid);
+    const int ds = dq < kBins ? dq : dtop;
+    if (d != ds) continue;
+    const uint32_t w = cur.hi - cur.lo;
+    const int shf = w == 0u ? 0 : max(0, 32 - __clz(w) - 8);
+    FSearch nx = cur;
+    const uint64_t lo = uint64_t(cur.lo) + (uint64_t(d) << shf);
+    const uint64_t hi = min(uint64_t(cur.hi), lo + (uint64_t(1) << shf) - 1);
+    nx.lo = uint32_t(lo);
+    nx.hi = uint32_t(hi);
+    nx.mabove = fm;
+    nx.cabove = fc;
+    if (lo == hi) {
+      nx.state = 2u;
+      nx.key = uint32_t(lo);
+      nx.kept = fc + cd;
+      nx.mfinal = fm + md;
+    }
+    st[q] = nx;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// verdict and draw
+// ---------------------------------------------------------------------------
+
+struct RowInfo {
+  float kk;    // log2 normaliser: p'(v) = exp2(z c - kk) for kept v
+  uint32_t t;  // threshold key (0: every token kept)
+  int idx;     // lowest-index argmax (greedy target rows)
+};
+
+struct VerShared {
+  RowInfo row[2 * SV_MAX_K + 1];
+  float chunk[kMaxChunks];
+  float wsum[kGroup][kVW];
+  float wtot[kVW];
+  int pi[kVW];
+  int a, resid, pick;
+  float u;
+};
+
+// Weights of the 8 elements first.. of a draw row pair (residual (pt' - pd')+
+// or pt'); 0 past the end.
+template <typename ET>
+__device__ __forceinline__ void elem8(const ET* rt, const ET* rd, int first, int V, bool al, const RowInfo& it,
+                                      const RowInfo& id, float c, bool resid, float (&w)[8]) {
+  constexpr int N = Elem<ET>::N;
+  uint4 t[8 / N], d[8 / N];
+#pragma unroll
+  for (int q = 0; q < 8 / N; ++q) {
+    t[q] = load_raw<ET>(rt, first + q * N, V, al);
+    if (resid) d[q] = load_raw<ET>(rd, first + q * N, V, al);
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float zt = Elem<ET>::get(t[j / N], j % N);
+    float x = (first + j < V && Key<ET>::of(zt) >= it.t) ? fast_exp2(fmaf(zt, c, -it.kk)) : 0.f;
+    if (resid) {
+      const float zd = Elem<ET>::get(d[j / N], j % N);
+      const float y = (first + j < V && Key<ET>::of(zd) >= id.t) ? fast_exp2(fmaf(zd, c, -id.kk)) : 0.f;
+      x = fmaxf(x - y, 0.f);
+    }
+    w[j] = x;
+  }
+}
+
+__device__ __forceinline__ int vt_max_int(int x, int* part, int tid) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = max(x, __shfl_xor(x, o, 64));
+  if ((tid & 63) == 0) part[tid >> 6] = x;
+  __syncthreads();
+  int m = part[0];
+  for (int q = 1; q < kVW; ++q) m = max(m, part[q]);
+  __syncthreads();
+  return m;
+}
+
+template <typename ET>
+__global__ __launch_bounds__(kVT) void filt_verify_kernel(FiltArgs a) {
+  __shared__ VerShared sh;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int b = blockIdx.x;
+  const int max_k = a.max_k, R = a.R, n = a.nseg2;
+  const ReqFilter f = req_filter(a, b);
+  const int K = f.K;
+  const bool greedy = !(f.T > 0.f);
+  const float c = kLog2e / (greedy ? 1.f : f.T);
+  // row statistics, thread rs for row slot rs
+  if (tid < R) {
+    const int rs = tid;
+    const bool valid = rs < max_k ? (rs < K && !greedy) : (rs - max_k <= K);
+    RowInfo info{0.f, 0u, 0};
+    int kept = -1;
+    if (valid) {
+      const Partial* p = a.partials + (size_t(b) * R + rs) * n;
+      if (greedy) {
+        float m = -INFINITY;
+        int idx = 0x7fffffff;
+        for (int s = 0; s < n; ++s) merge_argmax(m, idx, p[s].m, p[s].idx);
+        info.idx = idx;
+      } else {
+        float m = -INFINITY, sum = 0.f, cnt = 0.f;
+        for (int s = 0; s < n; ++s) merge_ms(m, sum, cnt, p[s].m, p[s].s + p[s].cnt, 0.f, c);
+        const float mc = m * c;
+        info.kk = mc + fast_log2(sum);
+        if (row_filtered(a, f, rs)) {
+          const FSearch* st = a.search + (size_t(b) * R + rs) * 2;
+          const FSearch& sk = st[0];
+          const FSearch& sp = st[1];
+          const FSearch& use = !f.on_k ? sp : !f.on_p ? sk : (sk.key >= sp.key ? sk : sp);
+          info.t = use.key;
+          info.kk = mc + (fast_log2(float(use.mfinal)) - 40.f);
+          kept = int(use.kept);
+        }
+      }
+    }
+    sh.row[rs] = info;
+    if (a.kept) a.kept[size_t(b) * R + rs] = kept;
+  }
+  __syncthreads();
+  // accept walk
+  if (tid == 0) {
+    int acc = K;
+    float u = 0.f;
+    int resid = 0;
+    for (int i = 0; i < max_k; ++i) {
+      const size_t o = size_t(b) * max_k + i;
+      float pd = NAN, pt = NAN;
+      int8_t lab = -1;
+      if (i < K) {
+        const int d = a.tokens[o];
+        bool ok;
+        if (greedy) {
+          ok = d == sh.row[max_k + i].idx;
+          pt = ok ? 1.f : 0.f;
+        } else {
+          const float zd = a.zval[size_t(b) * R + i], zt = a.zval[size_t(b) * R + max_k + i];
+          const RowInfo& id = sh.row[i];
+          const RowInfo& it = sh.row[max_k + i];
+          const float ld = Key<ET>::of(zd) >= id.t ? fmaf(zd, c, -id.kk) : -INFINITY;
+          const float lt = Key<ET>::of(zt) >= it.t ? fmaf(zt, c, -it.kk) : -INFINITY;
+          pd = fast_exp2(ld);
+          pt = fast_exp2(lt);
+          const float ratio = ld == -INFINITY ? INFINITY : fast_exp2(lt - ld);
+          ok = a.u_accept[o] < fminf(1.f, ratio);
+        }
+        if (i < acc) {
+          if (!ok) acc = i;
+          lab = ok ? 1 : 0;
+        }
+      }
+      if (a.p_draft) a.p_draft[o] = pd;
+      if (a.p_target) a.p_target[o] = pt;
+      if (a.labels) a.labels[o] = lab;
+    }
+    a.accept_len[b] = acc;
+    for (int i = 0; i <= max_k; ++i)
+      a.out_tokens[size_t(b) * (max_k + 1) + i] = i < acc ? a.tokens[size_t(b) * max_k + i] : -1;
+    if (greedy) {
+      a.out_tokens[size_t(b) * (max_k + 1) + acc] = sh.row[max_k + acc].idx;
+    } else {
+      resid = acc < K ? 1 : 0;
+      u = resid ? a.u_residual[b] : a.u_bonus[b];
+    }
+    sh.a = acc;
+    sh.resid = resid;
+    sh.u = u;
+  }
+  __syncthreads();
+  if (greedy) return;
+  const int acc = sh.a;
+  bool resid = sh.resid != 0;
+  const float u = sh.u;
+  const ET* rt = row_ptr<ET>(a, b, max_k + acc);
+  const ET* rd = resid ? row_ptr<ET>(a, b, acc) : rt;
+  const bool al = is_aligned16(rt) && is_aligned16(rd);
+  const RowInfo it = sh.row[max_k + acc];
+  const RowInfo id = resid ? sh.row[acc] : it;
+  const int nch = (a.V + kChunk - 1) / kChunk;
+  float Z = 0.f;
+  for (int pass = 0; pass < 2; ++pass) {
+    // chunk sums, kGroup chunks in flight
+    for (int g0 = 0; g0 < nch; g0 += kGroup) {
+      float w[kGroup][8];
+#pragma unroll
+      for (int q = 0; q < kGroup; ++q) elem8<ET>(rt, rd, (g0 + q) * kChunk + tid * 8, a.V, al, it, id, c, resid, w[q]);
+#pragma unroll
+      for (int q = 0; q < kGroup; ++q) {
+        float x = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x += w[q][j];
+        x = wave_sum(x);
+        if (lane == 0) sh.wsum[q][wv] = x;
+      }
+      __syncthreads();
+      if (tid < kGroup && g0 + tid < nch) {
+        float x = 0.f;
+        for (int q = 0; q < kVW; ++q) x += sh.wsum[tid][q];
+        sh.chunk[g0 + tid] = x;
+      }
+      __syncthreads();
+    }
+    if (tid == 0) {
+      float z = 0.f;
+      for (int q = 0; q < nch; ++q) z += sh.chunk[q];
+      sh.u = z;
+    }
+    __syncthreads();
+    Z = sh.u;
+    __syncthreads();
+    if (Z > 0.f || !resid) break;
+    resid = false;  // the residual has no mass: draw from the target row
+  }
+  const RowInfo& id2 = resid ? id : it;
+  // the chunk where the running sum first exceeds u Z; if rounding leaves
+  // none, the last chunk with weight and its last positive-weight token
+  if (tid == 0) {
+    const float t = u * Z;
+    float cum = 0.f;
+    int ch = -1;
+    for (int q = 0; q < nch; ++q) {
+      if (cum + sh.chunk[q] > t) {
+        ch = q;
+        break;
+      }
+      cum += sh.chunk[q];
+    }
+    int last = ch < 0 ? 1 : 0;
+    if (ch < 0) {
+      ch = 0;
+      for (int q = nch - 1; q >= 0; --q)
+        if (sh.chunk[q] > 0.f) {
+          ch = q;
+          break;
+        }
+    }
+    sh.pick = ch;
+    sh.resid = last;
+    sh.u = t - cum;  // the threshold left inside the chunk
+  }
+  __syncthreads();
+  const int ch = sh.pick;
+  const bool want_last = sh.resid != 0;
+  const float rem = sh.u;
+  __syncthreads();
+  float w[8];
+  elem8<ET>(rt, rd, ch * kChunk + tid * 8, a.V, al, it, id2, c, resid, w);
+  float own = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) own += w[j];
+  float incl = own;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) sh.wtot[wv] = incl;
+  __syncthreads();
+  float run = incl - own;
+  for (int q = 0; q < wv; ++q) run += sh.wtot[q];
+  int first = 0x7fffffff, lastpos = -1;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    run += w[j];
+    const int v = ch * kChunk + tid * 8 + j;
+    if (w[j] > 0.f) {
+      lastpos = v;
+      if (first == 0x7fffffff && run > rem) first = v;
+    }
+  }
+  const int fmin = -vt_max_int(-first, sh.pi, tid);
+  const int lmax = vt_max_int(lastpos, sh.pi, tid);
+  if (tid == 0) {
+    const int tok = (!want_last && fmin != 0x7fffffff) ? fmin : lmax;
+    a.out_tokens[size_t(b) * (max_k + 1) + acc] = tok;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_filtered(VerifyArgs va, const FilterIO& io, int dtype, hipStream_t stream) {
+  const uint64_t n1 = uint64_t(va.B) * uint64_t(va.R) * uint64_t(va.nseg2);
+  if (n1 >= (uint64_t(1) << 31)) return hipErrorInvalidValue;
+  hipError_t e = launch_stats(va, dtype, stream);
+  if (e != hipSuccess) return e;
+  FiltArgs a{va.B, va.V, va.max_k, va.R, va.nseg2, va.draft, va.draft_start, va.draft_stride, va.target,
+             va.target_start, va.target_stride, va.num_draft, va.tokens, va.temperature, io.top_k, io.top_p,
+             va.u_accept, va.u_residual, va.u_bonus, va.accept_len, va.out_tokens, va.labels, va.p_draft,
+             va.p_target, io.kept, va.partials, va.zval, io.hmass, io.hcount,
+             reinterpret_cast<FSearch*>(io.search)};
+  const unsigned g1 = unsigned(n1), g2 = unsigned(va.B) * unsigned(va.R);
+  const int levels = dtype == SV_BF16 ? 2 : 4;  // key digits after level 0
+  if (dtype == SV_BF16) {
+    hipLaunchKernelGGL((filt_hist_kernel<uint16_t, true>), dim3(g1), dim3(kFT), 0, stream, a);
+    hipLaunchKernelGGL((filt_select_kernel<uint16_t, true>), dim3(g2), dim3(kFT), 0, stream, a);
+    for (int l = 0; l < levels; ++l) {
+      hipLaunchKernelGGL((filt_hist_kernel<uint16_t, false>), dim3(g1), dim3(kFT), 0, stream, a);
+      hipLaunchKernelGGL((filt_select_kernel<uint16_t, false>), dim3(g2), dim3(kFT), 0, stream, a);
+    }
+    hipLaunchKernelGGL(filt_verify_kernel<uint16_t>, dim3(unsigned(va.B)), dim3(kVT), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((filt_hist_kernel<float, true>), dim3(g1), dim3(kFT), 0, stream, a);
+    hipLaunchKernelGGL((filt_select_kernel<float, true>), dim3(g2), dim3(kFT), 0, stream, a);
+    for (int l = 0; l < levels; ++l) {
+      hipLaunchKernelGGL((filt_hist_kernel<float, false>), dim3(g1), dim3(kFT), 0, stream, a);
+      hipLaunchKernelGGL((filt_select_kernel<float, false>), dim3(g2), dim3(kFT), 0, stream, a);
+    }
+    hipLaunchKernelGGL(filt_verify_kernel<float>, dim3(unsigned(va.B)), dim3(kVT), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace sv

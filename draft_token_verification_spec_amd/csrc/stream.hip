@@ -716,6 +716,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
 
 }  // namespace
 
+hipError_t launch_stats(VerifyArgs a, int dtype, hipStream_t stream) {
+  const uint64_t n1 = uint64_t(a.B) * uint64_t(a.R) * uint64_t(a.nseg2);
+  if (n1 == 0) return hipSuccess;
+  if (n1 >= (uint64_t(1) << 31)) return hipErrorInvalidValue;
+  if (dtype == SV_BF16)
+    hipLaunchKernelGGL(stats_kernel<uint16_t>, dim3(unsigned(n1)), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(stats_kernel<float>, dim3(unsigned(n1)), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_streaming(VerifyArgs a, int dtype, hipStream_t stream, const hipEvent_t* ev) {
   const uint64_t n1 = uint64_t(a.B) * uint64_t(a.R) * uint64_t(a.nseg2);
   const uint64_t n2 = uint64_t(a.B) * uint64_t(a.nseg2 + 1);  // weight workgroups, then one search per request

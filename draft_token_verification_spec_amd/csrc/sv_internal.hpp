@@ -96,6 +96,15 @@ static_assert(SV_MAX_B % kLineWords == 0, "arena slots");
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Filtered verification: after the verification layout, per (row slot,
+// 32 KiB segment, search) histograms of kFilterBins bins (fixed-point masses
+// and counts) and per (row slot, search) threshold-search states.
+constexpr int kFilterBins = 256;
+constexpr size_t kFilterSearchBytes = 48;
+struct FilterLayout {
+  size_t hmass, hcount, search, total;
+};
+
 // Hand-off slot of the draw kernel: 8 bytes written in one store, the low
 // word kSlotReady, the high word the value's bits.  The reader polls until
 // the low word is kSlotReady and clears the slot once it has the value.  The
@@ -120,6 +129,18 @@ struct WsLayout {
   int nseg2;  // 32 KiB half segments per row (partials are strided by this)
   int R;
 };
+
+inline WsLayout ws_layout(int B, int V, int max_k, int dtype);
+inline FilterLayout filter_layout(int B, int V, int max_k, int dtype) {
+  const WsLayout L = ws_layout(B, V, max_k, dtype);
+  const size_t slots = size_t(B) * L.R * L.nseg2 * 2 * kFilterBins;
+  FilterLayout F;
+  F.hmass = L.total;
+  F.hcount = F.hmass + align256(slots * 8);
+  F.search = F.hcount + align256(slots * 4);
+  F.total = F.search + align256(size_t(B) * L.R * 2 * kFilterSearchBytes);
+  return F;
+}
 
 inline WsLayout ws_layout(int B, int V, int max_k, int dtype) {
   WsLayout L;
@@ -197,6 +218,21 @@ bool launch_verify(VerifyArgs a, int dtype, hipStream_t stream, hipError_t* err,
 // The two streaming kernels (statistics, then the verdict and the draw).
 // `ev` (nullable): three events to record before, between and after them.
 hipError_t launch_streaming(VerifyArgs a, int dtype, hipStream_t stream, const hipEvent_t* ev = nullptr);
+// The statistics kernel alone (segment statistics and logits at the draft
+// tokens into the workspace).
+hipError_t launch_stats(VerifyArgs a, int dtype, hipStream_t stream);
+
+// Filtered verification: the statistics kernel, the threshold searches and
+// the verdict / draw kernel.
+struct FilterIO {
+  const int32_t* top_k;
+  const float* top_p;
+  int32_t* kept;
+  uint64_t* hmass;
+  uint32_t* hcount;
+  void* search;
+};
+hipError_t launch_filtered(VerifyArgs a, const FilterIO& io, int dtype, hipStream_t stream);
 hipError_t launch_av_score(const ScoreArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_av_budget(int B, int max_k, const float* score, const int32_t* num_draft, const float* draft_cost,
                             const float* verify_cost, int32_t* num_kept, int32_t* budget, hipStream_t stream);

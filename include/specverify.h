@@ -147,6 +147,61 @@ int sv_spec_verify(void* stream, int B, int V, int max_k, int dtype,
                    const float* av_params, float* av_feature, float* av_score,
                    void* workspace, size_t workspace_bytes);
 
+/* Bytes of workspace needed by sv_spec_verify_filtered (the verification
+ * workspace followed by the threshold-search histograms: about
+ * B * (2*max_k + 1) * nseg * 6 KiB, nseg = ceil(V * elem_bytes / 32 KiB)).
+ * Returns 0 for arguments that call would reject.  Same zero-fill-once
+ * contract as sv_workspace_size. */
+size_t sv_filtered_workspace_size(int B, int V, int max_k, int dtype);
+
+/* Batched speculative verification on top-k / top-p filtered distributions.
+ *
+ * [AV] "Adaptive Verification ohne Confidence Head", sections "Other
+ * features considered" and "Benchmarks", sample drafts and verify them at
+ * temperature 1 with top-p 0.95; the verification of [CS] "One speculative
+ * step" then compares the filtered draft and target distributions.  The
+ * pages define neither filter; the readings implemented:
+ *   top-p   token v of a row is kept when the tokens whose logit is strictly
+ *           larger than z_v hold less than top_p of softmax(row / T)
+ *           (equal logits are kept or dropped together);
+ *   top-k   v is kept when fewer than top_k tokens have a strictly larger
+ *           logit (the k largest values, ties included);
+ *   both    v must be kept by both, each evaluated on the full row;
+ * and every draft row and target row of a stochastic request is replaced by
+ * its filtered, renormalised distribution p'(v) = p(v) [v kept] / (sum of p
+ * over the kept tokens) before steps 2-4 of sv_spec_verify, which are
+ * otherwise unchanged (a draft token outside its draft row's kept set has
+ * p' = 0 and is accepted, the ratio being +inf).  Greedy requests (T = 0)
+ * are verified as in sv_spec_verify: the argmax is always kept.
+ *
+ * Arguments as for sv_spec_verify (no estimator outputs), plus:
+ *   top_k   int32 [B]   top_k[b] <= 0 or >= V: no top-k filter.
+ *   top_p   float [B]   top_p[b] >= 1 (or NaN): no top-p filter; otherwise
+ *           0 < top_p[b] < 1 (device precondition).
+ *   kept    int32 [B*(2*max_k+1)]  nullable: per row slot (draft rows
+ *           0..max_k-1, then target rows 0..max_k) the number of tokens kept
+ *           by the filters, -1 for rows not filtered or not read.
+ *   p_draft_at_token, p_target_at_token: the filtered probabilities p'.
+ *   workspace: at least sv_filtered_workspace_size(B, V, max_k, dtype)
+ *           bytes, zero-filled once.
+ * The kept sets are exact: a row's masses are summed in 2^-40 fixed point of
+ * the probability relative to the row maximum (the top-p comparison is made
+ * on those sums in binary64), the threshold found by a radix select over the
+ * logits' order-preserving keys.  Outputs are a deterministic function of
+ * the inputs.  Returns SV_OK, or a negative sv_status without launching. */
+int sv_spec_verify_filtered(void* stream, int B, int V, int max_k, int dtype,
+                            const void* draft_logits, const int64_t* draft_row_start,
+                            int64_t draft_row_stride,
+                            const void* target_logits, const int64_t* target_row_start,
+                            int64_t target_row_stride,
+                            const int32_t* num_draft, const int32_t* draft_tokens,
+                            const float* temperature, const int32_t* top_k,
+                            const float* top_p, const float* u_accept,
+                            const float* u_residual, const float* u_bonus,
+                            int32_t* accept_len, int32_t* out_tokens, int8_t* labels,
+                            float* p_draft_at_token, float* p_target_at_token,
+                            int32_t* kept, void* workspace, size_t workspace_bytes);
+
 /* Acceptance-estimator scoring of the draft rows, before verification.
  *
  * [AV] "Solution" / "Scoring the distribution": per draft row i of request b

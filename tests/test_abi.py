@@ -25,7 +25,8 @@ def test_every_declared_symbol_is_exported():
     names = declared_functions()
     assert set(names) == {"sv_workspace_size", "sv_spec_verify", "sv_av_score", "sv_av_fit_step",
                           "sv_status_string", "sv_set_verify_kernel", "sv_timing_enable", "sv_timing_read",
-                          "sv_av_budget", "sv_av_calib_accumulate", "sv_av_calib_metrics", "sv_tts_grad"}
+                          "sv_av_budget", "sv_av_calib_accumulate", "sv_av_calib_metrics", "sv_tts_grad",
+                          "sv_filtered_workspace_size", "sv_spec_verify_filtered"}
     lib = ctypes.CDLL(sv.lib_path())
     for n in names:
         assert hasattr(lib, n), n
@@ -130,6 +131,45 @@ def test_spec_verify_rejects_before_launch(kw, status):
 def test_spec_verify_empty_batch_is_a_noop():
     assert verify_call(B=0, ws=None, ws_bytes=0, target=None) in (-1, 0)
     assert verify_call(B=0) == 0
+
+
+def filtered_call(**kw):
+    args = dict(stream=None, B=4, V=1024, max_k=4, dtype=0, draft=FAKE, dstart=FAKE, dstride=1024, target=FAKE,
+                tstart=FAKE, tstride=1024, num_draft=FAKE, tokens=FAKE, temp=FAKE, top_k=FAKE, top_p=FAKE,
+                u_acc=FAKE, u_res=FAKE, u_bon=FAKE, accept_len=FAKE, out_tokens=FAKE, labels=None, p_d=None,
+                p_t=None, kept=None, ws=FAKE, ws_bytes=1 << 30)
+    args.update(kw)
+    return sv._load().sv_spec_verify_filtered(*args.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), -1),
+    (dict(max_k=17), -2),
+    (dict(dtype=5), -1),
+    (dict(top_k=None), -1),
+    (dict(top_p=None), -1),
+    (dict(target=None), -1),
+    (dict(draft=None), -1),
+    (dict(u_acc=None), -1),
+    (dict(tstride=1023), -1),
+    (dict(ws=None), -3),
+    (dict(ws_bytes=100), -3),
+])
+def test_spec_verify_filtered_rejects_before_launch(kw, status):
+    assert filtered_call(**kw) == status
+
+
+def test_filtered_workspace_size():
+    plain = sv.sv_workspace_size(256, 128256, 4, sv.SV_BF16)
+    filt = sv.sv_filtered_workspace_size(256, 128256, 4, sv.SV_BF16)
+    # the verification workspace, then 2 x 256 x 12 B of histograms per row
+    # segment and 48 B of search state per row and search
+    nseg = -(-128256 * 2 // 32768)
+    assert filt >= plain + 256 * 9 * nseg * 2 * 256 * 12 + 256 * 9 * 2 * 48
+    assert filt % 256 == 0
+    assert sv.sv_filtered_workspace_size(4, 1024, sv.SV_MAX_K + 1, 0) == 0
+    # one workspace one byte short is refused
+    assert filtered_call(ws_bytes=sv.sv_filtered_workspace_size(4, 1024, 4, 0) - 1) == -3
 
 
 def test_av_score_rejects_before_launch():
