@@ -394,6 +394,38 @@ def main():
         tts_ms = e0.elapsed_time(e1) / treps
         res["extra"]["tts_grad"][mode] = {"ms_per_call": tts_ms, "achieved_gbs": alg / (tts_ms * 1e-3) / 1e9,
                                           "frac": alg / (tts_ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    # verification on top-p 0.95 filtered rows (the sampling setting of the
+    # estimator page's measurements) over input set 0: statistics pass, the
+    # threshold searches' histogram passes, then the verdict and draw
+    log("timing the filtered verification")
+    tk = torch.zeros(B, dtype=torch.int32, device=dev)
+    tp = torch.full((B,), 0.95, dtype=torch.float32, device=dev)
+    fws = sv.Workspace()
+    fcall = lambda: sv.sv_spec_verify_filtered(d0["draft"], d0["draft_row_start"], d0["target"],
+                                               d0["target_row_start"], d0["num_draft"], d0["draft_tokens"],
+                                               d0["temperature"], tk, tp, d0["u_accept"], d0["u_residual"],
+                                               d0["u_bonus"], max_k=K, workspace=fws, out=fo)
+    fo = None
+    fo = fcall()
+    for _ in range(5):
+        fcall()
+    torch.cuda.synchronize(dev)
+    freps = 20
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(freps):
+        fcall()
+    e1.record()
+    torch.cuda.synchronize(dev)
+    f_ms = e0.elapsed_time(e1) / freps
+    fbytes = b0.algorithmic_bytes()
+    res["extra"]["filtered_verify"] = {
+        "top_p": 0.95, "ms_per_call": f_ms, "positions_per_s": positions / (f_ms * 1e-3),
+        "algorithmic_bytes": fbytes, "achieved_gbs": fbytes / (f_ms * 1e-3) / 1e9,
+        "frac": fbytes / (f_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "kept_tokens_mean": float(fo["kept"][fo["kept"] >= 0].float().mean()),
+        "mean_accept_len": float(fo["accept_len"].float().mean()),
+        "note": "back-to-back calls between two events; every logit read once counts as the algorithmic bytes"}
     if args.copy_calibration > 0:
         log("copy calibration")
         n = args.copy_calibration << 20

@@ -169,8 +169,15 @@ int sv_spec_verify_filtered(void* stream, int B, int V, int max_k, int dtype, co
                              temperature, u_accept, u_residual, u_bonus, accept_len, out_tokens, labels,
                              p_draft_at_token, p_target_at_token);
   char* ws = static_cast<char*>(workspace);
-  const FilterIO io{top_k, top_p, kept, reinterpret_cast<uint64_t*>(ws + F.hmass),
-                    reinterpret_cast<uint32_t*>(ws + F.hcount), ws + F.search};
+  const FilterIO io{top_k,
+                    top_p,
+                    kept,
+                    reinterpret_cast<uint64_t*>(ws + F.hmass),
+                    reinterpret_cast<uint32_t*>(ws + F.hcount),
+                    ws + F.search,
+                    ws + F.info,
+                    ws + F.desc,
+                    reinterpret_cast<float*>(ws + F.slices)};
   return to_status(launch_filtered(a, io, dtype, static_cast<hipStream_t>(stream)));
 }
 

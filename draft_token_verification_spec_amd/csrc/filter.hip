@@ -21,8 +21,8 @@
 // integer counts and masses in 2^-40 fixed point of exp2((z - max) * c), added
 // with LDS integer atomics, so the sums do not depend on the order) and a
 // selection (one workgroup per row: segment histograms merged in order,
-// exclusive scans, the boundary bin).  The verdict and the residual / bonus
-// draw then run one workgroup per request on the filtered rows.
+// exclusive scans, the boundary bin).  The verdict, the residual / bonus
+// weights and the draw then run on the filtered rows.
 #include "sv_device.hpp"
 
 namespace sv {
@@ -34,11 +34,6 @@ constexpr int kFV = 8;    // 16-byte vectors per thread and segment (32 KiB)
 constexpr int kBins = 256;
 constexpr int kBinsPerLog2 = 8;
 constexpr float kFix = 1099511627776.f;  // 2^40
-constexpr int kVT = 512;                 // threads of the verdict / draw kernel
-constexpr int kVW = kVT / 64;
-constexpr int kChunk = kVT * 8;          // elements of the draw per chunk (8 per thread)
-constexpr int kGroup = 4;                // chunks in flight per thread
-constexpr int kMaxChunks = (SV_MAX_V + kChunk - 1) / kChunk;
 static_assert(kFT * kFV * 16 == kHalfBytes, "a histogram segment is a 32 KiB sampling segment");
 
 // Order-preserving key of a logit: bf16 rows use the 16 bits of the value,
@@ -171,10 +166,34 @@ __device__ __forceinline__ float wave_row_max(const Partial* p, int n, int lane)
   return m;
 }
 
+// Vector of a row holding elements first..first+N-1; positions >= limit
+// hold a NaN (never a logit: rows have no NaN).
+template <typename ET>
+__device__ __forceinline__ uint4 load_nan_tail(const ET* row, int first, int limit, bool aligned) {
+  constexpr int N = Elem<ET>::N;
+  if (aligned && first + N <= limit) return *reinterpret_cast<const uint4*>(row + first);
+  constexpr uint32_t nan = N == 8 ? 0x7fc0u : 0x7fc00000u;
+  uint4 w;
+#pragma unroll
+  for (int j = 0; j < N; ++j) Elem<ET>::put(w, j, (first + j < limit) ? Elem<ET>::raw(row + first + j) : nan);
+  return w;
+}
+
 struct HistShared {
   uint64_t mass[2][kBins];
   uint32_t count[2][kBins];
 };
+
+// An element of a search interval into that search's digit histogram; out
+// of line, so that the streaming loop around it stays small (few elements of
+// a row fall in the interval).
+template <typename ET>
+__device__ __noinline__ void key_add(HistShared& sh, int q, float z, uint32_t lo, int shift, float c, float mc) {
+  const int dg = int((Key<ET>::of(z) - lo) >> shift);
+  atomicAdd(reinterpret_cast<unsigned long long*>(&sh.mass[q][dg]),
+            static_cast<unsigned long long>(fixed_mass(z, c, mc)));
+  atomicAdd(&sh.count[q][dg], 1u);
+}
 
 // One level of the histograms: workgroup = segment s of row slot rs of
 // request b.  Level 0 bins every element; later levels bin the elements
@@ -189,34 +208,44 @@ __global__ __launch_bounds__(kFT) void filt_hist_kernel(FiltArgs a) {
   const int s = int(item % uint32_t(n));
   const int rs = int((item / uint32_t(n)) % uint32_t(R));
   const int b = int(item / (uint32_t(n) * uint32_t(R)));
-  const ReqFilter f = req_filter(a, b);
-  if (!row_filtered(a, f, rs)) return;
   const size_t row = size_t(b) * R + rs;
-  uint32_t lo[2] = {0u, 0u}, hi[2] = {0u, 0u};
-  int shift[2] = {0, 0};
-  bool on[2] = {true, false};
+  // every scalar the workgroup needs in one round trip, before any decision:
+  // under a saturated memory system each dependent round trip is long
+  const ReqFilter f = req_filter(a, b);
+  const bool is_draft = rs < a.max_k;
+  const int64_t start = is_draft ? a.draft_start[b] : a.target_start[b];
+  uint32_t st_state[2] = {1u, 0u}, lo[2] = {0u, 0u}, hi[2] = {0u, 0u};
   if (!L0) {
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const FSearch& st = a.search[row * 2 + q];
-      on[q] = st.state == 1u;
+      st_state[q] = st.state;
       lo[q] = st.lo;
       hi[q] = st.hi;
-      const uint32_t w = hi[q] - lo[q];
-      shift[q] = w == 0u ? 0 : max(0, 32 - __clz(w) - 8);
     }
-    if (!on[0] && !on[1]) return;
   }
-  const ET* rp = row_ptr<ET>(a, b, rs);
+  if (!row_filtered(a, f, rs)) return;
+  bool on[2];
+  int shift[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    on[q] = st_state[q] == 1u;
+    const uint32_t w = hi[q] - lo[q];
+    shift[q] = w == 0u ? 0 : max(0, 32 - __clz(w) - 8);
+  }
+  if (!on[0] && !on[1]) return;
+  const ET* rp = is_draft ? static_cast<const ET*>(a.draft) + (start + rs) * a.draft_stride
+                          : static_cast<const ET*>(a.target) + (start + (rs - a.max_k)) * a.target_stride;
   const bool al = is_aligned16(rp);
   const int hb = s * kFT * kFV * N;
+  const bool full = hb + kFT * kFV * N <= a.V;
   uint4 v[kFV];
-  if (al && hb + kFT * kFV * N <= a.V) {
+  if (al && full) {
 #pragma unroll
     for (int k = 0; k < kFV; ++k) v[k] = load_stream16(rp + hb + (k * kFT + tid) * N);
   } else {
 #pragma unroll
-    for (int k = 0; k < kFV; ++k) v[k] = load_raw<ET>(rp, hb + (k * kFT + tid) * N, a.V, al);
+    for (int k = 0; k < kFV; ++k) v[k] = load_nan_tail<ET>(rp, hb + (k * kFT + tid) * N, a.V, al);
   }
   const float c = kLog2e / f.T;
   const float mc = wave_row_max(a.partials + row * n, n, tid & 63) * c;
@@ -224,32 +253,43 @@ __global__ __launch_bounds__(kFT) void filt_hist_kernel(FiltArgs a) {
     (&sh.mass[0][0])[j] = 0u;
     (&sh.count[0][0])[j] = 0u;
   }
+  // key levels: a slot's key interval as a value interval (the key order is
+  // the value order, -0 and +0 one value), so most elements are dismissed
+  // with two compares
+  float zlo[2], zhi[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    zlo[q] = on[q] ? Key<ET>::value(lo[q]) : INFINITY;
+    zhi[q] = on[q] ? Key<ET>::value(hi[q]) : -INFINITY;
+  }
   __syncthreads();
+  auto bin_elem = [&](float z) {
+    if (L0) {
+      const int bn = bin0(z, c, mc);
+      atomicAdd(reinterpret_cast<unsigned long long*>(&sh.mass[0][bn]),
+                static_cast<unsigned long long>(fixed_mass(z, c, mc)));
+      atomicAdd(&sh.count[0][bn], 1u);
+    } else {
 #pragma unroll
-  for (int k = 0; k < kFV; ++k) {
-    const int e0 = hb + (k * kFT + tid) * N;
-#pragma unroll
-    for (int j = 0; j < N; ++j) {
-      if (e0 + j >= a.V) continue;
-      const float z = Elem<ET>::get(v[k], j);
-      if (L0) {
-        const int bn = bin0(z, c, mc);
-        atomicAdd(reinterpret_cast<unsigned long long*>(&sh.mass[0][bn]),
-                  static_cast<unsigned long long>(fixed_mass(z, c, mc)));
-        atomicAdd(&sh.count[0][bn], 1u);
-      } else {
-        const uint32_t key = Key<ET>::of(z);
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          if (on[q] && key >= lo[q] && key <= hi[q]) {
-            const int dg = int((key - lo[q]) >> shift[q]);
-            atomicAdd(reinterpret_cast<unsigned long long*>(&sh.mass[q][dg]),
-                      static_cast<unsigned long long>(fixed_mass(z, c, mc)));
-            atomicAdd(&sh.count[q][dg], 1u);
-          }
-        }
-      }
+      for (int q = 0; q < 2; ++q)
+        if (z >= zlo[q] && z <= zhi[q]) key_add<ET>(sh, q, z, lo[q], shift[q], c, mc);
     }
+  };
+  // past the end of the row the tail loads hold NaN, which no key interval
+  // holds; level 0 skips it explicitly
+  if (full || !L0) {
+#pragma unroll
+    for (int k = 0; k < kFV; ++k)
+#pragma unroll
+      for (int j = 0; j < N; ++j) bin_elem(Elem<ET>::get(v[k], j));
+  } else {
+#pragma unroll
+    for (int k = 0; k < kFV; ++k)
+#pragma unroll
+      for (int j = 0; j < N; ++j) {
+        const float z = Elem<ET>::get(v[k], j);
+        if (z == z) bin_elem(z);
+      }
   }
   __syncthreads();
   const size_t base = (row * n + s) * 2;
@@ -339,6 +379,7 @@ __global__ __launch_bounds__(kFT) void filt_select_kernel(FiltArgs a) {
   if (L0) {
     uint64_t m = 0;
     uint32_t cnt = 0;
+#pragma unroll 8
     for (int s = 0; s < n; ++s) {
       const size_t h = ((row * n + s) * 2) * kBins + tid;
       m += a.hmass[h];
@@ -399,6 +440,7 @@ __global__ __launch_bounds__(kFT) void filt_select_kernel(FiltArgs a) {
     const int d = kBins - 1 - tid;
     uint64_t md = 0;
     uint32_t cd = 0;
+#pragma unroll 8
     for (int s = 0; s < n; ++s) {
       const size_t h = ((row * n + s) * 2 + q) * kBins + d;
       md += a.hmass[h];
@@ -436,258 +478,317 @@ __global__ __launch_bounds__(kFT) void filt_select_kernel(FiltArgs a) {
 // ---------------------------------------------------------------------------
 // verdict and draw
 // ---------------------------------------------------------------------------
+//
+// Three kernels, as the unfiltered path: the verdict (one wave per request:
+// row normalisers and thresholds, accept walk, outputs), the draw weights
+// (one workgroup per 32 KiB segment of the draw rows: the weights of its 8
+// slices of 4 KiB, for the residual and for the target row alone, the
+// fallback when the residual has no mass), and the search (one workgroup per
+// request: the slice sums scanned in token order, then the crossing slice).
 
 struct RowInfo {
   float kk;    // log2 normaliser: p'(v) = exp2(z c - kk) for kept v
   uint32_t t;  // threshold key (0: every token kept)
   int idx;     // lowest-index argmax (greedy target rows)
+  int pad;
 };
 
-struct VerShared {
-  RowInfo row[2 * SV_MAX_K + 1];
-  float chunk[kMaxChunks];
-  float wsum[kGroup][kVW];
-  float wtot[kVW];
-  int pi[kVW];
-  int a, resid, pick;
+static_assert(sizeof(RowInfo) == kFilterRowBytes, "row info layout");
+
+struct DrawDesc {
+  int acc;    // accept length
+  int mode;   // 0: greedy (token emitted), 1: residual at acc, 2: bonus from target row acc
   float u;
+  int pad;
 };
 
-// Weights of the 8 elements first.. of a draw row pair (residual (pt' - pd')+
-// or pt'); 0 past the end.
-template <typename ET>
-__device__ __forceinline__ void elem8(const ET* rt, const ET* rd, int first, int V, bool al, const RowInfo& it,
-                                      const RowInfo& id, float c, bool resid, float (&w)[8]) {
-  constexpr int N = Elem<ET>::N;
-  uint4 t[8 / N], d[8 / N];
-#pragma unroll
-  for (int q = 0; q < 8 / N; ++q) {
-    t[q] = load_raw<ET>(rt, first + q * N, V, al);
-    if (resid) d[q] = load_raw<ET>(rd, first + q * N, V, al);
-  }
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const float zt = Elem<ET>::get(t[j / N], j % N);
-    float x = (first + j < V && Key<ET>::of(zt) >= it.t) ? fast_exp2(fmaf(zt, c, -it.kk)) : 0.f;
-    if (resid) {
-      const float zd = Elem<ET>::get(d[j / N], j % N);
-      const float y = (first + j < V && Key<ET>::of(zd) >= id.t) ? fast_exp2(fmaf(zd, c, -id.kk)) : 0.f;
-      x = fmaxf(x - y, 0.f);
-    }
-    w[j] = x;
-  }
-}
+static_assert(sizeof(DrawDesc) == kFilterDescBytes, "draw descriptor layout");
+static_assert(kFV == kDrawSlices, "slices per draw segment");
+constexpr int kMaxSlices = int(int64_t(SV_MAX_V) * 4 / (kFT * 16));  // 4 KiB slices of the longest row
 
-__device__ __forceinline__ int vt_max_int(int x, int* part, int tid) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x = max(x, __shfl_xor(x, o, 64));
-  if ((tid & 63) == 0) part[tid >> 6] = x;
-  __syncthreads();
-  int m = part[0];
-  for (int q = 1; q < kVW; ++q) m = max(m, part[q]);
-  __syncthreads();
-  return m;
-}
-
-template <typename ET>
-__global__ __launch_bounds__(kVT) void filt_verify_kernel(FiltArgs a) {
-  __shared__ VerShared sh;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+__global__ __launch_bounds__(64) void filt_verdict_kernel_impl(FiltArgs a, RowInfo* info, DrawDesc* desc,
+                                                                bool bf16) {
+  __shared__ RowInfo row[2 * SV_MAX_K + 1];
+  const int tid = threadIdx.x;
   const int b = blockIdx.x;
   const int max_k = a.max_k, R = a.R, n = a.nseg2;
   const ReqFilter f = req_filter(a, b);
   const int K = f.K;
   const bool greedy = !(f.T > 0.f);
   const float c = kLog2e / (greedy ? 1.f : f.T);
-  // row statistics, thread rs for row slot rs
   if (tid < R) {
     const int rs = tid;
     const bool valid = rs < max_k ? (rs < K && !greedy) : (rs - max_k <= K);
-    RowInfo info{0.f, 0u, 0};
+    RowInfo r{0.f, 0u, 0, 0};
     int kept = -1;
     if (valid) {
       const Partial* p = a.partials + (size_t(b) * R + rs) * n;
       if (greedy) {
         float m = -INFINITY;
         int idx = 0x7fffffff;
+#pragma unroll 8
         for (int s = 0; s < n; ++s) merge_argmax(m, idx, p[s].m, p[s].idx);
-        info.idx = idx;
+        r.idx = idx;
       } else {
         float m = -INFINITY, sum = 0.f, cnt = 0.f;
+#pragma unroll 8
         for (int s = 0; s < n; ++s) merge_ms(m, sum, cnt, p[s].m, p[s].s + p[s].cnt, 0.f, c);
         const float mc = m * c;
-        info.kk = mc + fast_log2(sum);
+        r.kk = mc + fast_log2(sum);
         if (row_filtered(a, f, rs)) {
           const FSearch* st = a.search + (size_t(b) * R + rs) * 2;
           const FSearch& sk = st[0];
           const FSearch& sp = st[1];
           const FSearch& use = !f.on_k ? sp : !f.on_p ? sk : (sk.key >= sp.key ? sk : sp);
-          info.t = use.key;
-          info.kk = mc + (fast_log2(float(use.mfinal)) - 40.f);
+          r.t = use.key;
+          r.kk = mc + (fast_log2(float(use.mfinal)) - 40.f);
           kept = int(use.kept);
         }
       }
     }
-    sh.row[rs] = info;
+    row[rs] = r;
+    info[size_t(b) * R + rs] = r;
     if (a.kept) a.kept[size_t(b) * R + rs] = kept;
   }
   __syncthreads();
-  // accept walk
-  if (tid == 0) {
-    int acc = K;
-    float u = 0.f;
-    int resid = 0;
-    for (int i = 0; i < max_k; ++i) {
-      const size_t o = size_t(b) * max_k + i;
-      float pd = NAN, pt = NAN;
-      int8_t lab = -1;
-      if (i < K) {
-        const int d = a.tokens[o];
-        bool ok;
-        if (greedy) {
-          ok = d == sh.row[max_k + i].idx;
-          pt = ok ? 1.f : 0.f;
-        } else {
-          const float zd = a.zval[size_t(b) * R + i], zt = a.zval[size_t(b) * R + max_k + i];
-          const RowInfo& id = sh.row[i];
-          const RowInfo& it = sh.row[max_k + i];
-          const float ld = Key<ET>::of(zd) >= id.t ? fmaf(zd, c, -id.kk) : -INFINITY;
-          const float lt = Key<ET>::of(zt) >= it.t ? fmaf(zt, c, -it.kk) : -INFINITY;
-          pd = fast_exp2(ld);
-          pt = fast_exp2(lt);
-          const float ratio = ld == -INFINITY ? INFINITY : fast_exp2(lt - ld);
-          ok = a.u_accept[o] < fminf(1.f, ratio);
-        }
-        if (i < acc) {
-          if (!ok) acc = i;
-          lab = ok ? 1 : 0;
-        }
+  if (tid != 0) return;
+  int acc = K;
+  for (int i = 0; i < max_k; ++i) {
+    const size_t o = size_t(b) * max_k + i;
+    float pd = NAN, pt = NAN;
+    int8_t lab = -1;
+    if (i < K) {
+      const int d = a.tokens[o];
+      bool ok;
+      if (greedy) {
+        ok = d == row[max_k + i].idx;
+        pt = ok ? 1.f : 0.f;
+      } else {
+        const float zd = a.zval[size_t(b) * R + i], zt = a.zval[size_t(b) * R + max_k + i];
+        const RowInfo& id = row[i];
+        const RowInfo& it = row[max_k + i];
+        const uint32_t kd = bf16 ? Key<uint16_t>::of(zd) : Key<float>::of(zd);
+        const uint32_t kt = bf16 ? Key<uint16_t>::of(zt) : Key<float>::of(zt);
+        const float ld = kd >= id.t ? fmaf(zd, c, -id.kk) : -INFINITY;
+        const float lt = kt >= it.t ? fmaf(zt, c, -it.kk) : -INFINITY;
+        pd = fast_exp2(ld);
+        pt = fast_exp2(lt);
+        const float ratio = ld == -INFINITY ? INFINITY : fast_exp2(lt - ld);
+        ok = a.u_accept[o] < fminf(1.f, ratio);
       }
-      if (a.p_draft) a.p_draft[o] = pd;
-      if (a.p_target) a.p_target[o] = pt;
-      if (a.labels) a.labels[o] = lab;
+      if (i < acc) {
+        if (!ok) acc = i;
+        lab = ok ? 1 : 0;
+      }
     }
-    a.accept_len[b] = acc;
-    for (int i = 0; i <= max_k; ++i)
-      a.out_tokens[size_t(b) * (max_k + 1) + i] = i < acc ? a.tokens[size_t(b) * max_k + i] : -1;
-    if (greedy) {
-      a.out_tokens[size_t(b) * (max_k + 1) + acc] = sh.row[max_k + acc].idx;
-    } else {
-      resid = acc < K ? 1 : 0;
-      u = resid ? a.u_residual[b] : a.u_bonus[b];
+    if (a.p_draft) a.p_draft[o] = pd;
+    if (a.p_target) a.p_target[o] = pt;
+    if (a.labels) a.labels[o] = lab;
+  }
+  a.accept_len[b] = acc;
+  for (int i = 0; i <= max_k; ++i)
+    a.out_tokens[size_t(b) * (max_k + 1) + i] = i < acc ? a.tokens[size_t(b) * max_k + i] : -1;
+  DrawDesc dd{acc, 0, 0.f, 0};
+  if (greedy) {
+    a.out_tokens[size_t(b) * (max_k + 1) + acc] = row[max_k + acc].idx;
+  } else {
+    dd.mode = acc < K ? 1 : 2;
+    dd.u = acc < K ? a.u_residual[b] : a.u_bonus[b];
+  }
+  desc[b] = dd;
+}
+
+// Weight of one element pair: (pt' - pd')+ (residual) or pt'.
+template <typename ET>
+__device__ __forceinline__ void pair_w(float zt, float zd, const RowInfo& it, const RowInfo& id, float c, bool resid,
+                                       float* wr, float* wt) {
+  const float x = Key<ET>::of(zt) >= it.t ? fast_exp2(fmaf(zt, c, -it.kk)) : 0.f;
+  *wt = x;
+  if (resid) {
+    const float y = Key<ET>::of(zd) >= id.t ? fast_exp2(fmaf(zd, c, -id.kk)) : 0.f;
+    *wr = fmaxf(x - y, 0.f);
+  } else {
+    *wr = x;
+  }
+}
+
+// Draw weights: workgroup (b, s) sums its 32 KiB segment of the draw rows per
+// slice (slice k = vector k of every thread: 4 KiB of contiguous tokens).
+template <typename ET>
+__global__ __launch_bounds__(kFT) void filt_weight_kernel(FiltArgs a, const RowInfo* info, const DrawDesc* desc,
+                                                          float* slices) {
+  __shared__ float red[2][kFV][kFT / 64];
+  constexpr int N = Elem<ET>::N;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int n = a.nseg2;
+  const int b = int(blockIdx.x / uint32_t(n)), s = int(blockIdx.x % uint32_t(n));
+  // the request's scalars in one round trip, then the rows
+  const DrawDesc dd = desc[b];
+  const int64_t ds = a.draft_start[b], ts = a.target_start[b];
+  const float T = a.temperature[b];
+  if (dd.mode == 0) return;
+  const bool resid = dd.mode == 1;
+  const int R = a.R, max_k = a.max_k;
+  const ET* rt = static_cast<const ET*>(a.target) + (ts + dd.acc) * a.target_stride;
+  const ET* rd = resid ? static_cast<const ET*>(a.draft) + (ds + dd.acc) * a.draft_stride : rt;
+  const bool al = is_aligned16(rt) && is_aligned16(rd);
+  const int hb = s * kFT * kFV * N;
+  const bool full = al && hb + kFT * kFV * N <= a.V;
+  const float c = kLog2e / T;
+  uint4 vt[kFV], vd[kFV];
+#pragma unroll
+  for (int k = 0; k < kFV; ++k) {
+    const int e0 = hb + (k * kFT + tid) * N;
+    vt[k] = full ? load_stream16(rt + e0) : load_raw<ET>(rt, e0, a.V, al);
+    vd[k] = !resid ? vt[k] : full ? load_stream16(rd + e0) : load_raw<ET>(rd, e0, a.V, al);
+  }
+  const RowInfo it = info[size_t(b) * R + max_k + dd.acc];
+  const RowInfo id = resid ? info[size_t(b) * R + dd.acc] : it;
+#pragma unroll
+  for (int k = 0; k < kFV; ++k) {
+    const int e0 = hb + (k * kFT + tid) * N;
+    float sr = 0.f, st = 0.f;
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      float wr, wt;
+      pair_w<ET>(Elem<ET>::get(vt[k], j), Elem<ET>::get(vd[k], j), it, id, c, resid, &wr, &wt);
+      const bool in = e0 + j < a.V;
+      sr += in ? wr : 0.f;
+      st += in ? wt : 0.f;
     }
-    sh.a = acc;
-    sh.resid = resid;
-    sh.u = u;
+    sr = wave_sum(sr);
+    st = wave_sum(st);
+    if (lane == 0) {
+      red[0][k][wv] = sr;
+      red[1][k][wv] = st;
+    }
   }
   __syncthreads();
-  if (greedy) return;
-  const int acc = sh.a;
-  bool resid = sh.resid != 0;
-  const float u = sh.u;
-  const ET* rt = row_ptr<ET>(a, b, max_k + acc);
-  const ET* rd = resid ? row_ptr<ET>(a, b, acc) : rt;
-  const bool al = is_aligned16(rt) && is_aligned16(rd);
-  const RowInfo it = sh.row[max_k + acc];
-  const RowInfo id = resid ? sh.row[acc] : it;
-  const int nch = (a.V + kChunk - 1) / kChunk;
-  float Z = 0.f;
-  for (int pass = 0; pass < 2; ++pass) {
-    // chunk sums, kGroup chunks in flight
-    for (int g0 = 0; g0 < nch; g0 += kGroup) {
-      float w[kGroup][8];
-#pragma unroll
-      for (int q = 0; q < kGroup; ++q) elem8<ET>(rt, rd, (g0 + q) * kChunk + tid * 8, a.V, al, it, id, c, resid, w[q]);
-#pragma unroll
-      for (int q = 0; q < kGroup; ++q) {
-        float x = 0.f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) x += w[q][j];
-        x = wave_sum(x);
-        if (lane == 0) sh.wsum[q][wv] = x;
-      }
-      __syncthreads();
-      if (tid < kGroup && g0 + tid < nch) {
-        float x = 0.f;
-        for (int q = 0; q < kVW; ++q) x += sh.wsum[tid][q];
-        sh.chunk[g0 + tid] = x;
-      }
-      __syncthreads();
-    }
-    if (tid == 0) {
-      float z = 0.f;
-      for (int q = 0; q < nch; ++q) z += sh.chunk[q];
-      sh.u = z;
-    }
-    __syncthreads();
-    Z = sh.u;
-    __syncthreads();
-    if (Z > 0.f || !resid) break;
-    resid = false;  // the residual has no mass: draw from the target row
+  if (tid < 2 * kFV) {
+    const int q = tid / kFV, k = tid % kFV;
+    float x = 0.f;
+    for (int w = 0; w < kFT / 64; ++w) x += red[q][k][w];
+    slices[((size_t(b) * n + s) * 2 + q) * kFV + k] = x;
   }
-  const RowInfo& id2 = resid ? id : it;
-  // the chunk where the running sum first exceeds u Z; if rounding leaves
-  // none, the last chunk with weight and its last positive-weight token
+}
+
+__device__ __forceinline__ int ft_max_int(int x, int* part, int tid) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = max(x, __shfl_xor(x, o, 64));
+  if ((tid & 63) == 0) part[tid >> 6] = x;
+  __syncthreads();
+  int m = part[0];
+  for (int q = 1; q < kFT / 64; ++q) m = max(m, part[q]);
+  __syncthreads();
+  return m;
+}
+
+// The draw: running sums of the slice weights in token order locate the slice
+// where u Z is crossed, a scan of that slice the token.  If rounding leaves
+// no crossing, the last positive-weight token (of the row, or of the slice).
+template <typename ET>
+__global__ __launch_bounds__(kFT) void filt_search_kernel(FiltArgs a, const RowInfo* info, const DrawDesc* desc,
+                                                          const float* slices) {
+  __shared__ float part[kFT / 64];
+  __shared__ int ip[kFT / 64];
+  __shared__ int pick, last, mode;
+  __shared__ float rem;
+  __shared__ float sw[2][kMaxSlices];
+  constexpr int N = Elem<ET>::N;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int b = blockIdx.x, n = a.nseg2;
+  const DrawDesc dd = desc[b];
+  if (dd.mode == 0) return;
+  const int ns = n * kFV;  // slices of a row
+  // slice j = (segment j / kFV, vector j % kFV); its weights of kind q sit at
+  // ((j / kFV) * 2 + q) * kFV + j % kFV of the request's block
+  const float* sl = slices + size_t(b) * n * 2 * kFV;
+  for (int e = tid; e < 2 * ns; e += kFT) {
+    const int seg = e / (2 * kFV), q = (e / kFV) & 1, k = e % kFV;
+    sw[q][seg * kFV + k] = sl[e];
+  }
+  __syncthreads();
+  auto slice_w = [&](int j, int q) { return sw[q][j]; };
   if (tid == 0) {
-    const float t = u * Z;
+    int q = dd.mode == 1 ? 0 : 1;
+    float Z = 0.f;
+    for (int j = 0; j < ns; ++j) Z += slice_w(j, q);
+    if (q == 0 && !(Z > 0.f)) {  // the residual has no mass: draw from the target row
+      q = 1;
+      Z = 0.f;
+      for (int j = 0; j < ns; ++j) Z += slice_w(j, q);
+    }
+    const float t = dd.u * Z;
     float cum = 0.f;
     int ch = -1;
-    for (int q = 0; q < nch; ++q) {
-      if (cum + sh.chunk[q] > t) {
-        ch = q;
+    for (int j = 0; j < ns; ++j) {
+      const float w = slice_w(j, q);
+      if (cum + w > t) {
+        ch = j;
         break;
       }
-      cum += sh.chunk[q];
+      cum += w;
     }
-    int last = ch < 0 ? 1 : 0;
+    int want_last = 0;
     if (ch < 0) {
+      want_last = 1;
       ch = 0;
-      for (int q = nch - 1; q >= 0; --q)
-        if (sh.chunk[q] > 0.f) {
-          ch = q;
+      for (int j = ns - 1; j >= 0; --j)
+        if (slice_w(j, q) > 0.f) {
+          ch = j;
           break;
         }
     }
-    sh.pick = ch;
-    sh.resid = last;
-    sh.u = t - cum;  // the threshold left inside the chunk
+    pick = ch;
+    last = want_last;
+    mode = q;
+    rem = t - cum;
   }
   __syncthreads();
-  const int ch = sh.pick;
-  const bool want_last = sh.resid != 0;
-  const float rem = sh.u;
-  __syncthreads();
-  float w[8];
-  elem8<ET>(rt, rd, ch * kChunk + tid * 8, a.V, al, it, id2, c, resid, w);
+  const int ch = pick;
+  const bool resid = mode == 0;
+  const int R = a.R, max_k = a.max_k;
+  const RowInfo it = info[size_t(b) * R + max_k + dd.acc];
+  const RowInfo id = resid ? info[size_t(b) * R + dd.acc] : it;
+  const ET* rt = row_ptr<ET>(a, b, max_k + dd.acc);
+  const ET* rd = resid ? row_ptr<ET>(a, b, dd.acc) : rt;
+  const bool al = is_aligned16(rt) && is_aligned16(rd);
+  const float c = kLog2e / a.temperature[b];
+  // the slice: kFT * N contiguous tokens, thread t holding N of them
+  const int first = (ch / kFV) * kFT * kFV * N + (ch % kFV) * kFT * N + tid * N;
+  const uint4 vt = load_raw<ET>(rt, first, a.V, al);
+  const uint4 vd = resid ? load_raw<ET>(rd, first, a.V, al) : vt;
+  float w[N];
   float own = 0.f;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) own += w[j];
+  for (int j = 0; j < N; ++j) {
+    float wr, wt;
+    pair_w<ET>(Elem<ET>::get(vt, j), Elem<ET>::get(vd, j), it, id, c, resid, &wr, &wt);
+    w[j] = first + j < a.V ? wr : 0.f;
+    own += w[j];
+  }
   float incl = own;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
     const float y = __shfl_up(incl, o, 64);
     if (lane >= o) incl += y;
   }
-  if (lane == 63) sh.wtot[wv] = incl;
+  if (lane == 63) part[wv] = incl;
   __syncthreads();
   float run = incl - own;
-  for (int q = 0; q < wv; ++q) run += sh.wtot[q];
-  int first = 0x7fffffff, lastpos = -1;
+  for (int q = 0; q < wv; ++q) run += part[q];
+  int fst = 0x7fffffff, lastpos = -1;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
+  for (int j = 0; j < N; ++j) {
     run += w[j];
-    const int v = ch * kChunk + tid * 8 + j;
     if (w[j] > 0.f) {
-      lastpos = v;
-      if (first == 0x7fffffff && run > rem) first = v;
+      lastpos = first + j;
+      if (fst == 0x7fffffff && run > rem) fst = first + j;
     }
   }
-  const int fmin = -vt_max_int(-first, sh.pi, tid);
-  const int lmax = vt_max_int(lastpos, sh.pi, tid);
-  if (tid == 0) {
-    const int tok = (!want_last && fmin != 0x7fffffff) ? fmin : lmax;
-    a.out_tokens[size_t(b) * (max_k + 1) + acc] = tok;
-  }
+  const int fmin = -ft_max_int(-fst, ip, tid);
+  const int lmax = ft_max_int(lastpos, ip, tid);
+  if (tid == 0) a.out_tokens[size_t(b) * (max_k + 1) + dd.acc] = (!last && fmin != 0x7fffffff) ? fmin : lmax;
 }
 
 }  // namespace
@@ -703,6 +804,10 @@ hipError_t launch_filtered(VerifyArgs va, const FilterIO& io, int dtype, hipStre
              va.p_target, io.kept, va.partials, va.zval, io.hmass, io.hcount,
              reinterpret_cast<FSearch*>(io.search)};
   const unsigned g1 = unsigned(n1), g2 = unsigned(va.B) * unsigned(va.R);
+  const unsigned gw = unsigned(va.B) * unsigned(va.nseg2);
+  RowInfo* info = reinterpret_cast<RowInfo*>(io.info);
+  DrawDesc* desc = reinterpret_cast<DrawDesc*>(io.desc);
+  float* slices = io.slices;
   const int levels = dtype == SV_BF16 ? 2 : 4;  // key digits after level 0
   if (dtype == SV_BF16) {
     hipLaunchKernelGGL((filt_hist_kernel<uint16_t, true>), dim3(g1), dim3(kFT), 0, stream, a);
@@ -711,7 +816,10 @@ hipError_t launch_filtered(VerifyArgs va, const FilterIO& io, int dtype, hipStre
       hipLaunchKernelGGL((filt_hist_kernel<uint16_t, false>), dim3(g1), dim3(kFT), 0, stream, a);
       hipLaunchKernelGGL((filt_select_kernel<uint16_t, false>), dim3(g2), dim3(kFT), 0, stream, a);
     }
-    hipLaunchKernelGGL(filt_verify_kernel<uint16_t>, dim3(unsigned(va.B)), dim3(kVT), 0, stream, a);
+    hipLaunchKernelGGL(filt_verdict_kernel_impl, dim3(unsigned(va.B)), dim3(64), 0, stream, a, info, desc, true);
+    hipLaunchKernelGGL(filt_weight_kernel<uint16_t>, dim3(gw), dim3(kFT), 0, stream, a, info, desc, slices);
+    hipLaunchKernelGGL(filt_search_kernel<uint16_t>, dim3(unsigned(va.B)), dim3(kFT), 0, stream, a, info, desc,
+                       slices);
   } else {
     hipLaunchKernelGGL((filt_hist_kernel<float, true>), dim3(g1), dim3(kFT), 0, stream, a);
     hipLaunchKernelGGL((filt_select_kernel<float, true>), dim3(g2), dim3(kFT), 0, stream, a);
@@ -719,7 +827,10 @@ hipError_t launch_filtered(VerifyArgs va, const FilterIO& io, int dtype, hipStre
       hipLaunchKernelGGL((filt_hist_kernel<float, false>), dim3(g1), dim3(kFT), 0, stream, a);
       hipLaunchKernelGGL((filt_select_kernel<float, false>), dim3(g2), dim3(kFT), 0, stream, a);
     }
-    hipLaunchKernelGGL(filt_verify_kernel<float>, dim3(unsigned(va.B)), dim3(kVT), 0, stream, a);
+    hipLaunchKernelGGL(filt_verdict_kernel_impl, dim3(unsigned(va.B)), dim3(64), 0, stream, a, info, desc, false);
+    hipLaunchKernelGGL(filt_weight_kernel<float>, dim3(gw), dim3(kFT), 0, stream, a, info, desc, slices);
+    hipLaunchKernelGGL(filt_search_kernel<float>, dim3(unsigned(va.B)), dim3(kFT), 0, stream, a, info, desc,
+                       slices);
   }
   return hipGetLastError();
 }

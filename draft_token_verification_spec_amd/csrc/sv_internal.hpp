@@ -101,8 +101,10 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // and counts) and per (row slot, search) threshold-search states.
 constexpr int kFilterBins = 256;
 constexpr size_t kFilterSearchBytes = 48;
+constexpr size_t kFilterRowBytes = 16;   // per row slot: normaliser, threshold, argmax
+constexpr size_t kFilterDescBytes = 16;  // per request: accept length, draw kind, uniform
 struct FilterLayout {
-  size_t hmass, hcount, search, total;
+  size_t hmass, hcount, search, info, desc, slices, total;
 };
 
 // Hand-off slot of the draw kernel: 8 bytes written in one store, the low
@@ -138,7 +140,10 @@ inline FilterLayout filter_layout(int B, int V, int max_k, int dtype) {
   F.hmass = L.total;
   F.hcount = F.hmass + align256(slots * 8);
   F.search = F.hcount + align256(slots * 4);
-  F.total = F.search + align256(size_t(B) * L.R * 2 * kFilterSearchBytes);
+  F.info = F.search + align256(size_t(B) * L.R * 2 * kFilterSearchBytes);
+  F.desc = F.info + align256(size_t(B) * L.R * kFilterRowBytes);
+  F.slices = F.desc + align256(size_t(B) * kFilterDescBytes);
+  F.total = F.slices + align256(size_t(B) * L.nseg2 * 2 * kDrawSlices * 4);
   return F;
 }
 
@@ -231,6 +236,9 @@ struct FilterIO {
   uint64_t* hmass;
   uint32_t* hcount;
   void* search;
+  void* info;
+  void* desc;
+  float* slices;
 };
 hipError_t launch_filtered(VerifyArgs a, const FilterIO& io, int dtype, hipStream_t stream);
 hipError_t launch_av_score(const ScoreArgs& a, int dtype, hipStream_t stream);
