@@ -138,42 +138,61 @@ __device__ __forceinline__ double wave_sum_d(double v) {
 __global__ __launch_bounds__(kThreads) void av_fit_kernel(int B, int max_k, const float* feature,
                                                           const int8_t* labels, float* params, double* accum,
                                                           float damping_c, float ridge, int do_update) {
-  __shared__ double red[kWaves][6];
-  __shared__ double acc[SV_MAX_K][6];  // accumulator after this step
+  __shared__ double red[kWaves][SV_MAX_K][6];  // per wave and position, summed over the chunks in order
+  __shared__ double acc[SV_MAX_K][6];          // accumulator after this step
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // parameters and the incoming accumulator with the first chunk's items:
+  // one round trip to memory instead of one per position
   const double omega = params[0];
-  for (int i = 0; i < max_k; ++i) {
-    const double beta = params[1 + i];
-    double v[6] = {0, 0, 0, 0, 0, 0};
-    for (int b = tid; b < B; b += kThreads) {
-      const int y = labels[size_t(b) * max_k + i];
-      if (y != 0 && y != 1) continue;
-      const double x = feature[size_t(b) * max_k + i];
-      const double pi = sigmoid_d(omega * x + beta);
-      const double w = pi * (1.0 - pi);
-      const double r = pi - double(y);
-      v[0] += 1.0;
-      v[1] += w;
-      v[2] += w * x;
-      v[3] += w * x * x;
-      v[4] += r;
-      v[5] += r * x;
+  double beta[SV_MAX_K];
+#pragma unroll
+  for (int i = 0; i < SV_MAX_K; ++i) beta[i] = i < max_k ? double(params[1 + i]) : 0.0;
+  const double acc_in = tid < 6 * max_k ? accum[tid] : 0.0;
+  for (int e = tid; e < kWaves * SV_MAX_K * 6; e += kThreads) (&red[0][0][0])[e] = 0.0;
+  __syncthreads();
+  for (int b0 = 0; b0 < B; b0 += kThreads) {
+    const int b = b0 + tid;
+    int y[SV_MAX_K];
+    float x[SV_MAX_K];
+#pragma unroll
+    for (int i = 0; i < SV_MAX_K; ++i) {
+      const bool in = b < B && i < max_k;
+      y[i] = in ? labels[size_t(b) * max_k + i] : -1;
+      x[i] = in ? feature[size_t(b) * max_k + i] : 0.f;
     }
 #pragma unroll
-    for (int k = 0; k < 6; ++k) v[k] = wave_sum_d(v[k]);
-    if (lane == 0)
+    for (int i = 0; i < SV_MAX_K; ++i) {
+      if (i >= max_k) continue;  // uniform
+      double v[6] = {0, 0, 0, 0, 0, 0};
+      if (y[i] == 0 || y[i] == 1) {
+        const double xd = x[i];
+        const double pi = sigmoid_d(omega * xd + beta[i]);
+        const double w = pi * (1.0 - pi);
+        const double r = pi - double(y[i]);
+        v[0] = 1.0;
+        v[1] = w;
+        v[2] = w * xd;
+        v[3] = w * xd * xd;
+        v[4] = r;
+        v[5] = r * xd;
+      }
 #pragma unroll
-      for (int k = 0; k < 6; ++k) red[wave][k] = v[k];
-    __syncthreads();
-    if (tid < 6) {
-      double t = red[0][tid];
-      for (int w = 1; w < kWaves; ++w) t += red[w][tid];
-      t += accum[size_t(i) * 6 + tid];
-      acc[i][tid] = t;
-      if (!do_update) accum[size_t(i) * 6 + tid] = t;
+      for (int k = 0; k < 6; ++k) v[k] = wave_sum_d(v[k]);
+      if (lane == 0)
+#pragma unroll
+        for (int k = 0; k < 6; ++k) red[wave][i][k] += v[k];
     }
-    __syncthreads();
   }
+  __syncthreads();
+  if (tid < 6 * max_k) {
+    const int i = tid / 6, k = tid % 6;
+    double t = red[0][i][k];
+    for (int w = 1; w < kWaves; ++w) t += red[w][i][k];
+    t += acc_in;
+    acc[i][k] = t;
+    if (!do_update) accum[tid] = t;
+  }
+  __syncthreads();
   if (!do_update) return;
   if (tid == 0) {
     double N = 0.0, h = ridge, gw = 0.0;
