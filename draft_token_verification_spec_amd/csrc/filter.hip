@@ -31,8 +31,7 @@ namespace {
 
 constexpr int kFT = 256;  // threads of the histogram and selection kernels
 constexpr int kFV = 8;    // 16-byte vectors per thread and segment (32 KiB)
-constexpr int kBins = 256;
-constexpr int kBinsPerLog2 = 8;
+constexpr int kBins = 256;  // key-digit bins
 constexpr float kFix = 1099511627776.f;  // 2^40
 static_assert(kFT * kFV * 16 == kHalfBytes, "a histogram segment is a 32 KiB sampling segment");
 
@@ -70,30 +69,47 @@ struct Key<float> {
   }
 };
 
-// Level-0 bin: floor of 8 x (log2 of the probability ratio to the row
-// maximum), clamped to [0, 255].  Non-increasing in z.
-__device__ __forceinline__ int bin0(float z, float c, float mc) {
-  const float e = fmaf(z, c, -mc);
-  return e >= 0.f ? 0 : (e > -32.f ? int(-e * float(kBinsPerLog2)) : kBins - 1);
+// Level-0 bin: floor of t = 16 x log2(maximum weight / weight), clamped to
+// [0, 511].  Non-increasing in z.  Bin j < 511 holds the weights 2^(-t/16)
+// with t in [j, j+1) (bin 0 also t < 0, a rounding of the maximum's own
+// term), bin 511 everything from 2^-511/16 down.  Within bin j < 511 a weight
+// is the bin's lower edge 2^-(j+1)/16 times r = 2^((1 - (t - j))/16) in
+// (1, 2^(1/16)], and (r - 1) is kept in 2^-21 fixed point: the counts and
+// these sums are integers (32 bits each per segment suffice, added as the
+// two halves of one 64-bit word), so the bin masses edge x (count + sum
+// 2^-21) do not depend on the order of the additions and are exact to
+// 2^-22 relative.
+constexpr int kBins0 = 512;
+constexpr int kBinsPerLog2 = 16;
+constexpr float kFrac0 = 2097152.f;  // 2^21
+// t = 16 x log2(max weight / weight) = (max - z) * 16c, from the row's
+// c16 = 16c and mc16 = max * 16c; the bin is t clamped to [0, 511]
+__device__ __forceinline__ float bin_t(float z, float c16, float mc16) { return fmaf(z, -c16, mc16); }
+__device__ __forceinline__ int bin_of_t(float t) {
+  return int(__builtin_amdgcn_fmed3f(t, 0.f, float(kBins0 - 1)));
 }
+__device__ __forceinline__ int bin0(float z, float c16, float mc16) { return bin_of_t(bin_t(z, c16, mc16)); }
 
+// Weight of an element relative to the row maximum, in 2^-40 fixed point.
 __device__ __forceinline__ uint64_t fixed_mass(float z, float c, float mc) {
   return uint64_t(__builtin_rintf(fast_exp2(fmaf(z, c, -mc)) * kFix));
 }
 
 // State of one threshold search of one row (slot 0: top-k, slot 1: top-p).
+// Masses are in units of the row maximum's weight.
 struct FSearch {
-  uint32_t lo, hi;   // key interval holding the threshold
-  uint32_t cabove;   // tokens with a key above the interval
-  uint32_t state;    // 0 unused, 1 searching, 2 done
-  uint64_t mabove;   // fixed-point mass above the interval
-  uint64_t mfinal;   // done: mass of the kept tokens
-  double target;     // top-k: k; top-p: top_p x total mass
-  uint32_t key;      // done: the threshold key
-  uint32_t kept;     // done: kept tokens
+  uint32_t lo, hi;  // key interval holding the threshold
+  uint32_t cabove;  // tokens with a key above the interval
+  uint32_t state;   // 0 unused, 1 searching, 2 done
+  double mabove;    // mass above the interval (from the window pass on)
+  double mfinal;    // done: mass of the kept tokens
+  double target;    // top-k: k; top-p: top_p x the row's mass
+  uint32_t key;     // done: the threshold key
+  uint32_t kept;    // done: kept tokens
 };
 static_assert(sizeof(FSearch) == kFilterSearchBytes, "search state layout");
-static_assert(kBins == kFilterBins, "histogram bins");
+static_assert(kBins == kFilterBins && kBins0 == kFilterBins0, "histogram bins");
+static_assert(kFT * kFV * 16 / 2 * 0.0443 * 2097152.0 < 4294967296.0, "level-0 sums of a segment fit 32 bits");
 
 struct FiltArgs {
   int B, V, max_k, R, nseg2;
@@ -119,8 +135,8 @@ struct FiltArgs {
   int32_t* kept;
   const Partial* partials;  // [B][R][nseg2] of the statistics kernel
   const float* zval;        // [B][R] logits at the draft tokens
-  uint64_t* hmass;          // [B][R][nseg2][2][kBins]
-  uint32_t* hcount;         // [B][R][nseg2][2][kBins]
+  uint64_t* hmass;          // [B][R][nseg2][2][kBins]  key-level masses (digits wider than one key)
+  uint32_t* hcount;         // [B][R][nseg2][2][kBins0]  level 0: counts, fraction sums; key levels: counts
   FSearch* search;          // [B][R][2]
 };
 
@@ -166,6 +182,23 @@ __device__ __forceinline__ float wave_row_max(const Partial* p, int n, int lane)
   return m;
 }
 
+// Maximum and sum of exp2((z - max) c) of a row from its segment statistics,
+// merged by one wave (merge_ms is symmetric: every lane gets the same value).
+__device__ __forceinline__ void wave_row_ms(const Partial* p, int n, float c, int lane, float* mo, float* so) {
+  float m = -INFINITY, s = 0.f, cnt = 0.f;
+  for (int q = lane; q < n; q += 64) {
+    const Partial x = p[q];
+    merge_ms(m, s, cnt, x.m, x.s + x.cnt, 0.f, c);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float m2 = __shfl_xor(m, o, 64), s2 = __shfl_xor(s, o, 64);
+    merge_ms(m, s, cnt, m2, s2, 0.f, c);
+  }
+  *mo = m;
+  *so = s;
+}
+
 // Vector of a row holding elements first..first+N-1; positions >= limit
 // hold a NaN (never a logit: rows have no NaN).
 template <typename ET>
@@ -181,41 +214,34 @@ __device__ __forceinline__ uint4 load_nan_tail(const ET* row, int first, int lim
 
 struct HistShared {
   uint64_t mass[2][kBins];
-  uint32_t count[2][kBins];
+  union {
+    uint64_t bins[kBins0];      // level 0: fraction sum << 32 | count, by bin
+    uint32_t count[2][kBins0];  // key levels: [q][digit]
+  };
 };
 
-// An element of a search interval into that search's digit histogram; out
-// of line, so that the streaming loop around it stays small (few elements of
-// a row fall in the interval).
-template <typename ET>
-__device__ __noinline__ void key_add(HistShared& sh, int q, float z, uint32_t lo, int shift, float c, float mc) {
-  const int dg = int((Key<ET>::of(z) - lo) >> shift);
-  atomicAdd(reinterpret_cast<unsigned long long*>(&sh.mass[q][dg]),
-            static_cast<unsigned long long>(fixed_mass(z, c, mc)));
-  atomicAdd(&sh.count[q][dg], 1u);
-}
-
-// One level of the histograms: workgroup = segment s of row slot rs of
-// request b.  Level 0 bins every element; later levels bin the elements
-// whose key lies in a searching slot's interval by their digit there.
-template <typename ET, bool L0>
+// One histogram pass: workgroup = segment s of row slot rs of request b.
+//   LV 0  every element by level-0 bin: count and fraction sum;
+//   LV 1  per searching slot, the elements of its key interval by key digit:
+//         counts, and 2^-40 fixed-point masses when a digit spans several
+//         keys (a single key's mass is its count times its weight).
+template <typename ET, int LV>
 __global__ __launch_bounds__(kFT) void filt_hist_kernel(FiltArgs a) {
   __shared__ HistShared sh;
   constexpr int N = Elem<ET>::N;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int n = a.nseg2, R = a.R;
   const uint32_t item = blockIdx.x;
   const int s = int(item % uint32_t(n));
   const int rs = int((item / uint32_t(n)) % uint32_t(R));
   const int b = int(item / (uint32_t(n) * uint32_t(R)));
   const size_t row = size_t(b) * R + rs;
-  // every scalar the workgroup needs in one round trip, before any decision:
-  // under a saturated memory system each dependent round trip is long
+  // every scalar the workgroup needs in one round trip, before any decision
   const ReqFilter f = req_filter(a, b);
   const bool is_draft = rs < a.max_k;
   const int64_t start = is_draft ? a.draft_start[b] : a.target_start[b];
-  uint32_t st_state[2] = {1u, 0u}, lo[2] = {0u, 0u}, hi[2] = {0u, 0u};
-  if (!L0) {
+  uint32_t st_state[2] = {0u, 0u}, lo[2] = {0u, 0u}, hi[2] = {0u, 0u};
+  if (LV > 0) {
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const FSearch& st = a.search[row * 2 + q];
@@ -233,7 +259,7 @@ __global__ __launch_bounds__(kFT) void filt_hist_kernel(FiltArgs a) {
     const uint32_t w = hi[q] - lo[q];
     shift[q] = w == 0u ? 0 : max(0, 32 - __clz(w) - 8);
   }
-  if (!on[0] && !on[1]) return;
+  if (LV > 0 && !on[0] && !on[1]) return;
   const ET* rp = is_draft ? static_cast<const ET*>(a.draft) + (start + rs) * a.draft_stride
                           : static_cast<const ET*>(a.target) + (start + (rs - a.max_k)) * a.target_stride;
   const bool al = is_aligned16(rp);
@@ -248,62 +274,95 @@ __global__ __launch_bounds__(kFT) void filt_hist_kernel(FiltArgs a) {
     for (int k = 0; k < kFV; ++k) v[k] = load_nan_tail<ET>(rp, hb + (k * kFT + tid) * N, a.V, al);
   }
   const float c = kLog2e / f.T;
-  const float mc = wave_row_max(a.partials + row * n, n, tid & 63) * c;
-  for (int j = tid; j < 2 * kBins; j += kFT) {
-    (&sh.mass[0][0])[j] = 0u;
+  const float mrow = wave_row_max(a.partials + row * n, n, lane);
+  const float mc = mrow * c;
+  const float c16 = c * float(kBinsPerLog2), mc16 = mrow * c16;
+  for (int j = tid; j < 2 * kBins0; j += kFT) {
     (&sh.count[0][0])[j] = 0u;
+    if (j < 2 * kBins) (&sh.mass[0][0])[j] = 0u;
   }
-  // key levels: a slot's key interval as a value interval (the key order is
-  // the value order, -0 and +0 one value), so most elements are dismissed
-  // with two compares
+  // a slot's key interval as a value interval (the key order is the value
+  // order, -0 and +0 one value): two compares dismiss an element
   float zlo[2], zhi[2];
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     zlo[q] = on[q] ? Key<ET>::value(lo[q]) : INFINITY;
-    zhi[q] = on[q] ? Key<ET>::value(hi[q]) : -INFINITY;
+    zhi[q] = on[q] ? Key<ET>::value(hi[q]) : INFINITY;
   }
   __syncthreads();
-  auto bin_elem = [&](float z) {
-    if (L0) {
-      const int bn = bin0(z, c, mc);
-      atomicAdd(reinterpret_cast<unsigned long long*>(&sh.mass[0][bn]),
-                static_cast<unsigned long long>(fixed_mass(z, c, mc)));
-      atomicAdd(&sh.count[0][bn], 1u);
-    } else {
-#pragma unroll
-      for (int q = 0; q < 2; ++q)
-        if (z >= zlo[q] && z <= zhi[q]) key_add<ET>(sh, q, z, lo[q], shift[q], c, mc);
-    }
-  };
-  // past the end of the row the tail loads hold NaN, which no key interval
-  // holds; level 0 skips it explicitly
-  if (full || !L0) {
-#pragma unroll
-    for (int k = 0; k < kFV; ++k)
-#pragma unroll
-      for (int j = 0; j < N; ++j) bin_elem(Elem<ET>::get(v[k], j));
-  } else {
+  // past the end of the row the tail loads hold NaN: no interval holds it,
+  // and level 0 skips it
+  if (LV == 0) {
 #pragma unroll
     for (int k = 0; k < kFV; ++k)
 #pragma unroll
       for (int j = 0; j < N; ++j) {
         const float z = Elem<ET>::get(v[k], j);
-        if (z == z) bin_elem(z);
+        if (full || z == z) {
+          const float t = bin_t(z, c16, mc16);
+          const int bn = bin_of_t(t);
+          // r - 1 of the weight relative to the bin's lower edge, 2^-21 units
+          const float r = fast_exp2(fmaf(t - float(bn), -1.f / kBinsPerLog2, 1.f / kBinsPerLog2));
+          const uint32_t u =
+              bn < kBins0 - 1 ? uint32_t(fminf(fmaxf(__builtin_rintf(fmaf(r, kFrac0, -kFrac0)), 0.f), 131071.f)) : 0u;
+          atomicAdd(reinterpret_cast<unsigned long long*>(&sh.bins[bn]),
+                    (static_cast<unsigned long long>(u) << 32) | 1ull);
+        }
       }
+  } else {
+    // per element a test against each searching slot's value interval; the
+    // common case of one search gets a loop of its own
+    auto digit_add = [&](int q, float z) {
+      const int dg = int((Key<ET>::of(z) - lo[q]) >> shift[q]);
+      atomicAdd(&sh.count[q][dg], 1u);
+      if (shift[q] > 0)
+        atomicAdd(reinterpret_cast<unsigned long long*>(&sh.mass[q][dg]),
+                  static_cast<unsigned long long>(fixed_mass(z, c, mc)));
+    };
+    if (on[0] && on[1]) {
+#pragma unroll
+      for (int k = 0; k < kFV; ++k)
+#pragma unroll
+        for (int j = 0; j < N; ++j) {
+          const float z = Elem<ET>::get(v[k], j);
+#pragma unroll
+          for (int q = 0; q < 2; ++q)
+            if (z >= zlo[q] && z <= zhi[q]) digit_add(q, z);
+        }
+    } else {
+      const int q = on[0] ? 0 : 1;
+      const float l = zlo[q], h = zhi[q];
+#pragma unroll
+      for (int k = 0; k < kFV; ++k)
+#pragma unroll
+        for (int j = 0; j < N; ++j) {
+          const float z = Elem<ET>::get(v[k], j);
+          if (z >= l && z <= h) digit_add(q, z);
+        }
+    }
   }
   __syncthreads();
-  const size_t base = (row * n + s) * 2;
+  const size_t seg = row * n + s;
+  if (LV == 0) {
+    // counts, then fraction sums
+    for (int j = tid; j < kBins0; j += kFT) {
+      const uint64_t x = sh.bins[j];
+      a.hcount[seg * 2 * kBins0 + j] = uint32_t(x);
+      a.hcount[seg * 2 * kBins0 + kBins0 + j] = uint32_t(x >> 32);
+    }
+    return;
+  }
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     if (!on[q]) continue;
-    a.hmass[(base + q) * kBins + tid] = sh.mass[q][tid];
-    a.hcount[(base + q) * kBins + tid] = sh.count[q][tid];
+    if (shift[q] > 0) a.hmass[(seg * 2 + q) * kBins + tid] = sh.mass[q][tid];
+    a.hcount[seg * 2 * kBins0 + q * kBins0 + tid] = sh.count[q][tid];
   }
 }
 
-// Exclusive prefix over the workgroup in thread order (integers: exact).
-template <typename T>
-__device__ __forceinline__ T block_excl_scan(T x, T* part, int tid, T* total) {
+// Exclusive prefix over the workgroup (NT threads) in thread order.
+template <int NT, typename T>
+__device__ __forceinline__ T block_excl_scan(T x, T* part, int tid) {
   const int lane = tid & 63, w = tid >> 6;
   T incl = x;
 #pragma unroll
@@ -313,59 +372,140 @@ __device__ __forceinline__ T block_excl_scan(T x, T* part, int tid, T* total) {
   }
   if (lane == 63) part[w] = incl;
   __syncthreads();
-  T before = 0, all = 0;
-  for (int q = 0; q < kFT / 64; ++q) {
-    before += q < w ? part[q] : T(0);
-    all += part[q];
-  }
+  T before = 0;
+  for (int q = 0; q < w; ++q) before += part[q];
   __syncthreads();
-  *total = all;
   return before + incl - x;
 }
 
+template <int NT>
 __device__ __forceinline__ int block_max_int(int x, int* part, int tid) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) x = max(x, __shfl_xor(x, o, 64));
   if ((tid & 63) == 0) part[tid >> 6] = x;
   __syncthreads();
   int m = part[0];
-  for (int q = 1; q < kFT / 64; ++q) m = max(m, part[q]);
+  for (int q = 1; q < NT / 64; ++q) m = max(m, part[q]);
   __syncthreads();
   return m;
 }
 
-// Keys mapping to level-0 bin j (a contiguous interval: bin0 is monotone in z).
+// The smallest key whose level-0 bin is <= j and the largest whose bin is
+// >= j (bin0 is non-increasing in the key): the keys of bins [.., j] and
+// [j, ..].
 template <typename ET>
-__device__ void bin_keys(int j, float c, float mc, uint32_t* klo, uint32_t* khi) {
-  // klo: the smallest key with bin <= j (true at kMax); khi: the largest
-  // key with bin >= j (true at kMin)
+__device__ uint32_t key_lo_of_bin(int j, float c16, float mc16) {
   uint64_t lo = Key<ET>::kMin, hi = Key<ET>::kMax;
   while (lo < hi) {
     const uint64_t mid = (lo + hi) >> 1;
-    if (bin0(Key<ET>::value(uint32_t(mid)), c, mc) <= j) hi = mid;
+    if (bin0(Key<ET>::value(uint32_t(mid)), c16, mc16) <= j) hi = mid;
     else lo = mid + 1;
   }
-  *klo = uint32_t(lo);
-  lo = Key<ET>::kMin;
-  hi = Key<ET>::kMax;
+  return uint32_t(lo);
+}
+
+template <typename ET>
+__device__ uint32_t key_hi_of_bin(int j, float c16, float mc16) {
+  uint64_t lo = Key<ET>::kMin, hi = Key<ET>::kMax;
   while (lo < hi) {
     const uint64_t mid = (lo + hi + 1) >> 1;
-    if (bin0(Key<ET>::value(uint32_t(mid)), c, mc) >= j) lo = mid;
+    if (bin0(Key<ET>::value(uint32_t(mid)), c16, mc16) >= j) lo = mid;
     else hi = mid - 1;
   }
-  *khi = uint32_t(lo);
+  return uint32_t(lo);
+}
+
+constexpr int kS0 = kBins0;  // threads of the level-0 selection: one per bin
+
+struct Sel0Shared {
+  double pd[kS0 / 64];
+  uint32_t pu[kS0 / 64];
+  int pi[kS0 / 64];
+  uint32_t cab[2];
+  double mab[2];
+  uint32_t klo[2], khi[2];
+};
+
+// Level-0 selection: one workgroup (one thread per bin) per row slot.  The
+// row's segment histograms are merged in order; bin masses are
+// edge x (count + sum 2^-21) (the last bin's mass never enters: nothing is
+// below it).  The boundary bin of each search is the last non-empty bin whose
+// count (top-k) or mass (top-p, against top_p x the row's sum from the
+// statistics) above it is below the target; the search continues over that
+// bin's keys with the count and mass above it.
+template <typename ET>
+__global__ __launch_bounds__(kS0) void filt_select0_kernel(FiltArgs a) {
+  __shared__ Sel0Shared sh;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int n = a.nseg2, R = a.R;
+  const int rs = int(blockIdx.x % uint32_t(R));
+  const int b = int(blockIdx.x / uint32_t(R));
+  const ReqFilter f = req_filter(a, b);
+  if (!row_filtered(a, f, rs)) return;
+  const size_t row = size_t(b) * R + rs;
+  const int j = tid;
+  uint32_t cnt = 0, frac = 0;
+#pragma unroll 8
+  for (int s = 0; s < n; ++s) {
+    cnt += a.hcount[(row * n + s) * 2 * kBins0 + j];
+    frac += a.hcount[(row * n + s) * 2 * kBins0 + kBins0 + j];
+  }
+  const float c = kLog2e / f.T;
+  float m, S;
+  wave_row_ms(a.partials + row * n, n, c, lane, &m, &S);
+  const float c16 = c * float(kBinsPerLog2), mc16 = m * c16;
+  const double edge = double(fast_exp2(-float(j + 1) * (1.f / kBinsPerLog2)));
+  const double mass = j < kBins0 - 1 ? edge * (double(cnt) + double(frac) / double(kFrac0)) : 0.0;
+  const uint32_t fc = block_excl_scan<kS0, uint32_t>(cnt, sh.pu, tid);
+  const double fm = block_excl_scan<kS0, double>(mass, sh.pd, tid);
+  const double tk = double(f.top_k);
+  const double tp = double(f.top_p) * double(S);
+  const int top = -block_max_int<kS0>(cnt > 0u ? -j : -kBins0, sh.pi, tid);
+  const int jk = block_max_int<kS0>(f.on_k && cnt > 0u && double(fc) < tk ? j : -1, sh.pi, tid);
+  const int jp = block_max_int<kS0>(f.on_p && cnt > 0u && fm < tp ? j : -1, sh.pi, tid);
+  const int jq[2] = {jk >= 0 ? jk : top, jp >= 0 ? jp : top};
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+    if (j == jq[q]) {
+      sh.cab[q] = fc;
+      sh.mab[q] = fm;
+    }
+  if (lane == 0 && (tid >> 6) < 4) {
+    // the boundary bin's key interval: two bisections per search, one wave each
+    const int q = (tid >> 6) >> 1, side = (tid >> 6) & 1;
+    const bool on = q == 0 ? f.on_k : f.on_p;
+    if (on) {
+      if (side == 0) sh.klo[q] = key_lo_of_bin<ET>(jq[q], c16, mc16);
+      else sh.khi[q] = key_hi_of_bin<ET>(jq[q], c16, mc16);
+    }
+  }
+  __syncthreads();
+  if (tid < 2) {
+    const int q = tid;
+    const bool on = q == 0 ? f.on_k : f.on_p;
+    FSearch w{};
+    if (on) {
+      w.lo = sh.klo[q];
+      w.hi = sh.khi[q];
+      w.cabove = sh.cab[q];
+      w.mabove = sh.mab[q];
+      w.target = q == 0 ? tk : tp;
+      w.state = 1u;
+    }
+    a.search[row * 2 + q] = w;
+  }
 }
 
 struct SelShared {
-  uint64_t p64[kFT / 64];
+  double pd[kFT / 64];
   uint32_t p32[kFT / 64];
   int pi[kFT / 64];
-  uint32_t bl[2], bh[2];
 };
 
-// Selection after level 0 (L0) or a key level: one workgroup per row slot;
-// thread j owns bin / digit j.
-template <typename ET, bool L0>
+// Key-level selection: one workgroup per row slot; thread j owns digit
+// kBins - 1 - j, so that an exclusive scan in thread order sums the digits
+// of larger keys.
+template <typename ET>
 __global__ __launch_bounds__(kFT) void filt_select_kernel(FiltArgs a) {
   __shared__ SelShared sh;
   const int tid = threadIdx.x;
@@ -376,88 +516,37 @@ __global__ __launch_bounds__(kFT) void filt_select_kernel(FiltArgs a) {
   if (!row_filtered(a, f, rs)) return;
   const size_t row = size_t(b) * R + rs;
   FSearch* st = a.search + row * 2;
-  if (L0) {
-    uint64_t m = 0;
-    uint32_t cnt = 0;
-#pragma unroll 8
-    for (int s = 0; s < n; ++s) {
-      const size_t h = ((row * n + s) * 2) * kBins + tid;
-      m += a.hmass[h];
-      cnt += a.hcount[h];
-    }
-    uint64_t mtot;
-    uint32_t ctot;
-    const uint64_t fm = block_excl_scan<uint64_t>(m, sh.p64, tid, &mtot);
-    const uint32_t fc = block_excl_scan<uint32_t>(cnt, sh.p32, tid, &ctot);
-    const double tk = double(f.top_k);
-    const double tp = double(f.top_p) * double(mtot);
-    // boundary bin of each search: the last non-empty bin whose mass (count)
-    // above is below the target; the top non-empty bin when none is
-    const int jk = block_max_int(f.on_k && cnt > 0u && double(fc) < tk ? tid : -1, sh.pi, tid);
-    const int jp = block_max_int(f.on_p && cnt > 0u && double(fm) < tp ? tid : -1, sh.pi, tid);
-    const int top = -block_max_int(cnt > 0u ? -tid : -kBins, sh.pi, tid);
-    const int jq[2] = {jk >= 0 ? jk : top, jp >= 0 ? jp : top};
-    const float c = kLog2e / f.T;
-    const float mc = wave_row_max(a.partials + row * n, n, tid & 63) * c;
-    // the key interval of each boundary bin, one wave per search
-    if ((tid & 63) == 0 && (tid >> 6) < 2) {
-      const int q = tid >> 6;
-      uint32_t lo = 0, hi = 0;
-      if (q == 0 ? f.on_k : f.on_p) bin_keys<ET>(jq[q], c, mc, &lo, &hi);
-      sh.bl[q] = lo;
-      sh.bh[q] = hi;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const bool on = q == 0 ? f.on_k : f.on_p;
-      if (tid != jq[q]) continue;
-      FSearch w{};
-      if (on) {
-        w.lo = sh.bl[q];
-        w.hi = sh.bh[q];
-        w.cabove = fc;
-        w.mabove = fm;
-        w.target = q == 0 ? tk : tp;
-        w.state = 1u;
-        if (w.lo == w.hi) {
-          w.state = 2u;
-          w.key = w.lo;
-          w.kept = fc + cnt;
-          w.mfinal = fm + m;
-        }
-      }
-      st[q] = w;
-    }
-    return;
-  }
+  const float c = kLog2e / f.T;
+  const float mc = wave_row_max(a.partials + row * n, n, tid & 63) * c;
 #pragma unroll 1
   for (int q = 0; q < 2; ++q) {
     const FSearch cur = st[q];
     if (cur.state != 1u) continue;
-    // thread j owns digit d = kBins - 1 - j, so that an exclusive scan in
-    // thread order sums the digits of larger keys
+    const double mabove = cur.mabove;
+    const uint32_t w = cur.hi - cur.lo;
+    const int shf = w == 0u ? 0 : max(0, 32 - __clz(w) - 8);
     const int d = kBins - 1 - tid;
-    uint64_t md = 0;
+    uint64_t mfix = 0;
     uint32_t cd = 0;
 #pragma unroll 8
     for (int s = 0; s < n; ++s) {
-      const size_t h = ((row * n + s) * 2 + q) * kBins + d;
-      md += a.hmass[h];
-      cd += a.hcount[h];
+      cd += a.hcount[(row * n + s) * 2 * kBins0 + q * kBins0 + d];
+      if (shf > 0) mfix += a.hmass[((row * n + s) * 2 + q) * kBins + d];
     }
-    uint64_t mtot;
-    uint32_t ctot;
-    const uint64_t fm = cur.mabove + block_excl_scan<uint64_t>(md, sh.p64, tid, &mtot);
-    const uint32_t fc = cur.cabove + block_excl_scan<uint32_t>(cd, sh.p32, tid, &ctot);
-    const bool ok = cd > 0u && (q == 0 ? double(fc) < cur.target : double(fm) < cur.target);
+    // a one-key digit's mass: its count times the weight of that key, the
+    // same float expression as an element's weight
+    const double md = shf > 0 ? double(mfix) / double(kFix)
+                              : (cd > 0u ? double(cd) * double(fast_exp2(fmaf(Key<ET>::value(cur.lo + uint32_t(d)), c,
+                                                                                  -mc)))
+                                         : 0.0);
+    const double fm = mabove + block_excl_scan<kFT, double>(md, sh.pd, tid);
+    const uint32_t fc = cur.cabove + block_excl_scan<kFT, uint32_t>(cd, sh.p32, tid);
+    const bool ok = cd > 0u && (q == 0 ? double(fc) < cur.target : fm < cur.target);
     // the smallest qualifying digit (the largest non-empty one if none is)
-    const int dq = -block_max_int(ok ? -d : -kBins, sh.pi, tid);
-    const int dtop = block_max_int(cd > 0u ? d : -1, sh.pi, tid);
+    const int dq = -block_max_int<kFT>(ok ? -d : -kBins, sh.pi, tid);
+    const int dtop = block_max_int<kFT>(cd > 0u ? d : -1, sh.pi, tid);
     const int ds = dq < kBins ? dq : dtop;
     if (d != ds) continue;
-    const uint32_t w = cur.hi - cur.lo;
-    const int shf = w == 0u ? 0 : max(0, 32 - __clz(w) - 8);
     FSearch nx = cur;
     const uint64_t lo = uint64_t(cur.lo) + (uint64_t(d) << shf);
     const uint64_t hi = min(uint64_t(cur.hi), lo + (uint64_t(1) << shf) - 1);
@@ -541,7 +630,7 @@ __global__ __launch_bounds__(64) void filt_verdict_kernel_impl(FiltArgs a, RowIn
           const FSearch& sp = st[1];
           const FSearch& use = !f.on_k ? sp : !f.on_p ? sk : (sk.key >= sp.key ? sk : sp);
           r.t = use.key;
-          r.kk = mc + (fast_log2(float(use.mfinal)) - 40.f);
+          r.kk = mc + fast_log2(float(use.mfinal));
           kept = int(use.kept);
         }
       }
@@ -808,24 +897,24 @@ hipError_t launch_filtered(VerifyArgs va, const FilterIO& io, int dtype, hipStre
   RowInfo* info = reinterpret_cast<RowInfo*>(io.info);
   DrawDesc* desc = reinterpret_cast<DrawDesc*>(io.desc);
   float* slices = io.slices;
-  const int levels = dtype == SV_BF16 ? 2 : 4;  // key digits after level 0
+  const int levels = dtype == SV_BF16 ? 2 : 4;  // key-digit levels after level 0
   if (dtype == SV_BF16) {
-    hipLaunchKernelGGL((filt_hist_kernel<uint16_t, true>), dim3(g1), dim3(kFT), 0, stream, a);
-    hipLaunchKernelGGL((filt_select_kernel<uint16_t, true>), dim3(g2), dim3(kFT), 0, stream, a);
+    hipLaunchKernelGGL((filt_hist_kernel<uint16_t, 0>), dim3(g1), dim3(kFT), 0, stream, a);
+    hipLaunchKernelGGL(filt_select0_kernel<uint16_t>, dim3(g2), dim3(kS0), 0, stream, a);
     for (int l = 0; l < levels; ++l) {
-      hipLaunchKernelGGL((filt_hist_kernel<uint16_t, false>), dim3(g1), dim3(kFT), 0, stream, a);
-      hipLaunchKernelGGL((filt_select_kernel<uint16_t, false>), dim3(g2), dim3(kFT), 0, stream, a);
+      hipLaunchKernelGGL((filt_hist_kernel<uint16_t, 1>), dim3(g1), dim3(kFT), 0, stream, a);
+      hipLaunchKernelGGL(filt_select_kernel<uint16_t>, dim3(g2), dim3(kFT), 0, stream, a);
     }
     hipLaunchKernelGGL(filt_verdict_kernel_impl, dim3(unsigned(va.B)), dim3(64), 0, stream, a, info, desc, true);
     hipLaunchKernelGGL(filt_weight_kernel<uint16_t>, dim3(gw), dim3(kFT), 0, stream, a, info, desc, slices);
     hipLaunchKernelGGL(filt_search_kernel<uint16_t>, dim3(unsigned(va.B)), dim3(kFT), 0, stream, a, info, desc,
                        slices);
   } else {
-    hipLaunchKernelGGL((filt_hist_kernel<float, true>), dim3(g1), dim3(kFT), 0, stream, a);
-    hipLaunchKernelGGL((filt_select_kernel<float, true>), dim3(g2), dim3(kFT), 0, stream, a);
+    hipLaunchKernelGGL((filt_hist_kernel<float, 0>), dim3(g1), dim3(kFT), 0, stream, a);
+    hipLaunchKernelGGL(filt_select0_kernel<float>, dim3(g2), dim3(kS0), 0, stream, a);
     for (int l = 0; l < levels; ++l) {
-      hipLaunchKernelGGL((filt_hist_kernel<float, false>), dim3(g1), dim3(kFT), 0, stream, a);
-      hipLaunchKernelGGL((filt_select_kernel<float, false>), dim3(g2), dim3(kFT), 0, stream, a);
+      hipLaunchKernelGGL((filt_hist_kernel<float, 1>), dim3(g1), dim3(kFT), 0, stream, a);
+      hipLaunchKernelGGL(filt_select_kernel<float>, dim3(g2), dim3(kFT), 0, stream, a);
     }
     hipLaunchKernelGGL(filt_verdict_kernel_impl, dim3(unsigned(va.B)), dim3(64), 0, stream, a, info, desc, false);
     hipLaunchKernelGGL(filt_weight_kernel<float>, dim3(gw), dim3(kFT), 0, stream, a, info, desc, slices);

@@ -99,7 +99,8 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // Filtered verification: after the verification layout, per (row slot,
 // 32 KiB segment, search) histograms of kFilterBins bins (fixed-point masses
 // and counts) and per (row slot, search) threshold-search states.
-constexpr int kFilterBins = 256;
+constexpr int kFilterBins = 256;    // key-digit bins
+constexpr int kFilterBins0 = 512;  // level-0 bins
 constexpr size_t kFilterSearchBytes = 48;
 constexpr size_t kFilterRowBytes = 16;   // per row slot: normaliser, threshold, argmax
 constexpr size_t kFilterDescBytes = 16;  // per request: accept length, draw kind, uniform
@@ -135,11 +136,11 @@ struct WsLayout {
 inline WsLayout ws_layout(int B, int V, int max_k, int dtype);
 inline FilterLayout filter_layout(int B, int V, int max_k, int dtype) {
   const WsLayout L = ws_layout(B, V, max_k, dtype);
-  const size_t slots = size_t(B) * L.R * L.nseg2 * 2 * kFilterBins;
+  const size_t segs = size_t(B) * L.R * L.nseg2;
   FilterLayout F;
   F.hmass = L.total;
-  F.hcount = F.hmass + align256(slots * 8);
-  F.search = F.hcount + align256(slots * 4);
+  F.hcount = F.hmass + align256(segs * 2 * kFilterBins * 8);
+  F.search = F.hcount + align256(segs * 2 * kFilterBins0 * 4);
   F.info = F.search + align256(size_t(B) * L.R * 2 * kFilterSearchBytes);
   F.desc = F.info + align256(size_t(B) * L.R * kFilterRowBytes);
   F.slices = F.desc + align256(size_t(B) * kFilterDescBytes);
