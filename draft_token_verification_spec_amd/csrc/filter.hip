@@ -293,22 +293,30 @@ __global__ __launch_bounds__(kFT) void filt_hist_kernel(FiltArgs a) {
   // past the end of the row the tail loads hold NaN: no interval holds it,
   // and level 0 skips it
   if (LV == 0) {
+    auto add0 = [&](float z) {
+      const float t = bin_t(z, c16, mc16);
+      const int bn = bin_of_t(t);
+      // r - 1 of the weight relative to the bin's lower edge, in 2^-21 units
+      // rounded half up: in [0, 92840] for bins below 511 (the last bin's
+      // sum is never read; there the conversion saturates at 0)
+      const float r = fast_exp2(fmaf(t - float(bn), -1.f / kBinsPerLog2, 1.f / kBinsPerLog2));
+      const uint32_t u = uint32_t(fmaf(r, kFrac0, 0.5f - kFrac0));
+      atomicAdd(reinterpret_cast<unsigned long long*>(&sh.bins[bn]), (static_cast<unsigned long long>(u) << 32) | 1ull);
+    };
+    if (full) {
 #pragma unroll
-    for (int k = 0; k < kFV; ++k)
+      for (int k = 0; k < kFV; ++k)
 #pragma unroll
-      for (int j = 0; j < N; ++j) {
-        const float z = Elem<ET>::get(v[k], j);
-        if (full || z == z) {
-          const float t = bin_t(z, c16, mc16);
-          const int bn = bin_of_t(t);
-          // r - 1 of the weight relative to the bin's lower edge, 2^-21 units
-          const float r = fast_exp2(fmaf(t - float(bn), -1.f / kBinsPerLog2, 1.f / kBinsPerLog2));
-          const uint32_t u =
-              bn < kBins0 - 1 ? uint32_t(fminf(fmaxf(__builtin_rintf(fmaf(r, kFrac0, -kFrac0)), 0.f), 131071.f)) : 0u;
-          atomicAdd(reinterpret_cast<unsigned long long*>(&sh.bins[bn]),
-                    (static_cast<unsigned long long>(u) << 32) | 1ull);
+        for (int j = 0; j < N; ++j) add0(Elem<ET>::get(v[k], j));
+    } else {
+#pragma unroll
+      for (int k = 0; k < kFV; ++k)
+#pragma unroll
+        for (int j = 0; j < N; ++j) {
+          const float z = Elem<ET>::get(v[k], j);
+          if (z == z) add0(z);
         }
-      }
+    }
   } else {
     // per element a test against each searching slot's value interval; the
     // common case of one search gets a loop of its own
