@@ -282,6 +282,8 @@ def main():
     kernel_ms = float(np.mean(phases[:, 0]))
     second_ms = float(np.mean(phases[:, 1]))
     call_ms = kernel_ms + second_ms
+    pct = lambda x: [float(np.percentile(x, q)) for q in (10, 50, 90)]
+    kernel_pct, call_pct = pct(phases[:, 0]), pct(phases[:, 0] + phases[:, 1])
     value = positions / (ms_per_step * 1e-3)
     achieved = bytes_per_launch / (kernel_ms * 1e-3) / 1e9
     call_gbs = bytes_per_launch / (call_ms * 1e-3) / 1e9
@@ -324,8 +326,32 @@ def main():
                   "sv_spec_verify_call": {"kernels": "stats_kernel + draw_kernel" if kernel != "resident"
                                           else "resident_kernel",
                                           "ms": call_ms, "draw_kernel_ms": second_ms,
-                                          "achieved_gbs": call_gbs, "frac": call_gbs / PEAK_HBM_GBS}},
+                                          "achieved_gbs": call_gbs, "frac": call_gbs / PEAK_HBM_GBS,
+                                          "ms_p10_p50_p90": call_pct},
+                  "stats_kernel_ms_p10_p50_p90": kernel_pct},
     }
+    # streaming-read probe over a buffer of the same size: the statistics
+    # kernel's access pattern with no arithmetic (the ceiling a read reaches)
+    log("timing the read probe")
+    pbuf = torch.ones(bytes_per_launch // 4, dtype=torch.int32, device=dev)
+    sink = sv.sv_read_probe(pbuf)
+    for _ in range(3):
+        sv.sv_read_probe(pbuf, sink=sink)
+    torch.cuda.synchronize(dev)
+    preps = 20
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(preps):
+        sv.sv_read_probe(pbuf, sink=sink)
+    e1.record()
+    torch.cuda.synchronize(dev)
+    probe_ms = e0.elapsed_time(e1) / preps
+    probe_gbs = bytes_per_launch / (probe_ms * 1e-3) / 1e9
+    res["extra"]["read_probe"] = {"bytes": bytes_per_launch, "ms": probe_ms, "achieved_gbs": probe_gbs,
+                                  "frac": probe_gbs / PEAK_HBM_GBS,
+                                  "stats_kernel_frac_of_probe": achieved / probe_gbs,
+                                  "note": "back-to-back calls between two events (launch gaps included)"}
+    del pbuf
     # the estimator's global draft budget over the same batch's scores (one
     # workgroup, latency-bound): the decision of how many drafts to verify
     log("timing the global draft budget")

@@ -38,6 +38,8 @@ __all__ = [
     "sv_set_verify_kernel",
     "sv_timing_enable",
     "sv_timing_read",
+    "sv_read_probe_sink_words",
+    "sv_read_probe",
     "SV_KERNEL_AUTO",
     "SV_KERNEL_STREAMING",
     "SV_KERNEL_RESIDENT",
@@ -88,6 +90,8 @@ _SIGNATURES = {
     "sv_set_verify_kernel": (_i, [_i]),
     "sv_timing_enable": (_i, [_i]),
     "sv_timing_read": (_i, [_p, _i]),
+    "sv_read_probe_sink_words": (_sz, [_sz]),
+    "sv_read_probe": (_i, [_p, _p, _sz, _p, _sz]),
 }
 
 
@@ -117,6 +121,25 @@ def sv_status_string(status: int) -> str:
 def _check(status: int, what: str):
     if status != 0:
         raise RuntimeError(f"{what}: {sv_status_string(status)} (status {status})")
+
+
+def sv_read_probe_sink_words(nbytes: int) -> int:
+    return int(_load().sv_read_probe_sink_words(nbytes))
+
+
+def sv_read_probe(data: torch.Tensor, *, sink: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Read ``data`` (contiguous device tensor, 16-byte aligned, size a
+    multiple of 16 bytes) with the statistics kernel's access pattern; see
+    ``sv_read_probe``.  Returns the sink (uint32 words as int32)."""
+    if not data.is_cuda or not data.is_contiguous():
+        raise ValueError("data must be a contiguous device tensor")
+    nbytes = data.numel() * data.element_size()
+    words = sv_read_probe_sink_words(nbytes)
+    if sink is None or sink.numel() < words:
+        sink = torch.empty(max(words, 1), dtype=torch.int32, device=data.device)
+    _check(_load().sv_read_probe(_stream(data.device), _ptr(data), nbytes, _ptr(sink), sink.numel()),
+           "sv_read_probe")
+    return sink
 
 
 def sv_workspace_size(B: int, V: int, max_k: int, dtype: int) -> int:

@@ -290,6 +290,19 @@ int sv_tts_grad(void* stream, int B, int V, int max_k, int dtype, const void* dr
                                    loss_parts, tickets, R, nseg2, static_cast<hipStream_t>(stream)));
 }
 
+size_t sv_read_probe_sink_words(size_t bytes) {
+  return (bytes / 16 * 16 + kProbeBytesPerBlock - 1) / kProbeBytesPerBlock * (kThreads / 64);
+}
+
+int sv_read_probe(void* stream, const void* data, size_t bytes, uint32_t* sink, size_t sink_words) {
+  if (bytes == 0) return SV_OK;
+  if (!data || !sink || bytes % 16 != 0 || (reinterpret_cast<uintptr_t>(data) & 15u) != 0)
+    return SV_ERR_INVALID_ARG;
+  if (bytes / kProbeBytesPerBlock >= (uint64_t(1) << 31)) return SV_ERR_UNSUPPORTED;
+  if (sink_words < sv_read_probe_sink_words(bytes)) return SV_ERR_INVALID_ARG;
+  return to_status(launch_read_probe(data, bytes, sink, static_cast<hipStream_t>(stream)));
+}
+
 int sv_set_verify_kernel(int kernel) {
   if (kernel != SV_KERNEL_AUTO && kernel != SV_KERNEL_STREAMING && kernel != SV_KERNEL_RESIDENT)
     return SV_ERR_INVALID_ARG;

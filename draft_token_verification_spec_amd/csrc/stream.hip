@@ -714,7 +714,37 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
       if (sh.row[i].s < kRecomputeBelow) confident_feature<ET>(a, sh, b, i, c, tid);
 }
 
+// Bandwidth probe: the statistics kernel's access pattern (one workgroup per
+// 32 KiB, kNV 16-byte non-temporal loads per thread issued together) with
+// no arithmetic but an XOR of what was read, one word per wave.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) void read_probe_kernel(
+    const uint4* data, size_t n16, uint32_t* sink) {
+  const int tid = threadIdx.x;
+  const size_t base = size_t(blockIdx.x) * kThreads * kNV;
+  uint4 v[kNV];
+#pragma unroll
+  for (int k = 0; k < kNV; ++k) {
+    const size_t i = base + size_t(k) * kThreads + tid;
+    v[k] = i < n16 ? load_stream16(data + i) : make_uint4(0u, 0u, 0u, 0u);
+  }
+  uint32_t x = 0;
+#pragma unroll
+  for (int k = 0; k < kNV; ++k) x ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x ^= __shfl_xor(x, o, 64);
+  if ((tid & 63) == 0) sink[size_t(blockIdx.x) * kWaves + (tid >> 6)] = x;
+}
+
 }  // namespace
+
+hipError_t launch_read_probe(const void* data, size_t bytes, uint32_t* sink, hipStream_t stream) {
+  const size_t n16 = bytes / 16;
+  const size_t blocks = (n16 + size_t(kThreads) * kNV - 1) / (size_t(kThreads) * kNV);
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(read_probe_kernel, dim3(unsigned(blocks)), dim3(kThreads), 0, stream,
+                     static_cast<const uint4*>(data), n16, sink);
+  return hipGetLastError();
+}
 
 hipError_t launch_stats(VerifyArgs a, int dtype, hipStream_t stream) {
   const uint64_t n1 = uint64_t(a.B) * uint64_t(a.R) * uint64_t(a.nseg2);

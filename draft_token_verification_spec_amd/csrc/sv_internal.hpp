@@ -227,6 +227,9 @@ hipError_t launch_streaming(VerifyArgs a, int dtype, hipStream_t stream, const h
 // The statistics kernel alone (segment statistics and logits at the draft
 // tokens into the workspace).
 hipError_t launch_stats(VerifyArgs a, int dtype, hipStream_t stream);
+// Read probe (measurement aid): one word per 64 threads into sink.
+constexpr size_t kProbeBytesPerBlock = kHalfBytes;  // 32 KiB per workgroup
+hipError_t launch_read_probe(const void* data, size_t bytes, uint32_t* sink, hipStream_t stream);
 
 // Filtered verification: the statistics kernel, the threshold searches and
 // the verdict / draw kernel.

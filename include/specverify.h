@@ -388,6 +388,19 @@ int sv_set_verify_kernel(int kernel);
 int sv_timing_enable(int slots);
 int sv_timing_read(float* ms, int max_calls);
 
+/* Read-bandwidth probe, a measurement aid (not a step of the method): reads
+ * `bytes` of device memory at `data` with the statistics kernel's access
+ * pattern (one 256-thread workgroup per 32 KiB, eight 16-byte non-temporal
+ * loads per thread issued together) and no arithmetic beyond an XOR of what
+ * it read, so that its rate is the ceiling a streaming read reaches.  Writes
+ * one word per 64 threads into `sink` (device, caller-owned):
+ * sv_read_probe_sink_words(bytes) words, word 4*g + w the XOR of the 16-byte
+ * vectors (as four 32-bit words) that wave w of workgroup g read.  `data`
+ * 16-byte aligned, `bytes` a multiple of 16 (else SV_ERR_INVALID_ARG, as for
+ * a short sink); asynchronous on `stream`. */
+size_t sv_read_probe_sink_words(size_t bytes);
+int sv_read_probe(void* stream, const void* data, size_t bytes, uint32_t* sink, size_t sink_words);
+
 /* Static description of a status code. */
 const char* sv_status_string(int status);
 

@@ -26,7 +26,8 @@ def test_every_declared_symbol_is_exported():
     assert set(names) == {"sv_workspace_size", "sv_spec_verify", "sv_av_score", "sv_av_fit_step",
                           "sv_status_string", "sv_set_verify_kernel", "sv_timing_enable", "sv_timing_read",
                           "sv_av_budget", "sv_av_calib_accumulate", "sv_av_calib_metrics", "sv_tts_grad",
-                          "sv_filtered_workspace_size", "sv_spec_verify_filtered"}
+                          "sv_filtered_workspace_size", "sv_spec_verify_filtered", "sv_read_probe_sink_words",
+                          "sv_read_probe"}
     lib = ctypes.CDLL(sv.lib_path())
     for n in names:
         assert hasattr(lib, n), n
@@ -274,3 +275,19 @@ def test_tts_grad_rejects_before_launch():
     assert call(prev=f, pstart=None) == -1 and call(prev=f, pstart=f, pstride=10) == -1
     assert call(B=0) == 0 and call(K=0) == 0
     assert call(ws=f, wsb=sv.sv_workspace_size(4, 64, 4, 1) - 1) == -3  # too small a verification workspace
+
+
+def test_read_probe_sizes_and_rejections():
+    assert sv.sv_read_probe_sink_words(0) == 0
+    assert sv.sv_read_probe_sink_words(16) == 4  # one workgroup, four waves
+    assert sv.sv_read_probe_sink_words(32768) == 4
+    assert sv.sv_read_probe_sink_words(32768 + 16) == 8
+    lib = sv._load()
+    ok = dict(stream=None, data=FAKE, nbytes=1 << 20, sink=FAKE, words=1 << 20)
+    call = lambda **kw: lib.sv_read_probe(*{**ok, **kw}.values())
+    assert call(nbytes=0) == 0
+    assert call(data=None) == -1
+    assert call(sink=None) == -1
+    assert call(nbytes=(1 << 20) + 8) == -1  # not a multiple of 16
+    assert call(data=ctypes.c_void_p(0x10008)) == -1  # not 16-byte aligned
+    assert call(words=sv.sv_read_probe_sink_words(1 << 20) - 1) == -1
