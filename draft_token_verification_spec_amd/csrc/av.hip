@@ -114,14 +114,18 @@ hipError_t launch_av_score(const ScoreArgs& a, int dtype, hipStream_t stream) {
 }
 
 // ---------------------------------------------------------------------------
-// refit step: one workgroup.  For each position, threads take requests
-// b = tid, tid + 256, ... and accumulate the six sums in fp64; a fixed-order
-// reduction (wave butterfly, then waves in order) makes the result
-// deterministic.  On the round's last step thread 0 solves the arrowhead
+// refit step: one workgroup of 256 threads.  Thread t takes requests
+// b = t, t + 256, ..., loading all of a request's labels and features at
+// once; per position the six sums are formed in fp64, reduced per wave
+// (butterfly) into LDS and then over the waves in order, a fixed order that
+// makes the result deterministic.  On the round's last step thread 0 solves the arrowhead
 // Newton system H * delta = -g by eliminating the intercepts (Schur
 // complement on the slope), damps, updates the parameters and clears the
 // accumulator.
 // ---------------------------------------------------------------------------
+
+constexpr int kFitT = 256;  // threads of the refit (1024 measured slower: binary64-bound)
+constexpr int kFitW = kFitT / 64;
 
 __device__ __forceinline__ double sigmoid_d(double t) {
   if (t >= 0.0) return 1.0 / (1.0 + exp(-t));
@@ -135,10 +139,10 @@ __device__ __forceinline__ double wave_sum_d(double v) {
   return v;
 }
 
-__global__ __launch_bounds__(kThreads) void av_fit_kernel(int B, int max_k, const float* feature,
-                                                          const int8_t* labels, float* params, double* accum,
-                                                          float damping_c, float ridge, int do_update) {
-  __shared__ double red[kWaves][SV_MAX_K][6];  // per wave and position, summed over the chunks in order
+__global__ __launch_bounds__(kFitT) void av_fit_kernel(int B, int max_k, const float* feature,
+                                                       const int8_t* labels, float* params, double* accum,
+                                                       float damping_c, float ridge, int do_update) {
+  __shared__ double red[kFitW][SV_MAX_K][6];  // per wave and position, summed over the chunks in order
   __shared__ double acc[SV_MAX_K][6];          // accumulator after this step
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   // parameters and the incoming accumulator with the first chunk's items:
@@ -148,9 +152,9 @@ __global__ __launch_bounds__(kThreads) void av_fit_kernel(int B, int max_k, cons
 #pragma unroll
   for (int i = 0; i < SV_MAX_K; ++i) beta[i] = i < max_k ? double(params[1 + i]) : 0.0;
   const double acc_in = tid < 6 * max_k ? accum[tid] : 0.0;
-  for (int e = tid; e < kWaves * SV_MAX_K * 6; e += kThreads) (&red[0][0][0])[e] = 0.0;
+  for (int e = tid; e < kFitW * SV_MAX_K * 6; e += kFitT) (&red[0][0][0])[e] = 0.0;
   __syncthreads();
-  for (int b0 = 0; b0 < B; b0 += kThreads) {
+  for (int b0 = 0; b0 < B; b0 += kFitT) {
     const int b = b0 + tid;
     int y[SV_MAX_K];
     float x[SV_MAX_K];
@@ -187,7 +191,7 @@ __global__ __launch_bounds__(kThreads) void av_fit_kernel(int B, int max_k, cons
   if (tid < 6 * max_k) {
     const int i = tid / 6, k = tid % 6;
     double t = red[0][i][k];
-    for (int w = 1; w < kWaves; ++w) t += red[w][i][k];
+    for (int w = 1; w < kFitW; ++w) t += red[w][i][k];
     t += acc_in;
     acc[i][k] = t;
     if (!do_update) accum[tid] = t;
@@ -223,12 +227,12 @@ __global__ __launch_bounds__(kThreads) void av_fit_kernel(int B, int max_k, cons
     }
   }
   __syncthreads();
-  for (int k = tid; k < 6 * max_k; k += kThreads) accum[k] = 0.0;
+  for (int k = tid; k < 6 * max_k; k += kFitT) accum[k] = 0.0;
 }
 
 hipError_t launch_av_fit(int B, int max_k, const float* feature, const int8_t* labels, float* params,
                          double* accum, float damping_c, float ridge, int do_update, hipStream_t stream) {
-  hipLaunchKernelGGL(av_fit_kernel, dim3(1), dim3(kThreads), 0, stream, B, max_k, feature, labels, params, accum,
+  hipLaunchKernelGGL(av_fit_kernel, dim3(1), dim3(kFitT), 0, stream, B, max_k, feature, labels, params, accum,
                      damping_c, ridge, do_update);
   return hipGetLastError();
 }
