@@ -13,16 +13,17 @@
 // A row's kept set is {v : key(z_v) >= t} for a threshold key t (key = the
 // order-preserving integer image of the logit), found by an exact radix
 // select with deterministic histograms:
-//   level 0  bins of 1/8 unit of log2 probability below the row maximum
-//            (255 bins, the last one collecting everything further down);
-//   level L  8-bit digits of the key within the interval the previous level
-//            left, until one key remains (bf16 keys: 2 levels, fp32: 4).
-// Each level is a streaming pass (one workgroup per 32 KiB row segment:
-// integer counts and masses in 2^-40 fixed point of exp2((z - max) * c), added
-// with LDS integer atomics, so the sums do not depend on the order) and a
-// selection (one workgroup per row: segment histograms merged in order,
-// exclusive scans, the boundary bin).  The verdict, the residual / bonus
-// weights and the draw then run on the filtered rows.
+//   level 0  bins of 1/16 unit of log2 probability below the row maximum
+//            (511 bins, the last one collecting everything further down),
+//            each with its count and its mass exactly to 2^-22 relative;
+//   level L  8-bit digits of the key within the boundary bin's keys, until
+//            one key remains (bf16 keys: 2 levels at most, fp32: 4).
+// Each level is a streaming pass (one workgroup per 32 KiB row segment;
+// every sum an integer added with LDS atomics, so the result does not depend
+// on the order of the additions) and a selection (one workgroup per row:
+// segment histograms merged in order, exclusive scans, the boundary bin or
+// digit).  The verdict, the residual / bonus weights and the draw then run
+// on the filtered rows.
 #include "sv_device.hpp"
 
 namespace sv {
@@ -603,8 +604,8 @@ static_assert(sizeof(DrawDesc) == kFilterDescBytes, "draw descriptor layout");
 static_assert(kFV == kDrawSlices, "slices per draw segment");
 constexpr int kMaxSlices = int(int64_t(SV_MAX_V) * 4 / (kFT * 16));  // 4 KiB slices of the longest row
 
-__global__ __launch_bounds__(64) void filt_verdict_kernel_impl(FiltArgs a, RowInfo* info, DrawDesc* desc,
-                                                                bool bf16) {
+template <typename ET>
+__global__ __launch_bounds__(64) void filt_verdict_kernel(FiltArgs a, RowInfo* info, DrawDesc* desc) {
   __shared__ RowInfo row[2 * SV_MAX_K + 1];
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
@@ -664,8 +665,7 @@ __global__ __launch_bounds__(64) void filt_verdict_kernel_impl(FiltArgs a, RowIn
         const float zd = a.zval[size_t(b) * R + i], zt = a.zval[size_t(b) * R + max_k + i];
         const RowInfo& id = row[i];
         const RowInfo& it = row[max_k + i];
-        const uint32_t kd = bf16 ? Key<uint16_t>::of(zd) : Key<float>::of(zd);
-        const uint32_t kt = bf16 ? Key<uint16_t>::of(zt) : Key<float>::of(zt);
+        const uint32_t kd = Key<ET>::of(zd), kt = Key<ET>::of(zt);
         const float ld = kd >= id.t ? fmaf(zd, c, -id.kk) : -INFINITY;
         const float lt = kt >= it.t ? fmaf(zt, c, -it.kk) : -INFINITY;
         pd = fast_exp2(ld);
@@ -913,7 +913,7 @@ hipError_t launch_filtered(VerifyArgs va, const FilterIO& io, int dtype, hipStre
       hipLaunchKernelGGL((filt_hist_kernel<uint16_t, 1>), dim3(g1), dim3(kFT), 0, stream, a);
       hipLaunchKernelGGL(filt_select_kernel<uint16_t>, dim3(g2), dim3(kFT), 0, stream, a);
     }
-    hipLaunchKernelGGL(filt_verdict_kernel_impl, dim3(unsigned(va.B)), dim3(64), 0, stream, a, info, desc, true);
+    hipLaunchKernelGGL(filt_verdict_kernel<uint16_t>, dim3(unsigned(va.B)), dim3(64), 0, stream, a, info, desc);
     hipLaunchKernelGGL(filt_weight_kernel<uint16_t>, dim3(gw), dim3(kFT), 0, stream, a, info, desc, slices);
     hipLaunchKernelGGL(filt_search_kernel<uint16_t>, dim3(unsigned(va.B)), dim3(kFT), 0, stream, a, info, desc,
                        slices);
@@ -924,7 +924,7 @@ hipError_t launch_filtered(VerifyArgs va, const FilterIO& io, int dtype, hipStre
       hipLaunchKernelGGL((filt_hist_kernel<float, 1>), dim3(g1), dim3(kFT), 0, stream, a);
       hipLaunchKernelGGL(filt_select_kernel<float>, dim3(g2), dim3(kFT), 0, stream, a);
     }
-    hipLaunchKernelGGL(filt_verdict_kernel_impl, dim3(unsigned(va.B)), dim3(64), 0, stream, a, info, desc, false);
+    hipLaunchKernelGGL(filt_verdict_kernel<float>, dim3(unsigned(va.B)), dim3(64), 0, stream, a, info, desc);
     hipLaunchKernelGGL(filt_weight_kernel<float>, dim3(gw), dim3(kFT), 0, stream, a, info, desc, slices);
     hipLaunchKernelGGL(filt_search_kernel<float>, dim3(unsigned(va.B)), dim3(kFT), 0, stream, a, info, desc,
                        slices);
