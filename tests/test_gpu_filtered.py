@@ -264,3 +264,30 @@ def test_deterministic_and_workspace_reuse():
     for k in g1:
         np.testing.assert_array_equal(g1[k], g2[k], err_msg=k)
     assert compare_filtered(small, gs, oracle_filtered(small)) <= 1
+
+
+def test_max_k_zero_draws_bonus_from_filtered_target_rows():
+    """No drafts: every request draws its bonus token from target row 0,
+    filtered; the kept counts cover that one row."""
+    g = np.random.default_rng(31)
+    B, V = 12, 3000
+    zt = g.normal(0, 2.0, (B, 1, V)).astype(np.float32)
+    zd = np.zeros((B, 0, V), np.float32)
+    b = _batch(zd, zt, np.zeros((B, 0), np.int32), 1.0, 0, 0.8)
+    b = dataclasses.replace(b, top_k=np.array([0, 5, 0, 40] * 3, np.int32),
+                            top_p=np.array([0.8, 1.0, 0.5, 0.9] * 3, np.float32))
+    _log("case filtered max_k=0")
+    gout, o = _run(b)
+    assert compare_filtered(b, gout, o) == 0
+    assert gout["out_tokens"].shape == (B, 1) and np.all(gout["accept_len"] == 0)
+    assert np.all(gout["kept"][:, 0] >= 1)
+
+
+def test_greedy_batch_with_filters_is_unfiltered():
+    b = gen.make_batch("fp32_b32_k4_v1024_filter_mix")
+    b = dataclasses.replace(b, temperature=np.zeros(b.B, np.float32))
+    _log("case filtered all greedy")
+    gout, o = _run(b)
+    assert compare_filtered(b, gout, o) == 0
+    assert np.all(gout["kept"] == -1)
+    assert np.all(np.isnan(gout["p_draft"]))
