@@ -43,7 +43,6 @@ namespace {
 
 constexpr int kNV = 8;     // 16-byte vectors per thread: 32 KiB per workgroup
 constexpr int kSleep = 2;  // s_sleep argument while polling a slot
-constexpr int kRowsPerPass = 3;  // rows each wave merges per pass over the segment statistics
 
 // Hand a 32-bit value off in slot p.
 __device__ __forceinline__ void put_slot(uint64_t* p, uint32_t bits) {
@@ -172,17 +171,32 @@ __device__ __forceinline__ void merge_partial(Partial& p, const Partial& q, floa
     merge_ms(p.m, p.s, p.cnt, q.m, q.s, q.cnt, c);
 }
 
+// Wave reduction of per-lane (max, sum of exp2((z - max) * c)) pairs: the
+// wave maximum first, then each lane's sum rescaled to it (one exp2 per
+// lane) and added up.  The result in every lane.
+__device__ __forceinline__ void wave_ms(float& m, float& s, float c) {
+  float M = m;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+  s = wave_sum(m > -INFINITY ? s * fast_exp2((m - M) * c) : 0.f);
+  m = M;
+}
+
 // Workgroup reduction of a per-thread Partial; the result in thread 0.
 template <int MODE>
 __device__ __forceinline__ Partial block_reduce(Partial p, float c, Partial* lds, int tid) {
+  if (MODE == kSumInclusive) {
+    wave_ms(p.m, p.s, c);
+  } else {
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    Partial q;
-    q.m = __shfl_xor(p.m, o, 64);
-    q.s = __shfl_xor(p.s, o, 64);
-    q.cnt = __shfl_xor(p.cnt, o, 64);
-    q.idx = __shfl_xor(p.idx, o, 64);
-    merge_partial<MODE>(p, q, c);
+    for (int o = 32; o >= 1; o >>= 1) {
+      Partial q;
+      q.m = __shfl_xor(p.m, o, 64);
+      q.s = __shfl_xor(p.s, o, 64);
+      q.cnt = __shfl_xor(p.cnt, o, 64);
+      q.idx = __shfl_xor(p.idx, o, 64);
+      merge_partial<MODE>(p, q, c);
+    }
   }
   if ((tid & 63) == 0) lds[tid >> 6] = p;
   __syncthreads();
@@ -503,59 +517,46 @@ __device__ __forceinline__ void search_request(const VerifyArgs& a, DrawShared& 
 // Merge the segment statistics of the request's rows into sh.row, by row
 // slot (draft i at i, target j at max_k + j; slots of rows the statistics
 // kernel skipped hold stale values that nothing reads).  The loads do not
-// wait for the request's scalars.  Wave w takes slots w, w + kWaves, ...
-// (kRowsPerPass of them per pass, their loads in flight together); lane l
-// takes segments l, l + 64, ... in order, and a butterfly combines the lanes.
-// Every workgroup of the request evaluates the same function of the same
-// data, so all reach the same statistics.
+// wait for the request's scalars.  A row takes G lanes (G the smallest power
+// of two >= the segments per row, at most 64), so a wave merges 64 / G rows
+// at a time: lane j of a row's group merges segments j, j + G, ... in order,
+// then a butterfly over the group combines the lanes.  Every workgroup of
+// the request evaluates the same function of the same data, so all reach
+// the same statistics.
 __device__ __forceinline__ void merge_rows(const VerifyArgs& a, DrawShared& sh, int b, bool greedy, float c,
                                            int tid) {
   const int wave = tid >> 6, lane = tid & 63;
   const int n = a.nseg2, max_k = a.max_k, R = a.R;
+  int G = 1;
+  while (G < n && G < 64) G <<= 1;
+  const int RW = 64 / G;  // rows per wave and pass
+  const int g = lane / G, j = lane & (G - 1);
   const Partial* base = a.partials + size_t(b) * R * n;
-  const Partial none{-INFINITY, 0.f, 0.f, 0x7fffffff};
-  for (int q0 = wave; q0 < R; q0 += kWaves * kRowsPerPass) {
-    Partial acc[kRowsPerPass];
-    float z[kRowsPerPass];
-#pragma unroll
-    for (int r = 0; r < kRowsPerPass; ++r) {
-      const int q = q0 + r * kWaves;
-      acc[r] = none;
-      z[r] = (q < R && lane == 0) ? a.zval[size_t(b) * R + q] : NAN;
-    }
-    for (int s0 = 0; s0 < n; s0 += 64) {
-      Partial p[kRowsPerPass];
-#pragma unroll
-      for (int r = 0; r < kRowsPerPass; ++r) {
-        const int q = q0 + r * kWaves;
-        p[r] = (q < R && s0 + lane < n) ? base[size_t(q) * n + s0 + lane] : none;
-      }
-#pragma unroll
-      for (int r = 0; r < kRowsPerPass; ++r) {
-        if (greedy && q0 + r * kWaves >= max_k)
-          merge_argmax(acc[r].m, acc[r].idx, p[r].m, p[r].idx);
-        else
-          merge_ms(acc[r].m, acc[r].s, acc[r].cnt, p[r].m, p[r].s, p[r].cnt, c);
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < kRowsPerPass; ++r) {
-      const int q = q0 + r * kWaves;
-      const bool amax = greedy && q >= max_k;
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) {
-        Partial x;
-        x.m = __shfl_xor(acc[r].m, o, 64);
-        x.s = __shfl_xor(acc[r].s, o, 64);
-        x.cnt = __shfl_xor(acc[r].cnt, o, 64);
-        x.idx = __shfl_xor(acc[r].idx, o, 64);
+  for (int q0 = wave * RW; q0 < R; q0 += kWaves * RW) {
+    const int q = q0 + g;
+    const bool amax = greedy && q >= max_k;
+    const float z = (q < R && j == 0) ? a.zval[size_t(b) * R + q] : NAN;
+    Partial acc{-INFINITY, 0.f, 0.f, 0x7fffffff};
+    if (q < R)
+      for (int x = j; x < n; x += G) {
+        const Partial p = base[size_t(q) * n + x];
         if (amax)
-          merge_argmax(acc[r].m, acc[r].idx, x.m, x.idx);
+          merge_argmax(acc.m, acc.idx, p.m, p.idx);
         else
-          merge_ms(acc[r].m, acc[r].s, acc[r].cnt, x.m, x.s, x.cnt, c);
+          merge_ms(acc.m, acc.s, acc.cnt, p.m, p.s, p.cnt, c);
       }
-      if (lane == 0 && q < R) sh.row[q] = RowStat{acc[r].m, acc[r].s + acc[r].cnt, acc[r].idx, z[r]};
+    for (int o = G >> 1; o >= 1; o >>= 1) {
+      Partial y;
+      y.m = __shfl_xor(acc.m, o, 64);
+      y.s = __shfl_xor(acc.s, o, 64);
+      y.cnt = __shfl_xor(acc.cnt, o, 64);
+      y.idx = __shfl_xor(acc.idx, o, 64);
+      if (amax)
+        merge_argmax(acc.m, acc.idx, y.m, y.idx);
+      else
+        merge_ms(acc.m, acc.s, acc.cnt, y.m, y.s, y.cnt, c);
     }
+    if (j == 0 && q < R) sh.row[q] = RowStat{acc.m, acc.s + acc.cnt, acc.idx, z};
   }
   __syncthreads();
 }
@@ -607,19 +608,18 @@ __device__ __forceinline__ void confident_feature(const VerifyArgs& a, DrawShare
   __syncthreads();
 }
 
-// Workgroups 0 .. B*n-1: segment s of the draw rows of request b (weights);
-// then one search workgroup per request.  Requests in reverse order (the last
-// ones read by the statistics kernel are the likeliest to be cached); every
-// workgroup derives its request's verdict first.
+// Workgroup = segment s of the draw rows of request b (weights); the
+// request's last segment then collects all the weights and searches.
+// Requests in reverse order (the last ones read by the statistics kernel are
+// the likeliest to be cached); every workgroup derives its request's verdict
+// first.
 template <typename ET>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) void draw_kernel(VerifyArgs a) {
   __shared__ DrawShared sh;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n = a.nseg2, max_k = a.max_k;
-  const uint32_t nw = uint32_t(a.B) * uint32_t(n);
-  const bool search = blockIdx.x >= nw;
-  const int s = search ? -1 : int(blockIdx.x % uint32_t(n));
-  const int b = a.B - 1 - int(search ? blockIdx.x - nw : blockIdx.x / uint32_t(n));
+  const int s = int(blockIdx.x % uint32_t(n));
+  const int b = a.B - 1 - int(blockIdx.x / uint32_t(n));
   // every scalar of the request in one round trip, with the merge's loads
   const int kraw = a.num_draft[b];
   const float T = a.temperature[b];
@@ -631,10 +631,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
   const bool want_feat = a.av_feature != nullptr;
   const int nd = (!greedy || want_feat) ? K : 0;  // draft rows read
   const float c = uniform(kLog2e / (greedy ? 1.f : T));
-  // lane i of wave 0 tests position i: its token and uniform, in flight with the merge
+  // lane i of wave 0 tests position i: its token and uniform, in flight with
+  // the merge (loaded for every i < max_k, so that the loads need not wait
+  // for K)
   int dl = -1;
   float ul = 0.f;
-  if (wave == 0 && lane < K) {
+  if (wave == 0 && lane < max_k) {
     dl = a.tokens[size_t(b) * max_k + lane];
     ul = a.u_accept[size_t(b) * max_k + lane];
   }
@@ -672,15 +674,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
   const float kt = tr.m * c + fast_log2(tr.s);
   const float kd = dr.m * c + fast_log2(dr.s);
 
-  if (search) {
-    if (greedy) return;
-    if (resid)
-      search_request<ET, true>(a, sh, b, aa, c, kt, kd, u, rt, rd, tid);
-    else
-      search_request<ET, false>(a, sh, b, aa, c, kt, kd, u, rt, rd, tid);
-    return;
-  }
-
   // the request's outputs, by its first workgroup (the token at a of a
   // stochastic request comes from the search)
   if (s == 0 && wave == 0) {
@@ -703,10 +696,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
     }
   }
   if (!greedy) {
-    if (resid)
+    // the last segment waits only for workgroups dispatched before it
+    if (resid) {
       weight_segment<ET, true>(a, sh, b, s, c, kt, kd, rt, rd, tid);
-    else
+      if (s == n - 1) search_request<ET, true>(a, sh, b, aa, c, kt, kd, u, rt, rd, tid);
+    } else {
       weight_segment<ET, false>(a, sh, b, s, c, kt, kd, rt, rd, tid);
+      if (s == n - 1) search_request<ET, false>(a, sh, b, aa, c, kt, kd, u, rt, rd, tid);
+    }
   }
   // features of confident draft rows: position i by the workgroup of segment i mod n
   if (want_feat)
@@ -759,7 +756,7 @@ hipError_t launch_stats(VerifyArgs a, int dtype, hipStream_t stream) {
 
 hipError_t launch_streaming(VerifyArgs a, int dtype, hipStream_t stream, const hipEvent_t* ev) {
   const uint64_t n1 = uint64_t(a.B) * uint64_t(a.R) * uint64_t(a.nseg2);
-  const uint64_t n2 = uint64_t(a.B) * uint64_t(a.nseg2 + 1);  // weight workgroups, then one search per request
+  const uint64_t n2 = uint64_t(a.B) * uint64_t(a.nseg2);  // one workgroup per segment of the draw rows
   if (n1 == 0) {
     if (ev)
       for (int k = 0; k < 3; ++k) (void)hipEventRecord(ev[k], stream);
