@@ -298,25 +298,35 @@ __global__ __launch_bounds__(kTT) void tts_seg_kernel(TtsArgs a) {
   }
   const ET* rd = static_cast<const ET*>(a.draft) + (a.draft_start[b] + k) * a.draft_stride;
   const ET* rt = static_cast<const ET*>(a.target) + (a.target_start[b] + k) * a.target_stride;
-  const bool ald = is_aligned16(rd), alt = is_aligned16(rt);
+  // aligned rows of a whole number of vectors: every vector is wholly inside
+  // the row or wholly past its end
+  const bool vec_rows = is_aligned16(rd) && is_aligned16(rt) && a.V % N == 0;
   uint4 vd[HALF], vt[HALF];
+  // Vectors of a half at hb.  Past the end of the row every lane still loads
+  // (the row's last vector standing in) and only then are those vectors set
+  // to -inf, so that the loads are issued back to back.
   auto load_half = [&](int hb) {
-    if (ald && alt && hb + HE <= a.V) {
+    if (hb + HE <= a.V) {
 #pragma unroll
       for (int q = 0; q < HALF; ++q) {
         vd[q] = load_stream16(rd + hb + (q * kTT + tid) * N);
         vt[q] = load_stream16(rt + hb + (q * kTT + tid) * N);
       }
     } else {
+      constexpr uint32_t ninf = N == 8 ? (Elem<ET>::kNegInf << 16 | Elem<ET>::kNegInf) : Elem<ET>::kNegInf;
 #pragma unroll
       for (int q = 0; q < HALF; ++q) {
-        vd[q] = load_raw<ET>(rd, hb + (q * kTT + tid) * N, a.V, ald);
-        vt[q] = load_raw<ET>(rt, hb + (q * kTT + tid) * N, a.V, alt);
+        const int e = hb + (q * kTT + tid) * N;
+        vd[q] = load_stream16(rd + min(e, a.V - N));
+        vt[q] = load_stream16(rt + min(e, a.V - N));
       }
+#pragma unroll
+      for (int q = 0; q < HALF; ++q)
+        if (hb + (q * kTT + tid) * N >= a.V) vd[q] = vt[q] = make_uint4(ninf, ninf, ninf, ninf);
     }
   };
   // the first half's rows are in flight while the normalisers are merged
-  load_half(s * E);
+  if (vec_rows) load_half(s * E);
   const float T0 = a.temperature[b];
   const float T = T0 > 0.f ? T0 : 1.f;
   const float c = kLog2e / T, invT = 1.f / T;
@@ -327,22 +337,37 @@ __global__ __launch_bounds__(kTT) void tts_seg_kernel(TtsArgs a) {
   ET* g = static_cast<ET*>(a.grad) + o * size_t(a.V);
   const bool vec = is_aligned16(g);
   float loss = 0.f;
+  auto grad_vec = [&](const uint4& zd, const uint4& zt, int first) {
+    float gv[N];
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      const float lq = fmaf(Elem<ET>::get(zd, j), c, -kd);
+      const float lp = fmaf(Elem<ET>::get(zt, j), c, -kt);
+      const float qv = fast_exp2(lq), pv = fast_exp2(lp);
+      gv[j] = w * (qv - pv) * invT;
+      loss += pv > 0.f ? pv * (lp - lq) : 0.f;
+    }
+    // the loss terms are added here: left to the scheduler, they sink past
+    // the store's branches and hold every element's terms live (160 VGPRs)
+    asm volatile("" : "+v"(loss));
+    store_grad<ET>(g, first, a.V, gv, vec);
+  };
+  if (vec_rows) {
 #pragma unroll 1
-  for (int h = 0; h < 2; ++h) {
-    const int hb = s * E + h * HE;
-    if (h) load_half(hb);
+    for (int h = 0; h < 2; ++h) {
+      const int hb = s * E + h * HE;
+      if (h) load_half(hb);
 #pragma unroll
-    for (int q = 0; q < HALF; ++q) {
-      float gv[N];
-#pragma unroll
-      for (int j = 0; j < N; ++j) {
-        const float lq = fmaf(Elem<ET>::get(vd[q], j), c, -kd);
-        const float lp = fmaf(Elem<ET>::get(vt[q], j), c, -kt);
-        const float qv = fast_exp2(lq), pv = fast_exp2(lp);
-        gv[j] = w * (qv - pv) * invT;
-        loss += pv > 0.f ? pv * (lp - lq) : 0.f;
-      }
-      store_grad<ET>(g, hb + (q * kTT + tid) * N, a.V, gv, vec);
+      for (int q = 0; q < HALF; ++q) grad_vec(vd[q], vt[q], hb + (q * kTT + tid) * N);
+    }
+  } else {
+    // rows that are not 16-byte aligned, or of a length that is no whole
+    // number of vectors: element loads, one vector at a time
+    const bool ald = is_aligned16(rd), alt = is_aligned16(rt);
+#pragma unroll 1
+    for (int q = 0; q < 2 * HALF; ++q) {
+      const int first = s * E + (q * kTT + tid) * N;
+      grad_vec(load_raw<ET>(rd, first, a.V, ald), load_raw<ET>(rt, first, a.V, alt), first);
     }
   }
   loss = block_total(loss, red, tid);
