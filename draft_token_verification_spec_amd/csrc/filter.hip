@@ -709,6 +709,47 @@ __device__ __forceinline__ void pair_w(float zt, float zd, const RowInfo& it, co
   }
 }
 
+// Slice sums of one segment of the draw rows into red (residual and target
+// weights), read in two halves of kFV / 2 vectors so that a workgroup holds
+// 16 KiB of each row at a time.  Elements past the end of the row load as
+// -inf and weigh 0.
+template <typename ET, bool RESID>
+__device__ __forceinline__ void weight_slices(const ET* rt, const ET* rd, int hb, int V, bool full, bool al,
+                                              const RowInfo& it, const RowInfo& id, float c,
+                                              float (*red)[kFV][kFT / 64], int tid) {
+  constexpr int N = Elem<ET>::N;
+  constexpr int H = kFV / 2;
+  const int lane = tid & 63, wv = tid >> 6;
+#pragma unroll 1
+  for (int h = 0; h < 2; ++h) {
+    uint4 vt[H], vd[H];
+#pragma unroll
+    for (int k = 0; k < H; ++k) {
+      const int e0 = hb + ((h * H + k) * kFT + tid) * N;
+      vt[k] = full ? load_stream16(rt + e0) : load_raw<ET>(rt, e0, V, al);
+      if (RESID) vd[k] = full ? load_stream16(rd + e0) : load_raw<ET>(rd, e0, V, al);
+    }
+#pragma unroll
+    for (int k = 0; k < H; ++k) {
+      float sr = 0.f, st = 0.f;
+#pragma unroll
+      for (int j = 0; j < N; ++j) {
+        float wr, wt;
+        const float zt = Elem<ET>::get(vt[k], j);
+        pair_w<ET>(zt, RESID ? Elem<ET>::get(vd[k], j) : zt, it, id, c, RESID, &wr, &wt);
+        sr += wr;
+        st += wt;
+      }
+      sr = wave_sum(sr);
+      st = wave_sum(st);
+      if (lane == 0) {
+        red[0][h * H + k][wv] = sr;
+        red[1][h * H + k][wv] = st;
+      }
+    }
+  }
+}
+
 // Draw weights: workgroup (b, s) sums its 32 KiB segment of the draw rows per
 // slice (slice k = vector k of every thread: 4 KiB of contiguous tokens).
 template <typename ET>
@@ -716,7 +757,7 @@ __global__ __launch_bounds__(kFT) void filt_weight_kernel(FiltArgs a, const RowI
                                                           float* slices) {
   __shared__ float red[2][kFV][kFT / 64];
   constexpr int N = Elem<ET>::N;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x;
   const int n = a.nseg2;
   const int b = int(blockIdx.x / uint32_t(n)), s = int(blockIdx.x % uint32_t(n));
   // the request's scalars in one round trip, then the rows
@@ -732,34 +773,12 @@ __global__ __launch_bounds__(kFT) void filt_weight_kernel(FiltArgs a, const RowI
   const int hb = s * kFT * kFV * N;
   const bool full = al && hb + kFT * kFV * N <= a.V;
   const float c = kLog2e / T;
-  uint4 vt[kFV], vd[kFV];
-#pragma unroll
-  for (int k = 0; k < kFV; ++k) {
-    const int e0 = hb + (k * kFT + tid) * N;
-    vt[k] = full ? load_stream16(rt + e0) : load_raw<ET>(rt, e0, a.V, al);
-    vd[k] = !resid ? vt[k] : full ? load_stream16(rd + e0) : load_raw<ET>(rd, e0, a.V, al);
-  }
   const RowInfo it = info[size_t(b) * R + max_k + dd.acc];
   const RowInfo id = resid ? info[size_t(b) * R + dd.acc] : it;
-#pragma unroll
-  for (int k = 0; k < kFV; ++k) {
-    const int e0 = hb + (k * kFT + tid) * N;
-    float sr = 0.f, st = 0.f;
-#pragma unroll
-    for (int j = 0; j < N; ++j) {
-      float wr, wt;
-      pair_w<ET>(Elem<ET>::get(vt[k], j), Elem<ET>::get(vd[k], j), it, id, c, resid, &wr, &wt);
-      const bool in = e0 + j < a.V;
-      sr += in ? wr : 0.f;
-      st += in ? wt : 0.f;
-    }
-    sr = wave_sum(sr);
-    st = wave_sum(st);
-    if (lane == 0) {
-      red[0][k][wv] = sr;
-      red[1][k][wv] = st;
-    }
-  }
+  if (resid)
+    weight_slices<ET, true>(rt, rd, hb, a.V, full, al, it, id, c, red, tid);
+  else
+    weight_slices<ET, false>(rt, rd, hb, a.V, full, al, it, id, c, red, tid);
   __syncthreads();
   if (tid < 2 * kFV) {
     const int q = tid / kFV, k = tid % kFV;
