@@ -194,7 +194,7 @@ def _pool_worker(job):
     t0 = time.perf_counter()
     n = pos = 0
     feats, labs = [], []
-    r = w
+    r = w % batch.B
     while time.perf_counter() - t0 < budget_s or n < 2:
         k = int(batch.num_draft[r])
         ds, ts = int(batch.draft_row_start[r]), int(batch.target_row_start[r])
