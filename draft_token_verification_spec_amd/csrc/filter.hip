@@ -695,14 +695,27 @@ __global__ __launch_bounds__(64) void filt_verdict_kernel(FiltArgs a, RowInfo* i
   desc[b] = dd;
 }
 
-// Weight of one element pair: (pt' - pd')+ (residual) or pt'.
+// A row's kept set {key(z) >= t} as a value test z >= value(t): the key
+// order is the value order (-0 and +0 one value), so the two agree on every
+// non-NaN logit, and the compare is one instruction.
+struct KeptRow {
+  float zt;  // value(t)
+  float kk;  // log2 of the normaliser
+};
 template <typename ET>
-__device__ __forceinline__ void pair_w(float zt, float zd, const RowInfo& it, const RowInfo& id, float c, bool resid,
+__device__ __forceinline__ KeptRow kept_row(const RowInfo& r) {
+  // keys up to kMin (-inf; below it only NaN patterns, 0 for an unfiltered
+  // row) keep every logit
+  return KeptRow{r.t <= Key<ET>::kMin ? -INFINITY : Key<ET>::value(r.t), r.kk};
+}
+
+// Weight of one element pair: (pt' - pd')+ (residual) or pt'.
+__device__ __forceinline__ void pair_w(float zt, float zd, const KeptRow& it, const KeptRow& id, float c, bool resid,
                                        float* wr, float* wt) {
-  const float x = Key<ET>::of(zt) >= it.t ? fast_exp2(fmaf(zt, c, -it.kk)) : 0.f;
+  const float x = zt >= it.zt ? fast_exp2(fmaf(zt, c, -it.kk)) : 0.f;
   *wt = x;
   if (resid) {
-    const float y = Key<ET>::of(zd) >= id.t ? fast_exp2(fmaf(zd, c, -id.kk)) : 0.f;
+    const float y = zd >= id.zt ? fast_exp2(fmaf(zd, c, -id.kk)) : 0.f;
     *wr = fmaxf(x - y, 0.f);
   } else {
     *wr = x;
@@ -715,7 +728,7 @@ __device__ __forceinline__ void pair_w(float zt, float zd, const RowInfo& it, co
 // -inf and weigh 0.
 template <typename ET, bool RESID>
 __device__ __forceinline__ void weight_slices(const ET* rt, const ET* rd, int hb, int V, bool full, bool al,
-                                              const RowInfo& it, const RowInfo& id, float c,
+                                              const KeptRow& it, const KeptRow& id, float c,
                                               float (*red)[kFV][kFT / 64], int tid) {
   constexpr int N = Elem<ET>::N;
   constexpr int H = kFV / 2;
@@ -736,7 +749,7 @@ __device__ __forceinline__ void weight_slices(const ET* rt, const ET* rd, int hb
       for (int j = 0; j < N; ++j) {
         float wr, wt;
         const float zt = Elem<ET>::get(vt[k], j);
-        pair_w<ET>(zt, RESID ? Elem<ET>::get(vd[k], j) : zt, it, id, c, RESID, &wr, &wt);
+        pair_w(zt, RESID ? Elem<ET>::get(vd[k], j) : zt, it, id, c, RESID, &wr, &wt);
         sr += wr;
         st += wt;
       }
@@ -773,8 +786,8 @@ __global__ __launch_bounds__(kFT) void filt_weight_kernel(FiltArgs a, const RowI
   const int hb = s * kFT * kFV * N;
   const bool full = al && hb + kFT * kFV * N <= a.V;
   const float c = kLog2e / T;
-  const RowInfo it = info[size_t(b) * R + max_k + dd.acc];
-  const RowInfo id = resid ? info[size_t(b) * R + dd.acc] : it;
+  const KeptRow it = kept_row<ET>(info[size_t(b) * R + max_k + dd.acc]);
+  const KeptRow id = resid ? kept_row<ET>(info[size_t(b) * R + dd.acc]) : it;
   if (resid)
     weight_slices<ET, true>(rt, rd, hb, a.V, full, al, it, id, c, red, tid);
   else
@@ -866,6 +879,7 @@ __global__ __launch_bounds__(kFT) void filt_search_kernel(FiltArgs a, const RowI
   const int R = a.R, max_k = a.max_k;
   const RowInfo it = info[size_t(b) * R + max_k + dd.acc];
   const RowInfo id = resid ? info[size_t(b) * R + dd.acc] : it;
+  const KeptRow kit = kept_row<ET>(it), kid = kept_row<ET>(id);
   const ET* rt = row_ptr<ET>(a, b, max_k + dd.acc);
   const ET* rd = resid ? row_ptr<ET>(a, b, dd.acc) : rt;
   const bool al = is_aligned16(rt) && is_aligned16(rd);
@@ -879,7 +893,7 @@ __global__ __launch_bounds__(kFT) void filt_search_kernel(FiltArgs a, const RowI
 #pragma unroll
   for (int j = 0; j < N; ++j) {
     float wr, wt;
-    pair_w<ET>(Elem<ET>::get(vt, j), Elem<ET>::get(vd, j), it, id, c, resid, &wr, &wt);
+    pair_w(Elem<ET>::get(vt, j), Elem<ET>::get(vd, j), kit, kid, c, resid, &wr, &wt);
     w[j] = first + j < a.V ? wr : 0.f;
     own += w[j];
   }
