@@ -28,7 +28,14 @@ Readings (parity unpinned where marked):
 * H and g are evaluated at the round's fixed parameters; positions with no
   labels in the round drop out of the solve; a ridge ``ridge`` is added to
   H's diagonal and ``damping_c`` is the damping constant (both unpinned);
-  the slope's n is the total label count, each intercept's n its own count.
+  the slope's n is the total label count, each intercept's n its own count;
+* a step bound: far from the optimum a full Newton step on the logistic loss
+  overshoots (where the sigmoid is flat, H is tiny against g), and a position
+  whose labels all agree has no finite optimum at all, so the damped step is
+  scaled as a whole, when needed, until no parameter moves by more than
+  ``max_step`` in one refit.  Scaling keeps the Newton direction, a descent
+  direction of the convex loss; near the optimum the steps are small and the
+  page's damped step is taken unchanged (the bound's value is unpinned).
 """
 from __future__ import annotations
 
@@ -149,12 +156,14 @@ def hessian_gradient(sums: np.ndarray, ridge: float = 0.0):
     return H, g
 
 
-def newton_step(sums: np.ndarray, params, damping_c: float, ridge: float) -> np.ndarray:
+def newton_step(sums: np.ndarray, params, damping_c: float, ridge: float, max_step: float = 1.0) -> np.ndarray:
     """Damped Newton update of the parameters from accumulated sums.
 
     Solves H * delta = -g over the slope and the intercepts of positions that
     have labels, scales the slope's step by N/(N+c) (N = all labels) and each
-    intercept's by n_i/(n_i+c), and returns params + delta in float64.
+    intercept's by n_i/(n_i+c), then scales the whole damped step down so that
+    its largest component is at most ``max_step`` (infinity: no bound), and
+    returns params + delta in float64.
     """
     p = np.asarray(params, dtype=np.float32).astype(np.float64)
     n = sums[:, 0]
@@ -166,17 +175,21 @@ def newton_step(sums: np.ndarray, params, damping_c: float, ridge: float) -> np.
     delta = np.zeros_like(p)
     delta[keep] = np.linalg.solve(H[np.ix_(keep, keep)], -g[keep])
     scale = np.concatenate([[N / (N + damping_c)], n / (n + damping_c)])
-    return p + delta * scale
+    step = delta * scale
+    largest = np.max(np.abs(step))
+    if largest > max_step:
+        step = step * (max_step / largest)
+    return p + step
 
 
-def fit_step(feature_arr, labels, params, accum, damping_c=10.0, ridge=1e-6, do_update=False):
+def fit_step(feature_arr, labels, params, accum, damping_c=10.0, ridge=1e-6, do_update=False, max_step=1.0):
     """One call of the batched refit: add this step's sums to ``accum``
     ([max_k, 6] float64); on the round's last step solve, update and clear.
     Returns (params float32, accum float64)."""
     accum = np.asarray(accum, dtype=np.float64) + fit_sums(feature_arr, labels, params)
     params = np.asarray(params, dtype=np.float32)
     if do_update:
-        params = newton_step(accum, params, damping_c, ridge).astype(np.float32)
+        params = newton_step(accum, params, damping_c, ridge, max_step).astype(np.float32)
         accum = np.zeros_like(accum)
     return params, accum
 

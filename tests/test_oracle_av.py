@@ -110,7 +110,7 @@ def test_undamped_step_is_the_textbook_irls_step():
     K = 3
     x, lab = _synthetic_labels(rng, 400, K, 1.1, [0.3, -0.2, -0.6])
     theta = np.array([1.0, 0.0, 0.0, 0.0], dtype=np.float32)
-    new = av.newton_step(av.fit_sums(x, lab, theta), theta, damping_c=0.0, ridge=0.0)
+    new = av.newton_step(av.fit_sums(x, lab, theta), theta, damping_c=0.0, ridge=0.0, max_step=np.inf)
     # design matrix [x, onehot(position)] over labelled drafts
     rows, ys = [], []
     for b in range(x.shape[0]):
@@ -193,9 +193,74 @@ def test_damping_scales_each_coefficient_by_its_evidence():
     x, lab = _synthetic_labels(rng, 300, K, 0.9, [0.4, 0.0, -0.4])
     params = np.array([0.5, 0.0, 0.0, 0.0], dtype=np.float32)
     sums = av.fit_sums(x, lab, params)
-    raw = av.newton_step(sums, params, 0.0, 1e-6) - params
+    raw = av.newton_step(sums, params, 0.0, 1e-6, max_step=np.inf) - params
     c = 25.0
-    damped = av.newton_step(sums, params, c, 1e-6) - params
+    damped = av.newton_step(sums, params, c, 1e-6, max_step=np.inf) - params
     n = sums[:, 0]
     scale = np.concatenate([[n.sum() / (n.sum() + c)], n / (n + c)])
     assert np.allclose(damped, raw * scale, rtol=1e-12, atol=1e-15)
+
+
+def test_step_bound_keeps_the_newton_direction():
+    """A damped step larger than the bound is scaled as a whole: same
+    direction, largest component equal to the bound; smaller steps pass."""
+    rng = np.random.default_rng(9)
+    K = 3
+    x, lab = _synthetic_labels(rng, 300, K, 0.9, [2.0, 1.0, -1.0])
+    params = np.array([-1.0, -3.0, 2.0, 1.0], dtype=np.float32)  # far from the optimum
+    sums = av.fit_sums(x, lab, params)
+    free = av.newton_step(sums, params, 10.0, 1e-6, max_step=np.inf) - params
+    assert np.abs(free).max() > 0.5
+    for bound in (0.5 * np.abs(free).max(), 0.1):
+        got = av.newton_step(sums, params, 10.0, 1e-6, max_step=bound) - params
+        assert np.abs(got).max() == pytest.approx(bound, rel=1e-12)
+        ratio = got / free
+        assert np.allclose(ratio, ratio[0], rtol=1e-12)
+    wide = av.newton_step(sums, params, 10.0, 1e-6, max_step=2.0 * np.abs(free).max()) - params
+    assert np.array_equal(wide, free)
+
+
+def test_separable_position_moves_by_the_bound():
+    """Every draft at position 0 rejected, features all 0: the log-likelihood
+    has no finite optimum in beta_0.  At beta_0 = 0, pi = 1/2, so g = n/2 and
+    H = n/4 (+ ridge): the Newton step is -2 before damping, -2 n/(n+c)
+    after it, and the bound cuts it to exactly -max_step."""
+    n, c = 100, 10.0
+    x = np.zeros((n, 1), np.float32)
+    lab = np.zeros((n, 1), np.int8)
+    params = np.array([0.5, 0.0], dtype=np.float32)
+    sums = av.fit_sums(x, lab, params)
+    free = av.newton_step(sums, params, c, 1e-6, max_step=np.inf)
+    assert free[1] == pytest.approx(-2.0 * n / (n + c), rel=1e-6)
+    assert free[0] == pytest.approx(0.5, abs=1e-12)  # the slope sees no spread in x
+    bounded = av.newton_step(sums, params, c, 1e-6, max_step=1.0)
+    assert bounded[1] == pytest.approx(-1.0, rel=1e-12)
+
+
+def test_refit_on_the_benchmark_workload_stays_bounded():
+    """The benchmark's loop: the peaked B=256, K=4, V=128256 batch, features
+    and first-rejection labels from the oracle, a refit on every step from
+    omega = 1, beta = 0.  The page's undamped-by-distance Newton step runs
+    away there (features bunch near -4.8, where the sigmoid is flat, and the
+    deepest positions see labels of one class only); with the step bound the
+    parameters stay bounded and the log-loss falls."""
+    from oracle import verify as ov
+    from synth import gen
+
+    b = gen.make_batch("bf16_b256_k4_v128256_peaked")
+    x = av.av_score_batch(b)["feature"].astype(np.float32)
+    lab = ov.verify_batch(b)["labels"]
+    start = b.av_params.astype(np.float32)
+    n = int(((lab == 0) | (lab == 1)).sum())
+
+    def loop(max_step, steps):
+        p, acc = start.copy(), np.zeros((b.max_k, 6))
+        for _ in range(steps):
+            p, acc = av.fit_step(x, lab, p, acc, damping_c=10.0, ridge=1e-6, do_update=True, max_step=max_step)
+        return p
+
+    free = loop(np.inf, 3)
+    assert np.abs(free).max() > 1e3
+    bounded = loop(1.0, 30)
+    assert np.all(np.isfinite(bounded)) and np.abs(bounded).max() < 10.0
+    assert av.nll(x, lab, bounded) / n < 0.75 * av.nll(x, lab, start) / n
