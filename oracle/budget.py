@@ -21,13 +21,17 @@ Readings (the page elides the indices and sizes):
   token);
 * both cost tables are indexed by j, the number of draft tokens verified in
   the step, and hold at least N + 1 entries;
-* the survivals are products in binary32, left to right, exactly as the
-  kernel forms them: the ranking and the argmax are integer decisions, taken
-  here on the same survival values; the running sums and the ratios are
-  binary64;
+* the survivals are running products in binary32, left to right: the page
+  forms them with ``cumprod`` over the per-position probabilities held in a
+  floating-point tensor, whose default element type is binary32, and ranks
+  those values; the running sums of the survivals and the ratios are
+  binary64, as the page's ``np.cumsum`` and division over them;
 * equal survivals are ranked by their flat index b * max_k + i (lower
-  first), which keeps each request's kept drafts a prefix of its positions;
-  equal ratios give the smallest j (the first maximum).
+  first): the page's ``topk`` leaves the order of equal values open, and
+  this order makes the decision deterministic and keeps each request's kept
+  drafts a prefix of its positions (a later position's survival never
+  exceeds an earlier one's); equal ratios give the smallest j, the first
+  maximum, as ``np.argmax`` returns.
 
 Parity unpinned: the reading of the cost tables' index (no cost table is
 printed on the page; the tables are synthetic inputs here).

@@ -15,15 +15,15 @@ The metrics run over the labelled stream of the refit ([AV] "Fitting the
 coefficients": a draft is labelled 1 if accepted, 0 at the first rejection,
 and carries no label after it).
 
+The AUC is computed as the page defines it: over every (accepted,
+rejected) pair of labelled drafts, the share in which the accepted one has
+the higher score, an equal score counting one half (binary64 from the
+binary32 scores).
+
 Readings (the page gives no sizes or constants):
 
 * ECE uses 10 equal-width bins of [0, 1]; a score p falls into bin
   min(floor(10 p), 9);
-* the stream keeps, per class, a histogram of 4096 equal-width score bins
-  (bin min(floor(4096 p), 4095)); the AUC is that of the binned scores, so
-  two scores in one bin count as a tie - it equals the exact AUC when no
-  accepted and rejected draft share a bin, and differs from it by at most
-  half the share of accepted/rejected pairs that do;
 * log-loss clamps p to [1e-7, 1 - 1e-7] (parity unpinned: the constant).
 """
 from __future__ import annotations
@@ -31,7 +31,6 @@ from __future__ import annotations
 import numpy as np
 
 ECE_BINS = 10
-AUC_BINS = 4096
 EPS = 1e-7
 
 
@@ -46,14 +45,25 @@ def ece_bin(p32):
     return np.minimum(np.floor(np.asarray(p32, np.float32) * np.float32(ECE_BINS)).astype(np.int64), ECE_BINS - 1)
 
 
-def auc_bin(p32):
-    return np.minimum(np.floor(np.asarray(p32, np.float32) * np.float32(AUC_BINS)).astype(np.int64), AUC_BINS - 1)
+def auc(p, y) -> float:
+    """P(score of an accepted draft > score of a rejected one), ties one half,
+    over all pairs; NaN without both classes.  Each accepted draft's wins are
+    counted against the sorted rejected scores (a library sort and search)."""
+    p = np.asarray(p, np.float64)
+    y = np.asarray(y)
+    pos, neg = p[y == 1], np.sort(p[y == 0])
+    if len(pos) == 0 or len(neg) == 0:
+        return float("nan")
+    below = np.searchsorted(neg, pos, side="left")  # rejected drafts scoring lower
+    upto = np.searchsorted(neg, pos, side="right")  # ... lower or equal
+    wins = below.sum() + 0.5 * (upto - below).sum()
+    return float(wins) / (float(len(pos)) * float(len(neg)))
 
 
 def metrics(scores, labels) -> dict:
     """AUC, log-loss and ECE of the labelled items (labels 0/1; others skipped).
 
-    Bin indices are taken on the binary32 scores, as the kernels see them."""
+    ECE bin indices are taken on the binary32 scores, as the kernels see them."""
     p, y, p32 = _items(scores, labels)
     n = len(y)
     out = {"n": n, "n_pos": int(y.sum())}
@@ -70,14 +80,5 @@ def metrics(scores, labels) -> dict:
         if sel.any():
             ece += sel.sum() / n * abs(p[sel].mean() - y[sel].mean())
     out["ece"] = float(ece)
-    # AUC over the binned scores: P(pos > neg) + 1/2 P(pos == neg)
-    ab = auc_bin(p32)
-    pos = np.bincount(ab[y == 1], minlength=AUC_BINS).astype(np.float64)
-    neg = np.bincount(ab[y == 0], minlength=AUC_BINS).astype(np.float64)
-    npos, nneg = pos.sum(), neg.sum()
-    if npos == 0 or nneg == 0:
-        out["auc"] = float("nan")
-    else:
-        below = np.cumsum(neg) - neg  # rejected drafts in lower bins
-        out["auc"] = float((pos * below).sum() + 0.5 * (pos * neg).sum()) / (npos * nneg)
+    out["auc"] = auc(p, y)
     return out

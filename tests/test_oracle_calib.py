@@ -8,32 +8,32 @@ from sklearn.metrics import log_loss, roc_auc_score
 from oracle import calib as oc
 
 
-def _grid(g, n):
-    """Scores on the AUC grid (bin centres), where the binned AUC is exact."""
-    return ((g.integers(0, oc.AUC_BINS, n) + 0.5) / oc.AUC_BINS).astype(np.float32)
-
-
 @pytest.mark.parametrize("seed", range(5))
-def test_auc_on_grid_scores_equals_the_library(seed):
+def test_auc_equals_the_library_on_arbitrary_scores(seed):
     g = np.random.default_rng(seed)
-    p = _grid(g, 3000)
+    p = g.random(3000).astype(np.float32)
+    p[:300] = np.round(p[:300] * 20) / 20  # and some exact ties
     y = (g.random(3000) < p).astype(np.int8)
-    assert oc.metrics(p, y)["auc"] == pytest.approx(roc_auc_score(y, p), abs=1e-12)
+    assert oc.metrics(p, y)["auc"] == pytest.approx(roc_auc_score(y, p.astype(np.float64)), abs=1e-12)
 
 
 @pytest.mark.parametrize("seed", range(3))
 def test_auc_equals_a_direct_pair_count(seed):
-    # P(pos > neg) + 1/2 P(tie) over the binned scores, by counting pairs
+    # P(pos > neg) + 1/2 P(pos == neg), counting every pair by brute force
     g = np.random.default_rng(10 + seed)
-    p = g.random(400).astype(np.float32)
+    p = (np.round(g.random(400) * 50) / 50).astype(np.float32)  # many ties
     y = (g.random(400) < 0.6).astype(np.int8)
-    b = oc.auc_bin(p)
-    bp, bn = b[y == 1], b[y == 0]
-    wins = (bp[:, None] > bn[None, :]).sum() + 0.5 * (bp[:, None] == bn[None, :]).sum()
-    assert oc.metrics(p, y)["auc"] == pytest.approx(wins / (len(bp) * len(bn)), abs=1e-12)
-    # and the binned AUC is within half the tied-pair share of the exact one
-    ties = (bp[:, None] == bn[None, :]).mean()
-    assert abs(oc.metrics(p, y)["auc"] - roc_auc_score(y, p)) <= 0.5 * ties + 1e-12
+    pp, pn = p[y == 1], p[y == 0]
+    wins = (pp[:, None] > pn[None, :]).sum() + 0.5 * (pp[:, None] == pn[None, :]).sum()
+    assert oc.metrics(p, y)["auc"] == pytest.approx(wins / (len(pp) * len(pn)), abs=1e-12)
+
+
+def test_auc_tells_scores_one_float_step_apart():
+    # scores that any binning of [0, 1] would merge still order the pair
+    lo = np.float32(0.5)
+    hi = np.nextafter(lo, np.float32(1.0))
+    assert oc.metrics(np.array([hi, lo], np.float32), [1, 0])["auc"] == 1.0
+    assert oc.metrics(np.array([lo, lo], np.float32), [1, 0])["auc"] == 0.5
 
 
 def test_auc_separated_and_reversed():
@@ -81,6 +81,5 @@ def test_unlabelled_items_are_skipped_and_bins_edges():
     m = oc.metrics(p, y)
     assert m["n"] == 4 and m["n_pos"] == 3
     assert oc.ece_bin(np.float32(1.0)) == 9 and oc.ece_bin(np.float32(0.1)) == 1
-    assert oc.auc_bin(np.float32(1.0)) == oc.AUC_BINS - 1
     empty = oc.metrics(p, np.full(6, -1, np.int8))
     assert empty["n"] == 0 and np.isnan(empty["ece"])
