@@ -35,14 +35,7 @@ __all__ = [
     "sv_av_calib_accumulate",
     "sv_av_calib_metrics",
     "sv_tts_grad",
-    "sv_set_verify_kernel",
-    "sv_timing_enable",
-    "sv_timing_read",
-    "sv_read_probe_sink_words",
-    "sv_read_probe",
-    "SV_KERNEL_AUTO",
-    "SV_KERNEL_STREAMING",
-    "SV_KERNEL_RESIDENT",
+    "sv_workspace_status",
     "Workspace",
 ]
 
@@ -53,7 +46,6 @@ SV_BUDGET_MAX_ITEMS = 4096
 SV_CALIB_AUC_BINS = 4096
 SV_CALIB_WORDS = 33 + 2 * SV_CALIB_AUC_BINS
 SV_F32, SV_BF16 = 0, 1
-SV_KERNEL_AUTO, SV_KERNEL_STREAMING, SV_KERNEL_RESIDENT = 0, 1, 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libspecverify.so")
@@ -80,18 +72,14 @@ _SIGNATURES = {
                             _p, _p, _p,
                             _p, _sz]),
     "sv_av_score": (_i, [_p, _i, _i, _i, _i, _p, _p, _i64, _p, _p, _p, _f, _p, _p, _p, _p, _sz]),
-    "sv_av_fit_step": (_i, [_p, _i, _i, _p, _p, _p, _p, _f, _f, _i]),
+    "sv_av_fit_step": (_i, [_p, _i, _i, _p, _p, _p, _p, _f, _f, _f, _i]),
     "sv_status_string": (ctypes.c_char_p, [_i]),
     "sv_av_budget": (_i, [_p, _i, _i, _p, _p, _p, _p, _p, _p]),
     "sv_av_calib_accumulate": (_i, [_p, _i, _i, _p, _p, _p]),
     "sv_av_calib_metrics": (_i, [_p, _p, _p, _i]),
     "sv_tts_grad": (_i, [_p, _i, _i, _i, _i, _p, _p, _i64, _p, _p, _i64, _p, _p, _i64, _p, _p, _p, _f, _p, _p,
                          _p, _sz]),
-    "sv_set_verify_kernel": (_i, [_i]),
-    "sv_timing_enable": (_i, [_i]),
-    "sv_timing_read": (_i, [_p, _i]),
-    "sv_read_probe_sink_words": (_sz, [_sz]),
-    "sv_read_probe": (_i, [_p, _p, _sz, _p, _sz]),
+    "sv_workspace_status": (_i, [_p, _p, _sz, _p, _i]),
 }
 
 
@@ -121,25 +109,6 @@ def sv_status_string(status: int) -> str:
 def _check(status: int, what: str):
     if status != 0:
         raise RuntimeError(f"{what}: {sv_status_string(status)} (status {status})")
-
-
-def sv_read_probe_sink_words(nbytes: int) -> int:
-    return int(_load().sv_read_probe_sink_words(nbytes))
-
-
-def sv_read_probe(data: torch.Tensor, *, sink: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Read ``data`` (contiguous device tensor, 16-byte aligned, size a
-    multiple of 16 bytes) with the statistics kernel's access pattern; see
-    ``sv_read_probe``.  Returns the sink (uint32 words as int32)."""
-    if not data.is_cuda or not data.is_contiguous():
-        raise ValueError("data must be a contiguous device tensor")
-    nbytes = data.numel() * data.element_size()
-    words = sv_read_probe_sink_words(nbytes)
-    if sink is None or sink.numel() < words:
-        sink = torch.empty(max(words, 1), dtype=torch.int32, device=data.device)
-    _check(_load().sv_read_probe(_stream(data.device), _ptr(data), nbytes, _ptr(sink), sink.numel()),
-           "sv_read_probe")
-    return sink
 
 
 def sv_workspace_size(B: int, V: int, max_k: int, dtype: int) -> int:
@@ -244,34 +213,6 @@ def sv_tts_grad(draft_logits: torch.Tensor, draft_row_start: torch.Tensor, targe
     return o
 
 
-def sv_timing_enable(slots: int) -> None:
-    """Record HIP events around the kernels of the next sv_spec_verify calls
-    (a ring of `slots` calls); 0 turns timing off."""
-    _check(_load().sv_timing_enable(int(slots)), "sv_timing_enable")
-
-
-def sv_timing_read(max_calls: int):
-    """Milliseconds per recorded call, oldest first: an array of shape
-    (calls, 2) holding the statistics kernel's and the verdict + draw
-    kernel's time.  Waits for the events and empties the ring."""
-    import numpy as np
-
-    out = np.zeros((max(int(max_calls), 0), 2), dtype=np.float32)
-    n = int(_load().sv_timing_read(ctypes.c_void_p(out.ctypes.data), int(max_calls)))
-    if n < 0:
-        _check(n, "sv_timing_read")
-    return out[:n]
-
-
-def sv_set_verify_kernel(kernel: int) -> int:
-    """Select the kernel sv_spec_verify launches (process-wide); returns the
-    previous setting."""
-    prev = int(_load().sv_set_verify_kernel(int(kernel)))
-    if prev < 0:
-        _check(prev, "sv_set_verify_kernel")
-    return prev
-
-
 # ---------------------------------------------------------------------------
 # marshalling helpers
 # ---------------------------------------------------------------------------
@@ -326,6 +267,10 @@ class Workspace:
 
     def __init__(self):
         self._buf: dict = {}
+
+    def peek(self, device: torch.device) -> Optional[torch.Tensor]:
+        """The buffer held for ``device``, or None."""
+        return self._buf.get((device.type, device.index))
 
     def get(self, device: torch.device, nbytes: int) -> torch.Tensor:
         key = (device.type, device.index)
@@ -511,7 +456,8 @@ def sv_av_score(draft_logits: torch.Tensor, draft_row_start: torch.Tensor, num_d
 
 
 def sv_av_fit_step(feature: torch.Tensor, labels: torch.Tensor, params: torch.Tensor, accum: torch.Tensor,
-                   damping_c: float = 10.0, ridge: float = 1e-6, do_update: bool = False) -> None:
+                   damping_c: float = 10.0, ridge: float = 1e-6, do_update: bool = False,
+                   max_step: float = 1.0) -> None:
     """One refit step, in place on ``params`` (float32 [max_k+1]) and
     ``accum`` (float64 [max_k, 6]); see ``sv_av_fit_step``."""
     if feature.dim() != 2:
@@ -523,5 +469,24 @@ def sv_av_fit_step(feature: torch.Tensor, labels: torch.Tensor, params: torch.Te
     _dev(params, "params", torch.float32, max_k + 1)
     _dev(accum, "accum", torch.float64, 6 * max_k)
     st = _load().sv_av_fit_step(_stream(dev), B, max_k, _ptr(feature), _ptr(labels), _ptr(params),
-                                _ptr(accum), float(damping_c), float(ridge), int(bool(do_update)))
+                                _ptr(accum), float(damping_c), float(ridge), float(max_step), int(bool(do_update)))
     _check(st, "sv_av_fit_step")
+
+
+def sv_workspace_status(workspace: Workspace, device=None, clear: bool = True,
+                        out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The status word of ``workspace`` on ``device`` (default: the current
+    device) as an int32 [1] device tensor, 0 when every call on it completed
+    normally; ``clear`` zeroes the word afterwards.  See ``sv_workspace_status``.
+    A workspace never used on the device has status 0."""
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    if out is None:
+        out = torch.empty(1, dtype=torch.int32, device=dev)
+    _dev(out, "out", torch.int32, 1)
+    ws = workspace.peek(dev)
+    if ws is None:
+        out.zero_()
+        return out
+    _check(_load().sv_workspace_status(_stream(dev), _ptr(ws), ws.numel(), _ptr(out), int(bool(clear))),
+           "sv_workspace_status")
+    return out

@@ -31,24 +31,6 @@ int check_sizes(int B, int V, int max_k, int dtype) {
 
 int to_status(hipError_t e) { return e == hipSuccess ? SV_OK : SV_ERR_HIP; }
 
-int g_verify_kernel = SV_KERNEL_AUTO;  // accessed atomically
-
-// Benchmark timing (sv_timing_enable): a ring of three events per call.
-struct Timing {
-  hipEvent_t* ev = nullptr;
-  int slots = 0;
-  long calls = 0;  // calls recorded since the last read
-};
-Timing g_timing;
-
-// The next call's three events, or null when timing is off.
-const hipEvent_t* next_events() {
-  if (g_timing.slots == 0) return nullptr;
-  const int k = int(g_timing.calls % g_timing.slots);
-  ++g_timing.calls;
-  return g_timing.ev + 3 * k;
-}
-
 // Kernel arguments of a verification call (the estimator outputs unset).
 VerifyArgs verify_args(const WsLayout& L, void* workspace, int B, int V, int max_k, const void* draft_logits,
                        const int64_t* draft_row_start, int64_t draft_row_stride, const void* target_logits,
@@ -85,12 +67,9 @@ VerifyArgs verify_args(const WsLayout& L, void* workspace, int B, int V, int max
   a.av_feature = nullptr;
   a.av_score = nullptr;
   a.ctrl = reinterpret_cast<uint32_t*>(ws + L.ctrl);
-  a.reqw = reinterpret_cast<uint32_t*>(ws + L.reqw);
   a.partials = reinterpret_cast<Partial*>(ws + L.partials);
   a.zval = reinterpret_cast<float*>(ws + L.zval);
-  a.segsum = reinterpret_cast<float*>(ws + L.segsum);
   a.tagged = reinterpret_cast<uint64_t*>(ws + L.tagged);
-  a.parts = a.stride = 0;
   a.spin_limit = 0;
   return a;
 }
@@ -129,15 +108,7 @@ int sv_spec_verify(void* stream, int B, int V, int max_k, int dtype, const void*
   a.av_params = av_params;
   a.av_feature = av_feature;
   a.av_score = av_score;
-  const int kind = __atomic_load_n(&g_verify_kernel, __ATOMIC_RELAXED);
-  const hipStream_t hs = static_cast<hipStream_t>(stream);
-  hipError_t err = hipSuccess;
-  if (kind != SV_KERNEL_RESIDENT) return to_status(launch_streaming(a, dtype, hs, next_events()));
-  if (!launch_verify(a, dtype, hs, &err, next_events())) {
-    if (g_timing.slots) --g_timing.calls;  // nothing recorded
-    return SV_ERR_UNSUPPORTED;
-  }
-  return to_status(err);
+  return to_status(launch_streaming(a, dtype, static_cast<hipStream_t>(stream)));
 }
 
 size_t sv_filtered_workspace_size(int B, int V, int max_k, int dtype) {
@@ -220,13 +191,13 @@ int sv_av_score(void* stream, int B, int V, int max_k, int dtype, const void* dr
 }
 
 int sv_av_fit_step(void* stream, int B, int max_k, const float* feature, const int8_t* labels, float* params,
-                   double* accum, float damping_c, float ridge, int do_update) {
+                   double* accum, float damping_c, float ridge, float max_step, int do_update) {
   if (B < 0 || max_k < 0) return SV_ERR_INVALID_ARG;
   if (max_k > SV_MAX_K) return SV_ERR_UNSUPPORTED;
-  if (!(damping_c >= 0.f) || !(ridge >= 0.f)) return SV_ERR_INVALID_ARG;
+  if (!(damping_c >= 0.f) || !(ridge >= 0.f) || !(max_step > 0.f)) return SV_ERR_INVALID_ARG;
   if (max_k == 0) return SV_OK;
   if (!params || !accum || (B > 0 && (!feature || !labels))) return SV_ERR_INVALID_ARG;
-  return to_status(launch_av_fit(B, max_k, feature, labels, params, accum, damping_c, ridge, do_update,
+  return to_status(launch_av_fit(B, max_k, feature, labels, params, accum, damping_c, ridge, max_step, do_update,
                                  static_cast<hipStream_t>(stream)));
 }
 
@@ -290,62 +261,12 @@ int sv_tts_grad(void* stream, int B, int V, int max_k, int dtype, const void* dr
                                    loss_parts, tickets, R, nseg2, static_cast<hipStream_t>(stream)));
 }
 
-size_t sv_read_probe_sink_words(size_t bytes) {
-  return (bytes / 16 * 16 + kProbeBytesPerBlock - 1) / kProbeBytesPerBlock * (kThreads / 64);
-}
-
-int sv_read_probe(void* stream, const void* data, size_t bytes, uint32_t* sink, size_t sink_words) {
-  if (bytes == 0) return SV_OK;
-  if (!data || !sink || bytes % 16 != 0 || (reinterpret_cast<uintptr_t>(data) & 15u) != 0)
-    return SV_ERR_INVALID_ARG;
-  if (bytes / kProbeBytesPerBlock >= (uint64_t(1) << 31)) return SV_ERR_UNSUPPORTED;
-  if (sink_words < sv_read_probe_sink_words(bytes)) return SV_ERR_INVALID_ARG;
-  return to_status(launch_read_probe(data, bytes, sink, static_cast<hipStream_t>(stream)));
-}
-
-int sv_set_verify_kernel(int kernel) {
-  if (kernel != SV_KERNEL_AUTO && kernel != SV_KERNEL_STREAMING && kernel != SV_KERNEL_RESIDENT)
-    return SV_ERR_INVALID_ARG;
-  return __atomic_exchange_n(&g_verify_kernel, kernel, __ATOMIC_RELAXED);
-}
-
-int sv_timing_enable(int slots) {
-  if (slots < 0) return SV_ERR_INVALID_ARG;
-  hipError_t err = hipSuccess;
-  for (int i = 0; i < 3 * g_timing.slots; ++i) {
-    const hipError_t e = hipEventDestroy(g_timing.ev[i]);
-    if (err == hipSuccess) err = e;
-  }
-  delete[] g_timing.ev;
-  g_timing = Timing{};
-  if (slots == 0) return to_status(err);
-  g_timing.ev = new hipEvent_t[3 * size_t(slots)];
-  for (int i = 0; i < 3 * slots; ++i) {
-    const hipError_t e = hipEventCreate(&g_timing.ev[i]);
-    if (e != hipSuccess) {
-      for (int j = 0; j < i; ++j) (void)hipEventDestroy(g_timing.ev[j]);
-      delete[] g_timing.ev;
-      g_timing = Timing{};
-      return SV_ERR_HIP;
-    }
-  }
-  g_timing.slots = slots;
-  return to_status(err);
-}
-
-int sv_timing_read(float* ms, int max_calls) {
-  if (!ms || max_calls < 0) return SV_ERR_INVALID_ARG;
-  const long rec = g_timing.calls < g_timing.slots ? g_timing.calls : g_timing.slots;
-  const int n = int(rec < max_calls ? rec : max_calls);
-  const long first = g_timing.calls - n;  // the last n calls, oldest first
-  for (int c = 0; c < n; ++c) {
-    const hipEvent_t* ev = g_timing.ev + 3 * int((first + c) % g_timing.slots);
-    if (hipEventSynchronize(ev[2]) != hipSuccess || hipEventElapsedTime(&ms[2 * c], ev[0], ev[1]) != hipSuccess ||
-        hipEventElapsedTime(&ms[2 * c + 1], ev[1], ev[2]) != hipSuccess)
-      return SV_ERR_HIP;
-  }
-  g_timing.calls = 0;
-  return n;
+int sv_workspace_status(void* stream, void* workspace, size_t workspace_bytes, int32_t* status, int clear) {
+  if (!workspace || workspace_bytes < kCtrlBytes) return SV_ERR_WORKSPACE;
+  if (!status) return SV_ERR_INVALID_ARG;
+  char* ws = static_cast<char*>(workspace);
+  return to_status(launch_status(reinterpret_cast<uint32_t*>(ws + ws_layout(0, 1, 0, SV_F32).ctrl), status,
+                                 clear ? 1 : 0, static_cast<hipStream_t>(stream)));
 }
 
 const char* sv_status_string(int status) {

@@ -120,8 +120,8 @@ hipError_t launch_av_score(const ScoreArgs& a, int dtype, hipStream_t stream) {
 // (butterfly) into LDS and then over the waves in order, a fixed order that
 // makes the result deterministic.  On the round's last step thread 0 solves the arrowhead
 // Newton system H * delta = -g by eliminating the intercepts (Schur
-// complement on the slope), damps, updates the parameters and clears the
-// accumulator.
+// complement on the slope), damps, bounds the step, updates the parameters
+// and clears the accumulator.
 // ---------------------------------------------------------------------------
 
 constexpr int kFitT = 256;  // threads of the refit (1024 measured slower: binary64-bound)
@@ -141,7 +141,7 @@ __device__ __forceinline__ double wave_sum_d(double v) {
 
 __global__ __launch_bounds__(kFitT) void av_fit_kernel(int B, int max_k, const float* feature,
                                                        const int8_t* labels, float* params, double* accum,
-                                                       float damping_c, float ridge, int do_update) {
+                                                       float damping_c, float ridge, float max_step, int do_update) {
   __shared__ double red[kFitW][SV_MAX_K][6];  // per wave and position, summed over the chunks in order
   __shared__ double acc[SV_MAX_K][6];          // accumulator after this step
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -216,14 +216,24 @@ __global__ __launch_bounds__(kFitT) void av_fit_kernel(int B, int max_k, const f
         rhs += Bi * gb / D;
       }
       const double dw = (schur > 0.0) ? rhs / schur : 0.0;
-      params[0] = float(omega + dw * (N / (N + double(damping_c))));
+      // damped steps, then the whole step scaled so that no parameter moves
+      // by more than max_step (far from the optimum, or for a position whose
+      // labels all agree, the Newton step on the logistic loss overshoots)
+      double step[SV_MAX_K + 1];
+      step[0] = dw * (N / (N + double(damping_c)));
+      double largest = fabs(step[0]);
       for (int i = 0; i < max_k; ++i) {
         const double n = acc[i][0];
+        step[1 + i] = 0.0;
         if (n <= 0.0) continue;
         const double D = acc[i][1] + ridge, Bi = acc[i][2], gb = acc[i][4];
-        const double db = (-gb - Bi * dw) / D;
-        params[1 + i] = float(double(params[1 + i]) + db * (n / (n + double(damping_c))));
+        step[1 + i] = ((-gb - Bi * dw) / D) * (n / (n + double(damping_c)));
+        largest = fmax(largest, fabs(step[1 + i]));
       }
+      const double shrink = largest > double(max_step) ? double(max_step) / largest : 1.0;
+      params[0] = float(omega + step[0] * shrink);
+      for (int i = 0; i < max_k; ++i)
+        if (acc[i][0] > 0.0) params[1 + i] = float(double(params[1 + i]) + step[1 + i] * shrink);
     }
   }
   __syncthreads();
@@ -231,9 +241,10 @@ __global__ __launch_bounds__(kFitT) void av_fit_kernel(int B, int max_k, const f
 }
 
 hipError_t launch_av_fit(int B, int max_k, const float* feature, const int8_t* labels, float* params,
-                         double* accum, float damping_c, float ridge, int do_update, hipStream_t stream) {
+                         double* accum, float damping_c, float ridge, float max_step, int do_update,
+                         hipStream_t stream) {
   hipLaunchKernelGGL(av_fit_kernel, dim3(1), dim3(kFitT), 0, stream, B, max_k, feature, labels, params, accum,
-                     damping_c, ridge, do_update);
+                     damping_c, ridge, max_step, do_update);
   return hipGetLastError();
 }
 

@@ -711,37 +711,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
       if (sh.row[i].s < kRecomputeBelow) confident_feature<ET>(a, sh, b, i, c, tid);
 }
 
-// Bandwidth probe: the statistics kernel's access pattern (one workgroup per
-// 32 KiB, kNV 16-byte non-temporal loads per thread issued together) with
-// no arithmetic but an XOR of what was read, one word per wave.
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) void read_probe_kernel(
-    const uint4* data, size_t n16, uint32_t* sink) {
-  const int tid = threadIdx.x;
-  const size_t base = size_t(blockIdx.x) * kThreads * kNV;
-  uint4 v[kNV];
-#pragma unroll
-  for (int k = 0; k < kNV; ++k) {
-    const size_t i = base + size_t(k) * kThreads + tid;
-    v[k] = i < n16 ? load_stream16(data + i) : make_uint4(0u, 0u, 0u, 0u);
-  }
-  uint32_t x = 0;
-#pragma unroll
-  for (int k = 0; k < kNV; ++k) x ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x ^= __shfl_xor(x, o, 64);
-  if ((tid & 63) == 0) sink[size_t(blockIdx.x) * kWaves + (tid >> 6)] = x;
-}
-
 }  // namespace
-
-hipError_t launch_read_probe(const void* data, size_t bytes, uint32_t* sink, hipStream_t stream) {
-  const size_t n16 = bytes / 16;
-  const size_t blocks = (n16 + size_t(kThreads) * kNV - 1) / (size_t(kThreads) * kNV);
-  if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(read_probe_kernel, dim3(unsigned(blocks)), dim3(kThreads), 0, stream,
-                     static_cast<const uint4*>(data), n16, sink);
-  return hipGetLastError();
-}
 
 hipError_t launch_stats(VerifyArgs a, int dtype, hipStream_t stream) {
   const uint64_t n1 = uint64_t(a.B) * uint64_t(a.R) * uint64_t(a.nseg2);
@@ -754,28 +724,35 @@ hipError_t launch_stats(VerifyArgs a, int dtype, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_streaming(VerifyArgs a, int dtype, hipStream_t stream, const hipEvent_t* ev) {
+hipError_t launch_streaming(VerifyArgs a, int dtype, hipStream_t stream) {
   const uint64_t n1 = uint64_t(a.B) * uint64_t(a.R) * uint64_t(a.nseg2);
   const uint64_t n2 = uint64_t(a.B) * uint64_t(a.nseg2);  // one workgroup per segment of the draw rows
-  if (n1 == 0) {
-    if (ev)
-      for (int k = 0; k < 3; ++k) (void)hipEventRecord(ev[k], stream);
-    return hipSuccess;
-  }
+  if (n1 == 0) return hipSuccess;
   if (n1 >= (uint64_t(1) << 31)) return hipErrorInvalidValue;
   a.spin_limit = 1u << 18;  // a fraction of a second of polling: reached only if dispatch order were broken
   const bool bf = dtype == SV_BF16;
-  if (ev) (void)hipEventRecord(ev[0], stream);
   if (bf)
     hipLaunchKernelGGL(stats_kernel<uint16_t>, dim3(unsigned(n1)), dim3(kThreads), 0, stream, a);
   else
     hipLaunchKernelGGL(stats_kernel<float>, dim3(unsigned(n1)), dim3(kThreads), 0, stream, a);
-  if (ev) (void)hipEventRecord(ev[1], stream);
   if (bf)
     hipLaunchKernelGGL(draw_kernel<uint16_t>, dim3(unsigned(n2)), dim3(kThreads), 0, stream, a);
   else
     hipLaunchKernelGGL(draw_kernel<float>, dim3(unsigned(n2)), dim3(kThreads), 0, stream, a);
-  if (ev) (void)hipEventRecord(ev[2], stream);
+  return hipGetLastError();
+}
+
+namespace {
+
+__global__ void status_kernel(uint32_t* ctrl, int32_t* status, int clear) {
+  status[0] = int32_t(__hip_atomic_load(&ctrl[kCtrlError], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  if (clear) store_dev(&ctrl[kCtrlError], 0u);
+}
+
+}  // namespace
+
+hipError_t launch_status(uint32_t* ctrl, int32_t* status, int clear, hipStream_t stream) {
+  hipLaunchKernelGGL(status_kernel, dim3(1), dim3(1), 0, stream, ctrl, status, clear);
   return hipGetLastError();
 }
 

@@ -21,10 +21,8 @@ constexpr int kSegBytes = kThreads * kVecsPerThread * 16;
 // kGroup blocks, a block being 64 lanes x one 16-byte vector.
 constexpr int kGroup = 8;
 constexpr int kSampleSegBytes = kWaves * kGroup * 64 * 16;
-// A 32 KiB half segment: kHalfVecs 16-byte vectors per thread.  The
-// register-resident kernel pairs the half segment s of a draft row with the
-// same half of the target row, or takes a whole 64 KiB segment of a target row
-// that has no draft row beside it.
+// A 32 KiB half segment (kHalfVecs 16-byte vectors per thread): the unit of
+// the verification's statistics and draw workgroups.
 constexpr int kHalfVecs = kVecsPerThread / 2;
 constexpr int kHalfBytes = kThreads * kHalfVecs * 16;
 static_assert(kHalfBytes == kSampleSegBytes, "half segments are the sampling segments");
@@ -63,27 +61,15 @@ struct Partial {
 
 // Byte offsets inside the caller's workspace.
 //
-// The workspace starts with a fixed arena - a control block, a
-// per-request-slot array of SV_MAX_B words (scoring kernel), then SV_MAX_B
-// per-request blocks of kReqWords words (register-resident kernel) - which
-// every call leaves zeroed and no call writes partial data into, whatever its
-// shape.  After the arena comes the per-call region, laid out for the call's
-// (B, V, max_k).
-constexpr int kParts = 16;        // independent work schedules (claim counters)
+// The workspace starts with a fixed arena - a control line holding the status
+// word, then a per-request-slot array of SV_MAX_B arrival counters (scoring
+// and distillation kernels) - which every call leaves zeroed (the status word
+// aside) and no call writes partial data into, whatever its shape.  After the
+// arena comes the per-call region, laid out for the call's (B, V, max_k).
 constexpr int kLineWords = 32;    // 128 bytes: one counter per cache line
-constexpr size_t kCtrlBytes = size_t(kParts + 2) * kLineWords * 4;
-constexpr int kCtrlWork = 0;                         // claim counter of partition p: kCtrlWork + p * kLineWords
-constexpr int kCtrlExit = kParts * kLineWords;       // workgroups that finished
-constexpr int kCtrlError = (kParts + 1) * kLineWords;  // set if a bounded wait ever expired
-constexpr int kArenaArrays = 1;  // tickets (scoring and distillation kernels)
-// Words of request b's block (register-resident kernel), one 128-byte line:
-constexpr int kReqWords = 32;
-constexpr int kWRow = 0;      // kWRow + i: arrivals of row i (i = 0..SV_MAX_K)
-constexpr int kWMask = 18;    // 64-bit: bit i = row i has its verdict, bit 32 + i = row i rejected
-constexpr int kWDepart = 20;  // items that left the request
-constexpr int kWDraw = 21;    // kWDraw + r: arrivals of the draw's segment weights, round r (0, 1)
-static_assert(kWRow + SV_MAX_K < kWMask && kWMask % 2 == 0 && kWDraw + 1 < kReqWords, "request block");
-constexpr size_t kArenaBytes = kCtrlBytes + kArenaArrays * size_t(SV_MAX_B) * 4 + size_t(SV_MAX_B) * kReqWords * 4;
+constexpr size_t kCtrlBytes = 256;  // the control line, padded so that the arrays after it stay 256-byte aligned
+constexpr int kCtrlError = 0;     // status word: set if a bounded wait ever expired
+constexpr size_t kArenaBytes = kCtrlBytes + size_t(SV_MAX_B) * 4;
 
 // Slot of request b in the per-request arrays of the arena: consecutive
 // requests land 128 bytes apart (for b < SV_MAX_B / 32), so the atomics of
@@ -119,12 +105,10 @@ constexpr uint32_t kSlotReady = 0x7fb5a5a5u;
 __host__ __device__ constexpr uint64_t ready_slot(uint32_t bits) { return (uint64_t(bits) << 32) | kSlotReady; }
 
 struct WsLayout {
-  size_t ctrl;      // uint32 control block (claim/exit counters, error flag)
+  size_t ctrl;      // uint32 control line (status word)
   size_t tickets;   // uint32 [SV_MAX_B]  arrivals per request (scoring and distillation kernels)
-  size_t reqw;      // uint32 [SV_MAX_B][kReqWords]  request blocks (register-resident kernel)
   size_t partials;  // Partial [B][R][nseg2]
   size_t zval;      // float [B][R]       logit at the draft token, per row
-  size_t segsum;    // float [2][B][nseg2]  weight of each sampling segment per draw round (register-resident kernel)
   size_t tagged;    // uint64 [B][nseg2][kDrawSlices]  hand-off slots of the draw's slice weights
   size_t tts_loss;  // float [B][max_k][nseg2]  distillation loss per canvas row segment
   size_t total;
@@ -155,11 +139,9 @@ inline WsLayout ws_layout(int B, int V, int max_k, int dtype) {
   L.R = rows_per_request(max_k);
   L.ctrl = 0;
   L.tickets = kCtrlBytes;
-  L.reqw = L.tickets + size_t(SV_MAX_B) * 4;
   L.partials = kArenaBytes;
   L.zval = L.partials + align256(size_t(B) * L.R * L.nseg2 * sizeof(Partial));
-  L.segsum = L.zval + align256(size_t(B) * L.R * 4);
-  L.tagged = L.segsum + align256(2 * size_t(B) * L.nseg2 * 4);
+  L.tagged = L.zval + align256(size_t(B) * L.R * 4);
   L.tts_loss = L.tagged + align256(size_t(B) * L.nseg2 * kDrawSlices * 8);
   L.total = L.tts_loss + align256(size_t(B) * max_k * L.nseg2 * 4);
   return L;
@@ -188,16 +170,11 @@ struct VerifyArgs {
   float* av_feature;
   float* av_score;
   // workspace
-  uint32_t* ctrl;
-  uint32_t* reqw;     // request blocks
+  uint32_t* ctrl;     // status word at kCtrlError
   Partial* partials;  // [B][R][nseg2]
   float* zval;
-  float* segsum;      // [2][B][nseg2]
   uint64_t* tagged;   // hand-off slots (see WsLayout::tagged)
-  // work-item schedule (see the kernels)
-  int parts;         // independent schedules; partition p owns requests b = p (mod parts)
-  int stride;        // item slots per request (register-resident kernel)
-  uint32_t spin_limit;
+  uint32_t spin_limit;  // polls of a bounded wait before it gives up
 };
 
 struct ScoreArgs {
@@ -216,20 +193,13 @@ struct ScoreArgs {
   Partial* partials;
 };
 
-// The register-resident verification kernel: returns false (nothing
-// launched) if the sizes do not fit it; otherwise launches and stores the
-// launch status in *err.  `ev` (nullable): three events to record before the
-// kernel, after it, and after it again (an empty second phase).
-bool launch_verify(VerifyArgs a, int dtype, hipStream_t stream, hipError_t* err, const hipEvent_t* ev = nullptr);
 // The two streaming kernels (statistics, then the verdict and the draw).
-// `ev` (nullable): three events to record before, between and after them.
-hipError_t launch_streaming(VerifyArgs a, int dtype, hipStream_t stream, const hipEvent_t* ev = nullptr);
+hipError_t launch_streaming(VerifyArgs a, int dtype, hipStream_t stream);
 // The statistics kernel alone (segment statistics and logits at the draft
 // tokens into the workspace).
 hipError_t launch_stats(VerifyArgs a, int dtype, hipStream_t stream);
-// Read probe (measurement aid): one word per 64 threads into sink.
-constexpr size_t kProbeBytesPerBlock = kHalfBytes;  // 32 KiB per workgroup
-hipError_t launch_read_probe(const void* data, size_t bytes, uint32_t* sink, hipStream_t stream);
+// Copy the workspace's status word to *status and, if `clear`, zero it.
+hipError_t launch_status(uint32_t* ctrl, int32_t* status, int clear, hipStream_t stream);
 
 // Filtered verification: the statistics kernel, the threshold searches and
 // the verdict / draw kernel.
@@ -258,7 +228,7 @@ hipError_t launch_tts_grad(int B, int V, int max_k, int dtype, const void* draft
                            void* grad, float* loss, const Partial* stats, float* loss_parts, uint32_t* tickets, int R, int nseg2,
                            hipStream_t stream);
 hipError_t launch_av_fit(int B, int max_k, const float* feature, const int8_t* labels,
-                         float* params, double* accum, float damping_c, float ridge,
+                         float* params, double* accum, float damping_c, float ridge, float max_step,
                          int do_update, hipStream_t stream);
 
 }  // namespace sv

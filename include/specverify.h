@@ -68,16 +68,18 @@ typedef enum {
  * of B requests, vocabulary V, at most max_k drafts each, elements of type
  * `dtype`.  Returns 0 for arguments those calls would reject.
  *
- * The workspace starts with a fixed arena (work counters, one word and one
- * 128-byte block per request slot, SV_MAX_B slots), followed by per-row
- * partial statistics, logits at the draft tokens and draw weights.
+ * The workspace starts with a fixed arena (a status word, one arrival
+ * counter per request slot, SV_MAX_B slots), followed by per-row partial
+ * statistics, logits at the draft tokens and the draw's hand-off slots.
  * Zero-fill the workspace once after allocation; every call leaves the
- * counters at zero again, and no call writes anything else into the arena,
- * so one workspace (of the largest size needed) serves any sequence of calls
- * of any shapes on one stream without further clearing, and a call captured
- * in a HIP graph replays without any reset.  Calls that can run concurrently
- * (different streams) need different workspaces.  If a call is aborted part
- * way (device fault), zero-fill the workspace again. */
+ * counters and hand-off slots cleared again, and no call writes anything
+ * else into the arena, so one workspace (of the largest size needed) serves
+ * any sequence of calls of any shapes on one stream without further
+ * clearing, and a call captured in a HIP graph replays without any reset.
+ * Calls that can run concurrently (different streams) need different
+ * workspaces.  If a call is aborted part way (device fault), or
+ * sv_workspace_status reports a nonzero status, zero-fill the workspace
+ * again. */
 size_t sv_workspace_size(int B, int V, int max_k, int dtype);
 
 /* Batched speculative verification, one step for B requests.
@@ -237,15 +239,22 @@ int sv_av_score(void* stream, int B, int V, int max_k, int dtype,
  * If do_update != 0 (last step of the round) it then solves H * delta = -g
  * over the slope and the intercepts of positions with labels (ridge added to
  * H's diagonal), scales the slope's step by N/(N + damping_c) (N = all
- * labels) and each intercept's by n_i/(n_i + damping_c), adds delta to
- * params (fp32, in place) and zero-fills accum.
+ * labels) and each intercept's by n_i/(n_i + damping_c), then scales the
+ * whole step down, if needed, so that no parameter moves by more than
+ * max_step, adds it to params (fp32, in place) and zero-fills accum.  The
+ * bound is a safeguard the page does not state: far from the optimum (where
+ * the sigmoid is flat, so H is small against g) a full Newton step on the
+ * logistic loss overshoots, and a position whose labels all agree has no
+ * finite optimum; scaling keeps the Newton direction, a descent direction.
+ * Typical values: damping_c = 10, ridge = 1e-6, max_step = 1 (logit units);
+ * max_step = +inf disables the bound.
  *   feature  float [B*max_k], labels int8 [B*max_k] (e.g. from sv_spec_verify).
  *   params   float [max_k+1] in/out.   accum double [6*max_k] in/out,
  *            zero-filled by the caller before a round's first step.
  * A round with no labels leaves params unchanged. */
 int sv_av_fit_step(void* stream, int B, int max_k, const float* feature,
                    const int8_t* labels, float* params, double* accum,
-                   float damping_c, float ridge, int do_update);
+                   float damping_c, float ridge, float max_step, int do_update);
 
 /* The estimator's global draft budget: how many draft tokens of the batch to
  * verify, and which.
@@ -349,57 +358,21 @@ int sv_tts_grad(void* stream, int B, int V, int max_k, int dtype,
                 const int32_t* num_draft, const float* temperature, const float* weights, float lambda,
                 void* grad, float* loss, void* verify_workspace, size_t workspace_bytes);
 
-/* Which kernel sv_spec_verify launches: a process-wide setting, default
- * SV_KERNEL_AUTO.  Both kernels compute the same outputs.
- *   SV_KERNEL_STREAMING  a statistics pass over every row, then a second pass
- *                        over the rows the draw needs (one row pair, or the
- *                        bonus row, per stochastic request).
- *   SV_KERNEL_RESIDENT   every logit is read once: each row segment stays on
- *                        chip (registers and LDS) until its row's verdict is
- *                        known, and the token is drawn from that copy.  It
- *                        trades the second pass for waits between the
- *                        workgroups of a row.
- *   SV_KERNEL_AUTO       the streaming kernel (measured faster on MI355X for
- *                        rows of 64 KiB and more).
- * Returns the previous setting, or SV_ERR_INVALID_ARG for an unknown value
- * (the setting is then unchanged). */
-typedef enum {
-  SV_KERNEL_AUTO = 0,
-  SV_KERNEL_STREAMING = 1,
-  SV_KERNEL_RESIDENT = 2
-} sv_kernel;
-
-int sv_set_verify_kernel(int kernel);
-
-/* Kernel timing for benchmarks (a measurement aid, not part of the method).
- * sv_timing_enable(slots) with slots > 0 makes every later sv_spec_verify
- * record three HIP events on its stream: before its first kernel, between
- * the statistics kernel and the verdict + draw kernel, and after its last
- * kernel, into a ring of `slots` records (the resident kernel records its
- * one kernel as phase 0 and an empty phase 1).  slots = 0 turns timing off
- * and destroys the events.  The events are created here (no device memory is
- * allocated); calls from several host threads at once are not supported
- * while timing is on.
- * sv_timing_read(ms, max_calls) waits for the recorded events and writes,
- * for the last min(recorded, slots, max_calls) calls in call order, the
- * milliseconds of phase 0 at ms[2c] and of phase 1 at ms[2c + 1]; it then
- * empties the ring.  Returns the number of calls written, or a negative
- * sv_status (SV_ERR_HIP if an event query failed). */
-int sv_timing_enable(int slots);
-int sv_timing_read(float* ms, int max_calls);
-
-/* Read-bandwidth probe, a measurement aid (not a step of the method): reads
- * `bytes` of device memory at `data` with the statistics kernel's access
- * pattern (one 256-thread workgroup per 32 KiB, eight 16-byte non-temporal
- * loads per thread issued together) and no arithmetic beyond an XOR of what
- * it read, so that its rate is the ceiling a streaming read reaches.  Writes
- * one word per 64 threads into `sink` (device, caller-owned):
- * sv_read_probe_sink_words(bytes) words, word 4*g + w the XOR of the 16-byte
- * vectors (as four 32-bit words) that wave w of workgroup g read.  `data`
- * 16-byte aligned, `bytes` a multiple of 16 (else SV_ERR_INVALID_ARG, as for
- * a short sink); asynchronous on `stream`. */
-size_t sv_read_probe_sink_words(size_t bytes);
-int sv_read_probe(void* stream, const void* data, size_t bytes, uint32_t* sink, size_t sink_words);
+/* Status of a workspace, for the calls made on it so far.
+ *
+ * The draw of sv_spec_verify hands each row segment's weight to the
+ * request's last workgroup, which waits for it (the hardware dispatches
+ * workgroups in order, so the wait ends); the wait is bounded, and if it ever
+ * gave up - only possible if that dispatch order were broken - the call's
+ * emitted token for the request is not valid and the workspace's status word
+ * is set.  This call copies the status word to *status (device int32: 0 =
+ * every call so far completed normally) and, if clear != 0, zeroes it.  A
+ * nonzero status also means a hand-off slot may have been left filled: zero-
+ * fill the whole workspace before reusing it.  Asynchronous on `stream`, like
+ * the other calls: read *status once the stream has reached this point.
+ * Returns SV_OK, SV_ERR_WORKSPACE (workspace NULL or too small) or
+ * SV_ERR_INVALID_ARG (status NULL). */
+int sv_workspace_status(void* stream, void* workspace, size_t workspace_bytes, int32_t* status, int clear);
 
 /* Static description of a status code. */
 const char* sv_status_string(int status);

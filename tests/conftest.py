@@ -33,16 +33,69 @@ def golden():
     return load_golden
 
 
-VERIFY_KERNELS = {"streaming": 1, "resident": 2}  # sv_kernel values of include/specverify.h
+def _track_workspaces():
+    """Remember every Workspace the tests create (weakly), so that the status
+    word of each can be checked after a GPU test."""
+    import weakref
 
-
-@pytest.fixture(params=sorted(VERIFY_KERNELS))
-def verify_kernel(request):
-    """Run a test once per verification kernel (process-wide selector),
-    restoring the previous selection afterwards."""
     import draft_token_verification_spec_amd as sv
 
-    prev = sv.sv_set_verify_kernel(VERIFY_KERNELS[request.param])
-    print(f"[kernel {request.param}]", flush=True)
-    yield request.param
-    sv.sv_set_verify_kernel(prev)
+    live = weakref.WeakSet([sv._default_ws])
+    init = sv.Workspace.__init__
+
+    def tracked(self, *a, **kw):
+        init(self, *a, **kw)
+        live.add(self)
+
+    sv.Workspace.__init__ = tracked
+    return live
+
+
+_LIVE_WORKSPACES = None
+
+
+@pytest.fixture(autouse=True)
+def _gpu_case_bookkeeping(request):
+    """For GPU tests: name the running test in the flip log, and afterwards
+    assert that no bounded wait expired in any workspace the test used
+    (sv_workspace_status reads and clears each status word)."""
+    global _LIVE_WORKSPACES
+    if request.node.get_closest_marker("gpu") is None:
+        yield
+        return
+    import gpu_harness
+    import torch
+
+    import draft_token_verification_spec_amd as sv
+
+    if _LIVE_WORKSPACES is None:
+        _LIVE_WORKSPACES = _track_workspaces()
+    gpu_harness.CURRENT = request.node.nodeid.split("::", 1)[-1]
+    yield
+    if not torch.cuda.is_available():
+        return
+    bad = []
+    for ws in list(_LIVE_WORKSPACES):
+        for key in list(ws._buf):
+            st = sv.sv_workspace_status(ws, torch.device(*key))
+            if int(st.item()) != 0:
+                bad.append((key, int(st.item())))
+    assert not bad, f"workspace status words set (a bounded wait expired): {bad}"
+
+
+def pytest_terminal_summary(terminalreporter):
+    """Within-margin flips of every parity comparison, at the end of the run."""
+    try:
+        import gpu_harness
+    except Exception:
+        return
+    if not gpu_harness.FLIP_LOG:
+        return
+    tr = terminalreporter
+    tr.section("parity: within-margin flips per comparison")
+    total_req = total_flips = 0
+    for case, n, flips, ed, et in gpu_harness.FLIP_LOG:
+        tr.write_line(f"{case}: {n} requests compared, {flips} flips, max rel err pd(d) {ed:.2e} pt(d) {et:.2e}")
+        total_req += n
+        total_flips += flips
+    tr.write_line(f"total: {total_req} requests compared, {total_flips} within-margin flips")

@@ -24,10 +24,9 @@ def declared_functions():
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
     assert set(names) == {"sv_workspace_size", "sv_spec_verify", "sv_av_score", "sv_av_fit_step",
-                          "sv_status_string", "sv_set_verify_kernel", "sv_timing_enable", "sv_timing_read",
-                          "sv_av_budget", "sv_av_calib_accumulate", "sv_av_calib_metrics", "sv_tts_grad",
-                          "sv_filtered_workspace_size", "sv_spec_verify_filtered", "sv_read_probe_sink_words",
-                          "sv_read_probe"}
+                          "sv_status_string", "sv_av_budget", "sv_av_calib_accumulate", "sv_av_calib_metrics",
+                          "sv_tts_grad", "sv_filtered_workspace_size", "sv_spec_verify_filtered",
+                          "sv_workspace_status"}
     lib = ctypes.CDLL(sv.lib_path())
     for n in names:
         assert hasattr(lib, n), n
@@ -44,23 +43,17 @@ def test_header_constants_match_binding():
     assert re.search(r"#define SV_CALIB_WORDS \(33 \+ 2 \* SV_CALIB_AUC_BINS\)", text)
 
 
-def test_kernel_selector():
-    text = open(HEADER).read()
-    for name in ("SV_KERNEL_AUTO", "SV_KERNEL_STREAMING", "SV_KERNEL_RESIDENT"):
-        assert int(re.search(name + r" = (\d+)", text).group(1)) == getattr(sv, name)
-    assert sv.sv_set_verify_kernel(sv.SV_KERNEL_STREAMING) == sv.SV_KERNEL_AUTO
-    assert sv.sv_set_verify_kernel(sv.SV_KERNEL_RESIDENT) == sv.SV_KERNEL_STREAMING
-    with pytest.raises(RuntimeError):
-        sv.sv_set_verify_kernel(7)
-    assert sv.sv_set_verify_kernel(sv.SV_KERNEL_AUTO) == sv.SV_KERNEL_RESIDENT
+def test_no_process_wide_settings_or_measurement_aids_exported():
+    lib = ctypes.CDLL(sv.lib_path())
+    for name in ("sv_set_verify_kernel", "sv_timing_enable", "sv_timing_read", "sv_read_probe"):
+        assert not hasattr(lib, name), name
 
 
-def test_timing_without_events():
-    # no events exist: turning timing off and reading touch no device
-    sv.sv_timing_enable(0)
-    assert sv.sv_timing_read(4).shape == (0, 2)
-    with pytest.raises(RuntimeError):
-        sv.sv_timing_enable(-1)
+def test_workspace_status_rejections():
+    lib = sv._load()
+    assert lib.sv_workspace_status(None, None, 1 << 20, FAKE, 1) == -3
+    assert lib.sv_workspace_status(None, FAKE, 16, FAKE, 1) == -3
+    assert lib.sv_workspace_status(None, FAKE, 1 << 20, None, 1) == -1
 
 
 def test_status_strings():
@@ -195,14 +188,16 @@ def test_av_score_rejects_before_launch():
 def test_av_fit_rejects_before_launch():
     lib = sv._load()
     f = ctypes.c_float
-    assert lib.sv_av_fit_step(None, -1, 4, FAKE, FAKE, FAKE, FAKE, f(10), f(1e-6), 0) == -1
-    assert lib.sv_av_fit_step(None, 4, 17, FAKE, FAKE, FAKE, FAKE, f(10), f(1e-6), 0) == -2
-    assert lib.sv_av_fit_step(None, 4, 4, None, FAKE, FAKE, FAKE, f(10), f(1e-6), 0) == -1
-    assert lib.sv_av_fit_step(None, 4, 4, FAKE, FAKE, None, FAKE, f(10), f(1e-6), 0) == -1
-    assert lib.sv_av_fit_step(None, 4, 4, FAKE, FAKE, FAKE, None, f(10), f(1e-6), 0) == -1
-    assert lib.sv_av_fit_step(None, 4, 4, FAKE, FAKE, FAKE, FAKE, f(-1), f(1e-6), 0) == -1
-    assert lib.sv_av_fit_step(None, 4, 4, FAKE, FAKE, FAKE, FAKE, f(10), f(float("nan")), 0) == -1
-    assert lib.sv_av_fit_step(None, 4, 0, None, None, None, None, f(10), f(1e-6), 0) == 0
+    assert lib.sv_av_fit_step(None, -1, 4, FAKE, FAKE, FAKE, FAKE, f(10), f(1e-6), f(1.0), 0) == -1
+    assert lib.sv_av_fit_step(None, 4, 17, FAKE, FAKE, FAKE, FAKE, f(10), f(1e-6), f(1.0), 0) == -2
+    assert lib.sv_av_fit_step(None, 4, 4, None, FAKE, FAKE, FAKE, f(10), f(1e-6), f(1.0), 0) == -1
+    assert lib.sv_av_fit_step(None, 4, 4, FAKE, FAKE, None, FAKE, f(10), f(1e-6), f(1.0), 0) == -1
+    assert lib.sv_av_fit_step(None, 4, 4, FAKE, FAKE, FAKE, None, f(10), f(1e-6), f(1.0), 0) == -1
+    assert lib.sv_av_fit_step(None, 4, 4, FAKE, FAKE, FAKE, FAKE, f(-1), f(1e-6), f(1.0), 0) == -1
+    assert lib.sv_av_fit_step(None, 4, 4, FAKE, FAKE, FAKE, FAKE, f(10), f(float("nan")), f(1.0), 0) == -1
+    for bad in (0.0, -1.0, float("nan")):
+        assert lib.sv_av_fit_step(None, 4, 4, FAKE, FAKE, FAKE, FAKE, f(10), f(1e-6), f(bad), 0) == -1
+    assert lib.sv_av_fit_step(None, 4, 0, None, None, None, None, f(10), f(1e-6), f(1.0), 0) == 0
 
 
 def test_binding_refuses_host_tensors():
@@ -278,16 +273,18 @@ def test_tts_grad_rejects_before_launch():
 
 
 def test_read_probe_sizes_and_rejections():
-    assert sv.sv_read_probe_sink_words(0) == 0
-    assert sv.sv_read_probe_sink_words(16) == 4  # one workgroup, four waves
-    assert sv.sv_read_probe_sink_words(32768) == 4
-    assert sv.sv_read_probe_sink_words(32768 + 16) == 8
-    lib = sv._load()
+    from draft_token_verification_spec_amd import measure
+
+    assert measure.read_probe_sink_words(0) == 0
+    assert measure.read_probe_sink_words(16) == 4  # one workgroup, four waves
+    assert measure.read_probe_sink_words(32768) == 4
+    assert measure.read_probe_sink_words(32768 + 16) == 8
+    lib = measure._load()
     ok = dict(stream=None, data=FAKE, nbytes=1 << 20, sink=FAKE, words=1 << 20)
-    call = lambda **kw: lib.sv_read_probe(*{**ok, **kw}.values())
+    call = lambda **kw: lib.svb_read_probe(*{**ok, **kw}.values())
     assert call(nbytes=0) == 0
     assert call(data=None) == -1
     assert call(sink=None) == -1
     assert call(nbytes=(1 << 20) + 8) == -1  # not a multiple of 16
     assert call(data=ctypes.c_void_p(0x10008)) == -1  # not 16-byte aligned
-    assert call(words=sv.sv_read_probe_sink_words(1 << 20) - 1) == -1
+    assert call(words=measure.read_probe_sink_words(1 << 20) - 1) == -1

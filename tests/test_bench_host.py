@@ -54,7 +54,9 @@ def test_counter_summary_scales_by_the_calibration_copy(tmp_path):
     assert s["dispatches"] == 2
     assert s["fetch_bytes_per_launch"] == 288577.0 * 2 * 1024
     assert s["write_bytes_per_launch"] == 612.0 * 1024
-    assert rec["bytes_per_launch"] == s["fetch_bytes_per_launch"] + s["write_bytes_per_launch"]
+    d = rec["kernels"]["draw_kernel"]
+    assert rec["kernels_of_the_call"] == ["stats_kernel", "draw_kernel"]
+    assert rec["bytes_per_call"] == s["bytes_per_launch"] + d["bytes_per_launch"]
     assert rec["kernels"]["draw_kernel"]["fetch_bytes_per_launch"] == 66700.0 * 2 * 1024
     assert rec["kernel_source_sha256"] == bench.kernel_source_hash()
 
@@ -64,7 +66,44 @@ def test_cpu_baselines_report_their_cores_and_rate():
     one = bench.cpu_baseline(b, 0.2)
     assert one["cores"] == 1 and one["kind"] == "oracle" and one["unit"] == "positions/s"
     assert one["value"] > 0 and np.isfinite(one["value"])
-    pool = bench.cpu_baseline_pool(b, 0.2)
+    pool, seen = bench.cpu_baseline_pool(b, 0.2)
+    assert set(seen) == set(range(b.B))
     assert pool["cores"] == max(1, min(16, len(os.sched_getaffinity(0))))
     assert pool["kind"] == "oracle" and pool["value"] > 0 and np.isfinite(pool["value"])
     assert f"over {pool['cores']} processes" in pool["sample"]
+
+
+def _oracle_as_gpu(b, seen):
+    """Library-shaped outputs holding the oracle's own results."""
+    g = {"accept_len": np.zeros(b.B, np.int32), "out_tokens": np.full((b.B, b.max_k + 1), -1, np.int32),
+         "p_draft": np.full((b.B, b.max_k), np.nan, np.float32), "p_target": np.full((b.B, b.max_k), np.nan, np.float32)}
+    for r, o in seen.items():
+        g["accept_len"][r] = o["a"]
+        g["out_tokens"][r, :o["a"] + 1] = o["tokens"]
+        g["p_draft"][r, :o["kept"]] = o["pd"]
+        g["p_target"][r, :o["kept"]] = o["pt"]
+    return g
+
+
+def test_parity_block_counts_flips_and_failures():
+    b = gen.make_batch("tiny_fp32_b4_k4_v1024", trial=0, B=24)
+    _, seen = bench.cpu_baseline_pool(b, 0.2)
+    g = _oracle_as_gpu(b, seen)
+    ok = bench.parity_block(b, g, seen)
+    assert ok["ok"] and ok["requests_compared"] == b.B and ok["within_margin_flips"] == 0
+    assert ok["max_rel_err_p_draft"] < 1e-6 and ok["max_rel_err_p_target"] < 1e-6
+    # a different emitted token where the CDF margin is wide is a failure
+    r = max(seen, key=lambda q: seen[q]["cdf"])
+    bad = {k: v.copy() for k, v in g.items()}
+    bad["out_tokens"][r, bad["accept_len"][r]] ^= 1
+    rep = bench.parity_block(b, bad, seen)
+    assert rep["failures"] == 1 and not rep["ok"]
+    # the same change where the oracle's CDF margin is within 1e-5 is a flip
+    seen2 = {q: dict(o) for q, o in seen.items()}
+    seen2[r]["cdf"] = 1e-6
+    rep = bench.parity_block(b, bad, seen2)
+    assert rep["failures"] == 0 and rep["within_margin_flips"] == 1
+    # a probability off by more than the tolerance fails
+    off = {k: v.copy() for k, v in g.items()}
+    off["p_target"][0, 0] *= 1.01
+    assert not bench.parity_block(b, off, seen)["ok"]

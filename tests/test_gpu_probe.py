@@ -1,11 +1,11 @@
-"""The read-bandwidth probe reads every byte it is given: its per-wave XORs
+"""The read-bandwidth probe of the measurement library reads every byte it is given: its per-wave XORs
 equal those computed on the host from the same bytes with the same
 assignment of 16-byte vectors to workgroups, waves and loads."""
 import numpy as np
 import pytest
 import torch
 
-import draft_token_verification_spec_amd as sv
+from draft_token_verification_spec_amd import measure
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a HIP device")]
@@ -31,7 +31,7 @@ def test_probe_reads_every_byte(nbytes):
     words = g.integers(0, 2**32, nbytes // 4, dtype=np.uint64).astype(np.uint32)
     print(f"case probe bytes={nbytes}", flush=True)
     data = torch.from_numpy(words.view(np.int32)).cuda()
-    sink = sv.sv_read_probe(data)
+    sink = measure.read_probe(data)
     torch.cuda.synchronize()
     want = host_sink(words)
     got = sink.cpu().numpy().view(np.uint32)[:want.size]
