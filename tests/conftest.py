@@ -94,8 +94,12 @@ def pytest_terminal_summary(terminalreporter):
     tr = terminalreporter
     tr.section("parity: within-margin flips per comparison")
     total_req = total_flips = 0
-    for case, n, flips, ed, et in gpu_harness.FLIP_LOG:
-        tr.write_line(f"{case}: {n} requests compared, {flips} flips, max rel err pd(d) {ed:.2e} pt(d) {et:.2e}")
+    total_tight = 0
+    for case, n, flips, ed, et, tight in gpu_harness.FLIP_LOG:
+        tr.write_line(f"{case}: {n} requests compared, {tight} with a margin <= 1e-5, {flips} flips, "
+                      f"max rel err pd(d) {ed:.2e} pt(d) {et:.2e}")
         total_req += n
         total_flips += flips
-    tr.write_line(f"total: {total_req} requests compared, {total_flips} within-margin flips")
+        total_tight += tight
+    tr.write_line(f"total: {total_req} requests compared, {total_tight} with a margin <= 1e-5, "
+                  f"{total_flips} within-margin flips")

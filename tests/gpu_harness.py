@@ -117,8 +117,27 @@ def compare_verify(batch, gpu, ora, requests=None, tol=None, check_probs=True):
             assert np.isnan(gpu["p_draft"][b, k:]).all() and np.isnan(gpu["p_target"][b, k:]).all()
             err_d = max(err_d, rel_err(gpu["p_draft"][b, :k], ora["p_draft"][r, :k]))
             err_t = max(err_t, rel_err(gpu["p_target"][b, :k], ora["p_target"][r, :k]))
-    FLIP_LOG.append((CURRENT, len(idx), flips, err_d, err_t))
+    FLIP_LOG.append((CURRENT, len(idx), flips, err_d, err_t,
+                     tight_requests(ora, np.asarray(batch.num_draft)[idx])))
     return flips
+
+
+def tight_requests(ora, num_draft) -> int:
+    """Requests with an oracle decision margin (up to the first rejection) or
+    CDF margin within MARGIN: the only ones allowed to flip."""
+    n = 0
+    for r in range(len(ora["accept_len"])):
+        k = int(num_draft[r])
+        m = ora["accept_margin"][r, :min(int(ora["accept_len"][r]) + 1, k)]
+        n += int((m <= MARGIN).any() or ora["cdf_margin"][r] <= MARGIN)
+    return n
+
+
+def flip_budget(ora, num_draft) -> int:
+    """Flips tolerated in one comparison: a tenth of the tight requests (at
+    least 2).  Every flip is also checked to be within its margin; the
+    budget catches a systematic error, which would flip most tight requests."""
+    return max(2, -(-tight_requests(ora, num_draft) // 10))
 
 
 def rel_err(got, want) -> float:

@@ -6,7 +6,7 @@ import scipy.special as sp
 import torch
 
 import draft_token_verification_spec_amd as sv
-from gpu_harness import TOL, compare_scores, compare_verify, gpu_score, gpu_verify, rel_close, to_device
+from gpu_harness import TOL, compare_scores, compare_verify, flip_budget, gpu_score, gpu_verify, rel_close, to_device
 from oracle import av as oav
 from oracle import verify as ov
 from synth import gen
@@ -192,10 +192,12 @@ def test_score_prune_verify_refit_pipeline(B):
     pruned = dataclasses.replace(b, num_draft=kept.astype(np.int32))  # what the device verified
     gv = {k: t.cpu().numpy() for k, t in v.items()}
     ovr = ov.verify_batch(pruned)
-    assert compare_verify(pruned, gv, ovr) <= max(1, B // 256)
+    assert compare_verify(pruned, gv, ovr) <= flip_budget(ovr, pruned.num_draft)
     o_p, _ = oav.fit_step(os_["feature"].astype(np.float32), ovr["labels"], b.av_params, np.zeros((b.max_k, 6)),
                           do_update=True)
-    assert rel_close(p.cpu().numpy(), o_p, 2e-3).all(), (p.cpu().numpy(), o_p)
+    # parameters cross zero (the bounded step can take omega from 1 to ~0):
+    # tolerance scale max(1, |value|), as for the feature
+    assert rel_close(p.cpu().numpy(), o_p, 2e-3, scale_floor=1.0).all(), (p.cpu().numpy(), o_p)
 
 
 def test_refit_loop_of_the_benchmark_stays_bounded():
