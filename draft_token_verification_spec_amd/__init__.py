@@ -36,6 +36,8 @@ __all__ = [
     "sv_av_calib_metrics",
     "sv_tts_grad",
     "sv_workspace_status",
+    "sv_spec_verify_static",
+    "SV_STATIC_SCRATCH_BYTES",
     "Workspace",
 ]
 
@@ -46,6 +48,7 @@ SV_BUDGET_MAX_ITEMS = 4096
 SV_CALIB_AUC_BINS = 4096
 SV_CALIB_WORDS = 33 + 2 * SV_CALIB_AUC_BINS
 SV_F32, SV_BF16 = 0, 1
+SV_STATIC_SCRATCH_BYTES = 8 << 20
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libspecverify.so")
@@ -80,6 +83,11 @@ _SIGNATURES = {
     "sv_tts_grad": (_i, [_p, _i, _i, _i, _i, _p, _p, _i64, _p, _p, _i64, _p, _p, _i64, _p, _p, _p, _f, _p, _p,
                          _p, _sz]),
     "sv_workspace_status": (_i, [_p, _p, _sz, _p, _i]),
+    "sv_spec_verify_static": (_i, [_p, _i, _i, _i, _i,
+                                   _p, _p, _i64, _p, _p, _i64,
+                                   _p, _p, _p, _p, _p, _p,
+                                   _p, _p, _p, _p, _p,
+                                   _p, _p, _p]),
 }
 
 
@@ -288,22 +296,12 @@ _default_ws = Workspace()
 # entry points
 # ---------------------------------------------------------------------------
 
-def sv_spec_verify(draft_logits: torch.Tensor, draft_row_start: torch.Tensor,
-                   target_logits: torch.Tensor, target_row_start: torch.Tensor,
-                   num_draft: torch.Tensor, draft_tokens: torch.Tensor, temperature: torch.Tensor,
-                   u_accept: torch.Tensor, u_residual: torch.Tensor, u_bonus: torch.Tensor,
-                   max_k: int, *, av_params: Optional[torch.Tensor] = None, want_feature: bool = False,
-                   want_probs: bool = True, want_labels: bool = True, workspace: Optional[Workspace] = None,
-                   out: Optional[dict] = None) -> dict:
-    """Verify one step of B requests; see ``sv_spec_verify`` in specverify.h.
-
-    ``draft_logits`` [rows, V] and ``target_logits`` [rows, V] (bf16 or fp32,
-    same dtype); ``*_row_start`` int64 [B]; ``num_draft`` int32 [B];
-    ``draft_tokens`` int32 [B, max_k]; ``temperature`` float32 [B];
-    ``u_accept`` float32 [B, max_k]; ``u_residual``/``u_bonus`` float32 [B].
-    Returns a dict with accept_len, out_tokens, and when requested labels,
-    p_draft, p_target, av_feature, av_score.
-    """
+def _verify_args(draft_logits, draft_row_start, target_logits, target_row_start, num_draft, draft_tokens,
+                 temperature, u_accept, u_residual, u_bonus, max_k, av_params, want_feature, want_probs,
+                 want_labels, out):
+    """Check the verification's inputs, allocate missing outputs; returns
+    (B, V, dtype, device, outputs, the arguments of the C call between the
+    stream and the workspace)."""
     dtype = _logits(target_logits, "target_logits")
     V = target_logits.shape[1]
     B = num_draft.numel()
@@ -340,20 +338,57 @@ def sv_spec_verify(draft_logits: torch.Tensor, draft_row_start: torch.Tensor,
                        ("av_score", torch.float32, B * max_k)):
         if key in o:
             _dev(o[key], key, dt, n)
+    args = [B, V, max_k, dtype,
+            _ptr(draft_logits) if max_k > 0 else None, _ptr(draft_row_start),
+            draft_logits.stride(0) if max_k > 0 else V,
+            _ptr(target_logits), _ptr(target_row_start), target_logits.stride(0),
+            _ptr(num_draft), _ptr(draft_tokens), _ptr(temperature), _ptr(u_accept), _ptr(u_residual),
+            _ptr(u_bonus), _ptr(o["accept_len"]), _ptr(o["out_tokens"]), _ptr(o.get("labels")),
+            _ptr(o.get("p_draft")), _ptr(o.get("p_target")), _ptr(av_params), _ptr(o.get("av_feature")),
+            _ptr(o.get("av_score"))]
+    return B, V, dtype, dev, o, args
+
+
+def sv_spec_verify(draft_logits: torch.Tensor, draft_row_start: torch.Tensor,
+                   target_logits: torch.Tensor, target_row_start: torch.Tensor,
+                   num_draft: torch.Tensor, draft_tokens: torch.Tensor, temperature: torch.Tensor,
+                   u_accept: torch.Tensor, u_residual: torch.Tensor, u_bonus: torch.Tensor,
+                   max_k: int, *, av_params: Optional[torch.Tensor] = None, want_feature: bool = False,
+                   want_probs: bool = True, want_labels: bool = True, workspace: Optional[Workspace] = None,
+                   out: Optional[dict] = None) -> dict:
+    """Verify one step of B requests; see ``sv_spec_verify`` in specverify.h.
+
+    ``draft_logits`` [rows, V] and ``target_logits`` [rows, V] (bf16 or fp32,
+    same dtype); ``*_row_start`` int64 [B]; ``num_draft`` int32 [B];
+    ``draft_tokens`` int32 [B, max_k]; ``temperature`` float32 [B];
+    ``u_accept`` float32 [B, max_k]; ``u_residual``/``u_bonus`` float32 [B].
+    Returns a dict with accept_len, out_tokens, and when requested labels,
+    p_draft, p_target, av_feature, av_score.
+    """
+    B, V, dtype, dev, o, args = _verify_args(draft_logits, draft_row_start, target_logits, target_row_start,
+                                             num_draft, draft_tokens, temperature, u_accept, u_residual, u_bonus,
+                                             max_k, av_params, want_feature, want_probs, want_labels, out)
     nbytes = sv_workspace_size(B, V, max_k, dtype)
     if nbytes == 0 and B > 0:
         _check(-2, "sv_spec_verify")
     ws = (workspace or _default_ws).get(dev, nbytes)
-    st = _load().sv_spec_verify(
-        _stream(dev), B, V, max_k, dtype,
-        _ptr(draft_logits) if max_k > 0 else None, _ptr(draft_row_start),
-        draft_logits.stride(0) if max_k > 0 else V,
-        _ptr(target_logits), _ptr(target_row_start), target_logits.stride(0),
-        _ptr(num_draft), _ptr(draft_tokens), _ptr(temperature), _ptr(u_accept), _ptr(u_residual),
-        _ptr(u_bonus), _ptr(o["accept_len"]), _ptr(o["out_tokens"]), _ptr(o.get("labels")),
-        _ptr(o.get("p_draft")), _ptr(o.get("p_target")), _ptr(av_params), _ptr(o.get("av_feature")),
-        _ptr(o.get("av_score")), _ptr(ws), ws.numel())
-    _check(st, "sv_spec_verify")
+    _check(_load().sv_spec_verify(_stream(dev), *args, _ptr(ws), ws.numel()), "sv_spec_verify")
+    return o
+
+
+def sv_spec_verify_static(draft_logits: torch.Tensor, draft_row_start: torch.Tensor,
+                          target_logits: torch.Tensor, target_row_start: torch.Tensor,
+                          num_draft: torch.Tensor, draft_tokens: torch.Tensor, temperature: torch.Tensor,
+                          u_accept: torch.Tensor, u_residual: torch.Tensor, u_bonus: torch.Tensor,
+                          max_k: int, *, av_params: Optional[torch.Tensor] = None, want_feature: bool = False,
+                          want_probs: bool = True, want_labels: bool = True, out: Optional[dict] = None) -> dict:
+    """``sv_spec_verify`` on the library's static scratch instead of a
+    workspace; see ``sv_spec_verify_static``.  With every output supplied in
+    ``out`` nothing is allocated; otherwise the missing outputs are."""
+    _, _, _, dev, o, args = _verify_args(draft_logits, draft_row_start, target_logits, target_row_start,
+                                         num_draft, draft_tokens, temperature, u_accept, u_residual, u_bonus,
+                                         max_k, av_params, want_feature, want_probs, want_labels, out)
+    _check(_load().sv_spec_verify_static(_stream(dev), *args), "sv_spec_verify_static")
     return o
 
 
@@ -473,16 +508,22 @@ def sv_av_fit_step(feature: torch.Tensor, labels: torch.Tensor, params: torch.Te
     _check(st, "sv_av_fit_step")
 
 
-def sv_workspace_status(workspace: Workspace, device=None, clear: bool = True,
+def sv_workspace_status(workspace: Optional[Workspace], device=None, clear: bool = True,
                         out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """The status word of ``workspace`` on ``device`` (default: the current
     device) as an int32 [1] device tensor, 0 when every call on it completed
-    normally; ``clear`` zeroes the word afterwards.  See ``sv_workspace_status``.
+    normally; ``clear`` zeroes the word afterwards.  ``workspace`` None: the
+    static scratch of ``sv_spec_verify_static``.  See ``sv_workspace_status``.
     A workspace never used on the device has status 0."""
     dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
     if out is None:
         out = torch.empty(1, dtype=torch.int32, device=dev)
     _dev(out, "out", torch.int32, 1)
+    if workspace is None:
+        with torch.cuda.device(dev):
+            _check(_load().sv_workspace_status(_stream(dev), None, 0, _ptr(out), int(bool(clear))),
+                   "sv_workspace_status")
+        return out
     ws = workspace.peek(dev)
     if ws is None:
         out.zero_()

@@ -74,6 +74,46 @@ VerifyArgs verify_args(const WsLayout& L, void* workspace, int B, int V, int max
   return a;
 }
 
+// Host checks of a verification call's arguments (the workspace aside).
+int verify_arg_status(int B, int V, int max_k, int dtype, const void* draft_logits, const int64_t* draft_row_start,
+                      int64_t draft_row_stride, const void* target_logits, const int64_t* target_row_start,
+                      int64_t target_row_stride, const int32_t* num_draft, const int32_t* draft_tokens,
+                      const float* temperature, const float* u_accept, const float* u_residual,
+                      const float* u_bonus, const int32_t* accept_len, const int32_t* out_tokens,
+                      const float* av_params, const float* av_feature, const float* av_score) {
+  const int st = check_sizes(B, V, max_k, dtype);
+  if (st != SV_OK || B == 0) return st;
+  if (!target_logits || !target_row_start || !num_draft || !temperature || !u_residual || !u_bonus ||
+      !accept_len || !out_tokens)
+    return SV_ERR_INVALID_ARG;
+  if (max_k > 0 && (!draft_logits || !draft_row_start || !draft_tokens || !u_accept)) return SV_ERR_INVALID_ARG;
+  if (target_row_stride < V || (max_k > 0 && draft_row_stride < V)) return SV_ERR_INVALID_ARG;
+  if (av_score && (!av_feature || !av_params)) return SV_ERR_INVALID_ARG;
+  return SV_OK;
+}
+
+// The bytes of a workspace laid out by L that a verification call uses (the
+// distillation gradient's region after them is left alone).
+size_t verify_scratch_end(const WsLayout& L) { return L.tts_loss; }
+
+// Launch the verification on a checked workspace or scratch of layout L.
+int verify_on(void* stream, const WsLayout& L, int dtype, void* workspace, int B, int V, int max_k,
+              const void* draft_logits, const int64_t* draft_row_start, int64_t draft_row_stride,
+              const void* target_logits, const int64_t* target_row_start, int64_t target_row_stride,
+              const int32_t* num_draft, const int32_t* draft_tokens, const float* temperature,
+              const float* u_accept, const float* u_residual, const float* u_bonus, int32_t* accept_len,
+              int32_t* out_tokens, int8_t* labels, float* p_draft_at_token, float* p_target_at_token,
+              const float* av_params, float* av_feature, float* av_score) {
+  VerifyArgs a = verify_args(L, workspace, B, V, max_k, draft_logits, draft_row_start, draft_row_stride,
+                             target_logits, target_row_start, target_row_stride, num_draft, draft_tokens,
+                             temperature, u_accept, u_residual, u_bonus, accept_len, out_tokens, labels,
+                             p_draft_at_token, p_target_at_token);
+  a.av_params = av_params;
+  a.av_feature = av_feature;
+  a.av_score = av_score;
+  return to_status(launch_streaming(a, dtype, static_cast<hipStream_t>(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -90,25 +130,39 @@ int sv_spec_verify(void* stream, int B, int V, int max_k, int dtype, const void*
                    const float* u_residual, const float* u_bonus, int32_t* accept_len, int32_t* out_tokens,
                    int8_t* labels, float* p_draft_at_token, float* p_target_at_token, const float* av_params,
                    float* av_feature, float* av_score, void* workspace, size_t workspace_bytes) {
-  const int st = check_sizes(B, V, max_k, dtype);
-  if (st != SV_OK) return st;
-  if (B == 0) return SV_OK;
-  if (!target_logits || !target_row_start || !num_draft || !temperature || !u_residual || !u_bonus ||
-      !accept_len || !out_tokens)
-    return SV_ERR_INVALID_ARG;
-  if (max_k > 0 && (!draft_logits || !draft_row_start || !draft_tokens || !u_accept)) return SV_ERR_INVALID_ARG;
-  if (target_row_stride < V || (max_k > 0 && draft_row_stride < V)) return SV_ERR_INVALID_ARG;
-  if (av_score && (!av_feature || !av_params)) return SV_ERR_INVALID_ARG;
+  const int st = verify_arg_status(B, V, max_k, dtype, draft_logits, draft_row_start, draft_row_stride,
+                                   target_logits, target_row_start, target_row_stride, num_draft, draft_tokens,
+                                   temperature, u_accept, u_residual, u_bonus, accept_len, out_tokens, av_params,
+                                   av_feature, av_score);
+  if (st != SV_OK || B == 0) return st;
   const WsLayout L = ws_layout(B, V, max_k, dtype);
   if (!workspace || workspace_bytes < L.total) return SV_ERR_WORKSPACE;
-  VerifyArgs a = verify_args(L, workspace, B, V, max_k, draft_logits, draft_row_start, draft_row_stride,
-                             target_logits, target_row_start, target_row_stride, num_draft, draft_tokens,
-                             temperature, u_accept, u_residual, u_bonus, accept_len, out_tokens, labels,
-                             p_draft_at_token, p_target_at_token);
-  a.av_params = av_params;
-  a.av_feature = av_feature;
-  a.av_score = av_score;
-  return to_status(launch_streaming(a, dtype, static_cast<hipStream_t>(stream)));
+  return verify_on(stream, L, dtype, workspace, B, V, max_k, draft_logits, draft_row_start, draft_row_stride,
+                   target_logits, target_row_start, target_row_stride, num_draft, draft_tokens, temperature,
+                   u_accept, u_residual, u_bonus, accept_len, out_tokens, labels, p_draft_at_token,
+                   p_target_at_token, av_params, av_feature, av_score);
+}
+
+int sv_spec_verify_static(void* stream, int B, int V, int max_k, int dtype, const void* draft_logits,
+                          const int64_t* draft_row_start, int64_t draft_row_stride, const void* target_logits,
+                          const int64_t* target_row_start, int64_t target_row_stride, const int32_t* num_draft,
+                          const int32_t* draft_tokens, const float* temperature, const float* u_accept,
+                          const float* u_residual, const float* u_bonus, int32_t* accept_len, int32_t* out_tokens,
+                          int8_t* labels, float* p_draft_at_token, float* p_target_at_token,
+                          const float* av_params, float* av_feature, float* av_score) {
+  const int st = verify_arg_status(B, V, max_k, dtype, draft_logits, draft_row_start, draft_row_stride,
+                                   target_logits, target_row_start, target_row_stride, num_draft, draft_tokens,
+                                   temperature, u_accept, u_residual, u_bonus, accept_len, out_tokens, av_params,
+                                   av_feature, av_score);
+  if (st != SV_OK || B == 0) return st;
+  const WsLayout L = ws_layout(B, V, max_k, dtype);
+  if (verify_scratch_end(L) > size_t(SV_STATIC_SCRATCH_BYTES)) return SV_ERR_UNSUPPORTED;
+  void* scratch = nullptr;
+  if (static_scratch(static_cast<hipStream_t>(stream), &scratch) != hipSuccess) return SV_ERR_HIP;
+  return verify_on(stream, L, dtype, scratch, B, V, max_k, draft_logits, draft_row_start, draft_row_stride,
+                   target_logits, target_row_start, target_row_stride, num_draft, draft_tokens, temperature,
+                   u_accept, u_residual, u_bonus, accept_len, out_tokens, labels, p_draft_at_token,
+                   p_target_at_token, av_params, av_feature, av_score);
 }
 
 size_t sv_filtered_workspace_size(int B, int V, int max_k, int dtype) {
@@ -262,8 +316,12 @@ int sv_tts_grad(void* stream, int B, int V, int max_k, int dtype, const void* dr
 }
 
 int sv_workspace_status(void* stream, void* workspace, size_t workspace_bytes, int32_t* status, int clear) {
-  if (!workspace || workspace_bytes < kCtrlBytes) return SV_ERR_WORKSPACE;
   if (!status) return SV_ERR_INVALID_ARG;
+  if (!workspace) {  // the static scratch of sv_spec_verify_static on the current device
+    if (static_scratch(static_cast<hipStream_t>(stream), &workspace) != hipSuccess) return SV_ERR_HIP;
+    workspace_bytes = SV_STATIC_SCRATCH_BYTES;
+  }
+  if (workspace_bytes < kCtrlBytes) return SV_ERR_WORKSPACE;
   char* ws = static_cast<char*>(workspace);
   return to_status(launch_status(reinterpret_cast<uint32_t*>(ws + ws_layout(0, 1, 0, SV_F32).ctrl), status,
                                  clear ? 1 : 0, static_cast<hipStream_t>(stream)));

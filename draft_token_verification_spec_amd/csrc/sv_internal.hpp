@@ -198,6 +198,10 @@ hipError_t launch_streaming(VerifyArgs a, int dtype, hipStream_t stream);
 // The statistics kernel alone (segment statistics and logits at the draft
 // tokens into the workspace).
 hipError_t launch_stats(VerifyArgs a, int dtype, hipStream_t stream);
+// Device address of the static scratch of the current device (looked up once
+// per device, and zero-filled by a kernel on `stream` until a fill has run
+// outside a graph capture).
+hipError_t static_scratch(hipStream_t stream, void** out);
 // Copy the workspace's status word to *status and, if `clear`, zero it.
 hipError_t launch_status(uint32_t* ctrl, int32_t* status, int clear, hipStream_t stream);
 

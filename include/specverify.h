@@ -149,6 +149,37 @@ int sv_spec_verify(void* stream, int B, int V, int max_k, int dtype,
                    const float* av_params, float* av_feature, float* av_score,
                    void* workspace, size_t workspace_bytes);
 
+/* The verification without a workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, and
+ * harnesses that forbid allocation.
+ *
+ * Arguments, outputs, device preconditions and results exactly as for
+ * sv_spec_verify, with no workspace: the call uses the library's own static
+ * scratch instead, SV_STATIC_SCRATCH_BYTES of device memory that each GPU the
+ * library runs on holds from the first such call until the process ends (the
+ * first call on a device also zero-fills it, with a kernel on `stream`).  It
+ * allocates and frees nothing.  Shapes whose scratch would not fit return
+ * SV_ERR_UNSUPPORTED without launching (sv_workspace_size(B, V, max_k,
+ * dtype) <= SV_STATIC_SCRATCH_BYTES is sufficient; B = 256, K = 4, V = 128256
+ * bf16 needs about 1.5 MiB).  Every call on one GPU shares that GPU's
+ * scratch, whatever its stream: calls that can overlap on one GPU (different
+ * streams, or host threads without ordering) race and give wrong results;
+ * serialise them, or give each its own workspace and use sv_spec_verify.
+ * sv_workspace_status(stream, NULL, 0, ...) reads and clears the scratch's
+ * status word on the current device. */
+#define SV_STATIC_SCRATCH_BYTES (8u << 20)
+int sv_spec_verify_static(void* stream, int B, int V, int max_k, int dtype,
+                          const void* draft_logits, const int64_t* draft_row_start,
+                          int64_t draft_row_stride,
+                          const void* target_logits, const int64_t* target_row_start,
+                          int64_t target_row_stride,
+                          const int32_t* num_draft, const int32_t* draft_tokens,
+                          const float* temperature, const float* u_accept,
+                          const float* u_residual, const float* u_bonus,
+                          int32_t* accept_len, int32_t* out_tokens, int8_t* labels,
+                          float* p_draft_at_token, float* p_target_at_token,
+                          const float* av_params, float* av_feature, float* av_score);
+
 /* Bytes of workspace needed by sv_spec_verify_filtered (the verification
  * workspace followed by the threshold-search histograms: about
  * B * (2*max_k + 1) * nseg * 6 KiB, nseg = ceil(V * elem_bytes / 32 KiB)).
@@ -370,8 +401,10 @@ int sv_tts_grad(void* stream, int B, int V, int max_k, int dtype,
  * nonzero status also means a hand-off slot may have been left filled: zero-
  * fill the whole workspace before reusing it.  Asynchronous on `stream`, like
  * the other calls: read *status once the stream has reached this point.
- * Returns SV_OK, SV_ERR_WORKSPACE (workspace NULL or too small) or
- * SV_ERR_INVALID_ARG (status NULL). */
+ * workspace = NULL selects the static scratch of sv_spec_verify_static on
+ * the current device (workspace_bytes is then ignored).
+ * Returns SV_OK, SV_ERR_WORKSPACE (workspace too small), SV_ERR_INVALID_ARG
+ * (status NULL) or SV_ERR_HIP (the static scratch could not be set up). */
 int sv_workspace_status(void* stream, void* workspace, size_t workspace_bytes, int32_t* status, int clear);
 
 /* Static description of a status code. */

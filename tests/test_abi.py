@@ -26,7 +26,7 @@ def test_every_declared_symbol_is_exported():
     assert set(names) == {"sv_workspace_size", "sv_spec_verify", "sv_av_score", "sv_av_fit_step",
                           "sv_status_string", "sv_av_budget", "sv_av_calib_accumulate", "sv_av_calib_metrics",
                           "sv_tts_grad", "sv_filtered_workspace_size", "sv_spec_verify_filtered",
-                          "sv_workspace_status"}
+                          "sv_workspace_status", "sv_spec_verify_static"}
     lib = ctypes.CDLL(sv.lib_path())
     for n in names:
         assert hasattr(lib, n), n
@@ -51,9 +51,35 @@ def test_no_process_wide_settings_or_measurement_aids_exported():
 
 def test_workspace_status_rejections():
     lib = sv._load()
-    assert lib.sv_workspace_status(None, None, 1 << 20, FAKE, 1) == -3
     assert lib.sv_workspace_status(None, FAKE, 16, FAKE, 1) == -3
     assert lib.sv_workspace_status(None, FAKE, 1 << 20, None, 1) == -1
+    assert lib.sv_workspace_status(None, None, 0, None, 1) == -1
+
+
+def test_static_scratch_constant_and_rejections():
+    """sv_spec_verify_static: the scratch limit matches the binding, and bad
+    arguments or shapes beyond the static scratch are refused on the host
+    before the scratch is touched."""
+    text = open(HEADER).read()
+    assert re.search(r"#define SV_STATIC_SCRATCH_BYTES \(8u << 20\)", text)
+    assert sv.SV_STATIC_SCRATCH_BYTES == 8 << 20
+    lib = sv._load()
+    V, K = 1024, 4
+    ok = dict(stream=None, B=4, V=V, K=K, dt=0, draft=FAKE, dstart=FAKE, dstride=V, target=FAKE, tstart=FAKE,
+              tstride=V, nd=FAKE, toks=FAKE, temp=FAKE, ua=FAKE, ur=FAKE, ub=FAKE, al=FAKE, ot=FAKE, lab=None,
+              pd=None, pt=None, par=None, feat=None, score=None)
+    call = lambda **kw: lib.sv_spec_verify_static(*{**ok, **kw}.values())
+    assert call(B=-1) == -1 and call(V=0) == -1 and call(dt=5) == -1
+    assert call(K=sv.SV_MAX_K + 1) == -2
+    for k in ("target", "tstart", "nd", "temp", "ur", "ub", "al", "ot", "draft", "dstart", "toks", "ua"):
+        assert call(**{k: None}) == -1, k
+    assert call(tstride=V - 1) == -1
+    assert call(score=FAKE) == -1  # a score needs the feature and the parameters
+    assert call(B=0) == 0
+    # the B = 256, K = 4, V = 128256 bf16 workspace fits the static scratch; a
+    # batch of 2^16 requests of 16 drafts over 2^21 fp32 logits does not
+    assert sv.sv_workspace_size(256, 128256, 4, 1) <= sv.SV_STATIC_SCRATCH_BYTES
+    assert call(B=1 << 14, V=1 << 21, K=16, dt=0, dstride=1 << 21, tstride=1 << 21) == -2
 
 
 def test_status_strings():
