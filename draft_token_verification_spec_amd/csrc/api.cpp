@@ -43,7 +43,6 @@ VerifyArgs verify_args(const WsLayout& L, void* workspace, int B, int V, int max
   a.B = B;
   a.V = V;
   a.max_k = max_k;
-  a.nseg = L.nseg;
   a.nseg2 = L.nseg2;
   a.R = L.R;
   a.draft = draft_logits;
@@ -222,26 +221,14 @@ int sv_av_score(void* stream, int B, int V, int max_k, int dtype, const void* dr
   const WsLayout L = ws_layout(B, V, max_k, dtype);
   if (!workspace || workspace_bytes < L.total) return SV_ERR_WORKSPACE;
 
-  char* ws = static_cast<char*>(workspace);
-  ScoreArgs a;
-  a.B = B;
-  a.V = V;
-  a.max_k = max_k;
-  a.nseg = L.nseg;
-  a.R = L.R;
-  a.draft = draft_logits;
-  a.draft_start = draft_row_start;
-  a.draft_stride = draft_row_stride;
-  a.num_draft = num_draft;
-  a.temperature = temperature;
-  a.params = params;
-  a.threshold = prune_threshold;
-  a.feature = feature;
-  a.score = score;
-  a.num_kept = num_kept;
-  a.tickets = reinterpret_cast<uint32_t*>(ws + L.tickets);
-  a.partials = reinterpret_cast<Partial*>(ws + L.partials);
-  return to_status(launch_av_score(a, dtype, static_cast<hipStream_t>(stream)));
+  // the statistics kernel's layout: draft row i of request b in row slot i
+  VerifyArgs a = verify_args(L, workspace, B, V, max_k, draft_logits, draft_row_start, draft_row_stride, nullptr,
+                             nullptr, V, num_draft, nullptr, temperature, nullptr, nullptr, nullptr, nullptr, nullptr,
+                             nullptr, nullptr, nullptr);
+  a.av_params = params;
+  a.av_feature = feature;
+  a.av_score = score;
+  return to_status(launch_score(a, prune_threshold, num_kept, dtype, static_cast<hipStream_t>(stream)));
 }
 
 int sv_av_fit_step(void* stream, int B, int max_k, const float* feature, const int8_t* labels, float* params,

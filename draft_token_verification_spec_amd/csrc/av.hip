@@ -1,4 +1,6 @@
-// Online acceptance estimator for gfx950.
+// Online acceptance estimator for gfx950: the refit step.  (The scoring
+// pass - feature, score, survival prune - runs on the verification's
+// statistics kernel, in stream.hip.)
 //
 // Method: [AV] "Adaptive Verification ohne Confidence Head" (spke.com; Arabic
 // mirror "التحقق التكيفي بدون رأس ثقة"):
@@ -12,106 +14,6 @@
 #include "sv_device.hpp"
 
 namespace sv {
-
-// ---------------------------------------------------------------------------
-// scoring: workgroup (b, i, s) reduces segment s of draft row i; the
-// request's last workgroup turns the row statistics into feature, score,
-// survival and the kept count.
-// ---------------------------------------------------------------------------
-
-template <typename ET>
-__global__ __launch_bounds__(kThreads) void av_score_kernel(ScoreArgs a) {
-  __shared__ Partial lds_part[kWaves];
-  __shared__ Partial rows[SV_MAX_K];
-  __shared__ float sc[SV_MAX_K];
-  __shared__ int lds_flag;
-
-  constexpr int SEG = kSegBytes / int(sizeof(ET));
-  const int tid = threadIdx.x;
-  const int item = blockIdx.x;
-  const int s = item % a.nseg;
-  const int rr = item / a.nseg;
-  const int max_k = a.max_k;
-  const int mk1 = max_k > 0 ? max_k : 1;  // requests with no drafts still own one workgroup
-  const int i = rr % mk1;
-  const int b = rr / mk1;
-  const int K = min(max(a.num_draft[b], 0), max_k);
-  const float T = a.temperature[b];
-  const float c = kLog2e / ((T > 0.f) ? T : 1.f);
-
-  if (K == 0) {  // nothing to score: one workgroup fills the request's outputs
-    if (i == 0 && s == 0) {
-      if (tid < max_k) {
-        a.feature[size_t(b) * max_k + tid] = NAN;
-        a.score[size_t(b) * max_k + tid] = NAN;
-      }
-      if (tid == 0 && a.num_kept) a.num_kept[b] = 0;
-    }
-    return;
-  }
-  if (i >= K) return;
-
-  const ET* row = static_cast<const ET*>(a.draft) + (a.draft_start[b] + i) * a.draft_stride;
-  const Partial p = segment_stats<ET, kSumInclusive>(row, s * SEG, a.V, is_aligned16(row), c, lds_part);
-  if (tid == 0) publish(&a.partials[(size_t(b) * a.R + i) * a.nseg + s], p);
-
-  if (!arrive_last(&a.tickets[req_slot(b)], uint32_t(a.nseg) * uint32_t(K), &lds_flag)) return;
-
-  // row statistics (thread j < K combines row j), then the feature as in the
-  // verification kernel: S - 1 directly when S >= 1.5, else the exact sum
-  if (tid < K) rows[tid] = combine_published(&a.partials[(size_t(b) * a.R + tid) * a.nseg], a.nseg, c, false);
-  __syncthreads();
-  if (tid < max_k) {
-    float x = NAN, score = NAN;
-    if (tid < K && rows[tid].s >= kRecomputeBelow) {
-      x = feature_from_other(rows[tid].s - 1.f);
-      score = sigmoid_score(a.params, tid, x);
-    }
-    a.feature[size_t(b) * max_k + tid] = x;
-    a.score[size_t(b) * max_k + tid] = score;
-    sc[tid] = score;
-  }
-  __syncthreads();
-  for (int j = 0; j < K; ++j) {
-    if (!(rows[j].s < kRecomputeBelow)) continue;
-    const ET* rj = static_cast<const ET*>(a.draft) + (a.draft_start[b] + j) * a.draft_stride;
-    const float so = exact_other_sum<ET>(rj, &a.partials[(size_t(b) * a.R + j) * a.nseg], a.nseg, a.V, rows[j].m, c,
-                                         lds_part);
-    if (tid == 0) {
-      const float x = feature_from_other(so);
-      const float score = sigmoid_score(a.params, j, x);
-      a.feature[size_t(b) * max_k + j] = x;
-      a.score[size_t(b) * max_k + j] = score;
-      sc[j] = score;
-    }
-    __syncthreads();
-  }
-  if (tid == 0) {
-    if (a.num_kept) {
-      int kept = K;
-      if (a.threshold > 0.f) {
-        float surv = 1.f;
-        kept = 0;
-        for (int j = 0; j < K; ++j) {
-          surv *= sc[j];
-          if (!(surv >= a.threshold)) break;
-          ++kept;
-        }
-      }
-      a.num_kept[b] = kept;
-    }
-    store_dev(&a.tickets[req_slot(b)], 0u);
-  }
-}
-
-hipError_t launch_av_score(const ScoreArgs& a, int dtype, hipStream_t stream) {
-  const unsigned grid = unsigned(a.B) * unsigned(a.max_k > 0 ? a.max_k : 1) * unsigned(a.nseg);
-  if (dtype == SV_BF16)
-    hipLaunchKernelGGL(av_score_kernel<uint16_t>, dim3(grid), dim3(kThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL(av_score_kernel<float>, dim3(grid), dim3(kThreads), 0, stream, a);
-  return hipGetLastError();
-}
 
 // ---------------------------------------------------------------------------
 // refit step: one workgroup of 256 threads.  Thread t takes requests

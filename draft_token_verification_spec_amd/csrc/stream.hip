@@ -711,6 +711,93 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
       if (sh.row[i].s < kRecomputeBelow) confident_feature<ET>(a, sh, b, i, c, tid);
 }
 
+// ---------------------------------------------------------------------------
+// the estimator's scoring pass: statistics of the draft rows, then one
+// workgroup per request for feature, score, survival and the kept count
+// ---------------------------------------------------------------------------
+
+// Workgroup = segment s of draft row i of request b (the statistics kernel's
+// access pattern and partials layout).  Greedy requests are scored at T = 1.
+template <typename ET>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) void score_stats_kernel(
+    VerifyArgs a) {
+  __shared__ Partial red[kWaves];
+  const int tid = threadIdx.x;
+  const int n = a.nseg2, max_k = a.max_k;
+  const uint32_t item = blockIdx.x;
+  const int s = int(item % uint32_t(n));
+  const int i = int((item / uint32_t(n)) % uint32_t(max_k));
+  const int b = int(item / (uint32_t(n) * uint32_t(max_k)));
+  const int kraw = a.num_draft[b];
+  const float T = a.temperature[b];
+  const int64_t start = a.draft_start[b];
+  const int K = min(max(kraw, 0), max_k);
+  if (i >= K) return;
+  const float c = uniform(kLog2e / ((T > 0.f) ? T : 1.f));
+  const ET* row = static_cast<const ET*>(a.draft) + (start + i) * a.draft_stride;
+  stats_segment<ET, kSumInclusive>(a, red, b, i, s, false, c, row, -1, tid);
+}
+
+// Workgroup = request b: merge each draft row's segment statistics (lane
+// groups, as in the verdict), feature and score of every position (confident
+// rows re-summed exactly, as in the verification), then the survival prune.
+template <typename ET>
+__global__ __launch_bounds__(kThreads) void score_finish_kernel(VerifyArgs a, float threshold, int32_t* num_kept) {
+  __shared__ DrawShared sh;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int n = a.nseg2, max_k = a.max_k, R = a.R;
+  const int b = blockIdx.x;
+  const int K = min(max(a.num_draft[b], 0), max_k);
+  const float T = a.temperature[b];
+  const float c = uniform(kLog2e / ((T > 0.f) ? T : 1.f));
+  int G = 1;
+  while (G < n && G < 64) G <<= 1;
+  const int RW = 64 / G;
+  const int g = lane / G, j = lane & (G - 1);
+  const Partial* base = a.partials + size_t(b) * R * n;
+  for (int q0 = wave * RW; q0 < K; q0 += kWaves * RW) {
+    const int q = q0 + g;
+    Partial acc{-INFINITY, 0.f, 0.f, 0x7fffffff};
+    if (q < K)
+      for (int x = j; x < n; x += G) {
+        const Partial p = base[size_t(q) * n + x];
+        merge_ms(acc.m, acc.s, acc.cnt, p.m, p.s, p.cnt, c);
+      }
+    for (int o = G >> 1; o >= 1; o >>= 1) {
+      const float m2 = __shfl_xor(acc.m, o, 64), s2 = __shfl_xor(acc.s, o, 64), c2 = __shfl_xor(acc.cnt, o, 64);
+      merge_ms(acc.m, acc.s, acc.cnt, m2, s2, c2, c);
+    }
+    if (j == 0 && q < K) sh.row[q] = RowStat{acc.m, acc.s + acc.cnt, 0x7fffffff, NAN};
+  }
+  __syncthreads();
+  if (tid < max_k) {
+    const size_t o = size_t(b) * max_k + tid;
+    const bool conf = tid < K && sh.row[tid].s < kRecomputeBelow;  // below, exactly
+    if (!conf) {
+      const float x = tid < K ? feature_from_other(sh.row[tid].s - 1.f) : NAN;
+      a.av_feature[o] = x;
+      a.av_score[o] = tid < K ? sigmoid_score(a.av_params, tid, x) : NAN;
+    }
+  }
+  __syncthreads();
+  for (int i = 0; i < K; ++i)
+    if (sh.row[i].s < kRecomputeBelow) confident_feature<ET>(a, sh, b, i, c, tid);
+  if (tid == 0 && num_kept) {
+    // survival: the running product of the scores, kept while >= threshold
+    int kept = K;
+    if (threshold > 0.f) {
+      float surv = 1.f;
+      kept = 0;
+      for (int i = 0; i < K; ++i) {
+        surv *= a.av_score[size_t(b) * max_k + i];
+        if (!(surv >= threshold)) break;
+        ++kept;
+      }
+    }
+    num_kept[b] = kept;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_stats(VerifyArgs a, int dtype, hipStream_t stream) {
@@ -721,6 +808,26 @@ hipError_t launch_stats(VerifyArgs a, int dtype, hipStream_t stream) {
     hipLaunchKernelGGL(stats_kernel<uint16_t>, dim3(unsigned(n1)), dim3(kThreads), 0, stream, a);
   else
     hipLaunchKernelGGL(stats_kernel<float>, dim3(unsigned(n1)), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_score(VerifyArgs a, float threshold, int32_t* num_kept, int dtype, hipStream_t stream) {
+  const uint64_t n1 = uint64_t(a.B) * uint64_t(a.max_k) * uint64_t(a.nseg2);
+  if (a.B == 0) return hipSuccess;
+  if (n1 >= (uint64_t(1) << 31)) return hipErrorInvalidValue;
+  const bool bf = dtype == SV_BF16;
+  if (n1 > 0) {
+    if (bf)
+      hipLaunchKernelGGL(score_stats_kernel<uint16_t>, dim3(unsigned(n1)), dim3(kThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL(score_stats_kernel<float>, dim3(unsigned(n1)), dim3(kThreads), 0, stream, a);
+  }
+  if (bf)
+    hipLaunchKernelGGL(score_finish_kernel<uint16_t>, dim3(unsigned(a.B)), dim3(kThreads), 0, stream, a, threshold,
+                       num_kept);
+  else
+    hipLaunchKernelGGL(score_finish_kernel<float>, dim3(unsigned(a.B)), dim3(kThreads), 0, stream, a, threshold,
+                       num_kept);
   return hipGetLastError();
 }
 

@@ -10,33 +10,19 @@
 
 namespace sv {
 
-// Threads per workgroup (4 wave64s) and 16-byte vectors each thread loads per
-// row segment of a statistics item: one segment is kThreads * kVecsPerThread
-// 16-byte vectors = 64 KiB of a row, whatever the element type.
+// Threads per workgroup (4 wave64s).  Rows are processed in 32 KiB segments:
+// kHalfVecs 16-byte vectors per thread of a workgroup, whatever the element
+// type.
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kVecsPerThread = 16;
-constexpr int kSegBytes = kThreads * kVecsPerThread * 16;
-// The draw splits a row into 32 KiB sampling segments: kWaves groups of
-// kGroup blocks, a block being 64 lanes x one 16-byte vector.
-constexpr int kGroup = 8;
-constexpr int kSampleSegBytes = kWaves * kGroup * 64 * 16;
-// A 32 KiB half segment (kHalfVecs 16-byte vectors per thread): the unit of
-// the verification's statistics and draw workgroups.
-constexpr int kHalfVecs = kVecsPerThread / 2;
+constexpr int kHalfVecs = 8;
 constexpr int kHalfBytes = kThreads * kHalfVecs * 16;
-static_assert(kHalfBytes == kSampleSegBytes, "half segments are the sampling segments");
 // The draw's weights are handed off per slice: one 16-byte vector of every
 // thread of a 32 KiB draw segment, kDrawSlices slices per segment.
 constexpr int kDrawSlices = kHalfVecs;
 
-__host__ __device__ constexpr int elems_per_vec(int dtype) { return dtype == SV_BF16 ? 8 : 4; }
-__host__ __device__ constexpr int seg_elems(int dtype) { return kSegBytes / (dtype == SV_BF16 ? 2 : 4); }
-__host__ __device__ inline int num_segments(int V, int dtype) {
-  return (V + seg_elems(dtype) - 1) / seg_elems(dtype);
-}
 __host__ __device__ inline int num_sample_segments(int V, int dtype) {
-  const int e = kSampleSegBytes / (dtype == SV_BF16 ? 2 : 4);
+  const int e = kHalfBytes / (dtype == SV_BF16 ? 2 : 4);
   return (V + e - 1) / e;
 }
 
@@ -112,8 +98,7 @@ struct WsLayout {
   size_t tagged;    // uint64 [B][nseg2][kDrawSlices]  hand-off slots of the draw's slice weights
   size_t tts_loss;  // float [B][max_k][nseg2]  distillation loss per canvas row segment
   size_t total;
-  int nseg;   // 64 KiB statistics segments per row
-  int nseg2;  // 32 KiB half segments per row (partials are strided by this)
+  int nseg2;  // 32 KiB segments per row (partials are strided by this)
   int R;
 };
 
@@ -134,7 +119,6 @@ inline FilterLayout filter_layout(int B, int V, int max_k, int dtype) {
 
 inline WsLayout ws_layout(int B, int V, int max_k, int dtype) {
   WsLayout L;
-  L.nseg = num_segments(V, dtype);
   L.nseg2 = num_sample_segments(V, dtype);
   L.R = rows_per_request(max_k);
   L.ctrl = 0;
@@ -148,7 +132,7 @@ inline WsLayout ws_layout(int B, int V, int max_k, int dtype) {
 }
 
 struct VerifyArgs {
-  int B, V, max_k, nseg, nseg2, R;
+  int B, V, max_k, nseg2, R;
   const void* draft;
   const int64_t* draft_start;
   int64_t draft_stride;
@@ -177,22 +161,10 @@ struct VerifyArgs {
   uint32_t spin_limit;  // polls of a bounded wait before it gives up
 };
 
-struct ScoreArgs {
-  int B, V, max_k, nseg, R;
-  const void* draft;
-  const int64_t* draft_start;
-  int64_t draft_stride;
-  const int32_t* num_draft;
-  const float* temperature;
-  const float* params;
-  float threshold;
-  float* feature;
-  float* score;
-  int32_t* num_kept;
-  uint32_t* tickets;
-  Partial* partials;
-};
 
+// The estimator's scoring pass: statistics of the draft rows into the
+// workspace, then feature, score and kept count per request.
+hipError_t launch_score(VerifyArgs a, float threshold, int32_t* num_kept, int dtype, hipStream_t stream);
 // The two streaming kernels (statistics, then the verdict and the draw).
 hipError_t launch_streaming(VerifyArgs a, int dtype, hipStream_t stream);
 // The statistics kernel alone (segment statistics and logits at the draft
@@ -219,7 +191,6 @@ struct FilterIO {
   float* slices;
 };
 hipError_t launch_filtered(VerifyArgs a, const FilterIO& io, int dtype, hipStream_t stream);
-hipError_t launch_av_score(const ScoreArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_av_budget(int B, int max_k, const float* score, const int32_t* num_draft, const float* draft_cost,
                             const float* verify_cost, int32_t* num_kept, int32_t* budget, hipStream_t stream);
 hipError_t launch_calib_accumulate(int items, const float* score, const int8_t* labels, double* accum,
