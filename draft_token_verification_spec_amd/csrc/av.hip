@@ -29,18 +29,6 @@ namespace sv {
 constexpr int kFitT = 256;  // threads of the refit (1024 measured slower: binary64-bound)
 constexpr int kFitW = kFitT / 64;
 
-__device__ __forceinline__ double sigmoid_d(double t) {
-  if (t >= 0.0) return 1.0 / (1.0 + exp(-t));
-  const double e = exp(t);
-  return e / (1.0 + e);
-}
-
-__device__ __forceinline__ double wave_sum_d(double v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-
 __global__ __launch_bounds__(kFitT) void av_fit_kernel(int B, int max_k, const float* feature,
                                                        const int8_t* labels, float* params, double* accum,
                                                        float damping_c, float ridge, float max_step, int do_update) {
@@ -69,19 +57,8 @@ __global__ __launch_bounds__(kFitT) void av_fit_kernel(int B, int max_k, const f
 #pragma unroll
     for (int i = 0; i < SV_MAX_K; ++i) {
       if (i >= max_k) continue;  // uniform
-      double v[6] = {0, 0, 0, 0, 0, 0};
-      if (y[i] == 0 || y[i] == 1) {
-        const double xd = x[i];
-        const double pi = sigmoid_d(omega * xd + beta[i]);
-        const double w = pi * (1.0 - pi);
-        const double r = pi - double(y[i]);
-        v[0] = 1.0;
-        v[1] = w;
-        v[2] = w * xd;
-        v[3] = w * xd * xd;
-        v[4] = r;
-        v[5] = r * xd;
-      }
+      double v[6];
+      fit_item(omega, beta[i], x[i], y[i], v);
 #pragma unroll
       for (int k = 0; k < 6; ++k) v[k] = wave_sum_d(v[k]);
       if (lane == 0)
@@ -100,44 +77,7 @@ __global__ __launch_bounds__(kFitT) void av_fit_kernel(int B, int max_k, const f
   }
   __syncthreads();
   if (!do_update) return;
-  if (tid == 0) {
-    double N = 0.0, h = ridge, gw = 0.0;
-    for (int i = 0; i < max_k; ++i) {
-      N += acc[i][0];
-      h += acc[i][3];
-      gw += acc[i][5];
-    }
-    if (N > 0.0) {
-      // eliminate the intercepts of positions with labels
-      double schur = h, rhs = -gw;
-      for (int i = 0; i < max_k; ++i) {
-        const double n = acc[i][0];
-        if (n <= 0.0) continue;
-        const double D = acc[i][1] + ridge, Bi = acc[i][2], gb = acc[i][4];
-        schur -= Bi * Bi / D;
-        rhs += Bi * gb / D;
-      }
-      const double dw = (schur > 0.0) ? rhs / schur : 0.0;
-      // damped steps, then the whole step scaled so that no parameter moves
-      // by more than max_step (far from the optimum, or for a position whose
-      // labels all agree, the Newton step on the logistic loss overshoots)
-      double step[SV_MAX_K + 1];
-      step[0] = dw * (N / (N + double(damping_c)));
-      double largest = fabs(step[0]);
-      for (int i = 0; i < max_k; ++i) {
-        const double n = acc[i][0];
-        step[1 + i] = 0.0;
-        if (n <= 0.0) continue;
-        const double D = acc[i][1] + ridge, Bi = acc[i][2], gb = acc[i][4];
-        step[1 + i] = ((-gb - Bi * dw) / D) * (n / (n + double(damping_c)));
-        largest = fmax(largest, fabs(step[1 + i]));
-      }
-      const double shrink = largest > double(max_step) ? double(max_step) / largest : 1.0;
-      params[0] = float(omega + step[0] * shrink);
-      for (int i = 0; i < max_k; ++i)
-        if (acc[i][0] > 0.0) params[1 + i] = float(double(params[1 + i]) + step[1 + i] * shrink);
-    }
-  }
+  if (tid == 0) fit_update_params(acc, max_k, params, damping_c, ridge, max_step);
   __syncthreads();
   for (int k = tid; k < 6 * max_k; k += kFitT) accum[k] = 0.0;
 }

@@ -188,6 +188,7 @@ __device__ __forceinline__ int load_dev(const int* p) {
   return __hip_atomic_load(const_cast<int*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+
 // Arrival counter.  Thread 0 of every workgroup of a request has published
 // its results (device-scope stores above); it waits until they are complete,
 // then takes a ticket.  The workgroup taking the last ticket (want - 1)
@@ -227,6 +228,91 @@ __device__ __forceinline__ float feature_from_other(float so) {
 __device__ __forceinline__ float sigmoid_score(const float* params, int i, float x) {
   const float t = params[0] * x + params[1 + i];
   return 1.f / (1.f + fast_exp2(-t * kLog2e));
+}
+
+// ---------------------------------------------------------------------------
+// the estimator's refit: per-item sums and the damped Newton update
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ double sigmoid_d(double t) {
+  if (t >= 0.0) return 1.0 / (1.0 + exp(-t));
+  const double e = exp(t);
+  return e / (1.0 + e);
+}
+
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// The six sums of one labelled draft (label y in {0, 1}, feature x) at
+// parameters (omega, beta_i): n, w, w x, w x^2, r, r x with
+// pi = sigmoid(omega x + beta_i), w = pi (1 - pi), r = pi - y; zeros for
+// any other label.
+__device__ __forceinline__ void fit_item(double omega, double beta_i, float x, int y, double (&v)[6]) {
+#pragma unroll
+  for (int k = 0; k < 6; ++k) v[k] = 0.0;
+  if (y == 0 || y == 1) {
+    const double xd = x;
+    const double pi = sigmoid_d(omega * xd + beta_i);
+    const double w = pi * (1.0 - pi);
+    const double r = pi - double(y);
+    v[0] = 1.0;
+    v[1] = w;
+    v[2] = w * xd;
+    v[3] = w * xd * xd;
+    v[4] = r;
+    v[5] = r * xd;
+  }
+}
+
+// The round's update from its accumulated sums acc[i][k] (one thread): solve
+// the arrowhead system H delta = -g over the slope and the intercepts of
+// positions with labels by eliminating the intercepts (Schur complement on
+// the slope), damp each step by n / (n + damping_c), scale the whole step so
+// that no parameter moves by more than max_step, and add it to params.  A
+// round without labels leaves params unchanged.
+__device__ __forceinline__ void fit_update_params(const double (*acc)[6], int max_k, float* params, float damping_c,
+                                                  float ridge, float max_step) {
+  const double omega = params[0];
+  double N = 0.0, h = ridge, gw = 0.0;
+  for (int i = 0; i < max_k; ++i) {
+    N += acc[i][0];
+    h += acc[i][3];
+    gw += acc[i][5];
+  }
+  if (!(N > 0.0)) return;
+  double schur = h, rhs = -gw;
+  for (int i = 0; i < max_k; ++i) {
+    const double n = acc[i][0];
+    if (n <= 0.0) continue;
+    const double D = acc[i][1] + ridge, Bi = acc[i][2], gb = acc[i][4];
+    schur -= Bi * Bi / D;
+    rhs += Bi * gb / D;
+  }
+  const double dw = (schur > 0.0) ? rhs / schur : 0.0;
+  // damped steps, then the whole step scaled so that no parameter moves by
+  // more than max_step (far from the optimum, or for a position whose labels
+  // all agree, the Newton step on the logistic loss overshoots); each
+  // intercept's step is formed twice (for the bound, then for the update)
+  // rather than kept in an array indexed at run time
+  const double step_w = dw * (N / (N + double(damping_c)));
+  double largest = fabs(step_w);
+  for (int i = 0; i < max_k; ++i) {
+    const double n = acc[i][0];
+    if (n <= 0.0) continue;
+    const double D = acc[i][1] + ridge, Bi = acc[i][2], gb = acc[i][4];
+    largest = fmax(largest, fabs(((-gb - Bi * dw) / D) * (n / (n + double(damping_c)))));
+  }
+  const double shrink = largest > double(max_step) ? double(max_step) / largest : 1.0;
+  params[0] = float(omega + step_w * shrink);
+  for (int i = 0; i < max_k; ++i) {
+    const double n = acc[i][0];
+    if (n <= 0.0) continue;
+    const double D = acc[i][1] + ridge, Bi = acc[i][2], gb = acc[i][4];
+    params[1 + i] = float(double(params[1 + i]) + ((-gb - Bi * dw) / D) * (n / (n + double(damping_c))) * shrink);
+  }
 }
 
 }  // namespace sv
