@@ -94,7 +94,9 @@ def summarize_counters(args):
         mib = args.copy_calibration or 512
         scale[counter] = mib * 1024.0 / (sum(cal) / len(cal))
         for r in rows:
-            m = re.search(r"sv::(?:\(anonymous namespace\)::)?(\w+)", r["Kernel_Name"])
+            # the library's kernels, and the read probe of the measurement library
+            m = (re.search(r"sv::(?:\(anonymous namespace\)::)?(\w+)", r["Kernel_Name"])
+                 or re.search(r"(read_probe_kernel)", r["Kernel_Name"]))
             if m and "copyBuffer" not in r["Kernel_Name"]:
                 per.setdefault(m.group(1), {}).setdefault(counter, []).append(float(r["Counter_Value"]))
     out = {}
