@@ -23,8 +23,8 @@ Prints one JSON line:
                         graph of back-to-back calls timed with HIP events on
                         the launching stream, against the 8 TB/s HBM3E peak;
                         traffic: the HBM bytes rocprofv3 counters measured
-                        for the same kernels (profiles/traffic.json), if they
-                        describe the current kernel sources;
+                        for the same kernels (profiles/traffic_<workload>.json),
+                        if they describe the current kernel sources;
   parity                the GPU's outputs for input set 0 against the CPU
                         oracle's for the requests the oracle baseline ran;
   cpu_baseline          the oracle, untuned, on the host's cores over a
@@ -47,6 +47,15 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "verified draft positions/sec at B=256,K=4,V=128256 bf16; achieved HBM GB/s"
+
+
+def metric_name(wl) -> str:
+    """The headline metric for the default workload; for another workload the
+    same metric at its own shape."""
+    k = f"1..{wl.max_k}" if wl.ragged else str(wl.max_k)
+    dt = "bf16" if wl.dtype == "bf16" else "fp32"
+    name = f"verified draft positions/sec at B={wl.B},K={k},V={wl.V} {dt}; achieved HBM GB/s"
+    return METRIC if name.split(";")[0] == METRIC.split(";")[0] else name
 PEAK_HBM_GBS = 8000.0
 MARGIN = 1e-5  # parity: decisions closer than this to their threshold may flip
 
@@ -61,15 +70,19 @@ def parse_args(argv=None):
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extra", action="store_true", help="time the step and the call only")
-    p.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
-                   help="per-launch HBM bytes measured with rocprofv3 counters (optional)")
+    p.add_argument("--traffic", default=None,
+                   help="per-launch HBM bytes measured with rocprofv3 counters (optional; default "
+                        "profiles/traffic_<workload>.json)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="after timing, copy a MIB-sized device buffer 3 times (reference for HBM counters)")
     p.add_argument("--counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="no GPU work: turn the counter_collection.csv files of a FETCH_SIZE and a WRITE_SIZE "
                         "rocprofv3 pass (run with --copy-calibration) into per-launch HBM bytes, print them and "
                         "store them in --traffic")
-    return p.parse_args(argv)
+    args = p.parse_args(argv)
+    if args.traffic is None:
+        args.traffic = os.path.join(ROOT, "profiles", f"traffic_{args.workload}.json")
+    return args
 
 
 # ---------------------------------------------------------------------------
@@ -107,7 +120,10 @@ def summarize_counters(args):
                   "bytes_per_launch": f + w}
         print(f"{k:24s} {len(d['FETCH_SIZE']):3d} dispatches  fetch {f / 1e6:9.2f} MB  write {w / 1e6:8.2f} MB")
     print(f"scales: FETCH_SIZE x{scale['FETCH_SIZE']:.5f}, WRITE_SIZE x{scale['WRITE_SIZE']:.5f}")
-    call = [k for k in CALL_KERNELS if k in out]
+    from synth import workload
+
+    kernels = (SCORE_KERNELS if workload(args.workload).prune_threshold > 0.0 else ()) + CALL_KERNELS
+    call = [k for k in kernels if k in out]
     rec = {"workload": args.workload, "kernels_of_the_call": call,
            "bytes_per_call": sum(out[k]["bytes_per_launch"] for k in call),
            "fetch_scale": scale["FETCH_SIZE"], "write_scale": scale["WRITE_SIZE"], "kernels": out,
@@ -117,8 +133,10 @@ def summarize_counters(args):
         fh.write("\n")
 
 
-# the kernels one sv_spec_verify call launches
+# the kernels one sv_spec_verify call launches, and those of the scoring pass
+# that precedes it in a pruning workload's step
 CALL_KERNELS = ("stats_kernel", "draw_kernel")
+SCORE_KERNELS = ("score_stats_kernel", "score_finish_kernel")
 
 
 def kernel_source_hash() -> str:
@@ -513,12 +531,13 @@ def main(argv=None):
                               for i in range(len(sets))]))
 
     value = positions / (ms_per_step * 1e-3)
-    kernels = "av_score_kernel + stats_kernel + draw_kernel" if pruning else "stats_kernel + draw_kernel"
+    kernels = ("score_stats_kernel + score_finish_kernel + stats_kernel + draw_kernel" if pruning
+               else "stats_kernel + draw_kernel")
     rl = roofline(call_alg, call_ms, stored_traffic(args), kernel=("sv_av_score + " if pruning else "")
                   + "sv_spec_verify call (" + kernels + ")",
                   note="call time from a graph of back-to-back calls over the rotated input sets")
     res = {
-        "metric": METRIC,
+        "metric": metric_name(gen.workload(args.workload)),
         "value": value,
         "unit": "positions/s",
         "n_gpus": 1,
@@ -599,7 +618,8 @@ def extras(args, res, sv, sets, batches, outs, params, ws, call, dev, log):
                        prune_threshold=0.3, workspace=ws, out=s)
 
     ms, _ = graph_ms(rot(score_only), 20, dev)
-    ex["av_score"] = roofline(score_bytes(b0), ms, kernel="av_score_kernel", prune_threshold=0.3)
+    ex["av_score"] = roofline(score_bytes(b0), ms, kernel="score_stats_kernel + score_finish_kernel",
+                              prune_threshold=0.3)
 
     # read-bandwidth probe over a buffer of the verification's size: the
     # statistics kernel's access pattern with no arithmetic
