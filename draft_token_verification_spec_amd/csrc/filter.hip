@@ -453,7 +453,8 @@ __global__ __launch_bounds__(kS0) void filt_select0_kernel(FiltArgs a) {
   if (!row_filtered(a, f, rs)) return;
   const size_t row = size_t(b) * R + rs;
   const int j = tid;
-  uint32_t cnt = 0, frac = 0;
+  uint32_t cnt = 0;
+  uint64_t frac = 0;  // up to V x 92840: beyond 32 bits for long runs of equal logits
 #pragma unroll 8
   for (int s = 0; s < n; ++s) {
     cnt += a.hcount[(row * n + s) * 2 * kBins0 + j];

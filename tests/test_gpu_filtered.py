@@ -229,6 +229,43 @@ def test_ties_uniform_rows_neg_inf_and_signed_zeros():
     assert np.all(gout["kept"][0] == V)
 
 
+def test_long_runs_of_equal_logits_above_the_boundary():
+    """60000 equal logits in one level-0 bin above the top-p boundary: that
+    bin's fraction sum over the row needs more than 32 bits (a 32-bit sum
+    wraps and corrupts the mass above the boundary)."""
+    V, K = 128000, 1
+    zd = np.full((2, K, V), -0.4, np.float32)
+    zt = np.full((2, K + 1, V), -0.4, np.float32)
+    zd[:, :, :60000] = 0.6
+    zt[:, :, 30000:90000] = 0.6
+    toks = np.array([[5], [100000]])
+    for dtype in ("f32", "bf16"):
+        b = _batch(zd, zt, toks, 1.0, 0, 0.99, dtype=dtype)
+        _log(f"case filtered equal runs {dtype}")
+        gout, o = _run(b)
+        assert compare_filtered(b, gout, o) == 0
+        assert np.all(gout["kept"][:, [0, 1, 2]] == V)
+
+
+def test_segment_maxima_far_apart():
+    """Segments whose maxima lie hundreds of level-0 bins apart: some
+    wholly in the last bin, one without a finite logit, and in request 1
+    the row maximum outside the first segment."""
+    g = np.random.default_rng(23)
+    B, K, V = 4, 2, 131072
+    seg = 8192  # fp32 elements per 32 KiB segment
+    offs = -3.0 * (np.arange(V) // seg)  # 16 segments, each ~69 bins below the previous at T = 1
+    zd = (g.normal(0, 1.0, (B, K, V)) + offs).astype(np.float32)
+    zt = (g.normal(0, 1.0, (B, K + 1, V)) + offs).astype(np.float32)
+    zd[:, :, 3 * seg:4 * seg] = -np.inf
+    zt[1, :, :seg] -= 40.0  # request 1: the maxima in the second segment
+    for top_k, top_p, T in [(0, 0.999, 1.0), (20000, 1.0, 1.0), (0, 0.9999999, 0.25), (5000, 0.99, 4.0)]:
+        b = _batch(zd, zt, _draws(zd, T, 7), T, top_k, top_p)
+        _log(f"case filtered far segments k={top_k} p={top_p} T={T}")
+        gout, o = _run(b)
+        assert compare_filtered(b, gout, o) <= 1
+
+
 def test_temperatures_max_draft_length_and_largest_vocabulary():
     g = np.random.default_rng(2)
     B, K, V = 3, 16, 4096
