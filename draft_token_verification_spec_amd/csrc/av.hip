@@ -16,68 +16,71 @@
 namespace sv {
 
 // ---------------------------------------------------------------------------
-// refit step: one workgroup of 256 threads.  Thread t takes requests
-// b = t, t + 256, ..., loading all of a request's labels and features at
-// once; per position the six sums are formed in fp64, reduced per wave
-// (butterfly) into LDS and then over the waves in order, a fixed order that
-// makes the result deterministic.  On the round's last step thread 0 solves the arrowhead
-// Newton system H * delta = -g by eliminating the intercepts (Schur
-// complement on the slope), damps, bounds the step, updates the parameters
-// and clears the accumulator.
+// refit step: one workgroup of 256 threads.  The batch's labelled drafts are
+// items b * max_k + i; the first T = max_k * floor(256 / max_k) threads take
+// items t, t + T, ... (coalesced loads), so that every item a thread takes
+// belongs to the same position i = t mod max_k, and the thread keeps that
+// position's six sums, formed in fp64, in registers.  The threads' sums then
+// go to LDS and are added per position and sum in thread order, a fixed
+// order that makes the result deterministic.  On the round's last step the
+// first max_k threads solve the arrowhead Newton system H * delta = -g by
+// eliminating the intercepts (Schur complement on the slope), damp, bound
+// the step, update the parameters and clear the accumulator.
 // ---------------------------------------------------------------------------
 
-constexpr int kFitT = 256;  // threads of the refit (1024 measured slower: binary64-bound)
-constexpr int kFitW = kFitT / 64;
+constexpr int kFitT = 256;
 
 __global__ __launch_bounds__(kFitT) void av_fit_kernel(int B, int max_k, const float* feature,
                                                        const int8_t* labels, float* params, double* accum,
                                                        float damping_c, float ridge, float max_step, int do_update) {
-  __shared__ double red[kFitW][SV_MAX_K][6];  // per wave and position, summed over the chunks in order
-  __shared__ double acc[SV_MAX_K][6];          // accumulator after this step
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  // parameters and the incoming accumulator with the first chunk's items:
-  // one round trip to memory instead of one per position
+  __shared__ double part[6][kFitT];          // per thread, by sum
+  __shared__ double acc[SV_MAX_K][6];        // accumulator after this step
+  __shared__ FitShared fsh;
+  const int tid = threadIdx.x;
+  const int T = (kFitT / max_k) * max_k;  // threads taking items (max_k >= 1)
+  const int pos = tid % max_k;
+  // parameters and the incoming accumulator with the first items: one round
+  // trip to memory instead of one per item
   const double omega = params[0];
-  double beta[SV_MAX_K];
-#pragma unroll
-  for (int i = 0; i < SV_MAX_K; ++i) beta[i] = i < max_k ? double(params[1 + i]) : 0.0;
+  const double beta = params[1 + pos];
   const double acc_in = tid < 6 * max_k ? accum[tid] : 0.0;
-  for (int e = tid; e < kFitW * SV_MAX_K * 6; e += kFitT) (&red[0][0][0])[e] = 0.0;
-  __syncthreads();
-  for (int b0 = 0; b0 < B; b0 += kFitT) {
-    const int b = b0 + tid;
-    int y[SV_MAX_K];
-    float x[SV_MAX_K];
+  double sum[6] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+  if (tid < T) {
+    const int n = B * max_k;
+    // kChunk items per thread in flight: their loads are issued together
+    constexpr int kChunk = 8;
+    for (int it0 = tid; it0 < n; it0 += kChunk * T) {
+      float x[kChunk];
+      int y[kChunk];
 #pragma unroll
-    for (int i = 0; i < SV_MAX_K; ++i) {
-      const bool in = b < B && i < max_k;
-      y[i] = in ? labels[size_t(b) * max_k + i] : -1;
-      x[i] = in ? feature[size_t(b) * max_k + i] : 0.f;
-    }
+      for (int c = 0; c < kChunk; ++c) {
+        const int it = it0 + c * T;
+        x[c] = it < n ? feature[it] : 0.f;
+        y[c] = it < n ? labels[it] : -1;
+      }
 #pragma unroll
-    for (int i = 0; i < SV_MAX_K; ++i) {
-      if (i >= max_k) continue;  // uniform
-      double v[6];
-      fit_item(omega, beta[i], x[i], y[i], v);
+      for (int c = 0; c < kChunk; ++c) {
+        double v[6];
+        fit_item(omega, beta, x[c], y[c], v);
 #pragma unroll
-      for (int k = 0; k < 6; ++k) v[k] = wave_sum_d(v[k]);
-      if (lane == 0)
-#pragma unroll
-        for (int k = 0; k < 6; ++k) red[wave][i][k] += v[k];
+        for (int k = 0; k < 6; ++k) sum[k] += v[k];
+      }
     }
   }
+#pragma unroll
+  for (int k = 0; k < 6; ++k) part[k][tid] = sum[k];
   __syncthreads();
   if (tid < 6 * max_k) {
     const int i = tid / 6, k = tid % 6;
-    double t = red[0][i][k];
-    for (int w = 1; w < kFitW; ++w) t += red[w][i][k];
+    double t = 0.0;
+    for (int u = i; u < T; u += max_k) t += part[k][u];
     t += acc_in;
     acc[i][k] = t;
     if (!do_update) accum[tid] = t;
   }
   __syncthreads();
   if (!do_update) return;
-  if (tid == 0) fit_update_params(acc, max_k, params, damping_c, ridge, max_step);
+  fit_update_params(acc, max_k, params, damping_c, ridge, max_step, fsh, tid);
   __syncthreads();
   for (int k = tid; k < 6 * max_k; k += kFitT) accum[k] = 0.0;
 }

@@ -267,52 +267,68 @@ __device__ __forceinline__ void fit_item(double omega, double beta_i, float x, i
   }
 }
 
-// The round's update from its accumulated sums acc[i][k] (one thread): solve
+// The round's update from its accumulated sums acc[i][k], by the first
+// max_k threads of a workgroup (every thread of the workgroup calls it): solve
 // the arrowhead system H delta = -g over the slope and the intercepts of
 // positions with labels by eliminating the intercepts (Schur complement on
 // the slope), damp each step by n / (n + damping_c), scale the whole step so
-// that no parameter moves by more than max_step, and add it to params.  A
-// round without labels leaves params unchanged.
+// that no parameter moves by more than max_step, and add it to params.
+// Thread i forms position i's terms; thread 0 adds them in position order.
+// A round without labels leaves params unchanged.
+struct FitShared {
+  double term[SV_MAX_K][5];  // n, the slope's Hessian and gradient terms, Schur and right-hand-side terms
+  double step[SV_MAX_K];     // damped intercept steps
+  double dw, step_w, shrink;
+  int any;
+};
+
 __device__ __forceinline__ void fit_update_params(const double (*acc)[6], int max_k, float* params, float damping_c,
-                                                  float ridge, float max_step) {
-  const double omega = params[0];
-  double N = 0.0, h = ridge, gw = 0.0;
-  for (int i = 0; i < max_k; ++i) {
-    N += acc[i][0];
-    h += acc[i][3];
-    gw += acc[i][5];
+                                                  float ridge, float max_step, FitShared& sh, int tid) {
+  const double c = damping_c;
+  double n = 0.0, D = 1.0, Bi = 0.0, gb = 0.0;
+  if (tid < max_k) {
+    n = acc[tid][0];
+    D = acc[tid][1] + ridge;
+    Bi = acc[tid][2];
+    gb = acc[tid][4];
+    const bool has = n > 0.0;
+    sh.term[tid][0] = n;
+    sh.term[tid][1] = acc[tid][3];
+    sh.term[tid][2] = acc[tid][5];
+    sh.term[tid][3] = has ? Bi * Bi / D : 0.0;
+    sh.term[tid][4] = has ? Bi * gb / D : 0.0;
   }
-  if (!(N > 0.0)) return;
-  double schur = h, rhs = -gw;
-  for (int i = 0; i < max_k; ++i) {
-    const double n = acc[i][0];
-    if (n <= 0.0) continue;
-    const double D = acc[i][1] + ridge, Bi = acc[i][2], gb = acc[i][4];
-    schur -= Bi * Bi / D;
-    rhs += Bi * gb / D;
+  __syncthreads();
+  if (tid == 0) {
+    double N = 0.0, h = ridge, gw = 0.0, sch = 0.0, r = 0.0;
+    for (int i = 0; i < max_k; ++i) {
+      N += sh.term[i][0];
+      h += sh.term[i][1];
+      gw += sh.term[i][2];
+      sch += sh.term[i][3];
+      r += sh.term[i][4];
+    }
+    const double schur = h - sch, rhs = r - gw;
+    const double dw = (schur > 0.0) ? rhs / schur : 0.0;
+    sh.any = N > 0.0;
+    sh.dw = dw;
+    sh.step_w = dw * (N / (N + c));
   }
-  const double dw = (schur > 0.0) ? rhs / schur : 0.0;
+  __syncthreads();
+  if (!sh.any) return;
   // damped steps, then the whole step scaled so that no parameter moves by
   // more than max_step (far from the optimum, or for a position whose labels
-  // all agree, the Newton step on the logistic loss overshoots); each
-  // intercept's step is formed twice (for the bound, then for the update)
-  // rather than kept in an array indexed at run time
-  const double step_w = dw * (N / (N + double(damping_c)));
-  double largest = fabs(step_w);
-  for (int i = 0; i < max_k; ++i) {
-    const double n = acc[i][0];
-    if (n <= 0.0) continue;
-    const double D = acc[i][1] + ridge, Bi = acc[i][2], gb = acc[i][4];
-    largest = fmax(largest, fabs(((-gb - Bi * dw) / D) * (n / (n + double(damping_c)))));
+  // all agree, the Newton step on the logistic loss overshoots)
+  if (tid < max_k) sh.step[tid] = n > 0.0 ? ((-gb - Bi * sh.dw) / D) * (n / (n + c)) : 0.0;
+  __syncthreads();
+  if (tid == 0) {
+    double largest = fabs(sh.step_w);
+    for (int i = 0; i < max_k; ++i) largest = fmax(largest, fabs(sh.step[i]));
+    sh.shrink = largest > double(max_step) ? double(max_step) / largest : 1.0;
   }
-  const double shrink = largest > double(max_step) ? double(max_step) / largest : 1.0;
-  params[0] = float(omega + step_w * shrink);
-  for (int i = 0; i < max_k; ++i) {
-    const double n = acc[i][0];
-    if (n <= 0.0) continue;
-    const double D = acc[i][1] + ridge, Bi = acc[i][2], gb = acc[i][4];
-    params[1 + i] = float(double(params[1 + i]) + ((-gb - Bi * dw) / D) * (n / (n + double(damping_c))) * shrink);
-  }
+  __syncthreads();
+  if (tid == 0) params[0] = float(double(params[0]) + sh.step_w * sh.shrink);
+  if (tid < max_k && n > 0.0) params[1 + tid] = float(double(params[1 + tid]) + sh.step[tid] * sh.shrink);
 }
 
 }  // namespace sv
