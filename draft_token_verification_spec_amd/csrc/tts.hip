@@ -10,9 +10,9 @@
 // softmax(logits / T) (T = 0 counting as 1).
 //
 // One workgroup per canvas position: a statistics pass (online max and sum
-// of exp2 per row, each thread over its share, then the workgroup) and a
-// gradient pass over the same rows, 16 elements per row and thread in flight
-// per step.  HBM-bound: the rows are read twice, the gradient row written
+// of exp2 per row, each thread over its share, then the workgroup; 32
+// elements per row and thread in flight per step) and a gradient pass over
+// the same rows (16 per row and thread per step).  HBM-bound: the rows are read twice, the gradient row written
 // once.
 #include "sv_device.hpp"
 
@@ -22,39 +22,44 @@ namespace {
 
 constexpr int kTT = 256;  // threads
 // 16-byte vectors per row and thread per step: 16 elements of either type
+// in the gradient pass, 32 in the statistics pass (which holds no gradient)
 template <typename ET>
 constexpr int kTV = 16 / Elem<ET>::N;
+template <typename ET>
+constexpr int kTVS = 32 / Elem<ET>::N;
 constexpr float kLn2 = 0.6931471805599453f;
 
 // Vectors base/N + k * kTT + t (k < kTV) of a row for thread t: elements
 // base + (k * kTT + t) * N .. + N - 1; past V: -inf.
-template <typename ET>
-__device__ __forceinline__ void load_step(const ET* row, int base, int V, uint4 (&v)[kTV<ET>], int tid) {
+// The rows are streamed (non-temporal loads): the two passes over a row
+// are too far apart for the caches to keep it.
+template <typename ET, int TV>
+__device__ __forceinline__ void load_step(const ET* row, int base, int V, uint4 (&v)[TV], int tid) {
   constexpr int N = Elem<ET>::N;
   const bool al = is_aligned16(row);
-  if (al && base + kTT * kTV<ET> * N <= V) {
+  if (al && base + kTT * TV * N <= V) {
 #pragma unroll
-    for (int k = 0; k < kTV<ET>; ++k) v[k] = load_vec16<ET>(row + base + (k * kTT + tid) * N);
+    for (int k = 0; k < TV; ++k) v[k] = load_stream16(row + base + (k * kTT + tid) * N);
   } else {
 #pragma unroll
-    for (int k = 0; k < kTV<ET>; ++k) v[k] = load_raw<ET>(row, base + (k * kTT + tid) * N, V, al);
+    for (int k = 0; k < TV; ++k) v[k] = load_raw<ET>(row, base + (k * kTT + tid) * N, V, al);
   }
 }
 
 // Online (max, sum of exp2((z - max) * c)) of one thread's elements.
-template <typename ET>
-__device__ __forceinline__ void online(const uint4 (&v)[kTV<ET>], float c, float& m, float& s) {
+template <typename ET, int TV>
+__device__ __forceinline__ void online(const uint4 (&v)[TV], float c, float& m, float& s) {
   constexpr int N = Elem<ET>::N;
   float mx = -INFINITY;
 #pragma unroll
-  for (int k = 0; k < kTV<ET>; ++k)
+  for (int k = 0; k < TV; ++k)
 #pragma unroll
     for (int j = 0; j < N; ++j) mx = fmaxf(mx, Elem<ET>::get(v[k], j));
   if (mx == -INFINITY) return;
   const float mn = fmaxf(m, mx);
   float acc = (m == -INFINITY) ? 0.f : s * fast_exp2((m - mn) * c);
 #pragma unroll
-  for (int k = 0; k < kTV<ET>; ++k)
+  for (int k = 0; k < TV; ++k)
 #pragma unroll
     for (int j = 0; j < N; ++j) acc += fast_exp2(fmaf(Elem<ET>::get(v[k], j), c, -mn * c));
   m = mn;
@@ -178,18 +183,19 @@ __device__ __forceinline__ void tts_position(const TtsArgs& a, const ET* rd, con
   // partials of the draft and target rows and a pass over q_t's rows only
   float md = -INFINITY, sd = 0.f, mt = -INFINITY, st = 0.f, mp = -INFINITY, sp = 0.f;
   if (!REUSE || PREV) {
-    for (int base = 0; base < V; base += STEP) {
-      uint4 vd[TV], vt[TV], vp[TV];
+    constexpr int TS = kTVS<ET>;
+    for (int base = 0; base < V; base += kTT * TS * N) {
+      uint4 vd[TS], vt[TS], vp[TS];
       if (!REUSE) {
-        load_step<ET>(rd, base, V, vd, tid);
-        load_step<ET>(rt, base, V, vt, tid);
+        load_step<ET, TS>(rd, base, V, vd, tid);
+        load_step<ET, TS>(rt, base, V, vt, tid);
       }
-      if (PREV) load_step<ET>(rp, base, V, vp, tid);
+      if (PREV) load_step<ET, TS>(rp, base, V, vp, tid);
       if (!REUSE) {
-        online<ET>(vd, c, md, sd);
-        online<ET>(vt, c, mt, st);
+        online<ET, TS>(vd, c, md, sd);
+        online<ET, TS>(vt, c, mt, st);
       }
-      if (PREV) online<ET>(vp, c, mp, sp);
+      if (PREV) online<ET, TS>(vp, c, mp, sp);
     }
   }
   float kd, kt;
@@ -208,9 +214,9 @@ __device__ __forceinline__ void tts_position(const TtsArgs& a, const ET* rd, con
   float loss = 0.f;
   for (int base = 0; base < V; base += STEP) {
     uint4 vd[TV], vt[TV], vp[TV];
-    load_step<ET>(rd, base, V, vd, tid);
-    load_step<ET>(rt, base, V, vt, tid);
-    if (PREV) load_step<ET>(rp, base, V, vp, tid);
+    load_step<ET, TV>(rd, base, V, vd, tid);
+    load_step<ET, TV>(rt, base, V, vt, tid);
+    if (PREV) load_step<ET, TV>(rp, base, V, vp, tid);
 #pragma unroll
     for (int k = 0; k < TV; ++k) {
       float gv[N];
