@@ -9,7 +9,8 @@
 //
 // A batch holds at most SV_BUDGET_MAX_ITEMS positions (a serving batch times
 // its drafts), so the whole decision fits one workgroup and its LDS: the
-// survivals are formed in place, sorted (bitonic, descending), summed in
+// survivals are formed in place, sorted (descending: each wave sorts a
+// sixteenth in registers, then four rounds of merges by rank), summed in
 // binary64 and scanned for the best ratio; the kept drafts are then every
 // survival above the cut plus, of those equal to it, the first ones in flat
 // order (request-major), which keeps each request's kept drafts a prefix.
@@ -24,10 +25,12 @@ constexpr int kBW = kBT / 64;  // waves
 static_assert((SV_BUDGET_MAX_ITEMS & (SV_BUDGET_MAX_ITEMS - 1)) == 0, "the sort size is a power of two");
 
 constexpr int kPer = SV_BUDGET_MAX_ITEMS / kBT;  // sorted elements per thread at most
+static_assert(kPer == 1 || kPer == 2 || kPer == 4, "the wave sort is instantiated for 1, 2 and 4");
 
 struct BudgetShared {
   float surv[SV_BUDGET_MAX_ITEMS];  // survivals in flat order (b * max_k + i)
-  float vals[SV_BUDGET_MAX_ITEMS];  // exchange buffer of the sort, then the ranked survivals
+  float vals[SV_BUDGET_MAX_ITEMS];  // the survivals being sorted, then the ranked survivals
+  float tmp[SV_BUDGET_MAX_ITEMS];   // the other buffer of the merge rounds
   double dpart[kBW];
   int ipart[kBW];
   double best_r[kBW];
@@ -79,13 +82,60 @@ __device__ __forceinline__ void row_survivals(const float* score, int b, int K, 
   }
 }
 
-// One compare-exchange step of the bitonic network (pair distance `stride`
-// within blocks of `size`, descending overall) on element e = k * kBT + tid,
-// whose value is x and whose partner (e ^ stride) holds y.
-__device__ __forceinline__ float bitonic_keep(float x, float y, int e, int stride, int size) {
-  const bool lower = (e & stride) == 0;
-  const bool desc = ((e & ~stride) & size) == 0;  // direction of the pair's block
-  return (lower == desc) ? fmaxf(x, y) : fminf(x, y);
+// Descending bitonic sort of one wave's chunk of 64 * PER values, value
+// k * 64 + lane of the chunk in v[k] of that lane: pairs closer than 64 are
+// exchanged between lanes, the others inside a thread.  No LDS, no barrier;
+// every stride is a compile-time constant.
+template <int PER, int SIZE, int STRIDE>
+__device__ __forceinline__ void sort_stage(float (&v)[kPer], int lane) {
+  if constexpr (STRIDE >= 64) {
+    constexpr int ks = STRIDE / 64;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      if ((k & ks) == 0) {
+        const float x = v[k], y = v[k | ks];
+        const bool desc = ((k * 64 + lane) & SIZE) == 0;
+        v[k] = desc ? fmaxf(x, y) : fminf(x, y);
+        v[k | ks] = desc ? fminf(x, y) : fmaxf(x, y);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int e = k * 64 + lane;
+      const float y = __shfl_xor(v[k], STRIDE, 64);
+      const bool lower = (e & STRIDE) == 0;
+      const bool desc = (e & SIZE) == 0;
+      v[k] = (lower == desc) ? fmaxf(v[k], y) : fminf(v[k], y);
+    }
+  }
+  if constexpr (STRIDE > 1) sort_stage<PER, SIZE, STRIDE / 2>(v, lane);
+}
+
+template <int PER, int SIZE>
+__device__ __forceinline__ void sort_sizes(float (&v)[kPer], int lane) {
+  sort_stage<PER, SIZE, SIZE / 2>(v, lane);
+  if constexpr (SIZE < 64 * PER) sort_sizes<PER, SIZE * 2>(v, lane);
+}
+
+template <int PER>
+__device__ __forceinline__ void wave_sort(float (&v)[kPer], int lane) {
+  sort_sizes<PER, 2>(v, lane);
+}
+
+// Entries of the descending run r[0..n-1] that come before x in the merged
+// order: those greater than x, and (if x is from the right run of the pair)
+// those equal to it.
+__device__ __forceinline__ int merge_rank(const float* r, int n, float x, bool right) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (right ? r[mid] >= x : r[mid] > x)
+      lo = mid + 1;
+    else
+      hi = mid;
+  }
+  return lo;
 }
 
 __global__ __launch_bounds__(kBT) void av_budget_kernel(int B, int max_k, const float* score,
@@ -117,48 +167,45 @@ __global__ __launch_bounds__(kBT) void av_budget_kernel(int B, int max_k, const 
   int N = 0;
   (void)block_exclusive<int>(mine, sh.ipart, N, tid);  // also orders the stores above
 
-  // rank: bitonic sort, descending.  Pairs at distance < 64 are exchanged
-  // between the lanes of a wave, pairs at distance >= kBT inside a thread,
-  // and only the distances in between go through LDS.
-  float v[kPer];
+  // rank: wave w sorts values [w * C, (w + 1) * C) (C = P / 16) in
+  // registers, then four rounds merge pairs of sorted runs: each value's
+  // place in the merged run is its place in its own run plus the number of
+  // values of the other run before it (found by bisection), so the rounds
+  // need no compare-exchange network and one barrier each
+  {
+    const int C = 64 * per;
+    float v[kPer];
 #pragma unroll
-  for (int k = 0; k < kPer; ++k) v[k] = k < per ? sh.vals[k * kBT + tid] : 0.f;
-  for (int size = 2; size <= P; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      if (stride >= kBT) {
-        const int ks = stride / kBT;
+    for (int k = 0; k < kPer; ++k) v[k] = k < per ? sh.vals[wave * C + k * 64 + lane] : 0.f;
+    if (per == 1)
+      wave_sort<1>(v, lane);
+    else if (per == 2)
+      wave_sort<2>(v, lane);
+    else
+      wave_sort<4>(v, lane);
 #pragma unroll
-        for (int k = 0; k < kPer; ++k) {
-          if (k < per && (k & ks) == 0) {
-            const int e = k * kBT + tid;
-            const float x = v[k], y = v[k | ks];
-            const bool desc = (e & size) == 0;
-            v[k] = desc ? fmaxf(x, y) : fminf(x, y);
-            v[k | ks] = desc ? fminf(x, y) : fmaxf(x, y);
-          }
+    for (int k = 0; k < kPer; ++k)
+      if (k < per) sh.vals[wave * C + k * 64 + lane] = v[k];
+    float* src = sh.vals;
+    float* dst = sh.tmp;
+    for (int L = C; L < P; L <<= 1) {
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) {
+        if (k < per) {
+          const int g = k * kBT + tid;
+          const int run = g / L, i = g - run * L;
+          const float x = src[g];
+          dst[(run & ~1) * L + i + merge_rank(src + (run ^ 1) * L, L, x, run & 1)] = x;
         }
-      } else if (stride < 64) {
-#pragma unroll
-        for (int k = 0; k < kPer; ++k)
-          if (k < per) v[k] = bitonic_keep(v[k], __shfl_xor(v[k], stride, 64), k * kBT + tid, stride, size);
-      } else {
-        __syncthreads();
-#pragma unroll
-        for (int k = 0; k < kPer; ++k)
-          if (k < per) sh.vals[k * kBT + tid] = v[k];
-        __syncthreads();
-#pragma unroll
-        for (int k = 0; k < kPer; ++k)
-          if (k < per) v[k] = bitonic_keep(v[k], sh.vals[(k * kBT + tid) ^ stride], k * kBT + tid, stride, size);
       }
+      float* t = src;
+      src = dst;
+      dst = t;
     }
+    __syncthreads();
+    // four rounds: the ranked survivals are back in sh.vals
   }
-  __syncthreads();
-#pragma unroll
-  for (int k = 0; k < kPer; ++k)
-    if (k < per) sh.vals[k * kBT + tid] = v[k];
-  __syncthreads();
-
   // estimated tokens per cost for j = 0..N kept drafts (binary64 sums over
   // the ranked survivals, in rank order within each thread's run)
   const int c = (N + kBT - 1) / kBT;
