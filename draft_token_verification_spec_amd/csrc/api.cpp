@@ -11,8 +11,8 @@ using namespace sv;
 
 namespace {
 
-// Work items of one call are numbered with 32-bit claim counters; the
-// scoring kernel's 1-D grid is limited to 2^32 - 1 threads.
+// The kernels number a call's workgroups (row segments) in 32 bits, and a
+// 1-D grid holds at most 2^32 - 1 threads.
 constexpr uint64_t kMaxItems = uint64_t(1) << 31;
 constexpr uint64_t kMaxGrid = (uint64_t(1) << 32) / kThreads - 1;
 

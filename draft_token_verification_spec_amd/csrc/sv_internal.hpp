@@ -48,10 +48,11 @@ struct Partial {
 // Byte offsets inside the caller's workspace.
 //
 // The workspace starts with a fixed arena - a control line holding the status
-// word, then a per-request-slot array of SV_MAX_B arrival counters (scoring
-// and distillation kernels) - which every call leaves zeroed (the status word
-// aside) and no call writes partial data into, whatever its shape.  After the
-// arena comes the per-call region, laid out for the call's (B, V, max_k).
+// word, then a per-request-slot array of SV_MAX_B arrival counters (the
+// distillation gradient's segmented kernel) - which every call leaves zeroed
+// (the status word aside) and no call writes partial data into, whatever its
+// shape.  After the arena comes the per-call region, laid out for the call's
+// (B, V, max_k).
 constexpr int kLineWords = 32;    // 128 bytes: one counter per cache line
 constexpr size_t kCtrlBytes = 256;  // the control line, padded so that the arrays after it stay 256-byte aligned
 constexpr int kCtrlError = 0;     // status word: set if a bounded wait ever expired
@@ -92,7 +93,7 @@ __host__ __device__ constexpr uint64_t ready_slot(uint32_t bits) { return (uint6
 
 struct WsLayout {
   size_t ctrl;      // uint32 control line (status word)
-  size_t tickets;   // uint32 [SV_MAX_B]  arrivals per request (scoring and distillation kernels)
+  size_t tickets;   // uint32 [SV_MAX_B]  arrivals per request (the distillation gradient)
   size_t partials;  // Partial [B][R][nseg2]
   size_t zval;      // float [B][R]       logit at the draft token, per row
   size_t tagged;    // uint64 [B][nseg2][kDrawSlices]  hand-off slots of the draw's slice weights
