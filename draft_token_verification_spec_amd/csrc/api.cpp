@@ -282,7 +282,7 @@ int sv_tts_grad(void* stream, int B, int V, int max_k, int dtype, const void* dr
     return SV_ERR_INVALID_ARG;
   if (draft_row_stride < V || target_row_stride < V) return SV_ERR_INVALID_ARG;
   if (prev_logits && (!prev_row_start || prev_row_stride < V)) return SV_ERR_INVALID_ARG;
-  const Partial* stats = nullptr;
+  Partial* stats = nullptr;
   float* loss_parts = nullptr;
   uint32_t* tickets = nullptr;
   int R = 0, nseg2 = 0;
@@ -290,7 +290,7 @@ int sv_tts_grad(void* stream, int B, int V, int max_k, int dtype, const void* dr
     if (check_sizes(B, V, max_k, dtype) != SV_OK) return SV_ERR_UNSUPPORTED;
     const WsLayout L = ws_layout(B, V, max_k, dtype);
     if (workspace_bytes < L.total) return SV_ERR_WORKSPACE;
-    stats = reinterpret_cast<const Partial*>(static_cast<const char*>(verify_workspace) + L.partials);
+    stats = reinterpret_cast<Partial*>(static_cast<char*>(verify_workspace) + L.partials);
     loss_parts = reinterpret_cast<float*>(static_cast<char*>(verify_workspace) + L.tts_loss);
     tickets = reinterpret_cast<uint32_t*>(static_cast<char*>(verify_workspace) + L.tickets);
     R = L.R;

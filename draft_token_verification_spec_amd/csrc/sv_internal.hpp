@@ -201,7 +201,7 @@ hipError_t launch_tts_grad(int B, int V, int max_k, int dtype, const void* draft
                            int64_t draft_stride, const void* target, const int64_t* target_start,
                            int64_t target_stride, const void* prev, const int64_t* prev_start, int64_t prev_stride,
                            const int32_t* num_draft, const float* temperature, const float* weights, float lambda,
-                           void* grad, float* loss, const Partial* stats, float* loss_parts, uint32_t* tickets, int R, int nseg2,
+                           void* grad, float* loss, Partial* stats, float* loss_parts, uint32_t* tickets, int R, int nseg2,
                            hipStream_t stream);
 hipError_t launch_av_fit(int B, int max_k, const float* feature, const int8_t* labels,
                          float* params, double* accum, float damping_c, float ridge, float max_step,

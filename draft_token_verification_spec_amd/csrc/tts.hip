@@ -155,7 +155,7 @@ struct TtsArgs {
   float* loss;
   // row statistics of a preceding sv_spec_verify call on the same rows
   // (its workspace's segment partials), or null
-  const Partial* stats;
+  Partial* stats;
   float* loss_parts;  // [B][max_k][nseg2] (segmented kernel)
   uint32_t* tickets;  // arrival counters per request slot (segmented kernel)
   int R, nseg2;
@@ -389,6 +389,47 @@ __global__ __launch_bounds__(kTT) void tts_seg_kernel(TtsArgs a) {
   if (tid == 0) store_dev(ticket, 0u);
 }
 
+// A greedy request's target rows hold only (maximum, lowest argmax) per
+// segment in the verification's statistics; the gradient needs their
+// softmax sums (T = 0 counting as 1).  Workgroup (b, k): for a greedy
+// request and k < K_b, target row k is summed segment by segment, each
+// against the maximum its statistics already hold, and the sums are written
+// beside them; the workgroups of other rows leave at once.
+template <typename ET>
+__global__ __launch_bounds__(kTT) void greedy_target_sums_kernel(TtsArgs a) {
+  constexpr int N = Elem<ET>::N;
+  constexpr int SV = kHalfVecs;         // vectors per thread and segment
+  constexpr int E = kTT * SV * N;       // elements per 32 KiB segment, as the verification's
+  static_assert(kTT == kThreads, "the verification's segments");
+  __shared__ float red[kTT / 64];
+  const int tid = threadIdx.x;
+  const int b = int(blockIdx.x / uint32_t(a.max_k)), k = int(blockIdx.x % uint32_t(a.max_k));
+  const int K = min(max(a.num_draft[b], 0), a.max_k);
+  const float T = a.temperature[b];
+  const int64_t ts = a.target_start[b];
+  if (T > 0.f || k >= K) return;
+  const float c = kLog2e;
+  const ET* rt = static_cast<const ET*>(a.target) + (ts + k) * a.target_stride;
+  const bool al = is_aligned16(rt);
+  Partial* p = a.stats + (size_t(b) * a.R + a.max_k + k) * a.nseg2;
+  for (int s = 0; s < a.nseg2; ++s) {
+    const float m = p[s].m;
+    uint4 v[SV];
+#pragma unroll
+    for (int q = 0; q < SV; ++q) v[q] = load_raw<ET>(rt, s * E + (q * kTT + tid) * N, a.V, al);
+    float sum = 0.f;
+    if (m != -INFINITY) {
+      const float mc = m * c;
+#pragma unroll
+      for (int q = 0; q < SV; ++q)
+#pragma unroll
+        for (int j = 0; j < N; ++j) sum += fast_exp2(fmaf(Elem<ET>::get(v[q], j), c, -mc));
+    }
+    const float total = block_total(sum, red, tid);
+    if (tid == 0) p[s].s = total;
+  }
+}
+
 template <typename ET, bool PREV>
 void launch_tts_kind(const TtsArgs& a, unsigned grid, hipStream_t stream) {
   if (a.stats && !PREV) {
@@ -406,13 +447,19 @@ hipError_t launch_tts_grad(int B, int V, int max_k, int dtype, const void* draft
                            int64_t draft_stride, const void* target, const int64_t* target_start,
                            int64_t target_stride, const void* prev, const int64_t* prev_start, int64_t prev_stride,
                            const int32_t* num_draft, const float* temperature, const float* weights, float lambda,
-                           void* grad, float* loss, const Partial* stats, float* loss_parts, uint32_t* tickets,
+                           void* grad, float* loss, Partial* stats, float* loss_parts, uint32_t* tickets,
                            int R, int nseg2, hipStream_t stream) {
   const TtsArgs a{B,       V,       max_k,     draft,        draft_start, draft_stride, target,
                   target_start, target_stride, prev,   prev_start,  prev_stride,  num_draft, temperature,
                   weights, lambda,  grad,      loss,         stats,       loss_parts,   tickets,  R,
                   nseg2};
   const unsigned grid = unsigned(uint64_t(B) * uint64_t(max_k));
+  if (stats) {
+    if (dtype == SV_BF16)
+      hipLaunchKernelGGL(greedy_target_sums_kernel<uint16_t>, dim3(grid), dim3(kTT), 0, stream, a);
+    else
+      hipLaunchKernelGGL(greedy_target_sums_kernel<float>, dim3(grid), dim3(kTT), 0, stream, a);
+  }
   if (dtype == SV_BF16) {
     if (prev)
       launch_tts_kind<uint16_t, true>(a, grid, stream);

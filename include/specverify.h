@@ -376,7 +376,9 @@ int sv_av_calib_metrics(void* stream, double* accum, double* metrics, int reset)
  *                  into the workspace's own region and sums in segment order.
  *                  That call must have read every canvas draft row: each
  *                  request stochastic (T > 0), or the call made with
- *                  av_feature.
+ *                  av_feature.  A greedy request's target rows, of which
+ *                  the verification keeps only maxima and argmaxes, are
+ *                  summed again by this call (one pass over those rows).
  * Outputs (device): grad, elements of type dtype (bf16 rounded to nearest
  * even), [B*max_k, V] row-major; loss float [B*max_k].
  * Device preconditions as for sv_spec_verify.  Returns SV_OK, or a negative
