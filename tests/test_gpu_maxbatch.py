@@ -102,3 +102,29 @@ def test_largest_batch_verification_scoring_and_gradient():
             _, lref = ot.position(b.draft[r * K + k], b.target[r * (K + 1) + k], None, T, float(w[k]), 0.0)
             assert loss[r, k] == pytest.approx(lref, rel=1e-4, abs=1e-6), (r, k)
         assert np.all(np.isnan(loss[r, k_b:]))
+
+
+def test_largest_batch_filtered():
+    """Filtered verification at the largest batch: top-k / top-p mixed per
+    request (some requests unfiltered, a quarter greedy)."""
+    import dataclasses
+
+    from test_gpu_filtered import compare_filtered, gpu_filtered, oracle_filtered
+
+    b = _batch(seed=43)
+    B = b.B
+    r = np.arange(B)
+    b = dataclasses.replace(b, top_k=np.array([0, 5, 0, 20, 3], np.int32)[r % 5],
+                            top_p=np.array([0.9, 1.0, 0.5, 0.95, 1.0], np.float32)[r % 5])
+    print(f"case max batch filtered B={B}", flush=True)
+    g = gpu_filtered(b)
+    a = g["accept_len"]
+    assert np.all((a >= 0) & (a <= b.num_draft))
+    at = np.take_along_axis(g["out_tokens"], a[:, None].astype(np.int64), axis=1)[:, 0]
+    assert np.all((at >= 0) & (at < b.V))
+    # kept counts: -1 where a row is not filtered or not read, else 1..V
+    kept = g["kept"]
+    assert np.all((kept == -1) | ((kept >= 1) & (kept <= b.V)))
+    idx = _sample(B, 2000, 11)
+    o = oracle_filtered(b, idx)
+    assert compare_filtered(b, g, o, requests=idx) <= 2
