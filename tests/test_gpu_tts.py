@@ -154,32 +154,38 @@ def test_statistics_reused_from_the_verification(prev):
             assert loss[r, k] == pytest.approx(lref, rel=1e-4, abs=1e-6)
 
 
-def test_statistics_reused_with_greedy_requests():
-    """Greedy requests (T = 0) in the verification: their target rows'
-    statistics carry the softmax sum at T = 1 beside the argmax, so the
-    gradient reusing them equals the oracle's at T = 1 (the verification made
-    with the estimator feature, so that every canvas draft row was read)."""
+@pytest.mark.parametrize("prev", [False, True])
+def test_statistics_reused_with_greedy_requests(prev):
+    """Greedy requests (T = 0) in the verification, whose target rows'
+    statistics hold only maxima and argmaxes: the gradient reusing the
+    statistics equals the oracle's at T = 1 (the verification made with the
+    estimator feature, so that every canvas draft row was read)."""
     b = gen.make_batch("fp32_b1024_k1to3_v129280_greedy_mix", B=24)
     from gpu_harness import to_device
     d = to_device(b)
-    print("case tts reuse with greedy requests", flush=True)
+    print(f"case tts reuse with greedy requests prev={prev}", flush=True)
     ws = sv.Workspace()
     sv.sv_spec_verify(d["draft"], d["draft_row_start"], d["target"], d["target_row_start"], d["num_draft"],
                       d["draft_tokens"], d["temperature"], d["u_accept"], d["u_residual"], d["u_bonus"],
                       max_k=b.max_k, want_feature=True, workspace=ws)
     w = torch.linspace(1.0, 0.5, b.max_k, device=DEV)
+    lam = 0.3 if prev else 0.0
+    prev_rows = d["draft"] + 0.25 if prev else None
+    kw = dict(prev_logits=prev_rows, prev_row_start=d["draft_row_start"] if prev else None)
     out = sv.sv_tts_grad(d["draft"], d["draft_row_start"], d["target"], d["target_row_start"], d["num_draft"],
-                         d["temperature"], w, b.max_k, 0.0, verify_workspace=ws)
+                         d["temperature"], w, b.max_k, lam, verify_workspace=ws, **kw)
     torch.cuda.synchronize()
     loss = out["loss"].cpu().numpy()
     wh = w.cpu().numpy()
+    pr = prev_rows.cpu().numpy() if prev else None
     greedy = 0
     for r in range(b.B):
         greedy += int(b.temperature[r] == 0.0)
         for k in range(int(b.num_draft[r])):
             zd = b.draft[int(b.draft_row_start[r]) + k]
             zt = b.target[int(b.target_row_start[r]) + k]
-            gref, lref = ot.position(zd, zt, None, float(b.temperature[r]), float(wh[k]), 0.0)
+            zp = pr[int(b.draft_row_start[r]) + k] if prev else None
+            gref, lref = ot.position(zd, zt, zp, float(b.temperature[r]), float(wh[k]), lam)
             g = out["grad"][r * b.max_k + k].float().cpu().numpy()
             scale = row_scale(zd, zt, float(b.temperature[r]) or 1.0, float(wh[k]))
             assert np.all(np.abs(g - gref) <= REL["f32"] * np.abs(gref) + ABS["f32"] * scale), (r, k)
