@@ -21,8 +21,9 @@ namespace sv {
 // items t, t + T, ... (coalesced loads), so that every item a thread takes
 // belongs to the same position i = t mod max_k, and the thread keeps that
 // position's six sums, formed in fp64, in registers.  The threads' sums then
-// go to LDS and are added per position and sum in thread order, a fixed
-// order that makes the result deterministic.  On the round's last step the
+// go to LDS and are added per position and sum in thread order (chunks of
+// threads, then the chunk sums), a fixed order that makes the result
+// deterministic.  On the round's last step the
 // first max_k threads solve the arrowhead Newton system H * delta = -g by
 // eliminating the intercepts (Schur complement on the slope), damp, bound
 // the step, update the parameters and clear the accumulator.
@@ -34,6 +35,7 @@ __global__ __launch_bounds__(kFitT) void av_fit_kernel(int B, int max_k, const f
                                                        const int8_t* labels, float* params, double* accum,
                                                        float damping_c, float ridge, float max_step, int do_update) {
   __shared__ double part[6][kFitT];          // per thread, by sum
+  __shared__ double mid[kFitT];              // chunk sums
   __shared__ double acc[SV_MAX_K][6];        // accumulator after this step
   __shared__ FitShared fsh;
   const int tid = threadIdx.x;
@@ -70,10 +72,21 @@ __global__ __launch_bounds__(kFitT) void av_fit_kernel(int B, int max_k, const f
 #pragma unroll
   for (int k = 0; k < 6; ++k) part[k][tid] = sum[k];
   __syncthreads();
+  // each of the 6 * max_k sums adds the M = T / max_k threads of its
+  // position in two levels: C chunks of L threads, then the C chunk sums
+  const int M = T / max_k, C = kFitT / (6 * max_k), L = (M + C - 1) / C;
+  if (tid < 6 * max_k * C) {
+    const int o = tid / C, c = tid % C;
+    const int i = o / 6, k = o % 6;
+    double t = 0.0;
+    for (int u = c * L; u < min(M, (c + 1) * L); ++u) t += part[k][i + u * max_k];
+    mid[tid] = t;
+  }
+  __syncthreads();
   if (tid < 6 * max_k) {
     const int i = tid / 6, k = tid % 6;
     double t = 0.0;
-    for (int u = i; u < T; u += max_k) t += part[k][u];
+    for (int c = 0; c < C; ++c) t += mid[(i * 6 + k) * C + c];
     t += acc_in;
     acc[i][k] = t;
     if (!do_update) accum[tid] = t;
