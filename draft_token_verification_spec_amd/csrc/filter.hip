@@ -424,7 +424,7 @@ __device__ uint32_t key_hi_of_bin(int j, float c16, float mc16) {
   return uint32_t(lo);
 }
 
-constexpr int kS0 = kBins0;  // threads of the level-0 selection: one per bin
+constexpr int kS0 = kBins0 / 2;  // threads of the level-0 selection: two adjacent bins each
 
 struct Sel0Shared {
   double pd[kS0 / 64];
@@ -435,11 +435,11 @@ struct Sel0Shared {
   uint32_t klo[2], khi[2];
 };
 
-// Level-0 selection: one workgroup (one thread per bin) per row slot.  The
-// row's segment histograms are merged in order; bin masses are
-// edge x (count + sum 2^-21) (the last bin's mass never enters: nothing is
-// below it).  The boundary bin of each search is the last non-empty bin whose
-// count (top-k) or mass (top-p, against top_p x the row's sum from the
+// Level-0 selection: one workgroup per row slot, thread t holding bins 2t
+// and 2t + 1.  The row's segment histograms are merged in order; bin masses
+// are edge x (count + sum 2^-21) (the last bin's mass never enters: nothing
+// is below it).  The boundary bin of each search is the last non-empty bin
+// whose count (top-k) or mass (top-p, against top_p x the row's sum from the
 // statistics) above it is below the target; the search continues over that
 // bin's keys with the count and mass above it.
 template <typename ET>
@@ -452,34 +452,55 @@ __global__ __launch_bounds__(kS0) void filt_select0_kernel(FiltArgs a) {
   const ReqFilter f = req_filter(a, b);
   if (!row_filtered(a, f, rs)) return;
   const size_t row = size_t(b) * R + rs;
-  const int j = tid;
-  uint32_t cnt = 0;
-  uint64_t frac = 0;  // up to V x 92840: beyond 32 bits for long runs of equal logits
+  const int j0 = 2 * tid;
+  uint32_t cnt[2] = {0u, 0u};
+  uint64_t frac[2] = {0u, 0u};  // up to V x 92840: beyond 32 bits for long runs of equal logits
 #pragma unroll 8
   for (int s = 0; s < n; ++s) {
-    cnt += a.hcount[(row * n + s) * 2 * kBins0 + j];
-    frac += a.hcount[(row * n + s) * 2 * kBins0 + kBins0 + j];
+    const uint32_t* h = a.hcount + (row * n + s) * 2 * kBins0;
+    const uint2 cc = *reinterpret_cast<const uint2*>(h + j0);
+    const uint2 ff = *reinterpret_cast<const uint2*>(h + kBins0 + j0);
+    cnt[0] += cc.x;
+    cnt[1] += cc.y;
+    frac[0] += ff.x;
+    frac[1] += ff.y;
   }
   const float c = kLog2e / f.T;
   float m, S;
   wave_row_ms(a.partials + row * n, n, c, lane, &m, &S);
   const float c16 = c * float(kBinsPerLog2), mc16 = m * c16;
-  const double edge = double(fast_exp2(-float(j + 1) * (1.f / kBinsPerLog2)));
-  const double mass = j < kBins0 - 1 ? edge * (double(cnt) + double(frac) / double(kFrac0)) : 0.0;
-  const uint32_t fc = block_excl_scan<kS0, uint32_t>(cnt, sh.pu, tid);
-  const double fm = block_excl_scan<kS0, double>(mass, sh.pd, tid);
+  double mass[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int j = j0 + q;
+    const double edge = double(fast_exp2(-float(j + 1) * (1.f / kBinsPerLog2)));
+    mass[q] = j < kBins0 - 1 ? edge * (double(cnt[q]) + double(frac[q]) / double(kFrac0)) : 0.0;
+  }
+  const uint32_t fcb = block_excl_scan<kS0, uint32_t>(cnt[0] + cnt[1], sh.pu, tid);
+  const double fmb = block_excl_scan<kS0, double>(mass[0] + mass[1], sh.pd, tid);
+  const uint32_t fc[2] = {fcb, fcb + cnt[0]};
+  const double fm[2] = {fmb, fmb + mass[0]};
   const double tk = double(f.top_k);
   const double tp = double(f.top_p) * double(S);
-  const int top = -block_max_int<kS0>(cnt > 0u ? -j : -kBins0, sh.pi, tid);
-  const int jk = block_max_int<kS0>(f.on_k && cnt > 0u && double(fc) < tk ? j : -1, sh.pi, tid);
-  const int jp = block_max_int<kS0>(f.on_p && cnt > 0u && fm < tp ? j : -1, sh.pi, tid);
+  const int first = cnt[0] > 0u ? j0 : (cnt[1] > 0u ? j0 + 1 : kBins0);
+  int ck = -1, cp = -1;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    if (f.on_k && cnt[q] > 0u && double(fc[q]) < tk) ck = j0 + q;
+    if (f.on_p && cnt[q] > 0u && fm[q] < tp) cp = j0 + q;
+  }
+  const int top = -block_max_int<kS0>(-first, sh.pi, tid);
+  const int jk = block_max_int<kS0>(ck, sh.pi, tid);
+  const int jp = block_max_int<kS0>(cp, sh.pi, tid);
   const int jq[2] = {jk >= 0 ? jk : top, jp >= 0 ? jp : top};
 #pragma unroll
-  for (int q = 0; q < 2; ++q)
-    if (j == jq[q]) {
-      sh.cab[q] = fc;
-      sh.mab[q] = fm;
-    }
+  for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      if (j0 + q == jq[qq]) {
+        sh.cab[qq] = fc[q];
+        sh.mab[qq] = fm[q];
+      }
   if (lane == 0 && (tid >> 6) < 4) {
     // the boundary bin's key interval: two bisections per search, one wave each
     const int q = (tid >> 6) >> 1, side = (tid >> 6) & 1;
