@@ -146,7 +146,7 @@ def kernel_source_hash() -> str:
 
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "draft_token_verification_spec_amd", "csrc")
-    for name in ("stream.hip", "sv_device.hpp", "sv_internal.hpp"):
+    for name in ("stream.hip", "sv_segment.hpp", "sv_device.hpp", "sv_internal.hpp"):
         h.update(name.encode())
         h.update(open(os.path.join(csrc, name), "rb").read())
     return h.hexdigest()

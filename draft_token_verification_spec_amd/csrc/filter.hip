@@ -13,18 +13,21 @@
 // A row's kept set is {v : key(z_v) >= t} for a threshold key t (key = the
 // order-preserving integer image of the logit), found by an exact radix
 // select with deterministic histograms:
-//   level 0  bins of 1/16 unit of log2 probability below the row maximum
-//            (511 bins, the last one collecting everything further down),
-//            each with its count and its mass exactly to 2^-22 relative;
+//   level 0  bins of 1/8 unit of log2 weight on an absolute grid, the 511
+//            grid cells from the row maximum's down (the last bin collecting
+//            everything further down), each with its count and its mass
+//            exactly to 2^-22 relative; built by the statistics pass itself,
+//            so that one read of a filtered row serves both, and the row's
+//            total mass is the sum of its bins;
 //   level L  8-bit digits of the key within the boundary bin's keys, until
 //            one key remains (bf16 keys: 2 levels at most, fp32: 4).
-// Each level is a streaming pass (one workgroup per 32 KiB row segment;
-// every sum an integer added with LDS atomics, so the result does not depend
-// on the order of the additions) and a selection (one workgroup per row:
-// segment histograms merged in order, exclusive scans, the boundary bin or
-// digit).  The verdict, the residual / bonus weights and the draw then run
-// on the filtered rows.
-#include "sv_device.hpp"
+// Each level's counts come from a streaming pass (one workgroup per 32 KiB
+// row segment; every sum an integer added with LDS atomics, so the result
+// does not depend on the order of the additions) and a selection (one
+// workgroup per row: segment histograms merged in order, exclusive scans,
+// the boundary bin or digit).  The verdict, the residual / bonus weights and
+// the draw then run on the filtered rows.
+#include "sv_segment.hpp"
 
 namespace sv {
 
@@ -35,6 +38,7 @@ constexpr int kFV = 8;    // 16-byte vectors per thread and segment (32 KiB)
 constexpr int kBins = 256;  // key-digit bins
 constexpr float kFix = 1099511627776.f;  // 2^40
 static_assert(kFT * kFV * 16 == kHalfBytes, "a histogram segment is a 32 KiB sampling segment");
+static_assert(kFT == kThreads && kFV == kNV, "a histogram segment is a statistics segment");
 
 // Order-preserving key of a logit: bf16 rows use the 16 bits of the value,
 // fp32 rows all 32; -0 is keyed as +0.
@@ -70,26 +74,34 @@ struct Key<float> {
   }
 };
 
-// Level-0 bin: floor of t = 16 x log2(maximum weight / weight), clamped to
-// [0, 511].  Non-increasing in z.  Bin j < 511 holds the weights 2^(-t/16)
-// with t in [j, j+1) (bin 0 also t < 0, a rounding of the maximum's own
-// term), bin 511 everything from 2^-511/16 down.  Within bin j < 511 a weight
-// is the bin's lower edge 2^-(j+1)/16 times r = 2^((1 - (t - j))/16) in
-// (1, 2^(1/16)], and (r - 1) is kept in 2^-21 fixed point: the counts and
+// Level-0 bins.  The grid cell of a logit z is F(z) = floor(z * 8c) (the
+// product rounded once, then floored: a non-decreasing function of z alone),
+// and cell F holds the weights 2^(z c) in [2^(F/8), 2^((F+1)/8)).  A row's bin
+// of z is G - F(z) clamped to [0, 511], with G = ceil(max * 8c): bin 0 or 1
+// holds the maximum, bin 511 everything 511 cells or more below G, whose
+// weights are below 2^-63.6 of the maximum's (all of them together below
+// 2^-42 of it, even at the longest rows: they are left out of the row's
+// total).  The statistics pass bins a segment against its own grid point
+// Gs = ceil(segment max * 8c), and a segment bin shifts into the row bin by
+// the integer G - Gs, so that the segments need not know the row maximum.
+// Within a cell a weight is the cell's lower edge times r = 2^((z 8c - F)/8)
+// in [1, 2^(1/8)), and (r - 1) is kept in 2^-21 fixed point: the counts and
 // these sums are integers (32 bits each per segment suffice, added as the
 // two halves of one 64-bit word), so the bin masses edge x (count + sum
-// 2^-21) do not depend on the order of the additions and are exact to
-// 2^-22 relative.
+// 2^-21) do not depend on the order of the additions and are exact to 2^-22
+// relative.
 constexpr int kBins0 = 512;
-constexpr int kBinsPerLog2 = 16;
+constexpr int kBinsPerLog2 = 8;
 constexpr float kFrac0 = 2097152.f;  // 2^21
-// t = 16 x log2(max weight / weight) = (max - z) * 16c, from the row's
-// c16 = 16c and mc16 = max * 16c; the bin is t clamped to [0, 511]
-__device__ __forceinline__ float bin_t(float z, float c16, float mc16) { return fmaf(z, -c16, mc16); }
-__device__ __forceinline__ int bin_of_t(float t) {
-  return int(__builtin_amdgcn_fmed3f(t, 0.f, float(kBins0 - 1)));
+__device__ __forceinline__ float cell_of(float z, float c8) { return floorf(z * c8); }
+// the bin of z against grid point g (a whole number of cells): g - F(z),
+// exact where it is below 511, clamped to [0, 511]
+__device__ __forceinline__ float bin0f(float z, float c8, float g) {
+  return __builtin_amdgcn_fmed3f(g - cell_of(z, c8), 0.f, float(kBins0 - 1));
 }
-__device__ __forceinline__ int bin0(float z, float c16, float mc16) { return bin_of_t(bin_t(z, c16, mc16)); }
+__device__ __forceinline__ int bin0(float z, float c8, float g) { return int(bin0f(z, c8, g)); }
+// the grid point of a row or segment maximum m
+__device__ __forceinline__ float grid_point(float m, float c8) { return ceilf(m * c8); }
 
 // Weight of an element relative to the row maximum, in 2^-40 fixed point.
 __device__ __forceinline__ uint64_t fixed_mass(float z, float c, float mc) {
@@ -110,7 +122,7 @@ struct FSearch {
 };
 static_assert(sizeof(FSearch) == kFilterSearchBytes, "search state layout");
 static_assert(kBins == kFilterBins && kBins0 == kFilterBins0, "histogram bins");
-static_assert(kFT * kFV * 16 / 2 * 0.0443 * 2097152.0 < 4294967296.0, "level-0 sums of a segment fit 32 bits");
+static_assert(kFT * kFV * 16 / 2 * 0.0906 * 2097152.0 < 4294967296.0, "level-0 sums of a segment fit 32 bits");
 
 struct FiltArgs {
   int B, V, max_k, R, nseg2;
@@ -134,8 +146,8 @@ struct FiltArgs {
   float* p_draft;
   float* p_target;
   int32_t* kept;
-  const Partial* partials;  // [B][R][nseg2] of the statistics kernel
-  const float* zval;        // [B][R] logits at the draft tokens
+  Partial* partials;        // [B][R][nseg2] segment statistics
+  float* zval;              // [B][R] logits at the draft tokens
   uint64_t* hmass;          // [B][R][nseg2][2][kBins]  key-level masses (digits wider than one key)
   uint32_t* hcount;         // [B][R][nseg2][2][kBins0]  level 0: counts, fraction sums; key levels: counts
   FSearch* search;          // [B][R][2]
@@ -183,23 +195,6 @@ __device__ __forceinline__ float wave_row_max(const Partial* p, int n, int lane)
   return m;
 }
 
-// Maximum and sum of exp2((z - max) c) of a row from its segment statistics,
-// merged by one wave (merge_ms is symmetric: every lane gets the same value).
-__device__ __forceinline__ void wave_row_ms(const Partial* p, int n, float c, int lane, float* mo, float* so) {
-  float m = -INFINITY, s = 0.f, cnt = 0.f;
-  for (int q = lane; q < n; q += 64) {
-    const Partial x = p[q];
-    merge_ms(m, s, cnt, x.m, x.s + x.cnt, 0.f, c);
-  }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const float m2 = __shfl_xor(m, o, 64), s2 = __shfl_xor(s, o, 64);
-    merge_ms(m, s, cnt, m2, s2, 0.f, c);
-  }
-  *mo = m;
-  *so = s;
-}
-
 // Vector of a row holding elements first..first+N-1; positions >= limit
 // hold a NaN (never a logit: rows have no NaN).
 template <typename ET>
@@ -213,21 +208,150 @@ __device__ __forceinline__ uint4 load_nan_tail(const ET* row, int first, int lim
   return w;
 }
 
-struct HistShared {
-  uint64_t mass[2][kBins];
-  union {
-    uint64_t bins[kBins0];      // level 0: fraction sum << 32 | count, by bin
-    uint32_t count[2][kBins0];  // key levels: [q][digit]
-  };
+// ---------------------------------------------------------------------------
+// statistics and level 0
+// ---------------------------------------------------------------------------
+
+struct Stats0Shared {
+  uint64_t bins[kBins0];  // fraction sum << 32 | count, by segment bin
+  float red[kFT / 64];
+  Partial part[kWaves];
 };
 
-// One histogram pass: workgroup = segment s of row slot rs of request b.
-//   LV 0  every element by level-0 bin: count and fraction sum;
-//   LV 1  per searching slot, the elements of its key interval by key digit:
-//         counts, and 2^-40 fixed-point masses when a digit spans several
-//         keys (a single key's mass is its count times its weight).
-template <typename ET, int LV>
-__global__ __launch_bounds__(kFT) void filt_hist_kernel(FiltArgs a) {
+// Maximum of a segment held as bf16 pairs: the high half of each word is
+// compared as the word itself (the low half only adds bits below the bf16's
+// precision, and a word whose high half is -inf reads as a NaN, which
+// fmaxf passes over), the low half shifted up; the high halves' maximum is
+// cleared of the low bits at the end.  fp32 elements are compared directly.
+template <typename ET>
+__device__ __forceinline__ float segment_max(const uint4 (&v)[kFV]) {
+  if constexpr (Elem<ET>::N == 8) {
+    float hi = -INFINITY, lo = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kFV; ++k) {
+      const uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+#pragma unroll
+      for (int q = 0; q < 4; q += 2) {
+        hi = fmaxf(hi, fmaxf(__uint_as_float(w[q]), __uint_as_float(w[q + 1])));
+        lo = fmaxf(lo, fmaxf(__uint_as_float(w[q] << 16), __uint_as_float(w[q + 1] << 16)));
+      }
+    }
+    return fmaxf(__uint_as_float(__float_as_uint(hi) & 0xffff0000u), lo);
+  } else {
+    float m = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kFV; ++k)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) m = fmaxf(m, Elem<ET>::get(v[k], j));
+    return m;
+  }
+}
+
+// One workgroup per 32 KiB segment of every row slot (draft rows, then
+// target rows, of each request in turn).  Segments of a filtered row: the
+// segment maximum and the level-0 histogram against the segment's own grid
+// point, from one read; the row's total mass comes later from its merged
+// histogram.  Other rows read: the verification's statistics (lowest argmax
+// for greedy target rows).  The segment holding a draft token also stores
+// the logit there.
+template <typename ET>
+__global__ __launch_bounds__(kFT) __attribute__((amdgpu_waves_per_eu(8))) void filt_stats0_kernel(FiltArgs a) {
+  __shared__ Stats0Shared sh;
+  constexpr int N = Elem<ET>::N;
+  constexpr int E = kFT * kFV * N;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int n = a.nseg2, R = a.R, max_k = a.max_k;
+  const uint32_t item = blockIdx.x;
+  const int s = int(item % uint32_t(n));
+  const int rs = int((item / uint32_t(n)) % uint32_t(R));
+  const int b = int(item / (uint32_t(n) * uint32_t(R)));
+  // every scalar the workgroup needs in one round trip, before any decision
+  const ReqFilter f = req_filter(a, b);
+  const bool is_draft = rs < max_k;
+  const int i = is_draft ? rs : rs - max_k;
+  const int64_t start = is_draft ? a.draft_start[b] : a.target_start[b];
+  const int d = i < max_k ? a.tokens[size_t(b) * max_k + i] : -1;
+  const bool greedy = !(f.T > 0.f);
+  if (is_draft ? (greedy || i >= f.K) : (i > f.K)) return;  // not read
+  const float c = uniform(kLog2e / (greedy ? 1.f : f.T));
+  const ET* row = is_draft ? static_cast<const ET*>(a.draft) + (start + i) * a.draft_stride
+                           : static_cast<const ET*>(a.target) + (start + i) * a.target_stride;
+  const bool ztok = !greedy && i < f.K && d >= s * E && d < (s + 1) * E && d < a.V;
+  if (greedy) {
+    stats_segment<ET, kArgmax>(a, sh.part, b, rs, s, false, c, row, d, tid);
+    return;
+  }
+  if (!row_filtered(a, f, rs)) {
+    stats_segment<ET, kSumInclusive>(a, sh.part, b, rs, s, ztok, c, row, d, tid);
+    return;
+  }
+  const int hb = s * E;
+  float zd = 0.f;
+  if (ztok && tid == 0) zd = Elem<ET>::one(row + d);  // in flight with the segment
+  uint4 v[kFV];
+  load_seg<ET>(row, hb, a.V, v, tid);
+  for (int j = tid; j < kBins0; j += kFT) sh.bins[j] = 0u;
+  float m = segment_max<ET>(v);
+  if (N == 8) fence_regs(v);  // the words, not their shifted halves, live on into the binning
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  if (lane == 0) sh.red[wv] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(sh.red[0], sh.red[1]), fmaxf(sh.red[2], sh.red[3]));
+  const size_t row_slot = size_t(b) * R + rs;
+  if (tid == 0) {
+    a.partials[row_slot * n + s] = Partial{m, 0.f, 0.f, 0x7fffffff};
+    if (ztok) a.zval[row_slot] = zd;
+  }
+  if (m == -INFINITY) return;  // uniform; the selection reads no bin of a segment without a finite logit
+  const float c8 = c * float(kBinsPerLog2);
+  const float gs = grid_point(m, c8), g8 = gs * (1.f / kBinsPerLog2);
+  // r = 2^(z c - gs/8 + bin/8) in [1, 2^(1/8)); r - 1 in 2^-21 units rounded
+  // half up: in [0, 189812] for bins below 511 (the last bin is never read:
+  // there the conversion saturates at 0)
+  auto add0 = [&](float z, float jf) {
+    const float r = fast_exp2(fmaf(jf, 1.f / kBinsPerLog2, fmaf(z, c, -g8)));
+    const uint32_t u = uint32_t(fmaf(r, kFrac0, 0.5f - kFrac0));
+    atomicAdd(reinterpret_cast<unsigned long long*>(&sh.bins[int(jf)]),
+              (static_cast<unsigned long long>(u) << 32) | 1ull);
+  };
+  // past the end of the row the loads hold -inf (bin 511, never read by the
+  // selection): whole vectors of them are skipped, so that they do not pile
+  // onto one LDS word
+#pragma unroll
+  for (int k = 0; k < kFV; ++k) {
+    if (hb + (k * kFT + tid) * N >= a.V) continue;
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      const float z = Elem<ET>::get(v[k], j);
+      add0(z, bin0f(z, c8, gs));
+    }
+  }
+  __syncthreads();
+  // counts, then fraction sums
+  const size_t seg = row_slot * n + s;
+  for (int j = tid; j < kBins0; j += kFT) {
+    const uint64_t x = sh.bins[j];
+    a.hcount[seg * 2 * kBins0 + j] = uint32_t(x);
+    a.hcount[seg * 2 * kBins0 + kBins0 + j] = uint32_t(x >> 32);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// key levels
+// ---------------------------------------------------------------------------
+
+struct HistShared {
+  uint64_t mass[2][kBins];
+  uint32_t count[2][kBins];
+};
+
+// One key-level pass: workgroup = segment s of row slot rs of request b;
+// per searching slot, the elements of its key interval by key digit:
+// counts, and 2^-40 fixed-point masses when a digit spans several keys (a
+// single key's mass is its count times its weight).
+template <typename ET>
+__global__ __launch_bounds__(kFT) void filt_keys_kernel(FiltArgs a) {
   __shared__ HistShared sh;
   constexpr int N = Elem<ET>::N;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -241,15 +365,13 @@ __global__ __launch_bounds__(kFT) void filt_hist_kernel(FiltArgs a) {
   const ReqFilter f = req_filter(a, b);
   const bool is_draft = rs < a.max_k;
   const int64_t start = is_draft ? a.draft_start[b] : a.target_start[b];
-  uint32_t st_state[2] = {0u, 0u}, lo[2] = {0u, 0u}, hi[2] = {0u, 0u};
-  if (LV > 0) {
+  uint32_t st_state[2], lo[2], hi[2];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const FSearch& st = a.search[row * 2 + q];
-      st_state[q] = st.state;
-      lo[q] = st.lo;
-      hi[q] = st.hi;
-    }
+  for (int q = 0; q < 2; ++q) {
+    const FSearch& st = a.search[row * 2 + q];
+    st_state[q] = st.state;
+    lo[q] = st.lo;
+    hi[q] = st.hi;
   }
   if (!row_filtered(a, f, rs)) return;
   bool on[2];
@@ -260,7 +382,7 @@ __global__ __launch_bounds__(kFT) void filt_hist_kernel(FiltArgs a) {
     const uint32_t w = hi[q] - lo[q];
     shift[q] = w == 0u ? 0 : max(0, 32 - __clz(w) - 8);
   }
-  if (LV > 0 && !on[0] && !on[1]) return;
+  if (!on[0] && !on[1]) return;
   const ET* rp = is_draft ? static_cast<const ET*>(a.draft) + (start + rs) * a.draft_stride
                           : static_cast<const ET*>(a.target) + (start + (rs - a.max_k)) * a.target_stride;
   const bool al = is_aligned16(rp);
@@ -275,15 +397,14 @@ __global__ __launch_bounds__(kFT) void filt_hist_kernel(FiltArgs a) {
     for (int k = 0; k < kFV; ++k) v[k] = load_nan_tail<ET>(rp, hb + (k * kFT + tid) * N, a.V, al);
   }
   const float c = kLog2e / f.T;
-  const float mrow = wave_row_max(a.partials + row * n, n, lane);
-  const float mc = mrow * c;
-  const float c16 = c * float(kBinsPerLog2), mc16 = mrow * c16;
-  for (int j = tid; j < 2 * kBins0; j += kFT) {
+  const float mc = wave_row_max(a.partials + row * n, n, lane) * c;
+  for (int j = tid; j < 2 * kBins; j += kFT) {
     (&sh.count[0][0])[j] = 0u;
-    if (j < 2 * kBins) (&sh.mass[0][0])[j] = 0u;
+    (&sh.mass[0][0])[j] = 0u;
   }
   // a slot's key interval as a value interval (the key order is the value
-  // order, -0 and +0 one value): two compares dismiss an element
+  // order, -0 and +0 one value): two compares dismiss an element; past the
+  // end of the row the tail loads hold NaN, which no interval holds
   float zlo[2], zhi[2];
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
@@ -291,76 +412,38 @@ __global__ __launch_bounds__(kFT) void filt_hist_kernel(FiltArgs a) {
     zhi[q] = on[q] ? Key<ET>::value(hi[q]) : INFINITY;
   }
   __syncthreads();
-  // past the end of the row the tail loads hold NaN: no interval holds it,
-  // and level 0 skips it
-  if (LV == 0) {
-    auto add0 = [&](float z) {
-      const float t = bin_t(z, c16, mc16);
-      const int bn = bin_of_t(t);
-      // r - 1 of the weight relative to the bin's lower edge, in 2^-21 units
-      // rounded half up: in [0, 92840] for bins below 511 (the last bin's
-      // sum is never read; there the conversion saturates at 0)
-      const float r = fast_exp2(fmaf(t - float(bn), -1.f / kBinsPerLog2, 1.f / kBinsPerLog2));
-      const uint32_t u = uint32_t(fmaf(r, kFrac0, 0.5f - kFrac0));
-      atomicAdd(reinterpret_cast<unsigned long long*>(&sh.bins[bn]), (static_cast<unsigned long long>(u) << 32) | 1ull);
-    };
-    if (full) {
+  // per element a test against each searching slot's value interval; the
+  // common case of one search gets a loop of its own
+  auto digit_add = [&](int q, float z) {
+    const int dg = int((Key<ET>::of(z) - lo[q]) >> shift[q]);
+    atomicAdd(&sh.count[q][dg], 1u);
+    if (shift[q] > 0)
+      atomicAdd(reinterpret_cast<unsigned long long*>(&sh.mass[q][dg]),
+                static_cast<unsigned long long>(fixed_mass(z, c, mc)));
+  };
+  if (on[0] && on[1]) {
 #pragma unroll
-      for (int k = 0; k < kFV; ++k)
+    for (int k = 0; k < kFV; ++k)
 #pragma unroll
-        for (int j = 0; j < N; ++j) add0(Elem<ET>::get(v[k], j));
-    } else {
+      for (int j = 0; j < N; ++j) {
+        const float z = Elem<ET>::get(v[k], j);
 #pragma unroll
-      for (int k = 0; k < kFV; ++k)
-#pragma unroll
-        for (int j = 0; j < N; ++j) {
-          const float z = Elem<ET>::get(v[k], j);
-          if (z == z) add0(z);
-        }
-    }
+        for (int q = 0; q < 2; ++q)
+          if (z >= zlo[q] && z <= zhi[q]) digit_add(q, z);
+      }
   } else {
-    // per element a test against each searching slot's value interval; the
-    // common case of one search gets a loop of its own
-    auto digit_add = [&](int q, float z) {
-      const int dg = int((Key<ET>::of(z) - lo[q]) >> shift[q]);
-      atomicAdd(&sh.count[q][dg], 1u);
-      if (shift[q] > 0)
-        atomicAdd(reinterpret_cast<unsigned long long*>(&sh.mass[q][dg]),
-                  static_cast<unsigned long long>(fixed_mass(z, c, mc)));
-    };
-    if (on[0] && on[1]) {
+    const int q = on[0] ? 0 : 1;
+    const float l = zlo[q], h = zhi[q];
 #pragma unroll
-      for (int k = 0; k < kFV; ++k)
+    for (int k = 0; k < kFV; ++k)
 #pragma unroll
-        for (int j = 0; j < N; ++j) {
-          const float z = Elem<ET>::get(v[k], j);
-#pragma unroll
-          for (int q = 0; q < 2; ++q)
-            if (z >= zlo[q] && z <= zhi[q]) digit_add(q, z);
-        }
-    } else {
-      const int q = on[0] ? 0 : 1;
-      const float l = zlo[q], h = zhi[q];
-#pragma unroll
-      for (int k = 0; k < kFV; ++k)
-#pragma unroll
-        for (int j = 0; j < N; ++j) {
-          const float z = Elem<ET>::get(v[k], j);
-          if (z >= l && z <= h) digit_add(q, z);
-        }
-    }
+      for (int j = 0; j < N; ++j) {
+        const float z = Elem<ET>::get(v[k], j);
+        if (z >= l && z <= h) digit_add(q, z);
+      }
   }
   __syncthreads();
   const size_t seg = row * n + s;
-  if (LV == 0) {
-    // counts, then fraction sums
-    for (int j = tid; j < kBins0; j += kFT) {
-      const uint64_t x = sh.bins[j];
-      a.hcount[seg * 2 * kBins0 + j] = uint32_t(x);
-      a.hcount[seg * 2 * kBins0 + kBins0 + j] = uint32_t(x >> 32);
-    }
-    return;
-  }
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     if (!on[q]) continue;
@@ -400,28 +483,50 @@ __device__ __forceinline__ int block_max_int(int x, int* part, int tid) {
 }
 
 // The smallest key whose level-0 bin is <= j and the largest whose bin is
-// >= j (bin0 is non-increasing in the key): the keys of bins [.., j] and
+// >= j (the bin is non-increasing in the key): the keys of bins [.., j] and
 // [j, ..].
 template <typename ET>
-__device__ uint32_t key_lo_of_bin(int j, float c16, float mc16) {
+__device__ uint32_t key_lo_of_bin(int j, float c8, float g) {
   uint64_t lo = Key<ET>::kMin, hi = Key<ET>::kMax;
   while (lo < hi) {
     const uint64_t mid = (lo + hi) >> 1;
-    if (bin0(Key<ET>::value(uint32_t(mid)), c16, mc16) <= j) hi = mid;
+    if (bin0(Key<ET>::value(uint32_t(mid)), c8, g) <= j) hi = mid;
     else lo = mid + 1;
   }
   return uint32_t(lo);
 }
 
 template <typename ET>
-__device__ uint32_t key_hi_of_bin(int j, float c16, float mc16) {
+__device__ uint32_t key_hi_of_bin(int j, float c8, float g) {
   uint64_t lo = Key<ET>::kMin, hi = Key<ET>::kMax;
   while (lo < hi) {
     const uint64_t mid = (lo + hi + 1) >> 1;
-    if (bin0(Key<ET>::value(uint32_t(mid)), c16, mc16) >= j) lo = mid;
+    if (bin0(Key<ET>::value(uint32_t(mid)), c8, g) >= j) lo = mid;
     else hi = mid - 1;
   }
   return uint32_t(lo);
+}
+
+// Exclusive prefix over the workgroup as block_excl_scan, and the total.
+template <int NT>
+__device__ __forceinline__ double block_excl_scan_total(double x, double* part, int tid, double* total) {
+  const int lane = tid & 63, w = tid >> 6;
+  double incl = x;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const double y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) part[w] = incl;
+  __syncthreads();
+  double before = 0.0, all = 0.0;
+  for (int q = 0; q < NT / 64; ++q) {
+    if (q == w) before = all;
+    all += part[q];
+  }
+  __syncthreads();
+  *total = all;
+  return before + incl - x;
 }
 
 constexpr int kS0 = kBins0 / 2;  // threads of the level-0 selection: two adjacent bins each
@@ -436,12 +541,14 @@ struct Sel0Shared {
 };
 
 // Level-0 selection: one workgroup per row slot, thread t holding bins 2t
-// and 2t + 1.  The row's segment histograms are merged in order; bin masses
-// are edge x (count + sum 2^-21) (the last bin's mass never enters: nothing
-// is below it).  The boundary bin of each search is the last non-empty bin
-// whose count (top-k) or mass (top-p, against top_p x the row's sum from the
-// statistics) above it is below the target; the search continues over that
-// bin's keys with the count and mass above it.
+// and 2t + 1.  The row's segment histograms are shifted onto the row's grid
+// point and merged in segment order; bin masses, in units of the row
+// maximum's weight, are edge x (count + sum 2^-21), and the row's total mass
+// is the sum of the masses of bins 0..510 (bin 511's never enters; its count
+// is the row's length less the other bins').  The boundary bin of each
+// search is the last non-empty bin whose count (top-k) or mass (top-p,
+// against top_p x the row's total) above it is below the target; the search
+// continues over that bin's keys with the count and mass above it.
 template <typename ET>
 __global__ __launch_bounds__(kS0) void filt_select0_kernel(FiltArgs a) {
   __shared__ Sel0Shared sh;
@@ -453,35 +560,53 @@ __global__ __launch_bounds__(kS0) void filt_select0_kernel(FiltArgs a) {
   if (!row_filtered(a, f, rs)) return;
   const size_t row = size_t(b) * R + rs;
   const int j0 = 2 * tid;
-  uint32_t cnt[2] = {0u, 0u};
-  uint64_t frac[2] = {0u, 0u};  // up to V x 92840: beyond 32 bits for long runs of equal logits
-#pragma unroll 8
-  for (int s = 0; s < n; ++s) {
-    const uint32_t* h = a.hcount + (row * n + s) * 2 * kBins0;
-    const uint2 cc = *reinterpret_cast<const uint2*>(h + j0);
-    const uint2 ff = *reinterpret_cast<const uint2*>(h + kBins0 + j0);
-    cnt[0] += cc.x;
-    cnt[1] += cc.y;
-    frac[0] += ff.x;
-    frac[1] += ff.y;
-  }
   const float c = kLog2e / f.T;
-  float m, S;
-  wave_row_ms(a.partials + row * n, n, c, lane, &m, &S);
-  const float c16 = c * float(kBinsPerLog2), mc16 = m * c16;
+  const float c8 = c * float(kBinsPerLog2);
+  const float m = wave_row_max(a.partials + row * n, n, lane);
+  const float g = grid_point(m, c8);
+  uint32_t cnt[2] = {0u, 0u};
+  uint64_t frac[2] = {0u, 0u};  // up to V x 189812: beyond 32 bits for long runs of equal logits
+#pragma unroll 4
+  for (int s = 0; s < n; ++s) {
+    // cells between the row's grid point and the segment's; a segment
+    // without a finite logit (infinite shift) stored no bins
+    const float shc = g - grid_point(a.partials[row * n + s].m, c8);
+    const int jl = j0 - int(fminf(shc, float(kBins0)));
+    const uint32_t* h = a.hcount + (row * n + s) * 2 * kBins0;
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      if (j0 + q < kBins0 - 1 && jl + q >= 0) {
+        cnt[q] += h[jl + q];
+        frac[q] += h[kBins0 + jl + q];
+      }
+  }
+  // the last bin holds every element not in the others
+  uint32_t in_bins;
+  {
+    const uint32_t x = cnt[0] + cnt[1];
+    const uint32_t ex = block_excl_scan<kS0, uint32_t>(x, sh.pu, tid);
+    if (tid == kS0 - 1) sh.pu[0] = ex + x;
+    __syncthreads();
+    in_bins = sh.pu[0];
+    __syncthreads();
+  }
+  if (tid == kS0 - 1) cnt[1] = uint32_t(a.V) - in_bins;
+  // edge of bin j relative to the row maximum's weight: 2^((g - j)/8 - m c)
+  const double mc = double(m * c);
   double mass[2];
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int j = j0 + q;
-    const double edge = double(fast_exp2(-float(j + 1) * (1.f / kBinsPerLog2)));
-    mass[q] = j < kBins0 - 1 ? edge * (double(cnt[q]) + double(frac[q]) / double(kFrac0)) : 0.0;
+    const double edge = exp2(double(g - float(j)) * (1.0 / kBinsPerLog2) - mc);
+    mass[q] = j < kBins0 - 1 && cnt[q] > 0u ? edge * (double(cnt[q]) + double(frac[q]) / double(kFrac0)) : 0.0;
   }
   const uint32_t fcb = block_excl_scan<kS0, uint32_t>(cnt[0] + cnt[1], sh.pu, tid);
-  const double fmb = block_excl_scan<kS0, double>(mass[0] + mass[1], sh.pd, tid);
+  double S;
+  const double fmb = block_excl_scan_total<kS0>(mass[0] + mass[1], sh.pd, tid, &S);
   const uint32_t fc[2] = {fcb, fcb + cnt[0]};
   const double fm[2] = {fmb, fmb + mass[0]};
   const double tk = double(f.top_k);
-  const double tp = double(f.top_p) * double(S);
+  const double tp = double(f.top_p) * S;
   const int first = cnt[0] > 0u ? j0 : (cnt[1] > 0u ? j0 + 1 : kBins0);
   int ck = -1, cp = -1;
 #pragma unroll
@@ -506,8 +631,8 @@ __global__ __launch_bounds__(kS0) void filt_select0_kernel(FiltArgs a) {
     const int q = (tid >> 6) >> 1, side = (tid >> 6) & 1;
     const bool on = q == 0 ? f.on_k : f.on_p;
     if (on) {
-      if (side == 0) sh.klo[q] = key_lo_of_bin<ET>(jq[q], c16, mc16);
-      else sh.khi[q] = key_hi_of_bin<ET>(jq[q], c16, mc16);
+      if (side == 0) sh.klo[q] = key_lo_of_bin<ET>(jq[q], c8, g);
+      else sh.khi[q] = key_hi_of_bin<ET>(jq[q], c8, g);
     }
   }
   __syncthreads();
@@ -948,8 +1073,6 @@ __global__ __launch_bounds__(kFT) void filt_search_kernel(FiltArgs a, const RowI
 hipError_t launch_filtered(VerifyArgs va, const FilterIO& io, int dtype, hipStream_t stream) {
   const uint64_t n1 = uint64_t(va.B) * uint64_t(va.R) * uint64_t(va.nseg2);
   if (n1 >= (uint64_t(1) << 31)) return hipErrorInvalidValue;
-  hipError_t e = launch_stats(va, dtype, stream);
-  if (e != hipSuccess) return e;
   FiltArgs a{va.B, va.V, va.max_k, va.R, va.nseg2, va.draft, va.draft_start, va.draft_stride, va.target,
              va.target_start, va.target_stride, va.num_draft, va.tokens, va.temperature, io.top_k, io.top_p,
              va.u_accept, va.u_residual, va.u_bonus, va.accept_len, va.out_tokens, va.labels, va.p_draft,
@@ -962,10 +1085,10 @@ hipError_t launch_filtered(VerifyArgs va, const FilterIO& io, int dtype, hipStre
   float* slices = io.slices;
   const int levels = dtype == SV_BF16 ? 2 : 4;  // key-digit levels after level 0
   if (dtype == SV_BF16) {
-    hipLaunchKernelGGL((filt_hist_kernel<uint16_t, 0>), dim3(g1), dim3(kFT), 0, stream, a);
+    hipLaunchKernelGGL(filt_stats0_kernel<uint16_t>, dim3(g1), dim3(kFT), 0, stream, a);
     hipLaunchKernelGGL(filt_select0_kernel<uint16_t>, dim3(g2), dim3(kS0), 0, stream, a);
     for (int l = 0; l < levels; ++l) {
-      hipLaunchKernelGGL((filt_hist_kernel<uint16_t, 1>), dim3(g1), dim3(kFT), 0, stream, a);
+      hipLaunchKernelGGL(filt_keys_kernel<uint16_t>, dim3(g1), dim3(kFT), 0, stream, a);
       hipLaunchKernelGGL(filt_select_kernel<uint16_t>, dim3(g2), dim3(kFT), 0, stream, a);
     }
     hipLaunchKernelGGL(filt_verdict_kernel<uint16_t>, dim3(unsigned(va.B)), dim3(64), 0, stream, a, info, desc);
@@ -973,10 +1096,10 @@ hipError_t launch_filtered(VerifyArgs va, const FilterIO& io, int dtype, hipStre
     hipLaunchKernelGGL(filt_search_kernel<uint16_t>, dim3(unsigned(va.B)), dim3(kFT), 0, stream, a, info, desc,
                        slices);
   } else {
-    hipLaunchKernelGGL((filt_hist_kernel<float, 0>), dim3(g1), dim3(kFT), 0, stream, a);
+    hipLaunchKernelGGL(filt_stats0_kernel<float>, dim3(g1), dim3(kFT), 0, stream, a);
     hipLaunchKernelGGL(filt_select0_kernel<float>, dim3(g2), dim3(kS0), 0, stream, a);
     for (int l = 0; l < levels; ++l) {
-      hipLaunchKernelGGL((filt_hist_kernel<float, 1>), dim3(g1), dim3(kFT), 0, stream, a);
+      hipLaunchKernelGGL(filt_keys_kernel<float>, dim3(g1), dim3(kFT), 0, stream, a);
       hipLaunchKernelGGL(filt_select_kernel<float>, dim3(g2), dim3(kFT), 0, stream, a);
     }
     hipLaunchKernelGGL(filt_verdict_kernel<float>, dim3(unsigned(va.B)), dim3(64), 0, stream, a, info, desc);

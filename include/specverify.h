@@ -217,11 +217,15 @@ size_t sv_filtered_workspace_size(int B, int V, int max_k, int dtype);
  *   p_draft_at_token, p_target_at_token: the filtered probabilities p'.
  *   workspace: at least sv_filtered_workspace_size(B, V, max_k, dtype)
  *           bytes, zero-filled once.
- * The kept sets are exact: a row's masses are summed in 2^-40 fixed point of
- * the probability relative to the row maximum (the top-p comparison is made
- * on those sums in binary64), the threshold found by a radix select over the
- * logits' order-preserving keys.  Outputs are a deterministic function of
- * the inputs.  Returns SV_OK, or a negative sv_status without launching. */
+ * The kept sets are exact to the resolution of the mass sums, which are
+ * integers (level 0: 2^-21 of a bin's lower edge; key levels: 2^-40 of the
+ * row maximum's probability), so that every mass compared, the row's total
+ * included, is within 2^-22 of the row's total of the sum of the weights it
+ * stands for, and independent of the order of the additions;
+ * the top-p comparison is made on them in binary64, the threshold found by a
+ * radix select over the logits' order-preserving keys.  Outputs are a
+ * deterministic function of the inputs.  Returns SV_OK, or a negative
+ * sv_status without launching. */
 int sv_spec_verify_filtered(void* stream, int B, int V, int max_k, int dtype,
                             const void* draft_logits, const int64_t* draft_row_start,
                             int64_t draft_row_stride,
