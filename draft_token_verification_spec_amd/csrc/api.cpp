@@ -201,7 +201,10 @@ int sv_spec_verify_filtered(void* stream, int B, int V, int max_k, int dtype, co
                     ws + F.search,
                     ws + F.info,
                     ws + F.desc,
-                    reinterpret_cast<float*>(ws + F.slices)};
+                    reinterpret_cast<float*>(ws + F.slices),
+                    reinterpret_cast<uint32_t*>(ws + F.tickets),
+                    reinterpret_cast<uint32_t*>(ws + F.work),
+                    reinterpret_cast<uint32_t*>(ws + F.wcount)};
   return to_status(launch_filtered(a, io, dtype, static_cast<hipStream_t>(stream)));
 }
 

@@ -149,8 +149,12 @@ struct FiltArgs {
   Partial* partials;        // [B][R][nseg2] segment statistics
   float* zval;              // [B][R] logits at the draft tokens
   uint64_t* hmass;          // [B][R][nseg2][2][kBins]  key-level masses (digits wider than one key)
-  uint32_t* hcount;         // [B][R][nseg2][2][kBins0]  level 0: counts, fraction sums; key levels: counts
+  uint32_t* hcount;         // [B][R][nseg2][2][kBins0]  level 0: per bin fraction sum << 32 | count (u64);
+                            //   key levels: counts
   FSearch* search;          // [B][R][2]
+  uint32_t* tickets;        // [B][R]  arrivals per row (zero between passes)
+  uint32_t* work;           // [2][B][R][nseg2]  segments still searching, for the next key level
+  uint32_t* wcount;         // [kMaxKeyLevels]  entries of work per key level after the first
 };
 
 struct ReqFilter {
@@ -209,12 +213,347 @@ __device__ __forceinline__ uint4 load_nan_tail(const ET* row, int first, int lim
 }
 
 // ---------------------------------------------------------------------------
+// selection
+// ---------------------------------------------------------------------------
+//
+// Level 0 and the first key level are selected by kernels of their own (one
+// workgroup per row).  A later key level, where few rows still search, runs
+// on the listed segments only, and a row's selection is made there by the
+// workgroup that delivers the row's last segment histogram (every segment
+// workgroup publishes its histogram with device-scope stores, then takes a
+// ticket on the row's arrival counter; see arrive_last_all), reading the
+// others' histograms with device-scope loads.  The counter is back at zero
+// when the selection ends.
+
+constexpr int kMaxSegs = int(int64_t(SV_MAX_V) * 4 / (kFT * kFV * 16));  // 32 KiB segments of the longest row
+constexpr int kMaxKeyLevels = 4;  // fp32 keys: 4 digits of 8 bits
+
+__device__ __forceinline__ uint64_t load_dev64(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_dev64(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t load_dev32(const uint32_t* p) {
+  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Loads of another workgroup's histogram: device-scope within the kernel
+// that wrote it (DEV), plain in a later kernel.
+template <bool DEV>
+__device__ __forceinline__ uint32_t load_h32(const uint32_t* p) {
+  if constexpr (DEV) return load_dev32(p);
+  else return *p;
+}
+template <bool DEV>
+__device__ __forceinline__ uint64_t load_h64(const uint64_t* p) {
+  if constexpr (DEV) return load_dev64(p);
+  else return *p;
+}
+
+// 2^(-k/8), k = 0..7: a level-0 bin edge is 2^(-j/8) = 2^-(j/8 rounded down)
+// times the entry for j mod 8.
+__constant__ const double kPow2Eighth[8] = {0x1.0000000000000p+0, 0x1.d5818dcfba487p-1, 0x1.ae89f995ad3adp-1,
+                                            0x1.8ace5422aa0dbp-1, 0x1.6a09e667f3bcdp-1, 0x1.4bfdad5362a27p-1,
+                                            0x1.306fe0a31b715p-1, 0x1.172b83c7d517bp-1};
+
+// Arrival counter of a row, for histograms that every thread of the
+// workgroup published: each thread waits until its own stores have
+// completed, then thread 0 takes a ticket.  The workgroup taking the last
+// one (want - 1) selects the row; its loads of the published data are
+// issued after its ticket returned.  The verdict in all threads.
+__device__ __forceinline__ bool arrive_last_all(uint32_t* ticket, uint32_t want, int* lds_flag) {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);  // vmcnt(0): this thread's published stores have completed
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __syncthreads();
+  if (threadIdx.x == 0)
+    *lds_flag = (__hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == want - 1) ? 1 : 0;
+  __syncthreads();
+  return *lds_flag != 0;
+}
+
+// The smallest key whose level-0 bin is <= j and the largest whose bin is
+// >= j (the bin is non-increasing in the key): the keys of bins [.., j] and
+// [j, ..].
+template <typename ET>
+__device__ uint32_t key_lo_of_bin(int j, float c8, float g) {
+  uint64_t lo = Key<ET>::kMin, hi = Key<ET>::kMax;
+  while (lo < hi) {
+    const uint64_t mid = (lo + hi) >> 1;
+    if (bin0(Key<ET>::value(uint32_t(mid)), c8, g) <= j) hi = mid;
+    else lo = mid + 1;
+  }
+  return uint32_t(lo);
+}
+
+template <typename ET>
+__device__ uint32_t key_hi_of_bin(int j, float c8, float g) {
+  uint64_t lo = Key<ET>::kMin, hi = Key<ET>::kMax;
+  while (lo < hi) {
+    const uint64_t mid = (lo + hi + 1) >> 1;
+    if (bin0(Key<ET>::value(uint32_t(mid)), c8, g) >= j) lo = mid;
+    else hi = mid - 1;
+  }
+  return uint32_t(lo);
+}
+
+// Wave-wide reductions and exclusive prefix in lane order (every lane gets
+// the result).
+__device__ __forceinline__ int wave_max_int(int x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = max(x, __shfl_xor(x, o, 64));
+  return x;
+}
+template <typename T>
+__device__ __forceinline__ T wave_excl_scan(T x, int lane, T* total) {
+  T incl = x;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const T y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += y;
+  }
+  *total = __shfl(incl, 63, 64);
+  return incl - x;
+}
+
+constexpr int kSelBins = kBins0 / 64;  // level-0 bins per lane of the selection
+
+struct Sel0Shared {
+  float segm[kMaxSegs];  // segment maxima of the row
+  int segn[kMaxSegs];    // bins stored per segment
+  uint32_t cab[2];
+  double mab[2];
+  uint32_t klo[2], khi[2];
+};
+
+// Level-0 selection of a row slot by one wave, lane t holding bins 8t ..
+// 8t + 7.  The row's segment histograms are shifted onto the row's grid
+// point and merged in segment order; bin masses, in units of the row
+// maximum's weight, are edge x (count + sum 2^-21), and the row's total mass
+// is the sum of the masses of bins 0..510 (bin 511's never enters; its count
+// is the row's length less the other bins').  The boundary bin of each
+// search is the last non-empty bin whose count (top-k) or mass (top-p,
+// against top_p x the row's total) above it is below the target; the search
+// continues over that bin's keys with the count and mass above it.
+template <typename ET>
+__device__ void select0_row(const FiltArgs& a, const ReqFilter& f, size_t row, Sel0Shared& sh, int lane) {
+  static_assert(kSelBins == 8 && kBinsPerLog2 == 8, "a lane's bins are one log2 unit: edges 2^-t x 2^(-q/8)");
+  const int n = a.nseg2;
+  const int j0 = kSelBins * lane;
+  const float c = kLog2e / f.T;
+  const float c8 = c * float(kBinsPerLog2);
+  // the segment maxima and the row's
+  float m = -INFINITY;
+  for (int q = lane; q < n; q += 64) {
+    const Partial x = a.partials[row * n + q];
+    sh.segm[q] = x.m;
+    sh.segn[q] = x.idx;
+    m = fmaxf(m, x.m);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  __syncthreads();
+  const float g = grid_point(m, c8);
+  uint32_t cnt[kSelBins] = {};
+  uint64_t frac[kSelBins] = {};  // up to V x 189812: beyond 32 bits for long runs of equal logits
+  const uint64_t* h64 = reinterpret_cast<const uint64_t*>(a.hcount) + row * n * kBins0;
+#pragma unroll 2
+  for (int s = 0; s < n; ++s) {
+    // cells between the row's grid point and the segment's; a segment
+    // stored its bins 0 .. nbs - 1 (none without a finite logit)
+    const float shc = g - grid_point(sh.segm[s], c8);
+    const int jl = j0 - int(fminf(shc, float(kBins0)));
+    const int nbs = sh.segn[s];
+#pragma unroll
+    for (int q = 0; q < kSelBins; ++q)
+      if (j0 + q < kBins0 - 1 && jl + q >= 0 && jl + q < nbs) {
+        const uint64_t x = h64[size_t(s) * kBins0 + jl + q];
+        cnt[q] += uint32_t(x);
+        frac[q] += x >> 32;
+      }
+  }
+  // the last bin (lane 63's last) holds every element not in the others
+  uint32_t lc = 0;
+#pragma unroll
+  for (int q = 0; q < kSelBins; ++q) lc += cnt[q];
+  uint32_t in_bins;
+  (void)wave_excl_scan<uint32_t>(lc, lane, &in_bins);
+  if (lane == 63) cnt[kSelBins - 1] = uint32_t(a.V) - in_bins;
+  // edge of bin 8t + q relative to the row maximum's weight: 2^(g/8 - m c) 2^-t 2^(-q/8)
+  const double e0 = ldexp(exp2(double(g) * (1.0 / kBinsPerLog2) - double(m * c)), -lane);
+  double mass[kSelBins];
+  uint32_t tc = 0;
+  double tm = 0.0;
+#pragma unroll
+  for (int q = 0; q < kSelBins; ++q) {
+    mass[q] = j0 + q < kBins0 - 1 && cnt[q] > 0u
+                  ? e0 * kPow2Eighth[q] * (double(cnt[q]) + double(frac[q]) / double(kFrac0))
+                  : 0.0;
+    tc += cnt[q];
+    tm += mass[q];
+  }
+  uint32_t call;
+  double S;
+  uint32_t fc = wave_excl_scan<uint32_t>(tc, lane, &call);
+  double fm = wave_excl_scan<double>(tm, lane, &S);
+  const double tk = double(f.top_k);
+  const double tp = double(f.top_p) * S;
+  int first = kBins0, ck = -1, cp = -1;
+  uint32_t fcq[kSelBins];
+  double fmq[kSelBins];
+#pragma unroll
+  for (int q = 0; q < kSelBins; ++q) {
+    fcq[q] = fc;
+    fmq[q] = fm;
+    if (cnt[q] > 0u) {
+      first = min(first, j0 + q);
+      if (f.on_k && double(fc) < tk) ck = j0 + q;
+      if (f.on_p && fm < tp) cp = j0 + q;
+    }
+    fc += cnt[q];
+    fm += mass[q];
+  }
+  const int top = -wave_max_int(-first);
+  const int jk = wave_max_int(ck);
+  const int jp = wave_max_int(cp);
+  const int jq[2] = {jk >= 0 ? jk : top, jp >= 0 ? jp : top};
+#pragma unroll
+  for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+    for (int q = 0; q < kSelBins; ++q)
+      if (j0 + q == jq[qq]) {
+        sh.cab[qq] = fcq[q];
+        sh.mab[qq] = fmq[q];
+      }
+  if (lane < 4) {
+    // the boundary bin's key interval: two bisections per search, one lane each
+    const int q = lane >> 1, side = lane & 1;
+    const bool on = q == 0 ? f.on_k : f.on_p;
+    if (on) {
+      if (side == 0) sh.klo[q] = key_lo_of_bin<ET>(jq[q], c8, g);
+      else sh.khi[q] = key_hi_of_bin<ET>(jq[q], c8, g);
+    }
+  }
+  __syncthreads();
+  if (lane < 2) {
+    const int q = lane;
+    const bool on = q == 0 ? f.on_k : f.on_p;
+    FSearch w{};
+    if (on) {
+      w.lo = sh.klo[q];
+      w.hi = sh.khi[q];
+      w.cabove = sh.cab[q];
+      w.mabove = sh.mab[q];
+      w.target = q == 0 ? tk : tp;
+      w.state = 1u;
+    }
+    a.search[row * 2 + q] = w;
+  }
+}
+
+constexpr int kSelDigits = kBins / 64;  // key digits per lane of the selection
+
+// Key-level selection of a row by one wave; lane l owns digits
+// kBins - 1 - (4l + k), k = 0..3, so that a prefix in lane order (and k
+// order within a lane) sums the digits of larger keys.  The segment
+// histograms are merged in segment order.  Returns (in every lane) whether
+// a search of the row is still open.
+template <typename ET, bool DEV>
+__device__ bool select_row(const FiltArgs& a, float c, size_t row, int lane) {
+  const int n = a.nseg2;
+  FSearch* st = a.search + row * 2;
+  const float mc = wave_row_max(a.partials + row * n, n, lane) * c;
+  int more = 0;
+#pragma unroll 1
+  for (int q = 0; q < 2; ++q) {
+    const FSearch cur = st[q];
+    if (cur.state != 1u) continue;
+    const uint32_t w = cur.hi - cur.lo;
+    const int shf = w == 0u ? 0 : max(0, 32 - __clz(w) - 8);
+    const int nd = int(w >> shf);  // the interval's last digit (no others are stored)
+    uint32_t cd[kSelDigits];
+    double md[kSelDigits];
+    uint32_t tc = 0;
+    double tm = 0.0;
+#pragma unroll
+    for (int k = 0; k < kSelDigits; ++k) {
+      const int d = kBins - 1 - (kSelDigits * lane + k);
+      uint64_t mfix = 0;
+      cd[k] = 0;
+      if (d <= nd) {
+#pragma unroll 4
+        for (int s = 0; s < n; ++s) {
+          cd[k] += load_h32<DEV>(&a.hcount[(row * n + s) * 2 * kBins0 + q * kBins0 + d]);
+          if (shf > 0) mfix += load_h64<DEV>(&a.hmass[((row * n + s) * 2 + q) * kBins + d]);
+        }
+      }
+      // a one-key digit's mass: its count times the weight of that key, the
+      // same float expression as an element's weight
+      md[k] = shf > 0 ? double(mfix) / double(kFix)
+                      : (cd[k] > 0u ? double(cd[k]) * double(fast_exp2(fmaf(Key<ET>::value(cur.lo + uint32_t(d)), c,
+                                                                                -mc)))
+                                    : 0.0);
+      tc += cd[k];
+      tm += md[k];
+    }
+    uint32_t call;
+    double mall;
+    uint32_t fc = cur.cabove + wave_excl_scan<uint32_t>(tc, lane, &call);
+    double fm = cur.mabove + wave_excl_scan<double>(tm, lane, &mall);
+    // the smallest qualifying digit (the largest non-empty one if none is)
+    int dq = kBins, dtop = -1;
+    uint32_t fck[kSelDigits];
+    double fmk[kSelDigits];
+#pragma unroll
+    for (int k = 0; k < kSelDigits; ++k) {
+      const int d = kBins - 1 - (kSelDigits * lane + k);
+      fck[k] = fc;
+      fmk[k] = fm;
+      if (cd[k] > 0u) {
+        if (q == 0 ? double(fc) < cur.target : fm < cur.target) dq = min(dq, d);
+        dtop = max(dtop, d);
+      }
+      fc += cd[k];
+      fm += md[k];
+    }
+    dq = -wave_max_int(-dq);
+    dtop = wave_max_int(dtop);
+    const int ds = dq < kBins ? dq : dtop;
+    int open = 0;
+#pragma unroll
+    for (int k = 0; k < kSelDigits; ++k) {
+      const int d = kBins - 1 - (kSelDigits * lane + k);
+      if (d != ds) continue;
+      FSearch nx = cur;
+      const uint64_t lo = uint64_t(cur.lo) + (uint64_t(d) << shf);
+      const uint64_t hi = min(uint64_t(cur.hi), lo + (uint64_t(1) << shf) - 1);
+      nx.lo = uint32_t(lo);
+      nx.hi = uint32_t(hi);
+      nx.mabove = fmk[k];
+      nx.cabove = fck[k];
+      if (lo == hi) {
+        nx.state = 2u;
+        nx.key = uint32_t(lo);
+        nx.kept = fck[k] + cd[k];
+        nx.mfinal = fmk[k] + md[k];
+      } else {
+        open = 1;
+      }
+      st[q] = nx;
+    }
+    more |= wave_max_int(open);
+  }
+  return more != 0;
+}
+
+// ---------------------------------------------------------------------------
 // statistics and level 0
 // ---------------------------------------------------------------------------
 
 struct Stats0Shared {
   uint64_t bins[kBins0];  // fraction sum << 32 | count, by segment bin
   float red[kFT / 64];
+  int lastb[kFT / 64];
   Partial part[kWaves];
 };
 
@@ -250,10 +589,9 @@ __device__ __forceinline__ float segment_max(const uint4 (&v)[kFV]) {
 // One workgroup per 32 KiB segment of every row slot (draft rows, then
 // target rows, of each request in turn).  Segments of a filtered row: the
 // segment maximum and the level-0 histogram against the segment's own grid
-// point, from one read; the row's total mass comes later from its merged
-// histogram.  Other rows read: the verification's statistics (lowest argmax
-// for greedy target rows).  The segment holding a draft token also stores
-// the logit there.
+// point, from one read.  Other rows read:
+// the verification's statistics (lowest argmax for greedy target rows).  The
+// segment holding a draft token also stores the logit there.
 template <typename ET>
 __global__ __launch_bounds__(kFT) __attribute__((amdgpu_waves_per_eu(8))) void filt_stats0_kernel(FiltArgs a) {
   __shared__ Stats0Shared sh;
@@ -299,42 +637,62 @@ __global__ __launch_bounds__(kFT) __attribute__((amdgpu_waves_per_eu(8))) void f
   __syncthreads();
   m = fmaxf(fmaxf(sh.red[0], sh.red[1]), fmaxf(sh.red[2], sh.red[3]));
   const size_t row_slot = size_t(b) * R + rs;
-  if (tid == 0) {
-    a.partials[row_slot * n + s] = Partial{m, 0.f, 0.f, 0x7fffffff};
-    if (ztok) a.zval[row_slot] = zd;
-  }
-  if (m == -INFINITY) return;  // uniform; the selection reads no bin of a segment without a finite logit
-  const float c8 = c * float(kBinsPerLog2);
-  const float gs = grid_point(m, c8), g8 = gs * (1.f / kBinsPerLog2);
-  // r = 2^(z c - gs/8 + bin/8) in [1, 2^(1/8)); r - 1 in 2^-21 units rounded
-  // half up: in [0, 189812] for bins below 511 (the last bin is never read:
-  // there the conversion saturates at 0)
-  auto add0 = [&](float z, float jf) {
-    const float r = fast_exp2(fmaf(jf, 1.f / kBinsPerLog2, fmaf(z, c, -g8)));
-    const uint32_t u = uint32_t(fmaf(r, kFrac0, 0.5f - kFrac0));
-    atomicAdd(reinterpret_cast<unsigned long long*>(&sh.bins[int(jf)]),
-              (static_cast<unsigned long long>(u) << 32) | 1ull);
-  };
-  // past the end of the row the loads hold -inf (bin 511, never read by the
-  // selection): whole vectors of them are skipped, so that they do not pile
-  // onto one LDS word
+  if (tid == 0 && ztok) a.zval[row_slot] = zd;
+  // the segment's statistics: its maximum, and (in idx) how many of its
+  // bins, from bin 0, are stored: up to the last non-empty one below 511
+  int nb = 0;
+  if (m != -INFINITY) {  // uniform; the selection reads no bin of a segment without a finite logit
+    const float c8 = c * float(kBinsPerLog2);
+    const float gs = grid_point(m, c8), g8 = gs * (1.f / kBinsPerLog2);
+    // r = 2^(z c - gs/8 + bin/8) in [1, 2^(1/8)); r - 1 in 2^-21 units
+    // rounded half up: in [0, 189812] for bins below 511 (the last bin is
+    // never read: there the conversion saturates at 0)
+    auto add0 = [&](float z, float jf) {
+      const float r = fast_exp2(fmaf(jf, 1.f / kBinsPerLog2, fmaf(z, c, -g8)));
+      const uint32_t u = uint32_t(fmaf(r, kFrac0, 0.5f - kFrac0));
+      atomicAdd(reinterpret_cast<unsigned long long*>(&sh.bins[int(jf)]),
+                (static_cast<unsigned long long>(u) << 32) | 1ull);
+    };
+    // past the end of the row the loads hold -inf (bin 511, never read by
+    // the selection): whole vectors of them are skipped, so that they do
+    // not pile onto one LDS word
 #pragma unroll
-  for (int k = 0; k < kFV; ++k) {
-    if (hb + (k * kFT + tid) * N >= a.V) continue;
+    for (int k = 0; k < kFV; ++k) {
+      if (hb + (k * kFT + tid) * N >= a.V) continue;
 #pragma unroll
-    for (int j = 0; j < N; ++j) {
-      const float z = Elem<ET>::get(v[k], j);
-      add0(z, bin0f(z, c8, gs));
+      for (int j = 0; j < N; ++j) {
+        const float z = Elem<ET>::get(v[k], j);
+        add0(z, bin0f(z, c8, gs));
+      }
     }
+    __syncthreads();
+    int last = -1;
+    for (int j = tid; j < kBins0 - 1; j += kFT)
+      if (sh.bins[j] != 0u) last = j;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) last = max(last, __shfl_xor(last, o, 64));
+    if (lane == 0) sh.lastb[wv] = last;
+    __syncthreads();
+    nb = max(max(sh.lastb[0], sh.lastb[1]), max(sh.lastb[2], sh.lastb[3])) + 1;
+    uint64_t* h64 = reinterpret_cast<uint64_t*>(a.hcount) + (row_slot * n + s) * kBins0;
+    for (int j = tid; j < nb; j += kFT) h64[j] = sh.bins[j];
   }
-  __syncthreads();
-  // counts, then fraction sums
-  const size_t seg = row_slot * n + s;
-  for (int j = tid; j < kBins0; j += kFT) {
-    const uint64_t x = sh.bins[j];
-    a.hcount[seg * 2 * kBins0 + j] = uint32_t(x);
-    a.hcount[seg * 2 * kBins0 + kBins0 + j] = uint32_t(x >> 32);
-  }
+  if (tid == 0) a.partials[row_slot * n + s] = Partial{m, 0.f, 0.f, nb};
+}
+
+// Level-0 selection: one wave per row slot.  Workgroup 0 also clears the
+// counters of the key levels' lists.
+template <typename ET>
+__global__ __launch_bounds__(64) void filt_select0_kernel(FiltArgs a) {
+  __shared__ Sel0Shared sh;
+  const int tid = threadIdx.x;
+  if (blockIdx.x == 0 && tid < kMaxKeyLevels) a.wcount[tid] = 0u;
+  const int R = a.R;
+  const int rs = int(blockIdx.x % uint32_t(R));
+  const int b = int(blockIdx.x / uint32_t(R));
+  const ReqFilter f = req_filter(a, b);
+  if (!row_filtered(a, f, rs)) return;
+  select0_row<ET>(a, f, size_t(b) * R + rs, sh, tid);
 }
 
 // ---------------------------------------------------------------------------
@@ -344,22 +702,37 @@ __global__ __launch_bounds__(kFT) __attribute__((amdgpu_waves_per_eu(8))) void f
 struct HistShared {
   uint64_t mass[2][kBins];
   uint32_t count[2][kBins];
+  uint32_t base;
+  int last, more;
 };
 
-// One key-level pass: workgroup = segment s of row slot rs of request b;
-// per searching slot, the elements of its key interval by key digit:
-// counts, and 2^-40 fixed-point masses when a digit spans several keys (a
-// single key's mass is its count times its weight).
-template <typename ET>
-__global__ __launch_bounds__(kFT) void filt_keys_kernel(FiltArgs a) {
-  __shared__ HistShared sh;
+// The segments of a row still searching after key level `level` are listed
+// for the next level, if there is one.
+__device__ __forceinline__ void list_row(const FiltArgs& a, size_t row, int level, int levels, uint32_t* base,
+                                         int tid) {
+  if (level >= levels) return;
+  const int n = a.nseg2;
+  const int nxt = level - 1;  // list and counter of level + 1
+  if (tid == 0) *base = __hip_atomic_fetch_add(&a.wcount[nxt], uint32_t(n), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  uint32_t* list = a.work + size_t(nxt & 1) * (size_t(a.B) * a.R * n);
+  for (int q = tid; q < n; q += kFT) list[*base + q] = uint32_t(row * n + q);
+}
+
+// One key-level pass over segment s of row slot rs of request b: per
+// searching slot, the elements of its key interval by key digit: counts,
+// and 2^-40 fixed-point masses when a digit spans several keys (a single
+// key's mass is its count times its weight).  At the first key level they
+// are stored for the selection kernel; at later ones (LATER) they are
+// published for the row's selection, which the row's last arriving segment
+// workgroup then makes, listing the row for the next level if it still
+// searches.
+template <typename ET, bool LATER>
+__device__ void keys_segment(const FiltArgs& a, int b, int rs, int s, int level, int levels, HistShared& sh,
+                             int tid) {
   constexpr int N = Elem<ET>::N;
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int lane = tid & 63;
   const int n = a.nseg2, R = a.R;
-  const uint32_t item = blockIdx.x;
-  const int s = int(item % uint32_t(n));
-  const int rs = int((item / uint32_t(n)) % uint32_t(R));
-  const int b = int(item / (uint32_t(n) * uint32_t(R)));
   const size_t row = size_t(b) * R + rs;
   // every scalar the workgroup needs in one round trip, before any decision
   const ReqFilter f = req_filter(a, b);
@@ -382,7 +755,8 @@ __global__ __launch_bounds__(kFT) void filt_keys_kernel(FiltArgs a) {
     const uint32_t w = hi[q] - lo[q];
     shift[q] = w == 0u ? 0 : max(0, 32 - __clz(w) - 8);
   }
-  if (!on[0] && !on[1]) return;
+  // a listed row searches; at the first key level every filtered row does
+  // (the level-0 selection leaves each of its searches open)
   const ET* rp = is_draft ? static_cast<const ET*>(a.draft) + (start + rs) * a.draft_stride
                           : static_cast<const ET*>(a.target) + (start + (rs - a.max_k)) * a.target_stride;
   const bool al = is_aligned16(rp);
@@ -443,280 +817,74 @@ __global__ __launch_bounds__(kFT) void filt_keys_kernel(FiltArgs a) {
       }
   }
   __syncthreads();
+  // only the interval's digits are stored: the digits below ((hi - lo) >> shift) + 1
   const size_t seg = row * n + s;
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
-    if (!on[q]) continue;
-    if (shift[q] > 0) a.hmass[(seg * 2 + q) * kBins + tid] = sh.mass[q][tid];
-    a.hcount[seg * 2 * kBins0 + q * kBins0 + tid] = sh.count[q][tid];
+    if (!on[q] || tid > int((hi[q] - lo[q]) >> shift[q])) continue;
+    if (LATER) {
+      if (shift[q] > 0) store_dev64(&a.hmass[(seg * 2 + q) * kBins + tid], sh.mass[q][tid]);
+      store_dev(&a.hcount[seg * 2 * kBins0 + q * kBins0 + tid], sh.count[q][tid]);
+    } else {
+      if (shift[q] > 0) a.hmass[(seg * 2 + q) * kBins + tid] = sh.mass[q][tid];
+      a.hcount[seg * 2 * kBins0 + q * kBins0 + tid] = sh.count[q][tid];
+    }
   }
-}
-
-// Exclusive prefix over the workgroup (NT threads) in thread order.
-template <int NT, typename T>
-__device__ __forceinline__ T block_excl_scan(T x, T* part, int tid) {
-  const int lane = tid & 63, w = tid >> 6;
-  T incl = x;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const T y = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += y;
+  if (!LATER) return;
+  if (!arrive_last_all(&a.tickets[row], uint32_t(n), &sh.last)) return;
+  if (tid < 64) {
+    const bool more = select_row<ET, true>(a, c, row, tid);
+    if (tid == 0) sh.more = more ? 1 : 0;
   }
-  if (lane == 63) part[w] = incl;
   __syncthreads();
-  T before = 0;
-  for (int q = 0; q < w; ++q) before += part[q];
-  __syncthreads();
-  return before + incl - x;
+  if (sh.more) list_row(a, row, level, levels, &sh.base, tid);
+  if (tid == 0) store_dev(&a.tickets[row], 0u);
 }
 
-template <int NT>
-__device__ __forceinline__ int block_max_int(int x, int* part, int tid) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x = max(x, __shfl_xor(x, o, 64));
-  if ((tid & 63) == 0) part[tid >> 6] = x;
-  __syncthreads();
-  int m = part[0];
-  for (int q = 1; q < NT / 64; ++q) m = max(m, part[q]);
-  __syncthreads();
-  return m;
-}
-
-// The smallest key whose level-0 bin is <= j and the largest whose bin is
-// >= j (the bin is non-increasing in the key): the keys of bins [.., j] and
-// [j, ..].
+// The first key level: one workgroup per 32 KiB segment of every row slot.
 template <typename ET>
-__device__ uint32_t key_lo_of_bin(int j, float c8, float g) {
-  uint64_t lo = Key<ET>::kMin, hi = Key<ET>::kMax;
-  while (lo < hi) {
-    const uint64_t mid = (lo + hi) >> 1;
-    if (bin0(Key<ET>::value(uint32_t(mid)), c8, g) <= j) hi = mid;
-    else lo = mid + 1;
-  }
-  return uint32_t(lo);
-}
-
-template <typename ET>
-__device__ uint32_t key_hi_of_bin(int j, float c8, float g) {
-  uint64_t lo = Key<ET>::kMin, hi = Key<ET>::kMax;
-  while (lo < hi) {
-    const uint64_t mid = (lo + hi + 1) >> 1;
-    if (bin0(Key<ET>::value(uint32_t(mid)), c8, g) >= j) lo = mid;
-    else hi = mid - 1;
-  }
-  return uint32_t(lo);
-}
-
-// Exclusive prefix over the workgroup as block_excl_scan, and the total.
-template <int NT>
-__device__ __forceinline__ double block_excl_scan_total(double x, double* part, int tid, double* total) {
-  const int lane = tid & 63, w = tid >> 6;
-  double incl = x;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const double y = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += y;
-  }
-  if (lane == 63) part[w] = incl;
-  __syncthreads();
-  double before = 0.0, all = 0.0;
-  for (int q = 0; q < NT / 64; ++q) {
-    if (q == w) before = all;
-    all += part[q];
-  }
-  __syncthreads();
-  *total = all;
-  return before + incl - x;
-}
-
-constexpr int kS0 = kBins0 / 2;  // threads of the level-0 selection: two adjacent bins each
-
-struct Sel0Shared {
-  double pd[kS0 / 64];
-  uint32_t pu[kS0 / 64];
-  int pi[kS0 / 64];
-  uint32_t cab[2];
-  double mab[2];
-  uint32_t klo[2], khi[2];
-};
-
-// Level-0 selection: one workgroup per row slot, thread t holding bins 2t
-// and 2t + 1.  The row's segment histograms are shifted onto the row's grid
-// point and merged in segment order; bin masses, in units of the row
-// maximum's weight, are edge x (count + sum 2^-21), and the row's total mass
-// is the sum of the masses of bins 0..510 (bin 511's never enters; its count
-// is the row's length less the other bins').  The boundary bin of each
-// search is the last non-empty bin whose count (top-k) or mass (top-p,
-// against top_p x the row's total) above it is below the target; the search
-// continues over that bin's keys with the count and mass above it.
-template <typename ET>
-__global__ __launch_bounds__(kS0) void filt_select0_kernel(FiltArgs a) {
-  __shared__ Sel0Shared sh;
-  const int tid = threadIdx.x, lane = tid & 63;
+__global__ __launch_bounds__(kFT) void filt_keys_first_kernel(FiltArgs a) {
+  __shared__ HistShared sh;
   const int n = a.nseg2, R = a.R;
-  const int rs = int(blockIdx.x % uint32_t(R));
-  const int b = int(blockIdx.x / uint32_t(R));
-  const ReqFilter f = req_filter(a, b);
-  if (!row_filtered(a, f, rs)) return;
-  const size_t row = size_t(b) * R + rs;
-  const int j0 = 2 * tid;
-  const float c = kLog2e / f.T;
-  const float c8 = c * float(kBinsPerLog2);
-  const float m = wave_row_max(a.partials + row * n, n, lane);
-  const float g = grid_point(m, c8);
-  uint32_t cnt[2] = {0u, 0u};
-  uint64_t frac[2] = {0u, 0u};  // up to V x 189812: beyond 32 bits for long runs of equal logits
-#pragma unroll 4
-  for (int s = 0; s < n; ++s) {
-    // cells between the row's grid point and the segment's; a segment
-    // without a finite logit (infinite shift) stored no bins
-    const float shc = g - grid_point(a.partials[row * n + s].m, c8);
-    const int jl = j0 - int(fminf(shc, float(kBins0)));
-    const uint32_t* h = a.hcount + (row * n + s) * 2 * kBins0;
-#pragma unroll
-    for (int q = 0; q < 2; ++q)
-      if (j0 + q < kBins0 - 1 && jl + q >= 0) {
-        cnt[q] += h[jl + q];
-        frac[q] += h[kBins0 + jl + q];
-      }
-  }
-  // the last bin holds every element not in the others
-  uint32_t in_bins;
-  {
-    const uint32_t x = cnt[0] + cnt[1];
-    const uint32_t ex = block_excl_scan<kS0, uint32_t>(x, sh.pu, tid);
-    if (tid == kS0 - 1) sh.pu[0] = ex + x;
-    __syncthreads();
-    in_bins = sh.pu[0];
-    __syncthreads();
-  }
-  if (tid == kS0 - 1) cnt[1] = uint32_t(a.V) - in_bins;
-  // edge of bin j relative to the row maximum's weight: 2^((g - j)/8 - m c)
-  const double mc = double(m * c);
-  double mass[2];
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int j = j0 + q;
-    const double edge = exp2(double(g - float(j)) * (1.0 / kBinsPerLog2) - mc);
-    mass[q] = j < kBins0 - 1 && cnt[q] > 0u ? edge * (double(cnt[q]) + double(frac[q]) / double(kFrac0)) : 0.0;
-  }
-  const uint32_t fcb = block_excl_scan<kS0, uint32_t>(cnt[0] + cnt[1], sh.pu, tid);
-  double S;
-  const double fmb = block_excl_scan_total<kS0>(mass[0] + mass[1], sh.pd, tid, &S);
-  const uint32_t fc[2] = {fcb, fcb + cnt[0]};
-  const double fm[2] = {fmb, fmb + mass[0]};
-  const double tk = double(f.top_k);
-  const double tp = double(f.top_p) * S;
-  const int first = cnt[0] > 0u ? j0 : (cnt[1] > 0u ? j0 + 1 : kBins0);
-  int ck = -1, cp = -1;
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    if (f.on_k && cnt[q] > 0u && double(fc[q]) < tk) ck = j0 + q;
-    if (f.on_p && cnt[q] > 0u && fm[q] < tp) cp = j0 + q;
-  }
-  const int top = -block_max_int<kS0>(-first, sh.pi, tid);
-  const int jk = block_max_int<kS0>(ck, sh.pi, tid);
-  const int jp = block_max_int<kS0>(cp, sh.pi, tid);
-  const int jq[2] = {jk >= 0 ? jk : top, jp >= 0 ? jp : top};
-#pragma unroll
-  for (int qq = 0; qq < 2; ++qq)
-#pragma unroll
-    for (int q = 0; q < 2; ++q)
-      if (j0 + q == jq[qq]) {
-        sh.cab[qq] = fc[q];
-        sh.mab[qq] = fm[q];
-      }
-  if (lane == 0 && (tid >> 6) < 4) {
-    // the boundary bin's key interval: two bisections per search, one wave each
-    const int q = (tid >> 6) >> 1, side = (tid >> 6) & 1;
-    const bool on = q == 0 ? f.on_k : f.on_p;
-    if (on) {
-      if (side == 0) sh.klo[q] = key_lo_of_bin<ET>(jq[q], c8, g);
-      else sh.khi[q] = key_hi_of_bin<ET>(jq[q], c8, g);
-    }
-  }
-  __syncthreads();
-  if (tid < 2) {
-    const int q = tid;
-    const bool on = q == 0 ? f.on_k : f.on_p;
-    FSearch w{};
-    if (on) {
-      w.lo = sh.klo[q];
-      w.hi = sh.khi[q];
-      w.cabove = sh.cab[q];
-      w.mabove = sh.mab[q];
-      w.target = q == 0 ? tk : tp;
-      w.state = 1u;
-    }
-    a.search[row * 2 + q] = w;
-  }
+  const uint32_t item = blockIdx.x;
+  const int s = int(item % uint32_t(n));
+  const int rs = int((item / uint32_t(n)) % uint32_t(R));
+  const int b = int(item / (uint32_t(n) * uint32_t(R)));
+  keys_segment<ET, false>(a, b, rs, s, 1, 1, sh, threadIdx.x);
 }
 
-struct SelShared {
-  double pd[kFT / 64];
-  uint32_t p32[kFT / 64];
-  int pi[kFT / 64];
-};
-
-// Key-level selection: one workgroup per row slot; thread j owns digit
-// kBins - 1 - j, so that an exclusive scan in thread order sums the digits
-// of larger keys.
+// Selection of the first key level: one wave per row slot; a row still
+// searching is listed for the second.  Also clears the row's arrival
+// counter, used by the later levels.
 template <typename ET>
-__global__ __launch_bounds__(kFT) void filt_select_kernel(FiltArgs a) {
-  __shared__ SelShared sh;
+__global__ __launch_bounds__(64) void filt_select_kernel(FiltArgs a, int levels) {
+  __shared__ uint32_t base;
   const int tid = threadIdx.x;
-  const int n = a.nseg2, R = a.R;
+  const int R = a.R;
   const int rs = int(blockIdx.x % uint32_t(R));
   const int b = int(blockIdx.x / uint32_t(R));
+  const size_t row = size_t(b) * R + rs;
+  if (tid == 0) a.tickets[row] = 0u;
   const ReqFilter f = req_filter(a, b);
   if (!row_filtered(a, f, rs)) return;
-  const size_t row = size_t(b) * R + rs;
-  FSearch* st = a.search + row * 2;
-  const float c = kLog2e / f.T;
-  const float mc = wave_row_max(a.partials + row * n, n, tid & 63) * c;
-#pragma unroll 1
-  for (int q = 0; q < 2; ++q) {
-    const FSearch cur = st[q];
-    if (cur.state != 1u) continue;
-    const double mabove = cur.mabove;
-    const uint32_t w = cur.hi - cur.lo;
-    const int shf = w == 0u ? 0 : max(0, 32 - __clz(w) - 8);
-    const int d = kBins - 1 - tid;
-    uint64_t mfix = 0;
-    uint32_t cd = 0;
-#pragma unroll 8
-    for (int s = 0; s < n; ++s) {
-      cd += a.hcount[(row * n + s) * 2 * kBins0 + q * kBins0 + d];
-      if (shf > 0) mfix += a.hmass[((row * n + s) * 2 + q) * kBins + d];
-    }
-    // a one-key digit's mass: its count times the weight of that key, the
-    // same float expression as an element's weight
-    const double md = shf > 0 ? double(mfix) / double(kFix)
-                              : (cd > 0u ? double(cd) * double(fast_exp2(fmaf(Key<ET>::value(cur.lo + uint32_t(d)), c,
-                                                                                  -mc)))
-                                         : 0.0);
-    const double fm = mabove + block_excl_scan<kFT, double>(md, sh.pd, tid);
-    const uint32_t fc = cur.cabove + block_excl_scan<kFT, uint32_t>(cd, sh.p32, tid);
-    const bool ok = cd > 0u && (q == 0 ? double(fc) < cur.target : fm < cur.target);
-    // the smallest qualifying digit (the largest non-empty one if none is)
-    const int dq = -block_max_int<kFT>(ok ? -d : -kBins, sh.pi, tid);
-    const int dtop = block_max_int<kFT>(cd > 0u ? d : -1, sh.pi, tid);
-    const int ds = dq < kBins ? dq : dtop;
-    if (d != ds) continue;
-    FSearch nx = cur;
-    const uint64_t lo = uint64_t(cur.lo) + (uint64_t(d) << shf);
-    const uint64_t hi = min(uint64_t(cur.hi), lo + (uint64_t(1) << shf) - 1);
-    nx.lo = uint32_t(lo);
-    nx.hi = uint32_t(hi);
-    nx.mabove = fm;
-    nx.cabove = fc;
-    if (lo == hi) {
-      nx.state = 2u;
-      nx.key = uint32_t(lo);
-      nx.kept = fc + cd;
-      nx.mfinal = fm + md;
-    }
-    st[q] = nx;
+  if (select_row<ET, false>(a, kLog2e / f.T, row, tid)) list_row(a, row, 1, levels, &base, tid);
+}
+
+// Later key levels: the segments listed by the previous level's selections,
+// taken in list order by a grid of workgroups (most levels list none).
+template <typename ET>
+__global__ __launch_bounds__(kFT) void filt_keys_next_kernel(FiltArgs a, int level, int levels) {
+  __shared__ HistShared sh;
+  const int n = a.nseg2, R = a.R;
+  const uint32_t count = a.wcount[level - 2];
+  const uint32_t* list = a.work + size_t(level & 1) * (size_t(a.B) * R * n);
+  for (uint32_t e = blockIdx.x; e < count; e += gridDim.x) {
+    const uint32_t item = list[e];
+    const int s = int(item % uint32_t(n));
+    const int rs = int((item / uint32_t(n)) % uint32_t(R));
+    const int b = int(item / (uint32_t(n) * uint32_t(R)));
+    keys_segment<ET, true>(a, b, rs, s, level, levels, sh, threadIdx.x);
+    __syncthreads();  // the shared arrays are reused by the next segment
   }
 }
 
@@ -1077,31 +1245,32 @@ hipError_t launch_filtered(VerifyArgs va, const FilterIO& io, int dtype, hipStre
              va.target_start, va.target_stride, va.num_draft, va.tokens, va.temperature, io.top_k, io.top_p,
              va.u_accept, va.u_residual, va.u_bonus, va.accept_len, va.out_tokens, va.labels, va.p_draft,
              va.p_target, io.kept, va.partials, va.zval, io.hmass, io.hcount,
-             reinterpret_cast<FSearch*>(io.search)};
+             reinterpret_cast<FSearch*>(io.search), io.tickets, io.work, io.wcount};
   const unsigned g1 = unsigned(n1), g2 = unsigned(va.B) * unsigned(va.R);
   const unsigned gw = unsigned(va.B) * unsigned(va.nseg2);
+  const unsigned gn = unsigned(min(n1, uint64_t(2048)));  // workgroups of the later key levels
   RowInfo* info = reinterpret_cast<RowInfo*>(io.info);
   DrawDesc* desc = reinterpret_cast<DrawDesc*>(io.desc);
   float* slices = io.slices;
-  const int levels = dtype == SV_BF16 ? 2 : 4;  // key-digit levels after level 0
+  const int levels = dtype == SV_BF16 ? 2 : kMaxKeyLevels;  // key-digit levels after level 0
   if (dtype == SV_BF16) {
     hipLaunchKernelGGL(filt_stats0_kernel<uint16_t>, dim3(g1), dim3(kFT), 0, stream, a);
-    hipLaunchKernelGGL(filt_select0_kernel<uint16_t>, dim3(g2), dim3(kS0), 0, stream, a);
-    for (int l = 0; l < levels; ++l) {
-      hipLaunchKernelGGL(filt_keys_kernel<uint16_t>, dim3(g1), dim3(kFT), 0, stream, a);
-      hipLaunchKernelGGL(filt_select_kernel<uint16_t>, dim3(g2), dim3(kFT), 0, stream, a);
-    }
+    hipLaunchKernelGGL(filt_select0_kernel<uint16_t>, dim3(g2), dim3(64), 0, stream, a);
+    hipLaunchKernelGGL(filt_keys_first_kernel<uint16_t>, dim3(g1), dim3(kFT), 0, stream, a);
+    hipLaunchKernelGGL(filt_select_kernel<uint16_t>, dim3(g2), dim3(64), 0, stream, a, levels);
+    for (int l = 2; l <= levels; ++l)
+      hipLaunchKernelGGL(filt_keys_next_kernel<uint16_t>, dim3(gn), dim3(kFT), 0, stream, a, l, levels);
     hipLaunchKernelGGL(filt_verdict_kernel<uint16_t>, dim3(unsigned(va.B)), dim3(64), 0, stream, a, info, desc);
     hipLaunchKernelGGL(filt_weight_kernel<uint16_t>, dim3(gw), dim3(kFT), 0, stream, a, info, desc, slices);
     hipLaunchKernelGGL(filt_search_kernel<uint16_t>, dim3(unsigned(va.B)), dim3(kFT), 0, stream, a, info, desc,
                        slices);
   } else {
     hipLaunchKernelGGL(filt_stats0_kernel<float>, dim3(g1), dim3(kFT), 0, stream, a);
-    hipLaunchKernelGGL(filt_select0_kernel<float>, dim3(g2), dim3(kS0), 0, stream, a);
-    for (int l = 0; l < levels; ++l) {
-      hipLaunchKernelGGL(filt_keys_kernel<float>, dim3(g1), dim3(kFT), 0, stream, a);
-      hipLaunchKernelGGL(filt_select_kernel<float>, dim3(g2), dim3(kFT), 0, stream, a);
-    }
+    hipLaunchKernelGGL(filt_select0_kernel<float>, dim3(g2), dim3(64), 0, stream, a);
+    hipLaunchKernelGGL(filt_keys_first_kernel<float>, dim3(g1), dim3(kFT), 0, stream, a);
+    hipLaunchKernelGGL(filt_select_kernel<float>, dim3(g2), dim3(64), 0, stream, a, levels);
+    for (int l = 2; l <= levels; ++l)
+      hipLaunchKernelGGL(filt_keys_next_kernel<float>, dim3(gn), dim3(kFT), 0, stream, a, l, levels);
     hipLaunchKernelGGL(filt_verdict_kernel<float>, dim3(unsigned(va.B)), dim3(64), 0, stream, a, info, desc);
     hipLaunchKernelGGL(filt_weight_kernel<float>, dim3(gw), dim3(kFT), 0, stream, a, info, desc, slices);
     hipLaunchKernelGGL(filt_search_kernel<float>, dim3(unsigned(va.B)), dim3(kFT), 0, stream, a, info, desc,

@@ -71,14 +71,16 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Filtered verification: after the verification layout, per (row slot,
 // 32 KiB segment, search) histograms of kFilterBins bins (fixed-point masses
-// and counts) and per (row slot, search) threshold-search states.
+// and counts), per (row slot, search) threshold-search states, per row slot
+// an arrival counter, and the lists of segments still searching (two, used
+// by turns) with their counters.
 constexpr int kFilterBins = 256;    // key-digit bins
 constexpr int kFilterBins0 = 512;  // level-0 bins
 constexpr size_t kFilterSearchBytes = 48;
 constexpr size_t kFilterRowBytes = 16;   // per row slot: normaliser, threshold, argmax
 constexpr size_t kFilterDescBytes = 16;  // per request: accept length, draw kind, uniform
 struct FilterLayout {
-  size_t hmass, hcount, search, info, desc, slices, total;
+  size_t hmass, hcount, search, info, desc, slices, tickets, work, wcount, total;
 };
 
 // Hand-off slot of the draw kernel: 8 bytes written in one store, the low
@@ -114,7 +116,10 @@ inline FilterLayout filter_layout(int B, int V, int max_k, int dtype) {
   F.info = F.search + align256(size_t(B) * L.R * 2 * kFilterSearchBytes);
   F.desc = F.info + align256(size_t(B) * L.R * kFilterRowBytes);
   F.slices = F.desc + align256(size_t(B) * kFilterDescBytes);
-  F.total = F.slices + align256(size_t(B) * L.nseg2 * 2 * kDrawSlices * 4);
+  F.tickets = F.slices + align256(size_t(B) * L.nseg2 * 2 * kDrawSlices * 4);
+  F.work = F.tickets + align256(size_t(B) * L.R * 4);
+  F.wcount = F.work + align256(2 * segs * 4);
+  F.total = F.wcount + 256;
   return F;
 }
 
@@ -190,6 +195,9 @@ struct FilterIO {
   void* info;
   void* desc;
   float* slices;
+  uint32_t* tickets;
+  uint32_t* work;
+  uint32_t* wcount;
 };
 hipError_t launch_filtered(VerifyArgs a, const FilterIO& io, int dtype, hipStream_t stream);
 hipError_t launch_av_budget(int B, int max_k, const float* score, const int32_t* num_draft, const float* draft_cost,
