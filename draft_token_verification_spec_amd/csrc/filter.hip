@@ -647,10 +647,15 @@ __global__ __launch_bounds__(kFT) __attribute__((amdgpu_waves_per_eu(8))) void f
     // r = 2^(z c - gs/8 + bin/8) in [1, 2^(1/8)); r - 1 in 2^-21 units
     // rounded half up: in [0, 189812] for bins below 511 (the last bin is
     // never read: there the conversion saturates at 0)
-    auto add0 = [&](float z, float jf) {
-      const float r = fast_exp2(fmaf(jf, 1.f / kBinsPerLog2, fmaf(z, c, -g8)));
+    // The bin is taken as its byte offset in sh.bins, 8 (gs - F(z)) clamped
+    // to [0, 8 x 511] (bin0f's value times 8, exactly), so that it converts
+    // straight to an LDS address.
+    const float gs8 = gs * 8.f;
+    auto add0 = [&](float z) {
+      const float jb = __builtin_amdgcn_fmed3f(fmaf(cell_of(z, c8), -8.f, gs8), 0.f, float(8 * (kBins0 - 1)));
+      const float r = fast_exp2(fmaf(jb, 1.f / (8 * kBinsPerLog2), fmaf(z, c, -g8)));
       const uint32_t u = uint32_t(fmaf(r, kFrac0, 0.5f - kFrac0));
-      atomicAdd(reinterpret_cast<unsigned long long*>(&sh.bins[int(jf)]),
+      atomicAdd(reinterpret_cast<unsigned long long*>(reinterpret_cast<char*>(sh.bins) + int(jb)),
                 (static_cast<unsigned long long>(u) << 32) | 1ull);
     };
     // past the end of the row the loads hold -inf (bin 511, never read by
@@ -660,10 +665,7 @@ __global__ __launch_bounds__(kFT) __attribute__((amdgpu_waves_per_eu(8))) void f
     for (int k = 0; k < kFV; ++k) {
       if (hb + (k * kFT + tid) * N >= a.V) continue;
 #pragma unroll
-      for (int j = 0; j < N; ++j) {
-        const float z = Elem<ET>::get(v[k], j);
-        add0(z, bin0f(z, c8, gs));
-      }
+      for (int j = 0; j < N; ++j) add0(Elem<ET>::get(v[k], j));
     }
     __syncthreads();
     int last = -1;
