@@ -274,10 +274,22 @@ __device__ __forceinline__ bool arrive_last_all(uint32_t* ticket, uint32_t want,
 
 // The smallest key whose level-0 bin is <= j and the largest whose bin is
 // >= j (the bin is non-increasing in the key): the keys of bins [.., j] and
-// [j, ..].
+// [j, ..].  Bisections of the key space; they start from a few keys around
+// the bin edge's value ((g - j)/8c, resp. (g - j + 1)/8c) when those keys
+// are seen to enclose the answer, and from the whole key space otherwise.
 template <typename ET>
 __device__ uint32_t key_lo_of_bin(int j, float c8, float g) {
   uint64_t lo = Key<ET>::kMin, hi = Key<ET>::kMax;
+  const float ze = (g - float(j)) / c8;
+  if (isfinite(ze)) {
+    const uint64_t k0 = Key<ET>::of(ze);
+    const uint64_t l = max(k0, uint64_t(Key<ET>::kMin) + 4) - 4, h = min(k0 + 4, uint64_t(Key<ET>::kMax));
+    if (bin0(Key<ET>::value(uint32_t(h)), c8, g) <= j &&
+        (l == Key<ET>::kMin || bin0(Key<ET>::value(uint32_t(l - 1)), c8, g) > j)) {
+      lo = l;
+      hi = h;
+    }
+  }
   while (lo < hi) {
     const uint64_t mid = (lo + hi) >> 1;
     if (bin0(Key<ET>::value(uint32_t(mid)), c8, g) <= j) hi = mid;
@@ -289,6 +301,16 @@ __device__ uint32_t key_lo_of_bin(int j, float c8, float g) {
 template <typename ET>
 __device__ uint32_t key_hi_of_bin(int j, float c8, float g) {
   uint64_t lo = Key<ET>::kMin, hi = Key<ET>::kMax;
+  const float ze = (g - float(j) + 1.f) / c8;
+  if (isfinite(ze)) {
+    const uint64_t k0 = Key<ET>::of(ze);
+    const uint64_t l = max(k0, uint64_t(Key<ET>::kMin) + 4) - 4, h = min(k0 + 4, uint64_t(Key<ET>::kMax));
+    if (bin0(Key<ET>::value(uint32_t(l)), c8, g) >= j &&
+        (h == Key<ET>::kMax || bin0(Key<ET>::value(uint32_t(h + 1)), c8, g) < j)) {
+      lo = l;
+      hi = h;
+    }
+  }
   while (lo < hi) {
     const uint64_t mid = (lo + hi + 1) >> 1;
     if (bin0(Key<ET>::value(uint32_t(mid)), c8, g) >= j) lo = mid;
