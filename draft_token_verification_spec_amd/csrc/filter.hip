@@ -27,6 +27,8 @@
 // workgroup per row: segment histograms merged in order, exclusive scans,
 // the boundary bin or digit).  The verdict, the residual / bonus weights and
 // the draw then run on the filtered rows.
+#include <type_traits>
+
 #include "sv_segment.hpp"
 
 namespace sv {
@@ -175,6 +177,19 @@ __device__ __forceinline__ ReqFilter req_filter(const FiltArgs& a, int b) {
   f.on_k = stoch && f.top_k > 0 && f.top_k < a.V;
   f.on_p = stoch && f.top_p < 1.f;
   return f;
+}
+
+// The value is in a register at this point: loads written before a kernel's
+// first decision and pinned there go out together, instead of one round
+// trip after another as the compiler would otherwise issue them (each kernel
+// argument pointer loaded where it is first needed).
+template <typename A, typename B, typename C, typename D, typename E, typename F>
+__device__ __forceinline__ void pin(const A& x0, const B& x1, const C& x2, const D& x3, const E& x4, const F& x5) {
+  asm volatile("" ::"v"(x0), "v"(x1), "v"(x2), "v"(x3), "v"(x4), "v"(x5));
+}
+template <typename A, typename B, typename C>
+__device__ __forceinline__ void pin(const A& x0, const B& x1, const C& x2) {
+  asm volatile("" ::"v"(x0), "v"(x1), "v"(x2));
 }
 
 // Is row slot rs (draft i at i, target j at max_k + j) of the request read
@@ -358,16 +373,17 @@ struct Sel0Shared {
 // against top_p x the row's total) above it is below the target; the search
 // continues over that bin's keys with the count and mass above it.
 template <typename ET>
-__device__ void select0_row(const FiltArgs& a, const ReqFilter& f, size_t row, Sel0Shared& sh, int lane) {
+__device__ void select0_row(const FiltArgs& a, const ReqFilter& f, size_t row, const Partial& p0, Sel0Shared& sh,
+                            int lane) {
   static_assert(kSelBins == 8 && kBinsPerLog2 == 8, "a lane's bins are one log2 unit: edges 2^-t x 2^(-q/8)");
   const int n = a.nseg2;
   const int j0 = kSelBins * lane;
   const float c = kLog2e / f.T;
   const float c8 = c * float(kBinsPerLog2);
-  // the segment maxima and the row's
+  // the segment maxima and the row's (segment `lane` preloaded as p0)
   float m = -INFINITY;
   for (int q = lane; q < n; q += 64) {
-    const Partial x = a.partials[row * n + q];
+    const Partial x = q == lane ? p0 : a.partials[row * n + q];
     sh.segm[q] = x.m;
     sh.segn[q] = x.idx;
     m = fmaxf(m, x.m);
@@ -379,19 +395,34 @@ __device__ void select0_row(const FiltArgs& a, const ReqFilter& f, size_t row, S
   uint32_t cnt[kSelBins] = {};
   uint64_t frac[kSelBins] = {};  // up to V x 189812: beyond 32 bits for long runs of equal logits
   const uint64_t* h64 = reinterpret_cast<const uint64_t*>(a.hcount) + row * n * kBins0;
-#pragma unroll 2
-  for (int s = 0; s < n; ++s) {
-    // cells between the row's grid point and the segment's; a segment
-    // stored its bins 0 .. nbs - 1 (none without a finite logit)
-    const float shc = g - grid_point(sh.segm[s], c8);
-    const int jl = j0 - int(fminf(shc, float(kBins0)));
-    const int nbs = sh.segn[s];
+  // Segments are taken kGather at a time: every lane loads all its bins of
+  // them (clamped into each segment's array, those out of range masked
+  // afterwards) before adding any, so that the loads go out together.
+  constexpr int kGather = 4;
+  for (int s0 = 0; s0 < n; s0 += kGather) {
+    uint64_t x[kGather][kSelBins];
+    bool in[kGather][kSelBins];
 #pragma unroll
-    for (int q = 0; q < kSelBins; ++q)
-      if (j0 + q < kBins0 - 1 && jl + q >= 0 && jl + q < nbs) {
-        const uint64_t x = h64[size_t(s) * kBins0 + jl + q];
-        cnt[q] += uint32_t(x);
-        frac[q] += x >> 32;
+    for (int u = 0; u < kGather; ++u) {
+      const int s = min(s0 + u, n - 1);
+      // cells between the row's grid point and the segment's; a segment
+      // stored its bins 0 .. nbs - 1 (none without a finite logit)
+      const float shc = g - grid_point(sh.segm[s], c8);
+      const int jl = j0 - int(fminf(shc, float(kBins0)));
+      const int nbs = s0 + u < n ? sh.segn[s] : 0;
+#pragma unroll
+      for (int q = 0; q < kSelBins; ++q) {
+        const int jj = jl + q;
+        in[u][q] = j0 + q < kBins0 - 1 && jj >= 0 && jj < nbs;
+        x[u][q] = h64[size_t(s) * kBins0 + min(max(jj, 0), kBins0 - 1)];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kGather; ++u)
+#pragma unroll
+      for (int q = 0; q < kSelBins; ++q) {
+        cnt[q] += in[u][q] ? uint32_t(x[u][q]) : 0u;
+        frac[q] += in[u][q] ? (x[u][q] >> 32) : 0ull;
       }
   }
   // the last bin (lane 63's last) holds every element not in the others
@@ -481,10 +512,9 @@ constexpr int kSelDigits = kBins / 64;  // key digits per lane of the selection
 // histograms are merged in segment order.  Returns (in every lane) whether
 // a search of the row is still open.
 template <typename ET, bool DEV>
-__device__ bool select_row(const FiltArgs& a, float c, size_t row, int lane) {
+__device__ bool select_row(const FiltArgs& a, float c, float mc, size_t row, int lane) {
   const int n = a.nseg2;
   FSearch* st = a.search + row * 2;
-  const float mc = wave_row_max(a.partials + row * n, n, lane) * c;
   int more = 0;
 #pragma unroll 1
   for (int q = 0; q < 2; ++q) {
@@ -493,25 +523,50 @@ __device__ bool select_row(const FiltArgs& a, float c, size_t row, int lane) {
     const uint32_t w = cur.hi - cur.lo;
     const int shf = w == 0u ? 0 : max(0, 32 - __clz(w) - 8);
     const int nd = int(w >> shf);  // the interval's last digit (no others are stored)
-    uint32_t cd[kSelDigits];
+    uint32_t cd[kSelDigits] = {};
+    uint64_t mfix[kSelDigits] = {};
+    // segments kGather at a time, every load of them issued before any sum
+    // (digits past the interval's last and segments past the row's are
+    // loaded from within the arrays and masked)
+    constexpr int kGather = 4;
+    auto gather = [&](auto wide_t) {
+      constexpr bool wide = decltype(wide_t)::value;
+      for (int s0 = 0; s0 < n; s0 += kGather) {
+        uint32_t xc[kGather][kSelDigits];
+        uint64_t xm[kGather][kSelDigits];
+#pragma unroll
+        for (int u = 0; u < kGather; ++u) {
+          const size_t seg = row * n + min(s0 + u, n - 1);
+#pragma unroll
+          for (int k = 0; k < kSelDigits; ++k) {
+            const int d = kBins - 1 - (kSelDigits * lane + k);
+            xc[u][k] = load_h32<DEV>(&a.hcount[seg * 2 * kBins0 + q * kBins0 + d]);
+            if constexpr (wide) xm[u][k] = load_h64<DEV>(&a.hmass[(seg * 2 + q) * kBins + d]);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < kGather; ++u)
+#pragma unroll
+          for (int k = 0; k < kSelDigits; ++k) {
+            const int d = kBins - 1 - (kSelDigits * lane + k);
+            const bool in = s0 + u < n && d <= nd;
+            cd[k] += in ? xc[u][k] : 0u;
+            if constexpr (wide) mfix[k] += in ? xm[u][k] : 0ull;
+          }
+      }
+    };
+    // masses are stored only for digits wider than one key
+    if (shf > 0) gather(std::true_type{});
+    else gather(std::false_type{});
     double md[kSelDigits];
     uint32_t tc = 0;
     double tm = 0.0;
 #pragma unroll
     for (int k = 0; k < kSelDigits; ++k) {
       const int d = kBins - 1 - (kSelDigits * lane + k);
-      uint64_t mfix = 0;
-      cd[k] = 0;
-      if (d <= nd) {
-#pragma unroll 4
-        for (int s = 0; s < n; ++s) {
-          cd[k] += load_h32<DEV>(&a.hcount[(row * n + s) * 2 * kBins0 + q * kBins0 + d]);
-          if (shf > 0) mfix += load_h64<DEV>(&a.hmass[((row * n + s) * 2 + q) * kBins + d]);
-        }
-      }
       // a one-key digit's mass: its count times the weight of that key, the
       // same float expression as an element's weight
-      md[k] = shf > 0 ? double(mfix) / double(kFix)
+      md[k] = shf > 0 ? double(mfix[k]) / double(kFix)
                       : (cd[k] > 0u ? double(cd[k]) * double(fast_exp2(fmaf(Key<ET>::value(cur.lo + uint32_t(d)), c,
                                                                                 -mc)))
                                     : 0.0);
@@ -711,12 +766,16 @@ __global__ __launch_bounds__(64) void filt_select0_kernel(FiltArgs a) {
   __shared__ Sel0Shared sh;
   const int tid = threadIdx.x;
   if (blockIdx.x == 0 && tid < kMaxKeyLevels) a.wcount[tid] = 0u;
-  const int R = a.R;
+  const int R = a.R, n = a.nseg2;
   const int rs = int(blockIdx.x % uint32_t(R));
   const int b = int(blockIdx.x / uint32_t(R));
+  const size_t row = size_t(b) * R + rs;
+  // the row's first 64 segment statistics and the request's scalars in one round trip
+  const Partial p0 = a.partials[row * n + min(tid, n - 1)];
   const ReqFilter f = req_filter(a, b);
+  pin(f.K, f.T, f.top_k, f.top_p, p0.m, p0.idx);
   if (!row_filtered(a, f, rs)) return;
-  select0_row<ET>(a, f, size_t(b) * R + rs, sh, tid);
+  select0_row<ET>(a, f, row, p0, sh, tid);
 }
 
 // ---------------------------------------------------------------------------
@@ -857,7 +916,7 @@ __device__ void keys_segment(const FiltArgs& a, int b, int rs, int s, int level,
   if (!LATER) return;
   if (!arrive_last_all(&a.tickets[row], uint32_t(n), &sh.last)) return;
   if (tid < 64) {
-    const bool more = select_row<ET, true>(a, c, row, tid);
+    const bool more = select_row<ET, true>(a, c, mc, row, tid);
     if (tid == 0) sh.more = more ? 1 : 0;
   }
   __syncthreads();
@@ -888,10 +947,21 @@ __global__ __launch_bounds__(64) void filt_select_kernel(FiltArgs a, int levels)
   const int rs = int(blockIdx.x % uint32_t(R));
   const int b = int(blockIdx.x / uint32_t(R));
   const size_t row = size_t(b) * R + rs;
+  const int n = a.nseg2;
   if (tid == 0) a.tickets[row] = 0u;
+  // the row's segment maxima (the first 64), its search states and the
+  // request's scalars in one round trip
+  float m = a.partials[row * n + min(tid, n - 1)].m;
+  const uint32_t s0 = a.search[row * 2].state, s1 = a.search[row * 2 + 1].state;
   const ReqFilter f = req_filter(a, b);
+  pin(m, s0, s1, f.K, f.T, f.top_p);
+  pin(f.top_k, m, m);
   if (!row_filtered(a, f, rs)) return;
-  if (select_row<ET, false>(a, kLog2e / f.T, row, tid)) list_row(a, row, 1, levels, &base, tid);
+  for (int q = tid + 64; q < n; q += 64) m = fmaxf(m, a.partials[row * n + q].m);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  const float c = kLog2e / f.T;
+  if (select_row<ET, false>(a, c, m * c, row, tid)) list_row(a, row, 1, levels, &base, tid);
 }
 
 // Later key levels: the segments listed by the previous level's selections,
