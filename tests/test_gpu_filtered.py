@@ -266,6 +266,33 @@ def test_segment_maxima_far_apart():
         assert compare_filtered(b, gout, o) <= 1
 
 
+def test_boundary_among_dense_keys_near_zero():
+    """bf16 logits within a few hundredths of zero: the level-0 cell of the
+    boundary holds thousands of distinct keys, so the first key level
+    leaves the search open and the second one, over the segments of the
+    rows still searching only, finishes it; rows of ordinary spread in the
+    same batch finish at the first key level."""
+    g = np.random.default_rng(31)
+    B, K, V = 6, 2, 40000
+    zd = g.normal(0, 0.01, (B, K, V)).astype(np.float32)
+    zt = g.normal(0, 0.01, (B, K + 1, V)).astype(np.float32)
+    zd[3:] *= 300.0
+    zt[3:] *= 300.0
+    c8 = 8.0 * np.log2(np.e)
+    for top_k, top_p in [(0, 0.5), (V // 3, 1.0), (V // 2, 0.3)]:
+        b = _batch(zd, zt, _draws(zd, 1.0, 5), 1.0, top_k, top_p, dtype="bf16")
+        _log(f"case filtered dense keys k={top_k} p={top_p}")
+        gout, o = _run(b)
+        assert compare_filtered(b, gout, o) <= 1
+        # the claim above: a boundary cell with more distinct keys than one
+        # 8-bit key level resolves
+        rows = gen.bf16_bits_to_f32(b.target[:K + 1])
+        z = np.sort(rows[0])[::-1]
+        t = z[int(o["kept"][0, K]) - 1]
+        cell = np.floor(rows[0] * np.float32(c8))
+        assert len(np.unique(rows[0][cell == np.floor(np.float32(t) * np.float32(c8))])) > 256
+
+
 def test_temperatures_max_draft_length_and_largest_vocabulary():
     g = np.random.default_rng(2)
     B, K, V = 3, 16, 4096
