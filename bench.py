@@ -128,6 +128,9 @@ def summarize_counters(args):
            "bytes_per_call": sum(out[k]["bytes_per_launch"] for k in call),
            "fetch_scale": scale["FETCH_SIZE"], "write_scale": scale["WRITE_SIZE"], "kernels": out,
            "kernel_source_sha256": kernel_source_hash()}
+    if all(k in out for k in FILTERED_KERNELS):
+        rec["filtered_bytes_per_call"] = sum(out[k]["bytes_per_launch"] for k in FILTERED_KERNELS)
+        rec["filtered_kernel_source_sha256"] = kernel_source_hash(filtered=True)
     with open(args.traffic, "w") as fh:
         json.dump(rec, fh, indent=1)
         fh.write("\n")
@@ -139,31 +142,39 @@ CALL_KERNELS = ("stats_kernel", "draw_kernel")
 SCORE_KERNELS = ("score_stats_kernel", "score_finish_kernel")
 
 
-def kernel_source_hash() -> str:
-    """sha256 over the sources the verification kernels are built from, to
-    tell whether stored counter measurements still describe them."""
+def kernel_source_hash(filtered: bool = False) -> str:
+    """sha256 over the sources the verification kernels (or, with filtered,
+    the filtered verification's kernels) are built from, to tell whether
+    stored counter measurements still describe them."""
     import hashlib
 
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "draft_token_verification_spec_amd", "csrc")
-    for name in ("stream.hip", "sv_segment.hpp", "sv_device.hpp", "sv_internal.hpp"):
+    names = ("filter.hip",) if filtered else ("stream.hip",)
+    for name in names + ("sv_segment.hpp", "sv_device.hpp", "sv_internal.hpp"):
         h.update(name.encode())
         h.update(open(os.path.join(csrc, name), "rb").read())
     return h.hexdigest()
 
 
-def stored_traffic(args):
-    """Measured HBM bytes per call, if recorded for this workload and the
-    current kernel sources; else None."""
+# the kernels of one sv_spec_verify_filtered call
+FILTERED_KERNELS = ("filt_stats0_kernel", "filt_select0_kernel", "filt_keys_first_kernel", "filt_select_kernel",
+                    "filt_keys_next_kernel", "filt_verdict_kernel", "filt_weight_kernel", "filt_search_kernel")
+
+
+def stored_traffic(args, filtered: bool = False):
+    """Measured HBM bytes per call (of the filtered call, with filtered), if
+    recorded for this workload and the current kernel sources; else None."""
     if not os.path.exists(args.traffic):
         return None
     try:
         tr = json.load(open(args.traffic))
     except (OSError, ValueError):
         return None
-    if tr.get("workload") != args.workload or tr.get("kernel_source_sha256") != kernel_source_hash():
+    key = "filtered_" if filtered else ""
+    if tr.get("workload") != args.workload or tr.get(key + "kernel_source_sha256") != kernel_source_hash(filtered):
         return None
-    return tr.get("bytes_per_call")
+    return tr.get(key + "bytes_per_call")
 
 
 # ---------------------------------------------------------------------------
@@ -714,7 +725,8 @@ def extras(args, res, sv, sets, batches, outs, params, ws, call, dev, log):
             fcall(i)
         ms, _ = graph_ms(rot(fcall), 10, dev)
         fbytes = verify_bytes(b0, b0.num_draft)
-        ex["filtered_verify"] = roofline(fbytes, ms, kernel="sv_spec_verify_filtered call", top_p=0.95,
+        ex["filtered_verify"] = roofline(fbytes, ms, stored_traffic(args, filtered=True),
+                                         kernel="sv_spec_verify_filtered call", top_p=0.95,
                                          positions_per_s=pos / (ms * 1e-3),
                                          kept_tokens_mean=float(fo[0]["kept"][fo[0]["kept"] >= 0].float().mean()),
                                          mean_accept_len=float(fo[0]["accept_len"].float().mean()))

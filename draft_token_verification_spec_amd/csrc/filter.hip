@@ -396,7 +396,7 @@ __device__ void select0_row(const FiltArgs& a, const ReqFilter& f, size_t row, c
   uint64_t frac[kSelBins] = {};  // up to V x 189812: beyond 32 bits for long runs of equal logits
   const uint64_t* h64 = reinterpret_cast<const uint64_t*>(a.hcount) + row * n * kBins0;
   // Segments are taken kGather at a time: every lane loads all its bins of
-  // them (clamped into each segment's array, those out of range masked
+  // them (clamped into each segment's stored bins, those out of range masked
   // afterwards) before adding any, so that the loads go out together.
   constexpr int kGather = 4;
   for (int s0 = 0; s0 < n; s0 += kGather) {
@@ -414,7 +414,7 @@ __device__ void select0_row(const FiltArgs& a, const ReqFilter& f, size_t row, c
       for (int q = 0; q < kSelBins; ++q) {
         const int jj = jl + q;
         in[u][q] = j0 + q < kBins0 - 1 && jj >= 0 && jj < nbs;
-        x[u][q] = h64[size_t(s) * kBins0 + min(max(jj, 0), kBins0 - 1)];
+        x[u][q] = h64[size_t(s) * kBins0 + min(max(jj, 0), max(nbs - 1, 0))];
       }
     }
 #pragma unroll
@@ -526,8 +526,8 @@ __device__ bool select_row(const FiltArgs& a, float c, float mc, size_t row, int
     uint32_t cd[kSelDigits] = {};
     uint64_t mfix[kSelDigits] = {};
     // segments kGather at a time, every load of them issued before any sum
-    // (digits past the interval's last and segments past the row's are
-    // loaded from within the arrays and masked)
+    // (digits past the interval's last and segments past the row's load a
+    // stored entry instead and are masked)
     constexpr int kGather = 4;
     auto gather = [&](auto wide_t) {
       constexpr bool wide = decltype(wide_t)::value;
@@ -539,7 +539,7 @@ __device__ bool select_row(const FiltArgs& a, float c, float mc, size_t row, int
           const size_t seg = row * n + min(s0 + u, n - 1);
 #pragma unroll
           for (int k = 0; k < kSelDigits; ++k) {
-            const int d = kBins - 1 - (kSelDigits * lane + k);
+            const int d = min(kBins - 1 - (kSelDigits * lane + k), nd);  // within the stored digits
             xc[u][k] = load_h32<DEV>(&a.hcount[seg * 2 * kBins0 + q * kBins0 + d]);
             if constexpr (wide) xm[u][k] = load_h64<DEV>(&a.hmass[(seg * 2 + q) * kBins + d]);
           }
