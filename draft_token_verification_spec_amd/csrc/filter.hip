@@ -1023,23 +1023,42 @@ __global__ __launch_bounds__(64) void filt_verdict_kernel(FiltArgs a, RowInfo* i
   const int K = f.K;
   const bool greedy = !(f.T > 0.f);
   const float c = kLog2e / (greedy ? 1.f : f.T);
+  // lane i's position (i < max_k): token, logits at it, uniform, fetched now
+  // so that they arrive with the rows' statistics
+  const size_t o = size_t(b) * max_k + min(tid, max(max_k - 1, 0));
+  int d = 0;
+  float zd = 0.f, zt = 0.f, ua = 1.f;
+  if (tid < max_k) {
+    d = a.tokens[o];
+    zd = a.zval[size_t(b) * R + tid];
+    zt = a.zval[size_t(b) * R + max_k + tid];
+    ua = a.u_accept[o];
+  }
   if (tid < R) {
     const int rs = tid;
     const bool valid = rs < max_k ? (rs < K && !greedy) : (rs - max_k <= K);
     RowInfo r{0.f, 0u, 0, 0};
     int kept = -1;
     if (valid) {
+      // the row's segment statistics, eight at a time, every load of them
+      // issued before any merge
       const Partial* p = a.partials + (size_t(b) * R + rs) * n;
+      float m = -INFINITY, sum = 0.f, cnt = 0.f;
+      int idx = 0x7fffffff;
+      for (int s0 = 0; s0 < n; s0 += 8) {
+        Partial x[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) x[u] = p[min(s0 + u, n - 1)];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (s0 + u >= n) break;
+          if (greedy) merge_argmax(m, idx, x[u].m, x[u].idx);
+          else merge_ms(m, sum, cnt, x[u].m, x[u].s + x[u].cnt, 0.f, c);
+        }
+      }
       if (greedy) {
-        float m = -INFINITY;
-        int idx = 0x7fffffff;
-#pragma unroll 8
-        for (int s = 0; s < n; ++s) merge_argmax(m, idx, p[s].m, p[s].idx);
         r.idx = idx;
       } else {
-        float m = -INFINITY, sum = 0.f, cnt = 0.f;
-#pragma unroll 8
-        for (int s = 0; s < n; ++s) merge_ms(m, sum, cnt, p[s].m, p[s].s + p[s].cnt, 0.f, c);
         const float mc = m * c;
         r.kk = mc + fast_log2(sum);
         if (row_filtered(a, f, rs)) {
@@ -1058,42 +1077,37 @@ __global__ __launch_bounds__(64) void filt_verdict_kernel(FiltArgs a, RowInfo* i
     if (a.kept) a.kept[size_t(b) * R + rs] = kept;
   }
   __syncthreads();
-  if (tid != 0) return;
-  int acc = K;
-  for (int i = 0; i < max_k; ++i) {
-    const size_t o = size_t(b) * max_k + i;
-    float pd = NAN, pt = NAN;
-    int8_t lab = -1;
-    if (i < K) {
-      const int d = a.tokens[o];
-      bool ok;
-      if (greedy) {
-        ok = d == row[max_k + i].idx;
-        pt = ok ? 1.f : 0.f;
-      } else {
-        const float zd = a.zval[size_t(b) * R + i], zt = a.zval[size_t(b) * R + max_k + i];
-        const RowInfo& id = row[i];
-        const RowInfo& it = row[max_k + i];
-        const uint32_t kd = Key<ET>::of(zd), kt = Key<ET>::of(zt);
-        const float ld = kd >= id.t ? fmaf(zd, c, -id.kk) : -INFINITY;
-        const float lt = kt >= it.t ? fmaf(zt, c, -it.kk) : -INFINITY;
-        pd = fast_exp2(ld);
-        pt = fast_exp2(lt);
-        const float ratio = ld == -INFINITY ? INFINITY : fast_exp2(lt - ld);
-        ok = a.u_accept[o] < fminf(1.f, ratio);
-      }
-      if (i < acc) {
-        if (!ok) acc = i;
-        lab = ok ? 1 : 0;
-      }
+  // the accept tests, one position per lane; the accept length is the first
+  // rejection (K_b if none)
+  const int i = tid;
+  float pd = NAN, pt = NAN;
+  bool ok = true;
+  if (i < K) {
+    if (greedy) {
+      ok = d == row[max_k + i].idx;
+      pt = ok ? 1.f : 0.f;
+    } else {
+      const RowInfo& id = row[i];
+      const RowInfo& it = row[max_k + i];
+      const uint32_t kd = Key<ET>::of(zd), kt = Key<ET>::of(zt);
+      const float ld = kd >= id.t ? fmaf(zd, c, -id.kk) : -INFINITY;
+      const float lt = kt >= it.t ? fmaf(zt, c, -it.kk) : -INFINITY;
+      pd = fast_exp2(ld);
+      pt = fast_exp2(lt);
+      const float ratio = ld == -INFINITY ? INFINITY : fast_exp2(lt - ld);
+      ok = ua < fminf(1.f, ratio);
     }
+  }
+  const unsigned long long rej = __ballot(i < K && !ok);
+  const int acc = rej ? __ffsll(static_cast<long long>(rej)) - 1 : K;
+  if (i < max_k) {
     if (a.p_draft) a.p_draft[o] = pd;
     if (a.p_target) a.p_target[o] = pt;
-    if (a.labels) a.labels[o] = lab;
+    if (a.labels) a.labels[o] = int8_t(i < acc ? 1 : (i == acc && i < K ? 0 : -1));
   }
+  if (i <= max_k) a.out_tokens[size_t(b) * (max_k + 1) + i] = i < acc ? d : -1;
+  if (tid != 0) return;
   a.accept_len[b] = acc;
-  for (int i = 0; i <= max_k; ++i)
-    a.out_tokens[size_t(b) * (max_k + 1) + i] = i < acc ? a.tokens[size_t(b) * max_k + i] : -1;
   DrawDesc dd{acc, 0, 0.f, 0};
   if (greedy) {
     a.out_tokens[size_t(b) * (max_k + 1) + acc] = row[max_k + acc].idx;
@@ -1238,61 +1252,101 @@ __global__ __launch_bounds__(kFT) void filt_search_kernel(FiltArgs a, const RowI
   const DrawDesc dd = desc[b];
   if (dd.mode == 0) return;
   const int ns = n * kFV;  // slices of a row
-  // slice j = (segment j / kFV, vector j % kFV); its weights of kind q sit at
-  // ((j / kFV) * 2 + q) * kFV + j % kFV of the request's block
+  const int R = a.R, max_k = a.max_k;
+  // everything the draw needs besides the crossing slice, in one round trip:
+  // the slice weights (slice j = (segment j / kFV, vector j % kFV); its
+  // weights of kind q sit at ((j / kFV) * 2 + q) * kFV + j % kFV of the
+  // request's block), both candidate rows' thresholds and starts, T
   const float* sl = slices + size_t(b) * n * 2 * kFV;
   for (int e = tid; e < 2 * ns; e += kFT) {
     const int seg = e / (2 * kFV), q = (e / kFV) & 1, k = e % kFV;
     sw[q][seg * kFV + k] = sl[e];
   }
+  const RowInfo it = info[size_t(b) * R + max_k + dd.acc];
+  const RowInfo idr = info[size_t(b) * R + dd.acc];
+  const ET* rt = row_ptr<ET>(a, b, max_k + dd.acc);
+  const ET* rdr = row_ptr<ET>(a, b, dd.acc);
+  const float c = kLog2e / a.temperature[b];
   __syncthreads();
-  auto slice_w = [&](int j, int q) { return sw[q][j]; };
-  if (tid == 0) {
+  if (wv == 0) {
+    // wave 0: lane l sums slices l * per .. in order, a prefix over the
+    // lanes places each lane's run; the crossing lane scans its run
+    const int per = (ns + 63) / 64;
+    const int j0 = min(lane * per, ns), j1 = min(j0 + per, ns);
     int q = dd.mode == 1 ? 0 : 1;
-    float Z = 0.f;
-    for (int j = 0; j < ns; ++j) Z += slice_w(j, q);
+    auto lane_sum = [&](int qq) {
+      float x = 0.f;
+      for (int j = j0; j < j1; ++j) x += sw[qq][j];
+      return x;
+    };
+    float ls = lane_sum(q);
+    float incl = wave_inclusive_scan(ls, lane);
+    float Z = __shfl(incl, 63, 64);
     if (q == 0 && !(Z > 0.f)) {  // the residual has no mass: draw from the target row
       q = 1;
-      Z = 0.f;
-      for (int j = 0; j < ns; ++j) Z += slice_w(j, q);
+      ls = lane_sum(q);
+      incl = wave_inclusive_scan(ls, lane);
+      Z = __shfl(incl, 63, 64);
     }
     const float t = dd.u * Z;
+    float before = __shfl_up(incl, 1, 64);  // weight of the slices ahead of this lane's run
+    if (lane == 0) before = 0.f;
+    const unsigned long long hit = __ballot(incl > t && j1 > j0);
+    int ch = -1, want_last = 0;
     float cum = 0.f;
-    int ch = -1;
-    for (int j = 0; j < ns; ++j) {
-      const float w = slice_w(j, q);
-      if (cum + w > t) {
-        ch = j;
-        break;
-      }
-      cum += w;
-    }
-    int want_last = 0;
-    if (ch < 0) {
-      want_last = 1;
-      ch = 0;
-      for (int j = ns - 1; j >= 0; --j)
-        if (slice_w(j, q) > 0.f) {
-          ch = j;
-          break;
+    if (hit) {
+      const int l = __ffsll(static_cast<long long>(hit)) - 1;
+      if (lane == l) {
+        // the crossing slice of the run; if rounding leaves none there, the
+        // run's last slice with positive weight
+        cum = before;
+        int lastj = -1;
+        float cum_last = before;
+        for (int j = j0; j < j1; ++j) {
+          const float w = sw[q][j];
+          if (w > 0.f) {
+            lastj = j;
+            cum_last = cum;
+          }
+          if (cum + w > t) {
+            ch = j;
+            break;
+          }
+          cum += w;
         }
+        if (ch < 0) {
+          ch = max(lastj, j0);
+          cum = cum_last;
+        }
+      }
+      ch = __shfl(ch, l, 64);
+      cum = __shfl(cum, l, 64);
     }
-    pick = ch;
-    last = want_last;
-    mode = q;
-    rem = t - cum;
+    if (ch < 0) {
+      // rounding left no crossing: the last slice with positive weight
+      want_last = 1;
+      int lastp = -1;
+      for (int j = j0; j < j1; ++j)
+        if (sw[q][j] > 0.f) lastp = j;
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) lastp = max(lastp, __shfl_xor(lastp, o, 64));
+      ch = max(lastp, 0);
+      cum = t;
+    }
+    if (lane == 0) {
+      pick = ch;
+      last = want_last;
+      mode = q;
+      rem = t - cum;
+    }
   }
   __syncthreads();
   const int ch = pick;
   const bool resid = mode == 0;
-  const int R = a.R, max_k = a.max_k;
-  const RowInfo it = info[size_t(b) * R + max_k + dd.acc];
-  const RowInfo id = resid ? info[size_t(b) * R + dd.acc] : it;
+  const RowInfo id = resid ? idr : it;
   const KeptRow kit = kept_row<ET>(it), kid = kept_row<ET>(id);
-  const ET* rt = row_ptr<ET>(a, b, max_k + dd.acc);
-  const ET* rd = resid ? row_ptr<ET>(a, b, dd.acc) : rt;
+  const ET* rd = resid ? rdr : rt;
   const bool al = is_aligned16(rt) && is_aligned16(rd);
-  const float c = kLog2e / a.temperature[b];
   // the slice: kFT * N contiguous tokens, thread t holding N of them
   const int first = (ch / kFV) * kFT * kFV * N + (ch % kFV) * kFT * N + tid * N;
   const uint4 vt = load_raw<ET>(rt, first, a.V, al);
