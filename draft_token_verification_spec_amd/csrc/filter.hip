@@ -179,19 +179,6 @@ __device__ __forceinline__ ReqFilter req_filter(const FiltArgs& a, int b) {
   return f;
 }
 
-// The value is in a register at this point: loads written before a kernel's
-// first decision and pinned there go out together, instead of one round
-// trip after another as the compiler would otherwise issue them (each kernel
-// argument pointer loaded where it is first needed).
-template <typename A, typename B, typename C, typename D, typename E, typename F>
-__device__ __forceinline__ void pin(const A& x0, const B& x1, const C& x2, const D& x3, const E& x4, const F& x5) {
-  asm volatile("" ::"v"(x0), "v"(x1), "v"(x2), "v"(x3), "v"(x4), "v"(x5));
-}
-template <typename A, typename B, typename C>
-__device__ __forceinline__ void pin(const A& x0, const B& x1, const C& x2) {
-  asm volatile("" ::"v"(x0), "v"(x1), "v"(x2));
-}
-
 // Is row slot rs (draft i at i, target j at max_k + j) of the request read
 // and filtered?
 __device__ __forceinline__ bool row_filtered(const FiltArgs& a, const ReqFilter& f, int rs) {
@@ -773,7 +760,7 @@ __global__ __launch_bounds__(64) void filt_select0_kernel(FiltArgs a) {
   // the row's first 64 segment statistics and the request's scalars in one round trip
   const Partial p0 = a.partials[row * n + min(tid, n - 1)];
   const ReqFilter f = req_filter(a, b);
-  pin(f.K, f.T, f.top_k, f.top_p, p0.m, p0.idx);
+  pin_all(f.K, f.T, f.top_k, f.top_p, p0.m, p0.idx);
   if (!row_filtered(a, f, rs)) return;
   select0_row<ET>(a, f, row, p0, sh, tid);
 }
@@ -954,8 +941,7 @@ __global__ __launch_bounds__(64) void filt_select_kernel(FiltArgs a, int levels)
   float m = a.partials[row * n + min(tid, n - 1)].m;
   const uint32_t s0 = a.search[row * 2].state, s1 = a.search[row * 2 + 1].state;
   const ReqFilter f = req_filter(a, b);
-  pin(m, s0, s1, f.K, f.T, f.top_p);
-  pin(f.top_k, m, m);
+  pin_all(m, s0, s1, f.K, f.T, f.top_k, f.top_p);
   if (!row_filtered(a, f, rs)) return;
   for (int q = tid + 64; q < n; q += 64) m = fmaxf(m, a.partials[row * n + q].m);
 #pragma unroll

@@ -354,30 +354,46 @@ __device__ __forceinline__ void search_request(const VerifyArgs& a, DrawShared& 
 
 // Merge the segment statistics of the request's rows into sh.row, by row
 // slot (draft i at i, target j at max_k + j; slots of rows the statistics
-// kernel skipped hold stale values that nothing reads).  The loads do not
-// wait for the request's scalars.  A row takes G lanes (G the smallest power
-// of two >= the segments per row, at most 64), so a wave merges 64 / G rows
-// at a time: lane j of a row's group merges segments j, j + G, ... in order,
-// then a butterfly over the group combines the lanes.  Every workgroup of
-// the request evaluates the same function of the same data, so all reach
-// the same statistics.
-__device__ __forceinline__ void merge_rows(const VerifyArgs& a, DrawShared& sh, int b, bool greedy, float c,
-                                           int tid) {
-  const int wave = tid >> 6, lane = tid & 63;
-  const int n = a.nseg2, max_k = a.max_k, R = a.R;
+// kernel skipped hold stale values that nothing reads).  A row takes G lanes
+// (G the smallest power of two >= the segments per row, at most 64), so a
+// wave merges 64 / G rows at a time: lane j of a row's group merges
+// segments j, j + G, ... in order, then a butterfly over the group combines
+// the lanes.  Every workgroup of the request evaluates the same function of
+// the same data, so all reach the same statistics.  The first pass's loads
+// (MergeFirst) are issued beforehand, with the request's scalars.
+struct MergeFirst {
+  Partial p;  // the lane's first segment of its row in the first pass
+  float z;    // the row's logit at the draft token
+};
+__device__ __forceinline__ int merge_lanes(int n) {
   int G = 1;
   while (G < n && G < 64) G <<= 1;
+  return G;
+}
+__device__ __forceinline__ MergeFirst merge_first(const VerifyArgs& a, int b, int tid) {
+  const int wave = tid >> 6, lane = tid & 63;
+  const int n = a.nseg2, R = a.R;
+  const int G = merge_lanes(n);
+  const int q = min(wave * (64 / G) + lane / G, R - 1), x = min(lane & (G - 1), n - 1);
+  return MergeFirst{a.partials[(size_t(b) * R + q) * n + x], a.zval[size_t(b) * R + q]};
+}
+__device__ __forceinline__ void merge_rows(const VerifyArgs& a, DrawShared& sh, int b, bool greedy, float c,
+                                           const MergeFirst& first, int tid) {
+  const int wave = tid >> 6, lane = tid & 63;
+  const int n = a.nseg2, max_k = a.max_k, R = a.R;
+  const int G = merge_lanes(n);
   const int RW = 64 / G;  // rows per wave and pass
   const int g = lane / G, j = lane & (G - 1);
   const Partial* base = a.partials + size_t(b) * R * n;
   for (int q0 = wave * RW; q0 < R; q0 += kWaves * RW) {
     const int q = q0 + g;
     const bool amax = greedy && q >= max_k;
-    const float z = (q < R && j == 0) ? a.zval[size_t(b) * R + q] : NAN;
+    const bool pass0 = q0 == wave * RW;
+    const float z = (q < R && j == 0) ? (pass0 ? first.z : a.zval[size_t(b) * R + q]) : NAN;
     Partial acc{-INFINITY, 0.f, 0.f, 0x7fffffff};
     if (q < R)
       for (int x = j; x < n; x += G) {
-        const Partial p = base[size_t(q) * n + x];
+        const Partial p = (pass0 && x == j) ? first.p : base[size_t(q) * n + x];
         if (amax)
           merge_argmax(acc.m, acc.idx, p.m, p.idx);
         else
@@ -458,27 +474,36 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
   const int n = a.nseg2, max_k = a.max_k;
   const int s = int(blockIdx.x % uint32_t(n));
   const int b = a.B - 1 - int(blockIdx.x / uint32_t(n));
-  // every scalar of the request in one round trip, with the merge's loads
-  const int kraw = a.num_draft[b];
-  const float T = a.temperature[b];
-  const int64_t ts = a.target_start[b];
-  const int64_t ds = max_k > 0 ? a.draft_start[b] : 0;
-  const float ures = a.u_residual[b], ubon = a.u_bonus[b];
-  const int K = min(max(kraw, 0), max_k);
-  const bool greedy = !(T > 0.f);
-  const bool want_feat = a.av_feature != nullptr;
-  const int nd = (!greedy || want_feat) ? K : 0;  // draft rows read
-  const float c = uniform(kLog2e / (greedy ? 1.f : T));
-  // lane i of wave 0 tests position i: its token and uniform, in flight with
-  // the merge (loaded for every i < max_k, so that the loads need not wait
-  // for K)
+  // Everything the verdict needs in one round trip: the request's scalars,
+  // lane i's token and uniform, the merge's first loads.  The scalars are
+  // loaded by every lane (indexed through an opaque zero), so that they are
+  // vector loads: scalar loads would share one counter with the reloads of
+  // the kernel arguments, and each reload's wait would wait for them too.
+  const int z0 = fresh_tid() >> 16;  // 0
+  const int kraw_l = a.num_draft[b + z0];
+  const float T_l = a.temperature[b + z0];
+  const int64_t ts = a.target_start[b + z0];
+  const int64_t dsl = (max_k > 0 ? a.draft_start : a.target_start)[b + z0];
+  const float ures = a.u_residual[b + z0], ubon = a.u_bonus[b + z0];
+  // lane i of wave 0 tests position i: its token and uniform (loaded for
+  // every i < max_k, so that the loads need not wait for K)
   int dl = -1;
   float ul = 0.f;
   if (wave == 0 && lane < max_k) {
     dl = a.tokens[size_t(b) * max_k + lane];
     ul = a.u_accept[size_t(b) * max_k + lane];
   }
-  merge_rows(a, sh, b, greedy, c, tid);
+  const MergeFirst mf = merge_first(a, b, tid);
+  pin_all(kraw_l, T_l, ts, dsl, ures, ubon, dl, ul, mf.p.m, mf.p.s, mf.p.cnt, mf.p.idx, mf.z);
+  const int kraw = uniform(kraw_l);
+  const float T = uniform(T_l);
+  const int64_t ds = max_k > 0 ? dsl : 0;
+  const int K = min(max(kraw, 0), max_k);
+  const bool greedy = !(T > 0.f);
+  const bool want_feat = a.av_feature != nullptr;
+  const int nd = (!greedy || want_feat) ? K : 0;  // draft rows read
+  const float c = uniform(kLog2e / (greedy ? 1.f : T));
+  merge_rows(a, sh, b, greedy, c, mf, tid);
 
   // the accept tests, and the accept length a: the first rejection, else K
   float pd = NAN, pt = NAN;

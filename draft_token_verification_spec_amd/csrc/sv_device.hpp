@@ -189,6 +189,21 @@ __device__ __forceinline__ int load_dev(const int* p) {
 }
 
 
+// Loads written before a kernel's first decision go out together when their
+// values are pinned there: the compiler otherwise issues each load where its
+// value is first needed (a kernel argument pointer, then the value, one round
+// trip after another).  pin_all(x...) makes every x available at this point,
+// through one word that depends on all of them.
+__device__ __forceinline__ uint32_t pin_bits(uint32_t x) { return x; }
+__device__ __forceinline__ uint32_t pin_bits(int x) { return uint32_t(x); }
+__device__ __forceinline__ uint32_t pin_bits(float x) { return __float_as_uint(x); }
+__device__ __forceinline__ uint32_t pin_bits(int64_t x) { return uint32_t(x) ^ uint32_t(uint64_t(x) >> 32); }
+template <typename... T>
+__device__ __forceinline__ void pin_all(const T&... x) {
+  const uint32_t w = (pin_bits(x) ^ ...);
+  asm volatile("" ::"v"(w));
+}
+
 // Arrival counter.  Thread 0 of every workgroup of a request has published
 // its results (device-scope stores above); it waits until they are complete,
 // then takes a ticket.  The workgroup taking the last ticket (want - 1)
