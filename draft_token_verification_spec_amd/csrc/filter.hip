@@ -23,10 +23,11 @@
 //            one key remains (bf16 keys: 2 levels at most, fp32: 4).
 // Each level's counts come from a streaming pass (one workgroup per 32 KiB
 // row segment; every sum an integer added with LDS atomics, so the result
-// does not depend on the order of the additions) and a selection (one
-// workgroup per row: segment histograms merged in order, exclusive scans,
-// the boundary bin or digit).  The verdict, the residual / bonus weights and
-// the draw then run on the filtered rows.
+// does not depend on the order of the additions) and a selection (one wave
+// per row: segment histograms merged in order, exclusive scans, the boundary
+// bin or digit).  Key levels after the first read only the segments of the
+// rows still searching.  The verdict, the residual / bonus weights and the
+// draw then run on the filtered rows.
 #include <type_traits>
 
 #include "sv_segment.hpp"
@@ -219,7 +220,7 @@ __device__ __forceinline__ uint4 load_nan_tail(const ET* row, int first, int lim
 // ---------------------------------------------------------------------------
 //
 // Level 0 and the first key level are selected by kernels of their own (one
-// workgroup per row).  A later key level, where few rows still search, runs
+// wave per row).  A later key level, where few rows still search, runs
 // on the listed segments only, and a row's selection is made there by the
 // workgroup that delivers the row's last segment histogram (every segment
 // workgroup publishes its histogram with device-scope stores, then takes a
