@@ -56,9 +56,13 @@ __global__ __launch_bounds__(kFitT) void av_fit_kernel(int B, int max_k, const f
       int y[kChunk];
 #pragma unroll
       for (int c = 0; c < kChunk; ++c) {
-        const int it = it0 + c * T;
-        x[c] = it < n ? feature[it] : 0.f;
-        y[c] = it < n ? labels[it] : -1;
+        // every load unconditional (past the end: the last item, masked), so
+        // that the compiler does not order them one after another
+        const int it = it0 + c * T, itc = min(it, n - 1);
+        const float xv = feature[itc];
+        const int yv = labels[itc];
+        x[c] = it < n ? xv : 0.f;
+        y[c] = it < n ? yv : -1;
       }
 #pragma unroll
       for (int c = 0; c < kChunk; ++c) {
