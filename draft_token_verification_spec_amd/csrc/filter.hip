@@ -88,14 +88,19 @@ struct Key<float> {
 // Gs = ceil(segment max * 8c), and a segment bin shifts into the row bin by
 // the integer G - Gs, so that the segments need not know the row maximum.
 // Within a cell a weight is the cell's lower edge times r = 2^((z 8c - F)/8)
-// in [1, 2^(1/8)), and (r - 1) is kept in 2^-21 fixed point: the counts and
-// these sums are integers (32 bits each per segment suffice, added as the
-// two halves of one 64-bit word), so the bin masses edge x (count + sum
-// 2^-21) do not depend on the order of the additions and are exact to 2^-22
-// relative.
+// in [1, 2^(1/8)).  Each element adds one 64-bit word, 2^45 + bits(r): the
+// count in the top 19 bits and, below them, the sum of the binary32 bit
+// patterns of r (< 2^45 for the 2^14 elements of a segment).  For r in [1, 2)
+// bits(r) - bits(1) is (r - 1) 2^23 exactly, so a bin's mass is
+// edge x (count + (sum - count bits(1)) 2^-23): the sum of the weights r as
+// computed, added exactly, independent of the order of the additions.  (A
+// weight rounded just below 1 counts one unit of 2^-23 low.)
 constexpr int kBins0 = 512;
 constexpr int kBinsPerLog2 = 8;
-constexpr float kFrac0 = 2097152.f;  // 2^21
+constexpr int kCountShift0 = 45;  // level-0 word: count << 45 | sum of bits(r)
+constexpr uint64_t kOne0 = 1ull << kCountShift0;
+constexpr uint64_t kOneBits = 0x3f800000ull;  // bits(1.0f)
+constexpr double kFrac0 = 8388608.0;            // 2^23
 __device__ __forceinline__ float cell_of(float z, float c8) { return floorf(z * c8); }
 // the bin of z against grid point g (a whole number of cells): g - F(z),
 // exact where it is below 511, clamped to [0, 511]
@@ -152,7 +157,7 @@ struct FiltArgs {
   Partial* partials;        // [B][R][nseg2] segment statistics
   float* zval;              // [B][R] logits at the draft tokens
   uint64_t* hmass;          // [B][R][nseg2][2][kBins]  key-level masses (digits wider than one key)
-  uint32_t* hcount;         // [B][R][nseg2][2][kBins0]  level 0: per bin fraction sum << 32 | count (u64);
+  uint32_t* hcount;         // [B][R][nseg2][2][kBins0]  level 0: per bin count << 45 | sum of bits(r) (u64);
                             //   key levels: counts
   FSearch* search;          // [B][R][2]
   uint32_t* tickets;        // [B][R]  arrivals per row (zero between passes)
@@ -354,7 +359,7 @@ struct Sel0Shared {
 // Level-0 selection of a row slot by one wave, lane t holding bins 8t ..
 // 8t + 7.  The row's segment histograms are shifted onto the row's grid
 // point and merged in segment order; bin masses, in units of the row
-// maximum's weight, are edge x (count + sum 2^-21), and the row's total mass
+// maximum's weight, are edge x (count + excess 2^-23), and the row's total mass
 // is the sum of the masses of bins 0..510 (bin 511's never enters; its count
 // is the row's length less the other bins').  The boundary bin of each
 // search is the last non-empty bin whose count (top-k) or mass (top-p,
@@ -381,7 +386,7 @@ __device__ void select0_row(const FiltArgs& a, const ReqFilter& f, size_t row, c
   __syncthreads();
   const float g = grid_point(m, c8);
   uint32_t cnt[kSelBins] = {};
-  uint64_t frac[kSelBins] = {};  // up to V x 189812: beyond 32 bits for long runs of equal logits
+  int64_t frac[kSelBins] = {};  // sums of (r - 1) 2^23: up to V x 759237
   const uint64_t* h64 = reinterpret_cast<const uint64_t*>(a.hcount) + row * n * kBins0;
   // Segments are taken kGather at a time: every lane loads all its bins of
   // them (clamped into each segment's stored bins, those out of range masked
@@ -409,8 +414,10 @@ __device__ void select0_row(const FiltArgs& a, const ReqFilter& f, size_t row, c
     for (int u = 0; u < kGather; ++u)
 #pragma unroll
       for (int q = 0; q < kSelBins; ++q) {
-        cnt[q] += in[u][q] ? uint32_t(x[u][q]) : 0u;
-        frac[q] += in[u][q] ? (x[u][q] >> 32) : 0ull;
+        const uint32_t k = uint32_t(x[u][q] >> kCountShift0);
+        const int64_t e = int64_t(x[u][q] & (kOne0 - 1)) - int64_t(k) * int64_t(kOneBits);
+        cnt[q] += in[u][q] ? k : 0u;
+        frac[q] += in[u][q] ? e : 0;
       }
   }
   // the last bin (lane 63's last) holds every element not in the others
@@ -428,7 +435,7 @@ __device__ void select0_row(const FiltArgs& a, const ReqFilter& f, size_t row, c
 #pragma unroll
   for (int q = 0; q < kSelBins; ++q) {
     mass[q] = j0 + q < kBins0 - 1 && cnt[q] > 0u
-                  ? e0 * kPow2Eighth[q] * (double(cnt[q]) + double(frac[q]) / double(kFrac0))
+                  ? e0 * kPow2Eighth[q] * (double(cnt[q]) + double(frac[q]) / kFrac0)
                   : 0.0;
     tc += cnt[q];
     tm += mass[q];
@@ -616,7 +623,7 @@ __device__ bool select_row(const FiltArgs& a, float c, float mc, size_t row, int
 // ---------------------------------------------------------------------------
 
 struct Stats0Shared {
-  uint64_t bins[kBins0];  // fraction sum << 32 | count, by segment bin
+  uint64_t bins[kBins0];  // count << 45 | sum of bits(r), by segment bin
   float red[kFT / 64];
   int lastb[kFT / 64];
   Partial part[kWaves];
@@ -709,9 +716,8 @@ __global__ __launch_bounds__(kFT) __attribute__((amdgpu_waves_per_eu(8))) void f
   if (m != -INFINITY) {  // uniform; the selection reads no bin of a segment without a finite logit
     const float c8 = c * float(kBinsPerLog2);
     const float gs = grid_point(m, c8), g8 = gs * (1.f / kBinsPerLog2);
-    // r = 2^(z c - gs/8 + bin/8) in [1, 2^(1/8)); r - 1 in 2^-21 units
-    // rounded half up: in [0, 189812] for bins below 511 (the last bin is
-    // never read: there the conversion saturates at 0)
+    // r = 2^(z c - gs/8 + bin/8) in [1, 2^(1/8)) for bins below 511 (the
+    // last bin is never read: there r is below 1, down to 0)
     // The bin is taken as its byte offset in sh.bins, 8 (gs - F(z)) clamped
     // to [0, 8 x 511] (bin0f's value times 8, exactly), so that it converts
     // straight to an LDS address.
@@ -719,9 +725,8 @@ __global__ __launch_bounds__(kFT) __attribute__((amdgpu_waves_per_eu(8))) void f
     auto add0 = [&](float z) {
       const float jb = __builtin_amdgcn_fmed3f(fmaf(cell_of(z, c8), -8.f, gs8), 0.f, float(8 * (kBins0 - 1)));
       const float r = fast_exp2(fmaf(jb, 1.f / (8 * kBinsPerLog2), fmaf(z, c, -g8)));
-      const uint32_t u = uint32_t(fmaf(r, kFrac0, 0.5f - kFrac0));
       atomicAdd(reinterpret_cast<unsigned long long*>(reinterpret_cast<char*>(sh.bins) + int(jb)),
-                (static_cast<unsigned long long>(u) << 32) | 1ull);
+                static_cast<unsigned long long>(kOne0 | __float_as_uint(r)));
     };
     // past the end of the row the loads hold -inf (bin 511, never read by
     // the selection): whole vectors of them are skipped, so that they do

@@ -221,8 +221,9 @@ size_t sv_filtered_workspace_size(int B, int V, int max_k, int dtype);
  *   workspace: at least sv_filtered_workspace_size(B, V, max_k, dtype)
  *           bytes, zero-filled once.
  * The kept sets are exact to the resolution of the mass sums, which are
- * integers (level 0: 2^-21 of a bin's lower edge; key levels: 2^-40 of the
- * row maximum's probability), so that every mass compared, the row's total
+ * integers (level 0: 2^-23 of a bin's lower edge, the binary32 weights
+ * relative to that edge added exactly; key levels: 2^-40 of the row
+ * maximum's probability), so that every mass compared, the row's total
  * included, is within 2^-22 of the row's total of the sum of the weights it
  * stands for, and independent of the order of the additions;
  * the top-p comparison is made on them in binary64, the threshold found by a
