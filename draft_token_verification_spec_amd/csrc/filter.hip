@@ -13,21 +13,26 @@
 // A row's kept set is {v : key(z_v) >= t} for a threshold key t (key = the
 // order-preserving integer image of the logit), found by an exact radix
 // select with deterministic histograms:
-//   level 0  bins of 1/8 unit of log2 weight on an absolute grid, the 511
-//            grid cells from the row maximum's down (the last bin collecting
-//            everything further down), each with its count and its mass
-//            exactly to 2^-22 relative; built by the statistics pass itself,
-//            so that one read of a filtered row serves both, and the row's
-//            total mass is the sum of its bins;
-//   level L  8-bit digits of the key within the boundary bin's keys, until
-//            one key remains (bf16 keys: 2 levels at most, fp32: 4).
+//   level 0  built by the statistics pass itself, so that one read of a
+//            filtered row serves both.  fp32 rows: bins of 1/8 unit of log2
+//            weight on an absolute grid, the 511 grid cells from the row
+//            maximum's down (the last bin collecting everything further
+//            down), each with its count and its mass; the row's total mass
+//            is the sum of its bins.  bf16 rows: exact counts of the 1024
+//            keys from the row maximum's down, and the row's total mass from
+//            the segments' weight sums; a threshold inside that window is
+//            found here, with no key level;
+//   level L  8-bit digits of the key within the boundary bin's keys (bf16:
+//            the keys below the window), until one key remains (bf16 keys:
+//            2 levels at most, fp32: 4).
 // Each level's counts come from a streaming pass (one workgroup per 32 KiB
-// row segment; every sum an integer added with LDS atomics, so the result
+// row segment; every count an integer added with LDS atomics, so the result
 // does not depend on the order of the additions) and a selection (one wave
 // per row: segment histograms merged in order, exclusive scans, the boundary
-// bin or digit).  Key levels after the first read only the segments of the
-// rows still searching.  The verdict, the residual / bonus weights and the
-// draw then run on the filtered rows.
+// bin, key or digit).  Key levels read only the segments of the rows still
+// searching (fp32 rows: every filtered row at the first key level).  The
+// verdict, the residual / bonus weights and the draw then run on the
+// filtered rows.
 #include <type_traits>
 
 #include "sv_segment.hpp"
@@ -51,7 +56,7 @@ struct Key;
 template <>
 struct Key<uint16_t> {
   static constexpr uint32_t kMin = 0x007fu;  // -inf
-  static constexpr uint32_t kMax = 0xff80u;  // +inf
+  [[maybe_unused]] static constexpr uint32_t kMax = 0xff80u;  // +inf
   __device__ __forceinline__ static uint32_t of(float z) {
     uint32_t u = __float_as_uint(z) >> 16;
     if (u == 0x8000u) u = 0u;
@@ -101,6 +106,27 @@ constexpr int kCountShift0 = 45;  // level-0 word: count << 45 | sum of bits(r)
 constexpr uint64_t kOne0 = 1ull << kCountShift0;
 constexpr uint64_t kOneBits = 0x3f800000ull;  // bits(1.0f)
 constexpr double kFrac0 = 8388608.0;            // 2^23
+
+// bf16 rows take level 0 at key resolution instead: a bf16 logit has 2^16
+// possible values, and the 1024 keys from a maximum's down cover 8 octaves
+// of |z| (128 keys each), where a top-p boundary usually lies.  Each segment
+// counts its elements by key in that window below its own maximum's key
+// (every element of a key has the same weight, so a count is all a key
+// needs), and sums the weights of all its elements for the row's total.
+// The row's window is the one below the row maximum's key; a segment's
+// window reaches at least as far down, since its maximum is not above the
+// row's.  When the threshold lies below the row's window, the search
+// continues with the key levels over the keys below it.
+constexpr int kWin = 2 * kBins0;  // window keys: the level-0 histogram's words, as 32-bit counts
+template <typename ET>
+constexpr bool kKeyWindow = sizeof(ET) == 2;
+// km - Key<uint16_t>::of(z) for a bf16 value z, from its bits: with t the
+// bits sign-extended, the key is (t ^ (0x7fff if z < 0)) + 0x8000 (z + 0
+// turns -0 into +0 first)
+__device__ __forceinline__ uint32_t key_offset16(uint32_t km, float z) {
+  const int t = __float_as_int(z + 0.f) >> 16;
+  return uint32_t(int(km) - 0x8000 - (t ^ ((t >> 15) & 0x7fff)));
+}
 __device__ __forceinline__ float cell_of(float z, float c8) { return floorf(z * c8); }
 // the bin of z against grid point g (a whole number of cells): g - F(z),
 // exact where it is below 511, clamped to [0, 511]
@@ -130,7 +156,8 @@ struct FSearch {
 };
 static_assert(sizeof(FSearch) == kFilterSearchBytes, "search state layout");
 static_assert(kBins == kFilterBins && kBins0 == kFilterBins0, "histogram bins");
-static_assert(kFT * kFV * 16 / 2 * 0.0906 * 2097152.0 < 4294967296.0, "level-0 sums of a segment fit 32 bits");
+static_assert(kFT * kFV * 8 < (1 << (64 - kCountShift0)) && kFT * kFV * 8 * double(0x3f8b95c2u) < double(kOne0),
+              "level-0 counts and bit sums of a segment fit their fields");
 
 struct FiltArgs {
   int B, V, max_k, R, nseg2;
@@ -235,6 +262,11 @@ __device__ __forceinline__ uint4 load_nan_tail(const ET* row, int first, int lim
 
 constexpr int kMaxSegs = int(int64_t(SV_MAX_V) * 4 / (kFT * kFV * 16));  // 32 KiB segments of the longest row
 constexpr int kMaxKeyLevels = 4;  // fp32 keys: 4 digits of 8 bits
+// Entry of wcount counting the bf16 rows' segments listed for the first key
+// level (levels 2.. count theirs in entries 0..kMaxKeyLevels - 2; a bf16
+// search has 2 key levels at most, so the entry and list 1 of `work` are
+// free for it); cleared by the statistics pass.
+constexpr int kFirstList = kMaxKeyLevels - 1;
 
 __device__ __forceinline__ uint64_t load_dev64(const uint64_t* p) {
   return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -350,7 +382,9 @@ constexpr int kSelBins = kBins0 / 64;  // level-0 bins per lane of the selection
 
 struct Sel0Shared {
   float segm[kMaxSegs];  // segment maxima of the row
-  int segn[kMaxSegs];    // bins stored per segment
+  int segn[kMaxSegs];    // bins (bf16: window counts) stored per segment
+  double segt[kMaxSegs];  // bf16: the segments' weight sums relative to their maxima
+  uint32_t win[kWin + kWin / 16];  // bf16: the row's window counts, one pad word per 16
   uint32_t cab[2];
   double mab[2];
   uint32_t klo[2], khi[2];
@@ -499,6 +533,152 @@ __device__ void select0_row(const FiltArgs& a, const ReqFilter& f, size_t row, c
   }
 }
 
+// Level-0 selection of a bf16 row from its key windows, by one wave: lane t
+// holds the row's window keys km - (16t + i), i = 0..15 (km the row
+// maximum's key), so that a prefix in lane order sums the larger keys.  A
+// segment's counts shift into the row's window by the keys between its
+// maximum's and the row's; they are merged in segment order.  A key's mass
+// is its count times its weight (the same float expression as an element's
+// weight), and the row's total mass is the sum of the segments' weight sums,
+// each scaled from its maximum's weight to the row maximum's.  A search whose
+// threshold is in the window is done here; otherwise (the window holds less
+// than the target and the row has keys below it) it continues over the keys
+// below the window, with the window's count and mass above.
+template <typename ET>
+__device__ void select0_window(const FiltArgs& a, const ReqFilter& f, size_t row, const Partial& p0, Sel0Shared& sh,
+                               int lane) {
+  constexpr int kPer = kWin / 64;
+  const int n = a.nseg2;
+  const float c = kLog2e / f.T;
+  // the segment maxima, the row's, and the segments' weight sums relative
+  // to their own maxima (segment `lane` preloaded as p0)
+  float m = -INFINITY;
+  for (int q = lane; q < n; q += 64) {
+    const Partial x = q == lane ? p0 : a.partials[row * n + q];
+    sh.segm[q] = x.m;
+    sh.segn[q] = x.idx;
+    sh.segt[q] = double(x.s) + double(x.cnt);
+    m = fmaxf(m, x.m);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  __syncthreads();
+  const float mc = m * c;
+  const uint32_t km = Key<ET>::of(m);
+  double S = 0.0;
+  for (int q = lane; q < n; q += 64)
+    S += sh.segm[q] != -INFINITY ? sh.segt[q] * exp2(double(sh.segm[q] * c) - double(mc)) : 0.0;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) S += __shfl_xor(S, o, 64);
+  const uint32_t* h32 = a.hcount + row * n * (2 * kBins0);
+  // the merge reads offsets 64 i + lane (each load a contiguous 256 bytes),
+  // then hands each lane its 16 offsets through LDS
+  uint32_t cm[kPer] = {};
+  // segments kGather at a time, every load of them issued before any sum
+  // (offsets outside a segment's stored counts load a stored one, masked)
+  constexpr int kGather = 4;
+  for (int s0 = 0; s0 < n; s0 += kGather) {
+    uint32_t x[kGather][kPer];
+    bool in[kGather][kPer];
+#pragma unroll
+    for (int u = 0; u < kGather; ++u) {
+      const int sg = min(s0 + u, n - 1);
+      const int shift = int(km - Key<ET>::of(sh.segm[sg]));
+      const int nbs = s0 + u < n ? sh.segn[sg] : 0;
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const int ds = 64 * i + lane - shift;
+        in[u][i] = ds >= 0 && ds < nbs;
+        x[u][i] = h32[size_t(sg) * (2 * kBins0) + min(max(ds, 0), max(nbs - 1, 0))];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kGather; ++u)
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) cm[i] += in[u][i] ? x[u][i] : 0u;
+  }
+  // offset d at word d + d / 16: the lanes' runs of 16 start 17 words apart
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) sh.win[68 * i + lane + (lane >> 4)] = cm[i];
+  __syncthreads();
+  uint32_t cnt[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) cnt[i] = sh.win[17 * lane + i];
+  double mass[kPer];
+  uint32_t tc = 0;
+  double tm = 0.0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const float w = fast_exp2(fmaf(Key<ET>::value(km - uint32_t(kPer * lane + i)), c, -mc));
+    mass[i] = cnt[i] > 0u ? double(cnt[i]) * double(w) : 0.0;
+    tc += cnt[i];
+    tm += mass[i];
+  }
+  uint32_t call;
+  double mall;
+  const uint32_t fc0 = wave_excl_scan<uint32_t>(tc, lane, &call);
+  const double fm0 = wave_excl_scan<double>(tm, lane, &mall);
+  const bool below = uint32_t(a.V) > call;  // the row has keys below the window
+  bool any_open = false;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const bool on = q == 0 ? f.on_k : f.on_p;
+    const double target = q == 0 ? double(f.top_k) : double(f.top_p) * S;
+    // the smallest qualifying key (the largest offset; the maximum's key,
+    // offset 0, if none qualifies)
+    uint32_t fc = fc0;
+    double fm = fm0;
+    int dq = -1;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      if (cnt[i] > 0u && (q == 0 ? double(fc) < target : fm < target)) dq = kPer * lane + i;
+      fc += cnt[i];
+      fm += mass[i];
+    }
+    dq = max(wave_max_int(dq), 0);
+    const bool open = below && (q == 0 ? double(call) < target : mall < target);
+    FSearch w{};
+    if (on && open) {
+      w.lo = Key<ET>::kMin;
+      w.hi = km - uint32_t(kWin);
+      w.cabove = call;
+      w.mabove = mall;
+      w.target = target;
+      w.state = 1u;
+    }
+    fc = fc0;
+    fm = fm0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      if (on && !open && kPer * lane + i == dq) {
+        w.lo = w.hi = w.key = km - uint32_t(dq);
+        w.cabove = fc;
+        w.mabove = fm;
+        w.kept = fc + cnt[i];
+        w.mfinal = fm + mass[i];
+        w.target = target;
+        w.state = 2u;
+      }
+      fc += cnt[i];
+      fm += mass[i];
+    }
+    // the lane holding the threshold key writes a finished search, lane 0
+    // an open or unused one
+    const bool mine = on && !open ? (dq / kPer == lane) : lane == 0;
+    if (mine) a.search[row * 2 + q] = w;
+    any_open |= on && open;
+  }
+  // a row still searching lists its segments for the first key level
+  if (any_open) {
+    uint32_t base = 0;
+    if (lane == 0)
+      base = __hip_atomic_fetch_add(&a.wcount[kFirstList], uint32_t(n), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    base = __shfl(base, 0, 64);
+    uint32_t* list = a.work + size_t(a.B) * a.R * n;
+    for (int q = lane; q < n; q += 64) list[base + q] = uint32_t(row * n + q);
+  }
+}
+
 constexpr int kSelDigits = kBins / 64;  // key digits per lane of the selection
 
 // Key-level selection of a row by one wave; lane l owns digits
@@ -623,7 +803,11 @@ __device__ bool select_row(const FiltArgs& a, float c, float mc, size_t row, int
 // ---------------------------------------------------------------------------
 
 struct Stats0Shared {
-  uint64_t bins[kBins0];  // count << 45 | sum of bits(r), by segment bin
+  union {
+    uint64_t bins[kBins0];  // count << 45 | sum of bits(r), by segment bin
+    uint32_t win[kWin];     // bf16 rows: counts by key below the maximum's
+  };
+  double tot[kFT / 64];
   float red[kFT / 64];
   int lastb[kFT / 64];
   Partial part[kWaves];
@@ -682,6 +866,7 @@ __global__ __launch_bounds__(kFT) __attribute__((amdgpu_waves_per_eu(8))) void f
   const int64_t start = is_draft ? a.draft_start[b] : a.target_start[b];
   const int d = i < max_k ? a.tokens[size_t(b) * max_k + i] : -1;
   const bool greedy = !(f.T > 0.f);
+  if (kKeyWindow<ET> && item == 0u && tid == 0) a.wcount[kFirstList] = 0u;  // no list before the selection
   if (is_draft ? (greedy || i >= f.K) : (i > f.K)) return;  // not read
   const float c = uniform(kLog2e / (greedy ? 1.f : f.T));
   const ET* row = is_draft ? static_cast<const ET*>(a.draft) + (start + i) * a.draft_stride
@@ -710,6 +895,50 @@ __global__ __launch_bounds__(kFT) __attribute__((amdgpu_waves_per_eu(8))) void f
   m = fmaxf(fmaxf(sh.red[0], sh.red[1]), fmaxf(sh.red[2], sh.red[3]));
   const size_t row_slot = size_t(b) * R + rs;
   if (tid == 0 && ztok) a.zval[row_slot] = zd;
+  if constexpr (kKeyWindow<ET>) {
+    // the segment's statistics: its maximum, the sum of its weights
+    // relative to the maximum's (s + cnt, two floats), and (in idx) how many
+    // of its key counts, from the maximum's key down, are stored: up to the
+    // last non-empty one
+    int nb = 0;
+    double tot = 0.0;
+    if (m != -INFINITY) {  // uniform; the selection reads no count of a segment without a finite logit
+      const uint32_t km = Key<ET>::of(m);
+      const float mcs = m * c;
+      static_assert(N == 8, "a bf16 vector's weights are summed pairwise");
+#pragma unroll
+      for (int k = 0; k < kFV; ++k) {
+        if (hb + (k * kFT + tid) * N >= a.V) continue;  // past the end: nothing to count or weigh
+        float w[N];
+#pragma unroll
+        for (int j = 0; j < N; ++j) {
+          const float z = Elem<ET>::get(v[k], j);
+          const uint32_t dd = key_offset16(km, z);
+          if (dd < uint32_t(kWin)) atomicAdd(&sh.win[dd], 1u);
+          w[j] = fast_exp2(fmaf(z, c, -mcs));
+        }
+        tot += double(((w[0] + w[1]) + (w[2] + w[3])) + ((w[4] + w[5]) + (w[6] + w[7])));
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) tot += __shfl_xor(tot, o, 64);
+      if (lane == 0) sh.tot[wv] = tot;
+      __syncthreads();
+      int last = -1;
+      for (int j = tid; j < kWin; j += kFT)
+        if (sh.win[j] != 0u) last = j;
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) last = max(last, __shfl_xor(last, o, 64));
+      if (lane == 0) sh.lastb[wv] = last;
+      __syncthreads();
+      nb = max(max(sh.lastb[0], sh.lastb[1]), max(sh.lastb[2], sh.lastb[3])) + 1;
+      tot = ((sh.tot[0] + sh.tot[1]) + sh.tot[2]) + sh.tot[3];
+      uint32_t* h32 = a.hcount + (row_slot * n + s) * (2 * kBins0);
+      for (int j = tid; j < nb; j += kFT) h32[j] = sh.win[j];
+    }
+    const float th = float(tot);
+    if (tid == 0) a.partials[row_slot * n + s] = Partial{m, th, float(tot - double(th)), nb};
+    return;
+  }
   // the segment's statistics: its maximum, and (in idx) how many of its
   // bins, from bin 0, are stored: up to the last non-empty one below 511
   int nb = 0;
@@ -758,7 +987,7 @@ template <typename ET>
 __global__ __launch_bounds__(64) void filt_select0_kernel(FiltArgs a) {
   __shared__ Sel0Shared sh;
   const int tid = threadIdx.x;
-  if (blockIdx.x == 0 && tid < kMaxKeyLevels) a.wcount[tid] = 0u;
+  if (blockIdx.x == 0 && tid < kFirstList) a.wcount[tid] = 0u;
   const int R = a.R, n = a.nseg2;
   const int rs = int(blockIdx.x % uint32_t(R));
   const int b = int(blockIdx.x / uint32_t(R));
@@ -768,7 +997,8 @@ __global__ __launch_bounds__(64) void filt_select0_kernel(FiltArgs a) {
   const ReqFilter f = req_filter(a, b);
   pin_all(f.K, f.T, f.top_k, f.top_p, p0.m, p0.idx);
   if (!row_filtered(a, f, rs)) return;
-  select0_row<ET>(a, f, row, p0, sh, tid);
+  if constexpr (kKeyWindow<ET>) select0_window<ET>(a, f, row, p0, sh, tid);
+  else select0_row<ET>(a, f, row, p0, sh, tid);
 }
 
 // ---------------------------------------------------------------------------
@@ -831,8 +1061,10 @@ __device__ void keys_segment(const FiltArgs& a, int b, int rs, int s, int level,
     const uint32_t w = hi[q] - lo[q];
     shift[q] = w == 0u ? 0 : max(0, 32 - __clz(w) - 8);
   }
-  // a listed row searches; at the first key level every filtered row does
-  // (the level-0 selection leaves each of its searches open)
+  // a listed row searches; at the first key level, the rows whose level-0
+  // selection left a search open (fp32 rows: every one; bf16 rows: those
+  // whose threshold is below the key window)
+  if (!LATER && !(on[0] || on[1])) return;
   const ET* rp = is_draft ? static_cast<const ET*>(a.draft) + (start + rs) * a.draft_stride
                           : static_cast<const ET*>(a.target) + (start + (rs - a.max_k)) * a.target_stride;
   const bool al = is_aligned16(rp);
@@ -922,11 +1154,25 @@ template <typename ET>
 __global__ __launch_bounds__(kFT) void filt_keys_first_kernel(FiltArgs a) {
   __shared__ HistShared sh;
   const int n = a.nseg2, R = a.R;
-  const uint32_t item = blockIdx.x;
-  const int s = int(item % uint32_t(n));
-  const int rs = int((item / uint32_t(n)) % uint32_t(R));
-  const int b = int(item / (uint32_t(n) * uint32_t(R)));
-  keys_segment<ET, false>(a, b, rs, s, 1, 1, sh, threadIdx.x);
+  if constexpr (kKeyWindow<ET>) {
+    // the segments listed by the level-0 selection, in list order
+    const uint32_t count = a.wcount[kFirstList];
+    const uint32_t* list = a.work + size_t(a.B) * R * n;
+    for (uint32_t e = blockIdx.x; e < count; e += gridDim.x) {
+      const uint32_t item = list[e];
+      const int s = int(item % uint32_t(n));
+      const int rs = int((item / uint32_t(n)) % uint32_t(R));
+      const int b = int(item / (uint32_t(n) * uint32_t(R)));
+      keys_segment<ET, false>(a, b, rs, s, 1, 1, sh, threadIdx.x);
+      __syncthreads();  // the shared arrays are reused by the next segment
+    }
+  } else {
+    const uint32_t item = blockIdx.x;
+    const int s = int(item % uint32_t(n));
+    const int rs = int((item / uint32_t(n)) % uint32_t(R));
+    const int b = int(item / (uint32_t(n) * uint32_t(R)));
+    keys_segment<ET, false>(a, b, rs, s, 1, 1, sh, threadIdx.x);
+  }
 }
 
 // Selection of the first key level: one wave per row slot; a row still
@@ -948,7 +1194,7 @@ __global__ __launch_bounds__(64) void filt_select_kernel(FiltArgs a, int levels)
   const uint32_t s0 = a.search[row * 2].state, s1 = a.search[row * 2 + 1].state;
   const ReqFilter f = req_filter(a, b);
   pin_all(m, s0, s1, f.K, f.T, f.top_k, f.top_p);
-  if (!row_filtered(a, f, rs)) return;
+  if (!row_filtered(a, f, rs) || (s0 != 1u && s1 != 1u)) return;
   for (int q = tid + 64; q < n; q += 64) m = fmaxf(m, a.partials[row * n + q].m);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
@@ -1396,7 +1642,7 @@ hipError_t launch_filtered(VerifyArgs va, const FilterIO& io, int dtype, hipStre
   if (dtype == SV_BF16) {
     hipLaunchKernelGGL(filt_stats0_kernel<uint16_t>, dim3(g1), dim3(kFT), 0, stream, a);
     hipLaunchKernelGGL(filt_select0_kernel<uint16_t>, dim3(g2), dim3(64), 0, stream, a);
-    hipLaunchKernelGGL(filt_keys_first_kernel<uint16_t>, dim3(g1), dim3(kFT), 0, stream, a);
+    hipLaunchKernelGGL(filt_keys_first_kernel<uint16_t>, dim3(gn), dim3(kFT), 0, stream, a);
     hipLaunchKernelGGL(filt_select_kernel<uint16_t>, dim3(g2), dim3(64), 0, stream, a, levels);
     for (int l = 2; l <= levels; ++l)
       hipLaunchKernelGGL(filt_keys_next_kernel<uint16_t>, dim3(gn), dim3(kFT), 0, stream, a, l, levels);

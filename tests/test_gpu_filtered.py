@@ -229,6 +229,54 @@ def test_ties_uniform_rows_neg_inf_and_signed_zeros():
     assert np.all(gout["kept"][0] == V)
 
 
+def test_key_window_edges_bf16():
+    """bf16 rows select level 0 by exact key counts in the 1024 keys below
+    the row maximum's: request 0 has its maximum at +-0 (both zeros one
+    key); request 1 puts tokens on the lowest key of the window and on the
+    first key below it, so that top-k 600 ends in the window and top-k 601
+    one key below it (the search continues over the keys below); requests
+    2 and 3 have 16384-token segments whose maxima lie far apart, one
+    segment without a finite logit, the row maximum in the first or the
+    last segment."""
+    g = np.random.default_rng(41)
+    B, K, V = 4, 2, 65536
+    seg = 16384
+    zd = np.zeros((B, K, V), np.float32)
+    zt = np.zeros((B, K + 1, V), np.float32)
+    zero_vals = np.array([-0.0, 0.0, -0.5, -3.0], np.float32)
+    zd[0] = g.choice(zero_vals, (K, V), p=[0.3, 0.3, 0.2, 0.2])
+    zt[0] = g.choice(zero_vals, (K + 1, V), p=[0.3, 0.3, 0.2, 0.2])
+    lowest_in, first_below = 0.003936767578125, 0.00390625  # bf16 keys 0xbb81, 0xbb80 below 1.0's 0xbf80
+    edge = np.full(V, -1.0, np.float32)
+    edge[:100], edge[100:300], edge[300:600], edge[600:1000] = 1.0, 0.5, lowest_in, first_below
+    for r in range(K):
+        zd[1, r] = g.permutation(edge)
+    for r in range(K + 1):
+        zt[1, r] = g.permutation(edge)
+    offs = np.repeat(np.array([0.0, -30.0, 0.0, -3.0], np.float32), seg)
+    for q in (2, 3):
+        zd[q] = g.normal(0, 1.0, (K, V)) + offs
+        zt[q] = g.normal(0, 1.0, (K + 1, V)) + offs
+        zd[q, :, 2 * seg:3 * seg] = -np.inf
+        zt[q, :, 2 * seg:3 * seg] = -np.inf
+    zd[3, :, 3 * seg:] += 10.0
+    zt[3, :, 3 * seg:] += 10.0
+    toks = np.array([[1, 2], [3, 4], [5, 6], [3 * seg + 1, 3 * seg + 2]])
+    zeros = lambda rows: int(np.sum(gen.bf16_bits_to_f32(rows) == 0.0, axis=1)[0])
+    for top_k, top_p in [(0, 0.5), (0, 0.95), (600, 1.0), (601, 1.0), (300, 0.99)]:
+        b = _batch(zd, zt, toks, 1.0, top_k, top_p, dtype="bf16", seed=top_k)
+        _log(f"case filtered key window k={top_k} p={top_p}")
+        gout, o = _run(b)
+        assert compare_filtered(b, gout, o) == 0
+        if (top_k, top_p) == (600, 1.0):
+            assert np.all(gout["kept"][1] == 600)
+        if (top_k, top_p) == (601, 1.0):
+            assert np.all(gout["kept"][1] == 1000)
+        if (top_k, top_p) == (0, 0.5):  # the zeros, of both signs, and nothing else
+            for r in range(K + 1):
+                assert gout["kept"][0, K + r] == zeros(b.target[(K + 1) * 0 + r:(K + 1) * 0 + r + 1])
+
+
 def test_long_runs_of_equal_logits_above_the_boundary():
     """60000 equal logits in one level-0 bin above the top-p boundary: that
     bin's fraction sum over the row needs more than 32 bits (a 32-bit sum
