@@ -211,21 +211,24 @@ size_t sv_filtered_workspace_size(int B, int V, int max_k, int dtype);
  *   top_k   int32 [B]   top_k[b] <= 0 or >= V: no top-k filter.
  *   top_p   float [B]   top_p[b] >= 1 (or NaN): no top-p filter; otherwise
  *           0 < top_p[b] < 1 (device precondition).
- *   Device precondition of a filtered row (besides sv_spec_verify's): its
- *   logits z satisfy |z| * 8 * log2(e) / T < 2^21 (level-0 bins are cells of
- *   1/8 log2 unit on an absolute grid, formed exactly in fp32).
+ *   Device precondition of a filtered fp32 row (besides sv_spec_verify's):
+ *   its logits z satisfy |z| * 8 * log2(e) / T < 2^21 (level-0 bins are
+ *   cells of 1/8 log2 unit on an absolute grid, formed exactly in fp32).
  *   kept    int32 [B*(2*max_k+1)]  nullable: per row slot (draft rows
  *           0..max_k-1, then target rows 0..max_k) the number of tokens kept
  *           by the filters, -1 for rows not filtered or not read.
  *   p_draft_at_token, p_target_at_token: the filtered probabilities p'.
  *   workspace: at least sv_filtered_workspace_size(B, V, max_k, dtype)
  *           bytes, zero-filled once.
- * The kept sets are exact to the resolution of the mass sums, which are
- * integers (level 0: 2^-23 of a bin's lower edge, the binary32 weights
- * relative to that edge added exactly; key levels: 2^-40 of the row
- * maximum's probability), so that every mass compared, the row's total
- * included, is within 2^-22 of the row's total of the sum of the weights it
- * stands for, and independent of the order of the additions;
+ * The kept sets are exact to the resolution of the mass sums: fp32 rows'
+ * level-0 sums are integers (2^-23 of a bin's lower edge, the binary32
+ * weights relative to that edge added exactly); bf16 rows' level 0 counts
+ * tokens per key exactly (a key's mass is its count times its weight, in
+ * binary64) and takes the row's total from binary32 sums of eight weights
+ * added in binary64; key levels sum integers (2^-40 of the row maximum's
+ * probability).  Every mass compared, the row's total included, is within
+ * 2^-22 of the row's total of the sum of the weights it stands for, and
+ * independent of the order of the additions;
  * the top-p comparison is made on them in binary64, the threshold found by a
  * radix select over the logits' order-preserving keys.  Outputs are a
  * deterministic function of the inputs.  Returns SV_OK, or a negative
