@@ -158,6 +158,7 @@ static_assert(sizeof(FSearch) == kFilterSearchBytes, "search state layout");
 static_assert(kBins == kFilterBins && kBins0 == kFilterBins0, "histogram bins");
 static_assert(kFT * kFV * 8 < (1 << (64 - kCountShift0)) && kFT * kFV * 8 * double(0x3f8b95c2u) < double(kOne0),
               "level-0 counts and bit sums of a segment fit their fields");
+static_assert(kFT * kFV * 8 < 65536, "a bf16 segment's key counts fit 16 bits");
 
 struct FiltArgs {
   int B, V, max_k, R, nseg2;
@@ -570,8 +571,8 @@ __device__ void select0_window(const FiltArgs& a, const ReqFilter& f, size_t row
     S += sh.segm[q] != -INFINITY ? sh.segt[q] * exp2(double(sh.segm[q] * c) - double(mc)) : 0.0;
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) S += __shfl_xor(S, o, 64);
-  const uint32_t* h32 = a.hcount + row * n * (2 * kBins0);
-  // the merge reads offsets 64 i + lane (each load a contiguous 256 bytes),
+  const uint16_t* h16 = reinterpret_cast<const uint16_t*>(a.hcount + row * n * (2 * kBins0));
+  // the merge reads offsets 64 i + lane (each load a contiguous 128 bytes),
   // then hands each lane its 16 offsets through LDS
   uint32_t cm[kPer] = {};
   // segments kGather at a time, every load of them issued before any sum
@@ -589,7 +590,7 @@ __device__ void select0_window(const FiltArgs& a, const ReqFilter& f, size_t row
       for (int i = 0; i < kPer; ++i) {
         const int ds = 64 * i + lane - shift;
         in[u][i] = ds >= 0 && ds < nbs;
-        x[u][i] = h32[size_t(sg) * (2 * kBins0) + min(max(ds, 0), max(nbs - 1, 0))];
+        x[u][i] = h16[size_t(sg) * (4 * kBins0) + min(max(ds, 0), max(nbs - 1, 0))];
       }
     }
 #pragma unroll
@@ -932,8 +933,9 @@ __global__ __launch_bounds__(kFT) __attribute__((amdgpu_waves_per_eu(8))) void f
       __syncthreads();
       nb = max(max(sh.lastb[0], sh.lastb[1]), max(sh.lastb[2], sh.lastb[3])) + 1;
       tot = ((sh.tot[0] + sh.tot[1]) + sh.tot[2]) + sh.tot[3];
+      // stored as 16-bit counts (a segment's 2^14 tokens fit), two to a word
       uint32_t* h32 = a.hcount + (row_slot * n + s) * (2 * kBins0);
-      for (int j = tid; j < nb; j += kFT) h32[j] = sh.win[j];
+      for (int j = tid; 2 * j < nb; j += kFT) h32[j] = sh.win[2 * j] | (sh.win[2 * j + 1] << 16);
     }
     const float th = float(tot);
     if (tid == 0) a.partials[row_slot * n + s] = Partial{m, th, float(tot - double(th)), nb};
