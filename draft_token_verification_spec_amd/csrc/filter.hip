@@ -984,7 +984,8 @@ __global__ __launch_bounds__(kFT) __attribute__((amdgpu_waves_per_eu(8))) void f
 }
 
 // Level-0 selection: one wave per row slot.  Workgroup 0 also clears the
-// counters of the key levels' lists.
+// counters of the later key levels' lists; a bf16 row also clears its
+// arrival counter, which its first key level uses.
 template <typename ET>
 __global__ __launch_bounds__(64) void filt_select0_kernel(FiltArgs a) {
   __shared__ Sel0Shared sh;
@@ -998,6 +999,7 @@ __global__ __launch_bounds__(64) void filt_select0_kernel(FiltArgs a) {
   const Partial p0 = a.partials[row * n + min(tid, n - 1)];
   const ReqFilter f = req_filter(a, b);
   pin_all(f.K, f.T, f.top_k, f.top_p, p0.m, p0.idx);
+  if (kKeyWindow<ET> && tid == 0) a.tickets[row] = 0u;  // the later levels' arrival counter
   if (!row_filtered(a, f, rs)) return;
   if constexpr (kKeyWindow<ET>) select0_window<ET>(a, f, row, p0, sh, tid);
   else select0_row<ET>(a, f, row, p0, sh, tid);
@@ -1151,13 +1153,15 @@ __device__ void keys_segment(const FiltArgs& a, int b, int rs, int s, int level,
   if (tid == 0) store_dev(&a.tickets[row], 0u);
 }
 
-// The first key level: one workgroup per 32 KiB segment of every row slot.
+// The first key level.  fp32: one workgroup per 32 KiB segment of every row
+// slot, its selection a kernel of its own.  bf16: the segments listed by the
+// level-0 selection, in list order, each row's selection made by its last
+// arriving segment workgroup as at the later levels.
 template <typename ET>
-__global__ __launch_bounds__(kFT) void filt_keys_first_kernel(FiltArgs a) {
+__global__ __launch_bounds__(kFT) void filt_keys_first_kernel(FiltArgs a, int levels) {
   __shared__ HistShared sh;
   const int n = a.nseg2, R = a.R;
   if constexpr (kKeyWindow<ET>) {
-    // the segments listed by the level-0 selection, in list order
     const uint32_t count = a.wcount[kFirstList];
     const uint32_t* list = a.work + size_t(a.B) * R * n;
     for (uint32_t e = blockIdx.x; e < count; e += gridDim.x) {
@@ -1165,7 +1169,7 @@ __global__ __launch_bounds__(kFT) void filt_keys_first_kernel(FiltArgs a) {
       const int s = int(item % uint32_t(n));
       const int rs = int((item / uint32_t(n)) % uint32_t(R));
       const int b = int(item / (uint32_t(n) * uint32_t(R)));
-      keys_segment<ET, false>(a, b, rs, s, 1, 1, sh, threadIdx.x);
+      keys_segment<ET, true>(a, b, rs, s, 1, levels, sh, threadIdx.x);
       __syncthreads();  // the shared arrays are reused by the next segment
     }
   } else {
@@ -1644,8 +1648,7 @@ hipError_t launch_filtered(VerifyArgs va, const FilterIO& io, int dtype, hipStre
   if (dtype == SV_BF16) {
     hipLaunchKernelGGL(filt_stats0_kernel<uint16_t>, dim3(g1), dim3(kFT), 0, stream, a);
     hipLaunchKernelGGL(filt_select0_kernel<uint16_t>, dim3(g2), dim3(64), 0, stream, a);
-    hipLaunchKernelGGL(filt_keys_first_kernel<uint16_t>, dim3(gn), dim3(kFT), 0, stream, a);
-    hipLaunchKernelGGL(filt_select_kernel<uint16_t>, dim3(g2), dim3(64), 0, stream, a, levels);
+    hipLaunchKernelGGL(filt_keys_first_kernel<uint16_t>, dim3(gn), dim3(kFT), 0, stream, a, levels);
     for (int l = 2; l <= levels; ++l)
       hipLaunchKernelGGL(filt_keys_next_kernel<uint16_t>, dim3(gn), dim3(kFT), 0, stream, a, l, levels);
     hipLaunchKernelGGL(filt_verdict_kernel<uint16_t>, dim3(unsigned(va.B)), dim3(64), 0, stream, a, info, desc);
@@ -1655,7 +1658,7 @@ hipError_t launch_filtered(VerifyArgs va, const FilterIO& io, int dtype, hipStre
   } else {
     hipLaunchKernelGGL(filt_stats0_kernel<float>, dim3(g1), dim3(kFT), 0, stream, a);
     hipLaunchKernelGGL(filt_select0_kernel<float>, dim3(g2), dim3(64), 0, stream, a);
-    hipLaunchKernelGGL(filt_keys_first_kernel<float>, dim3(g1), dim3(kFT), 0, stream, a);
+    hipLaunchKernelGGL(filt_keys_first_kernel<float>, dim3(g1), dim3(kFT), 0, stream, a, levels);
     hipLaunchKernelGGL(filt_select_kernel<float>, dim3(g2), dim3(64), 0, stream, a, levels);
     for (int l = 2; l <= levels; ++l)
       hipLaunchKernelGGL(filt_keys_next_kernel<float>, dim3(gn), dim3(kFT), 0, stream, a, l, levels);
