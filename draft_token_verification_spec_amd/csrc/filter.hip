@@ -147,7 +147,7 @@ __device__ __forceinline__ uint64_t fixed_mass(float z, float c, float mc) {
 struct FSearch {
   uint32_t lo, hi;  // key interval holding the threshold
   uint32_t cabove;  // tokens with a key above the interval
-  uint32_t state;   // 0 unused, 1 searching, 2 done
+  uint32_t state;   // 0 unused, 1 searching, 2 done, 3 searching by weight cells (below)
   double mabove;    // mass above the interval (from the window pass on)
   double mfinal;    // done: mass of the kept tokens
   double target;    // top-k: k; top-p: top_p x the row's mass
@@ -265,8 +265,9 @@ constexpr int kMaxSegs = int(int64_t(SV_MAX_V) * 4 / (kFT * kFV * 16));  // 32 K
 constexpr int kMaxKeyLevels = 4;  // fp32 keys: 4 digits of 8 bits
 // Entry of wcount counting the bf16 rows' segments listed for the first key
 // level (levels 2.. count theirs in entries 0..kMaxKeyLevels - 2; a bf16
-// search has 2 key levels at most, so the entry and list 1 of `work` are
-// free for it); cleared by the statistics pass.
+// search has 3 key levels at most, so the entry is free for it, and list 1
+// of `work` is read by the first key level before the second lists the
+// third level's segments there); cleared by the statistics pass.
 constexpr int kFirstList = kMaxKeyLevels - 1;
 
 __device__ __forceinline__ uint64_t load_dev64(const uint64_t* p) {
@@ -359,6 +360,19 @@ __device__ uint32_t key_hi_of_bin(int j, float c8, float g) {
   }
   return uint32_t(lo);
 }
+
+// A bf16 search whose threshold lies below the key window (state
+// kSearchCells) takes its first key level by weight cells instead of key
+// digits: the keys below the window spread over many octaves of |z|, most of
+// them near zero, where a cell of 1/8 log2 unit of weight holds thousands of
+// keys but 8-bit key digits split nothing.  Digit 255 - j holds level-0 bin
+// j against the cell g of the interval's top value (j = g - F(z), the cells
+// g .. g - 254), digit 0 every lower cell; a digit's key range comes from
+// the level-0 bisections.  Each element adds one 64-bit word as at level 0,
+// 2^45 + bits(r) with r its weight relative to its cell's lower edge (1 in
+// digit 0, whose mass is only needed when it narrows to one key, and is
+// then its count times that key's weight).
+constexpr uint32_t kSearchCells = 3u;
 
 // Wave-wide reductions and exclusive prefix in lane order (every lane gets
 // the result).
@@ -645,7 +659,7 @@ __device__ void select0_window(const FiltArgs& a, const ReqFilter& f, size_t row
       w.cabove = call;
       w.mabove = mall;
       w.target = target;
-      w.state = 1u;
+      w.state = kSearchCells;
     }
     fc = fc0;
     fm = fm0;
@@ -695,16 +709,19 @@ __device__ bool select_row(const FiltArgs& a, float c, float mc, size_t row, int
 #pragma unroll 1
   for (int q = 0; q < 2; ++q) {
     const FSearch cur = st[q];
-    if (cur.state != 1u) continue;
+    if (cur.state != 1u && cur.state != kSearchCells) continue;
+    const bool cells = kKeyWindow<ET> && cur.state == kSearchCells;
     const uint32_t w = cur.hi - cur.lo;
     const int shf = w == 0u ? 0 : max(0, 32 - __clz(w) - 8);
-    const int nd = int(w >> shf);  // the interval's last digit (no others are stored)
+    const int nd = cells ? kBins - 1 : int(w >> shf);  // the interval's last digit (no others are stored)
+    const bool wide = cells || shf > 0;  // digits of several keys: their masses are stored
     uint32_t cd[kSelDigits] = {};
-    uint64_t mfix[kSelDigits] = {};
+    uint64_t mfix[kSelDigits] = {};  // fixed-point masses; weight cells: sums of (r - 1) 2^23
     // segments kGather at a time, every load of them issued before any sum
     // (digits past the interval's last and segments past the row's load a
     // stored entry instead and are masked)
-    constexpr int kGather = 4;
+    // (inside a streaming pass, two at a time: its registers bound the pass's waves)
+    constexpr int kGather = DEV ? 2 : 4;
     auto gather = [&](auto wide_t) {
       constexpr bool wide = decltype(wide_t)::value;
       for (int s0 = 0; s0 < n; s0 += kGather) {
@@ -727,22 +744,32 @@ __device__ bool select_row(const FiltArgs& a, float c, float mc, size_t row, int
             const int d = kBins - 1 - (kSelDigits * lane + k);
             const bool in = s0 + u < n && d <= nd;
             cd[k] += in ? xc[u][k] : 0u;
-            if constexpr (wide) mfix[k] += in ? xm[u][k] : 0ull;
+            if constexpr (wide)
+              mfix[k] += in ? (cells ? (xm[u][k] & (kOne0 - 1)) - uint64_t(xc[u][k]) * kOneBits : xm[u][k]) : 0ull;
           }
       }
     };
     // masses are stored only for digits wider than one key
-    if (shf > 0) gather(std::true_type{});
+    if (wide) gather(std::true_type{});
     else gather(std::false_type{});
     double md[kSelDigits];
     uint32_t tc = 0;
     double tm = 0.0;
+    // weight cells: the edge of digit d (bin j = 255 - d) relative to the row
+    // maximum's weight, 2^((g - j)/8 - m c)
+    const double ce = cells ? exp2(double(cell_of(Key<ET>::value(cur.hi), c * float(kBinsPerLog2))) / kBinsPerLog2 -
+                                   double(mc))
+                            : 0.0;
 #pragma unroll
     for (int k = 0; k < kSelDigits; ++k) {
       const int d = kBins - 1 - (kSelDigits * lane + k);
+      const int j = kBins - 1 - d;
       // a one-key digit's mass: its count times the weight of that key, the
       // same float expression as an element's weight
-      md[k] = shf > 0 ? double(mfix[k]) / double(kFix)
+      md[k] = cells ? (d > 0 && cd[k] > 0u ? ldexp(ce * kPow2Eighth[j & 7], -(j >> 3)) *
+                                                 (double(cd[k]) + double(int64_t(mfix[k])) / kFrac0)
+                                           : 0.0)
+            : wide ? double(mfix[k]) / double(kFix)
                       : (cd[k] > 0u ? double(cd[k]) * double(fast_exp2(fmaf(Key<ET>::value(cur.lo + uint32_t(d)), c,
                                                                                 -mc)))
                                     : 0.0);
@@ -772,23 +799,46 @@ __device__ bool select_row(const FiltArgs& a, float c, float mc, size_t row, int
     dq = -wave_max_int(-dq);
     dtop = wave_max_int(dtop);
     const int ds = dq < kBins ? dq : dtop;
-    int open = 0;
+    // the lane holding digit ds takes its figures out of the unrolled arrays,
+    // then forms the digit's key range once
+    int sd = -1;
+    uint32_t sc = 0, scd = 0;
+    double sm = 0.0, smd = 0.0;
 #pragma unroll
     for (int k = 0; k < kSelDigits; ++k) {
       const int d = kBins - 1 - (kSelDigits * lane + k);
       if (d != ds) continue;
+      sd = d;
+      sc = fck[k];
+      scd = cd[k];
+      sm = fmk[k];
+      smd = md[k];
+    }
+    int open = 0;
+    if (sd >= 0) {
       FSearch nx = cur;
-      const uint64_t lo = uint64_t(cur.lo) + (uint64_t(d) << shf);
-      const uint64_t hi = min(uint64_t(cur.hi), lo + (uint64_t(1) << shf) - 1);
+      uint64_t lo, hi;
+      if (cells) {
+        const float c8 = c * float(kBinsPerLog2);
+        const float g = cell_of(Key<ET>::value(cur.hi), c8);
+        const int j = kBins - 1 - sd;  // the level-0 bin against g
+        lo = j == kBins - 1 ? uint64_t(cur.lo) : max(uint64_t(cur.lo), uint64_t(key_lo_of_bin<ET>(j, c8, g)));
+        hi = min(uint64_t(cur.hi), uint64_t(key_hi_of_bin<ET>(j, c8, g)));
+      } else {
+        lo = uint64_t(cur.lo) + (uint64_t(sd) << shf);
+        hi = min(uint64_t(cur.hi), lo + (uint64_t(1) << shf) - 1);
+      }
       nx.lo = uint32_t(lo);
       nx.hi = uint32_t(hi);
-      nx.mabove = fmk[k];
-      nx.cabove = fck[k];
+      nx.mabove = sm;
+      nx.cabove = sc;
+      nx.state = 1u;
       if (lo == hi) {
         nx.state = 2u;
         nx.key = uint32_t(lo);
-        nx.kept = fck[k] + cd[k];
-        nx.mfinal = fmk[k] + md[k];
+        nx.kept = sc + scd;
+        // (a weight cell's mass by its one key's weight: digit 0 has none)
+        nx.mfinal = sm + (cells ? double(scd) * double(fast_exp2(fmaf(Key<ET>::value(uint32_t(lo)), c, -mc))) : smd);
       } else {
         open = 1;
       }
@@ -1057,11 +1107,12 @@ __device__ void keys_segment(const FiltArgs& a, int b, int rs, int s, int level,
     hi[q] = st.hi;
   }
   if (!row_filtered(a, f, rs)) return;
-  bool on[2];
+  bool on[2], cells[2];
   int shift[2];
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
-    on[q] = st_state[q] == 1u;
+    on[q] = st_state[q] == 1u || st_state[q] == kSearchCells;
+    cells[q] = st_state[q] == kSearchCells;
     const uint32_t w = hi[q] - lo[q];
     shift[q] = w == 0u ? 0 : max(0, 32 - __clz(w) - 8);
   }
@@ -1084,6 +1135,10 @@ __device__ void keys_segment(const FiltArgs& a, int b, int rs, int s, int level,
   }
   const float c = kLog2e / f.T;
   const float mc = wave_row_max(a.partials + row * n, n, lane) * c;
+  const float c8 = c * float(kBinsPerLog2);
+  float gc[2];  // a weight-cell search: the cell of the interval's top value
+#pragma unroll
+  for (int q = 0; q < 2; ++q) gc[q] = cells[q] ? cell_of(Key<ET>::value(hi[q]), c8) : 0.f;
   for (int j = tid; j < 2 * kBins; j += kFT) {
     (&sh.count[0][0])[j] = 0u;
     (&sh.mass[0][0])[j] = 0u;
@@ -1100,14 +1155,38 @@ __device__ void keys_segment(const FiltArgs& a, int b, int rs, int s, int level,
   __syncthreads();
   // per element a test against each searching slot's value interval; the
   // common case of one search gets a loop of its own
-  auto digit_add = [&](int q, float z) {
-    const int dg = int((Key<ET>::of(z) - lo[q]) >> shift[q]);
-    atomicAdd(&sh.count[q][dg], 1u);
-    if (shift[q] > 0)
-      atomicAdd(reinterpret_cast<unsigned long long*>(&sh.mass[q][dg]),
-                static_cast<unsigned long long>(fixed_mass(z, c, mc)));
+  auto digit_add = [&](int q, float z, auto cells_t) {
+    if constexpr (decltype(cells_t)::value) {
+      const float j = gc[q] - cell_of(z, c8);
+      const bool deep = !(j < float(kBins - 1));  // digit 0 (also -inf)
+      const float r = deep ? 1.f : fast_exp2(fmaf(j, 1.f / kBinsPerLog2, fmaf(z, c, gc[q] * (-1.f / kBinsPerLog2))));
+      atomicAdd(reinterpret_cast<unsigned long long*>(&sh.mass[q][deep ? 0 : kBins - 1 - int(j)]),
+                static_cast<unsigned long long>(kOne0 | __float_as_uint(r)));
+    } else {
+      const int dg = int((Key<ET>::of(z) - lo[q]) >> shift[q]);
+      atomicAdd(&sh.count[q][dg], 1u);
+      if (shift[q] > 0)
+        atomicAdd(reinterpret_cast<unsigned long long*>(&sh.mass[q][dg]),
+                  static_cast<unsigned long long>(fixed_mass(z, c, mc)));
+    }
   };
-  if (on[0] && on[1]) {
+  auto one_search = [&](int q, auto cells_t) {
+    const float l = zlo[q], h = zhi[q];
+#pragma unroll
+    for (int k = 0; k < kFV; ++k)
+#pragma unroll
+      for (int j = 0; j < N; ++j) {
+        const float z = Elem<ET>::get(v[k], j);
+        if (z >= l && z <= h) digit_add(q, z, cells_t);
+      }
+  };
+  // Weight cells are only a bf16 row's first key level, where every open
+  // search of the row has them over the same interval (the keys below the
+  // window): one histogram serves both.
+  const int q1 = on[0] ? 0 : 1;
+  if (kKeyWindow<ET> && cells[q1]) {
+    one_search(q1, std::true_type{});
+  } else if (on[0] && on[1]) {
 #pragma unroll
     for (int k = 0; k < kFV; ++k)
 #pragma unroll
@@ -1115,31 +1194,27 @@ __device__ void keys_segment(const FiltArgs& a, int b, int rs, int s, int level,
         const float z = Elem<ET>::get(v[k], j);
 #pragma unroll
         for (int q = 0; q < 2; ++q)
-          if (z >= zlo[q] && z <= zhi[q]) digit_add(q, z);
+          if (z >= zlo[q] && z <= zhi[q]) digit_add(q, z, std::false_type{});
       }
   } else {
-    const int q = on[0] ? 0 : 1;
-    const float l = zlo[q], h = zhi[q];
-#pragma unroll
-    for (int k = 0; k < kFV; ++k)
-#pragma unroll
-      for (int j = 0; j < N; ++j) {
-        const float z = Elem<ET>::get(v[k], j);
-        if (z >= l && z <= h) digit_add(q, z);
-      }
+    one_search(q1, std::false_type{});
   }
   __syncthreads();
   // only the interval's digits are stored: the digits below ((hi - lo) >> shift) + 1
   const size_t seg = row * n + s;
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
-    if (!on[q] || tid > int((hi[q] - lo[q]) >> shift[q])) continue;
+    if (!on[q] || tid > (cells[q] ? kBins - 1 : int((hi[q] - lo[q]) >> shift[q]))) continue;
+    const bool wide = cells[q] || shift[q] > 0;
+    const int hq = cells[q] ? q1 : q;  // a weight-cell histogram was built once
+    const uint64_t mw = sh.mass[hq][tid];
+    const uint32_t cw = cells[q] ? uint32_t(mw >> kCountShift0) : sh.count[hq][tid];
     if (LATER) {
-      if (shift[q] > 0) store_dev64(&a.hmass[(seg * 2 + q) * kBins + tid], sh.mass[q][tid]);
-      store_dev(&a.hcount[seg * 2 * kBins0 + q * kBins0 + tid], sh.count[q][tid]);
+      if (wide) store_dev64(&a.hmass[(seg * 2 + q) * kBins + tid], mw);
+      store_dev(&a.hcount[seg * 2 * kBins0 + q * kBins0 + tid], cw);
     } else {
-      if (shift[q] > 0) a.hmass[(seg * 2 + q) * kBins + tid] = sh.mass[q][tid];
-      a.hcount[seg * 2 * kBins0 + q * kBins0 + tid] = sh.count[q][tid];
+      if (wide) a.hmass[(seg * 2 + q) * kBins + tid] = mw;
+      a.hcount[seg * 2 * kBins0 + q * kBins0 + tid] = cw;
     }
   }
   if (!LATER) return;
@@ -1644,7 +1719,9 @@ hipError_t launch_filtered(VerifyArgs va, const FilterIO& io, int dtype, hipStre
   RowInfo* info = reinterpret_cast<RowInfo*>(io.info);
   DrawDesc* desc = reinterpret_cast<DrawDesc*>(io.desc);
   float* slices = io.slices;
-  const int levels = dtype == SV_BF16 ? 2 : kMaxKeyLevels;  // key-digit levels after level 0
+  // key levels after level 0: bf16, a weight-cell level (below the window)
+  // then two of 8-bit digits; fp32, four of 8-bit digits
+  const int levels = dtype == SV_BF16 ? 3 : kMaxKeyLevels;
   if (dtype == SV_BF16) {
     hipLaunchKernelGGL(filt_stats0_kernel<uint16_t>, dim3(g1), dim3(kFT), 0, stream, a);
     hipLaunchKernelGGL(filt_select0_kernel<uint16_t>, dim3(g2), dim3(64), 0, stream, a);

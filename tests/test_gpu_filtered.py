@@ -234,10 +234,10 @@ def test_key_window_edges_bf16():
     the row maximum's: request 0 has its maximum at +-0 (both zeros one
     key); request 1 puts tokens on the lowest key of the window and on the
     first key below it, so that top-k 600 ends in the window and top-k 601
-    one key below it (the search continues over the keys below); requests
-    2 and 3 have 16384-token segments whose maxima lie far apart, one
-    segment without a finite logit, the row maximum in the first or the
-    last segment."""
+    one key below it (the search continues over the keys below, by weight
+    cells, then by key digits); requests 2 and 3 have 16384-token segments
+    whose maxima lie far apart, one segment without a finite logit, the row
+    maximum in the first or the last segment."""
     g = np.random.default_rng(41)
     B, K, V = 4, 2, 65536
     seg = 16384
@@ -263,7 +263,10 @@ def test_key_window_edges_bf16():
     zt[3, :, 3 * seg:] += 10.0
     toks = np.array([[1, 2], [3, 4], [5, 6], [3 * seg + 1, 3 * seg + 2]])
     zeros = lambda rows: int(np.sum(gen.bf16_bits_to_f32(rows) == 0.0, axis=1)[0])
-    for top_k, top_p in [(0, 0.5), (0, 0.95), (600, 1.0), (601, 1.0), (300, 0.99)]:
+    # (0, 0.95), (300, 0.99), (40000, 0.95): thresholds below the window in
+    # requests 0, 2 and 3 (N(0, 1) segments), the last with both searches
+    # continuing there by weight cells
+    for top_k, top_p in [(0, 0.5), (0, 0.95), (600, 1.0), (601, 1.0), (300, 0.99), (40000, 0.95)]:
         b = _batch(zd, zt, toks, 1.0, top_k, top_p, dtype="bf16", seed=top_k)
         _log(f"case filtered key window k={top_k} p={top_p}")
         gout, o = _run(b)
