@@ -149,7 +149,7 @@ struct FSearch {
   uint32_t cabove;  // tokens with a key above the interval
   uint32_t state;   // 0 unused, 1 searching, 2 done, 3 searching by weight cells (below)
   double mabove;    // mass above the interval (from the window pass on)
-  double mfinal;    // done: mass of the kept tokens
+  double mfinal;    // done: mass of the kept tokens; weight cells: the edge of the top cell
   double target;    // top-k: k; top-p: top_p x the row's mass
   uint32_t key;     // done: the threshold key
   uint32_t kept;    // done: kept tokens
@@ -278,18 +278,6 @@ __device__ __forceinline__ void store_dev64(uint64_t* p, uint64_t v) {
 }
 __device__ __forceinline__ uint32_t load_dev32(const uint32_t* p) {
   return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// Loads of another workgroup's histogram: device-scope within the kernel
-// that wrote it (DEV), plain in a later kernel.
-template <bool DEV>
-__device__ __forceinline__ uint32_t load_h32(const uint32_t* p) {
-  if constexpr (DEV) return load_dev32(p);
-  else return *p;
-}
-template <bool DEV>
-__device__ __forceinline__ uint64_t load_h64(const uint64_t* p) {
-  if constexpr (DEV) return load_dev64(p);
-  else return *p;
 }
 
 // 2^(-k/8), k = 0..7: a level-0 bin edge is 2^(-j/8) = 2^-(j/8 rounded down)
@@ -660,6 +648,8 @@ __device__ void select0_window(const FiltArgs& a, const ReqFilter& f, size_t row
       w.mabove = mall;
       w.target = target;
       w.state = kSearchCells;
+      // the edge of the interval's top cell relative to the row maximum's weight
+      w.mfinal = exp2(double(cell_of(Key<ET>::value(w.hi), c * float(kBinsPerLog2))) / kBinsPerLog2 - double(mc));
     }
     fc = fc0;
     fm = fm0;
@@ -696,12 +686,12 @@ __device__ void select0_window(const FiltArgs& a, const ReqFilter& f, size_t row
 
 constexpr int kSelDigits = kBins / 64;  // key digits per lane of the selection
 
-// Key-level selection of a row by one wave; lane l owns digits
-// kBins - 1 - (4l + k), k = 0..3, so that a prefix in lane order (and k
-// order within a lane) sums the digits of larger keys.  The segment
-// histograms are merged in segment order.  Returns (in every lane) whether
-// a search of the row is still open.
-template <typename ET, bool DEV>
+// Key-level selection of a row by one wave, in a kernel of its own (an fp32
+// row's first key level); lane l owns digits kBins - 1 - (4l + k), k = 0..3,
+// so that a prefix in lane order (and k order within a lane) sums the digits
+// of larger keys.  The segment histograms are merged in segment order.
+// Returns (in every lane) whether a search of the row is still open.
+template <typename ET>
 __device__ bool select_row(const FiltArgs& a, float c, float mc, size_t row, int lane) {
   const int n = a.nseg2;
   FSearch* st = a.search + row * 2;
@@ -709,19 +699,16 @@ __device__ bool select_row(const FiltArgs& a, float c, float mc, size_t row, int
 #pragma unroll 1
   for (int q = 0; q < 2; ++q) {
     const FSearch cur = st[q];
-    if (cur.state != 1u && cur.state != kSearchCells) continue;
-    const bool cells = kKeyWindow<ET> && cur.state == kSearchCells;
+    if (cur.state != 1u) continue;
     const uint32_t w = cur.hi - cur.lo;
     const int shf = w == 0u ? 0 : max(0, 32 - __clz(w) - 8);
-    const int nd = cells ? kBins - 1 : int(w >> shf);  // the interval's last digit (no others are stored)
-    const bool wide = cells || shf > 0;  // digits of several keys: their masses are stored
+    const int nd = int(w >> shf);  // the interval's last digit (no others are stored)
     uint32_t cd[kSelDigits] = {};
-    uint64_t mfix[kSelDigits] = {};  // fixed-point masses; weight cells: sums of (r - 1) 2^23
+    uint64_t mfix[kSelDigits] = {};
     // segments kGather at a time, every load of them issued before any sum
     // (digits past the interval's last and segments past the row's load a
     // stored entry instead and are masked)
-    // (inside a streaming pass, two at a time: its registers bound the pass's waves)
-    constexpr int kGather = DEV ? 2 : 4;
+    constexpr int kGather = 4;
     auto gather = [&](auto wide_t) {
       constexpr bool wide = decltype(wide_t)::value;
       for (int s0 = 0; s0 < n; s0 += kGather) {
@@ -733,8 +720,8 @@ __device__ bool select_row(const FiltArgs& a, float c, float mc, size_t row, int
 #pragma unroll
           for (int k = 0; k < kSelDigits; ++k) {
             const int d = min(kBins - 1 - (kSelDigits * lane + k), nd);  // within the stored digits
-            xc[u][k] = load_h32<DEV>(&a.hcount[seg * 2 * kBins0 + q * kBins0 + d]);
-            if constexpr (wide) xm[u][k] = load_h64<DEV>(&a.hmass[(seg * 2 + q) * kBins + d]);
+            xc[u][k] = a.hcount[seg * 2 * kBins0 + q * kBins0 + d];
+            if constexpr (wide) xm[u][k] = a.hmass[(seg * 2 + q) * kBins + d];
           }
         }
 #pragma unroll
@@ -744,32 +731,22 @@ __device__ bool select_row(const FiltArgs& a, float c, float mc, size_t row, int
             const int d = kBins - 1 - (kSelDigits * lane + k);
             const bool in = s0 + u < n && d <= nd;
             cd[k] += in ? xc[u][k] : 0u;
-            if constexpr (wide)
-              mfix[k] += in ? (cells ? (xm[u][k] & (kOne0 - 1)) - uint64_t(xc[u][k]) * kOneBits : xm[u][k]) : 0ull;
+            if constexpr (wide) mfix[k] += in ? xm[u][k] : 0ull;
           }
       }
     };
     // masses are stored only for digits wider than one key
-    if (wide) gather(std::true_type{});
+    if (shf > 0) gather(std::true_type{});
     else gather(std::false_type{});
     double md[kSelDigits];
     uint32_t tc = 0;
     double tm = 0.0;
-    // weight cells: the edge of digit d (bin j = 255 - d) relative to the row
-    // maximum's weight, 2^((g - j)/8 - m c)
-    const double ce = cells ? exp2(double(cell_of(Key<ET>::value(cur.hi), c * float(kBinsPerLog2))) / kBinsPerLog2 -
-                                   double(mc))
-                            : 0.0;
 #pragma unroll
     for (int k = 0; k < kSelDigits; ++k) {
       const int d = kBins - 1 - (kSelDigits * lane + k);
-      const int j = kBins - 1 - d;
       // a one-key digit's mass: its count times the weight of that key, the
       // same float expression as an element's weight
-      md[k] = cells ? (d > 0 && cd[k] > 0u ? ldexp(ce * kPow2Eighth[j & 7], -(j >> 3)) *
-                                                 (double(cd[k]) + double(int64_t(mfix[k])) / kFrac0)
-                                           : 0.0)
-            : wide ? double(mfix[k]) / double(kFix)
+      md[k] = shf > 0 ? double(mfix[k]) / double(kFix)
                       : (cd[k] > 0u ? double(cd[k]) * double(fast_exp2(fmaf(Key<ET>::value(cur.lo + uint32_t(d)), c,
                                                                                 -mc)))
                                     : 0.0);
@@ -817,17 +794,8 @@ __device__ bool select_row(const FiltArgs& a, float c, float mc, size_t row, int
     int open = 0;
     if (sd >= 0) {
       FSearch nx = cur;
-      uint64_t lo, hi;
-      if (cells) {
-        const float c8 = c * float(kBinsPerLog2);
-        const float g = cell_of(Key<ET>::value(cur.hi), c8);
-        const int j = kBins - 1 - sd;  // the level-0 bin against g
-        lo = j == kBins - 1 ? uint64_t(cur.lo) : max(uint64_t(cur.lo), uint64_t(key_lo_of_bin<ET>(j, c8, g)));
-        hi = min(uint64_t(cur.hi), uint64_t(key_hi_of_bin<ET>(j, c8, g)));
-      } else {
-        lo = uint64_t(cur.lo) + (uint64_t(sd) << shf);
-        hi = min(uint64_t(cur.hi), lo + (uint64_t(1) << shf) - 1);
-      }
+      const uint64_t lo = uint64_t(cur.lo) + (uint64_t(sd) << shf);
+      const uint64_t hi = min(uint64_t(cur.hi), lo + (uint64_t(1) << shf) - 1);
       nx.lo = uint32_t(lo);
       nx.hi = uint32_t(hi);
       nx.mabove = sm;
@@ -837,8 +805,7 @@ __device__ bool select_row(const FiltArgs& a, float c, float mc, size_t row, int
         nx.state = 2u;
         nx.key = uint32_t(lo);
         nx.kept = sc + scd;
-        // (a weight cell's mass by its one key's weight: digit 0 has none)
-        nx.mfinal = sm + (cells ? double(scd) * double(fast_exp2(fmaf(Key<ET>::value(uint32_t(lo)), c, -mc))) : smd);
+        nx.mfinal = sm + smd;
       } else {
         open = 1;
       }
@@ -1064,7 +1031,137 @@ struct HistShared {
   uint32_t count[2][kBins];
   uint32_t base;
   int last, more;
+  // the workgroup selection's per-wave figures
+  uint32_t wc[kFT / 64];
+  double wm[kFT / 64];
+  int wq[kFT / 64], wt[kFT / 64];
 };
+
+// Key-level selection of a row by a whole workgroup, the one that delivered
+// the row's last segment histogram (the histograms read with device-scope
+// loads): thread t owns digit kBins - 1 - t, so that a prefix in thread
+// order (lanes, then waves) sums the digits of larger keys.  The rules are
+// select_row's; one digit per thread keeps the pass's register budget, and
+// with it its waves.  Returns (in every thread) whether a search of the row
+// is still open.
+template <typename ET>
+__device__ bool select_row_wg(const FiltArgs& a, float c, float mc, size_t row, HistShared& sh, int tid) {
+  static_assert(kFT == kBins, "one digit per thread");
+  const int n = a.nseg2, lane = tid & 63, wv = tid >> 6;
+  constexpr int kW = kFT / 64;
+  FSearch* st = a.search + row * 2;
+  int more = 0;
+#pragma unroll 1
+  for (int q = 0; q < 2; ++q) {
+    const FSearch cur = st[q];
+    if (cur.state != 1u && cur.state != kSearchCells) continue;
+    const bool cells = kKeyWindow<ET> && cur.state == kSearchCells;
+    const uint32_t w = cur.hi - cur.lo;
+    const int shf = w == 0u ? 0 : max(0, 32 - __clz(w) - 8);
+    const int nd = cells ? kBins - 1 : int(w >> shf);
+    const bool wide = cells || shf > 0;
+    const int d = kBins - 1 - tid;
+    uint32_t cd = 0;
+    uint64_t mfix = 0;  // fixed-point mass; weight cells: sum of (r - 1) 2^23
+    if (d <= nd) {
+      constexpr int kGather = 4;
+      for (int s0 = 0; s0 < n; s0 += kGather) {
+        uint32_t xc[kGather];
+        uint64_t xm[kGather];
+#pragma unroll
+        for (int u = 0; u < kGather; ++u) {
+          const size_t seg = row * n + min(s0 + u, n - 1);
+          xc[u] = load_dev32(&a.hcount[seg * 2 * kBins0 + q * kBins0 + d]);
+          xm[u] = wide ? load_dev64(&a.hmass[(seg * 2 + q) * kBins + d]) : 0ull;
+        }
+#pragma unroll
+        for (int u = 0; u < kGather; ++u) {
+          const bool in = s0 + u < n;
+          cd += in ? xc[u] : 0u;
+          mfix += in ? (cells ? (xm[u] & (kOne0 - 1)) - uint64_t(xc[u]) * kOneBits : xm[u]) : 0ull;
+        }
+      }
+    }
+    double md = 0.0;
+    if (cd > 0u) {
+      if (cells) {
+        const int j = kBins - 1 - d;
+        const double ce = cur.mfinal;  // the top cell's edge
+        md = d > 0 ? ldexp(ce * kPow2Eighth[j & 7], -(j >> 3)) * (double(cd) + double(int64_t(mfix)) / kFrac0)
+                   : 0.0;
+      } else if (wide) {
+        md = double(mfix) / double(kFix);
+      } else {
+        // a one-key digit: its count times that key's weight (an element's expression)
+        md = double(cd) * double(fast_exp2(fmaf(Key<ET>::value(cur.lo + uint32_t(d)), c, -mc)));
+      }
+    }
+    // exclusive prefix in thread order: within the wave, then the waves before
+    uint32_t wct;
+    double wmt;
+    const uint32_t pc = wave_excl_scan<uint32_t>(cd, lane, &wct);
+    const double pm = wave_excl_scan<double>(md, lane, &wmt);
+    if (lane == 0) {
+      sh.wc[wv] = wct;
+      sh.wm[wv] = wmt;
+    }
+    __syncthreads();
+    uint32_t fc = cur.cabove;
+    double fm = cur.mabove;
+    for (int u = 0; u < wv; ++u) {
+      fc += sh.wc[u];
+      fm += sh.wm[u];
+    }
+    fc += pc;
+    fm += pm;
+    // the smallest qualifying digit (the largest non-empty one if none is)
+    const bool qual = cd > 0u && (q == 0 ? double(fc) < cur.target : fm < cur.target);
+    int dq = -wave_max_int(qual ? -d : -kBins);
+    int dt = wave_max_int(cd > 0u ? d : -1);
+    if (lane == 0) {
+      sh.wq[wv] = dq;
+      sh.wt[wv] = dt;
+    }
+    __syncthreads();
+    for (int u = 0; u < kW; ++u) {
+      dq = min(dq, sh.wq[u]);
+      dt = max(dt, sh.wt[u]);
+    }
+    const int ds = dq < kBins ? dq : dt;
+    if (d == ds) {
+      FSearch nx = cur;
+      uint64_t lo, hi;
+      if (cells) {
+        const float c8 = c * float(kBinsPerLog2);
+        const float g = cell_of(Key<ET>::value(cur.hi), c8);
+        const int j = kBins - 1 - d;  // the level-0 bin against g
+        lo = j == kBins - 1 ? uint64_t(cur.lo) : max(uint64_t(cur.lo), uint64_t(key_lo_of_bin<ET>(j, c8, g)));
+        hi = min(uint64_t(cur.hi), uint64_t(key_hi_of_bin<ET>(j, c8, g)));
+      } else {
+        lo = uint64_t(cur.lo) + (uint64_t(d) << shf);
+        hi = min(uint64_t(cur.hi), lo + (uint64_t(1) << shf) - 1);
+      }
+      nx.lo = uint32_t(lo);
+      nx.hi = uint32_t(hi);
+      nx.mabove = fm;
+      nx.cabove = fc;
+      nx.state = 1u;
+      if (lo == hi) {
+        nx.state = 2u;
+        nx.key = uint32_t(lo);
+        nx.kept = fc + cd;
+        // (a weight cell's mass by its one key's weight: digit 0 has none)
+        nx.mfinal = fm + (cells ? double(cd) * double(fast_exp2(fmaf(Key<ET>::value(uint32_t(lo)), c, -mc))) : md);
+      } else {
+        sh.more = 1;
+      }
+      st[q] = nx;
+    }
+    __syncthreads();
+  }
+  more = sh.more;
+  return more != 0;
+}
 
 // The segments of a row still searching after key level `level` are listed
 // for the next level, if there is one.
@@ -1219,12 +1316,9 @@ __device__ void keys_segment(const FiltArgs& a, int b, int rs, int s, int level,
   }
   if (!LATER) return;
   if (!arrive_last_all(&a.tickets[row], uint32_t(n), &sh.last)) return;
-  if (tid < 64) {
-    const bool more = select_row<ET, true>(a, c, mc, row, tid);
-    if (tid == 0) sh.more = more ? 1 : 0;
-  }
+  if (tid == 0) sh.more = 0;
   __syncthreads();
-  if (sh.more) list_row(a, row, level, levels, &sh.base, tid);
+  if (select_row_wg<ET>(a, c, mc, row, sh, tid)) list_row(a, row, level, levels, &sh.base, tid);
   if (tid == 0) store_dev(&a.tickets[row], 0u);
 }
 
@@ -1280,7 +1374,7 @@ __global__ __launch_bounds__(64) void filt_select_kernel(FiltArgs a, int levels)
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
   const float c = kLog2e / f.T;
-  if (select_row<ET, false>(a, c, m * c, row, tid)) list_row(a, row, 1, levels, &base, tid);
+  if (select_row<ET>(a, c, m * c, row, tid)) list_row(a, row, 1, levels, &base, tid);
 }
 
 // Later key levels: the segments listed by the previous level's selections,
