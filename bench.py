@@ -730,6 +730,28 @@ def extras(args, res, sv, sets, batches, outs, params, ws, call, dev, log):
                                          positions_per_s=pos / (ms * 1e-3),
                                          kept_tokens_mean=float(fo[0]["kept"][fo[0]["kept"] >= 0].float().mean()),
                                          mean_accept_len=float(fo[0]["accept_len"].float().mean()))
+        if b0.dtype == "bf16":
+            # the same rows with their logits halved (noise N(0, 1)): the top-p
+            # 0.95 thresholds then lie below zero, under the 1024-key window
+            # below each maximum, so every search goes on through the
+            # weight-cell and key-digit levels, reading its row again
+            half = [dict(d, draft=d["draft"] * 0.5, target=d["target"] * 0.5) for d in sets]
+            ho = [None] * n_sets
+
+            def hcall(i):
+                d = half[i]
+                ho[i] = sv.sv_spec_verify_filtered(d["draft"], d["draft_row_start"], d["target"],
+                                                   d["target_row_start"], d["num_draft"], d["draft_tokens"],
+                                                   d["temperature"], tk, tp, d["u_accept"], d["u_residual"],
+                                                   d["u_bonus"], max_k=K, workspace=fws, out=ho[i])
+
+            for i in range(n_sets):
+                hcall(i)
+            ms_h, _ = graph_ms(rot(hcall), 10, dev)
+            ex["filtered_verify"]["thresholds_below_window"] = roofline(
+                fbytes, ms_h, kernel="sv_spec_verify_filtered call, logits halved",
+                kept_tokens_mean=float(ho[0]["kept"][ho[0]["kept"] >= 0].float().mean()))
+            del half, ho
     st = sv.sv_workspace_status(ws, dev)
     ex["workspace_status"] = int(st.item())
 
