@@ -128,8 +128,13 @@ def summarize_counters(args):
            "bytes_per_call": sum(out[k]["bytes_per_launch"] for k in call),
            "fetch_scale": scale["FETCH_SIZE"], "write_scale": scale["WRITE_SIZE"], "kernels": out,
            "kernel_source_sha256": kernel_source_hash()}
-    if all(k in out for k in FILTERED_KERNELS):
-        rec["filtered_bytes_per_call"] = sum(out[k]["bytes_per_launch"] for k in FILTERED_KERNELS)
+    if FILTERED_KERNELS[0] in out:
+        # a call launches the first pass once and some kernels several times
+        # (bf16: the later key levels twice): bytes of all their dispatches
+        # over the number of calls
+        calls = out[FILTERED_KERNELS[0]]["dispatches"]
+        rec["filtered_bytes_per_call"] = sum(out[k]["bytes_per_launch"] * out[k]["dispatches"]
+                                             for k in FILTERED_KERNELS if k in out) / calls
         rec["filtered_kernel_source_sha256"] = kernel_source_hash(filtered=True)
     with open(args.traffic, "w") as fh:
         json.dump(rec, fh, indent=1)
@@ -730,7 +735,8 @@ def extras(args, res, sv, sets, batches, outs, params, ws, call, dev, log):
                                          positions_per_s=pos / (ms * 1e-3),
                                          kept_tokens_mean=float(fo[0]["kept"][fo[0]["kept"] >= 0].float().mean()),
                                          mean_accept_len=float(fo[0]["accept_len"].float().mean()))
-        if b0.dtype == "bf16":
+        if b0.dtype == "bf16" and args.copy_calibration == 0:
+            # (not in a counter pass, whose filtered bytes are the call above's)
             # the same rows with their logits halved (noise N(0, 1)): the top-p
             # 0.95 thresholds then lie below zero, under the 1024-key window
             # below each maximum, so every search goes on through the

@@ -211,9 +211,11 @@ size_t sv_filtered_workspace_size(int B, int V, int max_k, int dtype);
  *   top_k   int32 [B]   top_k[b] <= 0 or >= V: no top-k filter.
  *   top_p   float [B]   top_p[b] >= 1 (or NaN): no top-p filter; otherwise
  *           0 < top_p[b] < 1 (device precondition).
- *   Device precondition of a filtered fp32 row (besides sv_spec_verify's):
- *   its logits z satisfy |z| * 8 * log2(e) / T < 2^21 (level-0 bins are
- *   cells of 1/8 log2 unit on an absolute grid, formed exactly in fp32).
+ *   Device precondition of a filtered row (besides sv_spec_verify's): its
+ *   logits z satisfy |z| * 8 * log2(e) / T < 2^21 (fp32 rows' level 0 and
+ *   the first key level of bf16 rows whose threshold lies below their key
+ *   window bin by cells of 1/8 log2 unit on an absolute grid, formed
+ *   exactly in fp32).
  *   kept    int32 [B*(2*max_k+1)]  nullable: per row slot (draft rows
  *           0..max_k-1, then target rows 0..max_k) the number of tokens kept
  *           by the filters, -1 for rows not filtered or not read.
