@@ -22,9 +22,10 @@
 //            keys from the row maximum's down, and the row's total mass from
 //            the segments' weight sums; a threshold inside that window is
 //            found here, with no key level;
-//   level L  8-bit digits of the key within the boundary bin's keys (bf16:
-//            the keys below the window), until one key remains (bf16 keys:
-//            2 levels at most, fp32: 4).
+//   level L  8-bit digits of the key within the boundary bin's keys, until
+//            one key remains (fp32: 4 levels at most); bf16 rows whose
+//            threshold lies below the window take the keys below it by
+//            weight cells first, then 2 levels of digits at most.
 // Each level's counts come from a streaming pass (one workgroup per 32 KiB
 // row segment; every count an integer added with LDS atomics, so the result
 // does not depend on the order of the additions) and a selection (one wave
@@ -252,14 +253,14 @@ __device__ __forceinline__ uint4 load_nan_tail(const ET* row, int first, int lim
 // selection
 // ---------------------------------------------------------------------------
 //
-// Level 0 and the first key level are selected by kernels of their own (one
-// wave per row).  A later key level, where few rows still search, runs
-// on the listed segments only, and a row's selection is made there by the
-// workgroup that delivers the row's last segment histogram (every segment
-// workgroup publishes its histogram with device-scope stores, then takes a
-// ticket on the row's arrival counter; see arrive_last_all), reading the
-// others' histograms with device-scope loads.  The counter is back at zero
-// when the selection ends.
+// Level 0 and an fp32 row's first key level are selected by kernels of their
+// own (one wave per row).  The other key levels, where few rows still
+// search, run on the listed segments only, and a row's selection is made
+// there by the workgroup that delivers the row's last segment histogram
+// (every segment workgroup publishes its histogram with device-scope stores,
+// then takes a ticket on the row's arrival counter; see arrive_last_all),
+// reading the others' histograms with device-scope loads.  The counter is
+// back at zero when the selection ends.
 
 constexpr int kMaxSegs = int(int64_t(SV_MAX_V) * 4 / (kFT * kFV * 16));  // 32 KiB segments of the longest row
 constexpr int kMaxKeyLevels = 4;  // fp32 keys: 4 digits of 8 bits
@@ -1179,11 +1180,11 @@ __device__ __forceinline__ void list_row(const FiltArgs& a, size_t row, int leve
 // One key-level pass over segment s of row slot rs of request b: per
 // searching slot, the elements of its key interval by key digit: counts,
 // and 2^-40 fixed-point masses when a digit spans several keys (a single
-// key's mass is its count times its weight).  At the first key level they
-// are stored for the selection kernel; at later ones (LATER) they are
-// published for the row's selection, which the row's last arriving segment
-// workgroup then makes, listing the row for the next level if it still
-// searches.
+// key's mass is its count times its weight), or by weight cells.  At an fp32
+// row's first key level they are stored for the selection kernel; otherwise
+// (LATER) they are published for the row's selection, which the row's last
+// arriving segment workgroup then makes, listing the row for the next level
+// if it still searches.
 template <typename ET, bool LATER>
 __device__ void keys_segment(const FiltArgs& a, int b, int rs, int s, int level, int levels, HistShared& sh,
                              int tid) {
@@ -1350,8 +1351,8 @@ __global__ __launch_bounds__(kFT) void filt_keys_first_kernel(FiltArgs a, int le
   }
 }
 
-// Selection of the first key level: one wave per row slot; a row still
-// searching is listed for the second.  Also clears the row's arrival
+// Selection of an fp32 row's first key level: one wave per row slot; a row
+// still searching is listed for the second.  Also clears the row's arrival
 // counter, used by the later levels.
 template <typename ET>
 __global__ __launch_bounds__(64) void filt_select_kernel(FiltArgs a, int levels) {
