@@ -204,7 +204,8 @@ def test_top1_is_greedy_and_tiny_top_p_keeps_the_maximum():
     assert np.all(gout2["kept"] == 1)
 
 
-def test_ties_uniform_rows_neg_inf_and_signed_zeros():
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_ties_uniform_rows_neg_inf_and_signed_zeros(dtype):
     V, K = 2048, 2
     zd = np.zeros((4, K, V), np.float32)
     zt = np.zeros((4, K + 1, V), np.float32)
@@ -220,11 +221,11 @@ def test_ties_uniform_rows_neg_inf_and_signed_zeros():
     zt[3] = g.choice(np.array([-0.0, 0.0, 1e-30, -1e-30, 1e-3, -1e-3, 2.0], np.float32), (K + 1, V))
     toks = np.array([[3, 7], [1, 2], [int(np.argmax(zd[2, 0])), 5], [0, 9]])
     for top_k, top_p in [(0, 0.5), (1500, 1.0), (100, 0.7)]:
-        b = _batch(zd, zt, toks, 1.0, top_k, top_p, seed=top_k)
-        _log(f"case filtered ties k={top_k} p={top_p}")
+        b = _batch(zd, zt, toks, 1.0, top_k, top_p, dtype=dtype, seed=top_k)
+        _log(f"case filtered ties {dtype} k={top_k} p={top_p}")
         gout, o = _run(b)
         assert compare_filtered(b, gout, o) == 0
-    b = _batch(zd, zt, toks, 1.0, 0, 0.5)
+    b = _batch(zd, zt, toks, 1.0, 0, 0.5, dtype=dtype)
     gout, _ = _run(b)
     assert np.all(gout["kept"][0] == V)
 
@@ -298,21 +299,23 @@ def test_long_runs_of_equal_logits_above_the_boundary():
         assert np.all(gout["kept"][:, [0, 1, 2]] == V)
 
 
-def test_segment_maxima_far_apart():
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_segment_maxima_far_apart(dtype):
     """Segments whose maxima lie hundreds of level-0 bins apart: some
-    wholly in the last bin, one without a finite logit, and in request 1
-    the row maximum outside the first segment."""
+    wholly in the last bin (fp32) or far below the row's key window (bf16),
+    one without a finite logit, and in request 1 the row maximum outside the
+    first segment."""
     g = np.random.default_rng(23)
     B, K, V = 4, 2, 131072
-    seg = 8192  # fp32 elements per 32 KiB segment
+    seg = 8192 if dtype == "f32" else 16384  # elements per 32 KiB segment
     offs = -3.0 * (np.arange(V) // seg)  # 16 segments, each ~69 bins below the previous at T = 1
     zd = (g.normal(0, 1.0, (B, K, V)) + offs).astype(np.float32)
     zt = (g.normal(0, 1.0, (B, K + 1, V)) + offs).astype(np.float32)
     zd[:, :, 3 * seg:4 * seg] = -np.inf
     zt[1, :, :seg] -= 40.0  # request 1: the maxima in the second segment
     for top_k, top_p, T in [(0, 0.999, 1.0), (20000, 1.0, 1.0), (0, 0.9999999, 0.25), (5000, 0.99, 4.0)]:
-        b = _batch(zd, zt, _draws(zd, T, 7), T, top_k, top_p)
-        _log(f"case filtered far segments k={top_k} p={top_p} T={T}")
+        b = _batch(zd, zt, _draws(zd, T, 7), T, top_k, top_p, dtype=dtype)
+        _log(f"case filtered far segments {dtype} k={top_k} p={top_p} T={T}")
         gout, o = _run(b)
         assert compare_filtered(b, gout, o) <= 1
 
@@ -358,13 +361,14 @@ def test_temperatures_max_draft_length_and_largest_vocabulary():
     V = sv.SV_MAX_V
     zd = g.normal(0, 2, (1, 1, V)).astype(np.float32)
     zt = g.normal(0, 2, (1, 2, V)).astype(np.float32)
-    b = _batch(zd, zt, _draws(zd, 1.0, 4), 1.0, 0, 0.95)
-    _log("case filtered V=2^21")
-    gout, o = _run(b)
-    # at this vocabulary every token's probability is ~1e-6, so the draw's
-    # CDF margin is below 1e-5 by construction: a differing token is a
-    # within-margin flip; kept counts and probabilities are still exact
-    assert compare_filtered(b, gout, o) <= 1
+    for dtype in ("f32", "bf16"):  # bf16: 128 segments per row, more than a wave's lanes
+        b = _batch(zd, zt, _draws(zd, 1.0, 4), 1.0, 0, 0.95, dtype=dtype)
+        _log(f"case filtered V=2^21 {dtype}")
+        gout, o = _run(b)
+        # at this vocabulary every token's probability is ~1e-6, so the draw's
+        # CDF margin is below 1e-5 by construction: a differing token is a
+        # within-margin flip; kept counts and probabilities are still exact
+        assert compare_filtered(b, gout, o) <= 1
 
 
 def test_deterministic_and_workspace_reuse():
