@@ -29,7 +29,9 @@ Prints one JSON line:
                         oracle's for the requests the oracle baseline ran;
   cpu_baseline          the oracle, untuned, on the host's cores over a
                         bounded sample of the same workload;
-  extra                 the other entry points on the same batch: the
+  extra                 call_ms_spread: the 10th, 50th and 90th percentiles
+                        of the call time over the graph's replays; and
+                        the other entry points on the same batch: the
                         scoring pass alone, the global draft budget,
                         calibration metrics, the distillation gradient, the
                         filtered verification, and a read-bandwidth probe.
@@ -417,10 +419,13 @@ def parity_block(batch, gpu, seen, gpu_kept=None):
 # GPU timing
 # ---------------------------------------------------------------------------
 
-def graph_ms(fns, reps, dev):
+def graph_ms(fns, reps, dev, spread=None):
     """Milliseconds per call of fns[0], fns[1], ... (one call each per
     rotation), captured once into a HIP graph and replayed ``reps`` times,
-    timed with events on the launching stream."""
+    timed with events on the launching stream.  With ``spread`` (a dict),
+    an event also follows every replay, and the 10th, 50th and 90th
+    percentiles of the per-call time over the replays go into it."""
+    import numpy as np
     import torch
 
     for f in fns:
@@ -433,11 +438,19 @@ def graph_ms(fns, reps, dev):
     g.replay()
     torch.cuda.synchronize(dev)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(reps)] if spread is not None else []
     e0.record()
-    for _ in range(reps):
+    for r in range(reps):
         g.replay()
+        if marks:
+            marks[r].record()
     e1.record()
     torch.cuda.synchronize(dev)
+    if marks:
+        per = [a.elapsed_time(b) / len(fns) for a, b in zip([e0] + marks[:-1], marks)]
+        p10, p50, p90 = np.percentile(per, [10, 50, 90])
+        spread.update({"p10": float(p10), "median": float(p50), "p90": float(p90), "replays": reps,
+                       "calls_per_replay": len(fns)})
     return e0.elapsed_time(e1) / (reps * len(fns)), reps * len(fns)
 
 
@@ -538,7 +551,8 @@ def main(argv=None):
     wall = time.perf_counter() - t0
     log("timing the call")
     call_reps = max(1, min(reps, 60 // len(sets) + 1))
-    call_ms, _ = graph_ms([lambda i=i: call(i) for i in range(len(sets))], call_reps, dev)
+    call_spread = {}
+    call_ms, _ = graph_ms([lambda i=i: call(i) for i in range(len(sets))], call_reps, dev, spread=call_spread)
     # the kept counts the timed calls verified (parameters fixed while the
     # call graph ran)
     kept = [outs[i][1]["num_kept"].cpu().numpy().copy() if pruning else batches[i].num_draft for i in
@@ -575,7 +589,8 @@ def main(argv=None):
         "roofline": rl,
         "extra": {"mean_accept_len": float(outs[0][0]["accept_len"].float().mean()),
                   "positions_per_step": positions, "timed_region_wall_s": wall,
-                  "call_ms": call_ms, "step_minus_call_ms": ms_per_step - call_ms},
+                  "call_ms": call_ms, "call_ms_spread": call_spread,
+                  "step_minus_call_ms": ms_per_step - call_ms},
     }
     if pruning:
         res["extra"]["verified_positions_per_step"] = float(np.mean([k.sum() for k in kept]))
