@@ -663,17 +663,6 @@ __global__ __launch_bounds__(kThreads) void score_finish_kernel(VerifyArgs a, fl
 
 }  // namespace
 
-hipError_t launch_stats(VerifyArgs a, int dtype, hipStream_t stream) {
-  const uint64_t n1 = uint64_t(a.B) * uint64_t(a.R) * uint64_t(a.nseg2);
-  if (n1 == 0) return hipSuccess;
-  if (n1 >= (uint64_t(1) << 31)) return hipErrorInvalidValue;
-  if (dtype == SV_BF16)
-    hipLaunchKernelGGL(stats_kernel<uint16_t>, dim3(unsigned(n1)), dim3(kThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL(stats_kernel<float>, dim3(unsigned(n1)), dim3(kThreads), 0, stream, a);
-  return hipGetLastError();
-}
-
 hipError_t launch_score(VerifyArgs a, float threshold, int32_t* num_kept, int dtype, hipStream_t stream) {
   const uint64_t n1 = uint64_t(a.B) * uint64_t(a.max_k) * uint64_t(a.nseg2);
   if (a.B == 0) return hipSuccess;

@@ -173,9 +173,6 @@ struct VerifyArgs {
 hipError_t launch_score(VerifyArgs a, float threshold, int32_t* num_kept, int dtype, hipStream_t stream);
 // The two streaming kernels (statistics, then the verdict and the draw).
 hipError_t launch_streaming(VerifyArgs a, int dtype, hipStream_t stream);
-// The statistics kernel alone (segment statistics and logits at the draft
-// tokens into the workspace).
-hipError_t launch_stats(VerifyArgs a, int dtype, hipStream_t stream);
 // Device address of the static scratch of the current device (looked up once
 // per device, and zero-filled by a kernel on `stream` until a fill has run
 // outside a graph capture).
