@@ -24,7 +24,9 @@ Prints one JSON line:
                         the launching stream, against the 8 TB/s HBM3E peak;
                         traffic: the HBM bytes rocprofv3 counters measured
                         for the same kernels (profiles/traffic_<workload>.json),
-                        if they describe the current kernel sources;
+                        if they describe the current kernel sources, and
+                        sustained_frac: those bytes over the call's time
+                        against the peak (the re-reads included);
   parity                the GPU's outputs for input set 0 against the CPU
                         oracle's for the requests the oracle baseline ran;
   cpu_baseline          the oracle, untuned, on the host's cores over a
@@ -455,9 +457,16 @@ def graph_ms(fns, reps, dev, spread=None):
 
 
 def roofline(nbytes, ms, traffic=None, **kw):
+    """achieved / frac: algorithmic bytes per launch over the launch time;
+    with counter-measured traffic, also the HBM rate those bytes moved at
+    (sustained_gbs, sustained_frac), which counts the call's re-reads."""
     gbs = nbytes / (ms * 1e-3) / 1e9
     out = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
            "traffic": traffic, "algorithmic_bytes_per_launch": int(nbytes), "ms_per_launch": ms}
+    if traffic:
+        moved = traffic / (ms * 1e-3) / 1e9
+        out["sustained_gbs"] = moved
+        out["sustained_frac"] = moved / PEAK_HBM_GBS
     out.update(kw)
     return out
 
