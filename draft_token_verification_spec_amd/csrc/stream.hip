@@ -464,16 +464,14 @@ __device__ __forceinline__ void confident_feature(const VerifyArgs& a, DrawShare
 
 // Workgroup = segment s of the draw rows of request b (weights); the
 // request's last segment then collects all the weights and searches.
-// Requests in reverse order (the last ones read by the statistics kernel are
-// the likeliest to be cached); every workgroup derives its request's verdict
-// first.
+// Requests in order; every workgroup derives its request's verdict first.
 template <typename ET>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) void draw_kernel(VerifyArgs a) {
   __shared__ DrawShared sh;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n = a.nseg2, max_k = a.max_k;
   const int s = int(blockIdx.x % uint32_t(n));
-  const int b = a.B - 1 - int(blockIdx.x / uint32_t(n));
+  const int b = int(blockIdx.x / uint32_t(n));
   // Everything the verdict needs in one round trip: the request's scalars,
   // lane i's token and uniform, the merge's first loads.  The scalars are
   // loaded by every lane (indexed through an opaque zero), so that they are
