@@ -26,7 +26,10 @@ Prints one JSON line:
                         for the same kernels (profiles/traffic_<workload>.json),
                         if they describe the current kernel sources, and
                         sustained_frac: those bytes over the call's time
-                        against the peak (the re-reads included);
+                        against the peak (the re-reads included), and
+                        design_bound_frac: the algorithmic fraction the call
+                        would reach if it moved those bytes at the read
+                        probe's rate;
   parity                the GPU's outputs for input set 0 against the CPU
                         oracle's for the requests the oracle baseline ran;
   cpu_baseline          the oracle, untuned, on the host's cores over a
@@ -673,6 +676,13 @@ def extras(args, res, sv, sets, batches, outs, params, ws, call, dev, log):
     ex["read_probe"] = {"bytes": nbytes, "ms": ms, "achieved_gbs": nbytes / (ms * 1e-3) / 1e9,
                         "frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
                         "call_frac_of_probe": ms / res["roofline"]["ms_per_launch"]}
+    rl = res["roofline"]
+    if rl.get("traffic") and not prunes(b0):
+        # the ceiling of the call's design: its counter-measured bytes moved at
+        # the probe's rate, against the algorithmic bytes
+        rl["design_bound_frac"] = (rl["algorithmic_bytes_per_launch"] * ex["read_probe"]["achieved_gbs"]
+                                   / rl["traffic"] / PEAK_HBM_GBS)
+        rl["frac_of_design_bound"] = rl["frac"] / rl["design_bound_frac"]
     del pbufs
 
     # the estimator's global draft budget over the batch's scores (one
