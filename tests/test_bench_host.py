@@ -107,3 +107,17 @@ def test_parity_block_counts_flips_and_failures():
     off = {k: v.copy() for k, v in g.items()}
     off["p_target"][0, 0] *= 1.01
     assert not bench.parity_block(b, off, seen)["ok"]
+
+
+def test_roofline_fields_follow_from_bytes_and_time():
+    # 591 MB in 123 us: 4.80 TB/s, 0.600 of 8 TB/s; 729 MB moved in that time
+    # is 5.93 TB/s, 0.741 of peak
+    rl = bench.roofline(591.0e6, 0.123, traffic=729.0e6)
+    assert abs(rl["achieved"] - 591.0e6 / 0.123e-3 / 1e9) < 1e-6
+    assert abs(rl["frac"] - 591.0e6 / 0.123e-3 / 1e9 / 8000.0) < 1e-12
+    assert abs(rl["sustained_frac"] - 729.0e6 / 0.123e-3 / 1e9 / 8000.0) < 1e-12
+    assert rl["sustained_frac"] > rl["frac"]
+    # without counter data there is no sustained rate
+    rl = bench.roofline(591.0e6, 0.123)
+    assert rl["traffic"] is None and "sustained_frac" not in rl
+
