@@ -33,6 +33,42 @@ def test_every_declared_symbol_is_exported():
     assert set(names) <= set(sv.__all__)
 
 
+def declared_prototypes():
+    """name -> (return type, [parameter types]) from the header's prototypes
+    (comments removed, each prototype up to its semicolon)."""
+    text = re.sub(r"/\*.*?\*/", " ", open(HEADER).read(), flags=re.S)
+    out = {}
+    for m in re.finditer(r"^\s*(size_t|int|const char\s*\*)\s*(sv_\w+)\s*\(([^;]*)\)\s*;", text, re.M):
+        params = [" ".join(q.split()) for q in m.group(3).split(",")]
+        out[m.group(2)] = (" ".join(m.group(1).split()), params)
+    return out
+
+
+def ctype_of(decl: str):
+    """The ctypes type a C parameter or return declaration passes as."""
+    d = decl.replace("const ", "")
+    if "*" in d:
+        return ctypes.c_char_p if d.startswith("char") else ctypes.c_void_p
+    base = d.split()[0]
+    return {"int": ctypes.c_int, "size_t": ctypes.c_size_t, "int64_t": ctypes.c_int64,
+            "float": ctypes.c_float}[base]
+
+
+def test_binding_signatures_match_header_prototypes():
+    # every entry point the binding calls passes exactly the header's
+    # parameters, in the header's types (a mismatch would corrupt arguments
+    # silently through ctypes)
+    protos = declared_prototypes()
+    assert set(protos) == set(declared_functions())
+    for name, (res, args) in sv._SIGNATURES.items():
+        ret, params = protos[name]
+        assert res == ctype_of(ret), name
+        assert len(args) == len(params), (name, len(args), len(params))
+        for i, (a, p) in enumerate(zip(args, params)):
+            assert a == ctype_of(p), (name, i, p)
+    assert set(sv._SIGNATURES) == set(protos)
+
+
 def test_header_constants_match_binding():
     text = open(HEADER).read()
     assert int(re.search(r"#define SV_MAX_K (\d+)", text).group(1)) == sv.SV_MAX_K
